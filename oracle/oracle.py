@@ -1,0 +1,139 @@
+"""ctypes wrapper of the CPU oracle (moe_oracle.c).
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, the smoke check and the
+benchmark's CPU-baseline leg.  The GPU library never imports it.  It takes the
+public-layout arrays produced by ``routed_expert_int4_amd.synth`` and returns
+fp64 results.  See moe_oracle.c for what is computed and which page passage
+each step follows.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+_d = ctypes.POINTER(ctypes.c_double)
+_i32 = ctypes.POINTER(ctypes.c_int32)
+_vp = ctypes.c_void_p
+
+
+def build() -> str:
+    """Compile the oracle with gcc (-O2 -fopenmp, no fast-math)."""
+    subprocess.run(["sh", os.path.join(_HERE, "build.sh")], check=True)
+    return _LIB_PATH
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(
+            os.path.join(_HERE, "moe_oracle.c")
+        ):
+            build()
+        L = ctypes.CDLL(_LIB_PATH)
+        L.oracle_expert_ffn.argtypes = [ctypes.c_int, ctypes.c_int] + [_vp] * 6 + [_d, _d, _d]
+        L.oracle_expert_ffn.restype = None
+        L.oracle_router_scores.argtypes = [ctypes.c_int, ctypes.c_int, _vp, _vp, _d, _d, _d, _d]
+        L.oracle_router_scores.restype = None
+        L.oracle_select.argtypes = [ctypes.c_int] * 4 + [ctypes.c_double, _d, _d, _i32, _d, _d]
+        L.oracle_select.restype = ctypes.c_int
+        L.oracle_layer_forward.argtypes = (
+            [ctypes.c_int] * 7 + [ctypes.c_double, _vp, _vp] + [_vp] * 6
+            + [_vp, ctypes.c_int, _vp, _d, _i32, _d, _d, _vp, ctypes.c_int]
+        )
+        L.oracle_layer_forward.restype = ctypes.c_int
+        L.oracle_max_threads.argtypes = []
+        L.oracle_max_threads.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _ptr(a: np.ndarray):
+    assert a.flags["C_CONTIGUOUS"], "oracle inputs must be C-contiguous"
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _dptr(a: np.ndarray):
+    assert a.dtype == np.float64 and a.flags["C_CONTIGUOUS"]
+    return a.ctypes.data_as(_d)
+
+
+def max_threads() -> int:
+    return lib().oracle_max_threads()
+
+
+def expert_ffn(hidden, inter, gate_q, gate_s, up_q, up_s, down_q, down_s, x: np.ndarray):
+    """One expert on one fp64 token vector x[hidden] -> (d[hidden], h[inter])."""
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    d = np.empty(hidden, np.float64)
+    h = np.empty(inter, np.float64)
+    arrs = [np.ascontiguousarray(a) for a in (gate_q, gate_s, up_q, up_s, down_q, down_s)]
+    lib().oracle_expert_ffn(hidden, inter, *[_ptr(a) for a in arrs], _dptr(x), _dptr(d), _dptr(h))
+    return d, h
+
+
+def router_scores(router_w: np.ndarray, bias: np.ndarray, x: np.ndarray):
+    """(logit, s, sb) of one fp64 token vector."""
+    e, hidden = router_w.shape
+    rw = np.ascontiguousarray(router_w, dtype=np.float32)
+    b = np.ascontiguousarray(bias, dtype=np.float32)
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    lg, s, sb = (np.empty(e, np.float64) for _ in range(3))
+    lib().oracle_router_scores(hidden, e, _ptr(rw), _ptr(b), _dptr(x), _dptr(lg), _dptr(s), _dptr(sb))
+    return lg, s, sb
+
+
+def select(n_groups, topk_group, top_k, rsf, s: np.ndarray, sb: np.ndarray):
+    """Group-limited top-k of one token -> (ids, w, gap)."""
+    s = np.ascontiguousarray(s, dtype=np.float64)
+    sb = np.ascontiguousarray(sb, dtype=np.float64)
+    ids = np.empty(top_k, np.int32)
+    w = np.empty(top_k, np.float64)
+    gap = np.empty(1, np.float64)
+    rc = lib().oracle_select(
+        len(s), n_groups, topk_group, top_k, float(rsf), _dptr(s), _dptr(sb),
+        ids.ctypes.data_as(_i32), _dptr(w), _dptr(gap),
+    )
+    if rc != 0:
+        raise ValueError("oracle_select: inconsistent arguments")
+    return ids, w, float(gap[0])
+
+
+def layer_forward(weights, x_bf16: np.ndarray, forced_ids=None, n_threads: int = 0, want_logits=False):
+    """Full layer on tokens x_bf16 [T, H] (bf16 bits).
+
+    Returns dict(y [T,H] f64, ids [T,k] i32, w [T,k] f64, gap [T] f64,
+    logits [T,E] f64 or None)."""
+    cfg = weights.cfg
+    x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
+    T = x.shape[0]
+    k = cfg.top_k
+    y = np.empty((T, cfg.hidden), np.float64)
+    ids = np.empty((T, k), np.int32)
+    w = np.empty((T, k), np.float64)
+    gap = np.empty(T, np.float64)
+    logits = np.empty((T, cfg.n_experts), np.float64) if want_logits else None
+    fid = None
+    if forced_ids is not None:
+        fid = np.ascontiguousarray(forced_ids, dtype=np.int32)
+        assert fid.shape == (T, k)
+    wt = weights
+    rc = lib().oracle_layer_forward(
+        cfg.hidden, cfg.inter, cfg.n_experts, cfg.n_groups, cfg.topk_group, k, cfg.n_shared,
+        float(cfg.routed_scaling_factor),
+        _ptr(wt.router_w), _ptr(wt.bias),
+        _ptr(wt.gate_q), _ptr(wt.gate_s), _ptr(wt.up_q), _ptr(wt.up_s), _ptr(wt.down_q), _ptr(wt.down_s),
+        _ptr(x), T, _ptr(fid) if fid is not None else None,
+        _dptr(y), ids.ctypes.data_as(_i32), _dptr(w), _dptr(gap),
+        logits.ctypes.data_as(ctypes.c_void_p) if logits is not None else None,
+        int(n_threads),
+    )
+    if rc != 0:
+        raise ValueError("oracle_layer_forward: bad arguments")
+    return {"y": y, "ids": ids, "w": w, "gap": gap, "logits": logits}

@@ -1,0 +1,127 @@
+"""Seeded synthetic inputs for the routed int4 MoE layer.
+
+This module draws random numbers and rounds them to the storage formats of the
+public weight layout; it contains none of the layer's arithmetic (no routing,
+no dequantisation, no expert math). Both the CPU oracle and the GPU path
+consume exactly the arrays produced here.
+
+Public layout of one layer (row-major, little-endian):
+
+* ``router_w``  float32 ``[E, H]``
+* ``bias``      float32 ``[E]`` (the expert-score correction bias)
+* per expert ``e`` in ``0..E-1`` followed by the shared expert(s) at index ``E``:
+  ``gate_q`` uint8 ``[I, H/2]``, ``gate_s`` float16 bits ``[I, H/32]``,
+  ``up_q``/``up_s`` likewise, ``down_q`` uint8 ``[H, I/2]``, ``down_s`` float16
+  bits ``[H, I/32]``.  A code byte holds two int4 values in two's complement,
+  the even column in the low nibble; one scale covers 32 consecutive input
+  columns.
+* activations: bfloat16 bits ``[T, H]``.
+
+Value distributions follow the GLM-5.2-shaped layer described on the pages
+(routed experts 256, top-8, ~19 MB of int4 codes per expert): codes are uniform
+random bytes (so both nibbles are independent and uniform over [-8, 7]),
+scales are exp(N(-4, 0.5)) rounded to fp16, the router weight is N(0, 0.02) in
+fp32, the bias N(0, 0.01) in fp32 and the activations N(0, 1) rounded to bf16.
+Draw order for a layer: router weight, bias, then for each expert (routed
+first, shared last) gate codes, gate scales, up codes, up scales, down codes,
+down scales.
+"""
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+
+
+@dataclasses.dataclass(frozen=True)
+class LayerConfig:
+    hidden: int
+    inter: int
+    n_experts: int
+    n_groups: int
+    topk_group: int
+    top_k: int
+    n_shared: int = 1
+    routed_scaling_factor: float = 2.5
+
+    @property
+    def n_total_experts(self) -> int:
+        return self.n_experts + self.n_shared
+
+    def expert_bytes(self) -> int:
+        """Bytes of one expert in the public layout (codes + fp16 scales)."""
+        h, i = self.hidden, self.inter
+        return 3 * (h * i // 2) + 3 * (h * i // 32) * 2
+
+
+# Tiny layer: hidden 256, intermediate 128, 16 experts in 4 groups, top-4 of 2 groups.
+TINY = LayerConfig(hidden=256, inter=128, n_experts=16, n_groups=4, topk_group=2, top_k=4)
+# GLM-5.2-shaped layer: hidden 6144, intermediate 2048, 256 experts in 8 groups, top-8 of 4 groups.
+GLM = LayerConfig(hidden=6144, inter=2048, n_experts=256, n_groups=8, topk_group=4, top_k=8)
+
+
+@dataclasses.dataclass
+class LayerWeights:
+    cfg: LayerConfig
+    router_w: np.ndarray  # float32 [E, H]
+    bias: np.ndarray      # float32 [E]
+    gate_q: np.ndarray    # uint8  [E+S, I, H/2]
+    gate_s: np.ndarray    # uint16 [E+S, I, H/32] (fp16 bits)
+    up_q: np.ndarray
+    up_s: np.ndarray
+    down_q: np.ndarray    # uint8  [E+S, H, I/2]
+    down_s: np.ndarray    # uint16 [E+S, H, I/32]
+
+    def expert_arrays(self, e: int):
+        return (self.gate_q[e], self.gate_s[e], self.up_q[e], self.up_s[e], self.down_q[e], self.down_s[e])
+
+
+def round_to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """float32 -> bfloat16 bit patterns, round to nearest even (storage format)."""
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    nan = np.isnan(a)
+    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+    r[nan] = 0x7FC0
+    return r
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    return (b.astype(np.uint32) << 16).view(np.float32)
+
+
+def _scales(rng: np.random.Generator, shape) -> np.ndarray:
+    return np.exp(rng.normal(-4.0, 0.5, size=shape)).astype(np.float16).view(np.uint16)
+
+
+def gen_layer(cfg: LayerConfig, seed: int) -> LayerWeights:
+    rng = np.random.Generator(np.random.PCG64(seed))
+    h, i, e_all = cfg.hidden, cfg.inter, cfg.n_total_experts
+    router_w = rng.normal(0.0, 0.02, size=(cfg.n_experts, h)).astype(np.float32)
+    bias = rng.normal(0.0, 0.01, size=(cfg.n_experts,)).astype(np.float32)
+    gq = np.empty((e_all, i, h // 2), np.uint8)
+    gs = np.empty((e_all, i, h // 32), np.uint16)
+    uq = np.empty_like(gq)
+    us = np.empty_like(gs)
+    dq = np.empty((e_all, h, i // 2), np.uint8)
+    ds = np.empty((e_all, h, i // 32), np.uint16)
+    for e in range(e_all):
+        gq[e] = rng.integers(0, 256, size=gq.shape[1:], dtype=np.uint8)
+        gs[e] = _scales(rng, gs.shape[1:])
+        uq[e] = rng.integers(0, 256, size=uq.shape[1:], dtype=np.uint8)
+        us[e] = _scales(rng, us.shape[1:])
+        dq[e] = rng.integers(0, 256, size=dq.shape[1:], dtype=np.uint8)
+        ds[e] = _scales(rng, ds.shape[1:])
+    return LayerWeights(cfg, router_w, bias, gq, gs, uq, us, dq, ds)
+
+
+def gen_tokens(cfg: LayerConfig, n_tokens: int, seed: int, std: float = 1.0) -> np.ndarray:
+    """bf16 bits [T, H] of N(0, std^2) activations."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    x = rng.normal(0.0, std, size=(n_tokens, cfg.hidden)).astype(np.float32)
+    return round_to_bf16_bits(x)
+
+
+def gen_noise(cfg: LayerConfig, n_tokens: int, seed: int, std: float) -> np.ndarray:
+    """float32 [T, H] of N(0, std^2) noise (used between stacked layers)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return rng.normal(0.0, std, size=(n_tokens, cfg.hidden)).astype(np.float32)

@@ -1,0 +1,366 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle itself.
+
+Each test checks the oracle against a closed form, an invariant, a brute-force
+enumeration, a library routine (numpy sort / matmul) on weights the test packs
+itself, or byte figures printed on the pages.  The checks are chosen so that a
+plausible mistake (wrong nibble order or sign, wrong scale group, a dropped
+bias, masked experts treated as 0 instead of ineligible, unnormalised weights,
+a missing shared expert, a transposed operand) fails at least one of them.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+from oracle import oracle
+from routed_expert_int4_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ----------------------------------------------------------------- helpers
+def pack_int4(q: np.ndarray) -> np.ndarray:
+    """Test-side packer: integer matrix [R, C] in [-8, 7] -> public bytes [R, C/2]
+    (two's complement nibbles, even column in the low nibble)."""
+    q = np.asarray(q, dtype=np.int64)
+    assert q.min() >= -8 and q.max() <= 7 and q.shape[1] % 2 == 0
+    nib = (q & 15).astype(np.uint8)
+    return (nib[:, 0::2] | (nib[:, 1::2] << 4)).astype(np.uint8)
+
+
+def f16_bits(a) -> np.ndarray:
+    return np.asarray(a, dtype=np.float16).view(np.uint16)
+
+
+def dense(q, s_bits):
+    """Dense fp64 matrix from integer codes [R, C] and fp16 scale bits [R, C/32]."""
+    s = s_bits.view(np.float16).astype(np.float64)
+    return np.asarray(q, np.float64) * np.repeat(s, 32, axis=1)
+
+
+def silu(z):
+    return z / (1.0 + np.exp(-z))
+
+
+def brute_force_select(s, sb, n_groups, topk_group, top_k, rsf):
+    """Exhaustive reading of group-limited top-k on tiny shapes.
+
+    Group score = max over pairs in the group of sb_a + sb_b (the sum of the
+    two largest).  Kept groups = the topk_group-subset with the largest total
+    group score.  Chosen experts = the top_k-subset of eligible experts with
+    the largest total sb.  Ties are not handled (inputs are continuous)."""
+    E = len(sb)
+    gsz = E // n_groups
+    gscore = [max(sb[a] + sb[b] for a, b in itertools.combinations(range(g * gsz, (g + 1) * gsz), 2))
+              for g in range(n_groups)]
+    best_groups = max(itertools.combinations(range(n_groups), topk_group), key=lambda c: sum(gscore[g] for g in c))
+    elig = [e for g in best_groups for e in range(g * gsz, (g + 1) * gsz)]
+    best = max(itertools.combinations(elig, top_k), key=lambda c: sum(sb[e] for e in c))
+    chosen = sorted(best, key=lambda e: -sb[e])
+    w = np.array([rsf * s[e] for e in chosen]) / sum(s[e] for e in chosen)
+    return np.array(chosen), w
+
+
+def dense_layer(wts, x_f64):
+    """Independent recomputation of one token with numpy matmuls on densely
+    dequantised weights and brute-force routing (tiny shapes only)."""
+    cfg = wts.cfg
+    logit = wts.router_w.astype(np.float64) @ x_f64
+    s = 1.0 / (1.0 + np.exp(-logit))
+    sb = s + wts.bias.astype(np.float64)
+    ids, w = brute_force_select(s, sb, cfg.n_groups, cfg.topk_group, cfg.top_k, cfg.routed_scaling_factor)
+
+    def unpack(b):
+        lo = (b & 15).astype(np.int64)
+        hi = (b >> 4).astype(np.int64)
+        q = np.empty((b.shape[0], b.shape[1] * 2), np.int64)
+        q[:, 0::2], q[:, 1::2] = lo, hi
+        return np.where(q >= 8, q - 16, q)
+
+    def ffn(e):
+        G = dense(unpack(wts.gate_q[e]), wts.gate_s[e])
+        U = dense(unpack(wts.up_q[e]), wts.up_s[e])
+        D = dense(unpack(wts.down_q[e]), wts.down_s[e])
+        g = G @ x_f64
+        return D @ (silu(g) * (U @ x_f64))
+
+    y = sum(wj * ffn(e) for wj, e in zip(w, ids))
+    for sh in range(cfg.n_shared):
+        y = y + ffn(cfg.n_experts + sh)
+    return y, ids, w
+
+
+@pytest.fixture(scope="module")
+def tiny():
+    return synth.gen_layer(synth.TINY, seed=0)
+
+
+@pytest.fixture(scope="module")
+def tiny_x():
+    return synth.gen_tokens(synth.TINY, 4, seed=1)
+
+
+# ----------------------------------------------------------------- P1/P2: dequant + expert FFN
+def test_expert_unit_vector_pins_nibbles_and_scale_groups():
+    """x = e_c gives g_i = W_g[i, c] and u_i = W_u[i, c]: pins nibble order,
+    two's complement and which 32-column group a scale covers."""
+    rng = np.random.default_rng(11)
+    H, I = 64, 32
+    Qg = rng.integers(-8, 8, size=(I, H))
+    Qu = rng.integers(-8, 8, size=(I, H))
+    Qd = rng.integers(-8, 8, size=(H, I))
+    Qg[0, :] = -8
+    Qg[1, :] = 7
+    Sg = f16_bits(np.exp(rng.normal(-1, 0.5, size=(I, H // 32))))
+    Su = f16_bits(np.exp(rng.normal(-1, 0.5, size=(I, H // 32))))
+    Sd = f16_bits(np.exp(rng.normal(-1, 0.5, size=(H, I // 32))))
+    args = (pack_int4(Qg), Sg, pack_int4(Qu), Su, pack_int4(Qd), Sd)
+    for c in (0, 1, 2, 31, 32, 33, 63):
+        x = np.zeros(H)
+        x[c] = 1.0
+        d, h = oracle.expert_ffn(H, I, *args, x)
+        g = Qg[:, c] * Sg.view(np.float16).astype(np.float64)[:, c // 32]
+        u = Qu[:, c] * Su.view(np.float16).astype(np.float64)[:, c // 32]
+        np.testing.assert_allclose(h, silu(g) * u, rtol=1e-14, atol=0)
+        # down projection against numpy's matmul on the test's own dense matrix
+        np.testing.assert_allclose(d, dense(Qd, Sd) @ h, rtol=1e-12, atol=1e-14)
+
+
+def test_expert_hand_computed_toy():
+    """32x32 toy with every code 1 and every scale 1: g = u = sum(x),
+    h = silu(sum x) * sum x, d_r = 32 h."""
+    H = I = 32
+    ones = np.ones((I, H), np.int64)
+    S = f16_bits(np.ones((I, 1)))
+    x = np.full(H, 0.5)
+    d, h = oracle.expert_ffn(H, I, pack_int4(ones), S, pack_int4(ones), S, pack_int4(ones), S, x)
+    sx = 16.0
+    h_ref = sx / (1.0 + math.exp(-sx)) * sx
+    assert np.allclose(h, h_ref, rtol=1e-15)
+    assert np.allclose(d, 32.0 * h_ref, rtol=1e-15)
+
+
+def test_expert_zero_input_and_extreme_codes():
+    rng = np.random.default_rng(3)
+    H, I = 64, 64
+    args = []
+    for shape in ((I, H), (I, H), (H, I)):
+        args += [pack_int4(rng.integers(-8, 8, size=shape)), f16_bits(np.full((shape[0], shape[1] // 32), 0.25))]
+    d, h = oracle.expert_ffn(H, I, *args, np.zeros(H))
+    assert np.all(h == 0) and np.all(d == 0)
+    # fp16 scale at the top of its range and subnormal scales decode exactly
+    S = f16_bits(np.array([[65504.0, 2.0 ** -24]]))
+    q = np.zeros((1, 64), np.int64)
+    q[0, 0], q[0, 40] = 7, -8
+    x = np.zeros(64)
+    x[0], x[40] = 1.0, 1.0
+    Sd = f16_bits(np.ones((64, 1)))
+    qd = np.zeros((64, 1 * 32 // 1), np.int64)[:, :32]
+    d, h = oracle.expert_ffn(64, 32, pack_int4(np.vstack([q] * 32)), np.vstack([S] * 32),
+                             pack_int4(np.vstack([q] * 32)), np.vstack([S] * 32),
+                             pack_int4(qd), Sd, x)
+    g = 7 * 65504.0 + (-8) * 2.0 ** -24
+    assert np.allclose(h, silu(g) * g, rtol=1e-15)
+
+
+# ----------------------------------------------------------------- P3-P6: routing
+def test_weights_sum_to_rsf_and_are_positive(tiny, tiny_x):
+    out = oracle.layer_forward(tiny, tiny_x)
+    rsf = tiny.cfg.routed_scaling_factor
+    assert np.allclose(out["w"].sum(axis=1), rsf, rtol=0, atol=1e-12)
+    assert np.all(out["w"] > 0) and np.all(out["w"] < rsf)
+
+
+def test_selection_matches_brute_force_tiny():
+    """Exhaustive enumeration over group pairs and expert subsets (tiny shape),
+    many random score vectors, including negative biased scores (where a
+    zero-fill of masked experts would differ from treating them as ineligible)."""
+    rng = np.random.default_rng(5)
+    cfg = synth.TINY
+    for trial in range(300):
+        s = 1 / (1 + np.exp(-rng.normal(0, 2, size=cfg.n_experts)))
+        bias = rng.normal(0, 0.01 if trial % 2 else 1.0, size=cfg.n_experts)
+        sb = s + bias
+        ids, w, gap = oracle.select(cfg.n_groups, cfg.topk_group, cfg.top_k, cfg.routed_scaling_factor, s, sb)
+        ref_ids, ref_w = brute_force_select(s, sb, cfg.n_groups, cfg.topk_group, cfg.top_k, cfg.routed_scaling_factor)
+        assert list(ids) == list(ref_ids), trial
+        np.testing.assert_allclose(w, ref_w, rtol=1e-13)
+        assert gap > 0
+
+
+def test_selection_glm_shape_against_argsort():
+    """GLM shape: all C(8,4)=70 group subsets enumerated, experts by numpy argsort."""
+    rng = np.random.default_rng(6)
+    cfg = synth.GLM
+    gsz = cfg.n_experts // cfg.n_groups
+    for trial in range(50):
+        s = 1 / (1 + np.exp(-rng.normal(0, 1.6, size=cfg.n_experts)))
+        sb = s + rng.normal(0, 0.01 if trial % 2 else 0.5, size=cfg.n_experts)
+        gscore = [np.sort(sb[g * gsz:(g + 1) * gsz])[-2:].sum() for g in range(cfg.n_groups)]
+        groups = max(itertools.combinations(range(cfg.n_groups), cfg.topk_group), key=lambda c: sum(gscore[g] for g in c))
+        elig = np.array([e for g in groups for e in range(g * gsz, (g + 1) * gsz)])
+        ref = elig[np.argsort(-sb[elig], kind="stable")[: cfg.top_k]]
+        ids, w, _ = oracle.select(cfg.n_groups, cfg.topk_group, cfg.top_k, cfg.routed_scaling_factor, s, sb)
+        assert list(ids) == list(ref)
+
+
+@pytest.mark.parametrize("n_groups,topk_group", [(4, 4), (1, 1)])
+def test_selection_reduces_to_plain_topk(n_groups, topk_group):
+    rng = np.random.default_rng(7)
+    for _ in range(100):
+        s = rng.uniform(0.01, 0.99, size=16)
+        sb = s + rng.normal(0, 0.3, size=16)
+        ids, w, _ = oracle.select(n_groups, topk_group, 4, 1.0, s, sb)
+        assert list(ids) == list(np.argsort(-sb, kind="stable")[:4])
+        np.testing.assert_allclose(w, s[ids] / s[ids].sum(), rtol=1e-14)
+
+
+def test_selection_ties_go_to_lower_index():
+    s = np.full(16, 0.5)
+    sb = np.full(16, 0.5)
+    ids, w, gap = oracle.select(4, 2, 4, 2.5, s, sb)
+    assert list(ids) == [0, 1, 2, 3] and gap == 0.0
+    np.testing.assert_allclose(w, 2.5 / 4)
+
+
+def test_gap_is_the_selection_margin():
+    s = np.full(16, 0.5)
+    sb = np.array([0.9, 0.8, 0.1, 0.0, 0.7, 0.6, 0.05, 0.0, 0.3, 0.2, 0.0, 0.0, 0.1, 0.1, 0.0, 0.0])
+    # group scores 1.7, 1.3, 0.5, 0.2 -> groups 0,1 kept (margin 0.8); experts
+    # 0.9,0.8,0.7,0.6 chosen, next eligible 0.1 -> margin 0.5
+    ids, _, gap = oracle.select(4, 2, 4, 1.0, s, sb)
+    assert list(ids) == [0, 1, 4, 5]
+    assert abs(gap - 0.5) < 1e-15
+
+
+def test_zero_input_routes_on_bias_and_returns_shared_only_output(tiny):
+    """x = 0: every s = 1/2, selection is group-limited top-k of the bias alone,
+    each weight is rsf/k and y = the shared expert's output = 0."""
+    cfg = tiny.cfg
+    x = np.zeros((2, cfg.hidden), np.uint16)
+    out = oracle.layer_forward(tiny, x)
+    ref_ids, _ = brute_force_select(np.full(cfg.n_experts, 0.5), 0.5 + tiny.bias.astype(np.float64),
+                                    cfg.n_groups, cfg.topk_group, cfg.top_k, cfg.routed_scaling_factor)
+    assert list(out["ids"][0]) == list(ref_ids)
+    np.testing.assert_array_equal(out["w"], np.full_like(out["w"], cfg.routed_scaling_factor / cfg.top_k))
+    assert np.all(out["y"] == 0.0)
+
+
+# ----------------------------------------------------------------- whole layer
+def test_layer_matches_dense_numpy_with_brute_force_routing(tiny, tiny_x):
+    out = oracle.layer_forward(tiny, tiny_x)
+    xf = synth.bf16_bits_to_f32(tiny_x).astype(np.float64)
+    for t in range(tiny_x.shape[0]):
+        y, ids, w = dense_layer(tiny, xf[t])
+        assert list(out["ids"][t]) == list(ids)
+        np.testing.assert_allclose(out["w"][t], w, rtol=1e-13)
+        np.testing.assert_allclose(out["y"][t], y, rtol=1e-11, atol=1e-12 * np.abs(y).max())
+
+
+def test_routed_off_gives_shared_expert_output(tiny, tiny_x):
+    import dataclasses
+    wts = dataclasses.replace(tiny, gate_q=tiny.gate_q.copy(), up_q=tiny.up_q.copy(), down_q=tiny.down_q.copy())
+    E = tiny.cfg.n_experts
+    wts.gate_q[:E] = 0
+    wts.up_q[:E] = 0
+    wts.down_q[:E] = 0
+    out = oracle.layer_forward(wts, tiny_x)
+    xf = synth.bf16_bits_to_f32(tiny_x).astype(np.float64)
+    for t in range(tiny_x.shape[0]):
+        d, _ = oracle.expert_ffn(tiny.cfg.hidden, tiny.cfg.inter, *tiny.expert_arrays(E), xf[t])
+        np.testing.assert_array_equal(out["y"][t], d)
+        assert np.any(d != 0)
+
+
+def test_rsf_scales_routed_part_linearly(tiny, tiny_x):
+    import dataclasses
+    base = oracle.layer_forward(tiny, tiny_x)
+    cfg2 = dataclasses.replace(tiny.cfg, routed_scaling_factor=2 * tiny.cfg.routed_scaling_factor)
+    out2 = oracle.layer_forward(dataclasses.replace(tiny, cfg=cfg2), tiny_x)
+    xf = synth.bf16_bits_to_f32(tiny_x).astype(np.float64)
+    E = tiny.cfg.n_experts
+    for t in range(tiny_x.shape[0]):
+        ds, _ = oracle.expert_ffn(tiny.cfg.hidden, tiny.cfg.inter, *tiny.expert_arrays(E), xf[t])
+        np.testing.assert_allclose(out2["y"][t] - ds, 2 * (base["y"][t] - ds), rtol=1e-12, atol=1e-12)
+
+
+def test_permuting_experts_within_a_group_maps_ids(tiny, tiny_x):
+    import dataclasses
+    cfg = tiny.cfg
+    gsz = cfg.n_experts // cfg.n_groups
+    perm = np.arange(cfg.n_experts)
+    rng = np.random.default_rng(9)
+    for g in range(cfg.n_groups):
+        perm[g * gsz:(g + 1) * gsz] = rng.permutation(np.arange(g * gsz, (g + 1) * gsz))
+    full = np.concatenate([perm, np.arange(cfg.n_experts, cfg.n_total_experts)])
+    wp = dataclasses.replace(
+        tiny, router_w=tiny.router_w[perm].copy(), bias=tiny.bias[perm].copy(),
+        gate_q=tiny.gate_q[full].copy(), gate_s=tiny.gate_s[full].copy(), up_q=tiny.up_q[full].copy(),
+        up_s=tiny.up_s[full].copy(), down_q=tiny.down_q[full].copy(), down_s=tiny.down_s[full].copy())
+    a = oracle.layer_forward(tiny, tiny_x)
+    b = oracle.layer_forward(wp, tiny_x)
+    inv = np.argsort(perm)
+    np.testing.assert_array_equal(inv[a["ids"]], b["ids"])
+    np.testing.assert_array_equal(a["y"], b["y"])
+
+
+def test_tokens_are_independent(tiny):
+    x = synth.gen_tokens(tiny.cfg, 6, seed=4)
+    full = oracle.layer_forward(tiny, x)
+    for t in range(6):
+        one = oracle.layer_forward(tiny, x[t:t + 1])
+        np.testing.assert_array_equal(one["y"][0], full["y"][t])
+        np.testing.assert_array_equal(one["ids"][0], full["ids"][t])
+
+
+def test_forced_ids_reweight_over_the_forced_set(tiny, tiny_x):
+    out = oracle.layer_forward(tiny, tiny_x, want_logits=True)
+    forced = np.tile(np.array([[3, 0, 9, 12]], np.int32), (tiny_x.shape[0], 1))
+    f = oracle.layer_forward(tiny, tiny_x, forced_ids=forced)
+    s = 1 / (1 + np.exp(-out["logits"]))
+    ref_w = tiny.cfg.routed_scaling_factor * s[:, [3, 0, 9, 12]] / s[:, [3, 0, 9, 12]].sum(axis=1, keepdims=True)
+    np.testing.assert_allclose(f["w"], ref_w, rtol=1e-13)
+    np.testing.assert_array_equal(f["ids"], forced)
+
+
+def test_router_logits_against_numpy(tiny, tiny_x):
+    out = oracle.layer_forward(tiny, tiny_x, want_logits=True)
+    xf = synth.bf16_bits_to_f32(tiny_x).astype(np.float64)
+    np.testing.assert_allclose(out["logits"], xf @ tiny.router_w.astype(np.float64).T, rtol=1e-12, atol=1e-14)
+
+
+# ----------------------------------------------------------------- P10: bytes vs the pages
+def test_byte_accounting_matches_pages():
+    g = json.load(open(os.path.join(GOLDEN, "byte_accounting.json")))
+    H, I, E, K, L = 6144, 2048, 256, 8, 75
+    n = 3 * H * I  # weights per expert
+
+    def close(key, v):
+        ref = g[key]
+        assert abs(v - ref["value"]) <= ref["rtol"] * ref["value"], (key, v, ref)
+
+    close("int4_codes_per_expert_bytes", n // 2)
+    close("int4_routed_bytes_per_token", K * L * n // 2)
+    close("int4_routed_experts_on_disk_bytes", (L + 1) * E * n // 2)
+    mxfp4 = n * 4.25 / 8
+    close("mxfp4_routed_gib_per_token", K * L * mxfp4 / 2 ** 30)
+    close("mxfp4_gib_per_s_for_5_tok_s", 5 * K * L * mxfp4 / 2 ** 30)
+    close("bf16_active_bytes_per_token", K * L * n * 2)
+    close("bf16_bytes_per_layer", E * n * 2)
+    close("bf16_whole_layer_bytes_per_token", L * E * n * 2)
+    close("int4_all_experts_bytes", L * E * synth.GLM.expert_bytes())
+    assert synth.GLM.expert_bytes() == 21_233_664
+    assert synth.TINY.expert_bytes() == 55_296
+
+
+def test_generator_is_deterministic_and_codes_uniform():
+    a = synth.gen_layer(synth.TINY, seed=0)
+    b = synth.gen_layer(synth.TINY, seed=0)
+    np.testing.assert_array_equal(a.gate_q, b.gate_q)
+    np.testing.assert_array_equal(a.router_w, b.router_w)
+    nib = np.concatenate([(a.gate_q & 15).ravel(), (a.gate_q >> 4).ravel()])
+    counts = np.bincount(nib, minlength=16)
+    assert counts.min() > 0.8 * counts.mean()

@@ -1,0 +1,204 @@
+/*
+ * moe.h - C ABI of the routed int4 Mixture-of-Experts layer for MI355X (gfx950).
+ *
+ * The layer is the one the pages are about: a GLM-5.2-shaped MoE block with
+ * 256 routed experts per layer of which a router keeps 8 per token, plus one
+ * always-on shared expert, with int4 expert weights (colibri summary on
+ * fr.news.hada.io topic 31297, sections "Execution d'un MoE basee sur le
+ * streaming disque" and "Principales fonctionnalites"; LightLX README,
+ * "How it works").  Per token it computes
+ *
+ *   s_e   = sigmoid(x . W_r[e])                    router affinity
+ *   sb_e  = s_e + bias_e                           biased score, selection only
+ *   groups of E/G contiguous experts are scored by the sum of their two
+ *   largest sb; the topk_group best groups stay eligible; the top_k eligible
+ *   experts by sb are chosen (ties to the lower index), in sb-descending order
+ *   w_j   = routed_scaling_factor * s_j / sum_chosen s
+ *   d_e   = W_d,e (silu(W_g,e x) * (W_u,e x))      SwiGLU expert, no biases
+ *   y     = sum_j w_j d_{e_j} + sum_shared d_s
+ *
+ * This is the DeepSeek-V3 "noaux_tc" sigmoid router with
+ * routed_scaling_factor and a shared expert that colibri and LightLX name
+ * (colibri summary, "Principales fonctionnalites"; LightLX README, "How it
+ * works"), and mlx-lm's SwitchGLU expert (LightLX README, "Run any model").
+ *
+ * Conventions for every entry point:
+ *  - Device pointers ("d_" prefix) are owned by the caller; the library never
+ *    frees them and never allocates device memory, except the per-layer copy
+ *    of the expert pointer table, which lives in the caller's workspace.
+ *  - "stream" is a hipStream_t passed as void* (NULL = the null stream).  All
+ *    GPU work is enqueued on it; calls return before the work completes
+ *    unless stated otherwise.  Device faults surface at the caller's next
+ *    synchronisation of that stream.
+ *  - Return value: MOE_OK (0) or a negative moe_status_t.  On an argument
+ *    error nothing is enqueued.  moe_last_error() describes the last failure
+ *    of the calling host thread.
+ *  - A handle may be used by one host thread at a time.
+ */
+#ifndef MOE_INT4_H
+#define MOE_INT4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_EINVAL = -1,        /* bad argument or shape */
+    MOE_ENOSLOT = -2,       /* expert cache: no slot can be freed right now */
+    MOE_EHIP = -3,          /* a HIP runtime call failed */
+    MOE_EUNSUPPORTED = -4   /* valid, but this build has no kernel for it */
+} moe_status_t;
+
+/* Layer shape.  hidden and inter are multiples of 32 (one fp16 scale per 32
+ * inputs); n_experts is a multiple of n_groups; top_k <= topk_group *
+ * (n_experts / n_groups).  Supported by the kernels in this build:
+ * hidden/32 in {8,16,32,64,128,192,256}, inter/32 in {4,8,16,32,64,128},
+ * hidden % 256 == 0, n_experts <= 256, experts per group >= 2 and a power
+ * of two times ceil(n_experts/64), n_shared in {0,1}, top_k <= 15. */
+typedef struct {
+    int hidden;
+    int inter;
+    int n_experts;
+    int n_groups;
+    int topk_group;
+    int top_k;
+    int n_shared;
+    float routed_scaling_factor;
+} moe_config_t;
+
+typedef struct moe_layer moe_layer_t;
+typedef struct moe_cache moe_cache_t;
+
+/* Last error message of the calling thread ("" if none). */
+const char* moe_last_error(void);
+
+/* ------------------------------------------------------------ expert weights
+ * Public layout of one expert (row-major, little-endian), as on the pages'
+ * int4 format with one fp16 scale per 32 inputs (colibri summary,
+ * "Principales fonctionnalites": packed int4 with dequant-on-use):
+ *   gate_q uint8 [inter][hidden/2]   two int4 codes per byte, two's
+ *                                    complement, even column in the low nibble
+ *   gate_s fp16  [inter][hidden/32]  scale of 32 consecutive input columns
+ *   up_q, up_s                       as gate
+ *   down_q uint8 [hidden][inter/2], down_s fp16 [hidden][inter/32]
+ * Weight value = fp32(scale) * code.
+ *
+ * moe_expert_bytes: size of one packed device blob (equal to the public
+ * layout's size: 3*hidden*inter/2 + 3*hidden*inter/16 bytes; 21,233,664 for
+ * hidden 6144, inter 2048).  Returns 0 for an invalid config.
+ *
+ * moe_expert_pack: host-only repack of one expert from the public layout
+ * (host pointers) into the blob format the kernels read (host buffer of
+ * moe_expert_bytes bytes).  The caller copies the blob to device memory or
+ * keeps it in pinned host memory for the expert cache. */
+size_t moe_expert_bytes(const moe_config_t* cfg);
+moe_status_t moe_expert_pack(const moe_config_t* cfg, const uint8_t* gate_q, const uint16_t* gate_s,
+                             const uint8_t* up_q, const uint16_t* up_s, const uint8_t* down_q,
+                             const uint16_t* down_s, void* dst_blob);
+
+/* ------------------------------------------------------------ layer
+ * moe_layer_create: d_router_w fp32 [n_experts][hidden], d_bias fp32
+ * [n_experts] (the correction bias), d_shared_blobs: host array of n_shared
+ * device pointers to packed shared-expert blobs.  The pointers are kept, not
+ * copied: the buffers must outlive the layer.
+ *
+ * moe_workspace_bytes: device workspace needed for calls with up to max_T
+ * tokens.  moe_layer_set_workspace: binds a caller-owned device buffer (256-
+ * byte aligned), clears its control words with a synchronous memset and
+ * stores the layer's expert table in it.  In all-resident mode each layer
+ * needs its own workspace; layers attached to an expert cache may share one
+ * when their calls are ordered on one stream.  A workspace must be bound
+ * before moe_layer_set_experts.
+ *
+ * moe_layer_set_experts: all-resident mode.  d_blobs is a host array of
+ * n_experts device pointers to packed expert blobs; the table is copied into
+ * the workspace (synchronously).  A layer with an attached cache must not use
+ * this call. */
+size_t moe_workspace_bytes(const moe_config_t* cfg, int max_T);
+moe_status_t moe_layer_create(const moe_config_t* cfg, const float* d_router_w, const float* d_bias,
+                              const void* const* d_shared_blobs, moe_layer_t** out);
+moe_status_t moe_layer_set_workspace(moe_layer_t* layer, void* d_ws, size_t bytes, int max_T);
+moe_status_t moe_layer_set_experts(moe_layer_t* layer, const void* const* d_blobs);
+void moe_layer_destroy(moe_layer_t* layer);
+
+/* moe_router_topk: router and group-limited top-k for T tokens.
+ * d_x bf16 bits [T][hidden]; writes d_ids int32 [T][top_k] (sb descending,
+ * ties to the lower index) and d_w fp32 [T][top_k].  T = 0 is a no-op.
+ * T must not exceed the workspace's max_T. */
+moe_status_t moe_router_topk(moe_layer_t* layer, const uint16_t* d_x, int T, int32_t* d_ids, float* d_w,
+                             void* stream);
+
+/* moe_layer_forward: the whole layer for T tokens.  d_x bf16 bits
+ * [T][hidden]; d_y fp32 [T][hidden] (the block output without residual);
+ * d_ids / d_w may be NULL, else receive the routing as in moe_router_topk.
+ * With all experts resident the call is asynchronous.  With an attached
+ * expert cache it blocks the host once per call until the routing of the
+ * call is known, issues the copies of missing experts on the cache's copy
+ * stream and orders the expert kernels after them with events. */
+moe_status_t moe_layer_forward(moe_layer_t* layer, const uint16_t* d_x, int T, float* d_y, int32_t* d_ids,
+                               float* d_w, void* stream);
+
+/* moe_layer_profile: when enable != 0, moe_layer_forward records HIP events
+ * around each of its kernel launches (on the call's stream) until profiling
+ * is disabled.  moe_layer_profile_read synchronises on the recorded events
+ * and returns, per kernel kind (0 router + shared expert gate/up, 1 routed
+ * gate/up, 2 down + combine), the summed duration in milliseconds and the
+ * number of launches since profiling was enabled; arrays of 3 entries.
+ * Profiling adds events between kernels; timings taken with it enabled are
+ * per-kernel durations, not end-to-end throughput. */
+moe_status_t moe_layer_profile(moe_layer_t* layer, int enable);
+moe_status_t moe_layer_profile_read(moe_layer_t* layer, double* total_ms, uint64_t* launches);
+
+/* ------------------------------------------------------------ expert cache
+ * An HBM cache of packed routed experts in front of a pinned host store,
+ * with one LRU per layer over a fixed set of slots (the per-layer LRU cache
+ * of colibri: fr.news.hada.io topic 31297, "Execution d'un MoE basee sur le
+ * streaming disque"; routed expert slots of LargerLM, "What It Proves").
+ *
+ * expert_cache_create: n_layers layers with slots_per_layer slots each,
+ * carved from the caller's device buffer d_slot_pool of pool_bytes (at least
+ * n_layers * slots_per_layer * moe_expert_bytes).  copy_stream (hipStream_t
+ * as void*) carries the host-to-device copies; the cache records its own
+ * events.  expert_cache_register: host blob of one routed expert, in pinned
+ * host memory the caller keeps alive until destroy.  expert_cache_prefetch:
+ * asynchronous copies of the listed experts into slots (no-op for resident
+ * ones; MOE_ENOSLOT if every slot of the layer is held by work that has not
+ * completed).  expert_cache_evict: frees the expert's slot once its last use
+ * has completed (no-op MOE_OK if not resident).  expert_cache_stats: counters
+ * of one layer.  moe_layer_attach_cache: routes the layer's routed experts
+ * through the cache as layer layer_id. */
+typedef struct {
+    uint64_t hits;
+    uint64_t misses;
+    uint64_t h2d_bytes;
+    uint64_t evictions;
+    uint64_t prefetches;
+} moe_cache_stats_t;
+
+moe_status_t expert_cache_create(const moe_config_t* cfg, int n_layers, int slots_per_layer, void* d_slot_pool,
+                                 size_t pool_bytes, void* copy_stream, moe_cache_t** out);
+moe_status_t expert_cache_register(moe_cache_t* cache, int layer, int expert, const void* h_pinned_blob,
+                                   size_t bytes);
+moe_status_t expert_cache_prefetch(moe_cache_t* cache, int layer, const int32_t* h_experts, int n);
+moe_status_t expert_cache_evict(moe_cache_t* cache, int layer, int expert);
+moe_status_t expert_cache_stats(const moe_cache_t* cache, int layer, moe_cache_stats_t* out);
+void expert_cache_destroy(moe_cache_t* cache);
+moe_status_t moe_layer_attach_cache(moe_layer_t* layer, moe_cache_t* cache, int layer_id);
+
+/* expert_cache_replay: host-only replay of the cache's slot policy (per-layer
+ * LRU; a miss takes a free slot, else the least recently used slot not needed
+ * by the same token) on a routing trace [n_tokens][top_k] of one layer, with
+ * no GPU work.  Writes the hit, miss and eviction counts the cache would
+ * record for the same trace from a cold start. */
+moe_status_t expert_cache_replay(int n_experts, int slots, int top_k, const int32_t* trace, int n_tokens,
+                                 uint64_t* hits, uint64_t* misses, uint64_t* evictions);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_INT4_H */

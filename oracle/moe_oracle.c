@@ -288,3 +288,35 @@ int oracle_max_threads(void) {
     return 1;
 #endif
 }
+
+/* Router and selection only, for T tokens (no expert math): ids [T][top_k],
+ * w [T][top_k], gap [T].  Same steps as oracle_layer_forward. */
+int oracle_route(int hidden, int n_experts, int n_groups, int topk_group, int top_k, double rsf,
+                 const float* router_w, const float* bias, const uint16_t* x_bf16, int T,
+                 int32_t* ids, double* w, double* gap, int n_threads) {
+    int status = 0;
+#ifdef _OPENMP
+    if (n_threads > 0) omp_set_num_threads(n_threads);
+#pragma omp parallel for schedule(dynamic, 4)
+#endif
+    for (int t = 0; t < T; ++t) {
+        double* x = (double*)malloc(sizeof(double) * (size_t)hidden);
+        double* lg = (double*)malloc(sizeof(double) * (size_t)n_experts);
+        double* s = (double*)malloc(sizeof(double) * (size_t)n_experts);
+        double* sb = (double*)malloc(sizeof(double) * (size_t)n_experts);
+        for (int c = 0; c < hidden; ++c) x[c] = bf16_to_double(x_bf16[(size_t)t * hidden + c]);
+        oracle_router_scores(hidden, n_experts, router_w, bias, x, lg, s, sb);
+        if (oracle_select(n_experts, n_groups, topk_group, top_k, rsf, s, sb, ids + (size_t)t * top_k,
+                          w + (size_t)t * top_k, gap + t) != 0) {
+#ifdef _OPENMP
+#pragma omp atomic write
+#endif
+            status = -1;
+        }
+        free(x);
+        free(lg);
+        free(s);
+        free(sb);
+    }
+    return status;
+}

@@ -48,6 +48,9 @@ def lib():
             + [_vp, ctypes.c_int, _vp, _d, _i32, _d, _d, _vp, ctypes.c_int]
         )
         L.oracle_layer_forward.restype = ctypes.c_int
+        L.oracle_route.argtypes = [ctypes.c_int] * 5 + [ctypes.c_double, _vp, _vp, _vp, ctypes.c_int, _i32, _d, _d,
+                                                         ctypes.c_int]
+        L.oracle_route.restype = ctypes.c_int
         L.oracle_max_threads.argtypes = []
         L.oracle_max_threads.restype = ctypes.c_int
         _lib = L
@@ -137,3 +140,20 @@ def layer_forward(weights, x_bf16: np.ndarray, forced_ids=None, n_threads: int =
     if rc != 0:
         raise ValueError("oracle_layer_forward: bad arguments")
     return {"y": y, "ids": ids, "w": w, "gap": gap, "logits": logits}
+
+
+def route(weights, x_bf16: np.ndarray, n_threads: int = 0):
+    """Router + selection for tokens x_bf16 [T, H] -> (ids [T,k], w [T,k], gap [T])."""
+    cfg = weights.cfg
+    x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
+    T = x.shape[0]
+    ids = np.empty((T, cfg.top_k), np.int32)
+    w = np.empty((T, cfg.top_k), np.float64)
+    gap = np.empty(T, np.float64)
+    rc = lib().oracle_route(
+        cfg.hidden, cfg.n_experts, cfg.n_groups, cfg.topk_group, cfg.top_k, float(cfg.routed_scaling_factor),
+        _ptr(weights.router_w), _ptr(weights.bias), _ptr(x), T, ids.ctypes.data_as(_i32), _dptr(w), _dptr(gap),
+        int(n_threads))
+    if rc != 0:
+        raise ValueError("oracle_route: bad arguments")
+    return ids, w, gap

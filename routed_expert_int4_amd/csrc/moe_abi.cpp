@@ -1,0 +1,373 @@
+// Host side of the C ABI declared in include/moe.h: argument validation,
+// expert packing, workspace carving and kernel dispatch.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/moe.h"
+#include "moe_cache.h"
+#include "moe_internal.h"
+#include "moe_kernels.h"
+#include "moe_layout.h"
+
+namespace moe {
+
+static thread_local std::string g_last_error;
+
+moe_status_t fail(moe_status_t code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return code;
+}
+
+moe_status_t hip_fail(hipError_t e, const char* what) {
+    return fail(MOE_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+moe_status_t validate_config(const moe_config_t* c) {
+    if (!c) return fail(MOE_EINVAL, "config is NULL");
+    if (c->hidden <= 0 || c->inter <= 0 || c->hidden % 32 || c->inter % 32)
+        return fail(MOE_EINVAL, "hidden (%d) and inter (%d) must be positive multiples of 32", c->hidden, c->inter);
+    if (c->n_experts <= 0 || c->n_groups <= 0 || c->n_experts % c->n_groups)
+        return fail(MOE_EINVAL, "n_experts (%d) must be a positive multiple of n_groups (%d)", c->n_experts,
+                    c->n_groups);
+    const int gsize = c->n_experts / c->n_groups;
+    if (gsize < 2) return fail(MOE_EINVAL, "groups need at least two experts (group size %d)", gsize);
+    if (c->topk_group < 1 || c->topk_group > c->n_groups)
+        return fail(MOE_EINVAL, "topk_group (%d) must be in [1, n_groups=%d]", c->topk_group, c->n_groups);
+    if (c->top_k < 1 || c->top_k > c->topk_group * gsize)
+        return fail(MOE_EINVAL, "top_k (%d) must be in [1, topk_group * group size = %d]", c->top_k,
+                    c->topk_group * gsize);
+    if (c->n_shared < 0) return fail(MOE_EINVAL, "n_shared must be >= 0");
+    if (!(c->routed_scaling_factor == c->routed_scaling_factor))
+        return fail(MOE_EINVAL, "routed_scaling_factor is NaN");
+    return MOE_OK;
+}
+
+moe_status_t validate_supported(const moe_config_t* c) {
+    moe_status_t st = validate_config(c);
+    if (st != MOE_OK) return st;
+    if (!decode_shape_supported(c->hidden, c->inter) || c->hidden % 256)
+        return fail(MOE_EUNSUPPORTED, "no kernel for hidden=%d inter=%d", c->hidden, c->inter);
+    if (c->n_experts > 256) return fail(MOE_EUNSUPPORTED, "n_experts > 256");
+    const int epl = c->n_experts <= 64 ? 1 : (c->n_experts <= 128 ? 2 : 4);
+    const int gsize = c->n_experts / c->n_groups;
+    const int lpg = gsize / epl;
+    if (gsize % epl || lpg < 1 || (lpg & (lpg - 1)) || lpg > 64)
+        return fail(MOE_EUNSUPPORTED, "group size %d does not map onto lanes", gsize);
+    if (c->n_shared > 1) return fail(MOE_EUNSUPPORTED, "at most one shared expert");
+    if (c->top_k > 15) return fail(MOE_EUNSUPPORTED, "top_k > 15");
+    return MOE_OK;
+}
+
+static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+WorkspaceLayout workspace_layout(const moe_config_t* c, int max_T) {
+    WorkspaceLayout W;
+    size_t o = 0;
+    const int slots = c->top_k + c->n_shared;
+    W.table = o;
+    o = align256(o + sizeof(void*) * (size_t)c->n_experts);
+    W.control = o;
+    o = align256(o + 256);
+    W.control_bytes = 256;
+    W.logits = o;
+    o = align256(o + sizeof(float) * (size_t)max_T * c->n_experts);
+    W.ids = o;
+    o = align256(o + sizeof(int32_t) * (size_t)max_T * c->top_k);
+    W.w = o;
+    o = align256(o + sizeof(float) * (size_t)max_T * c->top_k);
+    W.h = o;
+    o = align256(o + sizeof(float) * (size_t)slots * c->inter);
+    W.total = o;
+    return W;
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+const char* moe_last_error(void) { return g_last_error.c_str(); }
+
+size_t moe_expert_bytes(const moe_config_t* cfg) {
+    if (validate_config(cfg) != MOE_OK) return 0;
+    return blob_layout(cfg->hidden, cfg->inter).total;
+}
+
+moe_status_t moe_expert_pack(const moe_config_t* cfg, const uint8_t* gate_q, const uint16_t* gate_s,
+                             const uint8_t* up_q, const uint16_t* up_s, const uint8_t* down_q,
+                             const uint16_t* down_s, void* dst_blob) {
+    moe_status_t st = validate_config(cfg);
+    if (st != MOE_OK) return st;
+    if (!gate_q || !gate_s || !up_q || !up_s || !down_q || !down_s || !dst_blob)
+        return fail(MOE_EINVAL, "moe_expert_pack: NULL pointer");
+    const int H = cfg->hidden, I = cfg->inter;
+    const BlobLayout L = blob_layout(H, I);
+    uint8_t* dst = static_cast<uint8_t*>(dst_blob);
+    const size_t codes = (size_t)H * I / 2;
+    // codes: stored as q + 8 (flip bit 3 of every two's complement nibble)
+    const uint8_t* src_q[3] = {gate_q, up_q, down_q};
+    const size_t dst_q[3] = {L.gate_q, L.up_q, L.down_q};
+    for (int m = 0; m < 3; ++m)
+        for (size_t i = 0; i < codes; ++i) dst[dst_q[m] + i] = src_q[m][i] ^ 0x88u;
+    // scales: permuted into the per-lane packs the kernels read
+    auto pack_scales = [&](const uint16_t* src, size_t off, int rows, int kg, int p) {
+        uint16_t* d = reinterpret_cast<uint16_t*>(dst + off);
+        for (int r = 0; r < rows; ++r)
+            for (int g = 0; g < kg; ++g) d[scale_index(r, g, kg, p)] = src[(size_t)r * kg + g];
+    };
+    const int kh = H / 32, ki = I / 32;
+    if (I % gateup_rows(kh) || H % down_rows(ki))
+        return fail(MOE_EUNSUPPORTED, "moe_expert_pack: rows not a multiple of the scale pack");
+    pack_scales(gate_s, L.gate_s, I, kh, gateup_rows(kh));
+    pack_scales(up_s, L.up_s, I, kh, gateup_rows(kh));
+    pack_scales(down_s, L.down_s, H, ki, down_rows(ki));
+    return MOE_OK;
+}
+
+size_t moe_workspace_bytes(const moe_config_t* cfg, int max_T) {
+    if (validate_config(cfg) != MOE_OK || max_T < 1) return 0;
+    return workspace_layout(cfg, max_T).total;
+}
+
+moe_status_t moe_layer_create(const moe_config_t* cfg, const float* d_router_w, const float* d_bias,
+                              const void* const* d_shared_blobs, moe_layer_t** out) {
+    if (!out) return fail(MOE_EINVAL, "moe_layer_create: out is NULL");
+    *out = nullptr;
+    moe_status_t st = validate_supported(cfg);
+    if (st != MOE_OK) return st;
+    if (!d_router_w || !d_bias) return fail(MOE_EINVAL, "moe_layer_create: NULL router weight or bias");
+    if (cfg->n_shared > 0 && !d_shared_blobs) return fail(MOE_EINVAL, "moe_layer_create: NULL shared blobs");
+    moe_layer* L = new (std::nothrow) moe_layer();
+    if (!L) return fail(MOE_EINVAL, "moe_layer_create: out of host memory");
+    L->cfg = *cfg;
+    L->router_w = d_router_w;
+    L->bias = d_bias;
+    for (int s = 0; s < cfg->n_shared; ++s) {
+        if (!d_shared_blobs[s]) {
+            delete L;
+            return fail(MOE_EINVAL, "moe_layer_create: shared blob %d is NULL", s);
+        }
+        L->shared.push_back(static_cast<const uint8_t*>(d_shared_blobs[s]));
+    }
+    L->host_table.assign((size_t)cfg->n_experts, nullptr);
+    *out = L;
+    return MOE_OK;
+}
+
+moe_status_t moe_layer_set_workspace(moe_layer_t* layer, void* d_ws, size_t bytes, int max_T) {
+    if (!layer || !d_ws) return fail(MOE_EINVAL, "moe_layer_set_workspace: NULL argument");
+    if (max_T < 1) return fail(MOE_EINVAL, "moe_layer_set_workspace: max_T must be >= 1");
+    if (reinterpret_cast<uintptr_t>(d_ws) % 256) return fail(MOE_EINVAL, "workspace must be 256-byte aligned");
+    const WorkspaceLayout W = workspace_layout(&layer->cfg, max_T);
+    if (bytes < W.total)
+        return fail(MOE_EINVAL, "workspace too small: %zu bytes given, %zu needed for max_T=%d", bytes, W.total,
+                    max_T);
+    hipError_t e = hipMemset(static_cast<uint8_t*>(d_ws) + W.control, 0, W.control_bytes);
+    if (e != hipSuccess) return hip_fail(e, "hipMemset(workspace control)");
+    layer->ws = static_cast<uint8_t*>(d_ws);
+    layer->ws_bytes = bytes;
+    layer->max_T = max_T;
+    layer->W = W;
+    if (layer->experts_set) {
+        e = hipMemcpy(layer->ws + W.table, layer->host_table.data(), sizeof(void*) * layer->host_table.size(),
+                      hipMemcpyHostToDevice);
+        if (e != hipSuccess) return hip_fail(e, "hipMemcpy(expert table)");
+    }
+    return MOE_OK;
+}
+
+moe_status_t moe_layer_set_experts(moe_layer_t* layer, const void* const* d_blobs) {
+    if (!layer || !d_blobs) return fail(MOE_EINVAL, "moe_layer_set_experts: NULL argument");
+    if (!layer->ws) return fail(MOE_EINVAL, "moe_layer_set_experts: bind a workspace first");
+    if (layer->cache) return fail(MOE_EINVAL, "moe_layer_set_experts: layer uses an expert cache");
+    for (int e = 0; e < layer->cfg.n_experts; ++e) {
+        if (!d_blobs[e]) return fail(MOE_EINVAL, "moe_layer_set_experts: blob %d is NULL", e);
+        layer->host_table[e] = static_cast<const uint8_t*>(d_blobs[e]);
+    }
+    hipError_t e = hipMemcpy(layer->ws + layer->W.table, layer->host_table.data(),
+                             sizeof(void*) * layer->host_table.size(), hipMemcpyHostToDevice);
+    if (e != hipSuccess) return hip_fail(e, "hipMemcpy(expert table)");
+    layer->experts_set = true;
+    return MOE_OK;
+}
+
+void moe_layer_destroy(moe_layer_t* layer) {
+    if (!layer) return;
+    for (hipEvent_t e : layer->prof_events) (void)hipEventDestroy(e);
+    delete layer;
+}
+
+moe_status_t moe_layer_profile(moe_layer_t* layer, int enable) {
+    if (!layer) return fail(MOE_EINVAL, "moe_layer_profile: layer is NULL");
+    layer->profiling = enable != 0;
+    layer->prof_marks.clear();
+    layer->prof_used = 0;
+    return MOE_OK;
+}
+
+moe_status_t moe_layer_profile_read(moe_layer_t* layer, double* total_ms, uint64_t* launches) {
+    if (!layer || !total_ms || !launches) return fail(MOE_EINVAL, "moe_layer_profile_read: NULL argument");
+    for (int k = 0; k < 3; ++k) {
+        total_ms[k] = 0.0;
+        launches[k] = 0;
+    }
+    for (const auto& m : layer->prof_marks) {
+        hipEvent_t a = layer->prof_events[m.second], b = layer->prof_events[m.second + 1];
+        hipError_t e = hipEventSynchronize(b);
+        float ms = 0.0f;
+        if (e == hipSuccess) e = hipEventElapsedTime(&ms, a, b);
+        if (e != hipSuccess) return hip_fail(e, "moe_layer_profile_read");
+        total_ms[m.first] += ms;
+        launches[m.first] += 1;
+    }
+    return MOE_OK;
+}
+
+}  // extern "C"
+
+namespace moe {
+
+DecodeArgs decode_args(moe_layer_t* L, const uint16_t* x, int32_t* ids, float* w, float* y) {
+    DecodeArgs a;
+    const moe_config_t& c = L->cfg;
+    a.x = x;
+    a.router_w = L->router_w;
+    a.bias = L->bias;
+    a.table = reinterpret_cast<const uint8_t* const*>(L->ws + L->W.table);
+    a.shared_blob = c.n_shared > 0 ? L->shared[0] : nullptr;
+    a.logits = reinterpret_cast<float*>(L->ws + L->W.logits);
+    a.ticket = reinterpret_cast<unsigned*>(L->ws + L->W.control);
+    a.ids = ids;
+    a.w = w;
+    a.h = reinterpret_cast<float*>(L->ws + L->W.h);
+    a.y = y;
+    a.H = c.hidden;
+    a.I = c.inter;
+    a.E = c.n_experts;
+    a.G = c.n_groups;
+    a.TG = c.topk_group;
+    a.K = c.top_k;
+    a.S = c.n_shared;
+    a.rsf = c.routed_scaling_factor;
+    a.direct = 0;
+    a.n_slot_list = 0;
+    for (int j = 0; j < 16; ++j) {
+        a.blobs[j] = nullptr;
+        a.slot_list[j] = 0;
+    }
+    return a;
+}
+
+// Records a start and an end event around a launch when profiling is on.
+// Events come from a pool that grows on demand and is reused after
+// moe_layer_profile resets the marks.
+class ProfileScope {
+public:
+    ProfileScope(moe_layer* L, int kind, hipStream_t s) : L_(L), s_(s) {
+        if (!L_->profiling) return;
+        while (L_->prof_events.size() < L_->prof_used + 2) {
+            hipEvent_t ev;
+            if (hipEventCreate(&ev) != hipSuccess) return;
+            L_->prof_events.push_back(ev);
+        }
+        idx_ = (int)L_->prof_used;
+        L_->prof_used += 2;
+        (void)hipEventRecord(L_->prof_events[idx_], s_);
+        L_->prof_marks.emplace_back(kind, idx_);
+    }
+    void end() {
+        if (idx_ >= 0) (void)hipEventRecord(L_->prof_events[idx_ + 1], s_);
+        idx_ = -1;
+    }
+    ~ProfileScope() { end(); }
+
+private:
+    moe_layer* L_;
+    hipStream_t s_;
+    int idx_ = -1;
+};
+
+static moe_status_t check_call(moe_layer_t* L, const uint16_t* d_x, int T, const char* who) {
+    if (!L) return fail(MOE_EINVAL, "%s: layer is NULL", who);
+    if (T < 0) return fail(MOE_EINVAL, "%s: T < 0", who);
+    if (!L->ws) return fail(MOE_EINVAL, "%s: no workspace bound", who);
+    if (T > L->max_T) return fail(MOE_EINVAL, "%s: T=%d exceeds the workspace's max_T=%d", who, T, L->max_T);
+    if (T > 0 && !d_x) return fail(MOE_EINVAL, "%s: x is NULL", who);
+    return MOE_OK;
+}
+
+}  // namespace moe
+
+extern "C" {
+
+moe_status_t moe_router_topk(moe_layer_t* layer, const uint16_t* d_x, int T, int32_t* d_ids, float* d_w,
+                             void* stream) {
+    moe_status_t st = check_call(layer, d_x, T, "moe_router_topk");
+    if (st != MOE_OK) return st;
+    if (T > 0 && (!d_ids || !d_w)) return fail(MOE_EINVAL, "moe_router_topk: NULL ids or w");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const moe_config_t& c = layer->cfg;
+    for (int t = 0; t < T; ++t) {
+        DecodeArgs a = decode_args(layer, d_x + (size_t)t * c.hidden, d_ids + (size_t)t * c.top_k,
+                                   d_w + (size_t)t * c.top_k, nullptr);
+        a.S = 0;  // router only: no shared-expert blocks
+        hipError_t e = decode_router_and_shared(a, s);
+        if (e != hipSuccess) return hip_fail(e, "router kernel launch");
+    }
+    return MOE_OK;
+}
+
+moe_status_t moe_layer_forward(moe_layer_t* layer, const uint16_t* d_x, int T, float* d_y, int32_t* d_ids,
+                               float* d_w, void* stream) {
+    moe_status_t st = check_call(layer, d_x, T, "moe_layer_forward");
+    if (st != MOE_OK) return st;
+    if (T > 0 && !d_y) return fail(MOE_EINVAL, "moe_layer_forward: y is NULL");
+    if (!layer->cache && !layer->experts_set)
+        return fail(MOE_EINVAL, "moe_layer_forward: no experts set and no cache attached");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const moe_config_t& c = layer->cfg;
+    int32_t* ids_base = d_ids ? d_ids : reinterpret_cast<int32_t*>(layer->ws + layer->W.ids);
+    float* w_base = d_w ? d_w : reinterpret_cast<float*>(layer->ws + layer->W.w);
+    for (int t = 0; t < T; ++t) {
+        DecodeArgs a = decode_args(layer, d_x + (size_t)t * c.hidden, ids_base + (size_t)t * c.top_k,
+                                   w_base + (size_t)t * c.top_k, d_y + (size_t)t * c.hidden);
+        ProfileScope p0(layer, 0, s);
+        hipError_t e = decode_router_and_shared(a, s);
+        if (e != hipSuccess) return hip_fail(e, "router/shared kernel launch");
+        p0.end();
+        ProfileScope p1(layer, 1, s);
+        if (layer->cache) {
+            // resolves the routing on the host, copies missing experts and
+            // enqueues the routed gate/up (hits first)
+            st = cache_prepare_token(layer, a, s);
+            if (st != MOE_OK) return st;
+        } else {
+            e = decode_routed_gateup(a, s);
+            if (e != hipSuccess) return hip_fail(e, "gate/up kernel launch");
+        }
+        p1.end();
+        ProfileScope p2(layer, 2, s);
+        e = decode_down_combine(a, s);
+        if (e != hipSuccess) return hip_fail(e, "down/combine kernel launch");
+        p2.end();
+        if (layer->cache) {
+            st = cache_finish_token(layer, s);
+            if (st != MOE_OK) return st;
+        }
+    }
+    return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,51 @@
+// Host-side state of a layer and helpers shared by the ABI translation units.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+#include <utility>
+#include <vector>
+
+#include "../../include/moe.h"
+#include "moe_kernels.h"
+
+namespace moe {
+
+struct WorkspaceLayout {
+    size_t table = 0;          // [E] device blob pointers of the routed experts
+    size_t control = 0;        // tickets (must start at zero)
+    size_t control_bytes = 0;
+    size_t logits = 0;         // [max_T][E]
+    size_t ids = 0;            // [max_T][K] when the caller passes no ids buffer
+    size_t w = 0;              // [max_T][K]
+    size_t h = 0;              // [K + S][I]
+    size_t total = 0;
+};
+
+WorkspaceLayout workspace_layout(const moe_config_t* c, int max_T);
+moe_status_t fail(moe_status_t code, const char* fmt, ...);
+moe_status_t hip_fail(hipError_t e, const char* what);
+moe_status_t validate_config(const moe_config_t* c);
+moe_status_t validate_supported(const moe_config_t* c);
+
+}  // namespace moe
+
+struct moe_layer {
+    moe_config_t cfg{};
+    const float* router_w = nullptr;
+    const float* bias = nullptr;
+    std::vector<const uint8_t*> shared;
+    std::vector<const uint8_t*> host_table;  // mirror of the device table
+    bool experts_set = false;
+    uint8_t* ws = nullptr;
+    size_t ws_bytes = 0;
+    int max_T = 0;
+    moe::WorkspaceLayout W;
+    moe_cache* cache = nullptr;
+    int cache_layer = -1;
+    // per-kernel event timing (moe_layer_profile)
+    bool profiling = false;
+    std::vector<hipEvent_t> prof_events;          // pool
+    std::vector<std::pair<int, int>> prof_marks;  // (kind, index of start event)
+    size_t prof_used = 0;
+};

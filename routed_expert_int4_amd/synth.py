@@ -22,9 +22,10 @@ Value distributions follow the GLM-5.2-shaped layer described on the pages
 random bytes (so both nibbles are independent and uniform over [-8, 7]),
 scales are exp(N(-4, 0.5)) rounded to fp16, the router weight is N(0, 0.02) in
 fp32, the bias N(0, 0.01) in fp32 and the activations N(0, 1) rounded to bf16.
-Draw order for a layer: router weight, bias, then for each expert (routed
-first, shared last) gate codes, gate scales, up codes, up scales, down codes,
-down scales.
+Streams: SeedSequence(seed).spawn(1 + E + S); the first child draws the
+router weight then the bias; child 1 + e draws expert e (routed experts
+first, shared last) in the order gate codes, gate scales, up codes, up
+scales, down codes, down scales.  Activations come from their own seed.
 """
 from __future__ import annotations
 
@@ -89,13 +90,29 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
     return (b.astype(np.uint32) << 16).view(np.float32)
 
 
+def _codes(rng: np.random.Generator, shape) -> np.ndarray:
+    """Uniform random bytes (two independent uniform int4 codes each)."""
+    n = int(np.prod(shape))
+    assert n % 8 == 0
+    return rng.bit_generator.random_raw(n // 8).view(np.uint8).reshape(shape)
+
+
 def _scales(rng: np.random.Generator, shape) -> np.ndarray:
-    return np.exp(rng.normal(-4.0, 0.5, size=shape)).astype(np.float16).view(np.uint16)
+    """exp(N(-4, 0.5)) rounded to fp16 (bits)."""
+    z = rng.standard_normal(size=shape, dtype=np.float32)
+    return np.exp(z * np.float32(0.5) - np.float32(4.0)).astype(np.float16).view(np.uint16)
 
 
-def gen_layer(cfg: LayerConfig, seed: int) -> LayerWeights:
-    rng = np.random.Generator(np.random.PCG64(seed))
+def gen_layer(cfg: LayerConfig, seed: int, workers: int | None = None) -> LayerWeights:
+    """One layer from `seed`.  SeedSequence(seed) spawns one child stream for
+    the router (weight, then bias) and one per expert (routed 0..E-1, then
+    shared), so experts can be drawn in parallel threads."""
+    import concurrent.futures
+    import os
+
     h, i, e_all = cfg.hidden, cfg.inter, cfg.n_total_experts
+    children = np.random.SeedSequence(seed).spawn(1 + e_all)
+    rng = np.random.Generator(np.random.PCG64(children[0]))
     router_w = rng.normal(0.0, 0.02, size=(cfg.n_experts, h)).astype(np.float32)
     bias = rng.normal(0.0, 0.01, size=(cfg.n_experts,)).astype(np.float32)
     gq = np.empty((e_all, i, h // 2), np.uint8)
@@ -104,13 +121,19 @@ def gen_layer(cfg: LayerConfig, seed: int) -> LayerWeights:
     us = np.empty_like(gs)
     dq = np.empty((e_all, h, i // 2), np.uint8)
     ds = np.empty((e_all, h, i // 32), np.uint16)
-    for e in range(e_all):
-        gq[e] = rng.integers(0, 256, size=gq.shape[1:], dtype=np.uint8)
-        gs[e] = _scales(rng, gs.shape[1:])
-        uq[e] = rng.integers(0, 256, size=uq.shape[1:], dtype=np.uint8)
-        us[e] = _scales(rng, us.shape[1:])
-        dq[e] = rng.integers(0, 256, size=dq.shape[1:], dtype=np.uint8)
-        ds[e] = _scales(rng, ds.shape[1:])
+
+    def draw(e):
+        r = np.random.Generator(np.random.PCG64(children[1 + e]))
+        gq[e] = _codes(r, gq.shape[1:])
+        gs[e] = _scales(r, gs.shape[1:])
+        uq[e] = _codes(r, uq.shape[1:])
+        us[e] = _scales(r, us.shape[1:])
+        dq[e] = _codes(r, dq.shape[1:])
+        ds[e] = _scales(r, ds.shape[1:])
+
+    n_workers = workers or min(16, os.cpu_count() or 1)
+    with concurrent.futures.ThreadPoolExecutor(max_workers=n_workers) as ex:
+        list(ex.map(draw, range(e_all)))
     return LayerWeights(cfg, router_w, bias, gq, gs, uq, us, dq, ds)
 
 

@@ -1,0 +1,102 @@
+"""Host-side checks of the C-ABI library (no GPU needed): it loads, exports
+every entry point declared in include/moe.h, validates arguments, packs
+experts, and its cache slot policy matches a plain LRU replay."""
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import lru
+from routed_expert_int4_amd import binding as B
+from routed_expert_int4_amd import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "moe.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w]+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert len(names) >= 18, names
+    L = B.lib()
+    for n in names:
+        assert hasattr(L, n), f"{n} declared in moe.h but not exported"
+
+
+def test_expert_bytes_match_public_layout():
+    assert B.moe_expert_bytes(synth.GLM) == 21_233_664
+    assert B.moe_expert_bytes(synth.TINY) == 55_296
+    assert B.moe_expert_bytes(synth.GLM) == synth.GLM.expert_bytes()
+
+
+def test_invalid_configs_are_rejected():
+    import dataclasses
+    bad = [
+        dataclasses.replace(synth.TINY, hidden=250),
+        dataclasses.replace(synth.TINY, n_groups=3),
+        dataclasses.replace(synth.TINY, topk_group=5),
+        dataclasses.replace(synth.TINY, top_k=9),
+    ]
+    for cfg in bad:
+        assert B.moe_expert_bytes(cfg) == 0
+        with pytest.raises(B.MoeError) as e:
+            B.moe_layer_create(cfg, None, None, [])
+        assert e.value.code == B.MOE_EINVAL
+    with pytest.raises(B.MoeError) as e:
+        B.moe_layer_create(dataclasses.replace(synth.TINY, hidden=96 * 32), None, None, [])
+    assert e.value.code == B.MOE_EUNSUPPORTED
+    with pytest.raises(B.MoeError) as e:
+        B.moe_layer_create(synth.TINY, None, None, [])
+    assert e.value.code == B.MOE_EINVAL and "NULL" in B.last_error()
+
+
+def test_pack_keeps_codes_and_permutes_scales():
+    w = synth.gen_layer(synth.TINY, seed=0)
+    cfg = synth.TINY
+    nb = B.moe_expert_bytes(cfg)
+    blob = np.empty(nb, np.uint8)
+    B.moe_expert_pack(cfg, *w.expert_arrays(3), blob)
+    n = cfg.hidden * cfg.inter // 2
+    gq, gs, uq, us, dq, ds = w.expert_arrays(3)
+    # codes: same bytes with each nibble in offset binary (q + 8)
+    np.testing.assert_array_equal(blob[:n], gq.ravel() ^ 0x88)
+    np.testing.assert_array_equal(blob[n:2 * n], uq.ravel() ^ 0x88)
+    np.testing.assert_array_equal(blob[2 * n:3 * n], dq.ravel() ^ 0x88)
+    # scales: each matrix's scales are a permutation of the public ones
+    sc = blob[3 * n:].view(np.uint16)
+    m = sc.size // 3
+    for part, src in zip((sc[:m], sc[m:2 * m], sc[2 * m:]), (gs, us, ds)):
+        np.testing.assert_array_equal(np.sort(part), np.sort(src.ravel()))
+
+
+def test_pack_rejects_null():
+    code = B.lib().moe_expert_pack(B.MoeConfig.from_cfg(synth.TINY), None, None, None, None, None, None, None)
+    assert code == B.MOE_EINVAL
+
+
+def test_lru_oracle_textbook_pins():
+    # Textbook LRU example: reference string 1 2 3 4 1 2 5 1 2 3 4 5 gives
+    # 10 faults with 3 frames and 8 with 4 frames (one expert per token).
+    ref = [[v] for v in (1, 2, 3, 4, 1, 2, 5, 1, 2, 3, 4, 5)]
+    assert lru.replay(ref, 3)[1] == 10
+    assert lru.replay(ref, 4)[1] == 8
+    # enough slots for every expert: only compulsory misses
+    rng = np.random.default_rng(0)
+    tr = np.array([rng.choice(32, 4, replace=False) for _ in range(100)])
+    h, m, e = lru.replay(tr, 32)
+    assert m == len(np.unique(tr)) and e == 0 and h + m == tr.size
+
+
+@pytest.mark.parametrize("slots,skew", [(8, 0.0), (16, 1.1), (64, 1.1), (64, 0.0)])
+def test_cache_policy_matches_lru_replay(slots, skew):
+    rng = np.random.default_rng(slots)
+    E, k = 256, 8
+    p = 1.0 / np.arange(1, E + 1) ** skew
+    p /= p.sum()
+    trace = np.array([rng.choice(E, k, replace=False, p=p) for _ in range(400)], np.int32)
+    assert B.expert_cache_replay(E, slots, k, trace) == lru.replay(trace, slots)

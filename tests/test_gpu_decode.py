@@ -1,0 +1,199 @@
+"""GPU parity of the decode path (one token per kernel sequence) with the oracle.
+
+Every GPU test calls the library through the C ABI (ctypes binding) and
+compares element by element with the fp64 CPU oracle on the same seeded
+inputs: routed ids bit-exact unless the oracle's selection gap is below 1e-6
+(then the outputs are checked against the oracle forced onto the GPU's ids),
+weights within 1e-6 * rsf, outputs within 2e-3 * max|ref| per token.
+"""
+import dataclasses
+import sys
+
+import numpy as np
+import pytest
+
+from oracle import oracle
+from routed_expert_int4_amd import binding as B
+from routed_expert_int4_amd import synth
+from tests.helpers import check_layer, check_routing
+
+pytestmark = pytest.mark.gpu
+
+# Shapes that exercise every lane mapping of the kernels: rows narrower and
+# wider than a wave load, 1/2/4 experts per router lane, odd top_k.
+MID_A = synth.LayerConfig(hidden=1024, inter=256, n_experts=64, n_groups=8, topk_group=4, top_k=6,
+                          routed_scaling_factor=1.5)
+MID_B = synth.LayerConfig(hidden=4096, inter=1024, n_experts=128, n_groups=4, topk_group=2, top_k=8)
+MID_C = synth.LayerConfig(hidden=8192, inter=4096, n_experts=16, n_groups=4, topk_group=2, top_k=4)
+MID_D = synth.LayerConfig(hidden=512, inter=128, n_experts=256, n_groups=8, topk_group=4, top_k=8)
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def torch_cuda():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    B.lib()  # fails loudly if the HIP library is missing
+    return torch
+
+
+def run_layer(torch, weights, x_bits, max_T=None):
+    from routed_expert_int4_amd.layer import DeviceLayer
+    T = x_bits.shape[0]
+    layer = DeviceLayer(weights, max_T=max_T or max(T, 1))
+    x = DeviceLayer.to_device_bf16(x_bits)
+    y, ids, w = layer.forward(x)
+    torch.cuda.synchronize()
+    return layer, y.cpu().numpy(), ids.cpu().numpy(), w.cpu().numpy()
+
+
+@pytest.mark.parametrize("cfg_name", ["TINY", "MID_A", "MID_B", "MID_C", "MID_D"])
+def test_layer_parity(torch_cuda, cfg_name):
+    cfg = {"TINY": synth.TINY, "MID_A": MID_A, "MID_B": MID_B, "MID_C": MID_C, "MID_D": MID_D}[cfg_name]
+    say(f"[gpu] layer parity {cfg_name} {cfg}")
+    weights = synth.gen_layer(cfg, seed=0)
+    T = 4 if cfg.hidden * cfg.inter > 2 ** 24 else 13
+    x = synth.gen_tokens(cfg, T, seed=1)
+    layer, y, ids, w = run_layer(torch_cuda, weights, x)
+    res = check_layer(weights, x, y, ids, w)
+    say(f"[gpu] {cfg_name}: worst rel err {res['worst_rel']:.3g}, excused {res['excused']}")
+    layer.close()
+
+
+def test_tiny_router_topk_matches_oracle(torch_cuda):
+    say("[gpu] tiny router_topk")
+    weights = synth.gen_layer(synth.TINY, seed=0)
+    x = synth.gen_tokens(synth.TINY, 64, seed=2)
+    from routed_expert_int4_amd.layer import DeviceLayer
+    layer = DeviceLayer(weights, max_T=64)
+    ids, w = layer.router_topk(DeviceLayer.to_device_bf16(x))
+    torch_cuda.cuda.synchronize()
+    ids_ref, w_ref, gap = oracle.route(weights, x)
+    check_routing(synth.TINY, ids.cpu().numpy(), w.cpu().numpy(), ids_ref, w_ref, gap)
+    layer.close()
+
+
+@pytest.mark.parametrize("std", [1e-3, 1.0, 300.0])
+def test_activation_scale_range(torch_cuda, std):
+    """Inputs far from unit scale keep full accuracy (power-of-two range scaling)."""
+    say(f"[gpu] tiny activation std {std}")
+    weights = synth.gen_layer(synth.TINY, seed=0)
+    x = synth.gen_tokens(synth.TINY, 8, seed=3, std=std)
+    layer, y, ids, w = run_layer(torch_cuda, weights, x)
+    check_layer(weights, x, y, ids, w)
+    layer.close()
+
+
+def test_zero_input_gives_shared_only_output(torch_cuda):
+    """x = 0: weights rsf/k exactly, routing on the bias alone, y = 0."""
+    say("[gpu] tiny zero input")
+    weights = synth.gen_layer(synth.TINY, seed=0)
+    x = np.zeros((3, synth.TINY.hidden), np.uint16)
+    layer, y, ids, w = run_layer(torch_cuda, weights, x)
+    ref_ids, _, _ = oracle.route(weights, x)
+    np.testing.assert_array_equal(ids, ref_ids)
+    assert np.all(w == np.float32(synth.TINY.routed_scaling_factor / synth.TINY.top_k))
+    assert np.all(y == 0.0)
+    layer.close()
+
+
+def test_routed_off_gives_shared_expert(torch_cuda):
+    say("[gpu] tiny routed experts zeroed")
+    w0 = synth.gen_layer(synth.TINY, seed=0)
+    E = synth.TINY.n_experts
+    wz = dataclasses.replace(w0, gate_q=w0.gate_q.copy(), up_q=w0.up_q.copy(), down_q=w0.down_q.copy())
+    wz.gate_q[:E] = 0
+    wz.up_q[:E] = 0
+    wz.down_q[:E] = 0
+    x = synth.gen_tokens(synth.TINY, 5, seed=4)
+    layer, y, ids, w = run_layer(torch_cuda, wz, x)
+    check_layer(wz, x, y, ids, w)
+    layer.close()
+
+
+def test_empty_call_and_errors(torch_cuda):
+    say("[gpu] T=0 and argument errors")
+    weights = synth.gen_layer(synth.TINY, seed=0)
+    from routed_expert_int4_amd.layer import DeviceLayer
+    layer = DeviceLayer(weights, max_T=2)
+    x = DeviceLayer.to_device_bf16(synth.gen_tokens(synth.TINY, 3, seed=1))
+    y = torch_cuda.full((3, synth.TINY.hidden), 7.0, device="cuda:0")
+    B.moe_layer_forward(layer.handle, x, 0, y)
+    torch_cuda.cuda.synchronize()
+    assert torch_cuda.all(y == 7.0)
+    with pytest.raises(B.MoeError) as e:
+        B.moe_layer_forward(layer.handle, x, 3, y)  # T above max_T
+    assert e.value.code == B.MOE_EINVAL and "max_T" in B.last_error()
+    with pytest.raises(B.MoeError):
+        B.moe_layer_forward(layer.handle, None, 1, y)
+    layer.close()
+
+
+def test_repeatable_and_batch_independent(torch_cuda):
+    """Two runs are bit-identical; a token's result does not depend on the
+    other tokens of the call."""
+    say("[gpu] determinism / batch independence")
+    weights = synth.gen_layer(MID_A, seed=0)
+    x = synth.gen_tokens(MID_A, 9, seed=5)
+    layer, y1, ids1, w1 = run_layer(torch_cuda, weights, x)
+    from routed_expert_int4_amd.layer import DeviceLayer
+    y2, ids2, w2 = layer.forward(DeviceLayer.to_device_bf16(x))
+    np.testing.assert_array_equal(y1, y2.cpu().numpy())
+    np.testing.assert_array_equal(ids1, ids2.cpu().numpy())
+    for t in (0, 4, 8):
+        y3, _, _ = layer.forward(DeviceLayer.to_device_bf16(x[t:t + 1]))
+        np.testing.assert_array_equal(y1[t], y3.cpu().numpy()[0])
+    layer.close()
+
+
+# ---------------------------------------------------------------- GLM-5.2 shape
+@pytest.fixture(scope="module")
+def glm(torch_cuda):
+    say("[gpu] generating the GLM-shaped layer (seed 0)")
+    weights = synth.gen_layer(synth.GLM, seed=0)
+    from routed_expert_int4_amd.layer import DeviceLayer
+    layer = DeviceLayer(weights, max_T=1000)
+    yield weights, layer
+    layer.close()
+
+
+def test_glm_decode_1000_tokens(torch_cuda, glm):
+    """The benchmark's workload: 1,000 independent tokens at batch 1.  Routing
+    of all 1,000 tokens against the oracle; full outputs on a sample of tokens
+    (the first, the last, a spread, and the smallest-gap ones)."""
+    weights, layer = glm
+    say("[gpu] GLM 1000-token decode")
+    x = synth.gen_tokens(synth.GLM, 1000, seed=1)
+    from routed_expert_int4_amd.layer import DeviceLayer
+    y, ids, w = layer.forward(DeviceLayer.to_device_bf16(x))
+    torch_cuda.cuda.synchronize()
+    y, ids, w = y.cpu().numpy(), ids.cpu().numpy(), w.cpu().numpy()
+    ids_ref, w_ref, gap = oracle.route(weights, x)
+    excused = check_routing(synth.GLM, ids, w, ids_ref, w_ref, gap)
+    say(f"[gpu] GLM routing: {len(excused)} tokens excused by the 1e-6 gap rule, min gap {gap.min():.3g}")
+    np.testing.assert_allclose(w.sum(axis=1), synth.GLM.routed_scaling_factor, rtol=1e-6)
+    rows = sorted(set([0, 1, 137, 500, 998, 999] + list(np.argsort(gap)[:2])))
+    res = check_layer(weights, x, y, ids, w, rows=rows)
+    say(f"[gpu] GLM sampled outputs: worst rel err {res['worst_rel']:.3g}")
+    assert np.all(np.isfinite(y))
+
+
+def test_glm_zero_token_and_repeat(torch_cuda, glm):
+    weights, layer = glm
+    say("[gpu] GLM zero token + repeat")
+    x = synth.gen_tokens(synth.GLM, 3, seed=7)
+    x[1] = 0
+    from routed_expert_int4_amd.layer import DeviceLayer
+    xd = DeviceLayer.to_device_bf16(x)
+    y1, ids1, w1 = layer.forward(xd)
+    y2, ids2, w2 = layer.forward(xd)
+    torch_cuda.cuda.synchronize()
+    assert torch_cuda.equal(y1, y2) and torch_cuda.equal(ids1, ids2)
+    y1 = y1.cpu().numpy()
+    assert np.all(y1[1] == 0.0)
+    assert np.all(w1.cpu().numpy()[1] == np.float32(synth.GLM.routed_scaling_factor / synth.GLM.top_k))
+    check_layer(weights, x, y1, ids1.cpu().numpy(), w1.cpu().numpy(), rows=[0, 2])

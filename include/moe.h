@@ -58,7 +58,7 @@ typedef enum {
  * (n_experts / n_groups).  Supported by the kernels in this build:
  * hidden/32 in {8,16,32,64,128,192,256}, inter/32 in {4,8,16,32,64,128},
  * hidden % 256 == 0, n_experts <= 256, experts per group >= 2 and a power
- * of two times ceil(n_experts/64), n_shared in {0,1}, top_k <= 15. */
+ * of two times ceil(n_experts/64), n_shared in {0,1}, top_k <= 8. */
 typedef struct {
     int hidden;
     int inter;

@@ -56,7 +56,8 @@ moe_status_t validate_config(const moe_config_t* c) {
 moe_status_t validate_supported(const moe_config_t* c) {
     moe_status_t st = validate_config(c);
     if (st != MOE_OK) return st;
-    if (!decode_shape_supported(c->hidden, c->inter) || c->hidden % 256)
+    if (c->top_k > 8) return fail(MOE_EUNSUPPORTED, "top_k must be at most 8 (got %d)", c->top_k);
+    if (!decode_shape_supported(c->hidden, c->inter, c->top_k, c->n_shared))
         return fail(MOE_EUNSUPPORTED, "no kernel for hidden=%d inter=%d", c->hidden, c->inter);
     if (c->n_experts > 256) return fail(MOE_EUNSUPPORTED, "n_experts > 256");
     const int epl = c->n_experts <= 64 ? 1 : (c->n_experts <= 128 ? 2 : 4);
@@ -65,7 +66,6 @@ moe_status_t validate_supported(const moe_config_t* c) {
     if (gsize % epl || lpg < 1 || (lpg & (lpg - 1)) || lpg > 64)
         return fail(MOE_EUNSUPPORTED, "group size %d does not map onto lanes", gsize);
     if (c->n_shared > 1) return fail(MOE_EUNSUPPORTED, "at most one shared expert");
-    if (c->top_k > 15) return fail(MOE_EUNSUPPORTED, "top_k > 15");
     return MOE_OK;
 }
 
@@ -80,8 +80,16 @@ WorkspaceLayout workspace_layout(const moe_config_t* c, int max_T) {
     W.control = o;
     o = align256(o + 256);
     W.control_bytes = 256;
-    W.logits = o;
-    o = align256(o + sizeof(float) * (size_t)max_T * c->n_experts);
+    W.s = o;
+    o = align256(o + sizeof(float) * (size_t)c->n_experts);
+    W.sb = o;
+    o = align256(o + sizeof(float) * (size_t)c->n_experts);
+    W.xpairs = o;
+    o = align256(o + (size_t)chunks_per_lane(c->hidden / 32) * kWave * 16 * sizeof(unsigned));
+    W.kx = o;
+    o = align256(o + sizeof(int));
+    W.slot_blobs = o;
+    o = align256(o + sizeof(void*) * 16);
     W.ids = o;
     o = align256(o + sizeof(int32_t) * (size_t)max_T * c->top_k);
     W.w = o;
@@ -128,11 +136,18 @@ moe_status_t moe_expert_pack(const moe_config_t* cfg, const uint8_t* gate_q, con
             for (int g = 0; g < kg; ++g) d[scale_index(r, g, kg, p)] = src[(size_t)r * kg + g];
     };
     const int kh = H / 32, ki = I / 32;
-    if (I % gateup_rows(kh) || H % down_rows(ki))
+    if (I % gateup_rows(kh) || H % down_rows(H, ki, cfg->top_k))
         return fail(MOE_EUNSUPPORTED, "moe_expert_pack: rows not a multiple of the scale pack");
-    pack_scales(gate_s, L.gate_s, I, kh, gateup_rows(kh));
-    pack_scales(up_s, L.up_s, I, kh, gateup_rows(kh));
-    pack_scales(down_s, L.down_s, H, ki, down_rows(ki));
+    {
+        uint16_t* d = reinterpret_cast<uint16_t*>(dst + L.gu_s);
+        const int p = gateup_rows(kh);
+        for (int r = 0; r < I; ++r)
+            for (int g = 0; g < kh; ++g) {
+                d[gateup_scale_index(r, g, 0, kh, p)] = gate_s[(size_t)r * kh + g];
+                d[gateup_scale_index(r, g, 1, kh, p)] = up_s[(size_t)r * kh + g];
+            }
+    }
+    pack_scales(down_s, L.down_s, H, ki, down_rows(H, ki, cfg->top_k));
     return MOE_OK;
 }
 
@@ -247,8 +262,12 @@ DecodeArgs decode_args(moe_layer_t* L, const uint16_t* x, int32_t* ids, float* w
     a.bias = L->bias;
     a.table = reinterpret_cast<const uint8_t* const*>(L->ws + L->W.table);
     a.shared_blob = c.n_shared > 0 ? L->shared[0] : nullptr;
-    a.logits = reinterpret_cast<float*>(L->ws + L->W.logits);
-    a.ticket = reinterpret_cast<unsigned*>(L->ws + L->W.control);
+    a.s = reinterpret_cast<float*>(L->ws + L->W.s);
+    a.sb = reinterpret_cast<float*>(L->ws + L->W.sb);
+    a.xpairs = reinterpret_cast<unsigned*>(L->ws + L->W.xpairs);
+    a.kx = reinterpret_cast<int*>(L->ws + L->W.kx);
+    a.slot_blobs = reinterpret_cast<const uint8_t**>(L->ws + L->W.slot_blobs);
+    a.with_shared = 1;
     a.ids = ids;
     a.w = w;
     a.h = reinterpret_cast<float*>(L->ws + L->W.h);
@@ -262,6 +281,7 @@ DecodeArgs decode_args(moe_layer_t* L, const uint16_t* x, int32_t* ids, float* w
     a.S = c.n_shared;
     a.rsf = c.routed_scaling_factor;
     a.direct = 0;
+    a.use_slot_list = 0;
     a.n_slot_list = 0;
     for (int j = 0; j < 16; ++j) {
         a.blobs[j] = nullptr;
@@ -322,9 +342,10 @@ moe_status_t moe_router_topk(moe_layer_t* layer, const uint16_t* d_x, int T, int
     for (int t = 0; t < T; ++t) {
         DecodeArgs a = decode_args(layer, d_x + (size_t)t * c.hidden, d_ids + (size_t)t * c.top_k,
                                    d_w + (size_t)t * c.top_k, nullptr);
-        a.S = 0;  // router only: no shared-expert blocks
-        hipError_t e = decode_router_and_shared(a, s);
+        hipError_t e = decode_router(a, s);
         if (e != hipSuccess) return hip_fail(e, "router kernel launch");
+        e = decode_topk(a, s);
+        if (e != hipSuccess) return hip_fail(e, "top-k kernel launch");
     }
     return MOE_OK;
 }
@@ -344,13 +365,16 @@ moe_status_t moe_layer_forward(moe_layer_t* layer, const uint16_t* d_x, int T, f
         DecodeArgs a = decode_args(layer, d_x + (size_t)t * c.hidden, ids_base + (size_t)t * c.top_k,
                                    w_base + (size_t)t * c.top_k, d_y + (size_t)t * c.hidden);
         ProfileScope p0(layer, 0, s);
-        hipError_t e = decode_router_and_shared(a, s);
-        if (e != hipSuccess) return hip_fail(e, "router/shared kernel launch");
+        hipError_t e = decode_router(a, s);
+        if (e != hipSuccess) return hip_fail(e, "router kernel launch");
         p0.end();
         ProfileScope p1(layer, 1, s);
         if (layer->cache) {
-            // resolves the routing on the host, copies missing experts and
-            // enqueues the routed gate/up (hits first)
+            // the host needs the routing: a top-k launch, then the cache
+            // resolves it, copies missing experts and enqueues the routed
+            // gate/up (hits first)
+            e = decode_topk(a, s);
+            if (e != hipSuccess) return hip_fail(e, "top-k kernel launch");
             st = cache_prepare_token(layer, a, s);
             if (st != MOE_OK) return st;
         } else {

@@ -140,10 +140,12 @@ moe_status_t cache_prepare_token(moe_layer* layer, DecodeArgs& a, hipStream_t st
         }
     }
     a.direct = 1;
-    // gate/up of the hit experts first, then of the misses once copied
+    // gate/up of the shared expert and the hit experts first, then of the
+    // misses once copied
     for (int pass = 0; pass < 2; ++pass) {
         const std::vector<int>& js = pass == 0 ? hit_slots : miss_slots;
-        if (js.empty()) continue;
+        a.with_shared = pass == 0 ? 1 : 0;
+        if (js.empty() && !(pass == 0 && a.S > 0)) continue;
         for (int j : js) {
             const int s = slot_of_j[j];
             if (L.copy_recorded[s]) {
@@ -151,12 +153,15 @@ moe_status_t cache_prepare_token(moe_layer* layer, DecodeArgs& a, hipStream_t st
                 if (err != hipSuccess) return hip_fail(err, "expert cache: stream wait");
             }
         }
+        a.use_slot_list = 1;
         a.n_slot_list = (int)js.size();
         for (size_t i = 0; i < js.size(); ++i) a.slot_list[i] = js[i];
         err = decode_routed_gateup(a, st);
         if (err != hipSuccess) return hip_fail(err, "gate/up kernel launch");
     }
+    a.use_slot_list = 0;
     a.n_slot_list = 0;
+    a.with_shared = 1;
     c->pending_slots = slot_of_j;
     c->pending_layer = l;
     return MOE_OK;

@@ -1,14 +1,20 @@
 // Decode (one token per call) kernels of the routed int4 MoE layer, gfx950.
 //
-// Three launches per token, each streaming its weights from HBM once:
-//   1. router_shared: router logits (one fp32 row of W_r per wave) and, in
-//      the same grid, the shared expert's gate/up + SwiGLU (it does not depend
-//      on the routing).  The last router workgroup to finish (atomic ticket)
-//      runs the group-limited top-k on one wave.
-//   2. gateup: gate/up + SwiGLU of the top_k routed experts.
-//   3. down_combine: down projection of every selected expert and of the
-//      shared expert for a block of output rows, and the weighted combine in
-//      a fixed order (no float atomics: repeated calls are bit-identical).
+// Per token:
+//   1. router: router logits, one fp32 row of W_r per wave, turned into
+//      s = sigmoid(logit) and sb = s + bias; the token's activations are
+//      converted once into the fp16 pairs the expert kernels read.
+//   2. gateup: gate/up + SwiGLU of the shared expert (first: it does not
+//      depend on the routing, so its weights stream while each wave derives
+//      the group-limited top-k itself from s and sb with DPP reductions)
+//      and of the routed experts; the next item's loads are in flight while
+//      the current item is computed.  No top-k launch, no grid-wide handoff.
+//   3. down_combine: one wave per routed slot over a block of output rows,
+//      the shared expert's rows of the block split over the same waves,
+//      row loads pipelined; the block is combined in slot order (no float
+//      atomics: repeated calls are bit-identical).
+// A standalone top-k kernel serves the router-only entry point and the
+// expert-cache path, where the host needs the routing before the experts.
 //
 // Int4 GEMV scheme.  A lane owns one 32-input scale group of the reduction
 // dimension (several when a row has more than 64 groups) and keeps the
@@ -41,8 +47,20 @@ __host__ __device__ constexpr int ilog2(int v) { return v <= 1 ? 0 : 1 + ilog2(v
 
 __device__ __forceinline__ f16x2 as_h2(unsigned u) { return __builtin_bit_cast(f16x2, u); }
 
+// Weight and scale pointers reach the kernels through integers (blob
+// tables, lane reads), which loses their address space; casting them to the
+// global address space keeps the loads global_load rather than flat_load.
+// Flat loads count against both the vector-memory and the LDS counters, so
+// the compiler must drain every outstanding load before using any of them,
+// which would serialise the load pipelining below.
+#define MOE_GLOBAL __attribute__((address_space(1)))
+template <typename T>
+__device__ __forceinline__ const MOE_GLOBAL T* as_global(const void* p) {
+    return (const MOE_GLOBAL T*)(p);
+}
+
 __device__ __forceinline__ u32x4 load_stream16(const uint8_t* p) {
-    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return __builtin_nontemporal_load(as_global<u32x4>(p));
 }
 
 __device__ __forceinline__ float half_bits_to_float(unsigned bits16) {
@@ -95,45 +113,105 @@ __device__ __forceinline__ float dot_chunk_hilo(u32x4 c, const f16x2* hp, const 
     return acc;
 }
 
+// DPP lane permutations inside rows of 16 lanes.
+constexpr int kDppXor1 = 0xB1;         // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;         // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;  // lane i <-> 7-i within 8
+constexpr int kDppMirror = 0x140;      // lane i <-> 15-i within 16
+
+template <int CTRL>
+__device__ __forceinline__ unsigned dpp_u(unsigned v) {
+    return (unsigned)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __builtin_bit_cast(float, dpp_u<CTRL>(__builtin_bit_cast(unsigned, v)));
+}
+__device__ __forceinline__ unsigned umax(unsigned a, unsigned b) { return a > b ? a : b; }
+__device__ __forceinline__ float readlane_f(float v, int l) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+}
+
+// Value of the partner lane (lane index with bit BIT flipped, or for bits
+// below 4 the lane mirrored inside its group of 2^(BIT+1), which also flips
+// BIT) taken from `send`: permlane swaps across the halves and 16-lane rows
+// of the wave, DPP inside a row.  No LDS traffic.
+template <int BIT>
+__device__ __forceinline__ float partner_value(float send, int lane) {
+    const unsigned u = __builtin_bit_cast(unsigned, send);
+    if constexpr (BIT == 5) {
+        const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+        return __builtin_bit_cast(float, (lane & 32) ? r[0] : r[1]);
+    } else if constexpr (BIT == 4) {
+        const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+        return __builtin_bit_cast(float, (lane & 16) ? r[0] : r[1]);
+    } else if constexpr (BIT == 3) {
+        return dpp_f<kDppMirror>(send);
+    } else if constexpr (BIT == 2) {
+        return dpp_f<kDppHalfMirror>(send);
+    } else if constexpr (BIT == 1) {
+        return dpp_f<kDppXor2>(send);
+    } else {
+        return dpp_f<kDppXor1>(send);
+    }
+}
+
 // Sum of NV per-lane values over the lanes that differ only in bits [0, B),
 // scattered: on return the lane holds the total of value index
 // vi = (lane >> (B - log2 NV)) & (NV - 1), identical in the 2^(B - log2 NV)
-// lanes of its set.  Fixed order: deterministic.
-template <int NV, int B>
-__device__ __forceinline__ float reduce_scatter(float (&v)[NV], int lane) {
-    static_assert((NV & (NV - 1)) == 0 && ilog2(NV) <= B, "bad reduce shape");
-#pragma unroll
-    for (int s = 0; (NV >> s) > 1; ++s) {
-        const int m = NV >> s;
-        const int half = m / 2;
-        const int bit = B - 1 - s;
-        const bool upper = (lane >> bit) & 1;
+// lanes of its set.  Each scatter step halves the values a lane keeps (the
+// half selected by the step's lane bit) and adds the partner's copy of
+// them; the remaining bits are summed whole.  Fixed order: deterministic.
+template <int NV, int B, int S = 0>
+__device__ __forceinline__ void scatter_steps(float (&v)[NV], int lane) {
+    if constexpr ((NV >> S) > 1) {
+        constexpr int half = (NV >> S) / 2;
+        constexpr int BIT = B - 1 - S;
+        const bool upper = (lane >> BIT) & 1;
 #pragma unroll
         for (int t = 0; t < half; ++t) {
             const float keep = upper ? v[half + t] : v[t];
             const float send = upper ? v[t] : v[half + t];
-            v[t] = keep + __shfl_xor(send, 1 << bit);
+            v[t] = keep + partner_value<BIT>(send, lane);
         }
+        scatter_steps<NV, B, S + 1>(v, lane);
     }
-    float r = v[0];
-#pragma unroll
-    for (int bit = B - 1 - ilog2(NV); bit >= 0; --bit) r += __shfl_xor(r, 1 << bit);
-    return r;
+}
+template <int BIT>
+__device__ __forceinline__ float sum_bits_below(float r, int lane) {
+    if constexpr (BIT >= 0) {
+        r += partner_value<BIT>(r, lane);
+        return sum_bits_below<BIT - 1>(r, lane);
+    } else {
+        return r;
+    }
+}
+template <int NV, int B>
+__device__ __forceinline__ float reduce_scatter(float (&v)[NV], int lane) {
+    static_assert((NV & (NV - 1)) == 0 && ilog2(NV) <= B && B <= 6, "bad reduce shape");
+    scatter_steps<NV, B>(v, lane);
+    return sum_bits_below<B - 1 - ilog2(NV)>(v[0], lane);
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-    return v;
-}
-
+// Maximum over the wave, returned uniform (DPP inside rows, then the four
+// row results read as scalars).
 __device__ __forceinline__ unsigned wave_max_u32(unsigned v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-        const unsigned t = (unsigned)__shfl_xor((int)v, o);
-        v = t > v ? t : v;
-    }
-    return v;
+    v = umax(v, dpp_u<kDppXor1>(v));
+    v = umax(v, dpp_u<kDppXor2>(v));
+    v = umax(v, dpp_u<kDppHalfMirror>(v));
+    v = umax(v, dpp_u<kDppMirror>(v));
+    const unsigned a = __builtin_amdgcn_readlane(v, 0), b = __builtin_amdgcn_readlane(v, 16);
+    const unsigned c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
+    return umax(umax(a, b), umax(c, d));
+}
+
+// Sum over the wave in a fixed order, returned uniform.
+__device__ __forceinline__ float wave_sum(float v) {
+    v += dpp_f<kDppXor1>(v);
+    v += dpp_f<kDppXor2>(v);
+    v += dpp_f<kDppHalfMirror>(v);
+    v += dpp_f<kDppMirror>(v);
+    return (readlane_f(v, 0) + readlane_f(v, 16)) + (readlane_f(v, 32) + readlane_f(v, 48));
 }
 
 // Power-of-two exponent k such that max_abs * 2^k lies in [2^13, 2^14),
@@ -145,106 +223,141 @@ __device__ __forceinline__ int range_exponent(unsigned biased_exp) {
     return k > 100 ? 100 : (k < -100 ? -100 : k);
 }
 
+// Index of the calling wave inside its workgroup, as a wave-uniform value
+// (scalar register): item and slot arithmetic derived from it then stays on
+// the scalar unit instead of occupying vector registers.
+__device__ __forceinline__ int wave_in_block() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
+__device__ __forceinline__ const uint8_t* readlane_ptr(const uint8_t* p, int src) {
+    const uint64_t v = reinterpret_cast<uint64_t>(p);
+    const unsigned lo = __builtin_amdgcn_readlane((unsigned)v, src);
+    const unsigned hi = __builtin_amdgcn_readlane((unsigned)(v >> 32), src);
+    return reinterpret_cast<const uint8_t*>(((uint64_t)hi << 32) | lo);
+}
+
+// Per-lane copy of a 16-entry kernel-argument array without dynamic
+// indexing: lane j < 16 receives p[j].
+__device__ __forceinline__ const uint8_t* lane_pick(const uint8_t* const (&p)[16], int lane) {
+    const uint8_t* r = nullptr;
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+        if (lane == j) r = p[j];
+    return r;
+}
+
 // ---------------------------------------------------------------- top-k
-// Group-limited top-k of one token on one wave.  Lane l holds experts
-// l*EPL .. l*EPL+EPL-1.  Writes ids[k] (sb descending, ties to the lower
-// index) and w[k] = rsf * s / sum s.
+// Merge of two (largest, second largest) pairs.
+__device__ __forceinline__ void top2_merge(float& a1, float& a2, float b1, float b2) {
+    const float n1 = fmaxf(a1, b1);
+    const float n2 = a1 >= b1 ? fmaxf(a2, b1) : fmaxf(a1, b2);
+    a1 = n1;
+    a2 = n2;
+}
+
+// Group-limited top-k of one token on one wave (every lane must call it).
+// Lane l holds experts l*EPL .. l*EPL+EPL-1.  On return lane j < K holds
+// the j-th choice (sb descending, ties to the lower index) in *my_id and its
+// weight rsf * s_j / sum_chosen s in *my_w.  topk_load fetches a lane's
+// scores; wave_group_topk_values selects.
 template <int EPL>
-__device__ void wave_group_topk(const float* __restrict__ logits, const float* __restrict__ bias, int E, int G,
-                                int TG, int K, float rsf, int32_t* __restrict__ ids_out,
-                                float* __restrict__ w_out, int lane) {
-    float s[EPL], key[EPL];
+__device__ __forceinline__ void topk_load(const float* __restrict__ s_in, const float* __restrict__ sb_in, int E,
+                                          int lane, float (&s)[EPL], float (&key)[EPL]) {
     const float NEG = -__builtin_inff();
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
         const int e = lane * EPL + i;
-        if (e < E) {
-            const float l = logits[e];
-            s[i] = 1.0f / (1.0f + expf(-l));
-            key[i] = s[i] + bias[e];
-        } else {
-            s[i] = 0.0f;
-            key[i] = NEG;
-        }
+        s[i] = e < E ? s_in[e] : 0.0f;
+        key[i] = e < E ? sb_in[e] : NEG;
     }
-    // Group score: sum of the two largest biased scores of the group.
-    const int gsize = E / G;
-    const int lpg = gsize / EPL;  // lanes per group (power of two)
+}
+
+template <int EPL>
+__device__ void wave_group_topk_values(const float (&s)[EPL], const float (&key)[EPL], int E, int G, int TG, int K,
+                                       float rsf, int lane, int* my_id, float* my_w) {
+    const float NEG = -__builtin_inff();
+    // Group score: the two largest biased scores of the group.
+    const int lpg = (E / G) / EPL;  // lanes per group (power of two)
     float a1 = NEG, a2 = NEG;
 #pragma unroll
-    for (int i = 0; i < EPL; ++i) {
-        if (key[i] > a1) {
-            a2 = a1;
-            a1 = key[i];
-        } else if (key[i] > a2) {
-            a2 = key[i];
-        }
-    }
-    for (int o = 1; o < lpg; o <<= 1) {
-        const float b1 = __shfl_xor(a1, o), b2 = __shfl_xor(a2, o);
-        const float n1 = fmaxf(a1, b1);
-        const float n2 = a1 >= b1 ? fmaxf(a2, b1) : fmaxf(a1, b2);
-        a1 = n1;
-        a2 = n2;
-    }
+    for (int i = 0; i < EPL; ++i) top2_merge(a1, a2, key[i], NEG);
+    if (lpg > 1) top2_merge(a1, a2, dpp_f<kDppXor1>(a1), dpp_f<kDppXor1>(a2));
+    if (lpg > 2) top2_merge(a1, a2, dpp_f<kDppXor2>(a1), dpp_f<kDppXor2>(a2));
+    if (lpg > 4) top2_merge(a1, a2, dpp_f<kDppHalfMirror>(a1), dpp_f<kDppHalfMirror>(a2));
+    if (lpg > 8) top2_merge(a1, a2, dpp_f<kDppMirror>(a1), dpp_f<kDppMirror>(a2));
+    for (int o = 16; o < lpg; o <<= 1) top2_merge(a1, a2, __shfl_xor(a1, o), __shfl_xor(a2, o));
     const float gscore = a1 + a2;
     const int my_group = lane / lpg;
     int rank = 0;
     for (int g = 0; g < G; ++g) {
-        const float o = __shfl(gscore, g * lpg);
+        const float o = readlane_f(gscore, g * lpg);
         rank += (o > gscore || (o == gscore && g < my_group)) ? 1 : 0;
     }
-    const bool eligible = (lane * EPL < E) && rank < TG;
+    const bool eligible = rank < TG;
     bool live[EPL];
 #pragma unroll
     for (int i = 0; i < EPL; ++i) live[i] = eligible && (lane * EPL + i < E);
 
-    float sum_s = 0.0f;
-    float chosen_s[16];
-    int chosen_e[16];
+    float sum_s = 0.0f, mine_s = 0.0f;
+    int mine_e = 0;
     for (int j = 0; j < K; ++j) {
-        // lane-local best (lowest index among equals)
-        float lb = NEG;
-        int li = -1;
+        // lane-local best (lowest index among equals), as an order-preserving
+        // unsigned key (larger float -> larger key; 0 = nothing left)
+        unsigned ob = 0u;
+        int li = 0;
+        float ls = 0.0f;
 #pragma unroll
         for (int i = 0; i < EPL; ++i) {
-            if (live[i] && (li < 0 || key[i] > lb)) {
-                lb = key[i];
+            unsigned u = __builtin_bit_cast(unsigned, key[i]);
+            u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+            if (live[i] && u > ob) {
+                ob = u;
                 li = i;
+                ls = s[i];
             }
         }
-        // wave maximum of the lane bests
-        unsigned ob = __builtin_bit_cast(unsigned, lb);
-        // order-preserving map of floats to unsigned (larger float -> larger key)
-        ob = (ob & 0x80000000u) ? ~ob : (ob | 0x80000000u);
-        if (li < 0) ob = 0u;
         const unsigned mx = wave_max_u32(ob);
-        const unsigned long long hit = __ballot(li >= 0 && ob == mx);
+        const unsigned long long hit = __ballot(ob == mx && ob != 0u);
         const int wl = __ffsll((long long)hit) - 1;  // lowest lane holding the maximum
-        const int wi = __shfl(li, wl);
-        const int e = wl * EPL + wi;
-        const float se = __shfl(li >= 0 ? s[li < 0 ? 0 : li] : 0.0f, wl);
+        const int wi = __builtin_amdgcn_readlane(li, wl);
+        const float se = readlane_f(ls, wl);
         if (lane == wl) {
 #pragma unroll
             for (int i = 0; i < EPL; ++i)
                 if (i == wi) live[i] = false;
         }
-        chosen_e[j] = e;
-        chosen_s[j] = se;
+        if (lane == j) {
+            mine_e = wl * EPL + wi;
+            mine_s = se;
+        }
         sum_s += se;
     }
-    if (lane == 0) {
-        for (int j = 0; j < K; ++j) {
-            ids_out[j] = chosen_e[j];
-            w_out[j] = rsf * chosen_s[j] / sum_s;
-        }
+    *my_id = mine_e;
+    *my_w = rsf * mine_s / sum_s;
+}
+
+template <int EPL>
+__device__ __forceinline__ void wave_group_topk(const float* __restrict__ s_in, const float* __restrict__ sb_in, int E,
+                                                int G, int TG, int K, float rsf, int lane, int* my_id, float* my_w) {
+    float s[EPL], key[EPL];
+    topk_load<EPL>(s_in, sb_in, E, lane, s, key);
+    wave_group_topk_values<EPL>(s, key, E, G, TG, K, rsf, lane, my_id, my_w);
+}
+
+template <int EPL>
+__global__ void __launch_bounds__(64) topk_kernel(DecodeArgs a) {
+    const int lane = threadIdx.x;
+    int id;
+    float w;
+    wave_group_topk<EPL>(a.s, a.sb, a.E, a.G, a.TG, a.K, a.rsf, lane, &id, &w);
+    if (lane < a.K) {
+        a.ids[lane] = id;
+        a.w[lane] = w;
     }
 }
 
 // ---------------------------------------------------------------- gate/up
-// Work items of the gate/up stage: (slot, block of R rows).  Each wave keeps
-// the token's activations in registers and loops over items with a stride
-// of the number of waves in the grid.
+constexpr int kGateUpItemsPerRound = 3;
+// Work items of the gate/up stage: (slot, block of R rows of gate and up).
 template <int KG>
 struct GateUpShape {
     static constexpr int CPL = chunks_per_lane(KG);
@@ -253,13 +366,42 @@ struct GateUpShape {
     static constexpr int NL = R / RPL;  // wave loads per matrix per chunk column
     static constexpr int B = KG >= kWave ? 6 : ilog2(KG);
     static constexpr int NV = 2 * NL;
+    static_assert(RPL == 1 || NL == 1, "gate/up scale runs");
 };
+
+// NL consecutive fp16 scales (NL*2-byte aligned) -> (NL+1)/2 dwords.
+template <int NL>
+__device__ __forceinline__ void load_scales(const uint16_t* p, unsigned (&d)[(NL + 1) / 2]) {
+    if constexpr (NL == 1) {
+        d[0] = __builtin_nontemporal_load(as_global<uint16_t>(p));
+    } else if constexpr (NL == 2) {
+        d[0] = __builtin_nontemporal_load(as_global<unsigned>(p));
+    } else if constexpr (NL == 4) {
+        const u32x2 v = __builtin_nontemporal_load(as_global<u32x2>(p));
+        d[0] = v[0];
+        d[1] = v[1];
+    } else {
+        static_assert(NL % 8 == 0, "scale pack");
+#pragma unroll
+        for (int q = 0; q < NL / 8; ++q) {
+            const u32x4 v = __builtin_nontemporal_load(as_global<u32x4>(p) + q);
+            d[4 * q + 0] = v[0];
+            d[4 * q + 1] = v[1];
+            d[4 * q + 2] = v[2];
+            d[4 * q + 3] = v[3];
+        }
+    }
+}
+template <int N>
+__device__ __forceinline__ float scale_at(const unsigned (&d)[N], int n) {
+    return half_bits_to_float((n & 1) ? (d[n / 2] >> 16) : (d[n / 2] & 0xFFFFu));
+}
 
 // Loads this lane's activation groups (bf16) and converts them to scaled
 // fp16 pairs; returns the scaling exponent kx (activations * 2^kx).
 template <int KG>
-__device__ __forceinline__ int load_activation_pairs(const uint16_t* __restrict__ x, int lane,
-                                                     f16x2 (&xp)[GateUpShape<KG>::CPL][16]) {
+__device__ __forceinline__ int convert_activation_pairs(const uint16_t* __restrict__ x, int lane,
+                                                        f16x2 (&xp)[GateUpShape<KG>::CPL][16]) {
     using S = GateUpShape<KG>;
     const int g0 = KG >= kWave ? lane : (lane & (KG - 1));
     u32x4 raw[S::CPL][4];
@@ -273,9 +415,7 @@ __device__ __forceinline__ int load_activation_pairs(const uint16_t* __restrict_
 #pragma unroll
             for (int z = 0; z < 4; ++z) {
                 const unsigned d = raw[c][q][z];
-                const unsigned lo = d & 0x7FFFu, hi = (d >> 16) & 0x7FFFu;
-                mx = lo > mx ? lo : mx;
-                mx = hi > mx ? hi : mx;
+                mx = umax(mx, umax(d & 0x7FFFu, (d >> 16) & 0x7FFFu));
             }
         }
     }
@@ -306,70 +446,92 @@ __device__ __forceinline__ int load_activation_pairs(const uint16_t* __restrict_
     return kx;
 }
 
-// One gate/up work item: rows [rb*R, rb*R+R) of gate and up of one expert;
-// writes h = silu(g) * u (fp32) for those rows.
+// Activation pairs as written by the router kernel: lane l, chunk column c
+// at dwords [(c*64 + l)*16, +16).
 template <int KG>
-__device__ __forceinline__ void gateup_item(const uint8_t* __restrict__ blob, const BlobLayout& L, int rb,
-                                            int lane, const f16x2 (&xp)[GateUpShape<KG>::CPL][16], int kx,
-                                            float* __restrict__ h_out) {
+__device__ __forceinline__ void load_activation_pairs(const unsigned* __restrict__ xpairs, int lane,
+                                                      f16x2 (&xp)[GateUpShape<KG>::CPL][16]) {
+    using S = GateUpShape<KG>;
+#pragma unroll
+    for (int c = 0; c < S::CPL; ++c) {
+        const u32x4* p = reinterpret_cast<const u32x4*>(xpairs + ((size_t)c * kWave + lane) * 16);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const u32x4 v = p[q];
+            // element copied to a scalar first: __builtin_bit_cast applied to
+            // an ext-vector element reads the vector's first element
+#pragma unroll
+            for (int z = 0; z < 4; ++z) {
+                const unsigned e = v[z];
+                xp[c][4 * q + z] = __builtin_bit_cast(f16x2, e);
+            }
+        }
+    }
+}
+
+template <int KG>
+struct GateUpBuf {
+    using S = GateUpShape<KG>;
+    u32x4 cg[S::NL][S::CPL], cu[S::NL][S::CPL];
+    unsigned sgu[S::CPL][S::NL];  // halves 0..NL-1 gate, NL..2NL-1 up
+};
+
+template <int KG>
+__device__ __forceinline__ void gateup_issue(const uint8_t* __restrict__ blob, const BlobLayout& L, int rb, int lane,
+                                             GateUpBuf<KG>& b) {
     using S = GateUpShape<KG>;
     const int g0 = KG >= kWave ? lane : (lane & (KG - 1));
     const int row_sub = KG >= kWave ? 0 : (lane / KG);
-    u32x4 cg[S::NL][S::CPL], cu[S::NL][S::CPL];
 #pragma unroll
     for (int n = 0; n < S::NL; ++n) {
         const size_t row = (size_t)rb * S::R + n * S::RPL + row_sub;
 #pragma unroll
         for (int c = 0; c < S::CPL; ++c) {
             const size_t off = (row * KG + g0 + kWave * c) * 16;
-            cg[n][c] = load_stream16(blob + L.gate_q + off);
-            cu[n][c] = load_stream16(blob + L.up_q + off);
+            b.cg[n][c] = load_stream16(blob + L.gate_q + off);
+            b.cu[n][c] = load_stream16(blob + L.up_q + off);
         }
     }
-    // scales: NL consecutive fp16 per (lane, chunk column)
-    float sg[S::CPL][S::NL], su[S::CPL][S::NL];
 #pragma unroll
     for (int c = 0; c < S::CPL; ++c) {
-        const size_t si = ((size_t)rb * KG + g0 + kWave * c) * S::R + (size_t)row_sub * S::NL;
-        const uint16_t* pg = reinterpret_cast<const uint16_t*>(blob + L.gate_s) + si;
-        const uint16_t* pu = reinterpret_cast<const uint16_t*>(blob + L.up_s) + si;
-        if constexpr (S::NL == 4) {
-            const u32x2 a = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(pg));
-            const u32x2 b = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(pu));
-            sg[c][0] = half_bits_to_float(a[0] & 0xFFFFu);
-            sg[c][1] = half_bits_to_float(a[0] >> 16);
-            sg[c][2] = half_bits_to_float(a[1] & 0xFFFFu);
-            sg[c][3] = half_bits_to_float(a[1] >> 16);
-            su[c][0] = half_bits_to_float(b[0] & 0xFFFFu);
-            su[c][1] = half_bits_to_float(b[0] >> 16);
-            su[c][2] = half_bits_to_float(b[1] & 0xFFFFu);
-            su[c][3] = half_bits_to_float(b[1] >> 16);
+        const uint16_t* p =
+            reinterpret_cast<const uint16_t*>(blob + L.gu_s) + ((size_t)rb * KG + g0 + kWave * c) * 2 * S::R;
+        if constexpr (S::RPL == 1) {
+            load_scales<2 * S::NL>(p, b.sgu[c]);
         } else {
-#pragma unroll
-            for (int n = 0; n < S::NL; ++n) {
-                sg[c][n] = half_bits_to_float(pg[n]);
-                su[c][n] = half_bits_to_float(pu[n]);
-            }
+            const unsigned g = __builtin_nontemporal_load(as_global<uint16_t>(p + row_sub));
+            const unsigned u = __builtin_nontemporal_load(as_global<uint16_t>(p + S::R + row_sub));
+            b.sgu[c][0] = g | (u << 16);
         }
     }
+}
+
+// Computes one item from its loaded buffer: h = silu(g) * u for rows
+// [rb*R, rb*R + R), written as fp32.
+template <int KG>
+__device__ __forceinline__ void gateup_compute(const GateUpBuf<KG>& b, int rb, int lane,
+                                               const f16x2 (&xp)[GateUpShape<KG>::CPL][16], int kx,
+                                               float* __restrict__ h_out, bool store) {
+    using S = GateUpShape<KG>;
+    const int row_sub = KG >= kWave ? 0 : (lane / KG);
     float v[S::NV];
 #pragma unroll
     for (int n = 0; n < S::NL; ++n) {
         float ag = 0.0f, au = 0.0f;
 #pragma unroll
         for (int c = 0; c < S::CPL; ++c) {
-            ag = fmaf(sg[c][n], dot_chunk(cg[n][c], xp[c], 0.0f), ag);
-            au = fmaf(su[c][n], dot_chunk(cu[n][c], xp[c], 0.0f), au);
+            ag = fmaf(scale_at(b.sgu[c], n), dot_chunk(b.cg[n][c], xp[c], 0.0f), ag);
+            au = fmaf(scale_at(b.sgu[c], S::NL + n), dot_chunk(b.cu[n][c], xp[c], 0.0f), au);
         }
         v[n] = ag;
         v[S::NL + n] = au;
     }
     const float r = reduce_scatter<S::NV, S::B>(v, lane);
     // value index: top bit = matrix (0 gate, 1 up), low bits = row step n
-    const float other = __shfl_xor(r, 1 << (S::B - 1));
+    const float other = partner_value<S::B - 1>(r, lane);
     const int low_bits = S::B - ilog2(S::NV);
     const int vi = (lane >> low_bits) & (S::NV - 1);
-    if (vi < S::NL && (lane & ((1 << low_bits) - 1)) == 0) {
+    if (store && vi < S::NL && (lane & ((1 << low_bits) - 1)) == 0) {
         const float g = __builtin_ldexpf(r, -kx);
         const float u = __builtin_ldexpf(other, -kx);
         const float h = g / (1.0f + expf(-g)) * u;
@@ -377,44 +539,31 @@ __device__ __forceinline__ void gateup_item(const uint8_t* __restrict__ blob, co
     }
 }
 
-// Blob of a slot: routed slots 0..K-1 follow the routing, shared ones follow.
-__device__ __forceinline__ const uint8_t* slot_blob(const DecodeArgs& a, int slot) {
-    if (slot >= a.K) return a.shared_blob;
-    return a.direct ? a.blobs[slot] : a.table[a.ids[slot]];
-}
-
-// Slots [slot_begin, slot_end), or the launch's slot list when it has one.
-template <int KG>
-__device__ __forceinline__ void gateup_loop(const DecodeArgs& a, int slot_begin, int slot_end, bool use_list,
-                                            int wave_id, int n_waves, int lane) {
-    using S = GateUpShape<KG>;
-    f16x2 xp[S::CPL][16];
-    const int kx = load_activation_pairs<KG>(a.x, lane, xp);
-    const BlobLayout L = blob_layout(a.H, a.I);
-    const int per_slot = a.I / S::R;
-    const int n_slots = use_list ? a.n_slot_list : slot_end - slot_begin;
-    const int n_items = n_slots * per_slot;
-    for (int item = wave_id; item < n_items; item += n_waves) {
-        const int k = item / per_slot;
-        const int slot = use_list ? a.slot_list[k] : slot_begin + k;
-        const int rb = item % per_slot;
-        gateup_item<KG>(slot_blob(a, slot), L, rb, lane, xp, kx, a.h + (size_t)slot * a.I);
-    }
-}
-
 // ---------------------------------------------------------------- kernel 1
-template <int KG, int EPL>
-__global__ void __launch_bounds__(256) router_shared_kernel(DecodeArgs a, int n_router_wg, int n_shared_wg) {
+// Router: logit[e] = sum_h W_r[e][h] x[h] in fp32, one row per wave (lane l
+// covers floats [4l + 256c, 4l + 256c + 4)), turned into s and sb.  The
+// first wave of block 0 also writes the token's activation pairs.
+template <int KG>
+__global__ void __launch_bounds__(256) router_kernel(DecodeArgs a) {
+    using S = GateUpShape<KG>;
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    if ((int)blockIdx.x >= n_router_wg) {
-        // shared expert gate/up
-        const int wg = blockIdx.x - n_router_wg;
-        gateup_loop<KG>(a, a.K, a.K + a.S, false, wg * 4 + wave, n_shared_wg * 4, lane);
-        return;
+    const int wave = wave_in_block();
+    if (blockIdx.x == 0 && wave == 0) {
+        f16x2 xp[S::CPL][16];
+        const int kx = convert_activation_pairs<KG>(a.x, lane, xp);
+#pragma unroll
+        for (int c = 0; c < S::CPL; ++c) {
+            u32x4* p = reinterpret_cast<u32x4*>(a.xpairs + ((size_t)c * kWave + lane) * 16);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                u32x4 v;
+#pragma unroll
+                for (int z = 0; z < 4; ++z) v[z] = __builtin_bit_cast(unsigned, xp[c][4 * q + z]);
+                p[q] = v;
+            }
+        }
+        if (lane == 0) *a.kx = kx;
     }
-    // Router: logits[e] = sum_h W_r[e][h] x[h] in fp32.  Lane l covers
-    // floats [4l + 256c, 4l + 256c + 4) of a row.
     constexpr int CR = KG / 8;  // H / 256
     float xr[CR][4];
 #pragma unroll
@@ -425,7 +574,7 @@ __global__ void __launch_bounds__(256) router_shared_kernel(DecodeArgs a, int n_
         xr[c][2] = __builtin_bit_cast(float, xb[1] << 16);
         xr[c][3] = __builtin_bit_cast(float, xb[1] & 0xFFFF0000u);
     }
-    const int n_router_waves = n_router_wg * 4;
+    const int n_router_waves = gridDim.x * 4;
     for (int e = blockIdx.x * 4 + wave; e < a.E; e += n_router_waves) {
         const float* row = a.router_w + (size_t)e * a.H;
         f32x4 wv[CR];
@@ -441,103 +590,172 @@ __global__ void __launch_bounds__(256) router_shared_kernel(DecodeArgs a, int n_
             acc = fmaf(wv[c][3], xr[c][3], acc);
         }
         acc = wave_sum(acc);
-        if (lane == 0) a.logits[e] = acc;
-    }
-    // The last router workgroup to arrive runs the top-k.
-    __threadfence();
-    __syncthreads();
-    __shared__ int s_last;
-    if (threadIdx.x == 0) s_last = atomicAdd(a.ticket, 1u) == (unsigned)(n_router_wg - 1);
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
-    if (wave == 0) {
-        wave_group_topk<EPL>(a.logits, a.bias, a.E, a.G, a.TG, a.K, a.rsf, a.ids, a.w, lane);
-        if (lane == 0) atomicExch(a.ticket, 0u);
+        if (lane == 0) {
+            const float s = 1.0f / (1.0f + expf(-acc));
+            a.s[e] = s;
+            a.sb[e] = s + a.bias[e];
+        }
     }
 }
 
 // ---------------------------------------------------------------- kernel 2
-template <int KG>
+// Items: the shared expert's (when with_shared) come first, then those of
+// the routed slots.  A wave takes items wave_id + j * n_waves in rounds of
+// NI: each round issues the loads of its NI items, then computes them, in
+// straight-line code (items past the end are clamped to the last item and
+// their results not stored), so the compiler's wait counts stay exact and
+// the later items' loads stream while the first ones are computed.  A wave
+// whose first item is a shared one issues its loads before deriving the
+// routing, so HBM streams while the top-k runs.
+template <int KG, int EPL, bool EARLY>
 __global__ void __launch_bounds__(256) gateup_kernel(DecodeArgs a) {
+    using S = GateUpShape<KG>;
+    constexpr int NI = kGateUpItemsPerRound;
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    gateup_loop<KG>(a, 0, a.K, a.n_slot_list > 0, blockIdx.x * 4 + wave, gridDim.x * 4, lane);
+    const int wave = wave_in_block();
+    const int wave_id = blockIdx.x * 4 + wave;
+    const int n_waves = gridDim.x * 4;
+    const BlobLayout L = blob_layout(a.H, a.I);
+    const int per_slot = a.I / S::R;
+    const int n_shared_items = a.with_shared ? a.S * per_slot : 0;
+    const int n_routed_slots = a.use_slot_list ? a.n_slot_list : a.K;
+    const int n_items = n_shared_items + n_routed_slots * per_slot;
+    if (wave_id >= n_items) return;
+
+    // Small dependent inputs first (vector loads complete in order, so
+    // waiting for them must not mean waiting for weight streams issued
+    // before them): activation pairs, then the routing scores.
+    f16x2 xp[S::CPL][16];
+    load_activation_pairs<KG>(a.xpairs, lane, xp);
+    float tk_s[EPL], tk_key[EPL];
+    topk_load<EPL>(a.s, a.sb, a.E, lane, tk_s, tk_key);
+    __builtin_amdgcn_sched_barrier(0);
+    const int kx = *a.kx;
+    // EARLY: the launch guarantees every wave's first item is a shared one
+    GateUpBuf<KG> b[NI];
+    if constexpr (EARLY) gateup_issue<KG>(a.shared_blob, L, wave_id % per_slot, lane, b[0]);
+
+    // The slot -> blob table goes to this wave's LDS row: looking it up per
+    // item then waits only on the LDS counter, whereas reading a register
+    // that a global load filled earlier can make the compiler drain every
+    // outstanding weight load first.  The blobs of the chosen experts are
+    // fetched with scalar loads, which do not queue behind vector loads.
+    __shared__ const uint8_t* wave_blobs[4][16];
+    if (a.direct) {
+        if (lane < 16) wave_blobs[wave][lane] = lane_pick(a.blobs, lane);
+    } else {
+        int id;
+        float w;
+        wave_group_topk_values<EPL>(tk_s, tk_key, a.E, a.G, a.TG, a.K, a.rsf, lane, &id, &w);
+        // all table reads before any global store of this kernel, with
+        // wave-uniform addresses, so they can be scalar loads
+        const uint8_t* mine = nullptr;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            if (j < a.K) {
+                const uint8_t* p = a.table[__builtin_amdgcn_readlane(id, j)];
+                if (lane == j) mine = p;
+            }
+        }
+        if (lane < 16) wave_blobs[wave][lane] = mine;
+        if (wave_id == 0 && lane < a.K) {
+            a.ids[lane] = id;
+            a.w[lane] = w;
+            a.slot_blobs[lane] = mine;
+        }
+    }
+    __builtin_amdgcn_wave_barrier();
+    // Settle the activation registers here, once: an empty asm that reads
+    // and rewrites each of them makes the compiler wait for their loads at
+    // this point (after the top-k hid that latency) and treat them as
+    // ready afterwards, instead of re-waiting for them behind weight loads.
+#pragma unroll
+    for (int c = 0; c < S::CPL; ++c)
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            unsigned r = __builtin_bit_cast(unsigned, xp[c][k]);
+            asm volatile("" : "+v"(r));
+            xp[c][k] = __builtin_bit_cast(f16x2, r);
+        }
+
+    // item -> (slot, row block)
+    auto slot_of = [&](int item) {
+        if (item < n_shared_items) return a.K + item / per_slot;
+        const int k = (item - n_shared_items) / per_slot;
+        int s = k;
+        if (a.use_slot_list) {
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+                if (j == k) s = a.slot_list[j];
+        }
+        return s;
+    };
+    auto rb_of = [&](int item) {
+        return item < n_shared_items ? item % per_slot : (item - n_shared_items) % per_slot;
+    };
+    auto blob_of = [&](int slot) { return slot >= a.K ? a.shared_blob : wave_blobs[wave][slot]; };
+    auto issue = [&](int item, GateUpBuf<KG>& buf) {
+        const int it = item < n_items ? item : n_items - 1;
+        gateup_issue<KG>(blob_of(slot_of(it)), L, rb_of(it), lane, buf);
+    };
+    auto compute = [&](int item, const GateUpBuf<KG>& buf) {
+        const int it = item < n_items ? item : n_items - 1;
+        gateup_compute<KG>(buf, rb_of(it), lane, xp, kx, a.h + (size_t)slot_of(it) * a.I, item < n_items);
+    };
+
+    // round 0 (with EARLY its first item is already in flight)
+    if constexpr (!EARLY) issue(wave_id, b[0]);
+#pragma unroll
+    for (int k = 1; k < NI; ++k) issue(wave_id + k * n_waves, b[k]);
+#pragma unroll
+    for (int k = 0; k < NI; ++k) compute(wave_id + k * n_waves, b[k]);
+    for (int base = wave_id + NI * n_waves; base < n_items; base += NI * n_waves) {
+#pragma unroll
+        for (int k = 0; k < NI; ++k) issue(base + k * n_waves, b[k]);
+#pragma unroll
+        for (int k = 0; k < NI; ++k) compute(base + k * n_waves, b[k]);
+    }
 }
 
 // ---------------------------------------------------------------- kernel 3
-template <int KG>
+template <int KG, int NLD>
 struct DownShape {
     static constexpr int CPL = chunks_per_lane(KG);
     static constexpr int RPL = rows_per_load(KG);
-    static constexpr int R = down_rows(KG);
-    static constexpr int NL = R / RPL;
+    static constexpr int NL = NLD;          // wave-load steps per chunk column
+    static constexpr int R = NL * RPL;      // rows per workgroup
     static constexpr int B = KG >= kWave ? 6 : ilog2(KG);
+    static constexpr int WIN = NL < 8 ? NL : 8;  // load steps per round
 };
 
-// One workgroup = one wave per slot (routed experts, then shared ones) and a
-// block of R output rows.  Each wave computes its expert's R outputs; the
-// first R threads combine them in slot order.
-template <int KG, int MAXW>
-__global__ void __launch_bounds__(MAXW * 64) down_combine_kernel(DecodeArgs a) {
-    using S = DownShape<KG>;
-    const int lane = threadIdx.x & 63;
-    const int slot = threadIdx.x >> 6;
-    const int g0 = KG >= kWave ? lane : (lane & (KG - 1));
-    const int row_sub = KG >= kWave ? 0 : (lane / KG);
-    const int rb = blockIdx.x;
-    const uint8_t* blob = slot_blob(a, slot);
-    const BlobLayout L = blob_layout(a.H, a.I);
-
-    u32x4 code[S::NL][S::CPL];
+// h of one slot, this lane's groups (32 floats per chunk column).
+template <int CPL>
+__device__ __forceinline__ void load_h(const float* __restrict__ h, int g0, float (&hv)[CPL][32]) {
 #pragma unroll
-    for (int n = 0; n < S::NL; ++n) {
-        const size_t row = (size_t)rb * S::R + n * S::RPL + row_sub;
-#pragma unroll
-        for (int c = 0; c < S::CPL; ++c) code[n][c] = load_stream16(blob + L.down_q + (row * KG + g0 + kWave * c) * 16);
-    }
-    float sc[S::CPL][S::NL];
-#pragma unroll
-    for (int c = 0; c < S::CPL; ++c) {
-        const size_t si = ((size_t)rb * KG + g0 + kWave * c) * S::R + (size_t)row_sub * S::NL;
-        const uint16_t* ps = reinterpret_cast<const uint16_t*>(blob + L.down_s) + si;
-        if constexpr (S::NL % 8 == 0) {
-#pragma unroll
-            for (int n8 = 0; n8 < S::NL / 8; ++n8) {
-                const u32x4 q = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(ps + 8 * n8));
-#pragma unroll
-                for (int z = 0; z < 4; ++z) {
-                    sc[c][8 * n8 + 2 * z] = half_bits_to_float(q[z] & 0xFFFFu);
-                    sc[c][8 * n8 + 2 * z + 1] = half_bits_to_float(q[z] >> 16);
-                }
-            }
-        } else {
-#pragma unroll
-            for (int n = 0; n < S::NL; ++n) sc[c][n] = half_bits_to_float(ps[n]);
-        }
-    }
-    // h of this slot, this lane's groups: scaled per group to [2^13, 2^14),
-    // split into fp16 hi + lo pairs in the chunk's column order.
-    f16x2 hp[S::CPL][16], lp[S::CPL][16];
-    float hscale[S::CPL];
-#pragma unroll
-    for (int c = 0; c < S::CPL; ++c) {
-        const float* hg = a.h + (size_t)slot * a.I + 32 * (g0 + kWave * c);
-        float hv[32];
+    for (int c = 0; c < CPL; ++c) {
+        const float* hg = h + 32 * (g0 + kWave * c);
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
             const f32x4 t = *reinterpret_cast<const f32x4*>(hg + 4 * q);
-            hv[4 * q + 0] = t[0];
-            hv[4 * q + 1] = t[1];
-            hv[4 * q + 2] = t[2];
-            hv[4 * q + 3] = t[3];
+            hv[c][4 * q + 0] = t[0];
+            hv[c][4 * q + 1] = t[1];
+            hv[c][4 * q + 2] = t[2];
+            hv[c][4 * q + 3] = t[3];
         }
+    }
+}
+
+// h scaled per group to [2^13, 2^14) and split into fp16 hi + lo pairs in the
+// chunk's column order; hscale undoes the scaling.
+template <int CPL>
+__device__ __forceinline__ void h_to_pairs(const float (&hin)[CPL][32], f16x2 (&hp)[CPL][16], f16x2 (&lp)[CPL][16],
+                                           float (&hscale)[CPL]) {
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+        const float (&hv)[32] = hin[c];
         unsigned mx = 0;
 #pragma unroll
-        for (int i = 0; i < 32; ++i) {
-            const unsigned b = __builtin_bit_cast(unsigned, hv[i]) & 0x7FFFFFFFu;
-            mx = b > mx ? b : mx;
-        }
+        for (int i = 0; i < 32; ++i) mx = umax(mx, __builtin_bit_cast(unsigned, hv[i]) & 0x7FFFFFFFu);
         const int kh = range_exponent(mx >> 23);
         hscale[c] = __builtin_ldexpf(1.0f, -kh);
         const float up = __builtin_ldexpf(1.0f, kh);
@@ -547,103 +765,233 @@ __global__ void __launch_bounds__(MAXW * 64) down_combine_kernel(DecodeArgs a) {
             for (int j = 0; j < 4; ++j) {
                 const float fa = hv[8 * d + j] * up, fb = hv[8 * d + j + 4] * up;
                 const f16x2 hi = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(fa, fb));
-                const float ra = fa - (float)hi[0], rb2 = fb - (float)hi[1];
+                const float ra = fa - (float)hi[0], rb = fb - (float)hi[1];
                 hp[c][4 * d + j] = hi;
-                lp[c][4 * d + j] = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(ra, rb2));
+                lp[c][4 * d + j] = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(ra, rb));
             }
         }
     }
-    float v[S::NL];
+}
+
+// One workgroup = one wave per routed slot over a block of R output rows;
+// the shared expert's rows of the block are split evenly over the same
+// waves (at most kDownSharedSteps load steps each), so every SIMD carries
+// the same load.  Row loads go in rounds of WIN steps, the next round issued
+// before the current one is computed (sched_barrier keeps that order); the
+// first R threads combine the block in slot order.
+template <int KG, int NLD>
+__global__ void __launch_bounds__(512) down_combine_kernel(DecodeArgs a) {
+    using S = DownShape<KG, NLD>;
+    constexpr int MAXW = 8;
+    constexpr int WIN = S::WIN;
+    constexpr int NR = (S::NL + WIN - 1) / WIN;  // rounds
+    constexpr int SSMAX = kDownSharedSteps < S::NL ? kDownSharedSteps : S::NL;
+    constexpr int NVP = pow2_at_least(S::NL + SSMAX);
+    const int lane = threadIdx.x & 63;
+    const int slot = wave_in_block();
+    const int K = a.K;
+    const int g0 = KG >= kWave ? lane : (lane & (KG - 1));
+    const int row_sub = KG >= kWave ? 0 : (lane / KG);
+    const int rb = blockIdx.x;
+    const BlobLayout L = blob_layout(a.H, a.I);
+    const uint8_t* blob = a.direct ? readlane_ptr(lane_pick(a.blobs, lane), slot) : a.slot_blobs[slot];
+    const uint8_t* sblob = a.shared_blob;
+
+    // shared steps of this wave: [sh0, sh0 + n_sh)
+    const int ss = (S::NL + K - 1) / K;
+    const int sh0 = slot * ss;
+    const int n_sh = a.S > 0 ? (sh0 >= S::NL ? 0 : (S::NL - sh0 < ss ? S::NL - sh0 : ss)) : 0;
+
+    auto code_off = [&](int step, int c) {
+        const size_t row = (size_t)rb * S::R + step * S::RPL + row_sub;
+        return (row * KG + g0 + kWave * c) * 16;
+    };
+    // h of this slot and of the shared expert first: vector loads complete
+    // in order, so the conversion below must not wait behind weight loads.
+    float hraw[S::CPL][32], shraw[S::CPL][32];
+    load_h<S::CPL>(a.h + (size_t)slot * a.I, g0, hraw);
+    load_h<S::CPL>(a.h + (size_t)K * a.I, g0, shraw);
+    u32x4 code[S::NL][S::CPL];
+    auto issue_round = [&](int r) {
 #pragma unroll
-    for (int n = 0; n < S::NL; ++n) {
+        for (int n = r * WIN; n < (r + 1) * WIN && n < S::NL; ++n)
+#pragma unroll
+            for (int c = 0; c < S::CPL; ++c) code[n][c] = load_stream16(blob + L.down_q + code_off(n, c));
+    };
+    __builtin_amdgcn_sched_barrier(0);
+    issue_round(0);
+    unsigned sc[S::CPL][(S::NL + 1) / 2];
+#pragma unroll
+    for (int c = 0; c < S::CPL; ++c) {
+        const size_t si = ((size_t)rb * KG + g0 + kWave * c) * S::R + (size_t)row_sub * S::NL;
+        load_scales<S::NL>(reinterpret_cast<const uint16_t*>(blob + L.down_s) + si, sc[c]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // shared rows (clamped to a valid step when this wave has fewer)
+    u32x4 scode[SSMAX][S::CPL];
+    unsigned ssc_bits[SSMAX][S::CPL];
+#pragma unroll
+    for (int t = 0; t < SSMAX; ++t) {
+        const int step = sh0 + t < S::NL ? sh0 + t : S::NL - 1;
+#pragma unroll
+        for (int c = 0; c < S::CPL; ++c) {
+            scode[t][c] = load_stream16(sblob + L.down_q + code_off(step, c));
+            const size_t si = ((size_t)rb * KG + g0 + kWave * c) * S::R + (size_t)row_sub * S::NL + step;
+            ssc_bits[t][c] = __builtin_nontemporal_load(as_global<uint16_t>(sblob + L.down_s) + si);
+        }
+    }
+    if constexpr (NR > 1) issue_round(1);
+    __builtin_amdgcn_sched_barrier(0);
+
+    f16x2 hp[S::CPL][16], lp[S::CPL][16];
+    float hscale[S::CPL];
+    h_to_pairs<S::CPL>(hraw, hp, lp, hscale);
+    f16x2 shp[S::CPL][16], slp[S::CPL][16];
+    float shscale[S::CPL];
+    h_to_pairs<S::CPL>(shraw, shp, slp, shscale);
+
+    float v[NVP];
+#pragma unroll
+    for (int n = 0; n < NVP; ++n) v[n] = 0.0f;
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int n = r * WIN; n < (r + 1) * WIN && n < S::NL; ++n) {
+            float acc = 0.0f;
+#pragma unroll
+            for (int c = 0; c < S::CPL; ++c)
+                acc = fmaf(scale_at(sc[c], n) * hscale[c], dot_chunk_hilo(code[n][c], hp[c], lp[c], 0.0f), acc);
+            v[n] = acc;
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (r + 2 < NR) issue_round(r + 2);
+    }
+#pragma unroll
+    for (int t = 0; t < SSMAX; ++t) {
         float acc = 0.0f;
 #pragma unroll
         for (int c = 0; c < S::CPL; ++c)
-            acc = fmaf(sc[c][n] * hscale[c], dot_chunk_hilo(code[n][c], hp[c], lp[c], 0.0f), acc);
-        v[n] = acc;
+            acc = fmaf(half_bits_to_float(ssc_bits[t][c]) * shscale[c],
+                       dot_chunk_hilo(scode[t][c], shp[c], slp[c], 0.0f), acc);
+        v[S::NL + t] = t < n_sh ? acc : 0.0f;
     }
-    const float r = reduce_scatter<S::NL, S::B>(v, lane);
+    const float r = reduce_scatter<NVP, S::B>(v, lane);
     __shared__ float part[MAXW][S::R];
-    const int low_bits = S::B - ilog2(S::NL);
+    __shared__ float part_sh[S::R];
+    const int low_bits = S::B - ilog2(NVP);
+    const int vi = (lane >> low_bits) & (NVP - 1);
     if ((lane & ((1 << low_bits) - 1)) == 0) {
-        const int vi = (lane >> low_bits) & (S::NL - 1);
-        part[slot][vi * S::RPL + row_sub] = r;
+        if (vi < S::NL) part[slot][vi * S::RPL + row_sub] = r;
+        else if (vi - S::NL < n_sh) part_sh[(sh0 + vi - S::NL) * S::RPL + row_sub] = r;
     }
     __syncthreads();
     if ((int)threadIdx.x < S::R) {
         const int t = threadIdx.x;
         float y = 0.0f;
-        for (int j = 0; j < a.K; ++j) y = fmaf(a.w[j], part[j][t], y);
-        for (int j = a.K; j < a.K + a.S; ++j) y += part[j][t];
+        for (int j = 0; j < K; ++j) y = fmaf(a.w[j], part[j][t], y);
+        if (a.S > 0) y += part_sh[t];
         a.y[(size_t)rb * S::R + t] = y;
     }
 }
 
 // ---------------------------------------------------------------- launchers
-template <int KG, int EPL>
-hipError_t launch_router_shared(const DecodeArgs& a, hipStream_t st) {
-    const int n_router_wg = (a.E + 3) / 4;
-    const int shared_items = a.S * (a.I / GateUpShape<KG>::R);
-    const int shared_waves = shared_items < 512 ? shared_items : 512;
-    const int n_shared_wg = a.S > 0 ? (shared_waves + 3) / 4 : 0;
-    hipLaunchKernelGGL((router_shared_kernel<KG, EPL>), dim3(n_router_wg + n_shared_wg), dim3(256), 0, st, a,
-                       n_router_wg, n_shared_wg);
+template <int KG>
+hipError_t launch_router(const DecodeArgs& a, hipStream_t st) {
+    hipLaunchKernelGGL((router_kernel<KG>), dim3((a.E + 3) / 4), dim3(256), 0, st, a);
     return hipGetLastError();
 }
 
-template <int KG>
+template <int KG, int EPL>
 hipError_t launch_gateup(const DecodeArgs& a, hipStream_t st) {
-    const int n_slots = a.n_slot_list > 0 ? a.n_slot_list : a.K;
-    const int items = n_slots * (a.I / GateUpShape<KG>::R);
-    const int waves = items < 2048 ? items : 2048;
-    hipLaunchKernelGGL((gateup_kernel<KG>), dim3((waves + 3) / 4), dim3(256), 0, st, a);
+    const int per_slot = a.I / GateUpShape<KG>::R;
+    const int n_slots = (a.use_slot_list ? a.n_slot_list : a.K) + (a.with_shared ? a.S : 0);
+    if (n_slots == 0) return hipSuccess;
+    const int items = n_slots * per_slot;
+    // at least one round of kGateUpItemsPerRound items per wave, at most
+    // 2048 waves (8 per CU), at least 256 waves when there are enough items
+    int waves = (items + kGateUpItemsPerRound - 1) / kGateUpItemsPerRound;
+    if (waves < 256) waves = items < 256 ? items : 256;
+    if (waves > 2048) waves = 2048;
+    waves = (waves + 3) / 4 * 4;
+    const int n_shared_items = a.with_shared ? a.S * per_slot : 0;
+    if (n_shared_items >= waves)
+        hipLaunchKernelGGL((gateup_kernel<KG, EPL, true>), dim3(waves / 4), dim3(256), 0, st, a);
+    else
+        hipLaunchKernelGGL((gateup_kernel<KG, EPL, false>), dim3(waves / 4), dim3(256), 0, st, a);
     return hipGetLastError();
+}
+
+template <int KG, int NLD>
+hipError_t launch_down_nl(const DecodeArgs& a, hipStream_t st) {
+    using S = DownShape<KG, NLD>;
+    if constexpr (ilog2(pow2_at_least(S::NL + (kDownSharedSteps < S::NL ? kDownSharedSteps : S::NL))) <= S::B) {
+        const int grid = a.H / S::R;
+        hipLaunchKernelGGL((down_combine_kernel<KG, NLD>), dim3(grid), dim3(a.K * 64), 0, st, a);
+        return hipGetLastError();
+    } else {
+        return hipErrorInvalidValue;  // never chosen by down_rows
+    }
 }
 
 template <int KG>
 hipError_t launch_down(const DecodeArgs& a, hipStream_t st) {
-    const int nw = a.K + a.S;
-    const int grid = a.H / DownShape<KG>::R;
-    if (nw <= 9)
-        hipLaunchKernelGGL((down_combine_kernel<KG, 9>), dim3(grid), dim3(nw * 64), 0, st, a);
-    else
-        hipLaunchKernelGGL((down_combine_kernel<KG, 16>), dim3(grid), dim3(nw * 64), 0, st, a);
-    return hipGetLastError();
+    const int nl = down_rows(a.H, KG, a.K) / rows_per_load(KG);
+    switch (nl) {
+        case 1: return launch_down_nl<KG, 1>(a, st);
+        case 2: return launch_down_nl<KG, 2>(a, st);
+        case 4: return launch_down_nl<KG, 4>(a, st);
+        case 8: return launch_down_nl<KG, 8>(a, st);
+        case 16: return launch_down_nl<KG, 16>(a, st);
+        case 24: return launch_down_nl<KG, 24>(a, st);
+        case 32: return launch_down_nl<KG, 32>(a, st);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 template <int KG>
-hipError_t router_dispatch_epl(const DecodeArgs& a, hipStream_t st) {
-    if (a.E <= 64) return launch_router_shared<KG, 1>(a, st);
-    if (a.E <= 128) return launch_router_shared<KG, 2>(a, st);
-    return launch_router_shared<KG, 4>(a, st);
+hipError_t gateup_dispatch_epl(const DecodeArgs& a, hipStream_t st) {
+    if (a.E <= 64) return launch_gateup<KG, 1>(a, st);
+    if (a.E <= 128) return launch_gateup<KG, 2>(a, st);
+    return launch_gateup<KG, 4>(a, st);
 }
 
 }  // namespace
 
 // Kernels are instantiated for H/32 in {8,16,32,64,128,192,256} and
 // I/32 in {4,8,16,32,64,128}.
-hipError_t decode_router_and_shared(const DecodeArgs& a, hipStream_t st) {
+hipError_t decode_router(const DecodeArgs& a, hipStream_t st) {
     switch (a.H / 32) {
-        case 8: return router_dispatch_epl<8>(a, st);
-        case 16: return router_dispatch_epl<16>(a, st);
-        case 32: return router_dispatch_epl<32>(a, st);
-        case 64: return router_dispatch_epl<64>(a, st);
-        case 128: return router_dispatch_epl<128>(a, st);
-        case 192: return router_dispatch_epl<192>(a, st);
-        case 256: return router_dispatch_epl<256>(a, st);
+        case 8: return launch_router<8>(a, st);
+        case 16: return launch_router<16>(a, st);
+        case 32: return launch_router<32>(a, st);
+        case 64: return launch_router<64>(a, st);
+        case 128: return launch_router<128>(a, st);
+        case 192: return launch_router<192>(a, st);
+        case 256: return launch_router<256>(a, st);
         default: return hipErrorInvalidValue;
     }
 }
 
+hipError_t decode_topk(const DecodeArgs& a, hipStream_t st) {
+    if (a.E <= 64)
+        hipLaunchKernelGGL((topk_kernel<1>), dim3(1), dim3(64), 0, st, a);
+    else if (a.E <= 128)
+        hipLaunchKernelGGL((topk_kernel<2>), dim3(1), dim3(64), 0, st, a);
+    else
+        hipLaunchKernelGGL((topk_kernel<4>), dim3(1), dim3(64), 0, st, a);
+    return hipGetLastError();
+}
+
 hipError_t decode_routed_gateup(const DecodeArgs& a, hipStream_t st) {
     switch (a.H / 32) {
-        case 8: return launch_gateup<8>(a, st);
-        case 16: return launch_gateup<16>(a, st);
-        case 32: return launch_gateup<32>(a, st);
-        case 64: return launch_gateup<64>(a, st);
-        case 128: return launch_gateup<128>(a, st);
-        case 192: return launch_gateup<192>(a, st);
-        case 256: return launch_gateup<256>(a, st);
+        case 8: return gateup_dispatch_epl<8>(a, st);
+        case 16: return gateup_dispatch_epl<16>(a, st);
+        case 32: return gateup_dispatch_epl<32>(a, st);
+        case 64: return gateup_dispatch_epl<64>(a, st);
+        case 128: return gateup_dispatch_epl<128>(a, st);
+        case 192: return gateup_dispatch_epl<192>(a, st);
+        case 256: return gateup_dispatch_epl<256>(a, st);
         default: return hipErrorInvalidValue;
     }
 }
@@ -660,12 +1008,12 @@ hipError_t decode_down_combine(const DecodeArgs& a, hipStream_t st) {
     }
 }
 
-bool decode_shape_supported(int hidden, int inter) {
+bool decode_shape_supported(int hidden, int inter, int top_k, int n_shared) {
     const int kh = hidden / 32, ki = inter / 32;
     const bool h_ok = kh == 8 || kh == 16 || kh == 32 || kh == 64 || kh == 128 || kh == 192 || kh == 256;
     const bool i_ok = ki == 4 || ki == 8 || ki == 16 || ki == 32 || ki == 64 || ki == 128;
-    return h_ok && i_ok && hidden % 32 == 0 && inter % 32 == 0 && hidden % down_rows(ki) == 0 &&
-           inter % gateup_rows(kh) == 0;
+    return h_ok && i_ok && hidden % 256 == 0 && hidden % down_rows(hidden, ki, top_k) == 0 &&
+           inter % gateup_rows(kh) == 0 && top_k <= 8;
 }
 
 }  // namespace moe

@@ -8,14 +8,19 @@
 
 #include "../../include/moe.h"
 #include "moe_kernels.h"
+#include "moe_layout.h"
 
 namespace moe {
 
 struct WorkspaceLayout {
     size_t table = 0;          // [E] device blob pointers of the routed experts
-    size_t control = 0;        // tickets (must start at zero)
+    size_t control = 0;        // control words (cleared when bound)
     size_t control_bytes = 0;
-    size_t logits = 0;         // [max_T][E]
+    size_t s = 0;              // [E] router affinities of the token in flight
+    size_t sb = 0;             // [E] biased scores
+    size_t xpairs = 0;         // activation pairs of the token in flight
+    size_t kx = 0;             // their scaling exponent
+    size_t slot_blobs = 0;     // [16] blobs of the routed slots of the token in flight
     size_t ids = 0;            // [max_T][K] when the caller passes no ids buffer
     size_t w = 0;              // [max_T][K]
     size_t h = 0;              // [K + S][I]

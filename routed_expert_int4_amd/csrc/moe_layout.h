@@ -6,9 +6,10 @@
 //       the public row-major bytes with every nibble stored as q + 8
 //       (offset binary), so a kernel can place a nibble straight into the
 //       mantissa of an fp16 constant and subtract the offset exactly;
-//   gate scales, up scales, down scales (fp16 bits)
-//       permuted so that each lane of a wave finds the scales it needs for
-//       one work item in consecutive bytes (see scale_index).
+//   gate and up scales (interleaved per block of rows), down scales
+//       (fp16 bits), permuted so that each lane of a wave finds the scales it
+//       needs for one work item in consecutive bytes (see scale_index and
+//       gateup_scale_index).
 // The blob is exactly as large as the public layout.
 #pragma once
 
@@ -20,12 +21,9 @@
 namespace moe {
 
 constexpr int kWave = 64;
-// Rows of the down projection per workgroup (and per scale pack) when a row
-// fits in one wave load or more.
-constexpr int kDownRowsBase = 16;
-// Rows of gate (and of up) per gate/up work item when a row fits in one wave
-// load or more.
-constexpr int kGateUpRowsBase = 4;
+// Rows of gate (and of up) per gate/up work item when a row fits in one
+// wave load or more.
+constexpr int kGateUpRowsBase = 1;
 
 // A wave load covers 64 lanes x 16 bytes = 64 scale groups (32 codes each).
 // A matrix with kg groups per row needs rows_per_load rows per wave load when
@@ -35,8 +33,35 @@ __host__ __device__ constexpr int chunks_per_lane(int kg) { return kg >= kWave ?
 __host__ __device__ constexpr int gateup_rows(int kg_h) {
     return rows_per_load(kg_h) > kGateUpRowsBase ? rows_per_load(kg_h) : kGateUpRowsBase;
 }
-__host__ __device__ constexpr int down_rows(int kg_i) {
-    return rows_per_load(kg_i) > kDownRowsBase ? rows_per_load(kg_i) : kDownRowsBase;
+// Wave-load steps a down-projection workgroup may take per row slot; the
+// down kernel is instantiated for each of these counts.
+__host__ __device__ constexpr int down_step_option(int i) {
+    return i == 0 ? 32 : i == 1 ? 24 : i == 2 ? 16 : i == 3 ? 8 : i == 4 ? 4 : i == 5 ? 2 : 1;
+}
+// Shared-expert load steps a down-projection wave takes at most (the shared
+// expert's rows of a block are split over the routed slots' waves).
+constexpr int kDownSharedSteps = 4;
+
+__host__ __device__ constexpr int pow2_at_least(int v) { return v <= 1 ? 1 : 2 * pow2_at_least((v + 1) / 2); }
+
+// Rows per down-projection workgroup: about hidden/256 (so one round of
+// workgroups covers the 256 CUs), a multiple of rows_per_load(inter/32) that
+// divides hidden, with a step count s from down_step_option such that the
+// shared expert's s steps split over top_k waves give each at most
+// kDownSharedSteps, and s + kDownSharedSteps row partials, rounded up to a
+// power of two, fit the lanes that share a row (min(inter/32, 64)).
+__host__ __device__ inline int down_rows(int hidden, int kg_i, int top_k) {
+    const int rpl = rows_per_load(kg_i);
+    const int lanes_per_row = kg_i < kWave ? kg_i : kWave;
+    const int target = hidden / 256 > rpl ? hidden / 256 : rpl;
+    for (int i = 0; i < 7; ++i) {
+        const int steps = down_step_option(i);
+        const int r = steps * rpl;
+        if (r <= target && hidden % r == 0 && (steps + top_k - 1) / top_k <= kDownSharedSteps &&
+            pow2_at_least(steps + kDownSharedSteps) <= lanes_per_row)
+            return r;
+    }
+    return rpl;
 }
 
 // Position of the scale of (row r, group g) in a packed scale array of a
@@ -49,9 +74,19 @@ __host__ __device__ inline size_t scale_index(int r, int g, int kg, int p) {
     return ((size_t)(r / p) * kg + g) * p + (size_t)(i % rpl) * (p / rpl) + i / rpl;
 }
 
+// Gate (m = 0) and up (m = 1) scales share one array: for each block of p
+// rows and each group, the p gate scales then the p up scales, each in the
+// order of scale_index, so a lane that visits one row per load finds the
+// gate and up scales of its rows in one contiguous run.
+__host__ __device__ inline size_t gateup_scale_index(int r, int g, int m, int kg, int p) {
+    const int rpl = rows_per_load(kg);
+    const int i = r % p;
+    return (((size_t)(r / p) * kg + g) * 2 + m) * p + (size_t)(i % rpl) * (p / rpl) + i / rpl;
+}
+
 struct BlobLayout {
     size_t gate_q, up_q, down_q;  // byte offsets of the code arrays
-    size_t gate_s, up_s, down_s;  // byte offsets of the scale arrays
+    size_t gu_s, down_s;          // byte offsets of the scale arrays
     size_t total;
 };
 
@@ -62,8 +97,7 @@ __host__ __device__ inline BlobLayout blob_layout(int hidden, int inter) {
     L.gate_q = 0;
     L.up_q = codes;
     L.down_q = 2 * codes;
-    L.gate_s = 3 * codes;
-    L.up_s = 3 * codes + scales;
+    L.gu_s = 3 * codes;
     L.down_s = 3 * codes + 2 * scales;
     L.total = 3 * codes + 3 * scales;
     return L;

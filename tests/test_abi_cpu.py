@@ -67,11 +67,12 @@ def test_pack_keeps_codes_and_permutes_scales():
     np.testing.assert_array_equal(blob[:n], gq.ravel() ^ 0x88)
     np.testing.assert_array_equal(blob[n:2 * n], uq.ravel() ^ 0x88)
     np.testing.assert_array_equal(blob[2 * n:3 * n], dq.ravel() ^ 0x88)
-    # scales: each matrix's scales are a permutation of the public ones
+    # scales: gate and up scales (interleaved) are a permutation of the
+    # public ones, and so are the down scales
     sc = blob[3 * n:].view(np.uint16)
     m = sc.size // 3
-    for part, src in zip((sc[:m], sc[m:2 * m], sc[2 * m:]), (gs, us, ds)):
-        np.testing.assert_array_equal(np.sort(part), np.sort(src.ravel()))
+    np.testing.assert_array_equal(np.sort(sc[:2 * m]), np.sort(np.concatenate([gs.ravel(), us.ravel()])))
+    np.testing.assert_array_equal(np.sort(sc[2 * m:]), np.sort(ds.ravel()))
 
 
 def test_pack_rejects_null():

@@ -30,9 +30,22 @@ def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "gateup_kernel_glm_decode_traffic.md")
+KERNEL_SOURCES = [os.path.join(ROOT, "routed_expert_int4_amd", "csrc", f)
+                  for f in ("moe_decode.hip", "moe_kernels.h", "moe_layout.h")]
+
+
 def algorithmic_bytes(cfg):
-    """Bytes each stage must read at least once per token (batch 1)."""
+    """Bytes each stage must move at least once per token (batch 1).
+
+    Weights dominate: gate + up codes and scales of the 8 routed experts and
+    the shared expert for the gate/up launch, their down codes and scales
+    for the down launch, the fp32 router matrix for the router launch.  The
+    activations (bf16 x, fp32 h and y) are counted where a launch reads or
+    writes them.
+    """
     eb = cfg.expert_bytes()
+    n = cfg.top_k + cfg.n_shared
     gu = 2 * (cfg.hidden * cfg.inter // 2 + cfg.inter * (cfg.hidden // 32) * 2)  # gate + up, codes + scales
     dn = cfg.hidden * cfg.inter // 2 + cfg.hidden * (cfg.inter // 32) * 2
     router = cfg.n_experts * cfg.hidden * 4 + cfg.n_experts * 4
@@ -40,11 +53,40 @@ def algorithmic_bytes(cfg):
     return {
         "expert": eb,
         "routed_per_token": cfg.top_k * eb,
-        "layer_per_token": router + (cfg.top_k + cfg.n_shared) * eb + io,
-        "gateup_launch": cfg.top_k * gu,
-        "down_launch": (cfg.top_k + cfg.n_shared) * dn,
-        "router_shared_launch": router + cfg.n_shared * gu,
+        "layer_per_token": router + n * eb + io,
+        "router_launch": router + cfg.hidden * 2,
+        "gateup_launch": n * gu,
+        "down_launch": n * dn + n * cfg.inter * 4 + cfg.hidden * 4,
     }
+
+
+def source_digest() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per gate/up launch from the committed rocprofv3 counter record.
+
+    The record holds FETCH_SIZE and WRITE_SIZE per dispatch of the gate/up
+    kernel, each scaled by what the counter reads for a device copy of known
+    size, and the digest of the kernel source they were taken on.  Returns
+    None when there is no record or the kernel source has changed since.
+    """
+    if not os.path.exists(TRAFFIC_RECORD):
+        return None
+    rec = None
+    with open(TRAFFIC_RECORD) as f:
+        for line in f:
+            if line.startswith("traffic-record:"):
+                rec = json.loads(line.split(":", 1)[1])
+    if not rec or rec.get("source_sha256") != source_digest():
+        return None
+    return int(rec["hbm_bytes_per_launch"])
 
 
 def cpu_baseline(weights, x_bits, n_tokens: int, bytes_per_token: int):
@@ -73,7 +115,9 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--tokens", type=int, default=1000, help="independent batch-1 tokens per step")
-    ap.add_argument("--cpu-sample", type=int, default=128, help="tokens timed on the CPU oracle (0: skip)")
+    ap.add_argument("--cpu-sample", type=int, default=640, help="tokens timed on the CPU oracle (0: skip)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run one device copy of 256 MiB (a known-size kernel for HBM counter scaling)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported (this layer's path is "
@@ -99,6 +143,14 @@ def main() -> int:
     ids = torch.empty((args.tokens, cfg.top_k), dtype=torch.int32, device="cuda:0")
     w = torch.empty((args.tokens, cfg.top_k), dtype=torch.float32, device="cuda:0")
     stream = torch.cuda.current_stream()
+    if args.copy_calibration:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     def step():
         B.moe_layer_forward(layer.handle, x, args.tokens, y, ids, w, stream)
@@ -132,8 +184,8 @@ def main() -> int:
     avg_us = [1e3 * kms[k] / max(kn[k], 1) for k in range(3)]
     gateup_gbs = nbytes["gateup_launch"] / (avg_us[1] * 1e-6) / 1e9
     down_gbs = nbytes["down_launch"] / (avg_us[2] * 1e-6) / 1e9
-    rs_gbs = nbytes["router_shared_launch"] / (avg_us[0] * 1e-6) / 1e9
-    log(f"kernel avg us: router+shared {avg_us[0]:.2f} ({rs_gbs:.0f} GB/s), routed gate/up {avg_us[1]:.2f} "
+    router_gbs = nbytes["router_launch"] / (avg_us[0] * 1e-6) / 1e9
+    log(f"kernel avg us: router {avg_us[0]:.2f} ({router_gbs:.0f} GB/s), gate/up {avg_us[1]:.2f} "
         f"({gateup_gbs:.0f} GB/s), down+combine {avg_us[2]:.2f} ({down_gbs:.0f} GB/s)")
 
     # parity spot check of this very run against the oracle (2 tokens)
@@ -173,16 +225,18 @@ def main() -> int:
         "pct_of_hbm_peak": round(100 * routed_gbs / HBM_PEAK_GBS, 2),
         "layer_gbs": round(layer_gbs, 2),
         "bytes_per_token": {"routed": nbytes["routed_per_token"], "layer": nbytes["layer_per_token"]},
-        "kernels_avg_us": {"router_shared": round(avg_us[0], 3), "routed_gateup": round(avg_us[1], 3),
+        "kernels_avg_us": {"router": round(avg_us[0], 3), "gateup_swiglu": round(avg_us[1], 3),
                            "down_combine": round(avg_us[2], 3)},
+        "kernels_gbs": {"router": round(router_gbs, 1), "gateup_swiglu": round(gateup_gbs, 1),
+                        "down_combine": round(down_gbs, 1)},
         "roofline": {
-            "kernel": "routed gate/up + SwiGLU (gateup_kernel<192>)",
+            "kernel": "gate/up + SwiGLU of the 8 routed experts and the shared expert (gateup_kernel<192,4,true>)",
             "bound": "hbm",
             "achieved": round(gateup_gbs, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(gateup_gbs / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(),
             "bytes_per_launch": nbytes["gateup_launch"],
             "avg_launch_us": round(avg_us[1], 3),
         },

@@ -142,14 +142,18 @@ moe_status_t moe_router_topk(moe_layer_t* layer, const uint16_t* d_x, int T, int
 moe_status_t moe_layer_forward(moe_layer_t* layer, const uint16_t* d_x, int T, float* d_y, int32_t* d_ids,
                                float* d_w, void* stream);
 
-/* moe_layer_profile: when enable != 0, moe_layer_forward records HIP events
- * around each of its kernel launches (on the call's stream) until profiling
- * is disabled.  moe_layer_profile_read synchronises on the recorded events
- * and returns, per kernel kind (0 router + shared expert gate/up, 1 routed
- * gate/up, 2 down + combine), the summed duration in milliseconds and the
+/* moe_layer_profile: when enable != 0, moe_layer_forward times each of its
+ * kernel launches with HIP events on the call's stream until profiling is
+ * disabled: the events are stamped with the kernel's own begin and end
+ * (hipExtLaunchKernelGGL), except for the gate/up step of a layer with an
+ * attached cache, whose events span the top-k launch, the wait for the
+ * routing, the copies' ordering and the gate/up launches.
+ * moe_layer_profile_read synchronises on the recorded events and returns,
+ * per kernel kind (0 router, 1 gate/up + SwiGLU of the shared and routed
+ * experts, 2 down + combine), the summed duration in milliseconds and the
  * number of launches since profiling was enabled; arrays of 3 entries.
- * Profiling adds events between kernels; timings taken with it enabled are
- * per-kernel durations, not end-to-end throughput. */
+ * Timings taken with profiling enabled are per-kernel durations, not
+ * end-to-end throughput. */
 moe_status_t moe_layer_profile(moe_layer_t* layer, int enable);
 moe_status_t moe_layer_profile_read(moe_layer_t* layer, double* total_ms, uint64_t* launches);
 

@@ -98,9 +98,11 @@ def check(code: int) -> None:
 
 
 def _ptr(t) -> int | None:
-    """Raw address of a torch tensor / numpy array (None -> NULL)."""
+    """Raw address of a torch tensor / numpy array / int address (None -> NULL)."""
     if t is None:
         return None
+    if isinstance(t, int):
+        return t
     if isinstance(t, np.ndarray):
         return t.ctypes.data
     return t.data_ptr()
@@ -168,7 +170,7 @@ def moe_layer_profile(layer: int, enable: bool) -> None:
 
 
 def moe_layer_profile_read(layer: int):
-    """-> (total_ms[3], launches[3]) for router+shared, routed gate/up, down+combine."""
+    """-> (total_ms[3], launches[3]) for router, gate/up + SwiGLU, down + combine."""
     ms = (ctypes.c_double * 3)()
     n = (ctypes.c_uint64 * 3)()
     check(lib().moe_layer_profile_read(layer, ms, n))

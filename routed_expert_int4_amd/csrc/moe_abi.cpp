@@ -290,12 +290,15 @@ DecodeArgs decode_args(moe_layer_t* L, const uint16_t* x, int32_t* ids, float* w
     return a;
 }
 
-// Records a start and an end event around a launch when profiling is on.
-// Events come from a pool that grows on demand and is reused after
-// moe_layer_profile resets the marks.
+// Per-launch timing when profiling is on.  In kernel mode the two events are
+// handed to the launch (stamped with the kernel's own begin and end); in
+// span mode they are recorded around whatever is enqueued between the
+// constructor and end().  Events come from a pool that grows on demand and is
+// reused after moe_layer_profile resets the marks.
 class ProfileScope {
 public:
-    ProfileScope(moe_layer* L, int kind, hipStream_t s) : L_(L), s_(s) {
+    enum Mode { kKernel, kSpan };
+    ProfileScope(moe_layer* L, int kind, hipStream_t s, Mode mode) : L_(L), s_(s), mode_(mode) {
         if (!L_->profiling) return;
         while (L_->prof_events.size() < L_->prof_used + 2) {
             hipEvent_t ev;
@@ -304,11 +307,19 @@ public:
         }
         idx_ = (int)L_->prof_used;
         L_->prof_used += 2;
-        (void)hipEventRecord(L_->prof_events[idx_], s_);
+        if (mode_ == kSpan) (void)hipEventRecord(L_->prof_events[idx_], s_);
         L_->prof_marks.emplace_back(kind, idx_);
     }
+    LaunchTiming timing() const {
+        LaunchTiming t;
+        if (idx_ >= 0 && mode_ == kKernel) {
+            t.start = L_->prof_events[idx_];
+            t.stop = L_->prof_events[idx_ + 1];
+        }
+        return t;
+    }
     void end() {
-        if (idx_ >= 0) (void)hipEventRecord(L_->prof_events[idx_ + 1], s_);
+        if (idx_ >= 0 && mode_ == kSpan) (void)hipEventRecord(L_->prof_events[idx_ + 1], s_);
         idx_ = -1;
     }
     ~ProfileScope() { end(); }
@@ -316,6 +327,7 @@ public:
 private:
     moe_layer* L_;
     hipStream_t s_;
+    Mode mode_;
     int idx_ = -1;
 };
 
@@ -364,11 +376,11 @@ moe_status_t moe_layer_forward(moe_layer_t* layer, const uint16_t* d_x, int T, f
     for (int t = 0; t < T; ++t) {
         DecodeArgs a = decode_args(layer, d_x + (size_t)t * c.hidden, ids_base + (size_t)t * c.top_k,
                                    w_base + (size_t)t * c.top_k, d_y + (size_t)t * c.hidden);
-        ProfileScope p0(layer, 0, s);
-        hipError_t e = decode_router(a, s);
+        ProfileScope p0(layer, 0, s, ProfileScope::kKernel);
+        hipError_t e = decode_router(a, s, p0.timing());
         if (e != hipSuccess) return hip_fail(e, "router kernel launch");
         p0.end();
-        ProfileScope p1(layer, 1, s);
+        ProfileScope p1(layer, 1, s, layer->cache ? ProfileScope::kSpan : ProfileScope::kKernel);
         if (layer->cache) {
             // the host needs the routing: a top-k launch, then the cache
             // resolves it, copies missing experts and enqueues the routed
@@ -378,12 +390,12 @@ moe_status_t moe_layer_forward(moe_layer_t* layer, const uint16_t* d_x, int T, f
             st = cache_prepare_token(layer, a, s);
             if (st != MOE_OK) return st;
         } else {
-            e = decode_routed_gateup(a, s);
+            e = decode_routed_gateup(a, s, p1.timing());
             if (e != hipSuccess) return hip_fail(e, "gate/up kernel launch");
         }
         p1.end();
-        ProfileScope p2(layer, 2, s);
-        e = decode_down_combine(a, s);
+        ProfileScope p2(layer, 2, s, ProfileScope::kKernel);
+        e = decode_down_combine(a, s, p2.timing());
         if (e != hipSuccess) return hip_fail(e, "down/combine kernel launch");
         p2.end();
         if (layer->cache) {

@@ -28,6 +28,7 @@
 // Activations are scaled by a power of two before the fp16 conversion so
 // that any finite bf16 input keeps 11 significant bits; the intermediate h
 // of the down projection is split into fp16 hi + lo parts (about 22 bits).
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -896,14 +897,26 @@ __global__ void __launch_bounds__(512) down_combine_kernel(DecodeArgs a) {
 }
 
 // ---------------------------------------------------------------- launchers
-template <int KG>
-hipError_t launch_router(const DecodeArgs& a, hipStream_t st) {
-    hipLaunchKernelGGL((router_kernel<KG>), dim3((a.E + 3) / 4), dim3(256), 0, st, a);
+// With timing events the launch goes through hipExtLaunchKernelGGL, which
+// stamps the events with the kernel's own start and end (no gap from the
+// enqueue of separate event records).
+template <typename K>
+hipError_t launch_kernel(K kernel, dim3 grid, dim3 block, hipStream_t st, const LaunchTiming& tm,
+                         const DecodeArgs& a) {
+    if (tm.start)
+        hipExtLaunchKernelGGL(kernel, grid, block, 0, st, tm.start, tm.stop, 0, a);
+    else
+        hipLaunchKernelGGL(kernel, grid, block, 0, st, a);
     return hipGetLastError();
 }
 
+template <int KG>
+hipError_t launch_router(const DecodeArgs& a, hipStream_t st, const LaunchTiming& tm) {
+    return launch_kernel(router_kernel<KG>, dim3((a.E + 3) / 4), dim3(256), st, tm, a);
+}
+
 template <int KG, int EPL>
-hipError_t launch_gateup(const DecodeArgs& a, hipStream_t st) {
+hipError_t launch_gateup(const DecodeArgs& a, hipStream_t st, const LaunchTiming& tm) {
     const int per_slot = a.I / GateUpShape<KG>::R;
     const int n_slots = (a.use_slot_list ? a.n_slot_list : a.K) + (a.with_shared ? a.S : 0);
     if (n_slots == 0) return hipSuccess;
@@ -916,94 +929,91 @@ hipError_t launch_gateup(const DecodeArgs& a, hipStream_t st) {
     waves = (waves + 3) / 4 * 4;
     const int n_shared_items = a.with_shared ? a.S * per_slot : 0;
     if (n_shared_items >= waves)
-        hipLaunchKernelGGL((gateup_kernel<KG, EPL, true>), dim3(waves / 4), dim3(256), 0, st, a);
+        return launch_kernel(gateup_kernel<KG, EPL, true>, dim3(waves / 4), dim3(256), st, tm, a);
     else
-        hipLaunchKernelGGL((gateup_kernel<KG, EPL, false>), dim3(waves / 4), dim3(256), 0, st, a);
-    return hipGetLastError();
+        return launch_kernel(gateup_kernel<KG, EPL, false>, dim3(waves / 4), dim3(256), st, tm, a);
 }
 
 template <int KG, int NLD>
-hipError_t launch_down_nl(const DecodeArgs& a, hipStream_t st) {
+hipError_t launch_down_nl(const DecodeArgs& a, hipStream_t st, const LaunchTiming& tm) {
     using S = DownShape<KG, NLD>;
     if constexpr (ilog2(pow2_at_least(S::NL + (kDownSharedSteps < S::NL ? kDownSharedSteps : S::NL))) <= S::B) {
         const int grid = a.H / S::R;
-        hipLaunchKernelGGL((down_combine_kernel<KG, NLD>), dim3(grid), dim3(a.K * 64), 0, st, a);
-        return hipGetLastError();
+        return launch_kernel(down_combine_kernel<KG, NLD>, dim3(grid), dim3(a.K * 64), st, tm, a);
     } else {
         return hipErrorInvalidValue;  // never chosen by down_rows
     }
 }
 
 template <int KG>
-hipError_t launch_down(const DecodeArgs& a, hipStream_t st) {
+hipError_t launch_down(const DecodeArgs& a, hipStream_t st, const LaunchTiming& tm) {
     const int nl = down_rows(a.H, KG, a.K) / rows_per_load(KG);
     switch (nl) {
-        case 1: return launch_down_nl<KG, 1>(a, st);
-        case 2: return launch_down_nl<KG, 2>(a, st);
-        case 4: return launch_down_nl<KG, 4>(a, st);
-        case 8: return launch_down_nl<KG, 8>(a, st);
-        case 16: return launch_down_nl<KG, 16>(a, st);
-        case 24: return launch_down_nl<KG, 24>(a, st);
-        case 32: return launch_down_nl<KG, 32>(a, st);
+        case 1: return launch_down_nl<KG, 1>(a, st, tm);
+        case 2: return launch_down_nl<KG, 2>(a, st, tm);
+        case 4: return launch_down_nl<KG, 4>(a, st, tm);
+        case 8: return launch_down_nl<KG, 8>(a, st, tm);
+        case 16: return launch_down_nl<KG, 16>(a, st, tm);
+        case 24: return launch_down_nl<KG, 24>(a, st, tm);
+        case 32: return launch_down_nl<KG, 32>(a, st, tm);
         default: return hipErrorInvalidValue;
     }
 }
 
 template <int KG>
-hipError_t gateup_dispatch_epl(const DecodeArgs& a, hipStream_t st) {
-    if (a.E <= 64) return launch_gateup<KG, 1>(a, st);
-    if (a.E <= 128) return launch_gateup<KG, 2>(a, st);
-    return launch_gateup<KG, 4>(a, st);
+hipError_t gateup_dispatch_epl(const DecodeArgs& a, hipStream_t st, const LaunchTiming& tm) {
+    if (a.E <= 64) return launch_gateup<KG, 1>(a, st, tm);
+    if (a.E <= 128) return launch_gateup<KG, 2>(a, st, tm);
+    return launch_gateup<KG, 4>(a, st, tm);
 }
 
 }  // namespace
 
 // Kernels are instantiated for H/32 in {8,16,32,64,128,192,256} and
 // I/32 in {4,8,16,32,64,128}.
-hipError_t decode_router(const DecodeArgs& a, hipStream_t st) {
+hipError_t decode_router(const DecodeArgs& a, hipStream_t st, const LaunchTiming& tm) {
     switch (a.H / 32) {
-        case 8: return launch_router<8>(a, st);
-        case 16: return launch_router<16>(a, st);
-        case 32: return launch_router<32>(a, st);
-        case 64: return launch_router<64>(a, st);
-        case 128: return launch_router<128>(a, st);
-        case 192: return launch_router<192>(a, st);
-        case 256: return launch_router<256>(a, st);
+        case 8: return launch_router<8>(a, st, tm);
+        case 16: return launch_router<16>(a, st, tm);
+        case 32: return launch_router<32>(a, st, tm);
+        case 64: return launch_router<64>(a, st, tm);
+        case 128: return launch_router<128>(a, st, tm);
+        case 192: return launch_router<192>(a, st, tm);
+        case 256: return launch_router<256>(a, st, tm);
         default: return hipErrorInvalidValue;
     }
 }
 
-hipError_t decode_topk(const DecodeArgs& a, hipStream_t st) {
+hipError_t decode_topk(const DecodeArgs& a, hipStream_t st, const LaunchTiming& tm) {
     if (a.E <= 64)
-        hipLaunchKernelGGL((topk_kernel<1>), dim3(1), dim3(64), 0, st, a);
+        return launch_kernel(topk_kernel<1>, dim3(1), dim3(64), st, tm, a);
     else if (a.E <= 128)
-        hipLaunchKernelGGL((topk_kernel<2>), dim3(1), dim3(64), 0, st, a);
+        return launch_kernel(topk_kernel<2>, dim3(1), dim3(64), st, tm, a);
     else
-        hipLaunchKernelGGL((topk_kernel<4>), dim3(1), dim3(64), 0, st, a);
-    return hipGetLastError();
+        return launch_kernel(topk_kernel<4>, dim3(1), dim3(64), st, tm, a);
 }
 
-hipError_t decode_routed_gateup(const DecodeArgs& a, hipStream_t st) {
+hipError_t decode_routed_gateup(const DecodeArgs& a, hipStream_t st, const LaunchTiming& tm) {
     switch (a.H / 32) {
-        case 8: return gateup_dispatch_epl<8>(a, st);
-        case 16: return gateup_dispatch_epl<16>(a, st);
-        case 32: return gateup_dispatch_epl<32>(a, st);
-        case 64: return gateup_dispatch_epl<64>(a, st);
-        case 128: return gateup_dispatch_epl<128>(a, st);
-        case 192: return gateup_dispatch_epl<192>(a, st);
-        case 256: return gateup_dispatch_epl<256>(a, st);
+        case 8: return gateup_dispatch_epl<8>(a, st, tm);
+        case 16: return gateup_dispatch_epl<16>(a, st, tm);
+        case 32: return gateup_dispatch_epl<32>(a, st, tm);
+        case 64: return gateup_dispatch_epl<64>(a, st, tm);
+        case 128: return gateup_dispatch_epl<128>(a, st, tm);
+        case 192: return gateup_dispatch_epl<192>(a, st, tm);
+        case 256: return gateup_dispatch_epl<256>(a, st, tm);
         default: return hipErrorInvalidValue;
     }
 }
 
-hipError_t decode_down_combine(const DecodeArgs& a, hipStream_t st) {
+hipError_t decode_down_combine(const DecodeArgs& a, hipStream_t st, const LaunchTiming& tm) {
     switch (a.I / 32) {
-        case 4: return launch_down<4>(a, st);
-        case 8: return launch_down<8>(a, st);
-        case 16: return launch_down<16>(a, st);
-        case 32: return launch_down<32>(a, st);
-        case 64: return launch_down<64>(a, st);
-        case 128: return launch_down<128>(a, st);
+        case 4: return launch_down<4>(a, st, tm);
+        case 8: return launch_down<8>(a, st, tm);
+        case 16: return launch_down<16>(a, st, tm);
+        case 32: return launch_down<32>(a, st, tm);
+        case 64: return launch_down<64>(a, st, tm);
+        case 128: return launch_down<128>(a, st, tm);
         default: return hipErrorInvalidValue;
     }
 }

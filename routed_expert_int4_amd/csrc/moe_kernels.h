@@ -40,17 +40,24 @@ struct DecodeArgs {
     int with_shared;
 };
 
+// Optional timing of one launch: when start is set the launch stamps start
+// and stop with the kernel's own begin and end.
+struct LaunchTiming {
+    hipEvent_t start = nullptr;
+    hipEvent_t stop = nullptr;
+};
+
 // Router logits -> s, sb; activation pairs.
-hipError_t decode_router(const DecodeArgs& a, hipStream_t st);
+hipError_t decode_router(const DecodeArgs& a, hipStream_t st, const LaunchTiming& tm = {});
 // Group-limited top-k from s, sb on one wave -> ids, w.
-hipError_t decode_topk(const DecodeArgs& a, hipStream_t st);
+hipError_t decode_topk(const DecodeArgs& a, hipStream_t st, const LaunchTiming& tm = {});
 // Gate/up + SwiGLU of the shared expert (with_shared) and the routed
 // experts.  In table mode every wave also derives the routing itself from
 // s, sb (and the first wave writes ids, w and slot_blobs), so no separate
 // top-k launch is needed.
-hipError_t decode_routed_gateup(const DecodeArgs& a, hipStream_t st);
+hipError_t decode_routed_gateup(const DecodeArgs& a, hipStream_t st, const LaunchTiming& tm = {});
 // Down projection of every slot and the weighted combine into y.
-hipError_t decode_down_combine(const DecodeArgs& a, hipStream_t st);
+hipError_t decode_down_combine(const DecodeArgs& a, hipStream_t st, const LaunchTiming& tm = {});
 bool decode_shape_supported(int hidden, int inter, int top_k, int n_shared);
 
 }  // namespace moe

@@ -7,13 +7,83 @@ import numpy as np
 from . import binding as B
 
 
+def pack_expert(weights, e: int, out: np.ndarray | None = None) -> np.ndarray:
+    """Packed device blob of expert e (routed 0..E-1, shared at E..)."""
+    nb = B.moe_expert_bytes(weights.cfg)
+    if out is None:
+        out = np.empty(nb, np.uint8)
+    B.moe_expert_pack(weights.cfg, *weights.expert_arrays(e), out)
+    return out
+
+
+class HostExpertStore:
+    """Packed blobs of one layer's routed experts in pinned host memory
+    [E, expert_bytes], the store an expert cache copies from."""
+
+    def __init__(self, weights):
+        import torch
+
+        cfg = weights.cfg
+        self.nb = nb = B.moe_expert_bytes(cfg)
+        self.blobs = torch.empty((cfg.n_experts, nb), dtype=torch.uint8, pin_memory=True)
+        view = self.blobs.numpy()
+        for e in range(cfg.n_experts):
+            pack_expert(weights, e, view[e])
+
+    def ptr(self, e: int) -> int:
+        return self.blobs[e].data_ptr()
+
+
+class ExpertCache:
+    """Device slot pool, copy stream and the library's cache handle for
+    n_layers layers of one shape."""
+
+    def __init__(self, cfg, n_layers: int, slots: int, device: str = "cuda:0"):
+        import torch
+
+        self.cfg = cfg
+        self.n_layers, self.slots = n_layers, slots
+        self.nb = nb = B.moe_expert_bytes(cfg)
+        self.pool = torch.empty(n_layers * slots * nb, dtype=torch.uint8, device=device)
+        self.copy_stream = torch.cuda.Stream(device=device)
+        self.handle = B.expert_cache_create(cfg, n_layers, slots, self.pool, self.pool.numel(), self.copy_stream)
+        self.stores = {}
+
+    def register(self, layer: int, store: HostExpertStore) -> None:
+        for e in range(self.cfg.n_experts):
+            B.expert_cache_register(self.handle, layer, e, store.ptr(e), store.nb)
+        self.stores[layer] = store  # keeps the pinned blobs alive
+
+    def prefetch(self, layer: int, experts) -> None:
+        B.expert_cache_prefetch(self.handle, layer, experts)
+
+    def evict(self, layer: int, expert: int) -> None:
+        B.expert_cache_evict(self.handle, layer, expert)
+
+    def stats(self, layer: int) -> dict:
+        return B.expert_cache_stats(self.handle, layer)
+
+    def close(self) -> None:
+        if getattr(self, "handle", None):
+            B.expert_cache_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
 class DeviceLayer:
-    """One MoE layer with every expert resident in HBM.
+    """One MoE layer on the GPU.
 
-    Expert blobs live in one device tensor [E + S, expert_bytes] (rows stay
-    256-byte aligned because expert_bytes is a multiple of 256)."""
+    With resident=True every expert blob lives in one device tensor
+    [E + S, expert_bytes] (rows stay 256-byte aligned because expert_bytes is
+    a multiple of 256).  With resident=False only the shared expert(s) are
+    uploaded and the routed experts come from an attached ExpertCache."""
 
-    def __init__(self, weights, max_T: int = 1, device: str = "cuda:0"):
+    def __init__(self, weights, max_T: int = 1, device: str = "cuda:0", resident: bool = True):
         import torch
 
         cfg = weights.cfg
@@ -22,22 +92,29 @@ class DeviceLayer:
         self.expert_bytes = nb = B.moe_expert_bytes(cfg)
         if nb == 0:
             raise B.MoeError(B.MOE_EINVAL, B.last_error())
+        first = 0 if resident else cfg.n_experts
         n_all = cfg.n_total_experts
-        self.blobs = torch.empty((n_all, nb), dtype=torch.uint8, device=device)
+        self.blobs = torch.empty((cfg.n_experts if resident else 0) + cfg.n_shared, nb, dtype=torch.uint8,
+                                 device=device)
         host = np.empty(nb, np.uint8)
-        for e in range(n_all):
-            B.moe_expert_pack(cfg, *weights.expert_arrays(e), host)
-            self.blobs[e].copy_(torch.from_numpy(host))
+        for e in range(first, n_all):
+            pack_expert(weights, e, host)
+            self.blobs[e - first].copy_(torch.from_numpy(host))
         self.router_w = torch.from_numpy(np.ascontiguousarray(weights.router_w)).to(device)
         self.bias = torch.from_numpy(np.ascontiguousarray(weights.bias)).to(device)
-        shared = [self.blobs[cfg.n_experts + s] for s in range(cfg.n_shared)]
+        shared = [self.blobs[cfg.n_experts - first + s] for s in range(cfg.n_shared)]
         self.handle = B.moe_layer_create(cfg, self.router_w, self.bias, shared)
         self.max_T = max_T
         self.ws_bytes = B.moe_workspace_bytes(cfg, max_T)
         self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=device)
         torch.cuda.synchronize(device)
         B.moe_layer_set_workspace(self.handle, self.ws, self.ws_bytes, max_T)
-        B.moe_layer_set_experts(self.handle, [self.blobs[e] for e in range(cfg.n_experts)])
+        if resident:
+            B.moe_layer_set_experts(self.handle, [self.blobs[e] for e in range(cfg.n_experts)])
+
+    def attach_cache(self, cache: "ExpertCache", layer_id: int) -> None:
+        B.moe_layer_attach_cache(self.handle, cache.handle, layer_id)
+        self.cache = cache  # the cache outlives the layer's use of it
 
     def close(self):
         if getattr(self, "handle", None):

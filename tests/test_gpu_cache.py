@@ -1,0 +1,149 @@
+"""GPU tests of the HBM expert cache in front of a pinned host store.
+
+The cache follows the per-layer LRU expert cache of the colibri summary
+(fr.news.hada.io topic 31297, "Execution d'un MoE basee sur le streaming
+disque"), with pinned host RAM in place of the disk.  Checked here, through
+the C ABI:
+  * every layer's outputs against the fp64 oracle on the GPU's own input to
+    that layer (a stack of layers chained as in the 12-layer workload:
+    next input = bf16(y / rms(y) + N(0, 0.1) noise));
+  * outputs bit-identical to the same layer with every expert resident (the
+    cache changes where a blob is read from, not the arithmetic);
+  * hit / miss / eviction counts equal to a plain LRU replay of the GPU's
+    routing trace (oracle/lru.py), and h2d_bytes = misses x blob bytes;
+  * copy/compute ordering with the minimum slot count (every token evicts
+    experts the previous token read);
+  * prefetch and evict semantics and their errors.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+from oracle import lru
+from routed_expert_int4_amd import binding as B
+from routed_expert_int4_amd import synth
+from tests.helpers import check_layer
+
+pytestmark = pytest.mark.gpu
+
+CFG = synth.LayerConfig(hidden=1024, inter=256, n_experts=64, n_groups=8, topk_group=4, top_k=6)
+N_LAYERS = 3
+N_TOKENS = 40
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def torch_cuda():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    B.lib()
+    return torch
+
+
+def chain_input(y: np.ndarray, noise: np.ndarray) -> np.ndarray:
+    """Next layer's bf16 input: weightless RMS normalisation of y plus noise."""
+    rms = np.sqrt(np.mean(y.astype(np.float64) ** 2, axis=1, keepdims=True))
+    return synth.round_to_bf16_bits((y / rms + noise).astype(np.float32))
+
+
+def make_stack(torch, slots, n_layers=N_LAYERS, max_T=N_TOKENS):
+    from routed_expert_int4_amd.layer import DeviceLayer, ExpertCache, HostExpertStore
+    cache = ExpertCache(CFG, n_layers, slots)
+    weights, cached, resident = [], [], []
+    for l in range(n_layers):
+        wl = synth.gen_layer(CFG, seed=10 + l)
+        weights.append(wl)
+        cache.register(l, HostExpertStore(wl))
+        lay = DeviceLayer(wl, max_T=max_T, resident=False)
+        lay.attach_cache(cache, l)
+        cached.append(lay)
+        resident.append(DeviceLayer(wl, max_T=max_T))
+    torch.cuda.synchronize()
+    return cache, weights, cached, resident
+
+
+@pytest.mark.parametrize("slots", [16, CFG.top_k])
+def test_cache_stack_parity_and_lru(torch_cuda, slots):
+    torch = torch_cuda
+    from routed_expert_int4_amd.layer import DeviceLayer
+    say(f"[gpu] cache stack: {N_LAYERS} layers, {slots} slots, {N_TOKENS} tokens")
+    cache, weights, cached, resident = make_stack(torch, slots)
+    x_bits = synth.gen_tokens(CFG, N_TOKENS, seed=30)
+    for l in range(N_LAYERS):
+        x = DeviceLayer.to_device_bf16(x_bits)
+        y, ids, w = cached[l].forward(x)
+        y_res, ids_res, w_res = resident[l].forward(x)
+        torch.cuda.synchronize()
+        yh, idh, wh = y.cpu().numpy(), ids.cpu().numpy(), w.cpu().numpy()
+        res = check_layer(weights[l], x_bits, yh, idh, wh)
+        assert torch.equal(ids, ids_res) and torch.equal(w, w_res)
+        assert torch.equal(y, y_res), "cached and resident outputs differ"
+        st = cache.stats(l)
+        hits, misses, evictions = lru.replay(idh, slots)
+        say(f"[gpu] layer {l}: rel err {res['worst_rel']:.3g}, stats {st}, replay {(hits, misses, evictions)}")
+        assert (st["hits"], st["misses"], st["evictions"]) == (hits, misses, evictions)
+        assert st["h2d_bytes"] == misses * cache.nb
+        assert st["prefetches"] == 0
+        x_bits = chain_input(yh, synth.gen_noise(CFG, N_TOKENS, seed=40 + l, std=0.1))
+    for lay in cached + resident:
+        lay.close()
+    cache.close()
+
+
+def test_cache_prefetch_and_evict(torch_cuda):
+    torch = torch_cuda
+    from oracle import oracle
+    from routed_expert_int4_amd.layer import DeviceLayer
+    say("[gpu] cache prefetch/evict")
+    cache, weights, cached, resident = make_stack(torch, slots=8, n_layers=1, max_T=2)
+    x_bits = synth.gen_tokens(CFG, 1, seed=31)
+    ids_ref, _, _ = oracle.route(weights[0], x_bits)
+    need = [int(e) for e in ids_ref[0]]
+    cache.prefetch(0, need)
+    st = cache.stats(0)
+    assert st["prefetches"] == CFG.top_k and st["h2d_bytes"] == CFG.top_k * cache.nb
+    cache.prefetch(0, need)  # resident already: no new copies
+    assert cache.stats(0)["prefetches"] == CFG.top_k
+    x = DeviceLayer.to_device_bf16(x_bits)
+    y, ids, w = cached[0].forward(x)
+    torch.cuda.synchronize()
+    check_layer(weights[0], x_bits, y.cpu().numpy(), ids.cpu().numpy(), w.cpu().numpy())
+    st = cache.stats(0)
+    assert (st["hits"], st["misses"]) == (CFG.top_k, 0)
+    cache.evict(0, need[2])
+    cache.evict(0, need[2])  # not resident any more: no-op
+    assert cache.stats(0)["evictions"] == 1
+    y2, _, _ = cached[0].forward(x)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2)
+    st = cache.stats(0)
+    assert (st["hits"], st["misses"]) == (2 * CFG.top_k - 1, 1)
+    with pytest.raises(B.MoeError) as err:
+        cache.prefetch(0, list(range(9)))
+    assert err.value.code == B.MOE_ENOSLOT
+    with pytest.raises(B.MoeError) as err:
+        cache.prefetch(0, [CFG.n_experts])
+    assert err.value.code == B.MOE_EINVAL
+    with pytest.raises(B.MoeError):
+        cache.evict(0, -1)
+    for lay in cached + resident:
+        lay.close()
+    cache.close()
+
+
+def test_cache_register_errors(torch_cuda):
+    from routed_expert_int4_amd.layer import ExpertCache
+    cache = ExpertCache(CFG, 1, CFG.top_k)
+    buf = np.zeros(16, np.uint8)
+    with pytest.raises(B.MoeError):
+        B.expert_cache_register(cache.handle, 0, 0, buf.ctypes.data, 16)  # wrong size
+    with pytest.raises(B.MoeError):
+        B.expert_cache_register(cache.handle, 1, 0, buf.ctypes.data, cache.nb)  # bad layer
+    with pytest.raises(B.MoeError):
+        B.expert_cache_create(CFG, 1, CFG.top_k - 1, cache.pool, cache.pool.numel(), cache.copy_stream)
+    cache.close()

@@ -5,9 +5,10 @@ Workload: the GLM-5.2-shaped layer (hidden 6144, expert intermediate 2048,
 256 routed experts in 8 groups, top-8 of 4 groups, one shared expert, int4
 codes with fp16 group-32 scales, fp32 router), batch-1 decode of 1,000
 independent tokens (bf16 N(0,1) activations, uniform routing from a N(0,0.01)
-correction bias).  One step = the 1,000 tokens, each a full layer forward
-(router + top-k, 8 routed experts + shared expert, combine), all inputs
-resident in HBM before timing starts.
+correction bias).  One step = the 1,000 tokens, each its own
+moe_layer_forward call with T = 1 (router + top-k, 8 routed experts + shared
+expert, combine), enqueued back to back on one stream, all inputs resident in
+HBM before timing starts.
 
 Prints one JSON line on stdout; progress goes to stderr.
 """
@@ -137,7 +138,7 @@ def main() -> int:
     log("generating the GLM-shaped layer (seed 0) and 1000 tokens (seed 1)")
     weights = synth.gen_layer(cfg, seed=0)
     x_bits = synth.gen_tokens(cfg, args.tokens, seed=1)
-    layer = DeviceLayer(weights, max_T=args.tokens)
+    layer = DeviceLayer(weights, max_T=1)
     x = DeviceLayer.to_device_bf16(x_bits)
     y = torch.empty((args.tokens, cfg.hidden), dtype=torch.float32, device="cuda:0")
     ids = torch.empty((args.tokens, cfg.top_k), dtype=torch.int32, device="cuda:0")
@@ -152,8 +153,17 @@ def main() -> int:
         torch.cuda.synchronize()
         del src, dst
 
+    # one call per token (batch-1 decode): pointers of token t's rows
+    H, k = cfg.hidden, cfg.top_k
+    px, py, pi, pw = x.data_ptr(), y.data_ptr(), ids.data_ptr(), w.data_ptr()
+    st = stream.cuda_stream
+    fwd = B.lib().moe_layer_forward
+
     def step():
-        B.moe_layer_forward(layer.handle, x, args.tokens, y, ids, w, stream)
+        for t in range(args.tokens):
+            rc = fwd(layer.handle, px + 2 * H * t, 1, py + 4 * H * t, pi + 4 * k * t, pw + 4 * k * t, st)
+            if rc != 0:
+                raise B.MoeError(rc, B.last_error())
 
     log(f"warmup {args.warmup} step(s)")
     for _ in range(args.warmup):

@@ -60,6 +60,7 @@ _SIGNATURES = {
     "moe_layer_forward": ([_vp, _vp, _i, _vp, _vp, _vp, _vp], _i),
     "moe_layer_profile": ([_vp, _i], _i),
     "moe_layer_profile_read": ([_vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_uint64)], _i),
+    "moe_dispatch": ([_vp, _vp, _i, _vp, _vp, _vp, _vp, _vp, _vp], _i),
     "expert_cache_create": ([ctypes.POINTER(MoeConfig), _i, _i, _vp, _sz, _vp, ctypes.POINTER(_vp)], _i),
     "expert_cache_register": ([_vp, _i, _i, _vp, _sz], _i),
     "expert_cache_prefetch": ([_vp, _i, _vp, _i], _i),
@@ -163,6 +164,12 @@ def moe_router_topk(layer: int, d_x, T: int, d_ids, d_w, stream=None) -> None:
 def moe_layer_forward(layer: int, d_x, T: int, d_y, d_ids=None, d_w=None, stream=None) -> None:
     check(lib().moe_layer_forward(layer, _ptr(d_x), int(T), _ptr(d_y), _ptr(d_ids), _ptr(d_w),
                                   _stream_handle(stream)))
+
+
+def moe_dispatch(layer: int, d_ids, T: int, d_counts, d_offsets, d_perm, d_distinct, d_n_distinct,
+                 stream=None) -> None:
+    check(lib().moe_dispatch(layer, _ptr(d_ids), int(T), _ptr(d_counts), _ptr(d_offsets), _ptr(d_perm),
+                             _ptr(d_distinct), _ptr(d_n_distinct), _stream_handle(stream)))
 
 
 def moe_layer_profile(layer: int, enable: bool) -> None:

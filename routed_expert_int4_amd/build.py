@@ -8,7 +8,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmoe_int4.so")
-SOURCES = ["moe_decode.hip", "moe_abi.cpp", "moe_cache.cpp"]
+SOURCES = ["moe_decode.hip", "moe_batch.hip", "moe_abi.cpp", "moe_cache.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared", "-Wall",

@@ -57,7 +57,8 @@ moe_status_t validate_supported(const moe_config_t* c) {
     moe_status_t st = validate_config(c);
     if (st != MOE_OK) return st;
     if (c->top_k > 8) return fail(MOE_EUNSUPPORTED, "top_k must be at most 8 (got %d)", c->top_k);
-    if (!decode_shape_supported(c->hidden, c->inter, c->top_k, c->n_shared))
+    if (!decode_shape_supported(c->hidden, c->inter, c->top_k, c->n_shared) ||
+        !batch_shape_supported(c->hidden, c->inter))
         return fail(MOE_EUNSUPPORTED, "no kernel for hidden=%d inter=%d", c->hidden, c->inter);
     if (c->n_experts > 256) return fail(MOE_EUNSUPPORTED, "n_experts > 256");
     const int epl = c->n_experts <= 64 ? 1 : (c->n_experts <= 128 ? 2 : 4);
@@ -96,6 +97,33 @@ WorkspaceLayout workspace_layout(const moe_config_t* c, int max_T) {
     o = align256(o + sizeof(float) * (size_t)max_T * c->top_k);
     W.h = o;
     o = align256(o + sizeof(float) * (size_t)slots * c->inter);
+    if (max_T > 1) {
+        const int tb = max_T < kMaxDispatchEntries / c->top_k ? max_T : kMaxDispatchEntries / c->top_k;
+        const size_t E = (size_t)c->n_experts, H = (size_t)c->hidden, I = (size_t)c->inter;
+        const size_t n = (size_t)tb * c->top_k, P = (size_t)tb * slots;
+        W.batch_tokens = tb;
+        auto take = [&](size_t& field, size_t bytes) {
+            field = o;
+            o = align256(o + bytes);
+        };
+        take(W.b_s, sizeof(float) * tb * E);
+        take(W.b_sb, sizeof(float) * tb * E);
+        take(W.b_xa, 2 * tb * H);
+        take(W.b_kx, sizeof(int) * tb);
+        take(W.b_counts, sizeof(int32_t) * E);
+        take(W.b_offsets, sizeof(int32_t) * (E + 1));
+        take(W.b_perm, sizeof(int32_t) * n);
+        take(W.b_inv, sizeof(int32_t) * n);
+        take(W.b_distinct, sizeof(int32_t) * E);
+        take(W.b_n_distinct, sizeof(int32_t));
+        take(W.b_tiles, sizeof(Tile) * (size_t)batch_max_tiles(tb, c->top_k, c->n_experts, c->n_shared));
+        take(W.b_n_tiles, sizeof(int32_t));
+        take(W.b_h, sizeof(float) * P * I);
+        take(W.b_ha_hi, 2 * P * I);
+        take(W.b_ha_lo, 2 * P * I);
+        take(W.b_kh, sizeof(int) * P);
+        take(W.b_d, sizeof(float) * P * H);
+    }
     W.total = o;
     return W;
 }
@@ -331,6 +359,52 @@ private:
     int idx_ = -1;
 };
 
+// Arguments of one batched launch sequence over n tokens (n <= batch_tokens)
+// starting at x, with outputs at ids/w/y (any may be null for the router-only
+// or dispatch-only uses).
+BatchArgs batch_args(moe_layer_t* L, const uint16_t* x, int n, int32_t* ids, float* w, float* y) {
+    BatchArgs b;
+    const moe_config_t& c = L->cfg;
+    const WorkspaceLayout& W = L->W;
+    uint8_t* ws = L->ws;
+    b.x = x;
+    b.router_w = L->router_w;
+    b.bias = L->bias;
+    b.table = reinterpret_cast<const uint8_t* const*>(ws + W.table);
+    b.shared_blob = c.n_shared > 0 ? L->shared[0] : nullptr;
+    b.s = reinterpret_cast<float*>(ws + W.b_s);
+    b.sb = reinterpret_cast<float*>(ws + W.b_sb);
+    b.xa = reinterpret_cast<uint16_t*>(ws + W.b_xa);
+    b.kx = reinterpret_cast<int*>(ws + W.b_kx);
+    b.ids = ids;
+    b.w = w;
+    b.counts = reinterpret_cast<int32_t*>(ws + W.b_counts);
+    b.offsets = reinterpret_cast<int32_t*>(ws + W.b_offsets);
+    b.perm = reinterpret_cast<int32_t*>(ws + W.b_perm);
+    b.inv = reinterpret_cast<int32_t*>(ws + W.b_inv);
+    b.distinct = reinterpret_cast<int32_t*>(ws + W.b_distinct);
+    b.n_distinct = reinterpret_cast<int32_t*>(ws + W.b_n_distinct);
+    b.tiles = reinterpret_cast<Tile*>(ws + W.b_tiles);
+    b.n_tiles = reinterpret_cast<int32_t*>(ws + W.b_n_tiles);
+    b.h = reinterpret_cast<float*>(ws + W.b_h);
+    b.ha_hi = reinterpret_cast<uint16_t*>(ws + W.b_ha_hi);
+    b.ha_lo = reinterpret_cast<uint16_t*>(ws + W.b_ha_lo);
+    b.kh = reinterpret_cast<int*>(ws + W.b_kh);
+    b.d = reinterpret_cast<float*>(ws + W.b_d);
+    b.y = y;
+    b.T = n;
+    b.H = c.hidden;
+    b.I = c.inter;
+    b.E = c.n_experts;
+    b.G = c.n_groups;
+    b.TG = c.topk_group;
+    b.K = c.top_k;
+    b.S = c.n_shared;
+    b.down_p = down_rows(c.hidden, c.inter / 32, c.top_k);
+    b.rsf = c.routed_scaling_factor;
+    return b;
+}
+
 static moe_status_t check_call(moe_layer_t* L, const uint16_t* d_x, int T, const char* who) {
     if (!L) return fail(MOE_EINVAL, "%s: layer is NULL", who);
     if (T < 0) return fail(MOE_EINVAL, "%s: T < 0", who);
@@ -351,6 +425,18 @@ moe_status_t moe_router_topk(moe_layer_t* layer, const uint16_t* d_x, int T, int
     if (T > 0 && (!d_ids || !d_w)) return fail(MOE_EINVAL, "moe_router_topk: NULL ids or w");
     hipStream_t s = static_cast<hipStream_t>(stream);
     const moe_config_t& c = layer->cfg;
+    if (T > 1) {
+        const int tb = layer->W.batch_tokens;
+        for (int t0 = 0; t0 < T; t0 += tb) {
+            const int n = T - t0 < tb ? T - t0 : tb;
+            BatchArgs b = batch_args(layer, d_x + (size_t)t0 * c.hidden, n, d_ids + (size_t)t0 * c.top_k,
+                                     d_w + (size_t)t0 * c.top_k, nullptr);
+            hipError_t e = batch_router(b, s);
+            if (e == hipSuccess) e = batch_topk(b, false, s);
+            if (e != hipSuccess) return hip_fail(e, "batched router/top-k launch");
+        }
+        return MOE_OK;
+    }
     for (int t = 0; t < T; ++t) {
         DecodeArgs a = decode_args(layer, d_x + (size_t)t * c.hidden, d_ids + (size_t)t * c.top_k,
                                    d_w + (size_t)t * c.top_k, nullptr);
@@ -373,6 +459,32 @@ moe_status_t moe_layer_forward(moe_layer_t* layer, const uint16_t* d_x, int T, f
     const moe_config_t& c = layer->cfg;
     int32_t* ids_base = d_ids ? d_ids : reinterpret_cast<int32_t*>(layer->ws + layer->W.ids);
     float* w_base = d_w ? d_w : reinterpret_cast<float*>(layer->ws + layer->W.w);
+    if (T > 1 && !layer->cache) {
+        // batch union: every distinct expert of a launch sequence is read once
+        const int tb = layer->W.batch_tokens;
+        for (int t0 = 0; t0 < T; t0 += tb) {
+            const int n = T - t0 < tb ? T - t0 : tb;
+            BatchArgs b = batch_args(layer, d_x + (size_t)t0 * c.hidden, n, ids_base + (size_t)t0 * c.top_k,
+                                     w_base + (size_t)t0 * c.top_k, d_y + (size_t)t0 * c.hidden);
+            ProfileScope p0(layer, 0, s, ProfileScope::kSpan);
+            hipError_t e = batch_router(b, s);
+            if (e == hipSuccess) e = batch_topk(b, true, s);
+            if (e == hipSuccess) e = batch_dispatch(b, s);
+            if (e != hipSuccess) return hip_fail(e, "batched routing launch");
+            p0.end();
+            ProfileScope p1(layer, 1, s, ProfileScope::kSpan);
+            e = batch_gateup(b, s);
+            if (e == hipSuccess) e = batch_hprep(b, s);
+            if (e != hipSuccess) return hip_fail(e, "batched gate/up launch");
+            p1.end();
+            ProfileScope p2(layer, 2, s, ProfileScope::kSpan);
+            e = batch_down(b, s);
+            if (e == hipSuccess) e = batch_combine(b, s);
+            if (e != hipSuccess) return hip_fail(e, "batched down/combine launch");
+            p2.end();
+        }
+        return MOE_OK;
+    }
     for (int t = 0; t < T; ++t) {
         DecodeArgs a = decode_args(layer, d_x + (size_t)t * c.hidden, ids_base + (size_t)t * c.top_k,
                                    w_base + (size_t)t * c.top_k, d_y + (size_t)t * c.hidden);
@@ -403,6 +515,28 @@ moe_status_t moe_layer_forward(moe_layer_t* layer, const uint16_t* d_x, int T, f
             if (st != MOE_OK) return st;
         }
     }
+    return MOE_OK;
+}
+
+moe_status_t moe_dispatch(moe_layer_t* layer, const int32_t* d_ids, int T, int32_t* d_counts, int32_t* d_offsets,
+                          int32_t* d_perm, int32_t* d_distinct, int32_t* d_n_distinct, void* stream) {
+    if (!layer) return fail(MOE_EINVAL, "moe_dispatch: layer is NULL");
+    if (T < 0) return fail(MOE_EINVAL, "moe_dispatch: T < 0");
+    if (T == 0) return MOE_OK;
+    if (!d_ids || !d_counts || !d_offsets || !d_perm || !d_distinct || !d_n_distinct)
+        return fail(MOE_EINVAL, "moe_dispatch: NULL argument");
+    if (!layer->ws) return fail(MOE_EINVAL, "moe_dispatch: no workspace bound");
+    if (T > layer->W.batch_tokens)
+        return fail(MOE_EINVAL, "moe_dispatch: T=%d exceeds the workspace's batch of %d tokens", T,
+                    layer->W.batch_tokens);
+    BatchArgs b = batch_args(layer, nullptr, T, const_cast<int32_t*>(d_ids), nullptr, nullptr);
+    b.counts = d_counts;
+    b.offsets = d_offsets;
+    b.perm = d_perm;
+    b.distinct = d_distinct;
+    b.n_distinct = d_n_distinct;
+    hipError_t e = batch_dispatch(b, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "dispatch kernel launch");
     return MOE_OK;
 }
 

@@ -1,0 +1,679 @@
+// Batched kernels (several tokens per call) of the routed int4 MoE layer,
+// gfx950.
+//
+// The batch-union rule of the colibrì summary (fr.news.hada.io topic 31297,
+// "Principales fonctionnalités implémentées": in prefill and in the batched
+// verification forward, each distinct expert of the batch is read once and
+// applied to every position routed to it) on one GPU:
+//   1. router: logits of all tokens, W_r read once per 16 tokens;
+//   2. top-k: group-limited top-k per token (one wave each); the tokens'
+//      activations are converted to scaled fp16 in MFMA operand order;
+//   3. dispatch: one workgroup sorts the T*K (token, slot) entries by
+//      expert then token in LDS, and writes counts, offsets, the permutation
+//      and its inverse, the distinct experts and the tile list (up to 16
+//      entries of one expert per tile; the shared expert's T tokens last);
+//   4. gate/up: grouped int4 GEMM per (tile, 128 rows) on the matrix cores;
+//   5. h prep: h per entry as scaled fp16 hi + lo parts in MFMA order;
+//   6. down: grouped int4 GEMM per (tile, 128 output rows);
+//   7. combine: y = sum_j w_j d_j + d_shared in slot order (no atomics).
+//
+// Grouped GEMM scheme.  v_mfma_f32_16x16x32_f16 with the 16 tokens of a tile
+// as its A rows and 16 weight rows as its B columns; K = 32 is exactly one
+// scale group, so each MFMA's 16x16 result is scaled by the fp16 group scale
+// of its weight row and accumulated in fp32 (the int4 values enter the MFMA
+// exactly as fp16, the scale is applied in fp32: no rounding of weights).
+// A lane of quarter q loads 16 contiguous code bytes (one group of one row);
+// a 4x4 exchange of dwords between the four quarters (permlane32/16 swaps)
+// turns the four loads of a quarter-row into the B fragments of four
+// consecutive groups.  Codes become fp16 through the same mantissa-OR and
+// exact subtraction as in the decode kernels, which orders the 8 values of a
+// fragment as columns (0,4,1,5,2,6,3,7) of its k-block; the activations are
+// stored in that order.  Tokens' activations for a stage of K are staged
+// in LDS (double buffered, one barrier per stage) and read as A fragments.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "moe_device.h"
+#include "moe_kernels.h"
+#include "moe_layout.h"
+
+namespace moe {
+namespace {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kRouterTokens = 16;
+
+__device__ __forceinline__ float bf16_lo(unsigned d) { return __builtin_bit_cast(float, d << 16); }
+__device__ __forceinline__ float bf16_hi(unsigned d) { return __builtin_bit_cast(float, d & 0xFFFF0000u); }
+
+__device__ __forceinline__ unsigned pack_h2(_Float16 lo, _Float16 hi) {
+    return (unsigned)__builtin_bit_cast(unsigned short, lo) | ((unsigned)__builtin_bit_cast(unsigned short, hi) << 16);
+}
+
+// 8 offset-binary codes of one dword (columns 8q..8q+7 of a group, column c
+// at bits 4c) -> fp16 values in fragment order (columns 0,4,1,5,2,6,3,7).
+__device__ __forceinline__ f16x8 codes_to_f16x8(unsigned w) {
+    const f16x2 k_lo = {(_Float16)1032.0f, (_Float16)1032.0f};  // 1024 + 8
+    const f16x2 k_hi = {(_Float16)72.0f, (_Float16)72.0f};      // 64 + 8
+    const unsigned w8 = w >> 8;
+    const f16x2 q0 = as_h2((w & 0x000F000Fu) | 0x64006400u) - k_lo;
+    const f16x2 q1 = as_h2((w & 0x00F000F0u) | 0x54005400u) - k_hi;
+    const f16x2 q2 = as_h2((w8 & 0x000F000Fu) | 0x64006400u) - k_lo;
+    const f16x2 q3 = as_h2((w8 & 0x00F000F0u) | 0x54005400u) - k_hi;
+    const u32x4 v = {__builtin_bit_cast(unsigned, q0), __builtin_bit_cast(unsigned, q1),
+                     __builtin_bit_cast(unsigned, q2), __builtin_bit_cast(unsigned, q3)};
+    return __builtin_bit_cast(f16x8, v);
+}
+
+// Lane (i, q) = (lane & 15, lane >> 4) holds the 4 dwords T[q][0..3] of
+// group g+q of row i; afterwards d[m] holds T[m][q], i.e. dword q (columns
+// 8q..8q+7) of group g+m: the B fragment of group g+m.
+__device__ __forceinline__ void transpose_quarters(u32x4& d) {
+    const auto r02 = __builtin_amdgcn_permlane32_swap(d[0], d[2], false, false);
+    const auto r13 = __builtin_amdgcn_permlane32_swap(d[1], d[3], false, false);
+    const auto r01 = __builtin_amdgcn_permlane16_swap(r02[0], r13[0], false, false);
+    const auto r23 = __builtin_amdgcn_permlane16_swap(r02[1], r13[1], false, false);
+    d[0] = r01[0];
+    d[1] = r01[1];
+    d[2] = r23[0];
+    d[3] = r23[1];
+}
+
+__device__ __forceinline__ f32x4 mfma16(f16x8 a, f16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ int pair_token(const BatchArgs& a, int p) {
+    const int n = a.T * a.K;
+    return p < n ? a.perm[p] / a.K : p - n;
+}
+
+// Column of position j of a fragment inside its 8-column k-block.
+__device__ __forceinline__ constexpr int frag_col(int j) { return (j >> 1) + 4 * (j & 1); }
+
+// ---------------------------------------------------------------- router
+// One W_r row per wave, 16 tokens per workgroup column; per-lane fp32 FMA
+// chains over the lane's columns, then a fixed-order wave sum.
+__global__ void __launch_bounds__(256) batch_router_kernel(BatchArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int e = blockIdx.x * 4 + wave_in_block();
+    if (e >= a.E) return;
+    const int t0 = blockIdx.y * kRouterTokens;
+    const int nt = min(kRouterTokens, a.T - t0);
+    const float* wr = a.router_w + (size_t)e * a.H;
+    const uint16_t* xb = a.x + (size_t)t0 * a.H;
+    float acc[kRouterTokens];
+#pragma unroll
+    for (int t = 0; t < kRouterTokens; ++t) acc[t] = 0.0f;
+    for (int k = lane * 4; k < a.H; k += 4 * kWave) {
+        const f32x4 wv = *as_global<f32x4>(wr + k);
+#pragma unroll
+        for (int t = 0; t < kRouterTokens; ++t) {
+            if (t < nt) {
+                const u32x2 xv = *as_global<u32x2>(xb + (size_t)t * a.H + k);
+                float r = acc[t];
+                r = fmaf(wv[0], bf16_lo(xv[0]), r);
+                r = fmaf(wv[1], bf16_hi(xv[0]), r);
+                r = fmaf(wv[2], bf16_lo(xv[1]), r);
+                r = fmaf(wv[3], bf16_hi(xv[1]), r);
+                acc[t] = r;
+            }
+        }
+    }
+    const float b = a.bias[e];
+#pragma unroll
+    for (int t = 0; t < kRouterTokens; ++t) {
+        if (t < nt) {
+            const float l = wave_sum(acc[t]);
+            if (lane == 0) {
+                const float sv = 1.0f / (1.0f + expf(-l));
+                a.s[(size_t)(t0 + t) * a.E + e] = sv;
+                a.sb[(size_t)(t0 + t) * a.E + e] = sv + b;
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------- top-k
+// One wave per token: group-limited top-k, then (convert) the token's
+// activations as fp16 scaled by 2^kx (max |x| into [2^13, 2^14)), stored per
+// (group, quarter) as 8 values in fragment order.
+template <int EPL, int CPL>
+__global__ void __launch_bounds__(256) batch_topk_kernel(BatchArgs a, int convert) {
+    const int lane = threadIdx.x & 63;
+    const int t = blockIdx.x * 4 + wave_in_block();
+    if (t >= a.T) return;
+    int id;
+    float wt;
+    wave_group_topk<EPL>(a.s + (size_t)t * a.E, a.sb + (size_t)t * a.E, a.E, a.G, a.TG, a.K, a.rsf, lane, &id, &wt);
+    if (lane < a.K) {
+        a.ids[(size_t)t * a.K + lane] = id;
+        a.w[(size_t)t * a.K + lane] = wt;
+    }
+    if (!convert) return;
+    const int KG = a.H / 32;
+    const uint16_t* xr = a.x + (size_t)t * a.H;
+    u32x4 raw[CPL][4];
+    unsigned mx = 0;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+        const int g = lane + kWave * c;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            raw[c][q] = g < KG ? *as_global<u32x4>(xr + 32 * g + 8 * q) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int z = 0; z < 4; ++z) {
+                const unsigned d = raw[c][q][z];
+                mx = umax(mx, umax(d & 0x7FFFu, (d >> 16) & 0x7FFFu));
+            }
+        }
+    }
+    const int k = range_exponent(wave_max_u32(mx) >> 7);
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+        const int g = lane + kWave * c;
+        if (g >= KG) continue;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            _Float16 hv[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int col = frag_col(j);
+                const unsigned d = raw[c][q][col >> 1];
+                const float f = (col & 1) ? bf16_hi(d) : bf16_lo(d);
+                hv[j] = (_Float16)ldexpf(f, k);
+            }
+            const u32x4 o = {pack_h2(hv[0], hv[1]), pack_h2(hv[2], hv[3]), pack_h2(hv[4], hv[5]),
+                             pack_h2(hv[6], hv[7])};
+            *reinterpret_cast<u32x4*>(a.xa + (size_t)t * a.H + (size_t)(g * 4 + q) * 8) = o;
+        }
+    }
+    if (lane == 0) a.kx[t] = k;
+}
+
+// ---------------------------------------------------------------- dispatch
+__device__ __forceinline__ int wave_exclusive_scan(int v, int lane, int* total) {
+    int x = v;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const int y = __shfl_up(x, o);
+        if (lane >= o) x += y;
+    }
+    *total = __shfl(x, kWave - 1);
+    return x - v;
+}
+
+// One workgroup.  Keys (expert << 16 | entry) are unique, so the bitonic
+// sort gives the stable order by expert, then token, then slot.
+__global__ void __launch_bounds__(1024) batch_dispatch_kernel(BatchArgs a) {
+    __shared__ unsigned keys[kMaxDispatchEntries];
+    __shared__ int cnt[256], off[256], toff[256], dpos[256];
+    __shared__ int totals[3];
+    const int tid = threadIdx.x;
+    const int n = a.T * a.K;
+    int n2 = kWave;
+    while (n2 < n) n2 <<= 1;
+    for (int i = tid; i < n2; i += 1024) keys[i] = i < n ? (((unsigned)a.ids[i] << 16) | (unsigned)i) : 0xFFFFFFFFu;
+    if (tid < 256) cnt[tid] = 0;
+    __syncthreads();
+    for (int i = tid; i < n; i += 1024) atomicAdd(&cnt[a.ids[i]], 1);
+    for (int k = 2; k <= n2; k <<= 1) {
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            __syncthreads();
+            for (int i = tid; i < n2; i += 1024) {
+                const int p = i ^ j;
+                if (p > i) {
+                    const unsigned x = keys[i], y = keys[p];
+                    const bool up = (i & k) == 0;
+                    if ((x > y) == up) {
+                        keys[i] = y;
+                        keys[p] = x;
+                    }
+                }
+            }
+        }
+    }
+    __syncthreads();
+    if (tid < kWave) {
+        int c[4], nt[4], f[4];
+        int sc = 0, stl = 0, sf = 0;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int e = 4 * tid + r;
+            c[r] = e < a.E ? cnt[e] : 0;
+            nt[r] = (c[r] + kTileTokens - 1) / kTileTokens;
+            f[r] = c[r] > 0 ? 1 : 0;
+            sc += c[r];
+            stl += nt[r];
+            sf += f[r];
+        }
+        int tc, tt, tf;
+        int bc = wave_exclusive_scan(sc, tid, &tc);
+        int bt = wave_exclusive_scan(stl, tid, &tt);
+        int bf = wave_exclusive_scan(sf, tid, &tf);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int e = 4 * tid + r;
+            if (e < a.E) {
+                off[e] = bc;
+                toff[e] = bt;
+                dpos[e] = bf;
+            }
+            bc += c[r];
+            bt += nt[r];
+            bf += f[r];
+        }
+        if (tid == 0) {
+            totals[0] = tc;
+            totals[1] = tt;
+            totals[2] = tf;
+        }
+    }
+    __syncthreads();
+    for (int p = tid; p < n; p += 1024) {
+        const int idx = (int)(keys[p] & 0xFFFFu);
+        a.perm[p] = idx;
+        a.inv[idx] = p;
+    }
+    for (int e = tid; e < a.E; e += 1024) {
+        const int c = cnt[e];
+        a.counts[e] = c;
+        a.offsets[e] = off[e];
+        if (c > 0) {
+            a.distinct[dpos[e]] = e;
+            for (int i = 0; i * kTileTokens < c; ++i)
+                a.tiles[toff[e] + i] = Tile{e, off[e] + kTileTokens * i, min(kTileTokens, c - kTileTokens * i), 0};
+        }
+    }
+    if (tid == 0) {
+        a.offsets[a.E] = n;
+        a.n_distinct[0] = totals[2];
+        int nt = totals[1];
+        for (int s = 0; s < a.S; ++s)
+            for (int t0 = 0; t0 < a.T; t0 += kTileTokens)
+                a.tiles[nt++] = Tile{a.E, n + t0, min(kTileTokens, a.T - t0), 0};
+        a.n_tiles[0] = nt;
+    }
+}
+
+// ---------------------------------------------------------------- gate/up
+// Gate and up scales of row r for groups g..g+3 as dwords (gate | up << 16).
+template <int KG>
+__device__ __forceinline__ u32x4 gateup_scales4(const uint16_t* gus, int r, int g) {
+    if constexpr (KG >= kWave) {
+        return *as_global<u32x4>(gus + gateup_scale_index(r, g, 0, KG, 1));
+    } else {
+        constexpr int p = gateup_rows(KG);
+        u32x4 v;
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+            v[m] = (unsigned)*as_global<uint16_t>(gus + gateup_scale_index(r, g + m, 0, KG, p)) |
+                   ((unsigned)*as_global<uint16_t>(gus + gateup_scale_index(r, g + m, 1, KG, p)) << 16);
+        return v;
+    }
+}
+
+// Workgroup = 8 waves over 128 rows of gate and the same 128 rows of up for
+// the (up to) 16 tokens of one tile; wave w owns rows 16w..16w+15.
+template <int KG>
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) batch_gateup_kernel(BatchArgs a) {
+    constexpr int CK = KG < 32 ? KG : 32;   // groups per LDS stage
+    constexpr int NST = KG / CK;
+    constexpr int PT = CK * 64 / 512;       // 16-byte staging elements per thread
+    static_assert(CK % 4 == 0 && KG % CK == 0 && PT >= 1, "gate/up stage shape");
+    __shared__ u32x4 xs[2][CK * 64];        // [(g * 4 + q) * 16 + token]
+    const int tid = threadIdx.x, lane = tid & 63, wv = wave_in_block();
+    const int i = lane & 15, q = lane >> 4;
+    const int n_tiles = a.n_tiles[0];
+    const int rblocks = a.I / kBlockRows;
+    const int items = n_tiles * rblocks;
+    const BlobLayout L = blob_layout(a.H, a.I);
+    const int row_bytes = a.H / 2;
+    int gs = 0;  // stages so far: selects the LDS buffer
+    for (int item = blockIdx.x; item < items; item += gridDim.x) {
+        const int tile = item / rblocks, rb = item - tile * rblocks;
+        const Tile td = a.tiles[tile];
+        const uint8_t* blob = td.expert < a.E ? a.table[td.expert] : a.shared_blob;
+        const int row = rb * kBlockRows + wv * 16 + i;
+        const uint8_t* gq = blob + L.gate_q + (size_t)row * row_bytes;
+        const uint8_t* uq = blob + L.up_q + (size_t)row * row_bytes;
+        const uint16_t* gus = reinterpret_cast<const uint16_t*>(blob + L.gu_s);
+        const int sm = tid & 15;
+        const uint16_t* xsrc = sm < td.count ? a.xa + (size_t)pair_token(a, td.first_pair + sm) * a.H : nullptr;
+        f32x4 accg = {0.f, 0.f, 0.f, 0.f}, accu = {0.f, 0.f, 0.f, 0.f};
+        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+        u32x4 cg = *as_global<u32x4>(gq + q * 16);
+        u32x4 cu = *as_global<u32x4>(uq + q * 16);
+        u32x4 sc = gateup_scales4<KG>(gus, row, 0);
+        for (int st = 0; st < NST; ++st, ++gs) {
+            const int buf = gs & 1;
+            u32x4 v[PT];
+#pragma unroll
+            for (int r = 0; r < PT; ++r) {
+                const int e = tid + 512 * r;
+                v[r] = xsrc ? *as_global<u32x4>(xsrc + (size_t)((st * CK + (e >> 6)) * 4 + ((e >> 4) & 3)) * 8)
+                            : u32x4{0u, 0u, 0u, 0u};
+            }
+#pragma unroll
+            for (int r = 0; r < PT; ++r) xs[buf][tid + 512 * r] = v[r];
+            __syncthreads();
+#pragma unroll
+            for (int c = 0; c < CK / 4; ++c) {
+                const int g = st * CK + 4 * c;
+                // next step's codes and scales in flight while this step computes
+                u32x4 ng = cg, nu = cu, ns = sc;
+                if (g + 4 < KG) {
+                    ng = *as_global<u32x4>(gq + (g + 4 + q) * 16);
+                    nu = *as_global<u32x4>(uq + (g + 4 + q) * 16);
+                    ns = gateup_scales4<KG>(gus, row, g + 4);
+                }
+                transpose_quarters(cg);
+                transpose_quarters(cu);
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const f16x8 af = __builtin_bit_cast(f16x8, xs[buf][((4 * c + m) * 4 + q) * 16 + i]);
+                    const f32x4 dg = mfma16(af, codes_to_f16x8(cg[m]), zero);
+                    const f32x4 du = mfma16(af, codes_to_f16x8(cu[m]), zero);
+                    const float sg = half_bits_to_float(sc[m] & 0xFFFFu);
+                    const float su = half_bits_to_float(sc[m] >> 16);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        accg[j] = fmaf(sg, dg[j], accg[j]);
+                        accu[j] = fmaf(su, du[j], accu[j]);
+                    }
+                    // scale and accumulate now: one group's two products in
+                    // flight at a time (otherwise the compiler sinks the FMAs
+                    // to the end of the stage and spills every product)
+                    asm volatile("" : "+v"(accg), "+v"(accu));
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                cg = ng;
+                cu = nu;
+                sc = ns;
+                // keep one step of loads in flight, not the whole stage
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int tt = 4 * q + j;
+            if (tt < td.count) {
+                const int p = td.first_pair + tt;
+                const int kx = a.kx[pair_token(a, p)];
+                const float g = ldexpf(accg[j], -kx), u = ldexpf(accu[j], -kx);
+                a.h[(size_t)p * a.I + row] = g / (1.0f + expf(-g)) * u;
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------- h prep
+// One workgroup per entry: h as scaled fp16 hi + lo (hi = fp16(h 2^kh),
+// lo = fp16(h 2^kh - hi)), kh putting max |h| into [2^13, 2^14).
+template <int CPT>
+__global__ void __launch_bounds__(256) batch_hprep_kernel(BatchArgs a) {
+    __shared__ unsigned wmax[4];
+    const int p = blockIdx.x, tid = threadIdx.x;
+    const int n_el = (a.I / 32) * 4;  // (group, quarter) elements of 8 values
+    const float* hr = a.h + (size_t)p * a.I;
+    f32x4 v[CPT][2];
+    unsigned mx = 0;
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+        const int e = tid + 256 * c;
+#pragma unroll
+        for (int z = 0; z < 2; ++z) {
+            v[c][z] = e < n_el ? *as_global<f32x4>(hr + 8 * e + 4 * z) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int y = 0; y < 4; ++y) {
+                const float f = v[c][z][y];  // bit_cast of a vector element expression would read element 0
+                mx = umax(mx, __builtin_bit_cast(unsigned, f) & 0x7FFFFFFFu);
+            }
+        }
+    }
+    mx = wave_max_u32(mx);
+    if ((tid & 63) == 0) wmax[tid >> 6] = mx;
+    __syncthreads();
+    mx = umax(umax(wmax[0], wmax[1]), umax(wmax[2], wmax[3]));
+    const int k = range_exponent(mx >> 23);
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+        const int e = tid + 256 * c;
+        if (e >= n_el) continue;
+        _Float16 hi[8], lo[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int col = frag_col(j);
+            const float f = ldexpf(v[c][col >> 2][col & 3], k);
+            hi[j] = (_Float16)f;
+            lo[j] = (_Float16)(f - (float)hi[j]);
+        }
+        const size_t o = (size_t)p * a.I + (size_t)e * 8;
+        *reinterpret_cast<u32x4*>(a.ha_hi + o) = u32x4{pack_h2(hi[0], hi[1]), pack_h2(hi[2], hi[3]),
+                                                       pack_h2(hi[4], hi[5]), pack_h2(hi[6], hi[7])};
+        *reinterpret_cast<u32x4*>(a.ha_lo + o) = u32x4{pack_h2(lo[0], lo[1]), pack_h2(lo[2], lo[3]),
+                                                       pack_h2(lo[4], lo[5]), pack_h2(lo[6], lo[7])};
+    }
+    if (tid == 0) a.kh[p] = k;
+}
+
+// ---------------------------------------------------------------- down
+// Workgroup = 8 waves over 128 output rows for the (up to) 16 entries of one
+// tile; each group is two MFMAs (hi and lo parts of h) into one result.
+template <int KGI>
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) batch_down_kernel(BatchArgs a) {
+    constexpr int CK = KGI < 16 ? KGI : 16;
+    constexpr int NST = KGI / CK;
+    constexpr int PART = CK * 64;            // staging elements of one part
+    constexpr int PT = 2 * PART / 512;       // per thread (hi and lo)
+    static_assert(CK % 4 == 0 && KGI % CK == 0 && PT >= 1, "down stage shape");
+    __shared__ u32x4 hs[2][2 * PART];        // [part * PART + (g * 4 + q) * 16 + token]
+    const int tid = threadIdx.x, lane = tid & 63, wv = wave_in_block();
+    const int i = lane & 15, q = lane >> 4;
+    const int n_tiles = a.n_tiles[0];
+    const int rblocks = a.H / kBlockRows;
+    const int items = n_tiles * rblocks;
+    const BlobLayout L = blob_layout(a.H, a.I);
+    const int row_bytes = a.I / 2;
+    int gs = 0;
+    for (int item = blockIdx.x; item < items; item += gridDim.x) {
+        const int tile = item / rblocks, rb = item - tile * rblocks;
+        const Tile td = a.tiles[tile];
+        const uint8_t* blob = td.expert < a.E ? a.table[td.expert] : a.shared_blob;
+        const int row = rb * kBlockRows + wv * 16 + i;
+        const uint8_t* dq = blob + L.down_q + (size_t)row * row_bytes;
+        const uint16_t* dsc = reinterpret_cast<const uint16_t*>(blob + L.down_s);
+        const int sm = tid & 15;
+        const bool has = sm < td.count;
+        const size_t src = (size_t)(td.first_pair + sm) * a.I;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+        u32x4 cd = *as_global<u32x4>(dq + q * 16);
+        unsigned s4[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) s4[m] = *as_global<uint16_t>(dsc + scale_index(row, m, KGI, a.down_p));
+        for (int st = 0; st < NST; ++st, ++gs) {
+            const int buf = gs & 1;
+            u32x4 v[PT];
+#pragma unroll
+            for (int r = 0; r < PT; ++r) {
+                const int e = tid + 512 * r;
+                const int part = e / PART, rest = e - part * PART;
+                const uint16_t* base = part ? a.ha_lo : a.ha_hi;
+                v[r] = has ? *as_global<u32x4>(base + src + (size_t)((st * CK + (rest >> 6)) * 4 + ((rest >> 4) & 3)) * 8)
+                           : u32x4{0u, 0u, 0u, 0u};
+            }
+#pragma unroll
+            for (int r = 0; r < PT; ++r) hs[buf][tid + 512 * r] = v[r];
+            __syncthreads();
+#pragma unroll
+            for (int c = 0; c < CK / 4; ++c) {
+                const int g = st * CK + 4 * c;
+                u32x4 nd = cd;
+                unsigned ns[4] = {s4[0], s4[1], s4[2], s4[3]};
+                if (g + 4 < KGI) {
+                    nd = *as_global<u32x4>(dq + (g + 4 + q) * 16);
+#pragma unroll
+                    for (int m = 0; m < 4; ++m)
+                        ns[m] = *as_global<uint16_t>(dsc + scale_index(row, g + 4 + m, KGI, a.down_p));
+                }
+                transpose_quarters(cd);
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const int slot = ((4 * c + m) * 4 + q) * 16 + i;
+                    const f16x8 ah = __builtin_bit_cast(f16x8, hs[buf][slot]);
+                    const f16x8 al = __builtin_bit_cast(f16x8, hs[buf][PART + slot]);
+                    const f16x8 bw = codes_to_f16x8(cd[m]);
+                    const f32x4 d = mfma16(al, bw, mfma16(ah, bw, zero));
+                    const float s = half_bits_to_float(s4[m]);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) acc[j] = fmaf(s, d[j], acc[j]);
+                    asm volatile("" : "+v"(acc));
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                cd = nd;
+#pragma unroll
+                for (int m = 0; m < 4; ++m) s4[m] = ns[m];
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int tt = 4 * q + j;
+            if (tt < td.count) {
+                const int p = td.first_pair + tt;
+                a.d[(size_t)p * a.H + row] = ldexpf(acc[j], -a.kh[p]);
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------- combine
+__global__ void __launch_bounds__(256) batch_combine_kernel(BatchArgs a) {
+    const int t = blockIdx.x;
+    float wj[8];
+    const float* dj[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        wj[j] = j < a.K ? a.w[(size_t)t * a.K + j] : 0.0f;
+        dj[j] = j < a.K ? a.d + (size_t)a.inv[(size_t)t * a.K + j] * a.H : nullptr;
+    }
+    const float* dsh = a.S > 0 ? a.d + (size_t)(a.T * a.K + t) * a.H : nullptr;
+    for (int r = threadIdx.x * 4; r < a.H; r += 1024) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            if (j < a.K) {
+                const f32x4 v = *as_global<f32x4>(dj[j] + r);
+#pragma unroll
+                for (int z = 0; z < 4; ++z) acc[z] = fmaf(wj[j], v[z], acc[z]);
+            }
+        }
+        if (dsh) {
+            const f32x4 v = *as_global<f32x4>(dsh + r);
+#pragma unroll
+            for (int z = 0; z < 4; ++z) acc[z] += v[z];
+        }
+        *reinterpret_cast<f32x4*>(a.y + (size_t)t * a.H + r) = acc;
+    }
+}
+
+// ---------------------------------------------------------------- launchers
+constexpr int kGroupedGrid = 512;  // 2 workgroups of 8 waves per CU
+
+template <int EPL>
+hipError_t launch_topk(const BatchArgs& a, bool convert, hipStream_t st) {
+    const dim3 grid((a.T + 3) / 4);
+    switch ((a.H / 32 + kWave - 1) / kWave) {
+        case 1: hipLaunchKernelGGL((batch_topk_kernel<EPL, 1>), grid, dim3(256), 0, st, a, (int)convert); break;
+        case 2: hipLaunchKernelGGL((batch_topk_kernel<EPL, 2>), grid, dim3(256), 0, st, a, (int)convert); break;
+        case 3: hipLaunchKernelGGL((batch_topk_kernel<EPL, 3>), grid, dim3(256), 0, st, a, (int)convert); break;
+        case 4: hipLaunchKernelGGL((batch_topk_kernel<EPL, 4>), grid, dim3(256), 0, st, a, (int)convert); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+int grouped_grid(const BatchArgs& a, int rblocks) {
+    const long items = (long)batch_max_tiles(a.T, a.K, a.E, a.S) * rblocks;
+    return (int)(items < kGroupedGrid ? items : kGroupedGrid);
+}
+
+template <int KG>
+hipError_t launch_gateup(const BatchArgs& a, hipStream_t st) {
+    hipLaunchKernelGGL((batch_gateup_kernel<KG>), dim3(grouped_grid(a, a.I / kBlockRows)), dim3(512), 0, st, a);
+    return hipGetLastError();
+}
+
+template <int KGI>
+hipError_t launch_down(const BatchArgs& a, hipStream_t st) {
+    hipLaunchKernelGGL((batch_down_kernel<KGI>), dim3(grouped_grid(a, a.H / kBlockRows)), dim3(512), 0, st, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t batch_router(const BatchArgs& a, hipStream_t st) {
+    hipLaunchKernelGGL(batch_router_kernel, dim3((a.E + 3) / 4, (a.T + kRouterTokens - 1) / kRouterTokens), dim3(256),
+                       0, st, a);
+    return hipGetLastError();
+}
+
+hipError_t batch_topk(const BatchArgs& a, bool convert, hipStream_t st) {
+    if (a.E <= 64) return launch_topk<1>(a, convert, st);
+    if (a.E <= 128) return launch_topk<2>(a, convert, st);
+    return launch_topk<4>(a, convert, st);
+}
+
+hipError_t batch_dispatch(const BatchArgs& a, hipStream_t st) {
+    if (a.T * a.K > kMaxDispatchEntries || a.E > 256) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(batch_dispatch_kernel, dim3(1), dim3(1024), 0, st, a);
+    return hipGetLastError();
+}
+
+hipError_t batch_gateup(const BatchArgs& a, hipStream_t st) {
+    switch (a.H / 32) {
+        case 8: return launch_gateup<8>(a, st);
+        case 16: return launch_gateup<16>(a, st);
+        case 32: return launch_gateup<32>(a, st);
+        case 64: return launch_gateup<64>(a, st);
+        case 128: return launch_gateup<128>(a, st);
+        case 192: return launch_gateup<192>(a, st);
+        case 256: return launch_gateup<256>(a, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t batch_hprep(const BatchArgs& a, hipStream_t st) {
+    const int pairs = a.T * (a.K + a.S);
+    if ((a.I / 32) * 4 <= 256)
+        hipLaunchKernelGGL((batch_hprep_kernel<1>), dim3(pairs), dim3(256), 0, st, a);
+    else
+        hipLaunchKernelGGL((batch_hprep_kernel<2>), dim3(pairs), dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+
+hipError_t batch_down(const BatchArgs& a, hipStream_t st) {
+    switch (a.I / 32) {
+        case 4: return launch_down<4>(a, st);
+        case 8: return launch_down<8>(a, st);
+        case 16: return launch_down<16>(a, st);
+        case 32: return launch_down<32>(a, st);
+        case 64: return launch_down<64>(a, st);
+        case 128: return launch_down<128>(a, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t batch_combine(const BatchArgs& a, hipStream_t st) {
+    hipLaunchKernelGGL(batch_combine_kernel, dim3(a.T), dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+
+bool batch_shape_supported(int hidden, int inter) {
+    return hidden % 256 == 0 && inter % kBlockRows == 0 && hidden / 32 <= 256 && inter / 32 <= 128;
+}
+
+}  // namespace moe

@@ -24,6 +24,17 @@ struct WorkspaceLayout {
     size_t ids = 0;            // [max_T][K] when the caller passes no ids buffer
     size_t w = 0;              // [max_T][K]
     size_t h = 0;              // [K + S][I]
+    // batched path (max_T > 1), sized for batch_tokens tokens per launch sequence
+    int batch_tokens = 0;
+    size_t b_s = 0, b_sb = 0;  // [Tb][E]
+    size_t b_xa = 0;           // [Tb][H] fp16
+    size_t b_kx = 0;           // [Tb]
+    size_t b_counts = 0, b_offsets = 0, b_perm = 0, b_inv = 0, b_distinct = 0, b_n_distinct = 0;
+    size_t b_tiles = 0, b_n_tiles = 0;
+    size_t b_h = 0;            // [P][I] fp32, P = Tb * (K + S)
+    size_t b_ha_hi = 0, b_ha_lo = 0;  // [P][I] fp16
+    size_t b_kh = 0;           // [P]
+    size_t b_d = 0;            // [P][H] fp32
     size_t total = 0;
 };
 

@@ -60,4 +60,72 @@ hipError_t decode_routed_gateup(const DecodeArgs& a, hipStream_t st, const Launc
 hipError_t decode_down_combine(const DecodeArgs& a, hipStream_t st, const LaunchTiming& tm = {});
 bool decode_shape_supported(int hidden, int inter, int top_k, int n_shared);
 
+// ------------------------------------------------------------ batched path
+// Tokens per MFMA tile and output rows per workgroup of the grouped kernels.
+constexpr int kTileTokens = 16;
+constexpr int kBlockRows = 128;
+// Largest number of (token, routed slot) entries one dispatch sorts in LDS.
+constexpr int kMaxDispatchEntries = 8192;
+
+// One tile of the grouped kernels: up to kTileTokens consecutive entries
+// ("pairs") of one expert.  expert == E marks the shared expert.
+struct Tile {
+    int expert;
+    int first_pair;
+    int count;
+    int pad;
+};
+
+// Arguments of a batched call of T tokens.  Pairs p in [0, T*K) are the
+// routed (token, slot) entries sorted by expert then token; pairs T*K + t
+// are the shared expert's (one per token).
+struct BatchArgs {
+    const uint16_t* x;           // [T][H] bf16 bits
+    const float* router_w;       // [E][H]
+    const float* bias;           // [E]
+    const uint8_t* const* table; // [E] packed routed expert blobs
+    const uint8_t* shared_blob;  // packed shared expert (S == 1)
+    float* s;                    // [T][E]
+    float* sb;                   // [T][E]
+    uint16_t* xa;                // [T][H/32][4][8] scaled fp16 activations, MFMA order
+    int* kx;                     // [T] their scaling exponents
+    int32_t* ids;                // [T][K]
+    float* w;                    // [T][K]
+    int32_t* counts;             // [E]
+    int32_t* offsets;            // [E + 1]
+    int32_t* perm;               // [T*K] pair -> token*K + slot
+    int32_t* inv;                // [T*K] token*K + slot -> pair
+    int32_t* distinct;           // [E] experts with at least one entry, ascending
+    int32_t* n_distinct;         // [1]
+    Tile* tiles;                 // [max_tiles]
+    int32_t* n_tiles;            // [1]
+    float* h;                    // [P][I] SwiGLU outputs
+    uint16_t* ha_hi;             // [P][I/32][4][8] h as scaled fp16 hi part, MFMA order
+    uint16_t* ha_lo;             // [P][I/32][4][8] lo part
+    int* kh;                     // [P] scaling exponents of h
+    float* d;                    // [P][H] down projections
+    float* y;                    // [T][H]
+    int T, H, I, E, G, TG, K, S;
+    int down_p;                  // row-block size of the down scale packing
+    float rsf;
+};
+
+// Upper bound of the tiles of a call of T tokens.
+inline int batch_max_tiles(int T, int K, int E, int S) {
+    const int n = T * K;
+    return (n < E ? n : E) + (n + kTileTokens - 1) / kTileTokens + S * ((T + kTileTokens - 1) / kTileTokens);
+}
+
+hipError_t batch_router(const BatchArgs& a, hipStream_t st);
+// Group-limited top-k of every token (ids, w); with convert, also the
+// tokens' activations in MFMA order (xa, kx).
+hipError_t batch_topk(const BatchArgs& a, bool convert, hipStream_t st);
+// counts, offsets, perm, inv, distinct, tiles from ids (T*K <= kMaxDispatchEntries).
+hipError_t batch_dispatch(const BatchArgs& a, hipStream_t st);
+hipError_t batch_gateup(const BatchArgs& a, hipStream_t st);
+hipError_t batch_hprep(const BatchArgs& a, hipStream_t st);
+hipError_t batch_down(const BatchArgs& a, hipStream_t st);
+hipError_t batch_combine(const BatchArgs& a, hipStream_t st);
+bool batch_shape_supported(int hidden, int inter);
+
 }  // namespace moe

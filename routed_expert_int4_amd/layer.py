@@ -145,6 +145,23 @@ class DeviceLayer:
         B.moe_layer_forward(self.handle, x, T, y, ids, w, stream)
         return y, ids, w
 
+    def forward_each(self, x, y=None, ids=None, w=None, stream=None):
+        """Like forward, as T separate one-token calls (the decode path):
+        token t's call reads x[t] and writes y[t], ids[t], w[t]."""
+        import torch
+        T, H, k = x.shape[0], self.cfg.hidden, self.cfg.top_k
+        if y is None:
+            y = torch.empty((T, H), dtype=torch.float32, device=self.device)
+        if ids is None:
+            ids = torch.empty((T, k), dtype=torch.int32, device=self.device)
+        if w is None:
+            w = torch.empty((T, k), dtype=torch.float32, device=self.device)
+        px, py, pi, pw = x.data_ptr(), y.data_ptr(), ids.data_ptr(), w.data_ptr()
+        st = B._stream_handle(stream)
+        for t in range(T):
+            B.moe_layer_forward(self.handle, px + 2 * H * t, 1, py + 4 * H * t, pi + 4 * k * t, pw + 4 * k * t, st)
+        return y, ids, w
+
     def router_topk(self, x, stream=None):
         import torch
         T = x.shape[0]

@@ -2,6 +2,7 @@
 import numpy as np
 
 from oracle import oracle
+from routed_expert_int4_amd import synth
 
 GAP_EXCUSE = 1e-6      # selection margin below which differing ids are excused
 Y_RTOL = 2e-3          # max |y_gpu - y_ref| <= Y_RTOL * max |y_ref| per token
@@ -51,3 +52,26 @@ def check_layer(weights, x_bits, y_gpu, ids_gpu, w_gpu, rows=None):
         forced = oracle.layer_forward(weights, x_bits[rows[excused]], forced_ids=ids_gpu[rows[excused]])
         worst = max(worst, check_outputs(y_gpu[rows[excused]], forced["y"]))
     return {"excused": len(excused), "worst_rel": worst}
+
+
+# Shapes that exercise every lane mapping of the kernels: rows narrower and
+# wider than a wave load, 1/2/4 experts per router lane, odd top_k.
+MID_A = synth.LayerConfig(hidden=1024, inter=256, n_experts=64, n_groups=8, topk_group=4, top_k=6,
+                          routed_scaling_factor=1.5)
+MID_B = synth.LayerConfig(hidden=4096, inter=1024, n_experts=128, n_groups=4, topk_group=2, top_k=8)
+MID_C = synth.LayerConfig(hidden=8192, inter=4096, n_experts=16, n_groups=4, topk_group=2, top_k=4)
+MID_D = synth.LayerConfig(hidden=512, inter=128, n_experts=256, n_groups=8, topk_group=4, top_k=8)
+
+
+def zipf_glm_weights():
+    """GLM-shaped layer (weights seed 0) with the committed Zipf-calibrated
+    correction bias (tests/golden/zipf_bias_glm.json, written by
+    tests/golden/make_zipf_bias.py from the oracle)."""
+    import json
+    import os
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "zipf_bias_glm.json")
+    with open(path) as f:
+        rec = json.load(f)
+    weights = synth.gen_layer(synth.GLM, seed=0)
+    weights.bias = np.asarray(rec["bias"], dtype=np.float32)
+    return weights, rec

@@ -1,0 +1,217 @@
+"""GPU parity of the batched (batch-union) path with the oracle.
+
+Calls with T > 1 tokens route every token, dispatch the (token, slot)
+entries by expert (each distinct expert is read once per call, the colibrì
+summary's batch-union rule, fr.news.hada.io topic 31297, "Principales
+fonctionnalités implémentées") and run grouped gate/up and down projections
+on the matrix cores.  Checked through the C ABI against the oracle:
+  * the dispatch (counts, offsets, permutation, distinct experts) bit-exact
+    against oracle/dispatch.py, up to the largest sort (8192 entries) and
+    degenerate routings;
+  * layer outputs element by element (ids bit-exact unless the oracle's gap
+    is below 1e-6; outputs within 2e-3 * max|ref| per token) on every shape,
+    ragged tiles, an expert taking more than one tile, zero and repeated
+    tokens, launch sequences split by the sort capacity;
+  * GLM-shaped calls: batch 32 under Zipf-skewed routing and a 512-token
+    prefill chunk (routing of every token, outputs on samples).
+"""
+import sys
+
+import numpy as np
+import pytest
+
+from oracle import oracle
+from oracle.dispatch import dispatch as oracle_dispatch
+from routed_expert_int4_amd import binding as B
+from routed_expert_int4_amd import synth
+from tests.helpers import MID_A, MID_B, MID_C, MID_D, check_layer, check_routing, zipf_glm_weights
+
+pytestmark = pytest.mark.gpu
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def torch_cuda():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    B.lib()
+    return torch
+
+
+def run_batch(torch, layer, x_bits):
+    from routed_expert_int4_amd.layer import DeviceLayer
+    y, ids, w = layer.forward(DeviceLayer.to_device_bf16(x_bits))
+    torch.cuda.synchronize()
+    return y.cpu().numpy(), ids.cpu().numpy(), w.cpu().numpy()
+
+
+# ---------------------------------------------------------------- dispatch
+def gpu_dispatch(torch, layer, ids_np):
+    T, k = ids_np.shape
+    E = layer.cfg.n_experts
+    dev = "cuda:0"
+    ids = torch.from_numpy(np.ascontiguousarray(ids_np, dtype=np.int32)).to(dev)
+    counts = torch.full((E,), -1, dtype=torch.int32, device=dev)
+    offsets = torch.full((E + 1,), -1, dtype=torch.int32, device=dev)
+    perm = torch.full((max(T * k, 1),), -1, dtype=torch.int32, device=dev)
+    distinct = torch.full((E,), -1, dtype=torch.int32, device=dev)
+    nd = torch.full((1,), -1, dtype=torch.int32, device=dev)
+    B.moe_dispatch(layer.handle, ids, T, counts, offsets, perm, distinct, nd)
+    torch.cuda.synchronize()
+    n = int(nd.item())
+    return {"counts": counts.cpu().numpy(), "offsets": offsets.cpu().numpy(), "perm": perm.cpu().numpy()[:T * k],
+            "distinct": distinct.cpu().numpy()[:n]}
+
+
+@pytest.fixture(scope="module")
+def dispatch_layer(torch_cuda):
+    from routed_expert_int4_amd.layer import DeviceLayer
+    layer = DeviceLayer(synth.gen_layer(MID_D, seed=0), max_T=1024)
+    yield layer
+    layer.close()
+
+
+@pytest.mark.parametrize("T,kind", [(1, "uniform"), (2, "uniform"), (32, "zipf"), (37, "uniform"), (512, "uniform"),
+                                    (1024, "uniform"), (1024, "zipf"), (300, "same")])
+def test_dispatch_matches_oracle(torch_cuda, dispatch_layer, T, kind):
+    say(f"[gpu] dispatch T={T} {kind}")
+    E, k = MID_D.n_experts, MID_D.top_k
+    rng = np.random.default_rng(T)
+    if kind == "same":
+        ids = np.tile(np.arange(k, dtype=np.int32), (T, 1))
+    elif kind == "zipf":
+        p = np.arange(1, E + 1, dtype=np.float64) ** -1.1
+        ids = np.stack([rng.choice(E, k, replace=False, p=p / p.sum()) for _ in range(T)]).astype(np.int32)
+    else:
+        ids = np.stack([rng.choice(E, k, replace=False) for _ in range(T)]).astype(np.int32)
+    got = gpu_dispatch(torch_cuda, dispatch_layer, ids)
+    ref = oracle_dispatch(ids, E)
+    for key in ("counts", "offsets", "perm", "distinct"):
+        np.testing.assert_array_equal(got[key], ref[key], err_msg=key)
+
+
+def test_dispatch_errors(torch_cuda, dispatch_layer):
+    ids = torch_cuda.zeros((2000, MID_D.top_k), dtype=torch_cuda.int32, device="cuda:0")
+    z = torch_cuda.zeros(300, dtype=torch_cuda.int32, device="cuda:0")
+    with pytest.raises(B.MoeError):  # above the workspace's batch
+        B.moe_dispatch(dispatch_layer.handle, ids, 2000, z, z, z, z, z)
+    with pytest.raises(B.MoeError):
+        B.moe_dispatch(dispatch_layer.handle, ids, 4, None, z, z, z, z)
+    B.moe_dispatch(dispatch_layer.handle, ids, 0, z, z, z, z, z)  # T = 0: no-op
+
+
+# ---------------------------------------------------------------- layer
+@pytest.mark.parametrize("cfg_name,T", [("TINY", 4), ("TINY", 2), ("MID_A", 37), ("MID_B", 16), ("MID_C", 5),
+                                        ("MID_D", 100)])
+def test_batch_layer_parity(torch_cuda, cfg_name, T):
+    from routed_expert_int4_amd.layer import DeviceLayer
+    cfg = {"TINY": synth.TINY, "MID_A": MID_A, "MID_B": MID_B, "MID_C": MID_C, "MID_D": MID_D}[cfg_name]
+    say(f"[gpu] batched parity {cfg_name} T={T}")
+    weights = synth.gen_layer(cfg, seed=0)
+    x = synth.gen_tokens(cfg, T, seed=11)
+    layer = DeviceLayer(weights, max_T=T)
+    y, ids, w = run_batch(torch_cuda, layer, x)
+    res = check_layer(weights, x, y, ids, w)
+    say(f"[gpu] {cfg_name} T={T}: worst rel err {res['worst_rel']:.3g}, excused {res['excused']}")
+    layer.close()
+
+
+def test_batch_repeated_zero_and_scaled_tokens(torch_cuda):
+    """20 copies of one token (its experts get 20 entries: two tiles), zero
+    tokens, tokens far from unit scale; repeated calls are bit-identical."""
+    from routed_expert_int4_amd.layer import DeviceLayer
+    say("[gpu] batched repeated / zero / scaled tokens")
+    weights = synth.gen_layer(MID_A, seed=0)
+    x = synth.gen_tokens(MID_A, 33, seed=12)
+    x[1:20] = x[0]
+    x[25] = 0
+    x[26:29] = synth.gen_tokens(MID_A, 3, seed=13, std=300.0)
+    x[29:32] = synth.gen_tokens(MID_A, 3, seed=14, std=1e-3)
+    layer = DeviceLayer(weights, max_T=33)
+    y, ids, w = run_batch(torch_cuda, layer, x)
+    check_layer(weights, x, y, ids, w)
+    assert np.all(y[25] == 0.0)
+    for t in range(1, 20):
+        np.testing.assert_array_equal(y[t], y[0])
+    y2, ids2, _ = run_batch(torch_cuda, layer, x)
+    np.testing.assert_array_equal(y, y2)
+    np.testing.assert_array_equal(ids, ids2)
+    layer.close()
+
+
+def test_batch_split_by_sort_capacity(torch_cuda):
+    """T * top_k above the dispatch sort's 8192 entries: two launch sequences."""
+    from routed_expert_int4_amd.layer import DeviceLayer
+    say("[gpu] batched T=1100 (two launch sequences)")
+    weights = synth.gen_layer(MID_D, seed=1)
+    x = synth.gen_tokens(MID_D, 1100, seed=15)
+    layer = DeviceLayer(weights, max_T=1100)
+    y, ids, w = run_batch(torch_cuda, layer, x)
+    check_layer(weights, x, y, ids, w)
+    layer.close()
+
+
+def test_batch_router_topk(torch_cuda):
+    from routed_expert_int4_amd.layer import DeviceLayer
+    say("[gpu] batched router_topk MID_B T=64")
+    weights = synth.gen_layer(MID_B, seed=2)
+    x = synth.gen_tokens(MID_B, 64, seed=16)
+    layer = DeviceLayer(weights, max_T=64)
+    ids, w = layer.router_topk(DeviceLayer.to_device_bf16(x))
+    torch_cuda.cuda.synchronize()
+    ids_ref, w_ref, gap = oracle.route(weights, x)
+    check_routing(MID_B, ids.cpu().numpy(), w.cpu().numpy(), ids_ref, w_ref, gap)
+    layer.close()
+
+
+# ---------------------------------------------------------------- GLM shape
+@pytest.fixture(scope="module")
+def glm_zipf(torch_cuda):
+    from routed_expert_int4_amd.layer import DeviceLayer
+    say("[gpu] generating the GLM-shaped layer (seed 0) with the Zipf bias")
+    weights, rec = zipf_glm_weights()
+    layer = DeviceLayer(weights, max_T=512)
+    yield weights, layer
+    layer.close()
+
+
+def test_glm_batch32_zipf(torch_cuda, glm_zipf):
+    """Speculative-verify-sized calls: 4 calls of 32 tokens (x seed 4) with
+    Zipf-skewed routing; every token's routing, all outputs of the first call
+    and 4 tokens of each other call."""
+    weights, layer = glm_zipf
+    x_all = synth.gen_tokens(synth.GLM, 128, seed=4)
+    for c in range(4):
+        x = x_all[32 * c:32 * (c + 1)]
+        y, ids, w = run_batch(torch_cuda, layer, x)
+        ids_ref, w_ref, gap = oracle.route(weights, x)
+        check_routing(synth.GLM, ids, w, ids_ref, w_ref, gap)
+        rows = range(32) if c == 0 else [0, 9, 17, 31]
+        res = check_layer(weights, x, y, ids, w, rows=rows)
+        say(f"[gpu] GLM batch-32 call {c}: {len(set(ids.reshape(-1).tolist()))} distinct experts, "
+            f"worst rel err {res['worst_rel']:.3g}")
+
+
+def test_glm_prefill512(torch_cuda, glm_zipf):
+    """A 512-token prefill chunk (x seed 5) on the GLM-shaped layer with
+    uniform routing (bias N(0, 0.01)): routing of all 512 tokens, outputs of
+    a spread of tokens and the smallest-gap ones."""
+    from routed_expert_int4_amd.layer import DeviceLayer
+    weights_z, _ = glm_zipf
+    weights = synth.gen_layer(synth.GLM, seed=0)
+    say("[gpu] GLM prefill 512")
+    layer = DeviceLayer(weights, max_T=512)
+    x = synth.gen_tokens(synth.GLM, 512, seed=5)
+    y, ids, w = run_batch(torch_cuda, layer, x)
+    ids_ref, w_ref, gap = oracle.route(weights, x)
+    excused = check_routing(synth.GLM, ids, w, ids_ref, w_ref, gap)
+    rows = sorted(set([0, 1, 100, 255, 256, 400, 510, 511] + list(np.argsort(gap)[:2])))
+    res = check_layer(weights, x, y, ids, w, rows=rows)
+    counts = np.bincount(ids.reshape(-1), minlength=256)
+    say(f"[gpu] GLM prefill: {int((counts > 0).sum())} distinct experts, max {counts.max()} tokens/expert, "
+        f"{len(excused)} excused, worst rel err {res['worst_rel']:.3g}")
+    layer.close()

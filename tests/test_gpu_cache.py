@@ -7,8 +7,9 @@ the C ABI:
   * every layer's outputs against the fp64 oracle on the GPU's own input to
     that layer (a stack of layers chained as in the 12-layer workload:
     next input = bf16(y / rms(y) + N(0, 0.1) noise));
-  * outputs bit-identical to the same layer with every expert resident (the
-    cache changes where a blob is read from, not the arithmetic);
+  * outputs bit-identical to the same layer with every expert resident,
+    called one token at a time (the cache changes where a blob is read from,
+    not the arithmetic);
   * hit / miss / eviction counts equal to a plain LRU replay of the GPU's
     routing trace (oracle/lru.py), and h2d_bytes = misses x blob bytes;
   * copy/compute ordering with the minimum slot count (every token evicts
@@ -77,7 +78,7 @@ def test_cache_stack_parity_and_lru(torch_cuda, slots):
     for l in range(N_LAYERS):
         x = DeviceLayer.to_device_bf16(x_bits)
         y, ids, w = cached[l].forward(x)
-        y_res, ids_res, w_res = resident[l].forward(x)
+        y_res, ids_res, w_res = resident[l].forward_each(x)
         torch.cuda.synchronize()
         yh, idh, wh = y.cpu().numpy(), ids.cpu().numpy(), w.cpu().numpy()
         res = check_layer(weights[l], x_bits, yh, idh, wh)

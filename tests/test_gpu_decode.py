@@ -1,4 +1,4 @@
-"""GPU parity of the decode path (one token per kernel sequence) with the oracle.
+"""GPU parity of the decode path (one-token calls) with the oracle.
 
 Every GPU test calls the library through the C ABI (ctypes binding) and
 compares element by element with the fp64 CPU oracle on the same seeded
@@ -15,17 +15,9 @@ import pytest
 from oracle import oracle
 from routed_expert_int4_amd import binding as B
 from routed_expert_int4_amd import synth
-from tests.helpers import check_layer, check_routing
+from tests.helpers import MID_A, MID_B, MID_C, MID_D, check_layer, check_routing
 
 pytestmark = pytest.mark.gpu
-
-# Shapes that exercise every lane mapping of the kernels: rows narrower and
-# wider than a wave load, 1/2/4 experts per router lane, odd top_k.
-MID_A = synth.LayerConfig(hidden=1024, inter=256, n_experts=64, n_groups=8, topk_group=4, top_k=6,
-                          routed_scaling_factor=1.5)
-MID_B = synth.LayerConfig(hidden=4096, inter=1024, n_experts=128, n_groups=4, topk_group=2, top_k=8)
-MID_C = synth.LayerConfig(hidden=8192, inter=4096, n_experts=16, n_groups=4, topk_group=2, top_k=4)
-MID_D = synth.LayerConfig(hidden=512, inter=128, n_experts=256, n_groups=8, topk_group=4, top_k=8)
 
 
 def say(msg):
@@ -46,7 +38,7 @@ def run_layer(torch, weights, x_bits, max_T=None):
     T = x_bits.shape[0]
     layer = DeviceLayer(weights, max_T=max_T or max(T, 1))
     x = DeviceLayer.to_device_bf16(x_bits)
-    y, ids, w = layer.forward(x)
+    y, ids, w = layer.forward_each(x)
     torch.cuda.synchronize()
     return layer, y.cpu().numpy(), ids.cpu().numpy(), w.cpu().numpy()
 
@@ -141,7 +133,7 @@ def test_repeatable_and_batch_independent(torch_cuda):
     x = synth.gen_tokens(MID_A, 9, seed=5)
     layer, y1, ids1, w1 = run_layer(torch_cuda, weights, x)
     from routed_expert_int4_amd.layer import DeviceLayer
-    y2, ids2, w2 = layer.forward(DeviceLayer.to_device_bf16(x))
+    y2, ids2, w2 = layer.forward_each(DeviceLayer.to_device_bf16(x))
     np.testing.assert_array_equal(y1, y2.cpu().numpy())
     np.testing.assert_array_equal(ids1, ids2.cpu().numpy())
     for t in (0, 4, 8):
@@ -156,7 +148,7 @@ def glm(torch_cuda):
     say("[gpu] generating the GLM-shaped layer (seed 0)")
     weights = synth.gen_layer(synth.GLM, seed=0)
     from routed_expert_int4_amd.layer import DeviceLayer
-    layer = DeviceLayer(weights, max_T=1000)
+    layer = DeviceLayer(weights, max_T=1)
     yield weights, layer
     layer.close()
 
@@ -169,7 +161,7 @@ def test_glm_decode_1000_tokens(torch_cuda, glm):
     say("[gpu] GLM 1000-token decode")
     x = synth.gen_tokens(synth.GLM, 1000, seed=1)
     from routed_expert_int4_amd.layer import DeviceLayer
-    y, ids, w = layer.forward(DeviceLayer.to_device_bf16(x))
+    y, ids, w = layer.forward_each(DeviceLayer.to_device_bf16(x))
     torch_cuda.cuda.synchronize()
     y, ids, w = y.cpu().numpy(), ids.cpu().numpy(), w.cpu().numpy()
     ids_ref, w_ref, gap = oracle.route(weights, x)
@@ -189,8 +181,8 @@ def test_glm_zero_token_and_repeat(torch_cuda, glm):
     x[1] = 0
     from routed_expert_int4_amd.layer import DeviceLayer
     xd = DeviceLayer.to_device_bf16(x)
-    y1, ids1, w1 = layer.forward(xd)
-    y2, ids2, w2 = layer.forward(xd)
+    y1, ids1, w1 = layer.forward_each(xd)
+    y2, ids2, w2 = layer.forward_each(xd)
     torch_cuda.cuda.synchronize()
     assert torch_cuda.equal(y1, y2) and torch_cuda.equal(ids1, ids2)
     y1 = y1.cpu().numpy()

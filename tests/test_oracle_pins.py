@@ -364,3 +364,42 @@ def test_generator_is_deterministic_and_codes_uniform():
     nib = np.concatenate([(a.gate_q & 15).ravel(), (a.gate_q >> 4).ravel()])
     counts = np.bincount(nib, minlength=16)
     assert counts.min() > 0.8 * counts.mean()
+
+
+# ---------------------------------------------------------------- dispatch
+def test_dispatch_hand_example():
+    from oracle.dispatch import dispatch
+    # 3 tokens, top-2, 4 experts: entries 0..5 = (0,0) (0,1) (1,0) (1,1) (2,0) (2,1)
+    ids = np.array([[2, 0], [0, 3], [2, 0]])
+    r = dispatch(ids, 4)
+    assert r["counts"].tolist() == [3, 0, 2, 1]
+    assert r["offsets"].tolist() == [0, 3, 3, 5, 6]
+    assert r["perm"].tolist() == [1, 2, 5, 0, 4, 3]
+    assert r["distinct"].tolist() == [0, 2, 3]
+
+
+def test_dispatch_invariants_random():
+    from oracle.dispatch import dispatch
+    rng = np.random.default_rng(5)
+    for T, K, E in [(1, 8, 256), (32, 8, 256), (7, 4, 16), (100, 6, 64)]:
+        ids = np.stack([rng.choice(E, K, replace=False) for _ in range(T)])
+        r = dispatch(ids, E)
+        flat = ids.reshape(-1)
+        perm = r["perm"]
+        assert sorted(perm.tolist()) == list(range(T * K))           # a permutation
+        keys = [(flat[p], p) for p in perm]
+        assert keys == sorted(keys)                                    # expert, then entry order
+        for e in range(E):                                             # offsets delimit each expert
+            seg = perm[r["offsets"][e]:r["offsets"][e + 1]]
+            assert all(flat[p] == e for p in seg) and len(seg) == r["counts"][e]
+        assert r["distinct"].tolist() == sorted(set(flat.tolist()))
+        assert r["offsets"][-1] == T * K
+
+
+def test_dispatch_degenerate():
+    from oracle.dispatch import dispatch
+    r = dispatch(np.full((5, 1), 7), 8)                                # one expert takes everything
+    assert r["counts"].tolist() == [0] * 7 + [5] and r["perm"].tolist() == [0, 1, 2, 3, 4]
+    assert r["distinct"].tolist() == [7]
+    r = dispatch(np.zeros((0, 4), np.int32), 8)                        # empty routing
+    assert r["counts"].sum() == 0 and len(r["perm"]) == 0 and len(r["distinct"]) == 0

@@ -57,8 +57,9 @@ typedef enum {
  * inputs); n_experts is a multiple of n_groups; top_k <= topk_group *
  * (n_experts / n_groups).  Supported by the kernels in this build:
  * hidden/32 in {8,16,32,64,128,192,256}, inter/32 in {4,8,16,32,64,128},
- * hidden % 256 == 0, n_experts <= 256, experts per group >= 2 and a power
- * of two times ceil(n_experts/64), n_shared in {0,1}, top_k <= 8. */
+ * hidden % 256 == 0, n_experts <= 256 and a multiple of 16, experts per
+ * group >= 2 and a power of two times ceil(n_experts/64), n_shared in
+ * {0,1}, top_k <= 8. */
 typedef struct {
     int hidden;
     int inter;

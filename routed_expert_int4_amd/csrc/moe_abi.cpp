@@ -61,6 +61,7 @@ moe_status_t validate_supported(const moe_config_t* c) {
         !batch_shape_supported(c->hidden, c->inter))
         return fail(MOE_EUNSUPPORTED, "no kernel for hidden=%d inter=%d", c->hidden, c->inter);
     if (c->n_experts > 256) return fail(MOE_EUNSUPPORTED, "n_experts > 256");
+    if (c->n_experts % 16) return fail(MOE_EUNSUPPORTED, "n_experts must be a multiple of 16");
     const int epl = c->n_experts <= 64 ? 1 : (c->n_experts <= 128 ? 2 : 4);
     const int gsize = c->n_experts / c->n_groups;
     const int lpg = gsize / epl;
@@ -106,8 +107,7 @@ WorkspaceLayout workspace_layout(const moe_config_t* c, int max_T) {
             field = o;
             o = align256(o + bytes);
         };
-        take(W.b_s, sizeof(float) * tb * E);
-        take(W.b_sb, sizeof(float) * tb * E);
+        take(W.b_logit_part, sizeof(float) * (size_t)batch_router_splits(c->hidden) * tb * E);
         take(W.b_xa, 2 * tb * H);
         take(W.b_kx, sizeof(int) * tb);
         take(W.b_counts, sizeof(int32_t) * E);
@@ -288,14 +288,14 @@ DecodeArgs decode_args(moe_layer_t* L, const uint16_t* x, int32_t* ids, float* w
     a.x = x;
     a.router_w = L->router_w;
     a.bias = L->bias;
-    a.table = reinterpret_cast<const uint8_t* const*>(L->ws + L->W.table);
+    a.table = L->cache ? nullptr : reinterpret_cast<const uint8_t* const*>(L->ws + L->W.table);
+    a.counter = reinterpret_cast<unsigned*>(L->ws + L->W.control);
     a.shared_blob = c.n_shared > 0 ? L->shared[0] : nullptr;
     a.s = reinterpret_cast<float*>(L->ws + L->W.s);
     a.sb = reinterpret_cast<float*>(L->ws + L->W.sb);
     a.xpairs = reinterpret_cast<unsigned*>(L->ws + L->W.xpairs);
     a.kx = reinterpret_cast<int*>(L->ws + L->W.kx);
     a.slot_blobs = reinterpret_cast<const uint8_t**>(L->ws + L->W.slot_blobs);
-    a.with_shared = 1;
     a.ids = ids;
     a.w = w;
     a.h = reinterpret_cast<float*>(L->ws + L->W.h);
@@ -372,8 +372,7 @@ BatchArgs batch_args(moe_layer_t* L, const uint16_t* x, int n, int32_t* ids, flo
     b.bias = L->bias;
     b.table = reinterpret_cast<const uint8_t* const*>(ws + W.table);
     b.shared_blob = c.n_shared > 0 ? L->shared[0] : nullptr;
-    b.s = reinterpret_cast<float*>(ws + W.b_s);
-    b.sb = reinterpret_cast<float*>(ws + W.b_sb);
+    b.logit_part = reinterpret_cast<float*>(ws + W.b_logit_part);
     b.xa = reinterpret_cast<uint16_t*>(ws + W.b_xa);
     b.kx = reinterpret_cast<int*>(ws + W.b_kx);
     b.ids = ids;
@@ -401,6 +400,7 @@ BatchArgs batch_args(moe_layer_t* L, const uint16_t* x, int n, int32_t* ids, flo
     b.K = c.top_k;
     b.S = c.n_shared;
     b.down_p = down_rows(c.hidden, c.inter / 32, c.top_k);
+    b.router_splits = batch_router_splits(c.hidden);
     b.rsf = c.routed_scaling_factor;
     return b;
 }
@@ -442,8 +442,6 @@ moe_status_t moe_router_topk(moe_layer_t* layer, const uint16_t* d_x, int T, int
                                    d_w + (size_t)t * c.top_k, nullptr);
         hipError_t e = decode_router(a, s);
         if (e != hipSuccess) return hip_fail(e, "router kernel launch");
-        e = decode_topk(a, s);
-        if (e != hipSuccess) return hip_fail(e, "top-k kernel launch");
     }
     return MOE_OK;
 }
@@ -494,11 +492,9 @@ moe_status_t moe_layer_forward(moe_layer_t* layer, const uint16_t* d_x, int T, f
         p0.end();
         ProfileScope p1(layer, 1, s, layer->cache ? ProfileScope::kSpan : ProfileScope::kKernel);
         if (layer->cache) {
-            // the host needs the routing: a top-k launch, then the cache
-            // resolves it, copies missing experts and enqueues the routed
-            // gate/up (hits first)
-            e = decode_topk(a, s);
-            if (e != hipSuccess) return hip_fail(e, "top-k kernel launch");
+            // the host needs the routing: the cache reads it back, resolves
+            // it, copies missing experts and enqueues the routed gate/up
+            // (hits first)
             st = cache_prepare_token(layer, a, s);
             if (st != MOE_OK) return st;
         } else {

@@ -5,9 +5,11 @@
 // "Principales fonctionnalités implémentées": in prefill and in the batched
 // verification forward, each distinct expert of the batch is read once and
 // applied to every position routed to it) on one GPU:
-//   1. router: logits of all tokens, W_r read once per 16 tokens;
-//   2. top-k: group-limited top-k per token (one wave each); the tokens'
-//      activations are converted to scaled fp16 in MFMA operand order;
+//   1. router: partial logits of all tokens on the matrix cores (fp32) over
+//      column splits, W_r read once per 16 tokens;
+//   2. top-k: logits summed over the splits, sigmoid, bias, group-limited
+//      top-k per token (one wave each); the tokens' activations are converted
+//      to scaled fp16 in MFMA operand order;
 //   3. dispatch: one workgroup sorts the T*K (token, slot) entries by
 //      expert then token in LDS, and writes counts, offsets, the permutation
 //      and its inverse, the distinct experts and the tile list (up to 16
@@ -42,8 +44,6 @@ namespace moe {
 namespace {
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-
-constexpr int kRouterTokens = 16;
 
 __device__ __forceinline__ float bf16_lo(unsigned d) { return __builtin_bit_cast(float, d << 16); }
 __device__ __forceinline__ float bf16_hi(unsigned d) { return __builtin_bit_cast(float, d & 0xFFFF0000u); }
@@ -94,45 +94,51 @@ __device__ __forceinline__ int pair_token(const BatchArgs& a, int p) {
 __device__ __forceinline__ constexpr int frag_col(int j) { return (j >> 1) + 4 * (j & 1); }
 
 // ---------------------------------------------------------------- router
-// One W_r row per wave, 16 tokens per workgroup column; per-lane fp32 FMA
-// chains over the lane's columns, then a fixed-order wave sum.
+// Partial logits of a 16-token x 16-expert tile over one of router_splits
+// column ranges, on the matrix cores (v_mfma_f32_16x16x4_f32: tokens as A
+// rows, W_r rows as B columns, bf16 activations widened exactly to fp32).
+// The 4 waves of a workgroup split the range again and are summed in wave
+// order through LDS; the splits are summed in order by the top-k kernel
+// (deterministic).  A lane loads 4 consecutive columns of its token and of
+// its expert and feeds them to 4 MFMAs, one column each, so every k-block of
+// an MFMA covers the same columns in A and B.
 __global__ void __launch_bounds__(256) batch_router_kernel(BatchArgs a) {
-    const int lane = threadIdx.x & 63;
-    const int e = blockIdx.x * 4 + wave_in_block();
-    if (e >= a.E) return;
-    const int t0 = blockIdx.y * kRouterTokens;
-    const int nt = min(kRouterTokens, a.T - t0);
-    const float* wr = a.router_w + (size_t)e * a.H;
-    const uint16_t* xb = a.x + (size_t)t0 * a.H;
-    float acc[kRouterTokens];
-#pragma unroll
-    for (int t = 0; t < kRouterTokens; ++t) acc[t] = 0.0f;
-    for (int k = lane * 4; k < a.H; k += 4 * kWave) {
-        const f32x4 wv = *as_global<f32x4>(wr + k);
-#pragma unroll
-        for (int t = 0; t < kRouterTokens; ++t) {
-            if (t < nt) {
-                const u32x2 xv = *as_global<u32x2>(xb + (size_t)t * a.H + k);
-                float r = acc[t];
-                r = fmaf(wv[0], bf16_lo(xv[0]), r);
-                r = fmaf(wv[1], bf16_hi(xv[0]), r);
-                r = fmaf(wv[2], bf16_lo(xv[1]), r);
-                r = fmaf(wv[3], bf16_hi(xv[1]), r);
-                acc[t] = r;
-            }
-        }
+    __shared__ f32x4 part[4][kWave];
+    const int lane = threadIdx.x & 63, wv = wave_in_block();
+    const int m = lane & 15, q = lane >> 4;
+    const int e0 = blockIdx.x * 16, t0 = blockIdx.y * 16, split = blockIdx.z;
+    const int t = t0 + m;
+    const bool tok = t < a.T;
+    const int kw = a.H / (4 * a.router_splits);  // columns per wave (a multiple of 16)
+    const int c0 = (split * 4 + wv) * kw + 4 * q;
+    const uint16_t* xr = a.x + (size_t)(tok ? t : 0) * a.H + c0;
+    const float* wr = a.router_w + (size_t)(e0 + m) * a.H + c0;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+    for (int k = 0; k < kw; k += 16) {
+        const u32x2 xv = tok ? *as_global<u32x2>(xr + k) : u32x2{0u, 0u};
+        const f32x4 wv4 = *as_global<f32x4>(wr + k);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(bf16_lo(xv[0]), wv4[0], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(bf16_hi(xv[0]), wv4[1], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(bf16_lo(xv[1]), wv4[2], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(bf16_hi(xv[1]), wv4[3], acc, 0, 0, 0);
     }
-    const float b = a.bias[e];
+    part[wv][lane] = acc;
+    __syncthreads();
+    if (wv != 0) return;
+    f32x4 r = part[0][lane];
 #pragma unroll
-    for (int t = 0; t < kRouterTokens; ++t) {
-        if (t < nt) {
-            const float l = wave_sum(acc[t]);
-            if (lane == 0) {
-                const float sv = 1.0f / (1.0f + expf(-l));
-                a.s[(size_t)(t0 + t) * a.E + e] = sv;
-                a.sb[(size_t)(t0 + t) * a.E + e] = sv + b;
-            }
-        }
+    for (int w = 1; w < 4; ++w) {
+        const f32x4 v = part[w][lane];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) r[j] += v[j];
+    }
+    // lane holds tokens t0 + 4q + j of expert e0 + m
+    float* out = a.logit_part + (size_t)split * a.T * a.E;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int tt = t0 + 4 * q + j;
+        if (tt < a.T) out[(size_t)tt * a.E + e0 + m] = r[j];
     }
 }
 
@@ -145,9 +151,23 @@ __global__ void __launch_bounds__(256) batch_topk_kernel(BatchArgs a, int conver
     const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * 4 + wave_in_block();
     if (t >= a.T) return;
+    // logits = in-order sum of the router's partial sums; s = sigmoid, sb = s + bias
+    float sv[EPL], key[EPL];
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+        const int e = lane * EPL + i;
+        sv[i] = 0.0f;
+        key[i] = -__builtin_inff();
+        if (e < a.E) {
+            float l = 0.0f;
+            for (int sp = 0; sp < a.router_splits; ++sp) l += a.logit_part[((size_t)sp * a.T + t) * a.E + e];
+            sv[i] = 1.0f / (1.0f + expf(-l));
+            key[i] = sv[i] + a.bias[e];
+        }
+    }
     int id;
     float wt;
-    wave_group_topk<EPL>(a.s + (size_t)t * a.E, a.sb + (size_t)t * a.E, a.E, a.G, a.TG, a.K, a.rsf, lane, &id, &wt);
+    wave_group_topk_values<EPL>(sv, key, a.E, a.G, a.TG, a.K, a.rsf, lane, &id, &wt);
     if (lane < a.K) {
         a.ids[(size_t)t * a.K + lane] = id;
         a.w[(size_t)t * a.K + lane] = wt;
@@ -344,40 +364,51 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) b
         const uint16_t* xsrc = sm < td.count ? a.xa + (size_t)pair_token(a, td.first_pair + sm) * a.H : nullptr;
         f32x4 accg = {0.f, 0.f, 0.f, 0.f}, accu = {0.f, 0.f, 0.f, 0.f};
         const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-        u32x4 cg = *as_global<u32x4>(gq + q * 16);
-        u32x4 cu = *as_global<u32x4>(uq + q * 16);
-        u32x4 sc = gateup_scales4<KG>(gus, row, 0);
-        for (int st = 0; st < NST; ++st, ++gs) {
-            const int buf = gs & 1;
-            u32x4 v[PT];
+        constexpr int NS = KG / 4;  // steps of 4 groups
+        // codes and scales of a step: lane of quarter q reads group 4s + q
+        auto load_step = [&](int s, u32x4& g, u32x4& u, u32x4& sc) {
+            g = *as_global<u32x4>(gq + (4 * s + q) * 16);
+            u = *as_global<u32x4>(uq + (4 * s + q) * 16);
+            sc = gateup_scales4<KG>(gus, row, 4 * s);
+        };
+        auto stage_load = [&](int st, u32x4 (&v)[PT]) {
 #pragma unroll
             for (int r = 0; r < PT; ++r) {
                 const int e = tid + 512 * r;
                 v[r] = xsrc ? *as_global<u32x4>(xsrc + (size_t)((st * CK + (e >> 6)) * 4 + ((e >> 4) & 3)) * 8)
                             : u32x4{0u, 0u, 0u, 0u};
             }
+        };
+        // two steps of codes in flight ahead of the one being computed, and
+        // the next stage's activations in flight during a stage
+        u32x4 v[PT];
+        stage_load(0, v);
+        u32x4 cg0, cu0, sc0, cg1 = {0u, 0u, 0u, 0u}, cu1 = cg1, sc1 = cg1;
+        load_step(0, cg0, cu0, sc0);
+        if (NS > 1) load_step(1, cg1, cu1, sc1);
+        // fully unrolled over the stages: a loop back-edge here would make
+        // the compiler drain the prefetched loads (register rotation copies)
+#pragma unroll
+        for (int st = 0; st < NST; ++st, ++gs) {
+            const int buf = gs & 1;
 #pragma unroll
             for (int r = 0; r < PT; ++r) xs[buf][tid + 512 * r] = v[r];
             __syncthreads();
+            if (st + 1 < NST) stage_load(st + 1, v);
 #pragma unroll
             for (int c = 0; c < CK / 4; ++c) {
-                const int g = st * CK + 4 * c;
-                // next step's codes and scales in flight while this step computes
-                u32x4 ng = cg, nu = cu, ns = sc;
-                if (g + 4 < KG) {
-                    ng = *as_global<u32x4>(gq + (g + 4 + q) * 16);
-                    nu = *as_global<u32x4>(uq + (g + 4 + q) * 16);
-                    ns = gateup_scales4<KG>(gus, row, g + 4);
-                }
-                transpose_quarters(cg);
-                transpose_quarters(cu);
+                const int sidx = st * (CK / 4) + c;
+                u32x4 cg2 = cg1, cu2 = cu1, sc2 = sc1;
+                if (sidx + 2 < NS) load_step(sidx + 2, cg2, cu2, sc2);
+                transpose_quarters(cg0);
+                transpose_quarters(cu0);
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
                     const f16x8 af = __builtin_bit_cast(f16x8, xs[buf][((4 * c + m) * 4 + q) * 16 + i]);
-                    const f32x4 dg = mfma16(af, codes_to_f16x8(cg[m]), zero);
-                    const f32x4 du = mfma16(af, codes_to_f16x8(cu[m]), zero);
-                    const float sg = half_bits_to_float(sc[m] & 0xFFFFu);
-                    const float su = half_bits_to_float(sc[m] >> 16);
+                    const f32x4 dg = mfma16(af, codes_to_f16x8(cg0[m]), zero);
+                    const f32x4 du = mfma16(af, codes_to_f16x8(cu0[m]), zero);
+                    const float sg = half_bits_to_float(sc0[m] & 0xFFFFu);
+                    const float su = half_bits_to_float(sc0[m] >> 16);
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         accg[j] = fmaf(sg, dg[j], accg[j]);
@@ -389,10 +420,13 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) b
                     asm volatile("" : "+v"(accg), "+v"(accu));
                     __builtin_amdgcn_sched_barrier(0);
                 }
-                cg = ng;
-                cu = nu;
-                sc = ns;
-                // keep one step of loads in flight, not the whole stage
+                cg0 = cg1;
+                cu0 = cu1;
+                sc0 = sc1;
+                cg1 = cg2;
+                cu1 = cu2;
+                sc1 = sc2;
+                // keep the prefetch depth, not the whole stage, in flight
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
@@ -490,13 +524,13 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) b
         const size_t src = (size_t)(td.first_pair + sm) * a.I;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
         const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-        u32x4 cd = *as_global<u32x4>(dq + q * 16);
-        unsigned s4[4];
+        constexpr int NS = KGI / 4;  // steps of 4 groups
+        auto load_step = [&](int s, u32x4& c, u32x4& sc) {
+            c = *as_global<u32x4>(dq + (4 * s + q) * 16);
 #pragma unroll
-        for (int m = 0; m < 4; ++m) s4[m] = *as_global<uint16_t>(dsc + scale_index(row, m, KGI, a.down_p));
-        for (int st = 0; st < NST; ++st, ++gs) {
-            const int buf = gs & 1;
-            u32x4 v[PT];
+            for (int m = 0; m < 4; ++m) sc[m] = *as_global<uint16_t>(dsc + scale_index(row, 4 * s + m, KGI, a.down_p));
+        };
+        auto stage_load = [&](int st, u32x4 (&v)[PT]) {
 #pragma unroll
             for (int r = 0; r < PT; ++r) {
                 const int e = tid + 512 * r;
@@ -505,37 +539,42 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) b
                 v[r] = has ? *as_global<u32x4>(base + src + (size_t)((st * CK + (rest >> 6)) * 4 + ((rest >> 4) & 3)) * 8)
                            : u32x4{0u, 0u, 0u, 0u};
             }
+        };
+        u32x4 v[PT];
+        stage_load(0, v);
+        u32x4 cd0, sc0, cd1 = {0u, 0u, 0u, 0u}, sc1 = cd1;
+        load_step(0, cd0, sc0);
+        if (NS > 1) load_step(1, cd1, sc1);
+#pragma unroll
+        for (int st = 0; st < NST; ++st, ++gs) {
+            const int buf = gs & 1;
 #pragma unroll
             for (int r = 0; r < PT; ++r) hs[buf][tid + 512 * r] = v[r];
             __syncthreads();
+            if (st + 1 < NST) stage_load(st + 1, v);
 #pragma unroll
             for (int c = 0; c < CK / 4; ++c) {
-                const int g = st * CK + 4 * c;
-                u32x4 nd = cd;
-                unsigned ns[4] = {s4[0], s4[1], s4[2], s4[3]};
-                if (g + 4 < KGI) {
-                    nd = *as_global<u32x4>(dq + (g + 4 + q) * 16);
-#pragma unroll
-                    for (int m = 0; m < 4; ++m)
-                        ns[m] = *as_global<uint16_t>(dsc + scale_index(row, g + 4 + m, KGI, a.down_p));
-                }
-                transpose_quarters(cd);
+                const int sidx = st * (CK / 4) + c;
+                u32x4 cd2 = cd1, sc2 = sc1;
+                if (sidx + 2 < NS) load_step(sidx + 2, cd2, sc2);
+                transpose_quarters(cd0);
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
                     const int slot = ((4 * c + m) * 4 + q) * 16 + i;
                     const f16x8 ah = __builtin_bit_cast(f16x8, hs[buf][slot]);
                     const f16x8 al = __builtin_bit_cast(f16x8, hs[buf][PART + slot]);
-                    const f16x8 bw = codes_to_f16x8(cd[m]);
+                    const f16x8 bw = codes_to_f16x8(cd0[m]);
                     const f32x4 d = mfma16(al, bw, mfma16(ah, bw, zero));
-                    const float s = half_bits_to_float(s4[m]);
+                    const float s = half_bits_to_float(sc0[m]);
 #pragma unroll
                     for (int j = 0; j < 4; ++j) acc[j] = fmaf(s, d[j], acc[j]);
                     asm volatile("" : "+v"(acc));
                     __builtin_amdgcn_sched_barrier(0);
                 }
-                cd = nd;
-#pragma unroll
-                for (int m = 0; m < 4; ++m) s4[m] = ns[m];
+                cd0 = cd1;
+                sc0 = sc1;
+                cd1 = cd2;
+                sc1 = sc2;
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
@@ -553,6 +592,8 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) b
 // ---------------------------------------------------------------- combine
 __global__ void __launch_bounds__(256) batch_combine_kernel(BatchArgs a) {
     const int t = blockIdx.x;
+    const int r = blockIdx.y * 1024 + threadIdx.x * 4;
+    if (r >= a.H) return;
     float wj[8];
     const float* dj[8];
 #pragma unroll
@@ -561,7 +602,7 @@ __global__ void __launch_bounds__(256) batch_combine_kernel(BatchArgs a) {
         dj[j] = j < a.K ? a.d + (size_t)a.inv[(size_t)t * a.K + j] * a.H : nullptr;
     }
     const float* dsh = a.S > 0 ? a.d + (size_t)(a.T * a.K + t) * a.H : nullptr;
-    for (int r = threadIdx.x * 4; r < a.H; r += 1024) {
+    {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
@@ -616,8 +657,8 @@ hipError_t launch_down(const BatchArgs& a, hipStream_t st) {
 }  // namespace
 
 hipError_t batch_router(const BatchArgs& a, hipStream_t st) {
-    hipLaunchKernelGGL(batch_router_kernel, dim3((a.E + 3) / 4, (a.T + kRouterTokens - 1) / kRouterTokens), dim3(256),
-                       0, st, a);
+    if (a.E % 16 || a.router_splits < 1 || a.H % (64 * a.router_splits)) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(batch_router_kernel, dim3(a.E / 16, (a.T + 15) / 16, a.router_splits), dim3(256), 0, st, a);
     return hipGetLastError();
 }
 
@@ -668,7 +709,7 @@ hipError_t batch_down(const BatchArgs& a, hipStream_t st) {
 }
 
 hipError_t batch_combine(const BatchArgs& a, hipStream_t st) {
-    hipLaunchKernelGGL(batch_combine_kernel, dim3(a.T), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(batch_combine_kernel, dim3(a.T, (a.H + 1023) / 1024), dim3(256), 0, st, a);
     return hipGetLastError();
 }
 

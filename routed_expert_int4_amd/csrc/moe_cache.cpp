@@ -140,12 +140,11 @@ moe_status_t cache_prepare_token(moe_layer* layer, DecodeArgs& a, hipStream_t st
         }
     }
     a.direct = 1;
-    // gate/up of the shared expert and the hit experts first, then of the
-    // misses once copied
+    // gate/up of the hit experts first, then of the misses once copied (the
+    // shared expert's ran in the router launch)
     for (int pass = 0; pass < 2; ++pass) {
         const std::vector<int>& js = pass == 0 ? hit_slots : miss_slots;
-        a.with_shared = pass == 0 ? 1 : 0;
-        if (js.empty() && !(pass == 0 && a.S > 0)) continue;
+        if (js.empty()) continue;
         for (int j : js) {
             const int s = slot_of_j[j];
             if (L.copy_recorded[s]) {
@@ -161,7 +160,6 @@ moe_status_t cache_prepare_token(moe_layer* layer, DecodeArgs& a, hipStream_t st
     }
     a.use_slot_list = 0;
     a.n_slot_list = 0;
-    a.with_shared = 1;
     c->pending_slots = slot_of_j;
     c->pending_layer = l;
     return MOE_OK;

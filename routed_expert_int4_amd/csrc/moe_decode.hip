@@ -1,20 +1,19 @@
 // Decode (one token per call) kernels of the routed int4 MoE layer, gfx950.
 //
 // Per token:
-//   1. router: router logits, one fp32 row of W_r per wave, turned into
-//      s = sigmoid(logit) and sb = s + bias; the token's activations are
-//      converted once into the fp16 pairs the expert kernels read.
-//   2. gateup: gate/up + SwiGLU of the shared expert (first: it does not
-//      depend on the routing, so its weights stream while each wave derives
-//      the group-limited top-k itself from s and sb with DPP reductions)
-//      and of the routed experts; the next item's loads are in flight while
-//      the current item is computed.  No top-k launch, no grid-wide handoff.
+//   1. router: router logits, one fp32 row of W_r per wave, turned
+//      into s = sigmoid(logit) and sb = s + bias; the last router block to
+//      finish (device-scope counter) derives the group-limited top-k with DPP
+//      reductions and writes ids, weights and the routed slots' blobs; in
+//      the same launch other workgroups run the shared expert's gate/up +
+//      SwiGLU (no routing dependency) and convert the token's activations
+//      once into the fp16 pairs of the routed experts' kernel.
+//   2. gateup: gate/up + SwiGLU of the routed experts; the next items' loads
+//      are in flight while the current ones are computed.
 //   3. down_combine: one wave per routed slot over a block of output rows,
 //      the shared expert's rows of the block split over the same waves,
 //      row loads pipelined; the block is combined in slot order (no float
 //      atomics: repeated calls are bit-identical).
-// A standalone top-k kernel serves the router-only entry point and the
-// expert-cache path, where the host needs the routing before the experts.
 //
 // Int4 GEMV scheme.  A lane owns one 32-input scale group of the reduction
 // dimension (several when a row has more than 64 groups) and keeps the
@@ -86,20 +85,9 @@ __device__ __forceinline__ float dot_chunk_hilo(u32x4 c, const f16x2* hp, const 
     return acc;
 }
 
-template <int EPL>
-__global__ void __launch_bounds__(64) topk_kernel(DecodeArgs a) {
-    const int lane = threadIdx.x;
-    int id;
-    float w;
-    wave_group_topk<EPL>(a.s, a.sb, a.E, a.G, a.TG, a.K, a.rsf, lane, &id, &w);
-    if (lane < a.K) {
-        a.ids[lane] = id;
-        a.w[lane] = w;
-    }
-}
-
 // ---------------------------------------------------------------- gate/up
-constexpr int kGateUpItemsPerRound = 3;
+constexpr int kGateUpItemsPerRound = 2;   // routed gate/up kernel
+constexpr int kSharedItemsPerRound = 3;   // shared expert's gate/up in the router launch
 // Work items of the gate/up stage: (slot, block of R rows of gate and up).
 template <int KG>
 struct GateUpShape {
@@ -283,15 +271,37 @@ __device__ __forceinline__ void gateup_compute(const GateUpBuf<KG>& b, int rb, i
 }
 
 // ---------------------------------------------------------------- kernel 1
-// Router: logit[e] = sum_h W_r[e][h] x[h] in fp32, one row per wave (lane l
-// covers floats [4l + 256c, 4l + 256c + 4)), turned into s and sb.  The
-// first wave of block 0 also writes the token's activation pairs.
+// Three kinds of workgroups in one launch (the first two stream HBM side by
+// side, so the routing's serial tail overlaps the shared expert's weights):
+//  * router blocks [0, E/4): one W_r row per wave, logit[e] = sum_h
+//    W_r[e][h] x[h] in fp32 (fixed-order sums), turned into s and sb.  The
+//    last router block to finish (device-scope counter:
+//    release of each block's scores, acquire by the last) derives the
+//    group-limited top-k and writes ids, w and the routed slots' blobs, then
+//    resets the counter;
+//  * the next shared_blocks blocks: gate/up + SwiGLU of the shared expert
+//    (it does not depend on the routing), each wave converting the
+//    activations for itself;
+//  * the last block: the activation pairs and their exponent for the
+//    routed experts' kernel.
 template <int KG>
+__host__ __device__ inline int shared_gateup_blocks(int I) {
+    const int per_slot = I / GateUpShape<KG>::R;
+    return (per_slot + 4 * kSharedItemsPerRound - 1) / (4 * kSharedItemsPerRound);
+}
+
+template <int KG, int EPL>
 __global__ void __launch_bounds__(256) router_kernel(DecodeArgs a) {
     using S = GateUpShape<KG>;
+    constexpr int NI = kSharedItemsPerRound;
     const int lane = threadIdx.x & 63;
     const int wave = wave_in_block();
-    if (blockIdx.x == 0 && wave == 0) {
+    const int n_shared_blocks = a.S > 0 ? shared_gateup_blocks<KG>(a.I) : 0;
+    const int n_router_blocks = (a.E + 3) / 4;
+    const int b = blockIdx.x;
+    if (b >= n_router_blocks + n_shared_blocks) {
+        // activations -> scaled fp16 pairs for the routed experts' kernel
+        if (wave != 0) return;
         f16x2 xp[S::CPL][16];
         const int kx = convert_activation_pairs<KG>(a.x, lane, xp);
 #pragma unroll
@@ -306,19 +316,48 @@ __global__ void __launch_bounds__(256) router_kernel(DecodeArgs a) {
             }
         }
         if (lane == 0) *a.kx = kx;
+        return;
     }
-    constexpr int CR = KG / 8;  // H / 256
-    float xr[CR][4];
+    if (b >= n_router_blocks) {
+        // shared expert gate/up: items of R rows, rounds of NI per wave
+        const int per_slot = a.I / S::R;
+        const int wave_id = (b - n_router_blocks) * 4 + wave;
+        const int n_waves = n_shared_blocks * 4;
+        if (wave_id >= per_slot) return;
+        const BlobLayout L = blob_layout(a.H, a.I);
+        GateUpBuf<KG> buf[NI];
 #pragma unroll
-    for (int c = 0; c < CR; ++c) {
-        const u32x2 xb = *reinterpret_cast<const u32x2*>(a.x + 4 * lane + 256 * c);
-        xr[c][0] = __builtin_bit_cast(float, xb[0] << 16);
-        xr[c][1] = __builtin_bit_cast(float, xb[0] & 0xFFFF0000u);
-        xr[c][2] = __builtin_bit_cast(float, xb[1] << 16);
-        xr[c][3] = __builtin_bit_cast(float, xb[1] & 0xFFFF0000u);
+        for (int k = 0; k < NI; ++k) {
+            const int it = wave_id + k * n_waves;
+            gateup_issue<KG>(a.shared_blob, L, it < per_slot ? it : per_slot - 1, lane, buf[k]);
+        }
+        f16x2 xp[S::CPL][16];
+        const int kx = convert_activation_pairs<KG>(a.x, lane, xp);
+        float* h = a.h + (size_t)a.K * a.I;
+#pragma unroll
+        for (int k = 0; k < NI; ++k) {
+            const int it = wave_id + k * n_waves;
+            gateup_compute<KG>(buf[k], it < per_slot ? it : per_slot - 1, lane, xp, kx, h, it < per_slot);
+        }
+        for (int base = wave_id + NI * n_waves; base < per_slot; base += NI * n_waves) {
+#pragma unroll
+            for (int k = 0; k < NI; ++k) {
+                const int it = base + k * n_waves;
+                gateup_issue<KG>(a.shared_blob, L, it < per_slot ? it : per_slot - 1, lane, buf[k]);
+            }
+#pragma unroll
+            for (int k = 0; k < NI; ++k) {
+                const int it = base + k * n_waves;
+                gateup_compute<KG>(buf[k], it < per_slot ? it : per_slot - 1, lane, xp, kx, h, it < per_slot);
+            }
+        }
+        return;
     }
-    const int n_router_waves = gridDim.x * 4;
-    for (int e = blockIdx.x * 4 + wave; e < a.E; e += n_router_waves) {
+    // router rows: one per wave (lane l covering floats [4l + 256c, +4)),
+    // fixed-order wave sums
+    constexpr int CR = KG / 8;  // 16-byte chunks per lane of a row
+    const int e = b * 4 + wave;
+    if (e < a.E) {
         const float* row = a.router_w + (size_t)e * a.H;
         f32x4 wv[CR];
 #pragma unroll
@@ -327,30 +366,47 @@ __global__ void __launch_bounds__(256) router_kernel(DecodeArgs a) {
         float acc = 0.0f;
 #pragma unroll
         for (int c = 0; c < CR; ++c) {
-            acc = fmaf(wv[c][0], xr[c][0], acc);
-            acc = fmaf(wv[c][1], xr[c][1], acc);
-            acc = fmaf(wv[c][2], xr[c][2], acc);
-            acc = fmaf(wv[c][3], xr[c][3], acc);
+            const u32x2 xb = *reinterpret_cast<const u32x2*>(a.x + 4 * lane + 256 * c);
+            acc = fmaf(wv[c][0], __builtin_bit_cast(float, xb[0] << 16), acc);
+            acc = fmaf(wv[c][1], __builtin_bit_cast(float, xb[0] & 0xFFFF0000u), acc);
+            acc = fmaf(wv[c][2], __builtin_bit_cast(float, xb[1] << 16), acc);
+            acc = fmaf(wv[c][3], __builtin_bit_cast(float, xb[1] & 0xFFFF0000u), acc);
         }
         acc = wave_sum(acc);
         if (lane == 0) {
-            const float s = 1.0f / (1.0f + expf(-acc));
-            a.s[e] = s;
-            a.sb[e] = s + a.bias[e];
+            const float sv = 1.0f / (1.0f + expf(-acc));
+            a.s[e] = sv;
+            a.sb[e] = sv + a.bias[e];
         }
+    }
+    __shared__ int is_last;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        __threadfence();  // release this block's scores
+        const bool last = atomicAdd(a.counter, 1u) == (unsigned)(n_router_blocks - 1);
+        if (last) a.counter[0] = 0u;  // ready for the next call
+        is_last = last;
+    }
+    __syncthreads();
+    if (!is_last || wave != 0) return;
+    __threadfence();
+    int id;
+    float w;
+    wave_group_topk<EPL>(a.s, a.sb, a.E, a.G, a.TG, a.K, a.rsf, lane, &id, &w);
+    if (lane < a.K) {
+        a.ids[lane] = id;
+        a.w[lane] = w;
+        if (a.table) a.slot_blobs[lane] = a.table[id];
     }
 }
 
 // ---------------------------------------------------------------- kernel 2
-// Items: the shared expert's (when with_shared) come first, then those of
-// the routed slots.  A wave takes items wave_id + j * n_waves in rounds of
-// NI: each round issues the loads of its NI items, then computes them, in
-// straight-line code (items past the end are clamped to the last item and
-// their results not stored), so the compiler's wait counts stay exact and
-// the later items' loads stream while the first ones are computed.  A wave
-// whose first item is a shared one issues its loads before deriving the
-// routing, so HBM streams while the top-k runs.
-template <int KG, int EPL, bool EARLY>
+// Items: (routed slot, block of R rows); blobs from the router's top-k, or
+// given directly by the expert cache.  A wave takes items wave_id + j *
+// n_waves in rounds of NI, in straight-line code (items past the end are
+// clamped to the last item and their results not stored), so the
+// compiler's wait counts stay exact.
+template <int KG>
 __global__ void __launch_bounds__(256) gateup_kernel(DecodeArgs a) {
     using S = GateUpShape<KG>;
     constexpr int NI = kGateUpItemsPerRound;
@@ -360,58 +416,28 @@ __global__ void __launch_bounds__(256) gateup_kernel(DecodeArgs a) {
     const int n_waves = gridDim.x * 4;
     const BlobLayout L = blob_layout(a.H, a.I);
     const int per_slot = a.I / S::R;
-    const int n_shared_items = a.with_shared ? a.S * per_slot : 0;
     const int n_routed_slots = a.use_slot_list ? a.n_slot_list : a.K;
-    const int n_items = n_shared_items + n_routed_slots * per_slot;
+    const int n_items = n_routed_slots * per_slot;
     if (wave_id >= n_items) return;
 
     // Small dependent inputs first (vector loads complete in order, so
     // waiting for them must not mean waiting for weight streams issued
-    // before them): activation pairs, then the routing scores.
+    // before them): activation pairs, their exponent, the routed blobs.
     f16x2 xp[S::CPL][16];
     load_activation_pairs<KG>(a.xpairs, lane, xp);
-    float tk_s[EPL], tk_key[EPL];
-    topk_load<EPL>(a.s, a.sb, a.E, lane, tk_s, tk_key);
-    __builtin_amdgcn_sched_barrier(0);
     const int kx = *a.kx;
-    // EARLY: the launch guarantees every wave's first item is a shared one
-    GateUpBuf<KG> b[NI];
-    if constexpr (EARLY) gateup_issue<KG>(a.shared_blob, L, wave_id % per_slot, lane, b[0]);
-
     // The slot -> blob table goes to this wave's LDS row: looking it up per
     // item then waits only on the LDS counter, whereas reading a register
     // that a global load filled earlier can make the compiler drain every
-    // outstanding weight load first.  The blobs of the chosen experts are
-    // fetched with scalar loads, which do not queue behind vector loads.
+    // outstanding weight load first.
     __shared__ const uint8_t* wave_blobs[4][16];
-    if (a.direct) {
-        if (lane < 16) wave_blobs[wave][lane] = lane_pick(a.blobs, lane);
-    } else {
-        int id;
-        float w;
-        wave_group_topk_values<EPL>(tk_s, tk_key, a.E, a.G, a.TG, a.K, a.rsf, lane, &id, &w);
-        // all table reads before any global store of this kernel, with
-        // wave-uniform addresses, so they can be scalar loads
-        const uint8_t* mine = nullptr;
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            if (j < a.K) {
-                const uint8_t* p = a.table[__builtin_amdgcn_readlane(id, j)];
-                if (lane == j) mine = p;
-            }
-        }
-        if (lane < 16) wave_blobs[wave][lane] = mine;
-        if (wave_id == 0 && lane < a.K) {
-            a.ids[lane] = id;
-            a.w[lane] = w;
-            a.slot_blobs[lane] = mine;
-        }
-    }
+    if (lane < 16) wave_blobs[wave][lane] = a.direct ? lane_pick(a.blobs, lane)
+                                                     : (lane < a.K ? a.slot_blobs[lane] : nullptr);
     __builtin_amdgcn_wave_barrier();
     // Settle the activation registers here, once: an empty asm that reads
     // and rewrites each of them makes the compiler wait for their loads at
-    // this point (after the top-k hid that latency) and treat them as
-    // ready afterwards, instead of re-waiting for them behind weight loads.
+    // this point and treat them as ready afterwards, instead of re-waiting
+    // for them behind weight loads.
 #pragma unroll
     for (int c = 0; c < S::CPL; ++c)
 #pragma unroll
@@ -420,11 +446,11 @@ __global__ void __launch_bounds__(256) gateup_kernel(DecodeArgs a) {
             asm volatile("" : "+v"(r));
             xp[c][k] = __builtin_bit_cast(f16x2, r);
         }
+    GateUpBuf<KG> b[NI];
 
     // item -> (slot, row block)
     auto slot_of = [&](int item) {
-        if (item < n_shared_items) return a.K + item / per_slot;
-        const int k = (item - n_shared_items) / per_slot;
+        const int k = item / per_slot;
         int s = k;
         if (a.use_slot_list) {
 #pragma unroll
@@ -433,10 +459,8 @@ __global__ void __launch_bounds__(256) gateup_kernel(DecodeArgs a) {
         }
         return s;
     };
-    auto rb_of = [&](int item) {
-        return item < n_shared_items ? item % per_slot : (item - n_shared_items) % per_slot;
-    };
-    auto blob_of = [&](int slot) { return slot >= a.K ? a.shared_blob : wave_blobs[wave][slot]; };
+    auto rb_of = [&](int item) { return item % per_slot; };
+    auto blob_of = [&](int slot) { return wave_blobs[wave][slot]; };
     auto issue = [&](int item, GateUpBuf<KG>& buf) {
         const int it = item < n_items ? item : n_items - 1;
         gateup_issue<KG>(blob_of(slot_of(it)), L, rb_of(it), lane, buf);
@@ -446,10 +470,10 @@ __global__ void __launch_bounds__(256) gateup_kernel(DecodeArgs a) {
         gateup_compute<KG>(buf, rb_of(it), lane, xp, kx, a.h + (size_t)slot_of(it) * a.I, item < n_items);
     };
 
-    // round 0 (with EARLY its first item is already in flight)
-    if constexpr (!EARLY) issue(wave_id, b[0]);
+    // Rounds of NI items: issue the round's loads, then compute it (the
+    // other waves of the SIMD overlap their loads with this compute).
 #pragma unroll
-    for (int k = 1; k < NI; ++k) issue(wave_id + k * n_waves, b[k]);
+    for (int k = 0; k < NI; ++k) issue(wave_id + k * n_waves, b[k]);
 #pragma unroll
     for (int k = 0; k < NI; ++k) compute(wave_id + k * n_waves, b[k]);
     for (int base = wave_id + NI * n_waves; base < n_items; base += NI * n_waves) {
@@ -654,26 +678,26 @@ hipError_t launch_kernel(K kernel, dim3 grid, dim3 block, hipStream_t st, const 
 
 template <int KG>
 hipError_t launch_router(const DecodeArgs& a, hipStream_t st, const LaunchTiming& tm) {
-    return launch_kernel(router_kernel<KG>, dim3((a.E + 3) / 4), dim3(256), st, tm, a);
+    // router blocks, the shared expert's gate/up blocks, one conversion block
+    const dim3 grid((a.E + 3) / 4 + (a.S > 0 ? shared_gateup_blocks<KG>(a.I) : 0) + 1);
+    if (a.E <= 64) return launch_kernel(router_kernel<KG, 1>, grid, dim3(256), st, tm, a);
+    if (a.E <= 128) return launch_kernel(router_kernel<KG, 2>, grid, dim3(256), st, tm, a);
+    return launch_kernel(router_kernel<KG, 4>, grid, dim3(256), st, tm, a);
 }
 
-template <int KG, int EPL>
+template <int KG>
 hipError_t launch_gateup(const DecodeArgs& a, hipStream_t st, const LaunchTiming& tm) {
     const int per_slot = a.I / GateUpShape<KG>::R;
-    const int n_slots = (a.use_slot_list ? a.n_slot_list : a.K) + (a.with_shared ? a.S : 0);
+    const int n_slots = a.use_slot_list ? a.n_slot_list : a.K;
     if (n_slots == 0) return hipSuccess;
     const int items = n_slots * per_slot;
     // at least one round of kGateUpItemsPerRound items per wave, at most
-    // 2048 waves (8 per CU), at least 256 waves when there are enough items
+    // 4096 waves (16 per CU), at least 256 waves when there are enough items
     int waves = (items + kGateUpItemsPerRound - 1) / kGateUpItemsPerRound;
     if (waves < 256) waves = items < 256 ? items : 256;
-    if (waves > 2048) waves = 2048;
+    if (waves > 4096) waves = 4096;
     waves = (waves + 3) / 4 * 4;
-    const int n_shared_items = a.with_shared ? a.S * per_slot : 0;
-    if (n_shared_items >= waves)
-        return launch_kernel(gateup_kernel<KG, EPL, true>, dim3(waves / 4), dim3(256), st, tm, a);
-    else
-        return launch_kernel(gateup_kernel<KG, EPL, false>, dim3(waves / 4), dim3(256), st, tm, a);
+    return launch_kernel(gateup_kernel<KG>, dim3(waves / 4), dim3(256), st, tm, a);
 }
 
 template <int KG, int NLD>
@@ -702,12 +726,6 @@ hipError_t launch_down(const DecodeArgs& a, hipStream_t st, const LaunchTiming& 
     }
 }
 
-template <int KG>
-hipError_t gateup_dispatch_epl(const DecodeArgs& a, hipStream_t st, const LaunchTiming& tm) {
-    if (a.E <= 64) return launch_gateup<KG, 1>(a, st, tm);
-    if (a.E <= 128) return launch_gateup<KG, 2>(a, st, tm);
-    return launch_gateup<KG, 4>(a, st, tm);
-}
 
 }  // namespace
 
@@ -726,24 +744,15 @@ hipError_t decode_router(const DecodeArgs& a, hipStream_t st, const LaunchTiming
     }
 }
 
-hipError_t decode_topk(const DecodeArgs& a, hipStream_t st, const LaunchTiming& tm) {
-    if (a.E <= 64)
-        return launch_kernel(topk_kernel<1>, dim3(1), dim3(64), st, tm, a);
-    else if (a.E <= 128)
-        return launch_kernel(topk_kernel<2>, dim3(1), dim3(64), st, tm, a);
-    else
-        return launch_kernel(topk_kernel<4>, dim3(1), dim3(64), st, tm, a);
-}
-
 hipError_t decode_routed_gateup(const DecodeArgs& a, hipStream_t st, const LaunchTiming& tm) {
     switch (a.H / 32) {
-        case 8: return gateup_dispatch_epl<8>(a, st, tm);
-        case 16: return gateup_dispatch_epl<16>(a, st, tm);
-        case 32: return gateup_dispatch_epl<32>(a, st, tm);
-        case 64: return gateup_dispatch_epl<64>(a, st, tm);
-        case 128: return gateup_dispatch_epl<128>(a, st, tm);
-        case 192: return gateup_dispatch_epl<192>(a, st, tm);
-        case 256: return gateup_dispatch_epl<256>(a, st, tm);
+        case 8: return launch_gateup<8>(a, st, tm);
+        case 16: return launch_gateup<16>(a, st, tm);
+        case 32: return launch_gateup<32>(a, st, tm);
+        case 64: return launch_gateup<64>(a, st, tm);
+        case 128: return launch_gateup<128>(a, st, tm);
+        case 192: return launch_gateup<192>(a, st, tm);
+        case 256: return launch_gateup<256>(a, st, tm);
         default: return hipErrorInvalidValue;
     }
 }

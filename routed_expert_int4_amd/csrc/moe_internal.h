@@ -26,7 +26,7 @@ struct WorkspaceLayout {
     size_t h = 0;              // [K + S][I]
     // batched path (max_T > 1), sized for batch_tokens tokens per launch sequence
     int batch_tokens = 0;
-    size_t b_s = 0, b_sb = 0;  // [Tb][E]
+    size_t b_logit_part = 0;   // [splits][Tb][E] partial router logits
     size_t b_xa = 0;           // [Tb][H] fp16
     size_t b_kx = 0;           // [Tb]
     size_t b_counts = 0, b_offsets = 0, b_perm = 0, b_inv = 0, b_distinct = 0, b_n_distinct = 0;

@@ -12,7 +12,7 @@ struct DecodeArgs {
     const uint16_t* x;               // [H] bf16 bits
     const float* router_w;           // [E][H]
     const float* bias;               // [E]
-    const uint8_t* const* table;     // [E] packed routed expert blobs
+    const uint8_t* const* table;     // [E] packed routed expert blobs (null with an expert cache)
     const uint8_t* shared_blob;      // packed shared expert (when S == 1)
     float* s;                        // [E] router affinities sigmoid(logit) (scratch)
     float* sb;                       // [E] biased scores s + bias (scratch)
@@ -23,6 +23,7 @@ struct DecodeArgs {
     const uint8_t** slot_blobs;      // [16] blobs of the routed slots, resolved once (scratch)
     float* h;                        // [(K + S) * I] scratch
     float* y;                        // [H] output
+    unsigned* counter;               // router blocks done (workspace control word, 0 between calls)
     int H, I, E, G, TG, K, S;
     float rsf;
     // Expert-cache mode: routed slot j reads blobs[j] instead of
@@ -35,9 +36,6 @@ struct DecodeArgs {
     int use_slot_list;
     int n_slot_list;
     int slot_list[16];
-    // Whether this gate/up launch also covers the shared expert (its items
-    // come first; they do not depend on the routing).
-    int with_shared;
 };
 
 // Optional timing of one launch: when start is set the launch stamps start
@@ -47,14 +45,12 @@ struct LaunchTiming {
     hipEvent_t stop = nullptr;
 };
 
-// Router logits -> s, sb; activation pairs.
+// Router logits -> s, sb; group-limited top-k -> ids, w (and slot_blobs
+// from table when it is set); gate/up + SwiGLU of the shared expert;
+// activation pairs.
 hipError_t decode_router(const DecodeArgs& a, hipStream_t st, const LaunchTiming& tm = {});
-// Group-limited top-k from s, sb on one wave -> ids, w.
-hipError_t decode_topk(const DecodeArgs& a, hipStream_t st, const LaunchTiming& tm = {});
-// Gate/up + SwiGLU of the shared expert (with_shared) and the routed
-// experts.  In table mode every wave also derives the routing itself from
-// s, sb (and the first wave writes ids, w and slot_blobs), so no separate
-// top-k launch is needed.
+// Gate/up + SwiGLU of the routed experts (blobs from slot_blobs, or from
+// blobs in direct mode).
 hipError_t decode_routed_gateup(const DecodeArgs& a, hipStream_t st, const LaunchTiming& tm = {});
 // Down projection of every slot and the weighted combine into y.
 hipError_t decode_down_combine(const DecodeArgs& a, hipStream_t st, const LaunchTiming& tm = {});
@@ -85,8 +81,7 @@ struct BatchArgs {
     const float* bias;           // [E]
     const uint8_t* const* table; // [E] packed routed expert blobs
     const uint8_t* shared_blob;  // packed shared expert (S == 1)
-    float* s;                    // [T][E]
-    float* sb;                   // [T][E]
+    float* logit_part;           // [router_splits][T][E] partial router logits
     uint16_t* xa;                // [T][H/32][4][8] scaled fp16 activations, MFMA order
     int* kx;                     // [T] their scaling exponents
     int32_t* ids;                // [T][K]
@@ -107,6 +102,7 @@ struct BatchArgs {
     float* y;                    // [T][H]
     int T, H, I, E, G, TG, K, S;
     int down_p;                  // row-block size of the down scale packing
+    int router_splits;           // column splits of the router (power of two, hidden % (64 * splits) == 0)
     float rsf;
 };
 
@@ -114,6 +110,14 @@ struct BatchArgs {
 inline int batch_max_tiles(int T, int K, int E, int S) {
     const int n = T * K;
     return (n < E ? n : E) + (n + kTileTokens - 1) / kTileTokens + S * ((T + kTileTokens - 1) / kTileTokens);
+}
+
+// Router column splits for a hidden size: the largest power of two <= 16
+// with hidden % (64 * splits) == 0.
+inline int batch_router_splits(int hidden) {
+    int s = 16;
+    while (s > 1 && hidden % (64 * s)) s /= 2;
+    return s;
 }
 
 hipError_t batch_router(const BatchArgs& a, hipStream_t st);

@@ -103,6 +103,15 @@ def _scales(rng: np.random.Generator, shape) -> np.ndarray:
     return np.exp(z * np.float32(0.5) - np.float32(4.0)).astype(np.float16).view(np.uint16)
 
 
+def gen_router(cfg: LayerConfig, seed: int):
+    """The router weight and bias of gen_layer(cfg, seed), without the experts."""
+    child = np.random.SeedSequence(seed).spawn(1 + cfg.n_total_experts)[0]
+    rng = np.random.Generator(np.random.PCG64(child))
+    router_w = rng.normal(0.0, 0.02, size=(cfg.n_experts, cfg.hidden)).astype(np.float32)
+    bias = rng.normal(0.0, 0.01, size=(cfg.n_experts,)).astype(np.float32)
+    return router_w, bias
+
+
 def gen_layer(cfg: LayerConfig, seed: int, workers: int | None = None) -> LayerWeights:
     """One layer from `seed`.  SeedSequence(seed) spawns one child stream for
     the router (weight, then bias) and one per expert (routed 0..E-1, then
@@ -112,9 +121,7 @@ def gen_layer(cfg: LayerConfig, seed: int, workers: int | None = None) -> LayerW
 
     h, i, e_all = cfg.hidden, cfg.inter, cfg.n_total_experts
     children = np.random.SeedSequence(seed).spawn(1 + e_all)
-    rng = np.random.Generator(np.random.PCG64(children[0]))
-    router_w = rng.normal(0.0, 0.02, size=(cfg.n_experts, h)).astype(np.float32)
-    bias = rng.normal(0.0, 0.01, size=(cfg.n_experts,)).astype(np.float32)
+    router_w, bias = gen_router(cfg, seed)
     gq = np.empty((e_all, i, h // 2), np.uint8)
     gs = np.empty((e_all, i, h // 32), np.uint16)
     uq = np.empty_like(gq)

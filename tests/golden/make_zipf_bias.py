@@ -12,7 +12,11 @@ computed once by the oracle; only the selection is repeated per iteration, by
 the oracle's selection routine.  Only oracle/ and the input generators are
 used.
 
-Run: python tests/golden/make_zipf_bias.py   (writes zipf_bias_glm.json here)
+Run: python tests/golden/make_zipf_bias.py           (zipf_bias_glm.json: the
+     GLM-shaped layer of weights seed 0, permutation seed 2, tokens seed 3)
+     python tests/golden/make_zipf_bias.py --stack   (zipf_bias_stack.json:
+     12 stacked layers, layer l of weights seed 100 + l, permutation seed
+     200 + l, calibration tokens seed 250 + l)
 """
 import json
 import os
@@ -48,16 +52,16 @@ def capped_zipf_targets(n_experts, top_k, s, perm_seed):
     return ranks, np.minimum(1.0, c * base), c
 
 
-def main():
+def calibrate(weights_seed, perm_seed, cal_seed, verbose=True):
     cfg = synth.GLM
-    weights = synth.gen_layer(cfg, seed=0)
-    ranks, target, c = capped_zipf_targets(cfg.n_experts, cfg.top_k, ZIPF_S, PERM_SEED)
-    x = synth.gen_tokens(cfg, N_CAL, seed=CAL_SEED)
+    router_w, _ = synth.gen_router(cfg, weights_seed)
+    ranks, target, c = capped_zipf_targets(cfg.n_experts, cfg.top_k, ZIPF_S, perm_seed)
+    x = synth.gen_tokens(cfg, N_CAL, seed=cal_seed)
     xf = synth.bf16_bits_to_f32(x).astype(np.float64)
     zero_bias = np.zeros(cfg.n_experts, np.float32)
     s_all = np.empty((N_CAL, cfg.n_experts), np.float64)
     for t in range(N_CAL):
-        _, s_all[t], _ = oracle.router_scores(weights.router_w, zero_bias, xf[t])
+        _, s_all[t], _ = oracle.router_scores(router_w, zero_bias, xf[t])
     b = np.zeros(cfg.n_experts, np.float64)
     best = None
     for it in range(ITERS):
@@ -71,26 +75,47 @@ def main():
         err = float(np.abs(freq - target).max())
         if best is None or err < best[0]:
             best = (err, b32.copy(), freq.copy())
-        if it % 20 == 0:
-            print(f"iter {it}: max |freq - target| = {err:.4f}", flush=True)
+        if verbose and it % 20 == 0:
+            print(f"seed {weights_seed} iter {it}: max |freq - target| = {err:.4f}", flush=True)
         b = b + ETA * (target - freq)
     err, b_best, freq = best
     order = np.argsort(ranks)
     live = freq[order] > 0
     r = np.arange(1, cfg.n_experts + 1)[live]
     slope = float(np.polyfit(np.log(r[1:]), np.log(freq[order][live][1:]), 1)[0])
-    out = {
-        "what": "correction bias of the GLM-shaped layer (weights seed 0) for capped Zipf(1.1) routing",
-        "zipf_s": ZIPF_S, "perm_seed": PERM_SEED, "calibration_seed": CAL_SEED, "calibration_tokens": N_CAL,
-        "iterations": ITERS, "eta": ETA, "c": c, "max_abs_freq_error": err,
-        "realised_loglog_slope_ranks_2_up": slope,
-        "ranks": ranks.tolist(),
-        "bias": [float(v) for v in b_best.astype(np.float32)],
+    return {
+        "weights_seed": weights_seed, "perm_seed": perm_seed, "calibration_seed": cal_seed,
+        "zipf_s": ZIPF_S, "calibration_tokens": N_CAL, "iterations": ITERS, "eta": ETA, "c": c,
+        "max_abs_freq_error": err, "realised_loglog_slope_ranks_2_up": slope,
+        "ranks": ranks.tolist(), "bias": [float(v) for v in b_best.astype(np.float32)],
     }
-    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "zipf_bias_glm.json")
+
+
+def _stack_layer(l):
+    return calibrate(100 + l, 200 + l, 250 + l, verbose=False)
+
+
+def main():
+    here = os.path.dirname(os.path.abspath(__file__))
+    if "--stack" in sys.argv:
+        import multiprocessing
+        with multiprocessing.Pool(4) as pool:
+            layers = pool.map(_stack_layer, range(12))
+        out = {"what": "correction biases of 12 stacked GLM-shaped layers for capped Zipf(1.1) routing",
+               "layers": layers}
+        path = os.path.join(here, "zipf_bias_stack.json")
+        with open(path, "w") as f:
+            json.dump(out, f)
+        print(f"wrote {path}: max errors {[round(l['max_abs_freq_error'], 4) for l in layers]}")
+        return
+    rec = calibrate(0, PERM_SEED, CAL_SEED)
+    out = {"what": "correction bias of the GLM-shaped layer (weights seed 0) for capped Zipf(1.1) routing"}
+    out.update(rec)
+    path = os.path.join(here, "zipf_bias_glm.json")
     with open(path, "w") as f:
         json.dump(out, f)
-    print(f"wrote {path}: max error {err:.4f}, slope {slope:.3f}, c {c:.4f}")
+    print(f"wrote {path}: max error {rec['max_abs_freq_error']:.4f}, slope "
+          f"{rec['realised_loglog_slope_ranks_2_up']:.3f}, c {rec['c']:.4f}")
 
 
 if __name__ == "__main__":

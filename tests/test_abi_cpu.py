@@ -50,6 +50,9 @@ def test_invalid_configs_are_rejected():
     with pytest.raises(B.MoeError) as e:
         B.moe_layer_create(dataclasses.replace(synth.TINY, hidden=96 * 32), None, None, [])
     assert e.value.code == B.MOE_EUNSUPPORTED
+    with pytest.raises(B.MoeError) as e:  # valid shape, but the expert count is not a multiple of 16
+        B.moe_layer_create(dataclasses.replace(synth.TINY, n_experts=24, n_groups=3, topk_group=2), None, None, [])
+    assert e.value.code == B.MOE_EUNSUPPORTED
     with pytest.raises(B.MoeError) as e:
         B.moe_layer_create(synth.TINY, None, None, [])
     assert e.value.code == B.MOE_EINVAL and "NULL" in B.last_error()

@@ -111,8 +111,15 @@ __device__ __forceinline__ void load_scales(const uint16_t* p, unsigned (&d)[(NL
         const u32x2 v = __builtin_nontemporal_load(as_global<u32x2>(p));
         d[0] = v[0];
         d[1] = v[1];
+    } else if constexpr (NL % 8 != 0) {
+        static_assert(NL % 4 == 0, "scale pack");
+#pragma unroll
+        for (int q = 0; q < NL / 4; ++q) {
+            const u32x2 v = __builtin_nontemporal_load(as_global<u32x2>(p) + q);
+            d[2 * q + 0] = v[0];
+            d[2 * q + 1] = v[1];
+        }
     } else {
-        static_assert(NL % 8 == 0, "scale pack");
 #pragma unroll
         for (int q = 0; q < NL / 8; ++q) {
             const u32x4 v = __builtin_nontemporal_load(as_global<u32x4>(p) + q);
@@ -237,12 +244,24 @@ __device__ __forceinline__ void gateup_issue(const uint8_t* __restrict__ blob, c
     }
 }
 
+// Position of h[i] (i < inter) in a slot's h buffer: the order in which the
+// down kernel's lanes read it with contiguous 16-byte loads.  Lane g (group
+// g of a chunk column c, groups of 32 values) reads values 4q..4q+3 of its
+// group with load q of column c, so those 4 values sit at
+// ((c * 8 + q) * G + g) * 4 with G = min(inter / 32, 64).
+__device__ __forceinline__ size_t h_index(int i, int kgi) {
+    const int g = i >> 5, e = i & 31;
+    const int G = kgi < kWave ? kgi : kWave;
+    const int c = g / kWave, gi = g % kWave;
+    return ((size_t)(c * 8 + (e >> 2)) * G + gi) * 4 + (e & 3);
+}
+
 // Computes one item from its loaded buffer: h = silu(g) * u for rows
-// [rb*R, rb*R + R), written as fp32.
+// [rb*R, rb*R + R), written as fp32 at their h_index positions.
 template <int KG>
 __device__ __forceinline__ void gateup_compute(const GateUpBuf<KG>& b, int rb, int lane,
                                                const f16x2 (&xp)[GateUpShape<KG>::CPL][16], int kx,
-                                               float* __restrict__ h_out, bool store) {
+                                               float* __restrict__ h_out, int kgi, bool store) {
     using S = GateUpShape<KG>;
     const int row_sub = KG >= kWave ? 0 : (lane / KG);
     float v[S::NV];
@@ -266,7 +285,7 @@ __device__ __forceinline__ void gateup_compute(const GateUpBuf<KG>& b, int rb, i
         const float g = __builtin_ldexpf(r, -kx);
         const float u = __builtin_ldexpf(other, -kx);
         const float h = g / (1.0f + expf(-g)) * u;
-        h_out[(size_t)rb * S::R + vi * S::RPL + row_sub] = h;
+        h_out[h_index(rb * S::R + vi * S::RPL + row_sub, kgi)] = h;
     }
 }
 
@@ -337,7 +356,7 @@ __global__ void __launch_bounds__(256) router_kernel(DecodeArgs a) {
 #pragma unroll
         for (int k = 0; k < NI; ++k) {
             const int it = wave_id + k * n_waves;
-            gateup_compute<KG>(buf[k], it < per_slot ? it : per_slot - 1, lane, xp, kx, h, it < per_slot);
+            gateup_compute<KG>(buf[k], it < per_slot ? it : per_slot - 1, lane, xp, kx, h, a.I / 32, it < per_slot);
         }
         for (int base = wave_id + NI * n_waves; base < per_slot; base += NI * n_waves) {
 #pragma unroll
@@ -348,7 +367,7 @@ __global__ void __launch_bounds__(256) router_kernel(DecodeArgs a) {
 #pragma unroll
             for (int k = 0; k < NI; ++k) {
                 const int it = base + k * n_waves;
-                gateup_compute<KG>(buf[k], it < per_slot ? it : per_slot - 1, lane, xp, kx, h, it < per_slot);
+                gateup_compute<KG>(buf[k], it < per_slot ? it : per_slot - 1, lane, xp, kx, h, a.I / 32, it < per_slot);
             }
         }
         return;
@@ -467,7 +486,7 @@ __global__ void __launch_bounds__(256) gateup_kernel(DecodeArgs a) {
     };
     auto compute = [&](int item, const GateUpBuf<KG>& buf) {
         const int it = item < n_items ? item : n_items - 1;
-        gateup_compute<KG>(buf, rb_of(it), lane, xp, kx, a.h + (size_t)slot_of(it) * a.I, item < n_items);
+        gateup_compute<KG>(buf, rb_of(it), lane, xp, kx, a.h + (size_t)slot_of(it) * a.I, a.I / 32, item < n_items);
     };
 
     // Rounds of NI items: issue the round's loads, then compute it (the
@@ -495,15 +514,16 @@ struct DownShape {
     static constexpr int WIN = NL < 8 ? NL : 8;  // load steps per round
 };
 
-// h of one slot, this lane's groups (32 floats per chunk column).
-template <int CPL>
+// h of one slot, this lane's groups (32 floats per chunk column), stored
+// in h_index order so that every load is 64 lanes x 16 contiguous bytes.
+template <int CPL, int KG>
 __device__ __forceinline__ void load_h(const float* __restrict__ h, int g0, float (&hv)[CPL][32]) {
+    constexpr int G = KG < kWave ? KG : kWave;
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
-        const float* hg = h + 32 * (g0 + kWave * c);
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
-            const f32x4 t = *reinterpret_cast<const f32x4*>(hg + 4 * q);
+            const f32x4 t = *reinterpret_cast<const f32x4*>(h + ((size_t)(c * 8 + q) * G + g0) * 4);
             hv[c][4 * q + 0] = t[0];
             hv[c][4 * q + 1] = t[1];
             hv[c][4 * q + 2] = t[2];
@@ -576,8 +596,8 @@ __global__ void __launch_bounds__(512) down_combine_kernel(DecodeArgs a) {
     // h of this slot and of the shared expert first: vector loads complete
     // in order, so the conversion below must not wait behind weight loads.
     float hraw[S::CPL][32], shraw[S::CPL][32];
-    load_h<S::CPL>(a.h + (size_t)slot * a.I, g0, hraw);
-    load_h<S::CPL>(a.h + (size_t)K * a.I, g0, shraw);
+    load_h<S::CPL, KG>(a.h + (size_t)slot * a.I, g0, hraw);
+    load_h<S::CPL, KG>(a.h + (size_t)K * a.I, g0, shraw);
     u32x4 code[S::NL][S::CPL];
     auto issue_round = [&](int r) {
 #pragma unroll

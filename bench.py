@@ -33,7 +33,7 @@ def log(msg: str) -> None:
 
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "gateup_kernel_glm_decode_traffic.md")
 KERNEL_SOURCES = [os.path.join(ROOT, "routed_expert_int4_amd", "csrc", f)
-                  for f in ("moe_decode.hip", "moe_kernels.h", "moe_layout.h")]
+                  for f in ("moe_decode.hip", "moe_device.h", "moe_kernels.h", "moe_layout.h")]
 
 
 def algorithmic_bytes(cfg):
@@ -77,7 +77,7 @@ def measured_traffic():
 
     The record holds FETCH_SIZE and WRITE_SIZE per dispatch of the gate/up
     kernel, each scaled by what the counter reads for a device copy of known
-    size, and the digest of the kernel source they were taken on.  Returns
+    size, and the digest of the kernel sources they were taken on.  Returns
     None when there is no record or the kernel source has changed since.
     """
     if not os.path.exists(TRAFFIC_RECORD):

@@ -16,22 +16,56 @@ def pack_expert(weights, e: int, out: np.ndarray | None = None) -> np.ndarray:
     return out
 
 
+def _hip_runtime():
+    """The HIP runtime library (for exact-size pinned host allocations)."""
+    import ctypes
+    global _HIP
+    if _HIP is None:
+        _HIP = ctypes.CDLL("libamdhip64.so")
+        _HIP.hipHostMalloc.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_size_t, ctypes.c_uint]
+        _HIP.hipHostMalloc.restype = ctypes.c_int
+        _HIP.hipHostFree.argtypes = [ctypes.c_void_p]
+        _HIP.hipHostFree.restype = ctypes.c_int
+    return _HIP
+
+
+_HIP = None
+
+
 class HostExpertStore:
     """Packed blobs of one layer's routed experts in pinned host memory
-    [E, expert_bytes], the store an expert cache copies from."""
+    [E, expert_bytes], the store an expert cache copies from.  Allocated
+    with hipHostMalloc at its exact size (a caching pinned allocator would
+    round each multi-GB store up to a power of two)."""
 
     def __init__(self, weights):
-        import torch
+        import ctypes
 
         cfg = weights.cfg
         self.nb = nb = B.moe_expert_bytes(cfg)
-        self.blobs = torch.empty((cfg.n_experts, nb), dtype=torch.uint8, pin_memory=True)
-        view = self.blobs.numpy()
+        self.n = cfg.n_experts
+        ptr = ctypes.c_void_p()
+        rc = _hip_runtime().hipHostMalloc(ctypes.byref(ptr), self.n * nb, 0)
+        if rc != 0 or not ptr.value:
+            raise MemoryError(f"hipHostMalloc of {self.n * nb} bytes failed (error {rc})")
+        self.base = ptr.value
+        view = np.ctypeslib.as_array((ctypes.c_uint8 * (self.n * nb)).from_address(self.base)).reshape(self.n, nb)
         for e in range(cfg.n_experts):
             pack_expert(weights, e, view[e])
 
     def ptr(self, e: int) -> int:
-        return self.blobs[e].data_ptr()
+        return self.base + e * self.nb
+
+    def close(self) -> None:
+        if getattr(self, "base", None):
+            _hip_runtime().hipHostFree(self.base)
+            self.base = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 class ExpertCache:
@@ -67,6 +101,9 @@ class ExpertCache:
         if getattr(self, "handle", None):
             B.expert_cache_destroy(self.handle)
             self.handle = None
+        for store in self.stores.values():
+            store.close()
+        self.stores = {}
 
     def __del__(self):
         try:

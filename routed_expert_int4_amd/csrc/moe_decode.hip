@@ -88,6 +88,10 @@ __device__ __forceinline__ float dot_chunk_hilo(u32x4 c, const f16x2* hp, const 
 // ---------------------------------------------------------------- gate/up
 constexpr int kGateUpItemsPerRound = 2;   // routed gate/up kernel
 constexpr int kSharedItemsPerRound = 3;   // shared expert's gate/up in the router launch
+constexpr int kRouterWavesPerRow = 1;     // waves per router row (1, 2 or 4)
+__host__ __device__ constexpr int router_blocks(int n_experts) {
+    return (n_experts + 4 / kRouterWavesPerRow - 1) / (4 / kRouterWavesPerRow);
+}
 // Work items of the gate/up stage: (slot, block of R rows of gate and up).
 template <int KG>
 struct GateUpShape {
@@ -289,6 +293,33 @@ __device__ __forceinline__ void gateup_compute(const GateUpBuf<KG>& b, int rb, i
     }
 }
 
+// Group-limited top-k of the token from s and sb (written by the router
+// blocks), on one wave: lane j < K receives the j-th choice, its weight and
+// its blob from the table (null without a table, and in lanes >= K).  The
+// table entries of the lane's own experts are fetched beside its scores, so
+// resolving the blobs costs no dependent load.
+template <int EPL>
+__device__ __forceinline__ void route_token(const DecodeArgs& a, int lane, int* id, float* w, const uint8_t** blob) {
+    float sv[EPL], key[EPL];
+    const uint8_t* tab[EPL];
+    topk_load<EPL>(a.s, a.sb, a.E, lane, sv, key);
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+        const int e = lane * EPL + i;
+        tab[i] = a.table && e < a.E ? a.table[e] : nullptr;
+    }
+    wave_group_topk_values<EPL>(sv, key, a.E, a.G, a.TG, a.K, a.rsf, lane, id, w);
+    // lane j < K: the blob of its choice, held by lane id / EPL
+    const int owner = lane < a.K ? *id / EPL : 0, idx = lane < a.K ? *id % EPL : 0;
+    const uint8_t* b = nullptr;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+        const uint8_t* t = shfl_ptr(tab[i], owner);
+        if (i == idx) b = t;
+    }
+    *blob = lane < a.K ? b : nullptr;
+}
+
 // ---------------------------------------------------------------- kernel 1
 // Three kinds of workgroups in one launch (the first two stream HBM side by
 // side, so the routing's serial tail overlaps the shared expert's weights):
@@ -316,7 +347,7 @@ __global__ void __launch_bounds__(256) router_kernel(DecodeArgs a) {
     const int lane = threadIdx.x & 63;
     const int wave = wave_in_block();
     const int n_shared_blocks = a.S > 0 ? shared_gateup_blocks<KG>(a.I) : 0;
-    const int n_router_blocks = (a.E + 3) / 4;
+    const int n_router_blocks = router_blocks(a.E);
     const int b = blockIdx.x;
     if (b >= n_router_blocks + n_shared_blocks) {
         // activations -> scaled fp16 pairs for the routed experts' kernel
@@ -372,31 +403,50 @@ __global__ void __launch_bounds__(256) router_kernel(DecodeArgs a) {
         }
         return;
     }
-    // router rows: one per wave (lane l covering floats [4l + 256c, +4)),
-    // fixed-order wave sums
+    // router rows: kRouterWavesPerRow waves per row, wave q of a row taking
+    // chunks c = q, q + kRouterWavesPerRow, ... (lane l covering floats
+    // [4l + 256c, +4)); fixed-order sums (per wave, then over the row's waves)
     constexpr int CR = KG / 8;  // 16-byte chunks per lane of a row
-    const int e = b * 4 + wave;
+    constexpr int WPR = kRouterWavesPerRow;
+    constexpr int NC = (CR + WPR - 1) / WPR;
+    const int e = b * (4 / WPR) + wave / WPR;
+    const int q = wave % WPR;
+    float acc = 0.0f;
     if (e < a.E) {
         const float* row = a.router_w + (size_t)e * a.H;
-        f32x4 wv[CR];
+        f32x4 wv[NC];
 #pragma unroll
-        for (int c = 0; c < CR; ++c)
-            wv[c] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(row + 4 * lane + 256 * c));
-        float acc = 0.0f;
+        for (int k = 0; k < NC; ++k) {
+            const int c = q + k * WPR;
+            if (c < CR) wv[k] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(row + 4 * lane + 256 * c));
+        }
 #pragma unroll
-        for (int c = 0; c < CR; ++c) {
-            const u32x2 xb = *reinterpret_cast<const u32x2*>(a.x + 4 * lane + 256 * c);
-            acc = fmaf(wv[c][0], __builtin_bit_cast(float, xb[0] << 16), acc);
-            acc = fmaf(wv[c][1], __builtin_bit_cast(float, xb[0] & 0xFFFF0000u), acc);
-            acc = fmaf(wv[c][2], __builtin_bit_cast(float, xb[1] << 16), acc);
-            acc = fmaf(wv[c][3], __builtin_bit_cast(float, xb[1] & 0xFFFF0000u), acc);
+        for (int k = 0; k < NC; ++k) {
+            const int c = q + k * WPR;
+            if (c < CR) {
+                const u32x2 xb = *reinterpret_cast<const u32x2*>(a.x + 4 * lane + 256 * c);
+                acc = fmaf(wv[k][0], __builtin_bit_cast(float, xb[0] << 16), acc);
+                acc = fmaf(wv[k][1], __builtin_bit_cast(float, xb[0] & 0xFFFF0000u), acc);
+                acc = fmaf(wv[k][2], __builtin_bit_cast(float, xb[1] << 16), acc);
+                acc = fmaf(wv[k][3], __builtin_bit_cast(float, xb[1] & 0xFFFF0000u), acc);
+            }
         }
         acc = wave_sum(acc);
-        if (lane == 0) {
-            const float sv = 1.0f / (1.0f + expf(-acc));
-            a.s[e] = sv;
-            a.sb[e] = sv + a.bias[e];
+    }
+    if constexpr (WPR > 1) {
+        __shared__ float part[4];
+        if (lane == 0) part[wave] = acc;
+        __syncthreads();
+        if (q == 0) {
+            acc = part[wave];
+#pragma unroll
+            for (int j = 1; j < WPR; ++j) acc += part[wave + j];
         }
+    }
+    if (e < a.E && q == 0 && lane == 0) {
+        const float sv = 1.0f / (1.0f + expf(-acc));
+        a.s[e] = sv;
+        a.sb[e] = sv + a.bias[e];
     }
     __shared__ int is_last;
     __syncthreads();
@@ -411,11 +461,12 @@ __global__ void __launch_bounds__(256) router_kernel(DecodeArgs a) {
     __threadfence();
     int id;
     float w;
-    wave_group_topk<EPL>(a.s, a.sb, a.E, a.G, a.TG, a.K, a.rsf, lane, &id, &w);
+    const uint8_t* blob;
+    route_token<EPL>(a, lane, &id, &w, &blob);
     if (lane < a.K) {
         a.ids[lane] = id;
         a.w[lane] = w;
-        if (a.table) a.slot_blobs[lane] = a.table[id];
+        if (a.table) a.slot_blobs[lane] = blob;
     }
 }
 
@@ -450,8 +501,8 @@ __global__ void __launch_bounds__(256) gateup_kernel(DecodeArgs a) {
     // that a global load filled earlier can make the compiler drain every
     // outstanding weight load first.
     __shared__ const uint8_t* wave_blobs[4][16];
-    if (lane < 16) wave_blobs[wave][lane] = a.direct ? lane_pick(a.blobs, lane)
-                                                     : (lane < a.K ? a.slot_blobs[lane] : nullptr);
+    if (lane < 16)
+        wave_blobs[wave][lane] = a.direct ? lane_pick(a.blobs, lane) : (lane < a.K ? a.slot_blobs[lane] : nullptr);
     __builtin_amdgcn_wave_barrier();
     // Settle the activation registers here, once: an empty asm that reads
     // and rewrites each of them makes the compiler wait for their loads at
@@ -699,7 +750,7 @@ hipError_t launch_kernel(K kernel, dim3 grid, dim3 block, hipStream_t st, const 
 template <int KG>
 hipError_t launch_router(const DecodeArgs& a, hipStream_t st, const LaunchTiming& tm) {
     // router blocks, the shared expert's gate/up blocks, one conversion block
-    const dim3 grid((a.E + 3) / 4 + (a.S > 0 ? shared_gateup_blocks<KG>(a.I) : 0) + 1);
+    const dim3 grid(router_blocks(a.E) + (a.S > 0 ? shared_gateup_blocks<KG>(a.I) : 0) + 1);
     if (a.E <= 64) return launch_kernel(router_kernel<KG, 1>, grid, dim3(256), st, tm, a);
     if (a.E <= 128) return launch_kernel(router_kernel<KG, 2>, grid, dim3(256), st, tm, a);
     return launch_kernel(router_kernel<KG, 4>, grid, dim3(256), st, tm, a);

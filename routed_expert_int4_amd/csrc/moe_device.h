@@ -133,6 +133,25 @@ __device__ __forceinline__ unsigned wave_max_u32(unsigned v) {
     return umax(umax(a, b), umax(c, d));
 }
 
+// DPP move whose result the compiler folds into the consuming VALU op.
+template <int CTRL>
+__device__ __forceinline__ unsigned dpp_mov(unsigned v) {
+    return (unsigned)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, true);
+}
+
+// Maximum over the wave, in every lane: within 16-lane rows by DPP, across
+// rows by the permlane swaps (no scalar round trip).
+__device__ __forceinline__ unsigned wave_max_all(unsigned v) {
+    v = umax(v, dpp_mov<kDppXor1>(v));
+    v = umax(v, dpp_mov<kDppXor2>(v));
+    v = umax(v, dpp_mov<kDppHalfMirror>(v));
+    v = umax(v, dpp_mov<kDppMirror>(v));
+    const auto r32 = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    v = umax(r32[0], r32[1]);
+    const auto r16 = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return umax(r16[0], r16[1]);
+}
+
 // Sum over the wave in a fixed order, returned uniform.
 __device__ __forceinline__ float wave_sum(float v) {
     v += dpp_f<kDppXor1>(v);
@@ -160,6 +179,14 @@ __device__ __forceinline__ const uint8_t* readlane_ptr(const uint8_t* p, int src
     const uint64_t v = reinterpret_cast<uint64_t>(p);
     const unsigned lo = __builtin_amdgcn_readlane((unsigned)v, src);
     const unsigned hi = __builtin_amdgcn_readlane((unsigned)(v >> 32), src);
+    return reinterpret_cast<const uint8_t*>(((uint64_t)hi << 32) | lo);
+}
+
+// Pointer held by lane src, per lane (src may differ between lanes).
+__device__ __forceinline__ const uint8_t* shfl_ptr(const uint8_t* p, int src) {
+    const uint64_t v = reinterpret_cast<uint64_t>(p);
+    const unsigned lo = __shfl((unsigned)v, src);
+    const unsigned hi = __shfl((unsigned)(v >> 32), src);
     return reinterpret_cast<const uint8_t*>(((uint64_t)hi << 32) | lo);
 }
 
@@ -221,54 +248,72 @@ __device__ void wave_group_topk_values(const float (&s)[EPL], const float (&key)
         rank += (o > gscore || (o == gscore && g < my_group)) ? 1 : 0;
     }
     const bool eligible = rank < TG;
-    bool live[EPL];
+    // The lane's candidates as order-preserving unsigned keys (larger float
+    // -> larger key; 0 = not eligible or taken), sorted descending with ties
+    // to the lower expert index; each step takes the wave maximum of the
+    // lanes' heads, the lowest lane holding it wins (lanes own increasing
+    // index ranges), and the winner shifts its list.
+    unsigned u[EPL];
+    int ei[EPL];
+    float sv[EPL];
 #pragma unroll
-    for (int i = 0; i < EPL; ++i) live[i] = eligible && (lane * EPL + i < E);
-
+    for (int i = 0; i < EPL; ++i) {
+        const int e = lane * EPL + i;
+        unsigned v = __builtin_bit_cast(unsigned, key[i]);
+        v = (v & 0x80000000u) ? ~v : (v | 0x80000000u);
+        u[i] = eligible && e < E ? v : 0u;
+        ei[i] = e;
+        sv[i] = s[i];
+    }
+    auto order = [&](int p, int q) {
+        const bool swap = u[q] > u[p] || (u[q] == u[p] && ei[q] < ei[p]);
+        const unsigned tu = u[p];
+        const int te = ei[p];
+        const float ts = sv[p];
+        u[p] = swap ? u[q] : u[p];
+        ei[p] = swap ? ei[q] : ei[p];
+        sv[p] = swap ? sv[q] : sv[p];
+        u[q] = swap ? tu : u[q];
+        ei[q] = swap ? te : ei[q];
+        sv[q] = swap ? ts : sv[q];
+    };
+    if constexpr (EPL == 2) {
+        order(0, 1);
+    } else if constexpr (EPL == 4) {
+        order(0, 1);
+        order(2, 3);
+        order(0, 2);
+        order(1, 3);
+        order(1, 2);
+    }
+    static_assert(EPL == 1 || EPL == 2 || EPL == 4, "experts per lane");
     float sum_s = 0.0f, mine_s = 0.0f;
     int mine_e = 0;
-    for (int j = 0; j < K; ++j) {
-        // lane-local best (lowest index among equals), as an order-preserving
-        // unsigned key (larger float -> larger key; 0 = nothing left)
-        unsigned ob = 0u;
-        int li = 0;
-        float ls = 0.0f;
 #pragma unroll
-        for (int i = 0; i < EPL; ++i) {
-            unsigned u = __builtin_bit_cast(unsigned, key[i]);
-            u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-            if (live[i] && u > ob) {
-                ob = u;
-                li = i;
-                ls = s[i];
+    for (int j = 0; j < 8; ++j) {
+        if (j < K) {
+            const unsigned mx = wave_max_all(u[0]);
+            const int wl = __ffsll((long long)__ballot(u[0] == mx)) - 1;
+            const int we = __builtin_amdgcn_readlane(ei[0], wl);
+            const float se = readlane_f(sv[0], wl);
+            if (lane == wl) {
+#pragma unroll
+                for (int i = 0; i + 1 < EPL; ++i) {
+                    u[i] = u[i + 1];
+                    ei[i] = ei[i + 1];
+                    sv[i] = sv[i + 1];
+                }
+                u[EPL - 1] = 0u;
             }
+            if (lane == j) {
+                mine_e = we;
+                mine_s = se;
+            }
+            sum_s += se;
         }
-        const unsigned mx = wave_max_u32(ob);
-        const unsigned long long hit = __ballot(ob == mx && ob != 0u);
-        const int wl = __ffsll((long long)hit) - 1;  // lowest lane holding the maximum
-        const int wi = __builtin_amdgcn_readlane(li, wl);
-        const float se = readlane_f(ls, wl);
-        if (lane == wl) {
-#pragma unroll
-            for (int i = 0; i < EPL; ++i)
-                if (i == wi) live[i] = false;
-        }
-        if (lane == j) {
-            mine_e = wl * EPL + wi;
-            mine_s = se;
-        }
-        sum_s += se;
     }
     *my_id = mine_e;
     *my_w = rsf * mine_s / sum_s;
-}
-
-template <int EPL>
-__device__ __forceinline__ void wave_group_topk(const float* __restrict__ s_in, const float* __restrict__ sb_in, int E,
-                                                int G, int TG, int K, float rsf, int lane, int* my_id, float* my_w) {
-    float s[EPL], key[EPL];
-    topk_load<EPL>(s_in, sb_in, E, lane, s, key);
-    wave_group_topk_values<EPL>(s, key, E, G, TG, K, rsf, lane, my_id, my_w);
 }
 
 }  // namespace

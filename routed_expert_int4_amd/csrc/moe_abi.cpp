@@ -86,10 +86,8 @@ WorkspaceLayout workspace_layout(const moe_config_t* c, int max_T) {
     o = align256(o + sizeof(float) * (size_t)c->n_experts);
     W.sb = o;
     o = align256(o + sizeof(float) * (size_t)c->n_experts);
-    W.xpairs = o;
-    o = align256(o + (size_t)chunks_per_lane(c->hidden / 32) * kWave * 16 * sizeof(unsigned));
-    W.kx = o;
-    o = align256(o + sizeof(int));
+    W.xq = o;  // 16 byte dwords + (corr, factor) per lane and chunk column
+    o = align256(o + (size_t)chunks_per_lane(c->hidden / 32) * kWave * 18 * sizeof(unsigned));
     W.slot_blobs = o;
     o = align256(o + sizeof(void*) * 16);
     W.ids = o;
@@ -293,8 +291,7 @@ DecodeArgs decode_args(moe_layer_t* L, const uint16_t* x, int32_t* ids, float* w
     a.shared_blob = c.n_shared > 0 ? L->shared[0] : nullptr;
     a.s = reinterpret_cast<float*>(L->ws + L->W.s);
     a.sb = reinterpret_cast<float*>(L->ws + L->W.sb);
-    a.xpairs = reinterpret_cast<unsigned*>(L->ws + L->W.xpairs);
-    a.kx = reinterpret_cast<int*>(L->ws + L->W.kx);
+    a.xq = reinterpret_cast<unsigned*>(L->ws + L->W.xq);
     a.slot_blobs = reinterpret_cast<const uint8_t**>(L->ws + L->W.slot_blobs);
     a.ids = ids;
     a.w = w;

@@ -7,7 +7,7 @@
 //      reductions and writes ids, weights and the routed slots' blobs; in
 //      the same launch other workgroups run the shared expert's gate/up +
 //      SwiGLU (no routing dependency) and convert the token's activations
-//      once into the fp16 pairs of the routed experts' kernel.
+//      once into the integer operands of the routed experts' kernel.
 //   2. gateup: gate/up + SwiGLU of the routed experts; the next items' loads
 //      are in flight while the current ones are computed.
 //   3. down_combine: one wave per routed slot over a block of output rows,
@@ -17,16 +17,15 @@
 //
 // Int4 GEMV scheme.  A lane owns one 32-input scale group of the reduction
 // dimension (several when a row has more than 64 groups) and keeps the
-// matching activations in registers as fp16 pairs; every wave load is 64
-// lanes x 16 contiguous bytes.  A 16-byte chunk holds the 32 codes of one
-// group; each code (stored q+8) is OR-ed into the mantissa of an fp16
-// constant (1024+u or 64+u) and the constant minus 8 is subtracted, which
-// yields q exactly as fp16; v_dot2_f32_f16 then accumulates q*x pairs in
-// fp32.  The fp16 scale is applied once per chunk in fp32.  Partial sums of
+// matching activations in registers; every wave load is 64 lanes x 16
+// contiguous bytes.  A 16-byte chunk holds the 32 codes of one group (stored
+// q+8); masking the even and the odd nibbles gives two dwords of 8-bit codes
+// per code dword, which v_dot4_i32_i8 multiplies with the activations held
+// as exact 8-bit hi and lo parts of a 16-bit fixed-point form of the group
+// (power-of-two scale per group).  The dot is exact in int32; the offset 8 is
+// removed with a per-group correction, and the fp16 weight scale and the
+// group's power of two are applied once per chunk in fp32.  Partial sums of
 // the rows a wave visited are reduced across lanes with a reduce-scatter.
-// Activations are scaled by a power of two before the fp16 conversion so
-// that any finite bf16 input keeps 11 significant bits; the intermediate h
-// of the down projection is split into fp16 hi + lo parts (about 22 bits).
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
@@ -39,50 +38,72 @@
 namespace moe {
 namespace {
 
-// 32 offset-binary codes (public nibble order: column 8d+j at bits 4j of
-// dword d) dotted with activations arranged per dword d as the pairs
-// (x0,x4), (x1,x5), (x2,x6), (x3,x7) of columns 8d..8d+7.
-__device__ __forceinline__ float dot_chunk(u32x4 c, const f16x2* xp, float acc) {
-    const f16x2 k_lo = {(_Float16)1032.0f, (_Float16)1032.0f};  // 1024 + 8
-    const f16x2 k_hi = {(_Float16)72.0f, (_Float16)72.0f};      // 64 + 8
+// One 32-value group of an activation vector (x for gate/up, h for down) as
+// the signed 8-bit operands of v_dot4_i32_i8: the group scaled by a power of
+// two to integers a = round(v 2^k) with |a| <= 2^14, split exactly into
+// a = 256 hi + lo (hi in [-64, 64], lo in [-128, 127]).  Byte j of dword d
+// pairs with nibble 2j (he, le) or 2j + 1 (ho, lo) of code dword d, i.e. with
+// columns 8d + 2j and 8d + 2j + 1 of the group.  The codes hold q + 8, so
+// corr = 8 sum(a) is taken off the integer dot.
+struct HI8 {
+    u32x4 he, ho, le, lo;
+    int corr;
+};
+
+template <int CPL>
+__device__ __forceinline__ void to_i8(const float (&hin)[CPL][32], HI8 (&ha)[CPL], float (&hscale)[CPL]) {
 #pragma unroll
-    for (int d = 0; d < 4; ++d) {
-        const unsigned w = c[d];
-        const unsigned w8 = w >> 8;
-        const f16x2 q0 = as_h2((w & 0x000F000Fu) | 0x64006400u) - k_lo;
-        const f16x2 q1 = as_h2((w & 0x00F000F0u) | 0x54005400u) - k_hi;
-        const f16x2 q2 = as_h2((w8 & 0x000F000Fu) | 0x64006400u) - k_lo;
-        const f16x2 q3 = as_h2((w8 & 0x00F000F0u) | 0x54005400u) - k_hi;
-        acc = __builtin_amdgcn_fdot2(q0, xp[4 * d + 0], acc, false);
-        acc = __builtin_amdgcn_fdot2(q1, xp[4 * d + 1], acc, false);
-        acc = __builtin_amdgcn_fdot2(q2, xp[4 * d + 2], acc, false);
-        acc = __builtin_amdgcn_fdot2(q3, xp[4 * d + 3], acc, false);
+    for (int c = 0; c < CPL; ++c) {
+        const float (&hv)[32] = hin[c];
+        unsigned mx = 0;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) mx = umax(mx, __builtin_bit_cast(unsigned, hv[i]) & 0x7FFFFFFFu);
+        const int kh = range_exponent(mx >> 23);
+        hscale[c] = __builtin_ldexpf(1.0f, -kh);
+        const float up = __builtin_ldexpf(1.0f, kh);
+        int sum = 0;
+        unsigned vhe[4], vho[4], vle[4], vlo[4];
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            unsigned he = 0, ho = 0, le = 0, lo = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int ae = (int)__builtin_rintf(hv[8 * d + 2 * j] * up);
+                const int ao = (int)__builtin_rintf(hv[8 * d + 2 * j + 1] * up);
+                const int hie = (ae + 128) >> 8, hio = (ao + 128) >> 8;
+                he |= ((unsigned)hie & 0xFFu) << (8 * j);
+                ho |= ((unsigned)hio & 0xFFu) << (8 * j);
+                le |= ((unsigned)(ae - (hie << 8)) & 0xFFu) << (8 * j);
+                lo |= ((unsigned)(ao - (hio << 8)) & 0xFFu) << (8 * j);
+                sum += ae + ao;
+            }
+            vhe[d] = he;
+            vho[d] = ho;
+            vle[d] = le;
+            vlo[d] = lo;
+        }
+        ha[c].he = u32x4{vhe[0], vhe[1], vhe[2], vhe[3]};
+        ha[c].ho = u32x4{vho[0], vho[1], vho[2], vho[3]};
+        ha[c].le = u32x4{vle[0], vle[1], vle[2], vle[3]};
+        ha[c].lo = u32x4{vlo[0], vlo[1], vlo[2], vlo[3]};
+        ha[c].corr = 8 * sum;
     }
-    return acc;
 }
 
-// As dot_chunk with the activation given as hi + lo fp16 parts.
-__device__ __forceinline__ float dot_chunk_hilo(u32x4 c, const f16x2* hp, const f16x2* lp, float acc) {
-    const f16x2 k_lo = {(_Float16)1032.0f, (_Float16)1032.0f};
-    const f16x2 k_hi = {(_Float16)72.0f, (_Float16)72.0f};
+// Exact integer dot of one 16-byte code chunk (32 columns of a group) with
+// h in the HI8 form: sum_k q_k a_k, returned as float (|value| < 2^23).
+__device__ __forceinline__ float dot_chunk_i8(u32x4 c, const HI8& a) {
+    int hi = 0, lo = 0;
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
-        const unsigned w = c[d];
-        const unsigned w8 = w >> 8;
-        const f16x2 q0 = as_h2((w & 0x000F000Fu) | 0x64006400u) - k_lo;
-        const f16x2 q1 = as_h2((w & 0x00F000F0u) | 0x54005400u) - k_hi;
-        const f16x2 q2 = as_h2((w8 & 0x000F000Fu) | 0x64006400u) - k_lo;
-        const f16x2 q3 = as_h2((w8 & 0x00F000F0u) | 0x54005400u) - k_hi;
-        acc = __builtin_amdgcn_fdot2(q0, hp[4 * d + 0], acc, false);
-        acc = __builtin_amdgcn_fdot2(q0, lp[4 * d + 0], acc, false);
-        acc = __builtin_amdgcn_fdot2(q1, hp[4 * d + 1], acc, false);
-        acc = __builtin_amdgcn_fdot2(q1, lp[4 * d + 1], acc, false);
-        acc = __builtin_amdgcn_fdot2(q2, hp[4 * d + 2], acc, false);
-        acc = __builtin_amdgcn_fdot2(q2, lp[4 * d + 2], acc, false);
-        acc = __builtin_amdgcn_fdot2(q3, hp[4 * d + 3], acc, false);
-        acc = __builtin_amdgcn_fdot2(q3, lp[4 * d + 3], acc, false);
+        const unsigned w = c[d], he = a.he[d], ho = a.ho[d], le = a.le[d], lo_ = a.lo[d];
+        const int e = (int)(w & 0x0F0F0F0Fu), o = (int)((w >> 4) & 0x0F0F0F0Fu);
+        hi = __builtin_amdgcn_sdot4(e, (int)he, hi, false);
+        hi = __builtin_amdgcn_sdot4(o, (int)ho, hi, false);
+        lo = __builtin_amdgcn_sdot4(e, (int)le, lo, false);
+        lo = __builtin_amdgcn_sdot4(o, (int)lo_, lo, false);
     }
-    return acc;
+    return (float)(hi * 256 + lo - a.corr);
 }
 
 // ---------------------------------------------------------------- gate/up
@@ -139,75 +160,65 @@ __device__ __forceinline__ float scale_at(const unsigned (&d)[N], int n) {
     return half_bits_to_float((n & 1) ? (d[n / 2] >> 16) : (d[n / 2] & 0xFFFFu));
 }
 
-// Loads this lane's activation groups (bf16) and converts them to scaled
-// fp16 pairs; returns the scaling exponent kx (activations * 2^kx).
+// This lane's activation groups (bf16, natural column order) in the HI8
+// form, with the per-group factor that undoes the integer scaling.
 template <int KG>
-__device__ __forceinline__ int convert_activation_pairs(const uint16_t* __restrict__ x, int lane,
-                                                        f16x2 (&xp)[GateUpShape<KG>::CPL][16]) {
+__device__ __forceinline__ void convert_activations(const uint16_t* __restrict__ x, int lane,
+                                                    HI8 (&xa)[GateUpShape<KG>::CPL], float (&xs)[GateUpShape<KG>::CPL]) {
     using S = GateUpShape<KG>;
     const int g0 = KG >= kWave ? lane : (lane & (KG - 1));
-    u32x4 raw[S::CPL][4];
-    unsigned mx = 0;
+    float xv[S::CPL][32];
 #pragma unroll
     for (int c = 0; c < S::CPL; ++c) {
         const uint16_t* xg = x + 32 * (g0 + kWave * c);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            raw[c][q] = *reinterpret_cast<const u32x4*>(xg + 8 * q);
+            const u32x4 raw = *reinterpret_cast<const u32x4*>(xg + 8 * q);
 #pragma unroll
             for (int z = 0; z < 4; ++z) {
-                const unsigned d = raw[c][q][z];
-                mx = umax(mx, umax(d & 0x7FFFu, (d >> 16) & 0x7FFFu));
+                const unsigned d = raw[z];
+                xv[c][8 * q + 2 * z] = __builtin_bit_cast(float, d << 16);
+                xv[c][8 * q + 2 * z + 1] = __builtin_bit_cast(float, d & 0xFFFF0000u);
             }
         }
     }
-    mx = wave_max_u32(mx);
-    const int kx = range_exponent((mx >> 7) & 0xFFu);
-    const float sc = __builtin_ldexpf(1.0f, kx);
-#pragma unroll
-    for (int c = 0; c < S::CPL; ++c) {
-        unsigned dw[16];
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-#pragma unroll
-            for (int z = 0; z < 4; ++z) dw[4 * q + z] = raw[c][q][z];
-        // columns 8d..8d+7 live in dwords 4d..4d+3 (two bf16 each)
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const unsigned da = dw[4 * d + j / 2], db = dw[4 * d + 2 + j / 2];
-                const unsigned ba = (j & 1) ? (da & 0xFFFF0000u) : (da << 16);
-                const unsigned bb = (j & 1) ? (db & 0xFFFF0000u) : (db << 16);
-                const float fa = __builtin_bit_cast(float, ba) * sc;
-                const float fb = __builtin_bit_cast(float, bb) * sc;
-                xp[c][4 * d + j] = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(fa, fb));
-            }
-        }
-    }
-    return kx;
+    to_i8<S::CPL>(xv, xa, xs);
 }
 
-// Activation pairs as written by the router kernel: lane l, chunk column c
-// at dwords [(c*64 + l)*16, +16).
+// Converted activations in the workspace: lane l, chunk column c holds the
+// 16 byte dwords at [(c*64 + l)*16, +16) and (corr, factor) at
+// meta + (c*64 + l)*2, meta = 16*64*CPL dwords on.
 template <int KG>
-__device__ __forceinline__ void load_activation_pairs(const unsigned* __restrict__ xpairs, int lane,
-                                                      f16x2 (&xp)[GateUpShape<KG>::CPL][16]) {
+__device__ __forceinline__ void store_activations(unsigned* __restrict__ xq, int lane,
+                                                  const HI8 (&xa)[GateUpShape<KG>::CPL],
+                                                  const float (&xs)[GateUpShape<KG>::CPL]) {
     using S = GateUpShape<KG>;
 #pragma unroll
     for (int c = 0; c < S::CPL; ++c) {
-        const u32x4* p = reinterpret_cast<const u32x4*>(xpairs + ((size_t)c * kWave + lane) * 16);
+        u32x4* p = reinterpret_cast<u32x4*>(xq + ((size_t)c * kWave + lane) * 16);
+        p[0] = xa[c].he;
+        p[1] = xa[c].ho;
+        p[2] = xa[c].le;
+        p[3] = xa[c].lo;
+        u32x2* m = reinterpret_cast<u32x2*>(xq + (size_t)16 * kWave * S::CPL + ((size_t)c * kWave + lane) * 2);
+        *m = u32x2{(unsigned)xa[c].corr, __builtin_bit_cast(unsigned, xs[c])};
+    }
+}
+template <int KG>
+__device__ __forceinline__ void load_activations(const unsigned* __restrict__ xq, int lane,
+                                                 HI8 (&xa)[GateUpShape<KG>::CPL], float (&xs)[GateUpShape<KG>::CPL]) {
+    using S = GateUpShape<KG>;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const u32x4 v = p[q];
-            // element copied to a scalar first: __builtin_bit_cast applied to
-            // an ext-vector element reads the vector's first element
-#pragma unroll
-            for (int z = 0; z < 4; ++z) {
-                const unsigned e = v[z];
-                xp[c][4 * q + z] = __builtin_bit_cast(f16x2, e);
-            }
-        }
+    for (int c = 0; c < S::CPL; ++c) {
+        const u32x4* p = reinterpret_cast<const u32x4*>(xq + ((size_t)c * kWave + lane) * 16);
+        xa[c].he = p[0];
+        xa[c].ho = p[1];
+        xa[c].le = p[2];
+        xa[c].lo = p[3];
+        const u32x2 m = *reinterpret_cast<const u32x2*>(xq + (size_t)16 * kWave * S::CPL + ((size_t)c * kWave + lane) * 2);
+        const unsigned m0 = m[0], m1 = m[1];
+        xa[c].corr = (int)m0;
+        xs[c] = __builtin_bit_cast(float, m1);
     }
 }
 
@@ -264,8 +275,9 @@ __device__ __forceinline__ size_t h_index(int i, int kgi) {
 // [rb*R, rb*R + R), written as fp32 at their h_index positions.
 template <int KG>
 __device__ __forceinline__ void gateup_compute(const GateUpBuf<KG>& b, int rb, int lane,
-                                               const f16x2 (&xp)[GateUpShape<KG>::CPL][16], int kx,
-                                               float* __restrict__ h_out, int kgi, bool store) {
+                                               const HI8 (&xa)[GateUpShape<KG>::CPL],
+                                               const float (&xs)[GateUpShape<KG>::CPL], float* __restrict__ h_out,
+                                               int kgi, bool store) {
     using S = GateUpShape<KG>;
     const int row_sub = KG >= kWave ? 0 : (lane / KG);
     float v[S::NV];
@@ -274,8 +286,8 @@ __device__ __forceinline__ void gateup_compute(const GateUpBuf<KG>& b, int rb, i
         float ag = 0.0f, au = 0.0f;
 #pragma unroll
         for (int c = 0; c < S::CPL; ++c) {
-            ag = fmaf(scale_at(b.sgu[c], n), dot_chunk(b.cg[n][c], xp[c], 0.0f), ag);
-            au = fmaf(scale_at(b.sgu[c], S::NL + n), dot_chunk(b.cu[n][c], xp[c], 0.0f), au);
+            ag = fmaf(scale_at(b.sgu[c], n) * xs[c], dot_chunk_i8(b.cg[n][c], xa[c]), ag);
+            au = fmaf(scale_at(b.sgu[c], S::NL + n) * xs[c], dot_chunk_i8(b.cu[n][c], xa[c]), au);
         }
         v[n] = ag;
         v[S::NL + n] = au;
@@ -286,8 +298,7 @@ __device__ __forceinline__ void gateup_compute(const GateUpBuf<KG>& b, int rb, i
     const int low_bits = S::B - ilog2(S::NV);
     const int vi = (lane >> low_bits) & (S::NV - 1);
     if (store && vi < S::NL && (lane & ((1 << low_bits) - 1)) == 0) {
-        const float g = __builtin_ldexpf(r, -kx);
-        const float u = __builtin_ldexpf(other, -kx);
+        const float g = r, u = other;
         const float h = g / (1.0f + expf(-g)) * u;
         h_out[h_index(rb * S::R + vi * S::RPL + row_sub, kgi)] = h;
     }
@@ -350,22 +361,12 @@ __global__ void __launch_bounds__(256) router_kernel(DecodeArgs a) {
     const int n_router_blocks = router_blocks(a.E);
     const int b = blockIdx.x;
     if (b >= n_router_blocks + n_shared_blocks) {
-        // activations -> scaled fp16 pairs for the routed experts' kernel
+        // activations -> integer operands for the routed experts' kernel
         if (wave != 0) return;
-        f16x2 xp[S::CPL][16];
-        const int kx = convert_activation_pairs<KG>(a.x, lane, xp);
-#pragma unroll
-        for (int c = 0; c < S::CPL; ++c) {
-            u32x4* p = reinterpret_cast<u32x4*>(a.xpairs + ((size_t)c * kWave + lane) * 16);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                u32x4 v;
-#pragma unroll
-                for (int z = 0; z < 4; ++z) v[z] = __builtin_bit_cast(unsigned, xp[c][4 * q + z]);
-                p[q] = v;
-            }
-        }
-        if (lane == 0) *a.kx = kx;
+        HI8 xa[S::CPL];
+        float xs[S::CPL];
+        convert_activations<KG>(a.x, lane, xa, xs);
+        store_activations<KG>(a.xq, lane, xa, xs);
         return;
     }
     if (b >= n_router_blocks) {
@@ -381,13 +382,14 @@ __global__ void __launch_bounds__(256) router_kernel(DecodeArgs a) {
             const int it = wave_id + k * n_waves;
             gateup_issue<KG>(a.shared_blob, L, it < per_slot ? it : per_slot - 1, lane, buf[k]);
         }
-        f16x2 xp[S::CPL][16];
-        const int kx = convert_activation_pairs<KG>(a.x, lane, xp);
+        HI8 xa[S::CPL];
+        float xs[S::CPL];
+        convert_activations<KG>(a.x, lane, xa, xs);
         float* h = a.h + (size_t)a.K * a.I;
 #pragma unroll
         for (int k = 0; k < NI; ++k) {
             const int it = wave_id + k * n_waves;
-            gateup_compute<KG>(buf[k], it < per_slot ? it : per_slot - 1, lane, xp, kx, h, a.I / 32, it < per_slot);
+            gateup_compute<KG>(buf[k], it < per_slot ? it : per_slot - 1, lane, xa, xs, h, a.I / 32, it < per_slot);
         }
         for (int base = wave_id + NI * n_waves; base < per_slot; base += NI * n_waves) {
 #pragma unroll
@@ -398,7 +400,7 @@ __global__ void __launch_bounds__(256) router_kernel(DecodeArgs a) {
 #pragma unroll
             for (int k = 0; k < NI; ++k) {
                 const int it = base + k * n_waves;
-                gateup_compute<KG>(buf[k], it < per_slot ? it : per_slot - 1, lane, xp, kx, h, a.I / 32, it < per_slot);
+                gateup_compute<KG>(buf[k], it < per_slot ? it : per_slot - 1, lane, xa, xs, h, a.I / 32, it < per_slot);
             }
         }
         return;
@@ -492,10 +494,10 @@ __global__ void __launch_bounds__(256) gateup_kernel(DecodeArgs a) {
 
     // Small dependent inputs first (vector loads complete in order, so
     // waiting for them must not mean waiting for weight streams issued
-    // before them): activation pairs, their exponent, the routed blobs.
-    f16x2 xp[S::CPL][16];
-    load_activation_pairs<KG>(a.xpairs, lane, xp);
-    const int kx = *a.kx;
+    // before them): activation operands, the routed blobs.
+    HI8 xa[S::CPL];
+    float xs[S::CPL];
+    load_activations<KG>(a.xq, lane, xa, xs);
     // The slot -> blob table goes to this wave's LDS row: looking it up per
     // item then waits only on the LDS counter, whereas reading a register
     // that a global load filled earlier can make the compiler drain every
@@ -509,13 +511,10 @@ __global__ void __launch_bounds__(256) gateup_kernel(DecodeArgs a) {
     // this point and treat them as ready afterwards, instead of re-waiting
     // for them behind weight loads.
 #pragma unroll
-    for (int c = 0; c < S::CPL; ++c)
-#pragma unroll
-        for (int k = 0; k < 16; ++k) {
-            unsigned r = __builtin_bit_cast(unsigned, xp[c][k]);
-            asm volatile("" : "+v"(r));
-            xp[c][k] = __builtin_bit_cast(f16x2, r);
-        }
+    for (int c = 0; c < S::CPL; ++c) {
+        asm volatile("" : "+v"(xa[c].he), "+v"(xa[c].ho), "+v"(xa[c].le), "+v"(xa[c].lo));
+        asm volatile("" : "+v"(xa[c].corr), "+v"(xs[c]));
+    }
     GateUpBuf<KG> b[NI];
 
     // item -> (slot, row block)
@@ -537,7 +536,7 @@ __global__ void __launch_bounds__(256) gateup_kernel(DecodeArgs a) {
     };
     auto compute = [&](int item, const GateUpBuf<KG>& buf) {
         const int it = item < n_items ? item : n_items - 1;
-        gateup_compute<KG>(buf, rb_of(it), lane, xp, kx, a.h + (size_t)slot_of(it) * a.I, a.I / 32, item < n_items);
+        gateup_compute<KG>(buf, rb_of(it), lane, xa, xs, a.h + (size_t)slot_of(it) * a.I, a.I / 32, item < n_items);
     };
 
     // Rounds of NI items: issue the round's loads, then compute it (the
@@ -579,34 +578,6 @@ __device__ __forceinline__ void load_h(const float* __restrict__ h, int g0, floa
             hv[c][4 * q + 1] = t[1];
             hv[c][4 * q + 2] = t[2];
             hv[c][4 * q + 3] = t[3];
-        }
-    }
-}
-
-// h scaled per group to [2^13, 2^14) and split into fp16 hi + lo pairs in the
-// chunk's column order; hscale undoes the scaling.
-template <int CPL>
-__device__ __forceinline__ void h_to_pairs(const float (&hin)[CPL][32], f16x2 (&hp)[CPL][16], f16x2 (&lp)[CPL][16],
-                                           float (&hscale)[CPL]) {
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-        const float (&hv)[32] = hin[c];
-        unsigned mx = 0;
-#pragma unroll
-        for (int i = 0; i < 32; ++i) mx = umax(mx, __builtin_bit_cast(unsigned, hv[i]) & 0x7FFFFFFFu);
-        const int kh = range_exponent(mx >> 23);
-        hscale[c] = __builtin_ldexpf(1.0f, -kh);
-        const float up = __builtin_ldexpf(1.0f, kh);
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const float fa = hv[8 * d + j] * up, fb = hv[8 * d + j + 4] * up;
-                const f16x2 hi = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(fa, fb));
-                const float ra = fa - (float)hi[0], rb = fb - (float)hi[1];
-                hp[c][4 * d + j] = hi;
-                lp[c][4 * d + j] = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(ra, rb));
-            }
         }
     }
 }
@@ -681,12 +652,10 @@ __global__ void __launch_bounds__(512) down_combine_kernel(DecodeArgs a) {
     if constexpr (NR > 1) issue_round(1);
     __builtin_amdgcn_sched_barrier(0);
 
-    f16x2 hp[S::CPL][16], lp[S::CPL][16];
-    float hscale[S::CPL];
-    h_to_pairs<S::CPL>(hraw, hp, lp, hscale);
-    f16x2 shp[S::CPL][16], slp[S::CPL][16];
-    float shscale[S::CPL];
-    h_to_pairs<S::CPL>(shraw, shp, slp, shscale);
+    HI8 ha[S::CPL], sha[S::CPL];
+    float hscale[S::CPL], shscale[S::CPL];
+    to_i8<S::CPL>(hraw, ha, hscale);
+    to_i8<S::CPL>(shraw, sha, shscale);
 
     float v[NVP];
 #pragma unroll
@@ -699,7 +668,7 @@ __global__ void __launch_bounds__(512) down_combine_kernel(DecodeArgs a) {
             float acc = 0.0f;
 #pragma unroll
             for (int c = 0; c < S::CPL; ++c)
-                acc = fmaf(scale_at(sc[c], n) * hscale[c], dot_chunk_hilo(code[n][c], hp[c], lp[c], 0.0f), acc);
+                acc = fmaf(scale_at(sc[c], n) * hscale[c], dot_chunk_i8(code[n][c], ha[c]), acc);
             v[n] = acc;
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -710,8 +679,7 @@ __global__ void __launch_bounds__(512) down_combine_kernel(DecodeArgs a) {
         float acc = 0.0f;
 #pragma unroll
         for (int c = 0; c < S::CPL; ++c)
-            acc = fmaf(half_bits_to_float(ssc_bits[t][c]) * shscale[c],
-                       dot_chunk_hilo(scode[t][c], shp[c], slp[c], 0.0f), acc);
+            acc = fmaf(half_bits_to_float(ssc_bits[t][c]) * shscale[c], dot_chunk_i8(scode[t][c], sha[c]), acc);
         v[S::NL + t] = t < n_sh ? acc : 0.0f;
     }
     const float r = reduce_scatter<NVP, S::B>(v, lane);

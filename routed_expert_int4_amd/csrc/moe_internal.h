@@ -18,8 +18,7 @@ struct WorkspaceLayout {
     size_t control_bytes = 0;
     size_t s = 0;              // [E] router affinities of the token in flight
     size_t sb = 0;             // [E] biased scores
-    size_t xpairs = 0;         // activation pairs of the token in flight
-    size_t kx = 0;             // their scaling exponent
+    size_t xq = 0;             // activation operands of the token in flight
     size_t slot_blobs = 0;     // [16] blobs of the routed slots of the token in flight
     size_t ids = 0;            // [max_T][K] when the caller passes no ids buffer
     size_t w = 0;              // [max_T][K]

@@ -16,8 +16,7 @@ struct DecodeArgs {
     const uint8_t* shared_blob;      // packed shared expert (when S == 1)
     float* s;                        // [E] router affinities sigmoid(logit) (scratch)
     float* sb;                       // [E] biased scores s + bias (scratch)
-    unsigned* xpairs;                // activations as scaled fp16 pairs, per lane (scratch)
-    int* kx;                         // their power-of-two scaling exponent (scratch)
+    unsigned* xq;                    // activations as integer dot operands, per lane (scratch)
     int32_t* ids;                    // [K] routing output
     float* w;                        // [K]
     const uint8_t** slot_blobs;      // [16] blobs of the routed slots, resolved once (scratch)

@@ -220,7 +220,7 @@ def bench_cache_stack(args) -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int4 weights x fp16 activations, fp32 accumulate",
+        "dtype": "int4 weights x int16 fixed-point activations (two int8 parts), int32 dot, fp32 accumulate",
         "data": "synthetic (seeded: layer weights 100 + l, Zipf bias per layer, x0 seed 300, noise seed 400)",
         "config": {"workload": f"12 GLM-5.2-shaped MoE layers, {n_tok} sequential decode tokens, 64 HBM slots "
                                "per layer, pinned host expert store, cold start", "layers": n_layers,
@@ -448,7 +448,7 @@ def bench_decode(args) -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int4 weights x fp16 activations, fp32 accumulate",
+        "dtype": "int4 weights x int16 fixed-point activations (two int8 parts), int32 dot, fp32 accumulate",
         "data": "synthetic (seeded: weights seed 0, tokens seed 1)",
         "config": {
             "workload": "GLM-5.2-shaped MoE layer, batch-1 int4 decode, 1000 independent tokens per step",

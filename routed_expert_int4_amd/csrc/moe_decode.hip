@@ -305,7 +305,8 @@ __device__ __forceinline__ void gateup_compute(const GateUpBuf<KG>& b, int rb, i
 }
 
 // Group-limited top-k of the token from s and sb (written by the router
-// blocks), on one wave: lane j < K receives the j-th choice, its weight and
+// blocks with device-scope atomic stores, read back the same way), on one
+// wave: lane j < K receives the j-th choice, its weight and
 // its blob from the table (null without a table, and in lanes >= K).  The
 // table entries of the lane's own experts are fetched beside its scores, so
 // resolving the blobs costs no dependent load.
@@ -313,10 +314,11 @@ template <int EPL>
 __device__ __forceinline__ void route_token(const DecodeArgs& a, int lane, int* id, float* w, const uint8_t** blob) {
     float sv[EPL], key[EPL];
     const uint8_t* tab[EPL];
-    topk_load<EPL>(a.s, a.sb, a.E, lane, sv, key);
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
         const int e = lane * EPL + i;
+        sv[i] = e < a.E ? __hip_atomic_load(a.s + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0.0f;
+        key[i] = e < a.E ? __hip_atomic_load(a.sb + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : -__builtin_inff();
         tab[i] = a.table && e < a.E ? a.table[e] : nullptr;
     }
     wave_group_topk_values<EPL>(sv, key, a.E, a.G, a.TG, a.K, a.rsf, lane, id, w);
@@ -445,22 +447,28 @@ __global__ void __launch_bounds__(256) router_kernel(DecodeArgs a) {
             for (int j = 1; j < WPR; ++j) acc += part[wave + j];
         }
     }
+    // Hand-off of the scores to the last router block without cache-wide
+    // fences: the scores are written and read with device-scope atomic
+    // accesses (coherent across the XCDs' L2s), every wave waits until its
+    // stores are acknowledged before the workgroup takes its ticket, so a
+    // block that draws the last ticket sees every score.  (A release fence
+    // would also write back the whole L2, about 1 us per router block.)
     if (e < a.E && q == 0 && lane == 0) {
         const float sv = 1.0f / (1.0f + expf(-acc));
-        a.s[e] = sv;
-        a.sb[e] = sv + a.bias[e];
+        __hip_atomic_store(a.s + e, sv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(a.sb + e, sv + a.bias[e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
+    __builtin_amdgcn_s_waitcnt(0);
     __shared__ int is_last;
     __syncthreads();
     if (threadIdx.x == 0) {
-        __threadfence();  // release this block's scores
-        const bool last = atomicAdd(a.counter, 1u) == (unsigned)(n_router_blocks - 1);
-        if (last) a.counter[0] = 0u;  // ready for the next call
+        const unsigned ticket = __hip_atomic_fetch_add(a.counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const bool last = ticket == (unsigned)(n_router_blocks - 1);
+        if (last) a.counter[0] = 0u;  // ready for the next call (the launch boundary publishes it)
         is_last = last;
     }
     __syncthreads();
     if (!is_last || wave != 0) return;
-    __threadfence();
     int id;
     float w;
     const uint8_t* blob;

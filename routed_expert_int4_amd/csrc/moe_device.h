@@ -212,20 +212,7 @@ __device__ __forceinline__ void top2_merge(float& a1, float& a2, float b1, float
 // Group-limited top-k of one token on one wave (every lane must call it).
 // Lane l holds experts l*EPL .. l*EPL+EPL-1.  On return lane j < K holds
 // the j-th choice (sb descending, ties to the lower index) in *my_id and its
-// weight rsf * s_j / sum_chosen s in *my_w.  topk_load fetches a lane's
-// scores; wave_group_topk_values selects.
-template <int EPL>
-__device__ __forceinline__ void topk_load(const float* __restrict__ s_in, const float* __restrict__ sb_in, int E,
-                                          int lane, float (&s)[EPL], float (&key)[EPL]) {
-    const float NEG = -__builtin_inff();
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) {
-        const int e = lane * EPL + i;
-        s[i] = e < E ? s_in[e] : 0.0f;
-        key[i] = e < E ? sb_in[e] : NEG;
-    }
-}
-
+// weight rsf * s_j / sum_chosen s in *my_w.
 template <int EPL>
 __device__ void wave_group_topk_values(const float (&s)[EPL], const float (&key)[EPL], int E, int G, int TG, int K,
                                        float rsf, int lane, int* my_id, float* my_w) {

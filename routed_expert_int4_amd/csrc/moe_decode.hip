@@ -39,12 +39,13 @@ namespace moe {
 namespace {
 
 // One 32-value group of an activation vector (x for gate/up, h for down) as
-// the signed 8-bit operands of v_dot4_i32_i8: the group scaled by a power of
-// two to integers a = round(v 2^k) with |a| <= 2^14, split exactly into
-// a = 256 hi + lo (hi in [-64, 64], lo in [-128, 127]).  Byte j of dword d
-// pairs with nibble 2j (he, le) or 2j + 1 (ho, lo) of code dword d, i.e. with
-// columns 8d + 2j and 8d + 2j + 1 of the group.  The codes hold q + 8, so
-// corr = 8 sum(a) is taken off the integer dot.
+// 8-bit dot operands: the group scaled by a power of two to 16-bit integers
+// a = round(v 2^k) (group maximum in [2^14, 2^15)), split exactly into
+// a = 256 hi + lo with hi signed (v_dot4_i32_i8) and lo unsigned in [0, 255]
+// (v_dot4_u32_u8).  Byte j of dword d pairs with nibble 2j (he, le) or 2j + 1
+// (ho, lo) of code dword d, i.e. with columns 8d + 2j and 8d + 2j + 1 of the
+// group.  The codes hold q + 8, so corr = 8 sum(a) is taken off the integer
+// dot; |sum q a| < 2^23, so the int32 result converts to fp32 exactly.
 struct HI8 {
     u32x4 he, ho, le, lo;
     int corr;
@@ -58,23 +59,27 @@ __device__ __forceinline__ void to_i8(const float (&hin)[CPL][32], HI8 (&ha)[CPL
         unsigned mx = 0;
 #pragma unroll
         for (int i = 0; i < 32; ++i) mx = umax(mx, __builtin_bit_cast(unsigned, hv[i]) & 0x7FFFFFFFu);
-        const int kh = range_exponent(mx >> 23);
+        const int kh = range_exponent(mx >> 23) + 1;  // max |v| 2^kh in [2^14, 2^15)
         hscale[c] = __builtin_ldexpf(1.0f, -kh);
         const float up = __builtin_ldexpf(1.0f, kh);
         int sum = 0;
         unsigned vhe[4], vho[4], vle[4], vlo[4];
+        auto fix16 = [&](float v) {
+            const float r = __builtin_rintf(v * up);
+            return (int)(r > 32767.0f ? 32767.0f : (r < -32768.0f ? -32768.0f : r));
+        };
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
             unsigned he = 0, ho = 0, le = 0, lo = 0;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const int ae = (int)__builtin_rintf(hv[8 * d + 2 * j] * up);
-                const int ao = (int)__builtin_rintf(hv[8 * d + 2 * j + 1] * up);
-                const int hie = (ae + 128) >> 8, hio = (ao + 128) >> 8;
-                he |= ((unsigned)hie & 0xFFu) << (8 * j);
-                ho |= ((unsigned)hio & 0xFFu) << (8 * j);
-                le |= ((unsigned)(ae - (hie << 8)) & 0xFFu) << (8 * j);
-                lo |= ((unsigned)(ao - (hio << 8)) & 0xFFu) << (8 * j);
+                const int ae = fix16(hv[8 * d + 2 * j]);
+                const int ao = fix16(hv[8 * d + 2 * j + 1]);
+                // a = 256 hi + lo with hi = floor(a / 256) signed, lo = a mod 256 unsigned
+                he |= ((unsigned)(ae >> 8) & 0xFFu) << (8 * j);
+                ho |= ((unsigned)(ao >> 8) & 0xFFu) << (8 * j);
+                le |= ((unsigned)ae & 0xFFu) << (8 * j);
+                lo |= ((unsigned)ao & 0xFFu) << (8 * j);
                 sum += ae + ao;
             }
             vhe[d] = he;
@@ -100,8 +105,8 @@ __device__ __forceinline__ float dot_chunk_i8(u32x4 c, const HI8& a) {
         const int e = (int)(w & 0x0F0F0F0Fu), o = (int)((w >> 4) & 0x0F0F0F0Fu);
         hi = __builtin_amdgcn_sdot4(e, (int)he, hi, false);
         hi = __builtin_amdgcn_sdot4(o, (int)ho, hi, false);
-        lo = __builtin_amdgcn_sdot4(e, (int)le, lo, false);
-        lo = __builtin_amdgcn_sdot4(o, (int)lo_, lo, false);
+        lo = (int)__builtin_amdgcn_udot4((unsigned)e, le, (unsigned)lo, false);
+        lo = (int)__builtin_amdgcn_udot4((unsigned)o, lo_, (unsigned)lo, false);
     }
     return (float)(hi * 256 + lo - a.corr);
 }
@@ -644,18 +649,28 @@ __global__ void __launch_bounds__(512) down_combine_kernel(DecodeArgs a) {
         load_scales<S::NL>(reinterpret_cast<const uint16_t*>(blob + L.down_s) + si, sc[c]);
     }
     __builtin_amdgcn_sched_barrier(0);
-    // shared rows (clamped to a valid step when this wave has fewer)
+    // shared rows (clamped to a valid step when this wave has fewer); their
+    // scales are consecutive halves of the lane's scale run, fetched as the
+    // ND dwords that cover them (clamped to the run's last dword)
+    constexpr int ND = SSMAX / 2 + 1;
     u32x4 scode[SSMAX][S::CPL];
-    unsigned ssc_bits[SSMAX][S::CPL];
+    unsigned ssw[S::CPL][ND];
+    const int sh0c = sh0 < S::NL ? sh0 : S::NL - 1;
 #pragma unroll
     for (int t = 0; t < SSMAX; ++t) {
         const int step = sh0 + t < S::NL ? sh0 + t : S::NL - 1;
 #pragma unroll
-        for (int c = 0; c < S::CPL; ++c) {
-            scode[t][c] = load_stream16(sblob + L.down_q + code_off(step, c));
-            const size_t si = ((size_t)rb * KG + g0 + kWave * c) * S::R + (size_t)row_sub * S::NL + step;
-            ssc_bits[t][c] = __builtin_nontemporal_load(as_global<uint16_t>(sblob + L.down_s) + si);
-        }
+        for (int c = 0; c < S::CPL; ++c) scode[t][c] = load_stream16(sblob + L.down_q + code_off(step, c));
+    }
+    int sodd[S::CPL];
+#pragma unroll
+    for (int c = 0; c < S::CPL; ++c) {
+        const size_t run = ((size_t)rb * KG + g0 + kWave * c) * S::R + (size_t)row_sub * S::NL;
+        const size_t d0 = (run + sh0c) >> 1, dmax = (run + S::NL - 1) >> 1;
+        sodd[c] = (int)((run + sh0c) & 1);
+#pragma unroll
+        for (int j = 0; j < ND; ++j)
+            ssw[c][j] = __builtin_nontemporal_load(as_global<unsigned>(sblob + L.down_s) + (d0 + j < dmax ? d0 + j : dmax));
     }
     if constexpr (NR > 1) issue_round(1);
     __builtin_amdgcn_sched_barrier(0);
@@ -687,7 +702,12 @@ __global__ void __launch_bounds__(512) down_combine_kernel(DecodeArgs a) {
         float acc = 0.0f;
 #pragma unroll
         for (int c = 0; c < S::CPL; ++c)
-            acc = fmaf(half_bits_to_float(ssc_bits[t][c]) * shscale[c], dot_chunk_i8(scode[t][c], sha[c]), acc);
+        {
+            // half (odd + t) of the covering dwords
+            const unsigned word = ((t & 1) && sodd[c]) ? ssw[c][t / 2 + 1] : ssw[c][t / 2];
+            const unsigned bits = ((sodd[c] + t) & 1) ? (word >> 16) : (word & 0xFFFFu);
+            acc = fmaf(half_bits_to_float(bits) * shscale[c], dot_chunk_i8(scode[t][c], sha[c]), acc);
+        }
         v[S::NL + t] = t < n_sh ? acc : 0.0f;
     }
     const float r = reduce_scatter<NVP, S::B>(v, lane);

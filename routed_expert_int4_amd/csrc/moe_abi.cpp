@@ -162,7 +162,7 @@ moe_status_t moe_expert_pack(const moe_config_t* cfg, const uint8_t* gate_q, con
             for (int g = 0; g < kg; ++g) d[scale_index(r, g, kg, p)] = src[(size_t)r * kg + g];
     };
     const int kh = H / 32, ki = I / 32;
-    if (I % gateup_rows(kh) || H % down_rows(H, ki, cfg->top_k))
+    if (I % gateup_rows(kh) || H % down_rows(H, ki))
         return fail(MOE_EUNSUPPORTED, "moe_expert_pack: rows not a multiple of the scale pack");
     {
         uint16_t* d = reinterpret_cast<uint16_t*>(dst + L.gu_s);
@@ -173,7 +173,7 @@ moe_status_t moe_expert_pack(const moe_config_t* cfg, const uint8_t* gate_q, con
                 d[gateup_scale_index(r, g, 1, kh, p)] = up_s[(size_t)r * kh + g];
             }
     }
-    pack_scales(down_s, L.down_s, H, ki, down_rows(H, ki, cfg->top_k));
+    pack_scales(down_s, L.down_s, H, ki, down_rows(H, ki));
     return MOE_OK;
 }
 
@@ -396,7 +396,7 @@ BatchArgs batch_args(moe_layer_t* L, const uint16_t* x, int n, int32_t* ids, flo
     b.TG = c.topk_group;
     b.K = c.top_k;
     b.S = c.n_shared;
-    b.down_p = down_rows(c.hidden, c.inter / 32, c.top_k);
+    b.down_p = down_rows(c.hidden, c.inter / 32);
     b.router_splits = batch_router_splits(c.hidden);
     b.rsf = c.routed_scaling_factor;
     return b;

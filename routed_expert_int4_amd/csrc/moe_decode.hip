@@ -10,10 +10,9 @@
 //      once into the integer operands of the routed experts' kernel.
 //   2. gateup: gate/up + SwiGLU of the routed experts; the next items' loads
 //      are in flight while the current ones are computed.
-//   3. down_combine: one wave per routed slot over a block of output rows,
-//      the shared expert's rows of the block split over the same waves,
-//      row loads pipelined; the block is combined in slot order (no float
-//      atomics: repeated calls are bit-identical).
+//   3. down_combine: one wave per slot (routed and shared) over a block of
+//      output rows, row loads pipelined; the block is combined in slot order
+//      (no float atomics: repeated calls are bit-identical).
 //
 // Int4 GEMV scheme.  A lane owns one 32-input scale group of the reduction
 // dimension (several when a row has more than 64 groups) and keeps the
@@ -552,6 +551,20 @@ __global__ void __launch_bounds__(256) gateup_kernel(DecodeArgs a) {
         gateup_compute<KG>(buf, rb_of(it), lane, xa, xs, a.h + (size_t)slot_of(it) * a.I, a.I / 32, item < n_items);
     };
 
+    if (NI == 2 && wave_id + 3 * n_waves < n_items && wave_id + 4 * n_waves >= n_items) {
+        // Exactly four items (the launch gives every wave four when there
+        // are 4 x 4096 items): a straight-line two-buffer pipeline keeps one
+        // item's loads in flight while the other is computed.
+        issue(wave_id, b[0]);
+        issue(wave_id + n_waves, b[1]);
+        compute(wave_id, b[0]);
+        issue(wave_id + 2 * n_waves, b[0]);
+        compute(wave_id + n_waves, b[1]);
+        issue(wave_id + 3 * n_waves, b[1]);
+        compute(wave_id + 2 * n_waves, b[0]);
+        compute(wave_id + 3 * n_waves, b[1]);
+        return;
+    }
     // Rounds of NI items: issue the round's loads, then compute it (the
     // other waves of the SIMD overlap their loads with this compute).
 #pragma unroll
@@ -595,20 +608,18 @@ __device__ __forceinline__ void load_h(const float* __restrict__ h, int g0, floa
     }
 }
 
-// One workgroup = one wave per routed slot over a block of R output rows;
-// the shared expert's rows of the block are split evenly over the same
-// waves (at most kDownSharedSteps load steps each), so every SIMD carries
-// the same load.  Row loads go in rounds of WIN steps, the next round issued
-// before the current one is computed (sched_barrier keeps that order); the
-// first R threads combine the block in slot order.
+// One workgroup = one wave per slot (the routed slots, then the shared
+// expert) over a block of R output rows.  Row loads go in rounds of WIN
+// steps, the next round issued before the current one is computed
+// (sched_barrier keeps that order); the first R threads combine the block in
+// slot order.  Nine waves of at most 170 registers fit one CU.
 template <int KG, int NLD>
-__global__ void __launch_bounds__(512) down_combine_kernel(DecodeArgs a) {
+__global__ void __launch_bounds__(576) down_combine_kernel(DecodeArgs a) {
     using S = DownShape<KG, NLD>;
-    constexpr int MAXW = 8;
+    constexpr int MAXW = 9;
     constexpr int WIN = S::WIN;
     constexpr int NR = (S::NL + WIN - 1) / WIN;  // rounds
-    constexpr int SSMAX = kDownSharedSteps < S::NL ? kDownSharedSteps : S::NL;
-    constexpr int NVP = pow2_at_least(S::NL + SSMAX);
+    constexpr int NVP = pow2_at_least(S::NL);
     const int lane = threadIdx.x & 63;
     const int slot = wave_in_block();
     const int K = a.K;
@@ -616,23 +627,14 @@ __global__ void __launch_bounds__(512) down_combine_kernel(DecodeArgs a) {
     const int row_sub = KG >= kWave ? 0 : (lane / KG);
     const int rb = blockIdx.x;
     const BlobLayout L = blob_layout(a.H, a.I);
-    const uint8_t* blob = a.direct ? readlane_ptr(lane_pick(a.blobs, lane), slot) : a.slot_blobs[slot];
-    const uint8_t* sblob = a.shared_blob;
-
-    // shared steps of this wave: [sh0, sh0 + n_sh)
-    const int ss = (S::NL + K - 1) / K;
-    const int sh0 = slot * ss;
-    const int n_sh = a.S > 0 ? (sh0 >= S::NL ? 0 : (S::NL - sh0 < ss ? S::NL - sh0 : ss)) : 0;
-
+    const uint8_t* blob = slot >= K ? a.shared_blob
+                                    : (a.direct ? readlane_ptr(lane_pick(a.blobs, lane), slot) : a.slot_blobs[slot]);
     auto code_off = [&](int step, int c) {
         const size_t row = (size_t)rb * S::R + step * S::RPL + row_sub;
         return (row * KG + g0 + kWave * c) * 16;
     };
-    // h of this slot and of the shared expert first: vector loads complete
-    // in order, so the conversion below must not wait behind weight loads.
-    float hraw[S::CPL][32], shraw[S::CPL][32];
+    float hraw[S::CPL][32];
     load_h<S::CPL, KG>(a.h + (size_t)slot * a.I, g0, hraw);
-    load_h<S::CPL, KG>(a.h + (size_t)K * a.I, g0, shraw);
     u32x4 code[S::NL][S::CPL];
     auto issue_round = [&](int r) {
 #pragma unroll
@@ -648,38 +650,11 @@ __global__ void __launch_bounds__(512) down_combine_kernel(DecodeArgs a) {
         const size_t si = ((size_t)rb * KG + g0 + kWave * c) * S::R + (size_t)row_sub * S::NL;
         load_scales<S::NL>(reinterpret_cast<const uint16_t*>(blob + L.down_s) + si, sc[c]);
     }
-    __builtin_amdgcn_sched_barrier(0);
-    // shared rows (clamped to a valid step when this wave has fewer); their
-    // scales are consecutive halves of the lane's scale run, fetched as the
-    // ND dwords that cover them (clamped to the run's last dword)
-    constexpr int ND = SSMAX / 2 + 1;
-    u32x4 scode[SSMAX][S::CPL];
-    unsigned ssw[S::CPL][ND];
-    const int sh0c = sh0 < S::NL ? sh0 : S::NL - 1;
-#pragma unroll
-    for (int t = 0; t < SSMAX; ++t) {
-        const int step = sh0 + t < S::NL ? sh0 + t : S::NL - 1;
-#pragma unroll
-        for (int c = 0; c < S::CPL; ++c) scode[t][c] = load_stream16(sblob + L.down_q + code_off(step, c));
-    }
-    int sodd[S::CPL];
-#pragma unroll
-    for (int c = 0; c < S::CPL; ++c) {
-        const size_t run = ((size_t)rb * KG + g0 + kWave * c) * S::R + (size_t)row_sub * S::NL;
-        const size_t d0 = (run + sh0c) >> 1, dmax = (run + S::NL - 1) >> 1;
-        sodd[c] = (int)((run + sh0c) & 1);
-#pragma unroll
-        for (int j = 0; j < ND; ++j)
-            ssw[c][j] = __builtin_nontemporal_load(as_global<unsigned>(sblob + L.down_s) + (d0 + j < dmax ? d0 + j : dmax));
-    }
     if constexpr (NR > 1) issue_round(1);
     __builtin_amdgcn_sched_barrier(0);
-
-    HI8 ha[S::CPL], sha[S::CPL];
-    float hscale[S::CPL], shscale[S::CPL];
+    HI8 ha[S::CPL];
+    float hscale[S::CPL];
     to_i8<S::CPL>(hraw, ha, hscale);
-    to_i8<S::CPL>(shraw, sha, shscale);
-
     float v[NVP];
 #pragma unroll
     for (int n = 0; n < NVP; ++n) v[n] = 0.0f;
@@ -697,34 +672,17 @@ __global__ void __launch_bounds__(512) down_combine_kernel(DecodeArgs a) {
         __builtin_amdgcn_sched_barrier(0);
         if (r + 2 < NR) issue_round(r + 2);
     }
-#pragma unroll
-    for (int t = 0; t < SSMAX; ++t) {
-        float acc = 0.0f;
-#pragma unroll
-        for (int c = 0; c < S::CPL; ++c)
-        {
-            // half (odd + t) of the covering dwords
-            const unsigned word = ((t & 1) && sodd[c]) ? ssw[c][t / 2 + 1] : ssw[c][t / 2];
-            const unsigned bits = ((sodd[c] + t) & 1) ? (word >> 16) : (word & 0xFFFFu);
-            acc = fmaf(half_bits_to_float(bits) * shscale[c], dot_chunk_i8(scode[t][c], sha[c]), acc);
-        }
-        v[S::NL + t] = t < n_sh ? acc : 0.0f;
-    }
     const float r = reduce_scatter<NVP, S::B>(v, lane);
     __shared__ float part[MAXW][S::R];
-    __shared__ float part_sh[S::R];
     const int low_bits = S::B - ilog2(NVP);
     const int vi = (lane >> low_bits) & (NVP - 1);
-    if ((lane & ((1 << low_bits) - 1)) == 0) {
-        if (vi < S::NL) part[slot][vi * S::RPL + row_sub] = r;
-        else if (vi - S::NL < n_sh) part_sh[(sh0 + vi - S::NL) * S::RPL + row_sub] = r;
-    }
+    if ((lane & ((1 << low_bits) - 1)) == 0 && vi < S::NL) part[slot][vi * S::RPL + row_sub] = r;
     __syncthreads();
     if ((int)threadIdx.x < S::R) {
         const int t = threadIdx.x;
         float y = 0.0f;
         for (int j = 0; j < K; ++j) y = fmaf(a.w[j], part[j][t], y);
-        if (a.S > 0) y += part_sh[t];
+        if (a.S > 0) y += part[K][t];
         a.y[(size_t)rb * S::R + t] = y;
     }
 }
@@ -770,9 +728,9 @@ hipError_t launch_gateup(const DecodeArgs& a, hipStream_t st, const LaunchTiming
 template <int KG, int NLD>
 hipError_t launch_down_nl(const DecodeArgs& a, hipStream_t st, const LaunchTiming& tm) {
     using S = DownShape<KG, NLD>;
-    if constexpr (ilog2(pow2_at_least(S::NL + (kDownSharedSteps < S::NL ? kDownSharedSteps : S::NL))) <= S::B) {
+    if constexpr (ilog2(pow2_at_least(S::NL)) <= S::B && S::NL * S::CPL <= kDownMaxLoads) {
         const int grid = a.H / S::R;
-        return launch_kernel(down_combine_kernel<KG, NLD>, dim3(grid), dim3(a.K * 64), st, tm, a);
+        return launch_kernel(down_combine_kernel<KG, NLD>, dim3(grid), dim3((a.K + a.S) * 64), st, tm, a);
     } else {
         return hipErrorInvalidValue;  // never chosen by down_rows
     }
@@ -780,7 +738,7 @@ hipError_t launch_down_nl(const DecodeArgs& a, hipStream_t st, const LaunchTimin
 
 template <int KG>
 hipError_t launch_down(const DecodeArgs& a, hipStream_t st, const LaunchTiming& tm) {
-    const int nl = down_rows(a.H, KG, a.K) / rows_per_load(KG);
+    const int nl = down_rows(a.H, KG) / rows_per_load(KG);
     switch (nl) {
         case 1: return launch_down_nl<KG, 1>(a, st, tm);
         case 2: return launch_down_nl<KG, 2>(a, st, tm);
@@ -840,7 +798,7 @@ bool decode_shape_supported(int hidden, int inter, int top_k, int n_shared) {
     const int kh = hidden / 32, ki = inter / 32;
     const bool h_ok = kh == 8 || kh == 16 || kh == 32 || kh == 64 || kh == 128 || kh == 192 || kh == 256;
     const bool i_ok = ki == 4 || ki == 8 || ki == 16 || ki == 32 || ki == 64 || ki == 128;
-    return h_ok && i_ok && hidden % 256 == 0 && hidden % down_rows(hidden, ki, top_k) == 0 &&
+    return h_ok && i_ok && hidden % 256 == 0 && hidden % down_rows(hidden, ki) == 0 &&
            inter % gateup_rows(kh) == 0 && top_k <= 8;
 }
 

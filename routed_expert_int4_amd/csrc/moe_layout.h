@@ -33,32 +33,32 @@ __host__ __device__ constexpr int chunks_per_lane(int kg) { return kg >= kWave ?
 __host__ __device__ constexpr int gateup_rows(int kg_h) {
     return rows_per_load(kg_h) > kGateUpRowsBase ? rows_per_load(kg_h) : kGateUpRowsBase;
 }
-// Wave-load steps a down-projection workgroup may take per row slot; the
+// Wave-load steps a down-projection wave may take over its row block; the
 // down kernel is instantiated for each of these counts.
 __host__ __device__ constexpr int down_step_option(int i) {
     return i == 0 ? 32 : i == 1 ? 24 : i == 2 ? 16 : i == 3 ? 8 : i == 4 ? 4 : i == 5 ? 2 : 1;
 }
-// Shared-expert load steps a down-projection wave takes at most (the shared
-// expert's rows of a block are split over the routed slots' waves).
-constexpr int kDownSharedSteps = 4;
+// Code loads a down-projection wave keeps in registers at most (steps x
+// chunk columns).
+constexpr int kDownMaxLoads = 24;
 
 __host__ __device__ constexpr int pow2_at_least(int v) { return v <= 1 ? 1 : 2 * pow2_at_least((v + 1) / 2); }
 
 // Rows per down-projection workgroup: about hidden/256 (so one round of
 // workgroups covers the 256 CUs), a multiple of rows_per_load(inter/32) that
 // divides hidden, with a step count s from down_step_option such that the
-// shared expert's s steps split over top_k waves give each at most
-// kDownSharedSteps, and s + kDownSharedSteps row partials, rounded up to a
-// power of two, fit the lanes that share a row (min(inter/32, 64)).
-__host__ __device__ inline int down_rows(int hidden, int kg_i, int top_k) {
+// wave's s x chunks_per_lane code loads stay within kDownMaxLoads and its s
+// row partials, rounded up to a power of two, fit the lanes that share a row
+// (min(inter/32, 64)).
+__host__ __device__ inline int down_rows(int hidden, int kg_i) {
     const int rpl = rows_per_load(kg_i);
     const int lanes_per_row = kg_i < kWave ? kg_i : kWave;
     const int target = hidden / 256 > rpl ? hidden / 256 : rpl;
     for (int i = 0; i < 7; ++i) {
         const int steps = down_step_option(i);
         const int r = steps * rpl;
-        if (r <= target && hidden % r == 0 && (steps + top_k - 1) / top_k <= kDownSharedSteps &&
-            pow2_at_least(steps + kDownSharedSteps) <= lanes_per_row)
+        if (r <= target && hidden % r == 0 && steps * chunks_per_lane(kg_i) <= kDownMaxLoads &&
+            pow2_at_least(steps) <= lanes_per_row)
             return r;
     }
     return rpl;

@@ -151,7 +151,17 @@ __global__ void __launch_bounds__(256) batch_topk_kernel(BatchArgs a, int conver
     const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * 4 + wave_in_block();
     if (t >= a.T) return;
-    // logits = in-order sum of the router's partial sums; s = sigmoid, sb = s + bias
+    // logits = in-order sum of the router's partial sums (all partials
+    // loaded first, so the loads overlap); s = sigmoid, sb = s + bias
+    constexpr int MAXSP = kMaxRouterSplits;
+    float part[MAXSP][EPL];
+#pragma unroll
+    for (int sp = 0; sp < MAXSP; ++sp)
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) {
+            const int e = lane * EPL + i;
+            part[sp][i] = sp < a.router_splits && e < a.E ? a.logit_part[((size_t)sp * a.T + t) * a.E + e] : 0.0f;
+        }
     float sv[EPL], key[EPL];
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
@@ -160,7 +170,9 @@ __global__ void __launch_bounds__(256) batch_topk_kernel(BatchArgs a, int conver
         key[i] = -__builtin_inff();
         if (e < a.E) {
             float l = 0.0f;
-            for (int sp = 0; sp < a.router_splits; ++sp) l += a.logit_part[((size_t)sp * a.T + t) * a.E + e];
+#pragma unroll
+            for (int sp = 0; sp < MAXSP; ++sp)
+                if (sp < a.router_splits) l += part[sp][i];
             sv[i] = 1.0f / (1.0f + expf(-l));
             key[i] = sv[i] + a.bias[e];
         }

@@ -111,10 +111,11 @@ inline int batch_max_tiles(int T, int K, int E, int S) {
     return (n < E ? n : E) + (n + kTileTokens - 1) / kTileTokens + S * ((T + kTileTokens - 1) / kTileTokens);
 }
 
-// Router column splits for a hidden size: the largest power of two <= 16
-// with hidden % (64 * splits) == 0.
+// Router column splits for a hidden size: the largest power of two <=
+// kMaxRouterSplits with hidden % (64 * splits) == 0.
+constexpr int kMaxRouterSplits = 16;
 inline int batch_router_splits(int hidden) {
-    int s = 16;
+    int s = kMaxRouterSplits;
     while (s > 1 && hidden % (64 * s)) s /= 2;
     return s;
 }

@@ -96,6 +96,23 @@ def test_lru_oracle_textbook_pins():
     assert m == len(np.unique(tr)) and e == 0 and h + m == tr.size
 
 
+def test_lru_oracle_pinned_hand_worked():
+    # Worked by hand: 3 slots, top-2 routing, expert 0 pinned (LRU keeps 2).
+    #   t0 [0,1]: 0 pinned hit, 1 miss            LRU [1]
+    #   t1 [2,0]: 2 miss, 0 hit                    LRU [1,2]
+    #   t2 [1,3]: 1 hit; 3 miss evicts 2           LRU [1,3]
+    #   t3 [2,1]: 2 miss evicts 3 (1 is needed); 1 hit
+    tr = [[0, 1], [2, 0], [1, 3], [2, 1]]
+    assert lru.replay(tr, 3, pinned=[0]) == (4, 4, 2)
+    # the same trace without the pin: 3 hits, 5 misses, 2 evictions
+    assert lru.replay(tr, 3) == (3, 5, 2)
+    # every expert of the trace pinned: no miss at all
+    assert lru.replay(tr, 4, pinned=[0, 1, 2, 3]) == (8, 0, 0)
+    # usage counts and the hottest experts (ties to the lower index)
+    assert lru.usage(tr, 5) == [2, 3, 2, 1, 0]
+    assert lru.hottest(lru.usage(tr, 5), 3) == [1, 0, 2]
+
+
 @pytest.mark.parametrize("slots,skew", [(8, 0.0), (16, 1.1), (64, 1.1), (64, 0.0)])
 def test_cache_policy_matches_lru_replay(slots, skew):
     rng = np.random.default_rng(slots)

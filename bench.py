@@ -125,6 +125,9 @@ def main() -> int:
                     help="decode: the headline batch-1 line (default); batch32 / prefill512: the batched "
                          "workloads; cache-stack: 12 layers behind the HBM expert cache; each prints its own line")
     ap.add_argument("--stack-tokens", type=int, default=256, help="sequential tokens of the cache-stack workload")
+    ap.add_argument("--pin", type=int, default=-1,
+                    help="cache-stack: experts pinned per layer by learned usage (-1: slots - top_k, 0: plain LRU)")
+    ap.add_argument("--learn-tokens", type=int, default=128, help="cache-stack: tokens of the learning pass")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported (this layer's path is "
@@ -142,14 +145,20 @@ def bench_cache_stack(args) -> int:
 
     Layer l: weights seed 100 + l, the committed Zipf(1.1) bias of layer l
     (tests/golden/zipf_bias_stack.json); all 12 x 256 routed experts packed in
-    pinned host memory (65.2 GB), 64 HBM slots per layer with LRU eviction,
-    cold start.  Sequential decode of --stack-tokens tokens: token t enters
-    layer 0 as x0[t] (seed 300); each next layer's input is
-    bf16(y / rms(y) + N(0, 0.1) noise) (noise seed 400).  Every layer call is
-    one moe_layer_forward with T = 1, which reads the routing back to the
-    host and copies missing experts on the cache's copy stream.  The timed
-    region is the whole run (cold misses included); hit rates are reported
-    for the whole run and for the second half."""
+    pinned host memory (65.2 GB), 64 HBM slots per layer.  Sequential decode:
+    token t enters layer 0 as x0[t]; each next layer's input is
+    bf16(y / rms(y) + N(0, 0.1) noise).  Every layer call is one
+    moe_layer_forward with T = 1, which reads the routing back to the host
+    and copies missing experts on the cache's copy stream.
+
+    Learning cache (the default, as colibri's auto-pin): a learning pass of
+    --learn-tokens tokens (x0 seed 310, noise seed 410, not timed) records
+    each layer's expert usage; then every layer pins its --pin most used
+    experts (default slots - top_k, loaded before the timed region, as at
+    start-up) and keeps the other slots as an LRU.  The timed run decodes
+    --stack-tokens tokens (x0 seed 300, noise seed 400) with the LRU part
+    empty.  The same tokens are then run again with plain LRU over all slots
+    from a cold start (reported as lru_only).  --pin 0 times plain LRU only."""
     import numpy as np
     import torch
 
@@ -160,6 +169,7 @@ def bench_cache_stack(args) -> int:
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     cfg = synth.GLM
     n_layers, slots, n_tok = 12, 64, args.stack_tokens
+    n_pin = slots - cfg.top_k if args.pin < 0 else args.pin
     with open(os.path.join(ROOT, "tests", "golden", "zipf_bias_stack.json")) as f:
         biases = [np.asarray(l["bias"], dtype=np.float32) for l in json.load(f)["layers"]]
     cache = ExpertCache(cfg, n_layers, slots)
@@ -175,64 +185,98 @@ def bench_cache_stack(args) -> int:
         del w
         log(f"layer {l} ready ({time.perf_counter() - t0:.0f} s)")
     H = cfg.hidden
-    x0 = DeviceLayer.to_device_bf16(synth.gen_tokens(cfg, n_tok, seed=300))
-    noise = torch.from_numpy(synth.gen_noise(cfg, n_tok * n_layers, seed=400, std=0.1)).to("cuda:0")
     y = torch.empty((1, H), dtype=torch.float32, device="cuda:0")
     ids = torch.empty((1, cfg.top_k), dtype=torch.int32, device="cuda:0")
     w = torch.empty((1, cfg.top_k), dtype=torch.float32, device="cuda:0")
     stream = torch.cuda.current_stream()
-    half_stats = None
-    torch.cuda.synchronize()
-    log(f"decoding {n_tok} tokens through {n_layers} cached layers")
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    wall0 = time.perf_counter()
-    e0.record(stream)
-    for t in range(n_tok):
-        if t == n_tok // 2:
-            half_stats = [cache.stats(l) for l in range(n_layers)]
-        x = x0[t:t + 1]
+
+    def decode(x_seed, noise_seed, n):
+        """n sequential tokens through the stack; returns (ms, stats at n/2)."""
+        x0 = DeviceLayer.to_device_bf16(synth.gen_tokens(cfg, n, seed=x_seed))
+        noise = torch.from_numpy(synth.gen_noise(cfg, n * n_layers, seed=noise_seed, std=0.1)).to("cuda:0")
+        half = None
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for t in range(n):
+            if t == n // 2:
+                half = [cache.stats(l) for l in range(n_layers)]
+            x = x0[t:t + 1]
+            for l in range(n_layers):
+                B.moe_layer_forward(layers[l].handle, x, 1, y, ids, w, stream)
+                rms = torch.sqrt(torch.mean(y * y, dim=1, keepdim=True))
+                x = (y / rms + noise[t * n_layers + l:t * n_layers + l + 1]).to(torch.bfloat16)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1), half
+
+    def totals(stats):
+        return {k: sum(st[k] for st in stats) for k in ("hits", "misses", "h2d_bytes")}
+
+    def measured(label):
+        before = totals([cache.stats(l) for l in range(n_layers)])
+        log(f"{label}: decoding {n_tok} tokens through {n_layers} cached layers")
+        ms, half = decode(300, 400, n_tok)
+        after = totals([cache.stats(l) for l in range(n_layers)])
+        mid = totals(half)
+        d = {k: after[k] - before[k] for k in after}
+        d2 = {k: after[k] - mid[k] for k in after}
+        r = {"tokens_per_s": n_tok / (ms / 1e3), "ms": ms,
+             "hit_rate": d["hits"] / max(d["hits"] + d["misses"], 1),
+             "hit_rate_second_half": d2["hits"] / max(d2["hits"] + d2["misses"], 1),
+             "h2d_bytes": d["h2d_bytes"], "h2d_gbs": d["h2d_bytes"] / (ms / 1e3) / 1e9}
+        log(f"{label}: {r['tokens_per_s']:.1f} tokens/s, hit rate {r['hit_rate']:.4f}, "
+            f"H2D {r['h2d_bytes'] / 1e9:.1f} GB at {r['h2d_gbs']:.1f} GB/s")
+        return r
+
+    def empty_cache():
         for l in range(n_layers):
-            B.moe_layer_forward(layers[l].handle, x, 1, y, ids, w, stream)
-            rms = torch.sqrt(torch.mean(y * y, dim=1, keepdim=True))
-            x = (y / rms + noise[t * n_layers + l:t * n_layers + l + 1]).to(torch.bfloat16)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    ms = e0.elapsed_time(e1)
-    stats = [cache.stats(l) for l in range(n_layers)]
-    hits = sum(st["hits"] for st in stats)
-    misses = sum(st["misses"] for st in stats)
-    h2d = sum(st["h2d_bytes"] for st in stats)
-    hits2 = hits - sum(st["hits"] for st in half_stats)
-    misses2 = misses - sum(st["misses"] for st in half_stats)
-    tokens_per_s = n_tok / (ms / 1e3)
-    h2d_gbs = h2d / (ms / 1e3) / 1e9
-    log(f"{tokens_per_s:.1f} tokens/s, hit rate {hits / (hits + misses):.3f} (second half "
-        f"{hits2 / max(hits2 + misses2, 1):.3f}), H2D {h2d / 1e9:.1f} GB at {h2d_gbs:.1f} GB/s")
+            cache.unpin(l, list(range(cfg.n_experts)))
+            for e in range(cfg.n_experts):
+                cache.evict(l, e)
+
+    pinned = None
+    pin_load_s = 0.0
+    if n_pin > 0:
+        log(f"learning pass: {args.learn_tokens} tokens")
+        decode(310, 410, args.learn_tokens)
+        empty_cache()
+        p0 = time.perf_counter()
+        for l in range(n_layers):
+            cache.autopin(l, n_pin)
+        torch.cuda.synchronize()
+        pin_load_s = time.perf_counter() - p0
+        pinned = measured(f"autopin {n_pin}")
+        empty_cache()
+    lru_only = measured("plain LRU")
+    main_run = pinned if pinned else lru_only
     out = {
         "metric": "MoE-layer tokens/s through a 12-layer stack behind the HBM expert cache",
-        "value": round(tokens_per_s, 3),
+        "value": round(main_run["tokens_per_s"], 3),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": 1,
         "warmup": 0,
-        "ms_per_step": round(ms, 3),
+        "ms_per_step": round(main_run["ms"], 3),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "int4 weights x int16 fixed-point activations (two int8 parts), int32 dot, fp32 accumulate",
-        "data": "synthetic (seeded: layer weights 100 + l, Zipf bias per layer, x0 seed 300, noise seed 400)",
+        "data": "synthetic (seeded: layer weights 100 + l, Zipf bias per layer, x0 seed 300, noise seed 400; "
+                "learning pass x0 seed 310, noise seed 410)",
         "config": {"workload": f"12 GLM-5.2-shaped MoE layers, {n_tok} sequential decode tokens, 64 HBM slots "
-                               "per layer, pinned host expert store, cold start", "layers": n_layers,
-                   "slots_per_layer": slots, "tokens": n_tok},
-        "hit_rate": round(hits / (hits + misses), 4),
-        "hit_rate_second_half": round(hits2 / max(hits2 + misses2, 1), 4),
-        "h2d_gbytes": round(h2d / 1e9, 3),
-        "h2d_gbs": round(h2d_gbs, 2),
-        "wall_s": round(wall, 2),
+                               f"per layer ({n_pin} pinned by learned usage, the rest LRU), pinned host expert "
+                               "store", "layers": n_layers, "slots_per_layer": slots, "pinned_per_layer": n_pin,
+                   "learning_tokens": args.learn_tokens if n_pin > 0 else 0, "tokens": n_tok},
+        "hit_rate": round(main_run["hit_rate"], 4),
+        "hit_rate_second_half": round(main_run["hit_rate_second_half"], 4),
+        "h2d_gbytes": round(main_run["h2d_bytes"] / 1e9, 3),
+        "h2d_gbs": round(main_run["h2d_gbs"], 2),
+        "pin_load_s": round(pin_load_s, 3),
+        "lru_only": {k: round(v, 4) for k, v in lru_only.items()},
         "roofline": {"kernel": "host-to-device expert copies (hipMemcpyAsync, pinned host)", "bound": "pcie",
-                     "achieved": round(h2d_gbs, 2), "peak": 64.0, "unit": "GB/s",
-                     "frac": round(h2d_gbs / 64.0, 4), "traffic": None},
+                     "achieved": round(main_run["h2d_gbs"], 2), "peak": 64.0, "unit": "GB/s",
+                     "frac": round(main_run["h2d_gbs"] / 64.0, 4), "traffic": None},
         "cpu_baseline": None,
     }
     print(json.dumps(out), flush=True)

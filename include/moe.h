@@ -202,7 +202,8 @@ typedef struct {
     uint64_t misses;
     uint64_t h2d_bytes;
     uint64_t evictions;
-    uint64_t prefetches;
+    uint64_t prefetches;  /* experts copied by prefetch or pin */
+    uint64_t pinned;      /* experts pinned now */
 } moe_cache_stats_t;
 
 moe_status_t expert_cache_create(const moe_config_t* cfg, int n_layers, int slots_per_layer, void* d_slot_pool,
@@ -215,13 +216,34 @@ moe_status_t expert_cache_stats(const moe_cache_t* cache, int layer, moe_cache_s
 void expert_cache_destroy(moe_cache_t* cache);
 moe_status_t moe_layer_attach_cache(moe_layer_t* layer, moe_cache_t* cache, int layer_id);
 
+/* Learning cache with a pinned hot store (colibri summary, "Learning cache
+ * et attentes selon le materiel": routed experts are counted as they are
+ * used, and the hottest ones are pinned in memory).
+ * expert_cache_usage: copies layer's routed-use counts since creation (one
+ * per expert and routed slot of every token, hits and misses alike) into
+ * h_counts [n_experts].  expert_cache_pin: makes the listed experts resident
+ * (copies counted as prefetches) and pins them: a pinned slot is never
+ * evicted by the LRU; MOE_ENOSLOT (before any change) if the pinned experts
+ * would leave fewer than top_k slots, MOE_EINVAL on an id out of range.
+ * expert_cache_unpin: returns the listed experts' slots to the LRU (no-op for
+ * unpinned ones).  expert_cache_autopin: unpins the layer and pins its n most
+ * used experts (ties to the lower index); n must leave top_k slots.
+ * expert_cache_evict frees a pinned expert's slot too. */
+moe_status_t expert_cache_usage(const moe_cache_t* cache, int layer, uint64_t* h_counts);
+moe_status_t expert_cache_pin(moe_cache_t* cache, int layer, const int32_t* h_experts, int n);
+moe_status_t expert_cache_unpin(moe_cache_t* cache, int layer, const int32_t* h_experts, int n);
+moe_status_t expert_cache_autopin(moe_cache_t* cache, int layer, int n);
+
 /* expert_cache_replay: host-only replay of the cache's slot policy (per-layer
- * LRU; a miss takes a free slot, else the least recently used slot not needed
- * by the same token) on a routing trace [n_tokens][top_k] of one layer, with
- * no GPU work.  Writes the hit, miss and eviction counts the cache would
- * record for the same trace from a cold start. */
+ * LRU; a miss takes a free slot, else the least recently used unpinned slot
+ * not needed by the same token) on a routing trace [n_tokens][top_k] of one
+ * layer, with no GPU work.  The n_pinned experts of `pinned` (at most
+ * slots - top_k) are resident and pinned before the first token.  Writes the
+ * hit, miss and eviction counts the cache would record for the same trace
+ * from a cold start. */
 moe_status_t expert_cache_replay(int n_experts, int slots, int top_k, const int32_t* trace, int n_tokens,
-                                 uint64_t* hits, uint64_t* misses, uint64_t* evictions);
+                                 const int32_t* pinned, int n_pinned, uint64_t* hits, uint64_t* misses,
+                                 uint64_t* evictions);
 
 #ifdef __cplusplus
 }

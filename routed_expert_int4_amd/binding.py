@@ -36,7 +36,7 @@ class MoeConfig(ctypes.Structure):
 
 class MoeCacheStats(ctypes.Structure):
     _fields_ = [("hits", ctypes.c_uint64), ("misses", ctypes.c_uint64), ("h2d_bytes", ctypes.c_uint64),
-                ("evictions", ctypes.c_uint64), ("prefetches", ctypes.c_uint64)]
+                ("evictions", ctypes.c_uint64), ("prefetches", ctypes.c_uint64), ("pinned", ctypes.c_uint64)]
 
 
 class MoeError(RuntimeError):
@@ -68,8 +68,12 @@ _SIGNATURES = {
     "expert_cache_stats": ([_vp, _i, ctypes.POINTER(MoeCacheStats)], _i),
     "expert_cache_destroy": ([_vp], None),
     "moe_layer_attach_cache": ([_vp, _vp, _i], _i),
-    "expert_cache_replay": ([_i, _i, _i, _vp, _i, ctypes.POINTER(ctypes.c_uint64), ctypes.POINTER(ctypes.c_uint64),
-                             ctypes.POINTER(ctypes.c_uint64)], _i),
+    "expert_cache_usage": ([_vp, _i, _vp], _i),
+    "expert_cache_pin": ([_vp, _i, _vp, _i], _i),
+    "expert_cache_unpin": ([_vp, _i, _vp, _i], _i),
+    "expert_cache_autopin": ([_vp, _i, _i], _i),
+    "expert_cache_replay": ([_i, _i, _i, _vp, _i, _vp, _i, ctypes.POINTER(ctypes.c_uint64),
+                             ctypes.POINTER(ctypes.c_uint64), ctypes.POINTER(ctypes.c_uint64)], _i),
 }
 
 
@@ -211,6 +215,26 @@ def expert_cache_stats(cache: int, layer: int) -> dict:
     return {k: int(getattr(s, k)) for k, _ in MoeCacheStats._fields_}
 
 
+def expert_cache_usage(cache: int, layer: int, n_experts: int) -> np.ndarray:
+    out = np.zeros(int(n_experts), np.uint64)
+    check(lib().expert_cache_usage(cache, int(layer), out.ctypes.data))
+    return out
+
+
+def expert_cache_pin(cache: int, layer: int, experts) -> None:
+    a = np.ascontiguousarray(np.asarray(experts, dtype=np.int32))
+    check(lib().expert_cache_pin(cache, int(layer), a.ctypes.data, int(a.size)))
+
+
+def expert_cache_unpin(cache: int, layer: int, experts) -> None:
+    a = np.ascontiguousarray(np.asarray(experts, dtype=np.int32))
+    check(lib().expert_cache_unpin(cache, int(layer), a.ctypes.data, int(a.size)))
+
+
+def expert_cache_autopin(cache: int, layer: int, n: int) -> None:
+    check(lib().expert_cache_autopin(cache, int(layer), int(n)))
+
+
 def expert_cache_destroy(cache: int) -> None:
     lib().expert_cache_destroy(cache)
 
@@ -219,9 +243,11 @@ def moe_layer_attach_cache(layer: int, cache: int, layer_id: int) -> None:
     check(lib().moe_layer_attach_cache(layer, cache, int(layer_id)))
 
 
-def expert_cache_replay(n_experts: int, slots: int, top_k: int, trace: np.ndarray):
+def expert_cache_replay(n_experts: int, slots: int, top_k: int, trace: np.ndarray, pinned=()):
     t = np.ascontiguousarray(trace, dtype=np.int32)
+    p = np.ascontiguousarray(np.asarray(pinned, dtype=np.int32))
     h, m, e = ctypes.c_uint64(), ctypes.c_uint64(), ctypes.c_uint64()
     check(lib().expert_cache_replay(int(n_experts), int(slots), int(top_k), t.ctypes.data, int(t.shape[0]),
-                                    ctypes.byref(h), ctypes.byref(m), ctypes.byref(e)))
+                                    p.ctypes.data if p.size else None, int(p.size), ctypes.byref(h), ctypes.byref(m),
+                                    ctypes.byref(e)))
     return int(h.value), int(m.value), int(e.value)

@@ -36,6 +36,7 @@ struct LayerSlots {
     std::vector<hipEvent_t> last_use;      // [slots]
     std::vector<char> use_recorded;        // [slots]
     std::vector<char> copy_recorded;       // [slots]
+    std::vector<uint64_t> usage;           // [E] routed uses (the learning cache's counts)
     moe_cache_stats_t stats{};
 };
 
@@ -122,6 +123,7 @@ moe_status_t cache_prepare_token(moe_layer* layer, DecodeArgs& a, hipStream_t st
     std::vector<int> ids(c->pinned_ids, c->pinned_ids + K);
     for (int e : ids)
         if (e < 0 || e >= c->cfg.n_experts) return fail(MOE_EINVAL, "expert cache: routed id %d out of range", e);
+    for (int e : ids) ++L.usage[e];
     std::vector<int> hit_slots, miss_slots, slot_of_j(K);
     for (int j = 0; j < K; ++j) {
         int s = -1;
@@ -222,6 +224,7 @@ moe_status_t expert_cache_create(const moe_config_t* cfg, int n_layers, int slot
         L->last_use.assign(slots_per_layer, nullptr);
         L->use_recorded.assign(slots_per_layer, 0);
         L->copy_recorded.assign(slots_per_layer, 0);
+        L->usage.assign(cfg->n_experts, 0);
         for (int s = 0; s < slots_per_layer && err == hipSuccess; ++s) {
             err = hipEventCreateWithFlags(&L->copy_done[s], hipEventDisableTiming);
             if (err == hipSuccess) err = hipEventCreateWithFlags(&L->last_use[s], hipEventDisableTiming);
@@ -283,7 +286,73 @@ moe_status_t expert_cache_stats(const moe_cache_t* cache, int layer, moe_cache_s
     if (!cache || !out) return fail(MOE_EINVAL, "expert_cache_stats: NULL argument");
     if (layer < 0 || layer >= cache->n_layers) return fail(MOE_EINVAL, "expert_cache_stats: bad layer %d", layer);
     *out = cache->layers[layer]->stats;
+    out->pinned = (uint64_t)cache->layers[layer]->policy.n_pinned();
     return MOE_OK;
+}
+
+moe_status_t expert_cache_usage(const moe_cache_t* cache, int layer, uint64_t* h_counts) {
+    if (!cache || !h_counts) return fail(MOE_EINVAL, "expert_cache_usage: NULL argument");
+    if (layer < 0 || layer >= cache->n_layers) return fail(MOE_EINVAL, "expert_cache_usage: bad layer %d", layer);
+    const std::vector<uint64_t>& u = cache->layers[layer]->usage;
+    std::copy(u.begin(), u.end(), h_counts);
+    return MOE_OK;
+}
+
+moe_status_t expert_cache_pin(moe_cache_t* cache, int layer, const int32_t* h_experts, int n) {
+    if (!cache || (n > 0 && !h_experts)) return fail(MOE_EINVAL, "expert_cache_pin: NULL argument");
+    if (layer < 0 || layer >= cache->n_layers) return fail(MOE_EINVAL, "expert_cache_pin: bad layer %d", layer);
+    if (n < 0) return fail(MOE_EINVAL, "expert_cache_pin: n < 0");
+    std::vector<int> want(h_experts, h_experts + n);
+    LayerSlots& L = *cache->layers[layer];
+    int fresh = 0;
+    for (size_t i = 0; i < want.size(); ++i) {
+        const int e = want[i];
+        if (e < 0 || e >= cache->cfg.n_experts) return fail(MOE_EINVAL, "expert_cache_pin: expert %d", e);
+        bool dup = false;
+        for (size_t j = 0; j < i; ++j) dup = dup || want[j] == e;
+        if (!dup && !L.policy.is_pinned(e)) ++fresh;
+    }
+    // a token's top_k experts must always find unpinned slots
+    if (L.policy.n_pinned() + fresh > cache->slots - cache->cfg.top_k)
+        return fail(MOE_ENOSLOT, "expert_cache_pin: %d pinned experts leave fewer than top_k (%d) of %d slots",
+                    L.policy.n_pinned() + fresh, cache->cfg.top_k, cache->slots);
+    for (int e : want) {
+        if (L.policy.slot_of(e) < 0) {
+            int s = -1;
+            bool missed = false;
+            moe_status_t r = make_resident(cache, layer, e, want, &s, &missed);
+            if (r != MOE_OK) return r;
+            ++L.stats.prefetches;
+        }
+        L.policy.pin(e);
+    }
+    return MOE_OK;
+}
+
+moe_status_t expert_cache_unpin(moe_cache_t* cache, int layer, const int32_t* h_experts, int n) {
+    if (!cache || (n > 0 && !h_experts)) return fail(MOE_EINVAL, "expert_cache_unpin: NULL argument");
+    if (layer < 0 || layer >= cache->n_layers) return fail(MOE_EINVAL, "expert_cache_unpin: bad layer %d", layer);
+    if (n < 0) return fail(MOE_EINVAL, "expert_cache_unpin: n < 0");
+    for (int i = 0; i < n; ++i)
+        if (h_experts[i] < 0 || h_experts[i] >= cache->cfg.n_experts)
+            return fail(MOE_EINVAL, "expert_cache_unpin: expert %d", h_experts[i]);
+    for (int i = 0; i < n; ++i) cache->layers[layer]->policy.unpin(h_experts[i]);
+    return MOE_OK;
+}
+
+moe_status_t expert_cache_autopin(moe_cache_t* cache, int layer, int n) {
+    if (!cache) return fail(MOE_EINVAL, "expert_cache_autopin: cache is NULL");
+    if (layer < 0 || layer >= cache->n_layers) return fail(MOE_EINVAL, "expert_cache_autopin: bad layer %d", layer);
+    if (n < 0 || n > cache->slots - cache->cfg.top_k)
+        return fail(MOE_ENOSLOT, "expert_cache_autopin: %d pinned experts leave fewer than top_k (%d) of %d slots", n,
+                    cache->cfg.top_k, cache->slots);
+    LayerSlots& L = *cache->layers[layer];
+    const int E = cache->cfg.n_experts;
+    for (int e = 0; e < E; ++e) L.policy.unpin(e);
+    std::vector<int32_t> order(E);
+    for (int e = 0; e < E; ++e) order[e] = e;
+    std::stable_sort(order.begin(), order.end(), [&](int32_t x, int32_t y) { return L.usage[x] > L.usage[y]; });
+    return expert_cache_pin(cache, layer, order.data(), n);
 }
 
 void expert_cache_destroy(moe_cache_t* cache) { destroy_cache(cache); }
@@ -303,11 +372,21 @@ moe_status_t moe_layer_attach_cache(moe_layer_t* layer, moe_cache_t* cache, int 
 // Host-only replay of the slot policy on a routing trace (no GPU needed):
 // trace [n_tokens][top_k] expert ids; returns hits/misses/evictions.
 moe_status_t expert_cache_replay(int n_experts, int slots, int top_k, const int32_t* trace, int n_tokens,
-                                 uint64_t* hits, uint64_t* misses, uint64_t* evictions) {
+                                 const int32_t* pinned, int n_pinned, uint64_t* hits, uint64_t* misses,
+                                 uint64_t* evictions) {
     if (n_experts < 1 || slots < top_k || top_k < 1 || n_tokens < 0 || (n_tokens > 0 && !trace) || !hits ||
-        !misses || !evictions)
+        !misses || !evictions || n_pinned < 0 || (n_pinned > 0 && !pinned) || n_pinned > slots - top_k)
         return fail(MOE_EINVAL, "expert_cache_replay: bad arguments");
     SlotPolicy p(n_experts, slots);
+    for (int i = 0; i < n_pinned; ++i) {
+        const int e = pinned[i];
+        if (e < 0 || e >= n_experts) return fail(MOE_EINVAL, "expert_cache_replay: pinned id %d out of range", e);
+        if (p.slot_of(e) < 0) {
+            int ev = -1;
+            if (p.assign(e, {}, &ev) < 0) return fail(MOE_ENOSLOT, "expert_cache_replay: no slot to pin");
+        }
+        p.pin(e);
+    }
     *hits = *misses = *evictions = 0;
     for (int t = 0; t < n_tokens; ++t) {
         std::vector<int> ids(trace + (size_t)t * top_k, trace + (size_t)(t + 1) * top_k);

@@ -97,6 +97,18 @@ class ExpertCache:
     def stats(self, layer: int) -> dict:
         return B.expert_cache_stats(self.handle, layer)
 
+    def usage(self, layer: int):
+        return B.expert_cache_usage(self.handle, layer, self.cfg.n_experts)
+
+    def pin(self, layer: int, experts) -> None:
+        B.expert_cache_pin(self.handle, layer, experts)
+
+    def unpin(self, layer: int, experts) -> None:
+        B.expert_cache_unpin(self.handle, layer, experts)
+
+    def autopin(self, layer: int, n: int) -> None:
+        B.expert_cache_autopin(self.handle, layer, n)
+
     def close(self) -> None:
         if getattr(self, "handle", None):
             B.expert_cache_destroy(self.handle)

@@ -121,3 +121,16 @@ def test_cache_policy_matches_lru_replay(slots, skew):
     p /= p.sum()
     trace = np.array([rng.choice(E, k, replace=False, p=p) for _ in range(400)], np.int32)
     assert B.expert_cache_replay(E, slots, k, trace) == lru.replay(trace, slots)
+    # with the hottest experts of a separate learning trace pinned
+    learn = np.array([rng.choice(E, k, replace=False, p=p) for _ in range(200)], np.int32)
+    for n_pin in sorted({1, (slots - k) // 2, slots - k}):
+        if n_pin > slots - k:
+            continue  # pins must leave top_k slots
+        pins = lru.hottest(lru.usage(learn, E), n_pin)
+        assert B.expert_cache_replay(E, slots, k, trace, pinned=pins) == lru.replay(trace, slots, pinned=pins)
+
+
+def test_cache_replay_rejects_too_many_pins():
+    tr = np.zeros((1, 4), np.int32) + np.arange(4, dtype=np.int32)
+    with pytest.raises(B.MoeError):
+        B.expert_cache_replay(16, 8, 4, tr, pinned=list(range(5)))

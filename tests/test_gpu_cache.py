@@ -148,3 +148,58 @@ def test_cache_register_errors(torch_cuda):
     with pytest.raises(B.MoeError):
         B.expert_cache_create(CFG, 1, CFG.top_k - 1, cache.pool, cache.pool.numel(), cache.copy_stream)
     cache.close()
+
+
+def test_cache_learning_autopin(torch_cuda):
+    """Learning cache: usage counts equal the routing trace's histogram; after
+    autopin the n most used experts stay resident, and a run from an empty
+    LRU part records exactly the hits, misses and evictions of the oracle's
+    pinned replay, with outputs unchanged."""
+    torch = torch_cuda
+    from routed_expert_int4_amd.layer import DeviceLayer
+    slots, n_pin = 16, 8
+    say(f"[gpu] learning cache: {slots} slots, autopin {n_pin}")
+    cache, weights, cached, resident = make_stack(torch, slots, n_layers=1)
+    x1 = synth.gen_tokens(CFG, N_TOKENS, seed=50)
+    _, ids1, _ = cached[0].forward(DeviceLayer.to_device_bf16(x1))
+    torch.cuda.synchronize()
+    trace1 = ids1.cpu().numpy()
+    counts = cache.usage(0)
+    assert list(counts) == lru.usage(trace1, CFG.n_experts)
+    cache.autopin(0, n_pin)
+    pins = lru.hottest(lru.usage(trace1, CFG.n_experts), n_pin)
+    # empty the LRU part: every unpinned expert leaves its slot
+    for e in range(CFG.n_experts):
+        if e not in pins:
+            cache.evict(0, e)
+    st0 = cache.stats(0)
+    assert st0["pinned"] == n_pin
+    x2 = synth.gen_tokens(CFG, N_TOKENS, seed=51)
+    x = DeviceLayer.to_device_bf16(x2)
+    y, ids, w = cached[0].forward(x)
+    y_res, ids_res, w_res = resident[0].forward_each(x)
+    torch.cuda.synchronize()
+    idh = ids.cpu().numpy()
+    assert torch.equal(ids, ids_res) and torch.equal(y, y_res), "cached and resident outputs differ"
+    check_layer(weights[0], x2, y.cpu().numpy(), idh, w.cpu().numpy())
+    st = cache.stats(0)
+    got = (st["hits"] - st0["hits"], st["misses"] - st0["misses"], st["evictions"] - st0["evictions"])
+    want = lru.replay(idh, slots, pinned=pins)
+    say(f"[gpu] after autopin: {got}, oracle replay {want}, plain LRU would give {lru.replay(idh, slots)}")
+    assert got == want
+    assert B.expert_cache_replay(CFG.n_experts, slots, CFG.top_k, idh, pinned=pins) == want
+    # pins must leave top_k slots; ids out of range are rejected; unpinning
+    # an unpinned expert is a no-op
+    with pytest.raises(B.MoeError) as err:
+        cache.autopin(0, slots - CFG.top_k + 1)
+    assert err.value.code == B.MOE_ENOSLOT
+    with pytest.raises(B.MoeError) as err:
+        cache.pin(0, [CFG.n_experts])
+    assert err.value.code == B.MOE_EINVAL
+    cache.unpin(0, [p for p in range(CFG.n_experts) if p not in pins][:3])
+    assert cache.stats(0)["pinned"] == n_pin
+    cache.unpin(0, pins)
+    assert cache.stats(0)["pinned"] == 0
+    for lay in cached + resident:
+        lay.close()
+    cache.close()

@@ -377,11 +377,18 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) b
         f32x4 accg = {0.f, 0.f, 0.f, 0.f}, accu = {0.f, 0.f, 0.f, 0.f};
         const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
         constexpr int NS = KG / 4;  // steps of 4 groups
-        // codes and scales of a step: lane of quarter q reads group 4s + q
-        auto load_step = [&](int s, u32x4& g, u32x4& u, u32x4& sc) {
+        // codes of a step: lane of quarter q reads group 4s + q
+        auto load_step = [&](int s, u32x4& g, u32x4& u) {
             g = *as_global<u32x4>(gq + (4 * s + q) * 16);
             u = *as_global<u32x4>(uq + (4 * s + q) * 16);
-            sc = gateup_scales4<KG>(gus, row, 4 * s);
+        };
+        // scales, four steps at a time: for steps 4h .. 4h+3 lane (i, q)
+        // fetches step 4h + q of row i (16 bytes, so a wave load covers 16
+        // rows x 64 bytes); step s's scales come from lane (i, s % 4) by a
+        // lane shuffle
+        auto quad_scales = [&](int h) {
+            const int s = 4 * h + q;
+            return s < NS ? gateup_scales4<KG>(gus, row, 4 * s) : u32x4{0u, 0u, 0u, 0u};
         };
         auto stage_load = [&](int st, u32x4 (&v)[PT]) {
 #pragma unroll
@@ -395,9 +402,10 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) b
         // the next stage's activations in flight during a stage
         u32x4 v[PT];
         stage_load(0, v);
-        u32x4 cg0, cu0, sc0, cg1 = {0u, 0u, 0u, 0u}, cu1 = cg1, sc1 = cg1;
-        load_step(0, cg0, cu0, sc0);
-        if (NS > 1) load_step(1, cg1, cu1, sc1);
+        u32x4 scl = quad_scales(0), scn = scl;
+        u32x4 cg0, cu0, cg1 = {0u, 0u, 0u, 0u}, cu1 = cg1;
+        load_step(0, cg0, cu0);
+        if (NS > 1) load_step(1, cg1, cu1);
         // fully unrolled over the stages: a loop back-edge here would make
         // the compiler drain the prefetched loads (register rotation copies)
 #pragma unroll
@@ -410,8 +418,21 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) b
 #pragma unroll
             for (int c = 0; c < CK / 4; ++c) {
                 const int sidx = st * (CK / 4) + c;
-                u32x4 cg2 = cg1, cu2 = cu1, sc2 = sc1;
-                if (sidx + 2 < NS) load_step(sidx + 2, cg2, cu2, sc2);
+                u32x4 cg2 = cg1, cu2 = cu1;
+                if (sidx + 2 < NS) load_step(sidx + 2, cg2, cu2);
+                // the next four steps' scales two steps before they are needed
+                if ((sidx & 3) == 0 && sidx > 0) scl = scn;
+                if ((sidx & 3) == 2 && sidx + 2 < NS) scn = quad_scales(sidx / 4 + 1);
+                u32x4 sc0;
+                {
+                    const int src = i + 16 * (sidx & 3);
+                    const u32x4 h = scl;
+#pragma unroll
+                    for (int d = 0; d < 4; ++d) {
+                        const unsigned hv = h[d];  // element copied first (bit_cast of an element reads element 0)
+                        sc0[d] = (unsigned)__shfl((int)hv, src);
+                    }
+                }
                 transpose_quarters(cg0);
                 transpose_quarters(cu0);
 #pragma unroll
@@ -434,10 +455,8 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) b
                 }
                 cg0 = cg1;
                 cu0 = cu1;
-                sc0 = sc1;
                 cg1 = cg2;
                 cu1 = cu2;
-                sc1 = sc2;
                 // keep the prefetch depth, not the whole stage, in flight
                 __builtin_amdgcn_sched_barrier(0);
             }

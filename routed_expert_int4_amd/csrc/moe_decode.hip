@@ -340,17 +340,16 @@ __device__ __forceinline__ void route_token(const DecodeArgs& a, int lane, int* 
 // ---------------------------------------------------------------- kernel 1
 // Three kinds of workgroups in one launch (the first two stream HBM side by
 // side, so the routing's serial tail overlaps the shared expert's weights):
-//  * router blocks [0, E/4): one W_r row per wave, logit[e] = sum_h
-//    W_r[e][h] x[h] in fp32 (fixed-order sums), turned into s and sb.  The
-//    last router block to finish (device-scope counter:
-//    release of each block's scores, acquire by the last) derives the
-//    group-limited top-k and writes ids, w and the routed slots' blobs, then
-//    resets the counter;
+//  * router blocks [0, router_blocks(E)): W_r rows (one per wave by default),
+//    logit[e] = sum_h W_r[e][h] x[h] in fp32 (fixed-order sums), turned into
+//    s and sb.  The block that takes the last ticket of a device-scope
+//    counter derives the group-limited top-k and writes ids, w and the
+//    routed slots' blobs, then resets the counter;
 //  * the next shared_blocks blocks: gate/up + SwiGLU of the shared expert
 //    (it does not depend on the routing), each wave converting the
 //    activations for itself;
-//  * the last block: the activation pairs and their exponent for the
-//    routed experts' kernel.
+//  * the last block: the activations' integer operands for the routed
+//    experts' kernel.
 template <int KG>
 __host__ __device__ inline int shared_gateup_blocks(int I) {
     const int per_slot = I / GateUpShape<KG>::R;

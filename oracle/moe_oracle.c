@@ -33,9 +33,19 @@
  *    holds the even column in its low nibble, two's complement.  The weight
  *    value is fp32(scale) * q, which is exact in fp32.
  *
+ *  - Adaptive expert top-p (colibri summary, options list: --topp, an
+ *    adaptive expert top-p that cuts the expert reads).  Reading: with
+ *    top_p < 1, the selected experts are ranked by their share s_j / sum_sel s
+ *    (descending, ties: lower index) and only the smallest leading set whose
+ *    shares reach top_p is kept (an expert is kept when the shares ranked
+ *    before it sum to less than top_p); the kept weights are renormalised,
+ *    weight_j = routed_scaling_factor * s_j / sum_kept s, and a dropped slot
+ *    holds id -1 and weight 0.  top_p = 1 is plain top-k.
+ *
  * Diagnostics per token: the boundary gap of the selection (the smallest
  * margin by which a different choice of groups or experts would have been
- * made), used to excuse index mismatches caused by rounding.
+ * made), used to excuse index mismatches caused by rounding, and with top-p
+ * the margin of the keep decisions, min_j |shares ranked before j - top_p|.
  */
 #include <math.h>
 #include <stdint.h>
@@ -145,12 +155,12 @@ static int ranks_before(double va, int a, double vb, int b) {
  * the boundary gap: min over the group boundary and the expert boundary of
  * (last kept score - first rejected score); +inf where there is no rejected
  * candidate.  Returns 0, or -1 when the arguments are inconsistent. */
-int oracle_select(int n_experts, int n_groups, int topk_group, int top_k, double rsf,
-                  const double* s, const double* sb, int32_t* ids, double* w, double* gap) {
+int oracle_select(int n_experts, int n_groups, int topk_group, int top_k, double rsf, double top_p,
+                  const double* s, const double* sb, int32_t* ids, double* w, double* gap, double* pgap) {
     if (n_experts <= 0 || n_groups <= 0 || n_experts % n_groups) return -1;
     int gsize = n_experts / n_groups;
     if (gsize < 2 || topk_group < 1 || topk_group > n_groups) return -1;
-    if (top_k < 1 || top_k > topk_group * gsize) return -1;
+    if (top_k < 1 || top_k > topk_group * gsize || top_k > 64 || !(top_p > 0.0 && top_p <= 1.0)) return -1;
 
     double* gscore = (double*)malloc(sizeof(double) * (size_t)n_groups);
     int* gorder = (int*)malloc(sizeof(int) * (size_t)n_groups);
@@ -203,6 +213,25 @@ int oracle_select(int n_experts, int n_groups, int topk_group, int top_k, double
     if (top_k < n_el) gap_e = sb[eorder[top_k - 1]] - sb[eorder[top_k]];
     *gap = gap_e < gap_g ? gap_e : gap_g;
 
+    /* Adaptive top-p over the selected experts. */
+    *pgap = INFINITY;
+    if (top_p < 1.0) {
+        int keep[64];
+        double kept = 0.0;
+        for (int j = 0; j < top_k; ++j) {
+            double before = 0.0;
+            for (int k = 0; k < top_k; ++k)
+                if (ranks_before(s[ids[k]], ids[k], s[ids[j]], ids[j])) before += s[ids[k]] / denom;
+            keep[j] = before < top_p;
+            if (fabs(before - top_p) < *pgap) *pgap = fabs(before - top_p);
+            if (keep[j]) kept += s[ids[j]];
+        }
+        for (int j = 0; j < top_k; ++j) {
+            w[j] = keep[j] ? rsf * s[ids[j]] / kept : 0.0;
+            if (!keep[j]) ids[j] = -1;
+        }
+    }
+
     free(gscore);
     free(gorder);
     free(eorder);
@@ -220,13 +249,13 @@ int oracle_select(int n_experts, int n_groups, int topk_group, int top_k, double
  * Outputs: y [T][hidden], ids [T][top_k], w [T][top_k], gap [T],
  * logits (optional) [T][n_experts].  Returns 0 or -1 on bad arguments. */
 int oracle_layer_forward(int hidden, int inter, int n_experts, int n_groups, int topk_group, int top_k,
-                         int n_shared, double rsf,
+                         int n_shared, double rsf, double top_p,
                          const float* router_w, const float* bias,
                          const uint8_t* gate_q, const uint16_t* gate_s,
                          const uint8_t* up_q, const uint16_t* up_s,
                          const uint8_t* down_q, const uint16_t* down_s,
                          const uint16_t* x_bf16, int T, const int32_t* forced_ids,
-                         double* y, int32_t* ids, double* w, double* gap, double* logits,
+                         double* y, int32_t* ids, double* w, double* gap, double* pgap, double* logits,
                          int n_threads) {
     if (hidden % 32 || inter % 32 || T < 0 || n_shared < 0) return -1;
     const size_t gq_n = (size_t)inter * (hidden / 2), gs_n = (size_t)inter * (hidden / 32);
@@ -249,22 +278,25 @@ int oracle_layer_forward(int hidden, int inter, int n_experts, int n_groups, int
         for (int c = 0; c < hidden; ++c) x[c] = bf16_to_double(x_bf16[(size_t)t * hidden + c]);
         oracle_router_scores(hidden, n_experts, router_w, bias, x, lg, s, sb);
         if (logits) memcpy(logits + (size_t)t * n_experts, lg, sizeof(double) * (size_t)n_experts);
-        if (oracle_select(n_experts, n_groups, topk_group, top_k, rsf, s, sb, it, wt, gap + t) != 0) {
+        if (oracle_select(n_experts, n_groups, topk_group, top_k, rsf, top_p, s, sb, it, wt, gap + t,
+                          pgap + t) != 0) {
 #ifdef _OPENMP
 #pragma omp atomic write
 #endif
             status = -1;
         } else {
             if (forced_ids) {
+                /* forced experts (-1: empty slot), weights over the forced set */
                 double denom = 0.0;
                 for (int j = 0; j < top_k; ++j) {
                     it[j] = forced_ids[(size_t)t * top_k + j];
-                    denom += s[it[j]];
+                    if (it[j] >= 0) denom += s[it[j]];
                 }
-                for (int j = 0; j < top_k; ++j) wt[j] = rsf * s[it[j]] / denom;
+                for (int j = 0; j < top_k; ++j) wt[j] = it[j] >= 0 ? rsf * s[it[j]] / denom : 0.0;
             }
             for (int c = 0; c < hidden; ++c) yt[c] = 0.0;
             for (int j = 0; j < top_k + n_shared; ++j) {
+                if (j < top_k && it[j] < 0) continue; /* slot dropped by top-p */
                 int e = j < top_k ? it[j] : n_experts + (j - top_k);
                 double scale = j < top_k ? wt[j] : 1.0;
                 oracle_expert_ffn(hidden, inter, gate_q + e * gq_n, gate_s + e * gs_n, up_q + e * gq_n,
@@ -291,9 +323,9 @@ int oracle_max_threads(void) {
 
 /* Router and selection only, for T tokens (no expert math): ids [T][top_k],
  * w [T][top_k], gap [T].  Same steps as oracle_layer_forward. */
-int oracle_route(int hidden, int n_experts, int n_groups, int topk_group, int top_k, double rsf,
+int oracle_route(int hidden, int n_experts, int n_groups, int topk_group, int top_k, double rsf, double top_p,
                  const float* router_w, const float* bias, const uint16_t* x_bf16, int T,
-                 int32_t* ids, double* w, double* gap, int n_threads) {
+                 int32_t* ids, double* w, double* gap, double* pgap, int n_threads) {
     int status = 0;
 #ifdef _OPENMP
     if (n_threads > 0) omp_set_num_threads(n_threads);
@@ -306,8 +338,8 @@ int oracle_route(int hidden, int n_experts, int n_groups, int topk_group, int to
         double* sb = (double*)malloc(sizeof(double) * (size_t)n_experts);
         for (int c = 0; c < hidden; ++c) x[c] = bf16_to_double(x_bf16[(size_t)t * hidden + c]);
         oracle_router_scores(hidden, n_experts, router_w, bias, x, lg, s, sb);
-        if (oracle_select(n_experts, n_groups, topk_group, top_k, rsf, s, sb, ids + (size_t)t * top_k,
-                          w + (size_t)t * top_k, gap + t) != 0) {
+        if (oracle_select(n_experts, n_groups, topk_group, top_k, rsf, top_p, s, sb, ids + (size_t)t * top_k,
+                          w + (size_t)t * top_k, gap + t, pgap + t) != 0) {
 #ifdef _OPENMP
 #pragma omp atomic write
 #endif

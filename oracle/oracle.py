@@ -41,15 +41,15 @@ def lib():
         L.oracle_expert_ffn.restype = None
         L.oracle_router_scores.argtypes = [ctypes.c_int, ctypes.c_int, _vp, _vp, _d, _d, _d, _d]
         L.oracle_router_scores.restype = None
-        L.oracle_select.argtypes = [ctypes.c_int] * 4 + [ctypes.c_double, _d, _d, _i32, _d, _d]
+        L.oracle_select.argtypes = [ctypes.c_int] * 4 + [ctypes.c_double, ctypes.c_double, _d, _d, _i32, _d, _d, _d]
         L.oracle_select.restype = ctypes.c_int
         L.oracle_layer_forward.argtypes = (
-            [ctypes.c_int] * 7 + [ctypes.c_double, _vp, _vp] + [_vp] * 6
-            + [_vp, ctypes.c_int, _vp, _d, _i32, _d, _d, _vp, ctypes.c_int]
+            [ctypes.c_int] * 7 + [ctypes.c_double, ctypes.c_double, _vp, _vp] + [_vp] * 6
+            + [_vp, ctypes.c_int, _vp, _d, _i32, _d, _d, _d, _vp, ctypes.c_int]
         )
         L.oracle_layer_forward.restype = ctypes.c_int
-        L.oracle_route.argtypes = [ctypes.c_int] * 5 + [ctypes.c_double, _vp, _vp, _vp, ctypes.c_int, _i32, _d, _d,
-                                                         ctypes.c_int]
+        L.oracle_route.argtypes = [ctypes.c_int] * 5 + [ctypes.c_double, ctypes.c_double, _vp, _vp, _vp, ctypes.c_int,
+                                                         _i32, _d, _d, _d, ctypes.c_int]
         L.oracle_route.restype = ctypes.c_int
         L.oracle_max_threads.argtypes = []
         L.oracle_max_threads.restype = ctypes.c_int
@@ -92,27 +92,33 @@ def router_scores(router_w: np.ndarray, bias: np.ndarray, x: np.ndarray):
     return lg, s, sb
 
 
-def select(n_groups, topk_group, top_k, rsf, s: np.ndarray, sb: np.ndarray):
-    """Group-limited top-k of one token -> (ids, w, gap)."""
+def select(n_groups, topk_group, top_k, rsf, s: np.ndarray, sb: np.ndarray, top_p: float = 1.0,
+           with_pgap: bool = False):
+    """Group-limited top-k of one token (adaptive top-p when top_p < 1) ->
+    (ids, w, gap) or, with with_pgap, (ids, w, gap, pgap)."""
     s = np.ascontiguousarray(s, dtype=np.float64)
     sb = np.ascontiguousarray(sb, dtype=np.float64)
     ids = np.empty(top_k, np.int32)
     w = np.empty(top_k, np.float64)
     gap = np.empty(1, np.float64)
+    pgap = np.empty(1, np.float64)
     rc = lib().oracle_select(
-        len(s), n_groups, topk_group, top_k, float(rsf), _dptr(s), _dptr(sb),
-        ids.ctypes.data_as(_i32), _dptr(w), _dptr(gap),
+        len(s), n_groups, topk_group, top_k, float(rsf), float(top_p), _dptr(s), _dptr(sb),
+        ids.ctypes.data_as(_i32), _dptr(w), _dptr(gap), _dptr(pgap),
     )
     if rc != 0:
         raise ValueError("oracle_select: inconsistent arguments")
+    if with_pgap:
+        return ids, w, float(gap[0]), float(pgap[0])
     return ids, w, float(gap[0])
 
 
 def layer_forward(weights, x_bf16: np.ndarray, forced_ids=None, n_threads: int = 0, want_logits=False):
     """Full layer on tokens x_bf16 [T, H] (bf16 bits).
 
-    Returns dict(y [T,H] f64, ids [T,k] i32, w [T,k] f64, gap [T] f64,
-    logits [T,E] f64 or None)."""
+    Returns dict(y [T,H] f64, ids [T,k] i32 (-1: slot dropped by top-p),
+    w [T,k] f64, gap [T] f64, pgap [T] f64 (top-p decision margin, inf
+    without top-p), logits [T,E] f64 or None)."""
     cfg = weights.cfg
     x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
     T = x.shape[0]
@@ -121,6 +127,7 @@ def layer_forward(weights, x_bf16: np.ndarray, forced_ids=None, n_threads: int =
     ids = np.empty((T, k), np.int32)
     w = np.empty((T, k), np.float64)
     gap = np.empty(T, np.float64)
+    pgap = np.empty(T, np.float64)
     logits = np.empty((T, cfg.n_experts), np.float64) if want_logits else None
     fid = None
     if forced_ids is not None:
@@ -129,31 +136,35 @@ def layer_forward(weights, x_bf16: np.ndarray, forced_ids=None, n_threads: int =
     wt = weights
     rc = lib().oracle_layer_forward(
         cfg.hidden, cfg.inter, cfg.n_experts, cfg.n_groups, cfg.topk_group, k, cfg.n_shared,
-        float(cfg.routed_scaling_factor),
+        float(cfg.routed_scaling_factor), float(getattr(cfg, "top_p", 1.0)),
         _ptr(wt.router_w), _ptr(wt.bias),
         _ptr(wt.gate_q), _ptr(wt.gate_s), _ptr(wt.up_q), _ptr(wt.up_s), _ptr(wt.down_q), _ptr(wt.down_s),
         _ptr(x), T, _ptr(fid) if fid is not None else None,
-        _dptr(y), ids.ctypes.data_as(_i32), _dptr(w), _dptr(gap),
+        _dptr(y), ids.ctypes.data_as(_i32), _dptr(w), _dptr(gap), _dptr(pgap),
         logits.ctypes.data_as(ctypes.c_void_p) if logits is not None else None,
         int(n_threads),
     )
     if rc != 0:
         raise ValueError("oracle_layer_forward: bad arguments")
-    return {"y": y, "ids": ids, "w": w, "gap": gap, "logits": logits}
+    return {"y": y, "ids": ids, "w": w, "gap": gap, "pgap": pgap, "logits": logits}
 
 
-def route(weights, x_bf16: np.ndarray, n_threads: int = 0):
-    """Router + selection for tokens x_bf16 [T, H] -> (ids [T,k], w [T,k], gap [T])."""
+def route(weights, x_bf16: np.ndarray, n_threads: int = 0, with_pgap: bool = False):
+    """Router + selection for tokens x_bf16 [T, H] -> (ids [T,k], w [T,k], gap [T])
+    or, with with_pgap, (ids, w, gap, pgap [T])."""
     cfg = weights.cfg
     x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
     T = x.shape[0]
     ids = np.empty((T, cfg.top_k), np.int32)
     w = np.empty((T, cfg.top_k), np.float64)
     gap = np.empty(T, np.float64)
+    pgap = np.empty(T, np.float64)
     rc = lib().oracle_route(
         cfg.hidden, cfg.n_experts, cfg.n_groups, cfg.topk_group, cfg.top_k, float(cfg.routed_scaling_factor),
-        _ptr(weights.router_w), _ptr(weights.bias), _ptr(x), T, ids.ctypes.data_as(_i32), _dptr(w), _dptr(gap),
-        int(n_threads))
+        float(getattr(cfg, "top_p", 1.0)), _ptr(weights.router_w), _ptr(weights.bias), _ptr(x), T,
+        ids.ctypes.data_as(_i32), _dptr(w), _dptr(gap), _dptr(pgap), int(n_threads))
     if rc != 0:
         raise ValueError("oracle_route: bad arguments")
+    if with_pgap:
+        return ids, w, gap, pgap
     return ids, w, gap

@@ -44,6 +44,7 @@ class LayerConfig:
     top_k: int
     n_shared: int = 1
     routed_scaling_factor: float = 2.5
+    top_p: float = 1.0  # adaptive expert top-p over the selected experts (1: plain top-k)
 
     @property
     def n_total_experts(self) -> int:

@@ -403,3 +403,43 @@ def test_dispatch_degenerate():
     assert r["distinct"].tolist() == [7]
     r = dispatch(np.zeros((0, 4), np.int32), 8)                        # empty routing
     assert r["counts"].sum() == 0 and len(r["perm"]) == 0 and len(r["distinct"]) == 0
+
+
+def test_top_p_hand_worked():
+    # Selection of 4 of 8 experts (two groups, both kept), zero bias:
+    # ids by sb = [0, 6, 2, 7], shares by s = 0.9, 0.8, 0.6, 0.4 over 2.7.
+    s = np.array([0.9, 0.1, 0.6, 0.3, 0.2, 0.05, 0.8, 0.4])
+    ids, w, _, pgap = oracle.select(2, 2, 4, 2.5, s, s.copy(), top_p=0.6, with_pgap=True)
+    # shares before each: 0, 1/3 (kept), 0.6296 (>= 0.6: dropped), 0.8519 (dropped)
+    assert list(ids) == [0, 6, -1, -1]
+    assert np.allclose(w, [2.5 * 0.9 / 1.7, 2.5 * 0.8 / 1.7, 0.0, 0.0], rtol=0, atol=1e-15)
+    assert abs(pgap - (1.7 / 2.7 - 0.6)) < 1e-15
+    # a bias that moves expert 7 first in the selection order does not change
+    # which experts top-p keeps (it ranks by s), only their slots
+    sb = s.copy()
+    sb[7] += 1.0
+    ids, w, _ = oracle.select(2, 2, 4, 2.5, s, sb, top_p=0.6)
+    assert list(ids) == [-1, 0, 6, -1]
+    assert np.allclose(w, [0.0, 2.5 * 0.9 / 1.7, 2.5 * 0.8 / 1.7, 0.0], rtol=0, atol=1e-15)
+    # a tiny top_p keeps the single largest share; top_p = 1 is plain top-k
+    ids, w, _ = oracle.select(2, 2, 4, 2.5, s, sb, top_p=1e-9)
+    assert list(ids) == [-1, 0, -1, -1] and abs(w[1] - 2.5) < 1e-15
+    ids1, w1, g1 = oracle.select(2, 2, 4, 2.5, s, sb, top_p=1.0)
+    ids0, w0, g0 = oracle.select(2, 2, 4, 2.5, s, sb)
+    assert list(ids1) == list(ids0) == [7, 0, 6, 2] and np.array_equal(w1, w0)
+
+
+def test_top_p_layer_matches_forced_kept_experts(tiny, tiny_x):
+    import dataclasses
+    # the layer with top-p equals the layer forced onto the kept experts
+    # (empty slots skipped, weights renormalised over the kept ones)
+    cfg = dataclasses.replace(tiny.cfg, top_p=0.7)
+    wp = dataclasses.replace(tiny, cfg=cfg)
+    out = oracle.layer_forward(wp, tiny_x)
+    assert (out["ids"] < 0).any(), "top_p = 0.7 should drop some slot on the tiny tokens"
+    forced = oracle.layer_forward(tiny, tiny_x, forced_ids=out["ids"])
+    assert np.array_equal(out["y"], forced["y"])
+    assert np.allclose(out["w"], forced["w"], rtol=0, atol=1e-15)
+    # kept weights sum to rsf for every token; at least one expert is kept
+    assert np.allclose(out["w"].sum(axis=1), cfg.routed_scaling_factor, rtol=0, atol=1e-12)
+    assert ((out["ids"] >= 0).sum(axis=1) >= 1).all()

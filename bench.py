@@ -128,6 +128,8 @@ def main() -> int:
     ap.add_argument("--pin", type=int, default=-1,
                     help="cache-stack: experts pinned per layer by learned usage (-1: slots - top_k, 0: plain LRU)")
     ap.add_argument("--learn-tokens", type=int, default=128, help="cache-stack: tokens of the learning pass")
+    ap.add_argument("--top-p", type=float, default=1.0,
+                    help="decode: adaptive expert top-p (1: plain top-k); bytes are priced by the experts kept")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported (this layer's path is "
@@ -409,7 +411,8 @@ def bench_decode(args) -> int:
     from routed_expert_int4_amd.layer import DeviceLayer
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
-    cfg = synth.GLM
+    import dataclasses
+    cfg = dataclasses.replace(synth.GLM, top_p=args.top_p)
     nbytes = algorithmic_bytes(cfg)
     log("generating the GLM-shaped layer (seed 0) and 1000 tokens (seed 1)")
     weights = synth.gen_layer(cfg, seed=0)
@@ -457,6 +460,14 @@ def bench_decode(args) -> int:
     ms_total = e0.elapsed_time(e1)
     ms_per_step = ms_total / args.steps
     tokens_per_s = args.tokens * args.steps / (ms_total / 1e3)
+    # with the top-p cut only the kept routed experts are read: price the
+    # routed bytes by the mean kept count (every step routes the same tokens)
+    kept = float((ids >= 0).sum().item()) / args.tokens
+    if kept != cfg.top_k:
+        for key in ("routed_per_token", "gateup_launch"):
+            nbytes[key] = int(round(nbytes[key] * kept / cfg.top_k))
+        nbytes["layer_per_token"] -= int(round((cfg.top_k - kept) * nbytes["expert"]))
+        nbytes["down_launch"] = int(round(nbytes["down_launch"] * (kept + cfg.n_shared) / (cfg.top_k + cfg.n_shared)))
     routed_gbs = tokens_per_s * nbytes["routed_per_token"] / 1e9
     layer_gbs = tokens_per_s * nbytes["layer_per_token"] / 1e9
     log(f"{ms_per_step:.3f} ms/step, {tokens_per_s:.0f} tokens/s, routed {routed_gbs:.0f} GB/s (wall {wall:.2f} s)")
@@ -495,11 +506,13 @@ def bench_decode(args) -> int:
         "dtype": "int4 weights x int16 fixed-point activations (two int8 parts), int32 dot, fp32 accumulate",
         "data": "synthetic (seeded: weights seed 0, tokens seed 1)",
         "config": {
-            "workload": "GLM-5.2-shaped MoE layer, batch-1 int4 decode, 1000 independent tokens per step",
+            "workload": "GLM-5.2-shaped MoE layer, batch-1 int4 decode, 1000 independent tokens per step"
+                        + (f", adaptive expert top-p {cfg.top_p}" if cfg.top_p < 1.0 else ""),
             "hidden": cfg.hidden, "expert_intermediate": cfg.inter, "routed_experts": cfg.n_experts,
             "groups": cfg.n_groups, "topk_group": cfg.topk_group, "top_k": cfg.top_k, "shared_experts": cfg.n_shared,
             "tokens_per_step": args.tokens, "parallelism": "single GPU",
         },
+        "routed_experts_kept_per_token": round(kept, 3),
         "tokens_per_s": round(tokens_per_s, 1),
         "pct_of_hbm_peak": round(100 * routed_gbs / HBM_PEAK_GBS, 2),
         "layer_gbs": round(layer_gbs, 2),
@@ -515,7 +528,7 @@ def bench_decode(args) -> int:
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(gateup_gbs / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(),
+            "traffic": measured_traffic() if cfg.top_p >= 1.0 else None,
             "bytes_per_launch": nbytes["gateup_launch"],
             "avg_launch_us": round(avg_us[1], 3),
         },

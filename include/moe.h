@@ -59,7 +59,15 @@ typedef enum {
  * hidden/32 in {8,16,32,64,128,192,256}, inter/32 in {4,8,16,32,64,128},
  * hidden % 256 == 0, n_experts <= 256 and a multiple of 16, experts per
  * group >= 2 and a power of two times ceil(n_experts/64), n_shared in
- * {0,1}, top_k <= 8. */
+ * {0,1}, top_k <= 8.
+ * top_p in (0, 1]: adaptive expert top-p (colibri summary, options list:
+ * --topp cuts the expert reads).  With top_p < 1 the selected experts are
+ * ranked by their share s_j / sum_selected s (ties to the lower index), an
+ * expert is kept when the shares ranked before it sum to less than top_p,
+ * the kept weights are rsf * s_j / sum_kept s, and a dropped slot reports id
+ * -1 and weight 0 and is never read.  top_p = 1 is plain top-k.  top_p < 1 is
+ * served by the one-token path (T = 1 calls, and tokens behind an expert
+ * cache); T > 1 calls of an all-resident layer return MOE_EUNSUPPORTED. */
 typedef struct {
     int hidden;
     int inter;
@@ -69,6 +77,7 @@ typedef struct {
     int top_k;
     int n_shared;
     float routed_scaling_factor;
+    float top_p;
 } moe_config_t;
 
 typedef struct moe_layer moe_layer_t;

@@ -25,13 +25,13 @@ _sz = ctypes.c_size_t
 class MoeConfig(ctypes.Structure):
     _fields_ = [
         ("hidden", _i), ("inter", _i), ("n_experts", _i), ("n_groups", _i), ("topk_group", _i),
-        ("top_k", _i), ("n_shared", _i), ("routed_scaling_factor", ctypes.c_float),
+        ("top_k", _i), ("n_shared", _i), ("routed_scaling_factor", ctypes.c_float), ("top_p", ctypes.c_float),
     ]
 
     @classmethod
     def from_cfg(cls, cfg) -> "MoeConfig":
         return cls(cfg.hidden, cfg.inter, cfg.n_experts, cfg.n_groups, cfg.topk_group, cfg.top_k, cfg.n_shared,
-                   float(cfg.routed_scaling_factor))
+                   float(cfg.routed_scaling_factor), float(getattr(cfg, "top_p", 1.0)))
 
 
 class MoeCacheStats(ctypes.Structure):

@@ -50,6 +50,7 @@ moe_status_t validate_config(const moe_config_t* c) {
     if (c->n_shared < 0) return fail(MOE_EINVAL, "n_shared must be >= 0");
     if (!(c->routed_scaling_factor == c->routed_scaling_factor))
         return fail(MOE_EINVAL, "routed_scaling_factor is NaN");
+    if (!(c->top_p > 0.0f && c->top_p <= 1.0f)) return fail(MOE_EINVAL, "top_p must be in (0, 1]");
     return MOE_OK;
 }
 
@@ -90,6 +91,8 @@ WorkspaceLayout workspace_layout(const moe_config_t* c, int max_T) {
     o = align256(o + (size_t)chunks_per_lane(c->hidden / 32) * kWave * 18 * sizeof(unsigned));
     W.slot_blobs = o;
     o = align256(o + sizeof(void*) * 16);
+    W.kept = o;
+    o = align256(o + sizeof(int) * 17);
     W.ids = o;
     o = align256(o + sizeof(int32_t) * (size_t)max_T * c->top_k);
     W.w = o;
@@ -293,6 +296,7 @@ DecodeArgs decode_args(moe_layer_t* L, const uint16_t* x, int32_t* ids, float* w
     a.sb = reinterpret_cast<float*>(L->ws + L->W.sb);
     a.xq = reinterpret_cast<unsigned*>(L->ws + L->W.xq);
     a.slot_blobs = reinterpret_cast<const uint8_t**>(L->ws + L->W.slot_blobs);
+    a.kept = !L->cache && c.top_p < 1.0f ? reinterpret_cast<int*>(L->ws + L->W.kept) : nullptr;
     a.ids = ids;
     a.w = w;
     a.h = reinterpret_cast<float*>(L->ws + L->W.h);
@@ -305,6 +309,7 @@ DecodeArgs decode_args(moe_layer_t* L, const uint16_t* x, int32_t* ids, float* w
     a.K = c.top_k;
     a.S = c.n_shared;
     a.rsf = c.routed_scaling_factor;
+    a.top_p = c.top_p;
     a.direct = 0;
     a.use_slot_list = 0;
     a.n_slot_list = 0;
@@ -423,6 +428,7 @@ moe_status_t moe_router_topk(moe_layer_t* layer, const uint16_t* d_x, int T, int
     hipStream_t s = static_cast<hipStream_t>(stream);
     const moe_config_t& c = layer->cfg;
     if (T > 1) {
+        if (c.top_p < 1.0f) return fail(MOE_EUNSUPPORTED, "moe_router_topk: top_p < 1 needs T = 1 calls");
         const int tb = layer->W.batch_tokens;
         for (int t0 = 0; t0 < T; t0 += tb) {
             const int n = T - t0 < tb ? T - t0 : tb;
@@ -455,6 +461,7 @@ moe_status_t moe_layer_forward(moe_layer_t* layer, const uint16_t* d_x, int T, f
     int32_t* ids_base = d_ids ? d_ids : reinterpret_cast<int32_t*>(layer->ws + layer->W.ids);
     float* w_base = d_w ? d_w : reinterpret_cast<float*>(layer->ws + layer->W.w);
     if (T > 1 && !layer->cache) {
+        if (c.top_p < 1.0f) return fail(MOE_EUNSUPPORTED, "moe_layer_forward: top_p < 1 needs T = 1 calls");
         // batch union: every distinct expert of a launch sequence is read once
         const int tb = layer->W.batch_tokens;
         for (int t0 = 0; t0 < T; t0 += tb) {

@@ -179,7 +179,7 @@ __global__ void __launch_bounds__(256) batch_topk_kernel(BatchArgs a, int conver
     }
     int id;
     float wt;
-    wave_group_topk_values<EPL>(sv, key, a.E, a.G, a.TG, a.K, a.rsf, lane, &id, &wt);
+    wave_group_topk_values<EPL>(sv, key, a.E, a.G, a.TG, a.K, a.rsf, 1.0f, lane, &id, &wt);
     if (lane < a.K) {
         a.ids[(size_t)t * a.K + lane] = id;
         a.w[(size_t)t * a.K + lane] = wt;

@@ -121,14 +121,23 @@ moe_status_t cache_prepare_token(moe_layer* layer, DecodeArgs& a, hipStream_t st
     if (err == hipSuccess) err = hipEventSynchronize(c->ids_ready);
     if (err != hipSuccess) return hip_fail(err, "expert cache: reading the routing");
     std::vector<int> ids(c->pinned_ids, c->pinned_ids + K);
+    // id -1: a choice that the top-p cut dropped (weight 0, never read)
     for (int e : ids)
-        if (e < 0 || e >= c->cfg.n_experts) return fail(MOE_EINVAL, "expert cache: routed id %d out of range", e);
-    for (int e : ids) ++L.usage[e];
-    std::vector<int> hit_slots, miss_slots, slot_of_j(K);
+        if (e < -1 || e >= c->cfg.n_experts || (e == -1 && !(layer->cfg.top_p < 1.0f)))
+            return fail(MOE_EINVAL, "expert cache: routed id %d out of range", e);
+    std::vector<int> needed;
+    for (int e : ids)
+        if (e >= 0) {
+            ++L.usage[e];
+            needed.push_back(e);
+        }
+    std::vector<int> hit_slots, miss_slots, slot_of_j(K, -1);
     for (int j = 0; j < K; ++j) {
+        a.blobs[j] = nullptr;
+        if (ids[j] < 0) continue;
         int s = -1;
         bool missed = false;
-        moe_status_t r = make_resident(c, l, ids[j], ids, &s, &missed);
+        moe_status_t r = make_resident(c, l, ids[j], needed, &s, &missed);
         if (r != MOE_OK) return r;
         slot_of_j[j] = s;
         a.blobs[j] = c->slot_ptr(l, s);
@@ -162,7 +171,9 @@ moe_status_t cache_prepare_token(moe_layer* layer, DecodeArgs& a, hipStream_t st
     }
     a.use_slot_list = 0;
     a.n_slot_list = 0;
-    c->pending_slots = slot_of_j;
+    c->pending_slots.clear();
+    for (int s : slot_of_j)
+        if (s >= 0) c->pending_slots.push_back(s);
     c->pending_layer = l;
     return MOE_OK;
 }

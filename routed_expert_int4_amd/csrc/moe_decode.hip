@@ -325,16 +325,24 @@ __device__ __forceinline__ void route_token(const DecodeArgs& a, int lane, int* 
         key[i] = e < a.E ? __hip_atomic_load(a.sb + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : -__builtin_inff();
         tab[i] = a.table && e < a.E ? a.table[e] : nullptr;
     }
-    wave_group_topk_values<EPL>(sv, key, a.E, a.G, a.TG, a.K, a.rsf, lane, id, w);
-    // lane j < K: the blob of its choice, held by lane id / EPL
-    const int owner = lane < a.K ? *id / EPL : 0, idx = lane < a.K ? *id % EPL : 0;
+    wave_group_topk_values<EPL>(sv, key, a.E, a.G, a.TG, a.K, a.rsf, a.top_p, lane, id, w);
+    // lane j < K: the blob of its choice, held by lane id / EPL (none for a
+    // choice the top-p cut dropped)
+    const bool chosen = lane < a.K && *id >= 0;
+    const int owner = chosen ? *id / EPL : 0, idx = chosen ? *id % EPL : -1;
     const uint8_t* b = nullptr;
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
         const uint8_t* t = shfl_ptr(tab[i], owner);
         if (i == idx) b = t;
     }
-    *blob = lane < a.K ? b : nullptr;
+    *blob = chosen ? b : nullptr;
+    if (a.kept) {
+        // the kept routed slots, in increasing order, for the gate/up launch
+        const unsigned long long m = __ballot(chosen);
+        if (chosen) a.kept[1 + __popcll(m & ((1ull << lane) - 1))] = lane;
+        if (lane == 0) a.kept[0] = __popcll(m);
+    }
 }
 
 // ---------------------------------------------------------------- kernel 1
@@ -499,7 +507,14 @@ __global__ void __launch_bounds__(256) gateup_kernel(DecodeArgs a) {
     const int n_waves = gridDim.x * 4;
     const BlobLayout L = blob_layout(a.H, a.I);
     const int per_slot = a.I / S::R;
-    const int n_routed_slots = a.use_slot_list ? a.n_slot_list : a.K;
+    // With the router's kept-slot list (top-p cut) the items cover only the
+    // kept slots; the list goes to this wave's LDS row.
+    __shared__ int wave_kept[4][17];
+    if (a.kept) {
+        if (lane < 17) wave_kept[wave][lane] = lane <= a.K ? a.kept[lane] : 0;
+        __builtin_amdgcn_wave_barrier();
+    }
+    const int n_routed_slots = a.kept ? wave_kept[wave][0] : (a.use_slot_list ? a.n_slot_list : a.K);
     const int n_items = n_routed_slots * per_slot;
     if (wave_id >= n_items) return;
 
@@ -532,7 +547,9 @@ __global__ void __launch_bounds__(256) gateup_kernel(DecodeArgs a) {
     auto slot_of = [&](int item) {
         const int k = item / per_slot;
         int s = k;
-        if (a.use_slot_list) {
+        if (a.kept) {
+            s = wave_kept[wave][1 + k];
+        } else if (a.use_slot_list) {
 #pragma unroll
             for (int j = 0; j < 16; ++j)
                 if (j == k) s = a.slot_list[j];
@@ -550,18 +567,39 @@ __global__ void __launch_bounds__(256) gateup_kernel(DecodeArgs a) {
         gateup_compute<KG>(buf, rb_of(it), lane, xa, xs, a.h + (size_t)slot_of(it) * a.I, a.I / 32, item < n_items);
     };
 
-    if (NI == 2 && wave_id + 3 * n_waves < n_items && wave_id + 4 * n_waves >= n_items) {
-        // Exactly four items (the launch gives every wave four when there
-        // are 4 x 4096 items): a straight-line two-buffer pipeline keeps one
-        // item's loads in flight while the other is computed.
-        issue(wave_id, b[0]);
-        issue(wave_id + n_waves, b[1]);
-        compute(wave_id, b[0]);
-        issue(wave_id + 2 * n_waves, b[0]);
-        compute(wave_id + n_waves, b[1]);
-        issue(wave_id + 3 * n_waves, b[1]);
-        compute(wave_id + 2 * n_waves, b[0]);
-        compute(wave_id + 3 * n_waves, b[1]);
+    // One to four items for this wave (every wave gets four at 4 x 4096
+    // items, three when the top-p cut keeps 6 of 8 slots, ...): a
+    // straight-line two-buffer pipeline for each count keeps one item's loads
+    // in flight while the other is computed, and loads nothing beyond the
+    // wave's own items.
+    const int n_mine = (n_items - wave_id + n_waves - 1) / n_waves;
+    if (NI == 2 && n_mine <= 4) {
+        const int i0 = wave_id, i1 = wave_id + n_waves, i2 = wave_id + 2 * n_waves, i3 = wave_id + 3 * n_waves;
+        if (n_mine == 4) {
+            issue(i0, b[0]);
+            issue(i1, b[1]);
+            compute(i0, b[0]);
+            issue(i2, b[0]);
+            compute(i1, b[1]);
+            issue(i3, b[1]);
+            compute(i2, b[0]);
+            compute(i3, b[1]);
+        } else if (n_mine == 3) {
+            issue(i0, b[0]);
+            issue(i1, b[1]);
+            compute(i0, b[0]);
+            issue(i2, b[0]);
+            compute(i1, b[1]);
+            compute(i2, b[0]);
+        } else if (n_mine == 2) {
+            issue(i0, b[0]);
+            issue(i1, b[1]);
+            compute(i0, b[0]);
+            compute(i1, b[1]);
+        } else {
+            issue(i0, b[0]);
+            compute(i0, b[0]);
+        }
         return;
     }
     // Rounds of NI items: issue the round's loads, then compute it (the
@@ -628,54 +666,59 @@ __global__ void __launch_bounds__(576) down_combine_kernel(DecodeArgs a) {
     const BlobLayout L = blob_layout(a.H, a.I);
     const uint8_t* blob = slot >= K ? a.shared_blob
                                     : (a.direct ? readlane_ptr(lane_pick(a.blobs, lane), slot) : a.slot_blobs[slot]);
-    auto code_off = [&](int step, int c) {
-        const size_t row = (size_t)rb * S::R + step * S::RPL + row_sub;
-        return (row * KG + g0 + kWave * c) * 16;
-    };
-    float hraw[S::CPL][32];
-    load_h<S::CPL, KG>(a.h + (size_t)slot * a.I, g0, hraw);
-    u32x4 code[S::NL][S::CPL];
-    auto issue_round = [&](int r) {
-#pragma unroll
-        for (int n = r * WIN; n < (r + 1) * WIN && n < S::NL; ++n)
-#pragma unroll
-            for (int c = 0; c < S::CPL; ++c) code[n][c] = load_stream16(blob + L.down_q + code_off(n, c));
-    };
-    __builtin_amdgcn_sched_barrier(0);
-    issue_round(0);
-    unsigned sc[S::CPL][(S::NL + 1) / 2];
-#pragma unroll
-    for (int c = 0; c < S::CPL; ++c) {
-        const size_t si = ((size_t)rb * KG + g0 + kWave * c) * S::R + (size_t)row_sub * S::NL;
-        load_scales<S::NL>(reinterpret_cast<const uint16_t*>(blob + L.down_s) + si, sc[c]);
-    }
-    if constexpr (NR > 1) issue_round(1);
-    __builtin_amdgcn_sched_barrier(0);
-    HI8 ha[S::CPL];
-    float hscale[S::CPL];
-    to_i8<S::CPL>(hraw, ha, hscale);
-    float v[NVP];
-#pragma unroll
-    for (int n = 0; n < NVP; ++n) v[n] = 0.0f;
-#pragma unroll
-    for (int r = 0; r < NR; ++r) {
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int n = r * WIN; n < (r + 1) * WIN && n < S::NL; ++n) {
-            float acc = 0.0f;
-#pragma unroll
-            for (int c = 0; c < S::CPL; ++c)
-                acc = fmaf(scale_at(sc[c], n) * hscale[c], dot_chunk_i8(code[n][c], ha[c]), acc);
-            v[n] = acc;
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        if (r + 2 < NR) issue_round(r + 2);
-    }
-    const float r = reduce_scatter<NVP, S::B>(v, lane);
     __shared__ float part[MAXW][S::R];
-    const int low_bits = S::B - ilog2(NVP);
-    const int vi = (lane >> low_bits) & (NVP - 1);
-    if ((lane & ((1 << low_bits) - 1)) == 0 && vi < S::NL) part[slot][vi * S::RPL + row_sub] = r;
+    if (blob == nullptr) {
+        // a routed slot that the top-p cut dropped: weight 0, nothing read
+        for (int t = lane; t < S::R; t += kWave) part[slot][t] = 0.0f;
+    } else {
+        auto code_off = [&](int step, int c) {
+            const size_t row = (size_t)rb * S::R + step * S::RPL + row_sub;
+            return (row * KG + g0 + kWave * c) * 16;
+        };
+        float hraw[S::CPL][32];
+        load_h<S::CPL, KG>(a.h + (size_t)slot * a.I, g0, hraw);
+        u32x4 code[S::NL][S::CPL];
+        auto issue_round = [&](int r) {
+#pragma unroll
+            for (int n = r * WIN; n < (r + 1) * WIN && n < S::NL; ++n)
+#pragma unroll
+                for (int c = 0; c < S::CPL; ++c) code[n][c] = load_stream16(blob + L.down_q + code_off(n, c));
+        };
+        __builtin_amdgcn_sched_barrier(0);
+        issue_round(0);
+        unsigned sc[S::CPL][(S::NL + 1) / 2];
+#pragma unroll
+        for (int c = 0; c < S::CPL; ++c) {
+            const size_t si = ((size_t)rb * KG + g0 + kWave * c) * S::R + (size_t)row_sub * S::NL;
+            load_scales<S::NL>(reinterpret_cast<const uint16_t*>(blob + L.down_s) + si, sc[c]);
+        }
+        if constexpr (NR > 1) issue_round(1);
+        __builtin_amdgcn_sched_barrier(0);
+        HI8 ha[S::CPL];
+        float hscale[S::CPL];
+        to_i8<S::CPL>(hraw, ha, hscale);
+        float v[NVP];
+#pragma unroll
+        for (int n = 0; n < NVP; ++n) v[n] = 0.0f;
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int n = r * WIN; n < (r + 1) * WIN && n < S::NL; ++n) {
+                float acc = 0.0f;
+#pragma unroll
+                for (int c = 0; c < S::CPL; ++c)
+                    acc = fmaf(scale_at(sc[c], n) * hscale[c], dot_chunk_i8(code[n][c], ha[c]), acc);
+                v[n] = acc;
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            if (r + 2 < NR) issue_round(r + 2);
+        }
+        const float r = reduce_scatter<NVP, S::B>(v, lane);
+        const int low_bits = S::B - ilog2(NVP);
+        const int vi = (lane >> low_bits) & (NVP - 1);
+        if ((lane & ((1 << low_bits) - 1)) == 0 && vi < S::NL) part[slot][vi * S::RPL + row_sub] = r;
+    }
     __syncthreads();
     if ((int)threadIdx.x < S::R) {
         const int t = threadIdx.x;

@@ -215,7 +215,7 @@ __device__ __forceinline__ void top2_merge(float& a1, float& a2, float b1, float
 // weight rsf * s_j / sum_chosen s in *my_w.
 template <int EPL>
 __device__ void wave_group_topk_values(const float (&s)[EPL], const float (&key)[EPL], int E, int G, int TG, int K,
-                                       float rsf, int lane, int* my_id, float* my_w) {
+                                       float rsf, float top_p, int lane, int* my_id, float* my_w) {
     const float NEG = -__builtin_inff();
     // Group score: the two largest biased scores of the group.
     const int lpg = (E / G) / EPL;  // lanes per group (power of two)
@@ -299,8 +299,37 @@ __device__ void wave_group_topk_values(const float (&s)[EPL], const float (&key)
             sum_s += se;
         }
     }
-    *my_id = mine_e;
-    *my_w = rsf * mine_s / sum_s;
+    float denom = sum_s;
+    bool keep = true;
+    if (top_p < 1.0f) {
+        // Adaptive top-p over the chosen experts: a choice is kept when the
+        // shares s / sum_s of the choices ranked above it (larger s, ties to
+        // the lower index) add up to less than top_p, tested as
+        // sum of those s < top_p * sum_s; the kept weights are renormalised
+        // over the kept s and a dropped choice gets id -1.
+        float before = 0.0f;
+        bool first = true;  // the top-ranked choice is always kept
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            if (j < K) {
+                const float sj = readlane_f(mine_s, j);
+                const int ej = __builtin_amdgcn_readlane(mine_e, j);
+                if (sj > mine_s || (sj == mine_s && ej < mine_e)) {
+                    before += sj;
+                    first = false;
+                }
+            }
+        }
+        keep = lane < K && (first || before < top_p * sum_s);
+        const unsigned long long km = __ballot(keep);
+        float kept_s = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            if (j < K && ((km >> j) & 1ull)) kept_s += readlane_f(mine_s, j);
+        denom = kept_s;
+    }
+    *my_id = keep ? mine_e : -1;
+    *my_w = keep ? rsf * mine_s / denom : 0.0f;
 }
 
 }  // namespace

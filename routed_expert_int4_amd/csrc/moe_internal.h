@@ -20,6 +20,7 @@ struct WorkspaceLayout {
     size_t sb = 0;             // [E] biased scores
     size_t xq = 0;             // activation operands of the token in flight
     size_t slot_blobs = 0;     // [16] blobs of the routed slots of the token in flight
+    size_t kept = 0;           // [17] routed slots kept by the top-p cut (count first)
     size_t ids = 0;            // [max_T][K] when the caller passes no ids buffer
     size_t w = 0;              // [max_T][K]
     size_t h = 0;              // [K + S][I]

@@ -20,11 +20,17 @@ struct DecodeArgs {
     int32_t* ids;                    // [K] routing output
     float* w;                        // [K]
     const uint8_t** slot_blobs;      // [16] blobs of the routed slots, resolved once (scratch)
+    // With top_p < 1 and a table: the router writes kept[0] = number of
+    // routed slots that survive the top-p cut and kept[1 ..] = those slots in
+    // increasing order, and the gate/up launch covers only them (null
+    // otherwise).
+    int* kept;
     float* h;                        // [(K + S) * I] scratch
     float* y;                        // [H] output
     unsigned* counter;               // router blocks done (workspace control word, 0 between calls)
     int H, I, E, G, TG, K, S;
     float rsf;
+    float top_p;                     // adaptive expert top-p (1: plain top-k)
     // Expert-cache mode: routed slot j reads blobs[j] instead of
     // table[ids[j]] (the host resolved the routing before the launch).
     int direct;

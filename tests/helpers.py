@@ -9,16 +9,18 @@ Y_RTOL = 2e-3          # max |y_gpu - y_ref| <= Y_RTOL * max |y_ref| per token
 W_ATOL_PER_RSF = 1e-6  # |w_gpu - w_ref| <= W_ATOL_PER_RSF * rsf
 
 
-def check_routing(cfg, ids_gpu, w_gpu, ids_ref, w_ref, gap_ref):
-    """ids: equal (as sets and in order) unless the oracle's selection gap is
-    below GAP_EXCUSE; weights within W_ATOL_PER_RSF * rsf where ids agree.
-    Returns the indices of excused tokens."""
+def check_routing(cfg, ids_gpu, w_gpu, ids_ref, w_ref, gap_ref, pgap_ref=None):
+    """ids: equal (as sets and in order, -1 for a choice the top-p cut
+    dropped) unless the oracle's selection gap, or its top-p decision margin
+    (pgap_ref), is below GAP_EXCUSE; weights within W_ATOL_PER_RSF * rsf where
+    ids agree.  Returns the indices of excused tokens."""
     excused = []
     for t in range(ids_ref.shape[0]):
         same = list(ids_gpu[t]) == list(ids_ref[t])
         if not same:
-            assert gap_ref[t] < GAP_EXCUSE, (
-                f"token {t}: ids {list(ids_gpu[t])} != oracle {list(ids_ref[t])} with gap {gap_ref[t]:.3g}")
+            margin = gap_ref[t] if pgap_ref is None else min(gap_ref[t], pgap_ref[t])
+            assert margin < GAP_EXCUSE, (
+                f"token {t}: ids {list(ids_gpu[t])} != oracle {list(ids_ref[t])} with margin {margin:.3g}")
             excused.append(t)
             continue
         err = np.abs(w_gpu[t].astype(np.float64) - w_ref[t]).max()
@@ -45,7 +47,7 @@ def check_layer(weights, x_bits, y_gpu, ids_gpu, w_gpu, rows=None):
     the GPU's ids, so the expert math is still verified."""
     rows = np.arange(x_bits.shape[0]) if rows is None else np.asarray(rows)
     ref = oracle.layer_forward(weights, x_bits[rows])
-    excused = check_routing(weights.cfg, ids_gpu[rows], w_gpu[rows], ref["ids"], ref["w"], ref["gap"])
+    excused = check_routing(weights.cfg, ids_gpu[rows], w_gpu[rows], ref["ids"], ref["w"], ref["gap"], ref["pgap"])
     good = [i for i in range(len(rows)) if i not in excused]
     worst = check_outputs(y_gpu[rows], ref["y"], good)
     if excused:

@@ -41,6 +41,9 @@ def test_invalid_configs_are_rejected():
         dataclasses.replace(synth.TINY, n_groups=3),
         dataclasses.replace(synth.TINY, topk_group=5),
         dataclasses.replace(synth.TINY, top_k=9),
+        dataclasses.replace(synth.TINY, top_p=0.0),
+        dataclasses.replace(synth.TINY, top_p=1.5),
+        dataclasses.replace(synth.TINY, top_p=float("nan")),
     ]
     for cfg in bad:
         assert B.moe_expert_bytes(cfg) == 0

@@ -52,12 +52,12 @@ def chain_input(y: np.ndarray, noise: np.ndarray) -> np.ndarray:
     return synth.round_to_bf16_bits((y / rms + noise).astype(np.float32))
 
 
-def make_stack(torch, slots, n_layers=N_LAYERS, max_T=N_TOKENS):
+def make_stack(torch, slots, n_layers=N_LAYERS, max_T=N_TOKENS, cfg=CFG):
     from routed_expert_int4_amd.layer import DeviceLayer, ExpertCache, HostExpertStore
-    cache = ExpertCache(CFG, n_layers, slots)
+    cache = ExpertCache(cfg, n_layers, slots)
     weights, cached, resident = [], [], []
     for l in range(n_layers):
-        wl = synth.gen_layer(CFG, seed=10 + l)
+        wl = synth.gen_layer(cfg, seed=10 + l)
         weights.append(wl)
         cache.register(l, HostExpertStore(wl))
         lay = DeviceLayer(wl, max_T=max_T, resident=False)
@@ -200,6 +200,39 @@ def test_cache_learning_autopin(torch_cuda):
     assert cache.stats(0)["pinned"] == n_pin
     cache.unpin(0, pins)
     assert cache.stats(0)["pinned"] == 0
+    for lay in cached + resident:
+        lay.close()
+    cache.close()
+
+
+def test_cache_top_p(torch_cuda):
+    """Adaptive top-p behind the cache: a dropped choice (id -1) is never
+    made resident or copied; outputs equal the resident layer's one-token
+    calls bit for bit and the oracle's within tolerance; the counts are the
+    LRU replay of the kept choices only."""
+    import dataclasses
+    torch = torch_cuda
+    from routed_expert_int4_amd.layer import DeviceLayer
+    cfg = dataclasses.replace(CFG, top_p=0.6)
+    slots = CFG.top_k
+    say(f"[gpu] cache with top-p 0.6, {slots} slots")
+    cache, weights, cached, resident = make_stack(torch, slots, n_layers=1, cfg=cfg)
+    x_bits = synth.gen_tokens(cfg, N_TOKENS, seed=60)
+    x = DeviceLayer.to_device_bf16(x_bits)
+    y, ids, w = cached[0].forward(x)
+    y_res, ids_res, w_res = resident[0].forward_each(x)
+    torch.cuda.synchronize()
+    idh = ids.cpu().numpy()
+    assert (idh < 0).any(), "the cut dropped nothing"
+    assert torch.equal(ids, ids_res) and torch.equal(w, w_res) and torch.equal(y, y_res)
+    res = check_layer(weights[0], x_bits, y.cpu().numpy(), idh, w.cpu().numpy())
+    kept = [row[row >= 0] for row in idh]
+    st = cache.stats(0)
+    want = lru.replay(kept, slots)
+    say(f"[gpu] top-p cache: rel err {res['worst_rel']:.3g}, stats {st}, replay {want}")
+    assert (st["hits"], st["misses"], st["evictions"]) == want
+    assert st["h2d_bytes"] == want[1] * cache.nb
+    assert list(cache.usage(0)) == lru.usage(kept, CFG.n_experts)
     for lay in cached + resident:
         lay.close()
     cache.close()

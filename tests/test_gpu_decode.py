@@ -189,3 +189,97 @@ def test_glm_zero_token_and_repeat(torch_cuda, glm):
     assert np.all(y1[1] == 0.0)
     assert np.all(w1.cpu().numpy()[1] == np.float32(synth.GLM.routed_scaling_factor / synth.GLM.top_k))
     check_layer(weights, x, y1, ids1.cpu().numpy(), w1.cpu().numpy(), rows=[0, 2])
+
+
+# ---------------------------------------------------------------- adaptive top-p
+def with_top_p(weights, top_p):
+    return dataclasses.replace(weights, cfg=dataclasses.replace(weights.cfg, top_p=top_p))
+
+
+@pytest.mark.parametrize("cfg_name,top_p", [("TINY", 0.5), ("MID_A", 0.8), ("MID_B", 0.6), ("MID_D", 0.3)])
+def test_top_p_layer_parity(torch_cuda, cfg_name, top_p):
+    """One-token calls with the top-p cut: ids (-1 where dropped), weights
+    and outputs against the oracle; tokens whose top-p margin is below 1e-6
+    are excused and re-checked with the oracle forced onto the GPU's ids."""
+    cfg = {"TINY": synth.TINY, "MID_A": MID_A, "MID_B": MID_B, "MID_D": MID_D}[cfg_name]
+    say(f"[gpu] top-p {top_p} layer parity {cfg_name}")
+    weights = with_top_p(synth.gen_layer(cfg, seed=0), top_p)
+    x = synth.gen_tokens(cfg, 13, seed=2)
+    layer, y, ids, w = run_layer(torch_cuda, weights, x)
+    res = check_layer(weights, x, y, ids, w)
+    dropped = int((ids < 0).sum())
+    say(f"[gpu] {cfg_name} top-p {top_p}: dropped {dropped} of {ids.size} choices, "
+        f"worst rel err {res['worst_rel']:.3g}, excused {res['excused']}")
+    assert dropped > 0, "the cut dropped nothing: the case does not exercise top-p"
+    assert np.all(w[ids < 0] == 0.0)
+    kept = ids >= 0
+    np.testing.assert_allclose((w * kept).sum(axis=1), cfg.routed_scaling_factor, rtol=1e-6)
+    layer.close()
+
+
+def test_top_p_tiny_cut_keeps_one_expert(torch_cuda):
+    """top_p far below every share: only the choice with the largest
+    affinity survives, with the whole weight rsf."""
+    cfg = MID_A
+    say("[gpu] top-p 1e-4 keeps the top expert")
+    weights = with_top_p(synth.gen_layer(cfg, seed=0), 1e-4)
+    x = synth.gen_tokens(cfg, 5, seed=3)
+    layer, y, ids, w = run_layer(torch_cuda, weights, x)
+    assert np.all((ids >= 0).sum(axis=1) == 1)
+    np.testing.assert_allclose(w.max(axis=1), cfg.routed_scaling_factor, rtol=1e-6)
+    check_layer(weights, x, y, ids, w)
+    layer.close()
+
+
+def test_top_p_one_is_plain_top_k(torch_cuda):
+    """top_p = 1 routes and computes exactly as the plain top-k layer."""
+    say("[gpu] top-p 1.0 equals plain top-k")
+    base = synth.gen_layer(MID_A, seed=0)
+    x = synth.gen_tokens(MID_A, 6, seed=4)
+    l1, y1, ids1, w1 = run_layer(torch_cuda, base, x)
+    l2, y2, ids2, w2 = run_layer(torch_cuda, with_top_p(base, 1.0), x)
+    np.testing.assert_array_equal(ids1, ids2)
+    np.testing.assert_array_equal(w1, w2)
+    np.testing.assert_array_equal(y1, y2)
+    l1.close()
+    l2.close()
+
+
+def test_top_p_batched_call_unsupported(torch_cuda):
+    """T > 1 calls of an all-resident layer with top_p < 1 are refused."""
+    from routed_expert_int4_amd.layer import DeviceLayer
+    weights = with_top_p(synth.gen_layer(synth.TINY, seed=0), 0.5)
+    layer = DeviceLayer(weights, max_T=4)
+    x = DeviceLayer.to_device_bf16(synth.gen_tokens(synth.TINY, 4, seed=1))
+    with pytest.raises(B.MoeError) as ei:
+        layer.forward(x)
+    assert ei.value.code == B.MOE_EUNSUPPORTED
+    with pytest.raises(B.MoeError) as ei:
+        layer.router_topk(x)
+    assert ei.value.code == B.MOE_EUNSUPPORTED
+    y, ids, w = layer.forward(x[:1])
+    torch_cuda.cuda.synchronize()
+    layer.close()
+
+
+def test_glm_top_p_decode(torch_cuda, glm):
+    """GLM-shaped layer, top_p 0.7, 200 one-token calls: routing of every
+    token against the oracle, outputs on a sample."""
+    weights, _ = glm
+    say("[gpu] GLM top-p 0.7 decode, 200 tokens")
+    from routed_expert_int4_amd.layer import DeviceLayer
+    wp = with_top_p(weights, 0.7)
+    layer = DeviceLayer(wp, max_T=1)
+    x = synth.gen_tokens(synth.GLM, 200, seed=9)
+    y, ids, w = layer.forward_each(DeviceLayer.to_device_bf16(x))
+    torch_cuda.cuda.synchronize()
+    y, ids, w = y.cpu().numpy(), ids.cpu().numpy(), w.cpu().numpy()
+    ids_ref, w_ref, gap, pgap = oracle.route(wp, x, with_pgap=True)
+    excused = check_routing(wp.cfg, ids, w, ids_ref, w_ref, gap, pgap)
+    kept = (ids >= 0).sum(axis=1)
+    say(f"[gpu] GLM top-p: kept {kept.mean():.2f} of 8 experts per token, {len(excused)} excused")
+    assert kept.min() >= 1 and kept.mean() < 8
+    rows = sorted(set([0, 1, 99, 199] + list(np.argsort(np.minimum(gap, pgap))[:2])))
+    res = check_layer(wp, x, y, ids, w, rows=rows)
+    say(f"[gpu] GLM top-p sampled outputs: worst rel err {res['worst_rel']:.3g}")
+    layer.close()

@@ -129,7 +129,8 @@ def main() -> int:
                     help="cache-stack: experts pinned per layer by learned usage (-1: slots - top_k, 0: plain LRU)")
     ap.add_argument("--learn-tokens", type=int, default=128, help="cache-stack: tokens of the learning pass")
     ap.add_argument("--top-p", type=float, default=1.0,
-                    help="decode: adaptive expert top-p (1: plain top-k); bytes are priced by the experts kept")
+                    help="decode and cache-stack: adaptive expert top-p (1: plain top-k); decode prices its bytes "
+                         "by the experts kept")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported (this layer's path is "
@@ -169,7 +170,8 @@ def bench_cache_stack(args) -> int:
     from routed_expert_int4_amd.layer import DeviceLayer, ExpertCache, HostExpertStore
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
-    cfg = synth.GLM
+    import dataclasses
+    cfg = dataclasses.replace(synth.GLM, top_p=args.top_p)
     n_layers, slots, n_tok = 12, 64, args.stack_tokens
     n_pin = slots - cfg.top_k if args.pin < 0 else args.pin
     with open(os.path.join(ROOT, "tests", "golden", "zipf_bias_stack.json")) as f:
@@ -223,7 +225,8 @@ def bench_cache_stack(args) -> int:
         mid = totals(half)
         d = {k: after[k] - before[k] for k in after}
         d2 = {k: after[k] - mid[k] for k in after}
-        r = {"tokens_per_s": n_tok / (ms / 1e3), "ms": ms,
+        r = {"tokens_per_s": n_tok / (ms / 1e3), "ms": ms, "routed_uses_per_token_layer":
+             (d["hits"] + d["misses"]) / (n_tok * n_layers),
              "hit_rate": d["hits"] / max(d["hits"] + d["misses"], 1),
              "hit_rate_second_half": d2["hits"] / max(d2["hits"] + d2["misses"], 1),
              "h2d_bytes": d["h2d_bytes"], "h2d_gbs": d["h2d_bytes"] / (ms / 1e3) / 1e9}
@@ -268,7 +271,8 @@ def bench_cache_stack(args) -> int:
                 "learning pass x0 seed 310, noise seed 410)",
         "config": {"workload": f"12 GLM-5.2-shaped MoE layers, {n_tok} sequential decode tokens, 64 HBM slots "
                                f"per layer ({n_pin} pinned by learned usage, the rest LRU), pinned host expert "
-                               "store", "layers": n_layers, "slots_per_layer": slots, "pinned_per_layer": n_pin,
+                               "store" + (f", adaptive expert top-p {cfg.top_p}" if cfg.top_p < 1.0 else ""),
+                   "layers": n_layers, "slots_per_layer": slots, "pinned_per_layer": n_pin,
                    "learning_tokens": args.learn_tokens if n_pin > 0 else 0, "tokens": n_tok},
         "hit_rate": round(main_run["hit_rate"], 4),
         "hit_rate_second_half": round(main_run["hit_rate_second_half"], 4),

@@ -33,6 +33,16 @@
  *    holds the even column in its low nibble, two's complement.  The weight
  *    value is fp32(scale) * q, which is exact in fp32.
  *
+ *  - MXFP4 format (codec 1).  The LargerLM README ("What It Proves") runs a
+ *    GLM-5.2 MXFP4 layout; the pages name it only.  Reading: the OCP
+ *    Microscaling (MX) v1.0 MXFP4 element and scale types over blocks of 32
+ *    consecutive inputs, packed as the int4 codes are (even column in the
+ *    low nibble).  An E2M1 element has a sign bit, a 2-bit exponent (bias 1)
+ *    and a 1-bit mantissa: value (-1)^s * 2^(e-1) * (1 + m/2) for e > 0 and
+ *    (-1)^s * m/2 for e = 0 (no infinities or NaNs).  An E8M0 scale byte b
+ *    is 2^(b-127), b = 255 is NaN.  Weight value = scale * element, exact in
+ *    double.
+ *
  *  - Adaptive expert top-p (colibri summary, options list: --topp, an
  *    adaptive expert top-p that cuts the expert reads).  Reading: with
  *    top_p < 1, the selected experts are ranked by their share s_j / sum_sel s
@@ -108,6 +118,45 @@ static void int4_matvec(const uint8_t* q, const uint16_t* s, int rows, int cols,
     }
 }
 
+/* MXFP4: E2M1 element of column c in a packed row, and an E8M0 scale. */
+static double e2m1_at(const uint8_t* row, int c) {
+    int nib = (row[c >> 1] >> ((c & 1) * 4)) & 15;
+    int sgn = nib >> 3, ex = (nib >> 1) & 3, man = nib & 1;
+    double v = ex == 0 ? 0.5 * man : ldexp(1.0 + 0.5 * man, ex - 1);
+    return sgn ? -v : v;
+}
+static double e8m0_value(uint8_t b) { return b == 255 ? NAN : ldexp(1.0, (int)b - 127); }
+
+/* y[r] = sum_c W[r][c] x[c] for an MXFP4 matrix [rows][cols]: W[r][c] =
+ * E8M0(scale[r][c/32]) * E2M1(code[r][c]), formed exactly in double. */
+static void mxfp4_matvec(const uint8_t* q, const uint8_t* s, int rows, int cols, const double* x, double* y) {
+    for (int r = 0; r < rows; ++r) {
+        const uint8_t* qr = q + (size_t)r * (cols / 2);
+        const uint8_t* sr = s + (size_t)r * (cols / 32);
+        double acc = 0.0;
+        for (int g = 0; g < cols / 32; ++g) {
+            double scale = e8m0_value(sr[g]);
+            for (int c = 32 * g; c < 32 * g + 32; ++c) acc += (scale * e2m1_at(qr, c)) * x[c];
+        }
+        y[r] = acc;
+    }
+}
+
+/* Codec 0: int4 codes with fp16 scales; codec 1: MXFP4 (E2M1 codes, E8M0
+ * scales).  Scale arrays are uint16 (codec 0) or uint8 (codec 1). */
+static void codec_matvec(int codec, const uint8_t* q, const void* s, int rows, int cols, const double* x,
+                         double* y) {
+    if (codec == 1)
+        mxfp4_matvec(q, (const uint8_t*)s, rows, cols, x, y);
+    else
+        int4_matvec(q, (const uint16_t*)s, rows, cols, x, y);
+}
+
+/* Public matvec of one quantised matrix (for pins of the decoding). */
+void oracle_matvec(int codec, const uint8_t* q, const void* s, int rows, int cols, const double* x, double* y) {
+    codec_matvec(codec, q, s, rows, cols, x, y);
+}
+
 static double sigmoid(double z) { return 1.0 / (1.0 + exp(-z)); }
 
 /* ---------------------------------------------------------------- public API */
@@ -116,17 +165,17 @@ static double sigmoid(double z) { return 1.0 / (1.0 + exp(-z)); }
  * gate/up: [inter][hidden/2] codes, [inter][hidden/32] scales;
  * down: [hidden][inter/2] codes, [hidden][inter/32] scales.
  * h (optional, [inter]) receives the intermediate activation. */
-void oracle_expert_ffn(int hidden, int inter,
-                       const uint8_t* gate_q, const uint16_t* gate_s,
-                       const uint8_t* up_q, const uint16_t* up_s,
-                       const uint8_t* down_q, const uint16_t* down_s,
+void oracle_expert_ffn(int codec, int hidden, int inter,
+                       const uint8_t* gate_q, const void* gate_s,
+                       const uint8_t* up_q, const void* up_s,
+                       const uint8_t* down_q, const void* down_s,
                        const double* x, double* d, double* h_out) {
     double* g = (double*)malloc(sizeof(double) * (size_t)inter);
     double* u = (double*)malloc(sizeof(double) * (size_t)inter);
-    int4_matvec(gate_q, gate_s, inter, hidden, x, g);
-    int4_matvec(up_q, up_s, inter, hidden, x, u);
+    codec_matvec(codec, gate_q, gate_s, inter, hidden, x, g);
+    codec_matvec(codec, up_q, up_s, inter, hidden, x, u);
     for (int i = 0; i < inter; ++i) g[i] = g[i] * sigmoid(g[i]) * u[i];
-    int4_matvec(down_q, down_s, hidden, inter, g, d);
+    codec_matvec(codec, down_q, down_s, hidden, inter, g, d);
     if (h_out) memcpy(h_out, g, sizeof(double) * (size_t)inter);
     free(g);
     free(u);
@@ -248,16 +297,18 @@ int oracle_select(int n_experts, int n_groups, int topk_group, int top_k, double
  * router's choice; the weights are still rsf * s / sum s over them.
  * Outputs: y [T][hidden], ids [T][top_k], w [T][top_k], gap [T],
  * logits (optional) [T][n_experts].  Returns 0 or -1 on bad arguments. */
-int oracle_layer_forward(int hidden, int inter, int n_experts, int n_groups, int topk_group, int top_k,
+int oracle_layer_forward(int codec, int hidden, int inter, int n_experts, int n_groups, int topk_group, int top_k,
                          int n_shared, double rsf, double top_p,
                          const float* router_w, const float* bias,
-                         const uint8_t* gate_q, const uint16_t* gate_s,
-                         const uint8_t* up_q, const uint16_t* up_s,
-                         const uint8_t* down_q, const uint16_t* down_s,
+                         const uint8_t* gate_q, const void* gate_s,
+                         const uint8_t* up_q, const void* up_s,
+                         const uint8_t* down_q, const void* down_s,
                          const uint16_t* x_bf16, int T, const int32_t* forced_ids,
                          double* y, int32_t* ids, double* w, double* gap, double* pgap, double* logits,
                          int n_threads) {
-    if (hidden % 32 || inter % 32 || T < 0 || n_shared < 0) return -1;
+    if (hidden % 32 || inter % 32 || T < 0 || n_shared < 0 || codec < 0 || codec > 1) return -1;
+    const size_t ssz = codec == 1 ? 1 : 2; /* bytes per scale */
+    const uint8_t *gs_b = (const uint8_t*)gate_s, *us_b = (const uint8_t*)up_s, *ds_b = (const uint8_t*)down_s;
     const size_t gq_n = (size_t)inter * (hidden / 2), gs_n = (size_t)inter * (hidden / 32);
     const size_t dq_n = (size_t)hidden * (inter / 2), ds_n = (size_t)hidden * (inter / 32);
     int status = 0;
@@ -299,8 +350,8 @@ int oracle_layer_forward(int hidden, int inter, int n_experts, int n_groups, int
                 if (j < top_k && it[j] < 0) continue; /* slot dropped by top-p */
                 int e = j < top_k ? it[j] : n_experts + (j - top_k);
                 double scale = j < top_k ? wt[j] : 1.0;
-                oracle_expert_ffn(hidden, inter, gate_q + e * gq_n, gate_s + e * gs_n, up_q + e * gq_n,
-                                  up_s + e * gs_n, down_q + e * dq_n, down_s + e * ds_n, x, d, NULL);
+                oracle_expert_ffn(codec, hidden, inter, gate_q + e * gq_n, gs_b + e * gs_n * ssz, up_q + e * gq_n,
+                                  us_b + e * gs_n * ssz, down_q + e * dq_n, ds_b + e * ds_n * ssz, x, d, NULL);
                 for (int c = 0; c < hidden; ++c) yt[c] += scale * d[c];
             }
         }

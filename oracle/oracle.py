@@ -37,14 +37,16 @@ def lib():
         ):
             build()
         L = ctypes.CDLL(_LIB_PATH)
-        L.oracle_expert_ffn.argtypes = [ctypes.c_int, ctypes.c_int] + [_vp] * 6 + [_d, _d, _d]
+        L.oracle_expert_ffn.argtypes = [ctypes.c_int] * 3 + [_vp] * 6 + [_d, _d, _d]
         L.oracle_expert_ffn.restype = None
+        L.oracle_matvec.argtypes = [ctypes.c_int, _vp, _vp, ctypes.c_int, ctypes.c_int, _d, _d]
+        L.oracle_matvec.restype = None
         L.oracle_router_scores.argtypes = [ctypes.c_int, ctypes.c_int, _vp, _vp, _d, _d, _d, _d]
         L.oracle_router_scores.restype = None
         L.oracle_select.argtypes = [ctypes.c_int] * 4 + [ctypes.c_double, ctypes.c_double, _d, _d, _i32, _d, _d, _d]
         L.oracle_select.restype = ctypes.c_int
         L.oracle_layer_forward.argtypes = (
-            [ctypes.c_int] * 7 + [ctypes.c_double, ctypes.c_double, _vp, _vp] + [_vp] * 6
+            [ctypes.c_int] * 8 + [ctypes.c_double, ctypes.c_double, _vp, _vp] + [_vp] * 6
             + [_vp, ctypes.c_int, _vp, _d, _i32, _d, _d, _d, _vp, ctypes.c_int]
         )
         L.oracle_layer_forward.restype = ctypes.c_int
@@ -71,14 +73,36 @@ def max_threads() -> int:
     return lib().oracle_max_threads()
 
 
-def expert_ffn(hidden, inter, gate_q, gate_s, up_q, up_s, down_q, down_s, x: np.ndarray):
+CODECS = {"int4": 0, "mxfp4": 1}
+
+
+def _scale_dtype(codec: str):
+    return np.uint8 if codec == "mxfp4" else np.uint16
+
+
+def expert_ffn(hidden, inter, gate_q, gate_s, up_q, up_s, down_q, down_s, x: np.ndarray, codec: str = "int4"):
     """One expert on one fp64 token vector x[hidden] -> (d[hidden], h[inter])."""
     x = np.ascontiguousarray(x, dtype=np.float64)
     d = np.empty(hidden, np.float64)
     h = np.empty(inter, np.float64)
     arrs = [np.ascontiguousarray(a) for a in (gate_q, gate_s, up_q, up_s, down_q, down_s)]
-    lib().oracle_expert_ffn(hidden, inter, *[_ptr(a) for a in arrs], _dptr(x), _dptr(d), _dptr(h))
+    for a in arrs[1::2]:
+        assert a.dtype == _scale_dtype(codec), "scale dtype does not match the codec"
+    lib().oracle_expert_ffn(CODECS[codec], hidden, inter, *[_ptr(a) for a in arrs], _dptr(x), _dptr(d), _dptr(h))
     return d, h
+
+
+def matvec(q: np.ndarray, s: np.ndarray, x: np.ndarray, codec: str = "int4") -> np.ndarray:
+    """y = W x for one quantised matrix: codes q [rows, cols/2], scales s
+    [rows, cols/32] (fp16 bits for int4, E8M0 bytes for mxfp4)."""
+    q = np.ascontiguousarray(q, dtype=np.uint8)
+    s = np.ascontiguousarray(s, dtype=_scale_dtype(codec))
+    rows, cols = q.shape[0], 2 * q.shape[1]
+    assert s.shape == (rows, cols // 32)
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    y = np.empty(rows, np.float64)
+    lib().oracle_matvec(CODECS[codec], _ptr(q), _ptr(s), rows, cols, _dptr(x), _dptr(y))
+    return y
 
 
 def router_scores(router_w: np.ndarray, bias: np.ndarray, x: np.ndarray):
@@ -134,8 +158,11 @@ def layer_forward(weights, x_bf16: np.ndarray, forced_ids=None, n_threads: int =
         fid = np.ascontiguousarray(forced_ids, dtype=np.int32)
         assert fid.shape == (T, k)
     wt = weights
+    codec = getattr(cfg, "codec", "int4")
+    for a in (weights.gate_s, weights.up_s, weights.down_s):
+        assert a.dtype == _scale_dtype(codec), "scale dtype does not match the codec"
     rc = lib().oracle_layer_forward(
-        cfg.hidden, cfg.inter, cfg.n_experts, cfg.n_groups, cfg.topk_group, k, cfg.n_shared,
+        CODECS[codec], cfg.hidden, cfg.inter, cfg.n_experts, cfg.n_groups, cfg.topk_group, k, cfg.n_shared,
         float(cfg.routed_scaling_factor), float(getattr(cfg, "top_p", 1.0)),
         _ptr(wt.router_w), _ptr(wt.bias),
         _ptr(wt.gate_q), _ptr(wt.gate_s), _ptr(wt.up_q), _ptr(wt.up_s), _ptr(wt.down_q), _ptr(wt.down_s),

@@ -17,11 +17,17 @@ Public layout of one layer (row-major, little-endian):
   columns.
 * activations: bfloat16 bits ``[T, H]``.
 
+With ``codec="mxfp4"`` the codes are MXFP4 elements (E2M1 nibbles, same
+packing) and every scale array is uint8 E8M0 bytes (one per 32 inputs).
+
 Value distributions follow the GLM-5.2-shaped layer described on the pages
 (routed experts 256, top-8, ~19 MB of int4 codes per expert): codes are uniform
 random bytes (so both nibbles are independent and uniform over [-8, 7]),
 scales are exp(N(-4, 0.5)) rounded to fp16, the router weight is N(0, 0.02) in
 fp32, the bias N(0, 0.01) in fp32 and the activations N(0, 1) rounded to bf16.
+MXFP4 layers draw their codes the same way (uniform bytes: every E2M1 code
+equally likely, rms element 2.93) and E8M0 scale bytes 127 + round(N(-5, 0.75))
+(about 2^-5, so the weights have the int4 layer's magnitude).
 Streams: SeedSequence(seed).spawn(1 + E + S); the first child draws the
 router weight then the bias; child 1 + e draws expert e (routed experts
 first, shared last) in the order gate codes, gate scales, up codes, up
@@ -45,15 +51,20 @@ class LayerConfig:
     n_shared: int = 1
     routed_scaling_factor: float = 2.5
     top_p: float = 1.0  # adaptive expert top-p over the selected experts (1: plain top-k)
+    codec: str = "int4"  # "int4" (fp16 scales) or "mxfp4" (E2M1 codes, E8M0 scales)
 
     @property
     def n_total_experts(self) -> int:
         return self.n_experts + self.n_shared
 
+    @property
+    def scale_bytes(self) -> int:
+        return 1 if self.codec == "mxfp4" else 2
+
     def expert_bytes(self) -> int:
-        """Bytes of one expert in the public layout (codes + fp16 scales)."""
+        """Bytes of one expert in the public layout (codes + scales)."""
         h, i = self.hidden, self.inter
-        return 3 * (h * i // 2) + 3 * (h * i // 32) * 2
+        return 3 * (h * i // 2) + 3 * (h * i // 32) * self.scale_bytes
 
 
 # Tiny layer: hidden 256, intermediate 128, 16 experts in 4 groups, top-4 of 2 groups.
@@ -68,7 +79,7 @@ class LayerWeights:
     router_w: np.ndarray  # float32 [E, H]
     bias: np.ndarray      # float32 [E]
     gate_q: np.ndarray    # uint8  [E+S, I, H/2]
-    gate_s: np.ndarray    # uint16 [E+S, I, H/32] (fp16 bits)
+    gate_s: np.ndarray    # uint16 [E+S, I, H/32] (fp16 bits; uint8 E8M0 for mxfp4)
     up_q: np.ndarray
     up_s: np.ndarray
     down_q: np.ndarray    # uint8  [E+S, H, I/2]
@@ -104,6 +115,12 @@ def _scales(rng: np.random.Generator, shape) -> np.ndarray:
     return np.exp(z * np.float32(0.5) - np.float32(4.0)).astype(np.float16).view(np.uint16)
 
 
+def _e8m0_scales(rng: np.random.Generator, shape) -> np.ndarray:
+    """E8M0 bytes 127 + round(N(-5, 0.75))."""
+    z = rng.standard_normal(size=shape, dtype=np.float32)
+    return (np.rint(z * np.float32(0.75) - np.float32(5.0)) + 127).astype(np.uint8)
+
+
 def gen_router(cfg: LayerConfig, seed: int):
     """The router weight and bias of gen_layer(cfg, seed), without the experts."""
     child = np.random.SeedSequence(seed).spawn(1 + cfg.n_total_experts)[0]
@@ -123,21 +140,22 @@ def gen_layer(cfg: LayerConfig, seed: int, workers: int | None = None) -> LayerW
     h, i, e_all = cfg.hidden, cfg.inter, cfg.n_total_experts
     children = np.random.SeedSequence(seed).spawn(1 + e_all)
     router_w, bias = gen_router(cfg, seed)
+    sdt, scales = (np.uint8, _e8m0_scales) if cfg.codec == "mxfp4" else (np.uint16, _scales)
     gq = np.empty((e_all, i, h // 2), np.uint8)
-    gs = np.empty((e_all, i, h // 32), np.uint16)
+    gs = np.empty((e_all, i, h // 32), sdt)
     uq = np.empty_like(gq)
     us = np.empty_like(gs)
     dq = np.empty((e_all, h, i // 2), np.uint8)
-    ds = np.empty((e_all, h, i // 32), np.uint16)
+    ds = np.empty((e_all, h, i // 32), sdt)
 
     def draw(e):
         r = np.random.Generator(np.random.PCG64(children[1 + e]))
         gq[e] = _codes(r, gq.shape[1:])
-        gs[e] = _scales(r, gs.shape[1:])
+        gs[e] = scales(r, gs.shape[1:])
         uq[e] = _codes(r, uq.shape[1:])
-        us[e] = _scales(r, us.shape[1:])
+        us[e] = scales(r, us.shape[1:])
         dq[e] = _codes(r, dq.shape[1:])
-        ds[e] = _scales(r, ds.shape[1:])
+        ds[e] = scales(r, ds.shape[1:])
 
     n_workers = workers or min(16, os.cpu_count() or 1)
     with concurrent.futures.ThreadPoolExecutor(max_workers=n_workers) as ex:

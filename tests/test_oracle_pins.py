@@ -443,3 +443,111 @@ def test_top_p_layer_matches_forced_kept_experts(tiny, tiny_x):
     # kept weights sum to rsf for every token; at least one expert is kept
     assert np.allclose(out["w"].sum(axis=1), cfg.routed_scaling_factor, rtol=0, atol=1e-12)
     assert ((out["ids"] >= 0).sum(axis=1) >= 1).all()
+
+
+# ----------------------------------------------------------------- MXFP4 codec
+# The OCP Microscaling (MX) v1.0 FP4 (E2M1) value set, listed as the standard's
+# table gives it (the oracle computes it from the bit fields instead), and the
+# E8M0 scale 2^(b - 127).
+E2M1_TABLE = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0, -0.0, -0.5, -1.0, -1.5, -2.0, -3.0, -4.0, -6.0]
+
+
+def pack_nibbles(n: np.ndarray) -> np.ndarray:
+    """Nibble matrix [R, C] (0..15) -> bytes [R, C/2], even column in the low nibble."""
+    n = np.asarray(n, dtype=np.uint8)
+    return (n[:, 0::2] | (n[:, 1::2] << 4)).astype(np.uint8)
+
+
+def test_mxfp4_every_code_and_scale_decodes_to_the_standard_value():
+    """Row r holds code r in every column; with x = e_c the matvec returns
+    the weight W[r, c]: every E2M1 code, both nibble positions, several E8M0
+    scale bytes including the extremes 0 (2^-127) and 254 (2^127)."""
+    rows, cols = 16, 64
+    codes = np.repeat(np.arange(16, dtype=np.uint8)[:, None], cols, axis=1)
+    for b0, b1 in ((127, 127), (126, 130), (0, 254), (100, 1)):
+        s = np.array([[b0, b1]] * rows, np.uint8)
+        for c in (0, 1, 30, 31, 32, 33, 62, 63):
+            x = np.zeros(cols)
+            x[c] = 1.0
+            y = oracle.matvec(pack_nibbles(codes), s, x, codec="mxfp4")
+            b = b0 if c < 32 else b1
+            want = np.array([E2M1_TABLE[r] * 2.0 ** (b - 127) for r in range(16)])
+            np.testing.assert_array_equal(y, want)
+    # scale byte 255 is NaN: it poisons its row (NaN * 0 is NaN), not the others
+    s = np.array([[127, 127]] * rows, np.uint8)
+    s[5, 1] = 255
+    x = np.zeros(cols)
+    x[40] = 1.0
+    y = oracle.matvec(pack_nibbles(codes), s, x, codec="mxfp4")
+    assert np.isnan(y[5])
+    np.testing.assert_array_equal(np.delete(y, 5), np.delete(np.array(E2M1_TABLE), 5))
+
+
+def test_mxfp4_mixed_nibbles_against_numpy():
+    """Random codes and scales: the oracle's matvec equals numpy's product of
+    x with the test's own dense matrix (table lookup, low nibble first)."""
+    rng = np.random.default_rng(21)
+    rows, cols = 24, 96
+    nib = rng.integers(0, 16, size=(rows, cols))
+    s = rng.integers(110, 140, size=(rows, cols // 32)).astype(np.uint8)
+    W = np.array(E2M1_TABLE)[nib] * np.repeat(2.0 ** (s.astype(np.float64) - 127), 32, axis=1)
+    x = rng.normal(size=cols)
+    np.testing.assert_allclose(oracle.matvec(pack_nibbles(nib), s, x, codec="mxfp4"), W @ x, rtol=1e-13, atol=1e-15)
+
+
+def test_mxfp4_layer_equals_int4_layer_on_shared_values():
+    """An MXFP4 layer whose codes take only integer values {0, +-1, +-2, +-3,
+    +-4, +-6} and whose scales are powers of two within fp16's range is the
+    same layer as the int4 one with q = value and fp16 scale = 2^(b - 127):
+    the oracle gives bit-identical routing and outputs for both codecs."""
+    import dataclasses
+    cfg4 = synth.TINY
+    cfg_fp4 = dataclasses.replace(cfg4, codec="mxfp4")
+    base = synth.gen_layer(cfg4, seed=3)
+    rng = np.random.default_rng(5)
+    int_codes = np.array([0, 2, 4, 5, 6, 7, 8, 10, 12, 13, 14, 15])  # E2M1 codes with integer values
+    int_vals = np.array([E2M1_TABLE[c] for c in int_codes]).astype(np.int64)
+
+    def make(shape_q):
+        n = int_codes[rng.integers(0, len(int_codes), size=(shape_q[0], shape_q[1] * 2))]
+        q = np.array([int_vals[list(int_codes).index(c)] for c in n.ravel()]).reshape(n.shape)
+        b = rng.integers(127 - 12, 127 + 8, size=(shape_q[0], shape_q[1] * 2 // 32)).astype(np.uint8)
+        return pack_nibbles(n), b, pack_int4(q), f16_bits(2.0 ** (b.astype(np.float64) - 127))
+
+    fp4, i4 = {}, {}
+    for name in ("gate", "up", "down"):
+        qs = getattr(base, name + "_q")
+        parts = [make(qs.shape[1:]) for _ in range(qs.shape[0])]
+        fp4[name + "_q"] = np.stack([p[0] for p in parts])
+        fp4[name + "_s"] = np.stack([p[1] for p in parts])
+        i4[name + "_q"] = np.stack([p[2] for p in parts])
+        i4[name + "_s"] = np.stack([p[3] for p in parts])
+    w4 = dataclasses.replace(base, **i4)
+    wf = dataclasses.replace(base, cfg=cfg_fp4, **fp4)
+    x = synth.gen_tokens(cfg4, 5, seed=6)
+    a, b = oracle.layer_forward(w4, x), oracle.layer_forward(wf, x)
+    np.testing.assert_array_equal(a["ids"], b["ids"])
+    np.testing.assert_array_equal(a["w"], b["w"])
+    np.testing.assert_array_equal(a["y"], b["y"])
+    assert np.abs(a["y"]).max() > 0
+
+
+def test_mxfp4_byte_accounting_matches_largerlm():
+    """19.125 MiB per GLM-shaped MXFP4 expert (codes + one E8M0 byte per 32
+    weights), and 8 experts x 75 layers of it = the 11.206 GiB per token the
+    LargerLM README prints."""
+    import dataclasses
+    g = json.load(open(os.path.join(GOLDEN, "byte_accounting.json")))
+    eb = dataclasses.replace(synth.GLM, codec="mxfp4").expert_bytes()
+    assert eb == 20_054_016 and eb / 2 ** 20 == 19.125
+    ref = g["mxfp4_routed_gib_per_token"]
+    assert abs(8 * 75 * eb / 2 ** 30 - ref["value"]) <= ref["rtol"] * ref["value"]
+
+
+def test_mxfp4_generator_dtypes_and_scale_range():
+    import dataclasses
+    w = synth.gen_layer(dataclasses.replace(synth.TINY, codec="mxfp4"), seed=0)
+    assert w.gate_s.dtype == np.uint8 and w.down_s.dtype == np.uint8
+    assert 110 <= int(w.gate_s.min()) and int(w.gate_s.max()) <= 135
+    out = oracle.layer_forward(w, synth.gen_tokens(synth.TINY, 3, seed=1))
+    assert np.all(np.isfinite(out["y"]))

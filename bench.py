@@ -36,6 +36,12 @@ KERNEL_SOURCES = [os.path.join(ROOT, "routed_expert_int4_amd", "csrc", f)
                   for f in ("moe_decode.hip", "moe_device.h", "moe_kernels.h", "moe_layout.h")]
 
 
+DTYPES = {
+    "int4": "int4 weights x int16 fixed-point activations (two int8 parts), int32 dot, fp32 accumulate",
+    "mxfp4": "MXFP4 weights (E2M1, E8M0 scales) x fp16 activation pairs, fp32 dot2 accumulate",
+}
+
+
 def algorithmic_bytes(cfg):
     """Bytes each stage must move at least once per token (batch 1).
 
@@ -48,8 +54,9 @@ def algorithmic_bytes(cfg):
     """
     eb = cfg.expert_bytes()
     n = cfg.top_k + cfg.n_shared
-    gu = 2 * (cfg.hidden * cfg.inter // 2 + cfg.inter * (cfg.hidden // 32) * 2)  # gate + up, codes + scales
-    dn = cfg.hidden * cfg.inter // 2 + cfg.hidden * (cfg.inter // 32) * 2
+    sb = cfg.scale_bytes  # 2 (int4, fp16 scales) or 1 (MXFP4, E8M0 scales)
+    gu = 2 * (cfg.hidden * cfg.inter // 2 + cfg.inter * (cfg.hidden // 32) * sb)  # gate + up, codes + scales
+    dn = cfg.hidden * cfg.inter // 2 + cfg.hidden * (cfg.inter // 32) * sb
     router = cfg.n_experts * cfg.hidden * 4 + cfg.n_experts * 4
     io = cfg.hidden * 2 + cfg.hidden * 4
     return {
@@ -128,6 +135,8 @@ def main() -> int:
     ap.add_argument("--pin", type=int, default=-1,
                     help="cache-stack: experts pinned per layer by learned usage (-1: slots - top_k, 0: plain LRU)")
     ap.add_argument("--learn-tokens", type=int, default=128, help="cache-stack: tokens of the learning pass")
+    ap.add_argument("--codec", default="int4", choices=["int4", "mxfp4"],
+                    help="decode and cache-stack: expert weight codec (mxfp4: E2M1 codes, E8M0 scales)")
     ap.add_argument("--top-p", type=float, default=1.0,
                     help="decode and cache-stack: adaptive expert top-p (1: plain top-k); decode prices its bytes "
                          "by the experts kept")
@@ -171,7 +180,7 @@ def bench_cache_stack(args) -> int:
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     import dataclasses
-    cfg = dataclasses.replace(synth.GLM, top_p=args.top_p)
+    cfg = dataclasses.replace(synth.GLM, top_p=args.top_p, codec=args.codec)
     n_layers, slots, n_tok = 12, 64, args.stack_tokens
     n_pin = slots - cfg.top_k if args.pin < 0 else args.pin
     with open(os.path.join(ROOT, "tests", "golden", "zipf_bias_stack.json")) as f:
@@ -266,12 +275,13 @@ def bench_cache_stack(args) -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int4 weights x int16 fixed-point activations (two int8 parts), int32 dot, fp32 accumulate",
+        "dtype": DTYPES[cfg.codec],
         "data": "synthetic (seeded: layer weights 100 + l, Zipf bias per layer, x0 seed 300, noise seed 400; "
                 "learning pass x0 seed 310, noise seed 410)",
         "config": {"workload": f"12 GLM-5.2-shaped MoE layers, {n_tok} sequential decode tokens, 64 HBM slots "
                                f"per layer ({n_pin} pinned by learned usage, the rest LRU), pinned host expert "
-                               "store" + (f", adaptive expert top-p {cfg.top_p}" if cfg.top_p < 1.0 else ""),
+                               "store" + (f", adaptive expert top-p {cfg.top_p}" if cfg.top_p < 1.0 else "")
+                               + (f", {cfg.codec} experts" if cfg.codec != "int4" else ""),
                    "layers": n_layers, "slots_per_layer": slots, "pinned_per_layer": n_pin,
                    "learning_tokens": args.learn_tokens if n_pin > 0 else 0, "tokens": n_tok},
         "hit_rate": round(main_run["hit_rate"], 4),
@@ -416,7 +426,7 @@ def bench_decode(args) -> int:
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     import dataclasses
-    cfg = dataclasses.replace(synth.GLM, top_p=args.top_p)
+    cfg = dataclasses.replace(synth.GLM, top_p=args.top_p, codec=args.codec)
     nbytes = algorithmic_bytes(cfg)
     log("generating the GLM-shaped layer (seed 0) and 1000 tokens (seed 1)")
     weights = synth.gen_layer(cfg, seed=0)
@@ -507,10 +517,10 @@ def bench_decode(args) -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int4 weights x int16 fixed-point activations (two int8 parts), int32 dot, fp32 accumulate",
+        "dtype": DTYPES[cfg.codec],
         "data": "synthetic (seeded: weights seed 0, tokens seed 1)",
         "config": {
-            "workload": "GLM-5.2-shaped MoE layer, batch-1 int4 decode, 1000 independent tokens per step"
+            "workload": f"GLM-5.2-shaped MoE layer, batch-1 {cfg.codec} decode, 1000 independent tokens per step"
                         + (f", adaptive expert top-p {cfg.top_p}" if cfg.top_p < 1.0 else ""),
             "hidden": cfg.hidden, "expert_intermediate": cfg.inter, "routed_experts": cfg.n_experts,
             "groups": cfg.n_groups, "topk_group": cfg.topk_group, "top_k": cfg.top_k, "shared_experts": cfg.n_shared,
@@ -532,7 +542,7 @@ def bench_decode(args) -> int:
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(gateup_gbs / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic() if cfg.top_p >= 1.0 else None,
+            "traffic": measured_traffic() if cfg.top_p >= 1.0 and cfg.codec == "int4" else None,
             "bytes_per_launch": nbytes["gateup_launch"],
             "avg_launch_us": round(avg_us[1], 3),
         },

@@ -68,6 +68,20 @@ typedef enum {
  * -1 and weight 0 and is never read.  top_p = 1 is plain top-k.  top_p < 1 is
  * served by the one-token path (T = 1 calls, and tokens behind an expert
  * cache); T > 1 calls of an all-resident layer return MOE_EUNSUPPORTED. */
+/* Expert weight codecs.  Both hold 32-input scale groups and two 4-bit codes
+ * per byte (even column in the low nibble).
+ * MOE_CODEC_INT4: two's complement int4 codes, fp16 scales (the layer's
+ *   stated format).
+ * MOE_CODEC_MXFP4: the GLM-5.2 MXFP4 layout that the LargerLM README streams
+ *   ("What It Proves"), read as OCP MX v1.0 MXFP4: E2M1 codes (sign, 2-bit
+ *   exponent with bias 1, 1-bit mantissa: 0, 0.5, 1, 1.5, 2, 3, 4, 6 and
+ *   their negatives), one E8M0 scale byte b = 2^(b-127) per group (b = 255,
+ *   NaN, is refused by moe_expert_pack).  19.125 MiB per expert at hidden
+ *   6144, inter 2048.  Served by the one-token path (T = 1 calls, and tokens
+ *   behind an expert cache); T > 1 calls of an all-resident layer return
+ *   MOE_EUNSUPPORTED. */
+enum { MOE_CODEC_INT4 = 0, MOE_CODEC_MXFP4 = 1 };
+
 typedef struct {
     int hidden;
     int inter;
@@ -78,6 +92,7 @@ typedef struct {
     int n_shared;
     float routed_scaling_factor;
     float top_p;
+    int codec; /* MOE_CODEC_INT4 or MOE_CODEC_MXFP4 (layout of the expert weights) */
 } moe_config_t;
 
 typedef struct moe_layer moe_layer_t;
@@ -97,18 +112,22 @@ const char* moe_last_error(void);
  *   down_q uint8 [hidden][inter/2], down_s fp16 [hidden][inter/32]
  * Weight value = fp32(scale) * code.
  *
+ * With codec MOE_CODEC_MXFP4 the codes are E2M1 and the three scale arrays
+ * hold uint8 E8M0 bytes with the same shapes.
+ *
  * moe_expert_bytes: size of one packed device blob (equal to the public
- * layout's size: 3*hidden*inter/2 + 3*hidden*inter/16 bytes; 21,233,664 for
- * hidden 6144, inter 2048).  Returns 0 for an invalid config.
+ * layout's size: 3*hidden*inter/2 + 3*hidden*inter/32 * scale bytes (2 for
+ * int4, 1 for MXFP4); 21,233,664 (int4) or 20,054,016 (MXFP4) for hidden
+ * 6144, inter 2048).  Returns 0 for an invalid config.
  *
  * moe_expert_pack: host-only repack of one expert from the public layout
  * (host pointers) into the blob format the kernels read (host buffer of
  * moe_expert_bytes bytes).  The caller copies the blob to device memory or
  * keeps it in pinned host memory for the expert cache. */
 size_t moe_expert_bytes(const moe_config_t* cfg);
-moe_status_t moe_expert_pack(const moe_config_t* cfg, const uint8_t* gate_q, const uint16_t* gate_s,
-                             const uint8_t* up_q, const uint16_t* up_s, const uint8_t* down_q,
-                             const uint16_t* down_s, void* dst_blob);
+moe_status_t moe_expert_pack(const moe_config_t* cfg, const uint8_t* gate_q, const void* gate_s,
+                             const uint8_t* up_q, const void* up_s, const uint8_t* down_q, const void* down_s,
+                             void* dst_blob);
 
 /* ------------------------------------------------------------ layer
  * moe_layer_create: d_router_w fp32 [n_experts][hidden], d_bias fp32

@@ -26,17 +26,23 @@ class MoeConfig(ctypes.Structure):
     _fields_ = [
         ("hidden", _i), ("inter", _i), ("n_experts", _i), ("n_groups", _i), ("topk_group", _i),
         ("top_k", _i), ("n_shared", _i), ("routed_scaling_factor", ctypes.c_float), ("top_p", ctypes.c_float),
+        ("codec", _i),
     ]
 
     @classmethod
     def from_cfg(cls, cfg) -> "MoeConfig":
         return cls(cfg.hidden, cfg.inter, cfg.n_experts, cfg.n_groups, cfg.topk_group, cfg.top_k, cfg.n_shared,
-                   float(cfg.routed_scaling_factor), float(getattr(cfg, "top_p", 1.0)))
+                   float(cfg.routed_scaling_factor), float(getattr(cfg, "top_p", 1.0)),
+                   CODECS[getattr(cfg, "codec", "int4")])
 
 
 class MoeCacheStats(ctypes.Structure):
     _fields_ = [("hits", ctypes.c_uint64), ("misses", ctypes.c_uint64), ("h2d_bytes", ctypes.c_uint64),
                 ("evictions", ctypes.c_uint64), ("prefetches", ctypes.c_uint64), ("pinned", ctypes.c_uint64)]
+
+
+MOE_CODEC_INT4, MOE_CODEC_MXFP4 = 0, 1
+CODECS = {"int4": MOE_CODEC_INT4, "mxfp4": MOE_CODEC_MXFP4}
 
 
 class MoeError(RuntimeError):

@@ -51,6 +51,7 @@ moe_status_t validate_config(const moe_config_t* c) {
     if (!(c->routed_scaling_factor == c->routed_scaling_factor))
         return fail(MOE_EINVAL, "routed_scaling_factor is NaN");
     if (!(c->top_p > 0.0f && c->top_p <= 1.0f)) return fail(MOE_EINVAL, "top_p must be in (0, 1]");
+    if (c->codec != kCodecInt4 && c->codec != kCodecMxfp4) return fail(MOE_EINVAL, "unknown codec %d", c->codec);
     return MOE_OK;
 }
 
@@ -129,6 +130,25 @@ WorkspaceLayout workspace_layout(const moe_config_t* c, int max_T) {
     return W;
 }
 
+// Scale arrays of one expert, permuted into the per-lane packs the kernels
+// read (T = uint16_t fp16 bits or uint8_t E8M0 bytes).
+template <typename T>
+void pack_scale_arrays(uint8_t* dst, const BlobLayout& L, int H, int I, const T* gate_s, const T* up_s,
+                              const T* down_s) {
+    const int kh = H / 32, ki = I / 32;
+    T* gu = reinterpret_cast<T*>(dst + L.gu_s);
+    const int p = gateup_rows(kh);
+    for (int r = 0; r < I; ++r)
+        for (int g = 0; g < kh; ++g) {
+            gu[gateup_scale_index(r, g, 0, kh, p)] = gate_s[(size_t)r * kh + g];
+            gu[gateup_scale_index(r, g, 1, kh, p)] = up_s[(size_t)r * kh + g];
+        }
+    T* dn = reinterpret_cast<T*>(dst + L.down_s);
+    const int pd = down_rows(H, ki);
+    for (int r = 0; r < H; ++r)
+        for (int g = 0; g < ki; ++g) dn[scale_index(r, g, ki, pd)] = down_s[(size_t)r * ki + g];
+}
+
 }  // namespace moe
 
 using namespace moe;
@@ -139,44 +159,43 @@ const char* moe_last_error(void) { return g_last_error.c_str(); }
 
 size_t moe_expert_bytes(const moe_config_t* cfg) {
     if (validate_config(cfg) != MOE_OK) return 0;
-    return blob_layout(cfg->hidden, cfg->inter).total;
+    return blob_layout(cfg->hidden, cfg->inter, cfg->codec).total;
 }
 
-moe_status_t moe_expert_pack(const moe_config_t* cfg, const uint8_t* gate_q, const uint16_t* gate_s,
-                             const uint8_t* up_q, const uint16_t* up_s, const uint8_t* down_q,
-                             const uint16_t* down_s, void* dst_blob) {
+moe_status_t moe_expert_pack(const moe_config_t* cfg, const uint8_t* gate_q, const void* gate_s,
+                             const uint8_t* up_q, const void* up_s, const uint8_t* down_q, const void* down_s,
+                             void* dst_blob) {
     moe_status_t st = validate_config(cfg);
     if (st != MOE_OK) return st;
     if (!gate_q || !gate_s || !up_q || !up_s || !down_q || !down_s || !dst_blob)
         return fail(MOE_EINVAL, "moe_expert_pack: NULL pointer");
     const int H = cfg->hidden, I = cfg->inter;
-    const BlobLayout L = blob_layout(H, I);
+    const BlobLayout L = blob_layout(H, I, cfg->codec);
     uint8_t* dst = static_cast<uint8_t*>(dst_blob);
     const size_t codes = (size_t)H * I / 2;
-    // codes: stored as q + 8 (flip bit 3 of every two's complement nibble)
-    const uint8_t* src_q[3] = {gate_q, up_q, down_q};
-    const size_t dst_q[3] = {L.gate_q, L.up_q, L.down_q};
-    for (int m = 0; m < 3; ++m)
-        for (size_t i = 0; i < codes; ++i) dst[dst_q[m] + i] = src_q[m][i] ^ 0x88u;
-    // scales: permuted into the per-lane packs the kernels read
-    auto pack_scales = [&](const uint16_t* src, size_t off, int rows, int kg, int p) {
-        uint16_t* d = reinterpret_cast<uint16_t*>(dst + off);
-        for (int r = 0; r < rows; ++r)
-            for (int g = 0; g < kg; ++g) d[scale_index(r, g, kg, p)] = src[(size_t)r * kg + g];
-    };
     const int kh = H / 32, ki = I / 32;
     if (I % gateup_rows(kh) || H % down_rows(H, ki))
         return fail(MOE_EUNSUPPORTED, "moe_expert_pack: rows not a multiple of the scale pack");
-    {
-        uint16_t* d = reinterpret_cast<uint16_t*>(dst + L.gu_s);
-        const int p = gateup_rows(kh);
-        for (int r = 0; r < I; ++r)
-            for (int g = 0; g < kh; ++g) {
-                d[gateup_scale_index(r, g, 0, kh, p)] = gate_s[(size_t)r * kh + g];
-                d[gateup_scale_index(r, g, 1, kh, p)] = up_s[(size_t)r * kh + g];
-            }
+    const uint8_t* src_q[3] = {gate_q, up_q, down_q};
+    const size_t dst_q[3] = {L.gate_q, L.up_q, L.down_q};
+    if (cfg->codec == kCodecMxfp4) {
+        // E8M0 byte 255 is NaN: refused rather than carried into the kernels
+        const uint8_t* src_s[3] = {static_cast<const uint8_t*>(gate_s), static_cast<const uint8_t*>(up_s),
+                                   static_cast<const uint8_t*>(down_s)};
+        const size_t n_s = (size_t)H * I / 32;
+        for (int m = 0; m < 3; ++m)
+            for (size_t i = 0; i < n_s; ++i)
+                if (src_s[m][i] == 255) return fail(MOE_EINVAL, "moe_expert_pack: E8M0 scale 255 (NaN)");
+        // codes: E2M1 nibbles as they are
+        for (int m = 0; m < 3; ++m) std::memcpy(dst + dst_q[m], src_q[m], codes);
+        pack_scale_arrays(dst, L, H, I, src_s[0], src_s[1], src_s[2]);
+    } else {
+        // codes: stored as q + 8 (flip bit 3 of every two's complement nibble)
+        for (int m = 0; m < 3; ++m)
+            for (size_t i = 0; i < codes; ++i) dst[dst_q[m] + i] = src_q[m][i] ^ 0x88u;
+        pack_scale_arrays(dst, L, H, I, static_cast<const uint16_t*>(gate_s), static_cast<const uint16_t*>(up_s),
+                          static_cast<const uint16_t*>(down_s));
     }
-    pack_scales(down_s, L.down_s, H, ki, down_rows(H, ki));
     return MOE_OK;
 }
 
@@ -310,6 +329,7 @@ DecodeArgs decode_args(moe_layer_t* L, const uint16_t* x, int32_t* ids, float* w
     a.S = c.n_shared;
     a.rsf = c.routed_scaling_factor;
     a.top_p = c.top_p;
+    a.codec = c.codec;
     a.direct = 0;
     a.use_slot_list = 0;
     a.n_slot_list = 0;
@@ -462,6 +482,7 @@ moe_status_t moe_layer_forward(moe_layer_t* layer, const uint16_t* d_x, int T, f
     float* w_base = d_w ? d_w : reinterpret_cast<float*>(layer->ws + layer->W.w);
     if (T > 1 && !layer->cache) {
         if (c.top_p < 1.0f) return fail(MOE_EUNSUPPORTED, "moe_layer_forward: top_p < 1 needs T = 1 calls");
+        if (c.codec != kCodecInt4) return fail(MOE_EUNSUPPORTED, "moe_layer_forward: MXFP4 experts need T = 1 calls");
         // batch union: every distinct expert of a launch sequence is read once
         const int tb = layer->W.batch_tokens;
         for (int t0 = 0; t0 < T; t0 += tb) {

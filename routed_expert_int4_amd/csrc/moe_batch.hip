@@ -361,7 +361,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) b
     const int n_tiles = a.n_tiles[0];
     const int rblocks = a.I / kBlockRows;
     const int items = n_tiles * rblocks;
-    const BlobLayout L = blob_layout(a.H, a.I);
+    const BlobLayout L = blob_layout(a.H, a.I, kCodecInt4);  // int4 only
     const int row_bytes = a.H / 2;
     int gs = 0;  // stages so far: selects the LDS buffer
     for (int item = blockIdx.x; item < items; item += gridDim.x) {
@@ -540,7 +540,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) b
     const int n_tiles = a.n_tiles[0];
     const int rblocks = a.H / kBlockRows;
     const int items = n_tiles * rblocks;
-    const BlobLayout L = blob_layout(a.H, a.I);
+    const BlobLayout L = blob_layout(a.H, a.I, kCodecInt4);  // int4 only
     const int row_bytes = a.I / 2;
     int gs = 0;
     for (int item = blockIdx.x; item < items; item += gridDim.x) {

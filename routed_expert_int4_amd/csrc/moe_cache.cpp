@@ -208,7 +208,7 @@ moe_status_t expert_cache_create(const moe_config_t* cfg, int n_layers, int slot
                     cfg->top_k);
     if (slots_per_layer > cfg->n_experts)
         return fail(MOE_EINVAL, "expert_cache_create: more slots than experts");
-    const size_t eb = blob_layout(cfg->hidden, cfg->inter).total;
+    const size_t eb = blob_layout(cfg->hidden, cfg->inter, cfg->codec).total;
     const size_t need = eb * (size_t)n_layers * (size_t)slots_per_layer;
     if (!d_slot_pool || pool_bytes < need)
         return fail(MOE_EINVAL, "expert_cache_create: slot pool of %zu bytes is smaller than %zu", pool_bytes, need);
@@ -373,7 +373,8 @@ moe_status_t moe_layer_attach_cache(moe_layer_t* layer, moe_cache_t* cache, int 
     if (layer_id < 0 || layer_id >= cache->n_layers)
         return fail(MOE_EINVAL, "moe_layer_attach_cache: layer_id %d out of range", layer_id);
     const moe_config_t &a = layer->cfg, &b = cache->cfg;
-    if (a.hidden != b.hidden || a.inter != b.inter || a.n_experts != b.n_experts || a.top_k != b.top_k)
+    if (a.hidden != b.hidden || a.inter != b.inter || a.n_experts != b.n_experts || a.top_k != b.top_k ||
+        a.codec != b.codec)
         return fail(MOE_EINVAL, "moe_layer_attach_cache: cache and layer shapes differ");
     layer->cache = cache;
     layer->cache_layer = layer_id;

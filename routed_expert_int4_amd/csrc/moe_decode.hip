@@ -110,6 +110,70 @@ __device__ __forceinline__ float dot_chunk_i8(u32x4 c, const HI8& a) {
     return (float)(hi * 256 + lo - a.corr);
 }
 
+// MXFP4 scheme: the activation group as fp16 pairs in natural column order,
+// scaled by a power of two so that its maximum lies in [2^14, 2^15) (exact
+// for bf16 x; round to nearest for h), held in the HI8 container: dword j of
+// he, ho, le, lo (code dword d = 0, 1, 2, 3) pairs with byte j of code dword
+// d, i.e. columns 8d + 2j (low nibble) and 8d + 2j + 1 (high nibble).
+template <int CPL>
+__device__ __forceinline__ void to_f16(const float (&hin)[CPL][32], HI8 (&ha)[CPL], float (&hscale)[CPL]) {
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+        const float (&hv)[32] = hin[c];
+        unsigned mx = 0;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) mx = umax(mx, __builtin_bit_cast(unsigned, hv[i]) & 0x7FFFFFFFu);
+        const int kh = range_exponent(mx >> 23) + 1;  // max |v| 2^kh in [2^14, 2^15)
+        hscale[c] = __builtin_ldexpf(1.0f, -kh);
+        const float up = __builtin_ldexpf(1.0f, kh);
+        unsigned p[16];
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            const f16x2 pair = {(_Float16)(hv[2 * k] * up), (_Float16)(hv[2 * k + 1] * up)};
+            p[k] = __builtin_bit_cast(unsigned, pair);
+        }
+        ha[c].he = u32x4{p[0], p[1], p[2], p[3]};
+        ha[c].ho = u32x4{p[4], p[5], p[6], p[7]};
+        ha[c].le = u32x4{p[8], p[9], p[10], p[11]};
+        ha[c].lo = u32x4{p[12], p[13], p[14], p[15]};
+        ha[c].corr = 0;
+    }
+}
+
+// Dot of one 16-byte chunk of E2M1 codes with the fp16 pairs: each code byte
+// becomes an fp16 pair with v_cvt_scalef32_pk_f16_fp4 (scale 1, so the pair
+// holds the E2M1 values exactly), multiplied and summed in fp32 by
+// v_dot2c_f32_f16.
+__device__ __forceinline__ float dot_chunk_fp4(u32x4 c, const HI8& a) {
+    float acc0 = 0.0f, acc1 = 0.0f;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        const unsigned w = c[d];
+        const u32x4 x = d == 0 ? a.he : d == 1 ? a.ho : d == 2 ? a.le : a.lo;
+        acc0 = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0), as_h2(x[0]), acc0, false);
+        acc1 = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1), as_h2(x[1]), acc1, false);
+        acc0 = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2), as_h2(x[2]), acc0, false);
+        acc1 = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3), as_h2(x[3]), acc1, false);
+    }
+    return acc0 + acc1;
+}
+
+// Codec dispatch of the operand form and the chunk dot.
+template <int F, int CPL>
+__device__ __forceinline__ void to_operands(const float (&hin)[CPL][32], HI8 (&ha)[CPL], float (&hscale)[CPL]) {
+    if constexpr (F == kCodecMxfp4)
+        to_f16<CPL>(hin, ha, hscale);
+    else
+        to_i8<CPL>(hin, ha, hscale);
+}
+template <int F>
+__device__ __forceinline__ float dot_chunk(u32x4 c, const HI8& a) {
+    if constexpr (F == kCodecMxfp4)
+        return dot_chunk_fp4(c, a);
+    else
+        return dot_chunk_i8(c, a);
+}
+
 // ---------------------------------------------------------------- gate/up
 constexpr int kGateUpItemsPerRound = 2;   // routed gate/up kernel
 constexpr int kSharedItemsPerRound = 3;   // shared expert's gate/up in the router launch
@@ -159,14 +223,65 @@ __device__ __forceinline__ void load_scales(const uint16_t* p, unsigned (&d)[(NL
         }
     }
 }
-template <int N>
+// NL consecutive E8M0 bytes (NL-byte aligned, up to 4 per dword).
+template <int NL, int M>
+__device__ __forceinline__ void load_scale_bytes(const uint8_t* p, unsigned (&d)[M]) {
+    static_assert(M * 4 >= NL, "scale pack");
+    if constexpr (NL == 1) {
+        d[0] = __builtin_nontemporal_load(as_global<uint8_t>(p));
+    } else if constexpr (NL == 2) {
+        d[0] = __builtin_nontemporal_load(as_global<uint16_t>(p));
+    } else if constexpr (NL == 4) {
+        d[0] = __builtin_nontemporal_load(as_global<unsigned>(p));
+    } else if constexpr (NL % 16 != 0) {
+        static_assert(NL % 8 == 0, "scale pack");
+#pragma unroll
+        for (int q = 0; q < NL / 8; ++q) {
+            const u32x2 v = __builtin_nontemporal_load(as_global<u32x2>(p) + q);
+            d[2 * q + 0] = v[0];
+            d[2 * q + 1] = v[1];
+        }
+    } else {
+#pragma unroll
+        for (int q = 0; q < NL / 16; ++q) {
+            const u32x4 v = __builtin_nontemporal_load(as_global<u32x4>(p) + q);
+            d[4 * q + 0] = v[0];
+            d[4 * q + 1] = v[1];
+            d[4 * q + 2] = v[2];
+            d[4 * q + 3] = v[3];
+        }
+    }
+}
+
+// NL consecutive scales of codec F starting at byte pointer p.
+template <int F, int NL, int M>
+__device__ __forceinline__ void load_scales_c(const uint8_t* p, unsigned (&d)[M]) {
+    if constexpr (F == kCodecMxfp4) {
+        load_scale_bytes<NL>(p, d);
+    } else {
+        static_assert(M == (NL + 1) / 2, "scale pack");
+        load_scales<NL>(reinterpret_cast<const uint16_t*>(p), d);
+    }
+}
+
+// E8M0 byte b -> 2^(b - 127) (b = 0 is the subnormal 2^-127; the packer
+// refuses 255).
+__device__ __forceinline__ float e8m0_to_float(unsigned b) {
+    return __builtin_bit_cast(float, b ? b << 23 : 0x00400000u);
+}
+
+// Scale n of a run loaded by load_scales_c.
+template <int F, int N>
 __device__ __forceinline__ float scale_at(const unsigned (&d)[N], int n) {
-    return half_bits_to_float((n & 1) ? (d[n / 2] >> 16) : (d[n / 2] & 0xFFFFu));
+    if constexpr (F == kCodecMxfp4)
+        return e8m0_to_float((d[n / 4] >> (8 * (n % 4))) & 0xFFu);
+    else
+        return half_bits_to_float((n & 1) ? (d[n / 2] >> 16) : (d[n / 2] & 0xFFFFu));
 }
 
 // This lane's activation groups (bf16, natural column order) in the HI8
 // form, with the per-group factor that undoes the integer scaling.
-template <int KG>
+template <int KG, int F>
 __device__ __forceinline__ void convert_activations(const uint16_t* __restrict__ x, int lane,
                                                     HI8 (&xa)[GateUpShape<KG>::CPL], float (&xs)[GateUpShape<KG>::CPL]) {
     using S = GateUpShape<KG>;
@@ -186,7 +301,7 @@ __device__ __forceinline__ void convert_activations(const uint16_t* __restrict__
             }
         }
     }
-    to_i8<S::CPL>(xv, xa, xs);
+    to_operands<F, S::CPL>(xv, xa, xs);
 }
 
 // Converted activations in the workspace: lane l, chunk column c holds the
@@ -233,7 +348,7 @@ struct GateUpBuf {
     unsigned sgu[S::CPL][S::NL];  // halves 0..NL-1 gate, NL..2NL-1 up
 };
 
-template <int KG>
+template <int KG, int F>
 __device__ __forceinline__ void gateup_issue(const uint8_t* __restrict__ blob, const BlobLayout& L, int rb, int lane,
                                              GateUpBuf<KG>& b) {
     using S = GateUpShape<KG>;
@@ -251,13 +366,17 @@ __device__ __forceinline__ void gateup_issue(const uint8_t* __restrict__ blob, c
     }
 #pragma unroll
     for (int c = 0; c < S::CPL; ++c) {
-        const uint16_t* p =
-            reinterpret_cast<const uint16_t*>(blob + L.gu_s) + ((size_t)rb * KG + g0 + kWave * c) * 2 * S::R;
+        const uint8_t* p = blob + L.gu_s + ((size_t)rb * KG + g0 + kWave * c) * 2 * S::R * scale_bytes(F);
         if constexpr (S::RPL == 1) {
-            load_scales<2 * S::NL>(p, b.sgu[c]);
+            load_scales_c<F, 2 * S::NL>(p, b.sgu[c]);
+        } else if constexpr (F == kCodecMxfp4) {
+            const unsigned g = __builtin_nontemporal_load(as_global<uint8_t>(p + row_sub));
+            const unsigned u = __builtin_nontemporal_load(as_global<uint8_t>(p + S::R + row_sub));
+            b.sgu[c][0] = g | (u << 8);
         } else {
-            const unsigned g = __builtin_nontemporal_load(as_global<uint16_t>(p + row_sub));
-            const unsigned u = __builtin_nontemporal_load(as_global<uint16_t>(p + S::R + row_sub));
+            const uint16_t* p16 = reinterpret_cast<const uint16_t*>(p);
+            const unsigned g = __builtin_nontemporal_load(as_global<uint16_t>(p16 + row_sub));
+            const unsigned u = __builtin_nontemporal_load(as_global<uint16_t>(p16 + S::R + row_sub));
             b.sgu[c][0] = g | (u << 16);
         }
     }
@@ -277,7 +396,7 @@ __device__ __forceinline__ size_t h_index(int i, int kgi) {
 
 // Computes one item from its loaded buffer: h = silu(g) * u for rows
 // [rb*R, rb*R + R), written as fp32 at their h_index positions.
-template <int KG>
+template <int KG, int F>
 __device__ __forceinline__ void gateup_compute(const GateUpBuf<KG>& b, int rb, int lane,
                                                const HI8 (&xa)[GateUpShape<KG>::CPL],
                                                const float (&xs)[GateUpShape<KG>::CPL], float* __restrict__ h_out,
@@ -290,8 +409,8 @@ __device__ __forceinline__ void gateup_compute(const GateUpBuf<KG>& b, int rb, i
         float ag = 0.0f, au = 0.0f;
 #pragma unroll
         for (int c = 0; c < S::CPL; ++c) {
-            ag = fmaf(scale_at(b.sgu[c], n) * xs[c], dot_chunk_i8(b.cg[n][c], xa[c]), ag);
-            au = fmaf(scale_at(b.sgu[c], S::NL + n) * xs[c], dot_chunk_i8(b.cu[n][c], xa[c]), au);
+            ag = fmaf(scale_at<F>(b.sgu[c], n) * xs[c], dot_chunk<F>(b.cg[n][c], xa[c]), ag);
+            au = fmaf(scale_at<F>(b.sgu[c], S::NL + n) * xs[c], dot_chunk<F>(b.cu[n][c], xa[c]), au);
         }
         v[n] = ag;
         v[S::NL + n] = au;
@@ -364,7 +483,7 @@ __host__ __device__ inline int shared_gateup_blocks(int I) {
     return (per_slot + 4 * kSharedItemsPerRound - 1) / (4 * kSharedItemsPerRound);
 }
 
-template <int KG, int EPL>
+template <int KG, int EPL, int F>
 __global__ void __launch_bounds__(256) router_kernel(DecodeArgs a) {
     using S = GateUpShape<KG>;
     constexpr int NI = kSharedItemsPerRound;
@@ -378,7 +497,7 @@ __global__ void __launch_bounds__(256) router_kernel(DecodeArgs a) {
         if (wave != 0) return;
         HI8 xa[S::CPL];
         float xs[S::CPL];
-        convert_activations<KG>(a.x, lane, xa, xs);
+        convert_activations<KG, F>(a.x, lane, xa, xs);
         store_activations<KG>(a.xq, lane, xa, xs);
         return;
     }
@@ -388,32 +507,32 @@ __global__ void __launch_bounds__(256) router_kernel(DecodeArgs a) {
         const int wave_id = (b - n_router_blocks) * 4 + wave;
         const int n_waves = n_shared_blocks * 4;
         if (wave_id >= per_slot) return;
-        const BlobLayout L = blob_layout(a.H, a.I);
+        const BlobLayout L = blob_layout(a.H, a.I, F);
         GateUpBuf<KG> buf[NI];
 #pragma unroll
         for (int k = 0; k < NI; ++k) {
             const int it = wave_id + k * n_waves;
-            gateup_issue<KG>(a.shared_blob, L, it < per_slot ? it : per_slot - 1, lane, buf[k]);
+            gateup_issue<KG, F>(a.shared_blob, L, it < per_slot ? it : per_slot - 1, lane, buf[k]);
         }
         HI8 xa[S::CPL];
         float xs[S::CPL];
-        convert_activations<KG>(a.x, lane, xa, xs);
+        convert_activations<KG, F>(a.x, lane, xa, xs);
         float* h = a.h + (size_t)a.K * a.I;
 #pragma unroll
         for (int k = 0; k < NI; ++k) {
             const int it = wave_id + k * n_waves;
-            gateup_compute<KG>(buf[k], it < per_slot ? it : per_slot - 1, lane, xa, xs, h, a.I / 32, it < per_slot);
+            gateup_compute<KG, F>(buf[k], it < per_slot ? it : per_slot - 1, lane, xa, xs, h, a.I / 32, it < per_slot);
         }
         for (int base = wave_id + NI * n_waves; base < per_slot; base += NI * n_waves) {
 #pragma unroll
             for (int k = 0; k < NI; ++k) {
                 const int it = base + k * n_waves;
-                gateup_issue<KG>(a.shared_blob, L, it < per_slot ? it : per_slot - 1, lane, buf[k]);
+                gateup_issue<KG, F>(a.shared_blob, L, it < per_slot ? it : per_slot - 1, lane, buf[k]);
             }
 #pragma unroll
             for (int k = 0; k < NI; ++k) {
                 const int it = base + k * n_waves;
-                gateup_compute<KG>(buf[k], it < per_slot ? it : per_slot - 1, lane, xa, xs, h, a.I / 32, it < per_slot);
+                gateup_compute<KG, F>(buf[k], it < per_slot ? it : per_slot - 1, lane, xa, xs, h, a.I / 32, it < per_slot);
             }
         }
         return;
@@ -497,7 +616,7 @@ __global__ void __launch_bounds__(256) router_kernel(DecodeArgs a) {
 // n_waves in rounds of NI, in straight-line code (items past the end are
 // clamped to the last item and their results not stored), so the
 // compiler's wait counts stay exact.
-template <int KG>
+template <int KG, int F>
 __global__ void __launch_bounds__(256) gateup_kernel(DecodeArgs a) {
     using S = GateUpShape<KG>;
     constexpr int NI = kGateUpItemsPerRound;
@@ -505,7 +624,7 @@ __global__ void __launch_bounds__(256) gateup_kernel(DecodeArgs a) {
     const int wave = wave_in_block();
     const int wave_id = blockIdx.x * 4 + wave;
     const int n_waves = gridDim.x * 4;
-    const BlobLayout L = blob_layout(a.H, a.I);
+    const BlobLayout L = blob_layout(a.H, a.I, F);
     const int per_slot = a.I / S::R;
     // With the router's kept-slot list (top-p cut) the items cover only the
     // kept slots; the list goes to this wave's LDS row.
@@ -560,11 +679,11 @@ __global__ void __launch_bounds__(256) gateup_kernel(DecodeArgs a) {
     auto blob_of = [&](int slot) { return wave_blobs[wave][slot]; };
     auto issue = [&](int item, GateUpBuf<KG>& buf) {
         const int it = item < n_items ? item : n_items - 1;
-        gateup_issue<KG>(blob_of(slot_of(it)), L, rb_of(it), lane, buf);
+        gateup_issue<KG, F>(blob_of(slot_of(it)), L, rb_of(it), lane, buf);
     };
     auto compute = [&](int item, const GateUpBuf<KG>& buf) {
         const int it = item < n_items ? item : n_items - 1;
-        gateup_compute<KG>(buf, rb_of(it), lane, xa, xs, a.h + (size_t)slot_of(it) * a.I, a.I / 32, item < n_items);
+        gateup_compute<KG, F>(buf, rb_of(it), lane, xa, xs, a.h + (size_t)slot_of(it) * a.I, a.I / 32, item < n_items);
     };
 
     // One to four items for this wave (every wave gets four at 4 x 4096
@@ -650,7 +769,7 @@ __device__ __forceinline__ void load_h(const float* __restrict__ h, int g0, floa
 // steps, the next round issued before the current one is computed
 // (sched_barrier keeps that order); the first R threads combine the block in
 // slot order.  Nine waves of at most 170 registers fit one CU.
-template <int KG, int NLD>
+template <int KG, int NLD, int F>
 __global__ void __launch_bounds__(576) down_combine_kernel(DecodeArgs a) {
     using S = DownShape<KG, NLD>;
     constexpr int MAXW = 9;
@@ -663,7 +782,7 @@ __global__ void __launch_bounds__(576) down_combine_kernel(DecodeArgs a) {
     const int g0 = KG >= kWave ? lane : (lane & (KG - 1));
     const int row_sub = KG >= kWave ? 0 : (lane / KG);
     const int rb = blockIdx.x;
-    const BlobLayout L = blob_layout(a.H, a.I);
+    const BlobLayout L = blob_layout(a.H, a.I, F);
     const uint8_t* blob = slot >= K ? a.shared_blob
                                     : (a.direct ? readlane_ptr(lane_pick(a.blobs, lane), slot) : a.slot_blobs[slot]);
     __shared__ float part[MAXW][S::R];
@@ -690,13 +809,13 @@ __global__ void __launch_bounds__(576) down_combine_kernel(DecodeArgs a) {
 #pragma unroll
         for (int c = 0; c < S::CPL; ++c) {
             const size_t si = ((size_t)rb * KG + g0 + kWave * c) * S::R + (size_t)row_sub * S::NL;
-            load_scales<S::NL>(reinterpret_cast<const uint16_t*>(blob + L.down_s) + si, sc[c]);
+            load_scales_c<F, S::NL>(blob + L.down_s + si * scale_bytes(F), sc[c]);
         }
         if constexpr (NR > 1) issue_round(1);
         __builtin_amdgcn_sched_barrier(0);
         HI8 ha[S::CPL];
         float hscale[S::CPL];
-        to_i8<S::CPL>(hraw, ha, hscale);
+        to_operands<F, S::CPL>(hraw, ha, hscale);
         float v[NVP];
 #pragma unroll
         for (int n = 0; n < NVP; ++n) v[n] = 0.0f;
@@ -708,7 +827,7 @@ __global__ void __launch_bounds__(576) down_combine_kernel(DecodeArgs a) {
                 float acc = 0.0f;
 #pragma unroll
                 for (int c = 0; c < S::CPL; ++c)
-                    acc = fmaf(scale_at(sc[c], n) * hscale[c], dot_chunk_i8(code[n][c], ha[c]), acc);
+                    acc = fmaf(scale_at<F>(sc[c], n) * hscale[c], dot_chunk<F>(code[n][c], ha[c]), acc);
                 v[n] = acc;
             }
             __builtin_amdgcn_sched_barrier(0);
@@ -743,13 +862,18 @@ hipError_t launch_kernel(K kernel, dim3 grid, dim3 block, hipStream_t st, const 
     return hipGetLastError();
 }
 
-template <int KG>
-hipError_t launch_router(const DecodeArgs& a, hipStream_t st, const LaunchTiming& tm) {
+template <int KG, int F>
+hipError_t launch_router_c(const DecodeArgs& a, hipStream_t st, const LaunchTiming& tm) {
     // router blocks, the shared expert's gate/up blocks, one conversion block
     const dim3 grid(router_blocks(a.E) + (a.S > 0 ? shared_gateup_blocks<KG>(a.I) : 0) + 1);
-    if (a.E <= 64) return launch_kernel(router_kernel<KG, 1>, grid, dim3(256), st, tm, a);
-    if (a.E <= 128) return launch_kernel(router_kernel<KG, 2>, grid, dim3(256), st, tm, a);
-    return launch_kernel(router_kernel<KG, 4>, grid, dim3(256), st, tm, a);
+    if (a.E <= 64) return launch_kernel(router_kernel<KG, 1, F>, grid, dim3(256), st, tm, a);
+    if (a.E <= 128) return launch_kernel(router_kernel<KG, 2, F>, grid, dim3(256), st, tm, a);
+    return launch_kernel(router_kernel<KG, 4, F>, grid, dim3(256), st, tm, a);
+}
+template <int KG>
+hipError_t launch_router(const DecodeArgs& a, hipStream_t st, const LaunchTiming& tm) {
+    return a.codec == kCodecMxfp4 ? launch_router_c<KG, kCodecMxfp4>(a, st, tm)
+                                  : launch_router_c<KG, kCodecInt4>(a, st, tm);
 }
 
 template <int KG>
@@ -764,7 +888,9 @@ hipError_t launch_gateup(const DecodeArgs& a, hipStream_t st, const LaunchTiming
     if (waves < 256) waves = items < 256 ? items : 256;
     if (waves > 4096) waves = 4096;
     waves = (waves + 3) / 4 * 4;
-    return launch_kernel(gateup_kernel<KG>, dim3(waves / 4), dim3(256), st, tm, a);
+    if (a.codec == kCodecMxfp4)
+        return launch_kernel(gateup_kernel<KG, kCodecMxfp4>, dim3(waves / 4), dim3(256), st, tm, a);
+    return launch_kernel(gateup_kernel<KG, kCodecInt4>, dim3(waves / 4), dim3(256), st, tm, a);
 }
 
 template <int KG, int NLD>
@@ -772,7 +898,11 @@ hipError_t launch_down_nl(const DecodeArgs& a, hipStream_t st, const LaunchTimin
     using S = DownShape<KG, NLD>;
     if constexpr (ilog2(pow2_at_least(S::NL)) <= S::B && S::NL * S::CPL <= kDownMaxLoads) {
         const int grid = a.H / S::R;
-        return launch_kernel(down_combine_kernel<KG, NLD>, dim3(grid), dim3((a.K + a.S) * 64), st, tm, a);
+        if (a.codec == kCodecMxfp4)
+            return launch_kernel(down_combine_kernel<KG, NLD, kCodecMxfp4>, dim3(grid), dim3((a.K + a.S) * 64), st,
+                                 tm, a);
+        return launch_kernel(down_combine_kernel<KG, NLD, kCodecInt4>, dim3(grid), dim3((a.K + a.S) * 64), st, tm,
+                             a);
     } else {
         return hipErrorInvalidValue;  // never chosen by down_rows
     }

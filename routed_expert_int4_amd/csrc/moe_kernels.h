@@ -31,6 +31,7 @@ struct DecodeArgs {
     int H, I, E, G, TG, K, S;
     float rsf;
     float top_p;                     // adaptive expert top-p (1: plain top-k)
+    int codec;                       // kCodecInt4 or kCodecMxfp4
     // Expert-cache mode: routed slot j reads blobs[j] instead of
     // table[ids[j]] (the host resolved the routing before the launch).
     int direct;

@@ -3,13 +3,13 @@
 //
 // A blob holds, in order:
 //   gate codes [I][H/2], up codes [I][H/2], down codes [H][I/2]
-//       the public row-major bytes with every nibble stored as q + 8
-//       (offset binary), so a kernel can place a nibble straight into the
-//       mantissa of an fp16 constant and subtract the offset exactly;
+//       the public row-major bytes; int4 nibbles are stored as q + 8
+//       (offset binary, the kernels take the offset off with a per-group
+//       correction), MXFP4 (E2M1) nibbles as they are;
 //   gate and up scales (interleaved per block of rows), down scales
-//       (fp16 bits), permuted so that each lane of a wave finds the scales it
-//       needs for one work item in consecutive bytes (see scale_index and
-//       gateup_scale_index).
+//       (fp16 bits for int4, E8M0 bytes for MXFP4), permuted so that each
+//       lane of a wave finds the scales it needs for one work item in
+//       consecutive bytes (see scale_index and gateup_scale_index).
 // The blob is exactly as large as the public layout.
 #pragma once
 
@@ -21,6 +21,10 @@
 namespace moe {
 
 constexpr int kWave = 64;
+// Weight codecs (the moe_config_t codec values).
+constexpr int kCodecInt4 = 0;   // int4 codes, fp16 scale per 32 inputs
+constexpr int kCodecMxfp4 = 1;  // E2M1 codes, E8M0 scale per 32 inputs
+__host__ __device__ constexpr int scale_bytes(int codec) { return codec == kCodecMxfp4 ? 1 : 2; }
 // Rows of gate (and of up) per gate/up work item when a row fits in one
 // wave load or more.
 constexpr int kGateUpRowsBase = 1;
@@ -90,10 +94,10 @@ struct BlobLayout {
     size_t total;
 };
 
-__host__ __device__ inline BlobLayout blob_layout(int hidden, int inter) {
+__host__ __device__ inline BlobLayout blob_layout(int hidden, int inter, int codec) {
     BlobLayout L;
     const size_t codes = (size_t)hidden * inter / 2;
-    const size_t scales = (size_t)hidden * (inter / 32) * 2;
+    const size_t scales = (size_t)hidden * (inter / 32) * scale_bytes(codec);
     L.gate_q = 0;
     L.up_q = codes;
     L.down_q = 2 * codes;

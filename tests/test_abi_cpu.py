@@ -81,6 +81,38 @@ def test_pack_keeps_codes_and_permutes_scales():
     np.testing.assert_array_equal(np.sort(sc[2 * m:]), np.sort(ds.ravel()))
 
 
+def test_pack_mxfp4_keeps_codes_and_permutes_e8m0_scales():
+    import dataclasses
+    cfg = dataclasses.replace(synth.TINY, codec="mxfp4")
+    w = synth.gen_layer(cfg, seed=0)
+    nb = B.moe_expert_bytes(cfg)
+    assert nb == cfg.expert_bytes() == 3 * cfg.hidden * cfg.inter // 2 + 3 * cfg.hidden * cfg.inter // 32
+    assert B.moe_expert_bytes(dataclasses.replace(synth.GLM, codec="mxfp4")) == 20_054_016  # 19.125 MiB
+    blob = np.empty(nb, np.uint8)
+    B.moe_expert_pack(cfg, *w.expert_arrays(5), blob)
+    n = cfg.hidden * cfg.inter // 2
+    gq, gs, uq, us, dq, ds = w.expert_arrays(5)
+    # E2M1 codes are kept as they are
+    np.testing.assert_array_equal(blob[:n], gq.ravel())
+    np.testing.assert_array_equal(blob[n:2 * n], uq.ravel())
+    np.testing.assert_array_equal(blob[2 * n:3 * n], dq.ravel())
+    sc = blob[3 * n:]
+    m = sc.size // 3
+    np.testing.assert_array_equal(np.sort(sc[:2 * m]), np.sort(np.concatenate([gs.ravel(), us.ravel()])))
+    np.testing.assert_array_equal(np.sort(sc[2 * m:]), np.sort(ds.ravel()))
+    # the NaN scale byte is refused
+    bad = ds.copy()
+    bad[0, 0] = 255
+    with pytest.raises(B.MoeError) as e:
+        B.moe_expert_pack(cfg, gq, gs, uq, us, dq, bad, blob)
+    assert e.value.code == B.MOE_EINVAL
+    # an unknown codec value is an invalid config
+    import ctypes
+    c = B.MoeConfig.from_cfg(cfg)
+    c.codec = 7
+    assert B.lib().moe_expert_bytes(ctypes.byref(c)) == 0
+
+
 def test_pack_rejects_null():
     code = B.lib().moe_expert_pack(B.MoeConfig.from_cfg(synth.TINY), None, None, None, None, None, None, None)
     assert code == B.MOE_EINVAL

@@ -236,3 +236,32 @@ def test_cache_top_p(torch_cuda):
     for lay in cached + resident:
         lay.close()
     cache.close()
+
+
+def test_cache_mxfp4(torch_cuda):
+    """MXFP4 experts behind the cache: outputs equal the resident MXFP4
+    layer's one-token calls bit for bit, and the oracle's within tolerance;
+    copies move MXFP4 blobs (h2d_bytes = misses x MXFP4 blob bytes)."""
+    import dataclasses
+    torch = torch_cuda
+    from routed_expert_int4_amd.layer import DeviceLayer
+    cfg = dataclasses.replace(CFG, codec="mxfp4")
+    slots = CFG.top_k
+    say(f"[gpu] mxfp4 cache, {slots} slots")
+    cache, weights, cached, resident = make_stack(torch, slots, n_layers=1, cfg=cfg)
+    assert cache.nb == cfg.expert_bytes()
+    x_bits = synth.gen_tokens(cfg, N_TOKENS, seed=70)
+    x = DeviceLayer.to_device_bf16(x_bits)
+    y, ids, w = cached[0].forward(x)
+    y_res, ids_res, w_res = resident[0].forward_each(x)
+    torch.cuda.synchronize()
+    assert torch.equal(ids, ids_res) and torch.equal(w, w_res) and torch.equal(y, y_res)
+    idh = ids.cpu().numpy()
+    res = check_layer(weights[0], x_bits, y.cpu().numpy(), idh, w.cpu().numpy())
+    st = cache.stats(0)
+    assert (st["hits"], st["misses"], st["evictions"]) == lru.replay(idh, slots)
+    assert st["h2d_bytes"] == st["misses"] * cache.nb
+    say(f"[gpu] mxfp4 cache: rel err {res['worst_rel']:.3g}, stats {st}")
+    for lay in cached + resident:
+        lay.close()
+    cache.close()

@@ -283,3 +283,86 @@ def test_glm_top_p_decode(torch_cuda, glm):
     res = check_layer(wp, x, y, ids, w, rows=rows)
     say(f"[gpu] GLM top-p sampled outputs: worst rel err {res['worst_rel']:.3g}")
     layer.close()
+
+
+# ---------------------------------------------------------------- MXFP4 codec
+def with_codec(cfg, codec="mxfp4"):
+    return dataclasses.replace(cfg, codec=codec)
+
+
+@pytest.mark.parametrize("cfg_name", ["TINY", "MID_A", "MID_B", "MID_C", "MID_D"])
+def test_mxfp4_layer_parity(torch_cuda, cfg_name):
+    """One-token calls of MXFP4 layers against the oracle (E2M1 codes, E8M0
+    scales), every lane mapping of the kernels."""
+    cfg = with_codec({"TINY": synth.TINY, "MID_A": MID_A, "MID_B": MID_B, "MID_C": MID_C, "MID_D": MID_D}[cfg_name])
+    say(f"[gpu] mxfp4 layer parity {cfg_name}")
+    weights = synth.gen_layer(cfg, seed=0)
+    T = 4 if cfg.hidden * cfg.inter > 2 ** 24 else 13
+    x = synth.gen_tokens(cfg, T, seed=1)
+    layer, y, ids, w = run_layer(torch_cuda, weights, x)
+    res = check_layer(weights, x, y, ids, w)
+    say(f"[gpu] mxfp4 {cfg_name}: worst rel err {res['worst_rel']:.3g}, excused {res['excused']}")
+    layer.close()
+
+
+def test_mxfp4_extreme_scales_and_activations(torch_cuda):
+    """E8M0 bytes far from the generator's range (2^-40 .. 2^-20 and 2^+10 ..
+    2^+20 per group) with activations of std 1e-3 and 300: the fp16
+    activation pairs and the scale decoding keep the outputs within
+    tolerance."""
+    cfg = with_codec(MID_A)
+    say("[gpu] mxfp4 extreme scales")
+    base = synth.gen_layer(cfg, seed=2)
+    rng = np.random.default_rng(7)
+    for lo, hi in ((127 - 40, 127 - 20), (127 + 10, 127 + 20)):
+        arrs = {n: rng.integers(lo, hi, size=getattr(base, n).shape).astype(np.uint8)
+                for n in ("gate_s", "up_s", "down_s")}
+        weights = dataclasses.replace(base, **arrs)
+        for std in (1e-3, 300.0):
+            x = synth.gen_tokens(cfg, 3, seed=8, std=std)
+            layer, y, ids, w = run_layer(torch_cuda, weights, x)
+            res = check_layer(weights, x, y, ids, w)
+            say(f"[gpu] mxfp4 scales [{lo}, {hi}) std {std}: worst rel err {res['worst_rel']:.3g}")
+            layer.close()
+
+
+def test_mxfp4_batched_call_unsupported(torch_cuda):
+    from routed_expert_int4_amd.layer import DeviceLayer
+    weights = synth.gen_layer(with_codec(synth.TINY), seed=0)
+    layer = DeviceLayer(weights, max_T=4)
+    x = DeviceLayer.to_device_bf16(synth.gen_tokens(synth.TINY, 4, seed=1))
+    with pytest.raises(B.MoeError) as ei:
+        layer.forward(x)
+    assert ei.value.code == B.MOE_EUNSUPPORTED
+    layer.forward(x[:1])
+    torch_cuda.cuda.synchronize()
+    layer.close()
+
+
+def test_glm_mxfp4_decode(torch_cuda):
+    """GLM-shaped MXFP4 layer (19.125 MiB per expert), 300 one-token calls:
+    routing of every token against the oracle, outputs on a sample; then the
+    same layer with top_p 0.7."""
+    cfg = with_codec(synth.GLM)
+    say("[gpu] generating the GLM-shaped MXFP4 layer (seed 0)")
+    weights = synth.gen_layer(cfg, seed=0)
+    from routed_expert_int4_amd.layer import DeviceLayer
+    assert B.moe_expert_bytes(cfg) == 20_054_016
+    layer = DeviceLayer(weights, max_T=1)
+    x = synth.gen_tokens(cfg, 300, seed=1)
+    y, ids, w = layer.forward_each(DeviceLayer.to_device_bf16(x))
+    torch_cuda.cuda.synchronize()
+    y, ids, w = y.cpu().numpy(), ids.cpu().numpy(), w.cpu().numpy()
+    ids_ref, w_ref, gap = oracle.route(weights, x)
+    excused = check_routing(cfg, ids, w, ids_ref, w_ref, gap)
+    rows = sorted(set([0, 1, 150, 299] + list(np.argsort(gap)[:2])))
+    res = check_layer(weights, x, y, ids, w, rows=rows)
+    say(f"[gpu] GLM mxfp4: {len(excused)} excused, sampled worst rel err {res['worst_rel']:.3g}")
+    layer.close()
+    wp = with_top_p(weights, 0.7)
+    layer = DeviceLayer(wp, max_T=1)
+    y, ids, w = layer.forward_each(DeviceLayer.to_device_bf16(x[:40]))
+    torch_cuda.cuda.synchronize()
+    res = check_layer(wp, x[:40], y.cpu().numpy(), ids.cpu().numpy(), w.cpu().numpy(), rows=[0, 7, 39])
+    say(f"[gpu] GLM mxfp4 top-p 0.7: worst rel err {res['worst_rel']:.3g}")
+    layer.close()

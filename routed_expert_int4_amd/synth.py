@@ -19,6 +19,8 @@ Public layout of one layer (row-major, little-endian):
 
 With ``codec="mxfp4"`` the codes are MXFP4 elements (E2M1 nibbles, same
 packing) and every scale array is uint8 E8M0 bytes (one per 32 inputs).
+With ``codec="int8"`` every code is one two's complement byte (code arrays
+``[I, H]`` and ``[H, I]``) with the same fp16 scales.
 
 Value distributions follow the GLM-5.2-shaped layer described on the pages
 (routed experts 256, top-8, ~19 MB of int4 codes per expert): codes are uniform
@@ -27,7 +29,9 @@ scales are exp(N(-4, 0.5)) rounded to fp16, the router weight is N(0, 0.02) in
 fp32, the bias N(0, 0.01) in fp32 and the activations N(0, 1) rounded to bf16.
 MXFP4 layers draw their codes the same way (uniform bytes: every E2M1 code
 equally likely, rms element 2.93) and E8M0 scale bytes 127 + round(N(-5, 0.75))
-(about 2^-5, so the weights have the int4 layer's magnitude).
+(about 2^-5, so the weights have the int4 layer's magnitude).  Int8 layers
+draw uniform code bytes and scales exp(N(-6.77, 0.5)) (the int4 scale times
+4.64 / 73.9, the ratio of the codes' rms values).
 Streams: SeedSequence(seed).spawn(1 + E + S); the first child draws the
 router weight then the bias; child 1 + e draws expert e (routed experts
 first, shared last) in the order gate codes, gate scales, up codes, up
@@ -51,7 +55,7 @@ class LayerConfig:
     n_shared: int = 1
     routed_scaling_factor: float = 2.5
     top_p: float = 1.0  # adaptive expert top-p over the selected experts (1: plain top-k)
-    codec: str = "int4"  # "int4" (fp16 scales) or "mxfp4" (E2M1 codes, E8M0 scales)
+    codec: str = "int4"  # "int4", "int8" (fp16 scales) or "mxfp4" (E2M1 codes, E8M0 scales)
 
     @property
     def n_total_experts(self) -> int:
@@ -61,10 +65,14 @@ class LayerConfig:
     def scale_bytes(self) -> int:
         return 1 if self.codec == "mxfp4" else 2
 
+    @property
+    def codes_per_byte(self) -> int:
+        return 1 if self.codec == "int8" else 2
+
     def expert_bytes(self) -> int:
         """Bytes of one expert in the public layout (codes + scales)."""
         h, i = self.hidden, self.inter
-        return 3 * (h * i // 2) + 3 * (h * i // 32) * self.scale_bytes
+        return 3 * (h * i // self.codes_per_byte) + 3 * (h * i // 32) * self.scale_bytes
 
 
 # Tiny layer: hidden 256, intermediate 128, 16 experts in 4 groups, top-4 of 2 groups.
@@ -115,6 +123,12 @@ def _scales(rng: np.random.Generator, shape) -> np.ndarray:
     return np.exp(z * np.float32(0.5) - np.float32(4.0)).astype(np.float16).view(np.uint16)
 
 
+def _int8_scales(rng: np.random.Generator, shape) -> np.ndarray:
+    """exp(N(-6.77, 0.5)) rounded to fp16 (bits)."""
+    z = rng.standard_normal(size=shape, dtype=np.float32)
+    return np.exp(z * np.float32(0.5) - np.float32(6.77)).astype(np.float16).view(np.uint16)
+
+
 def _e8m0_scales(rng: np.random.Generator, shape) -> np.ndarray:
     """E8M0 bytes 127 + round(N(-5, 0.75))."""
     z = rng.standard_normal(size=shape, dtype=np.float32)
@@ -140,12 +154,14 @@ def gen_layer(cfg: LayerConfig, seed: int, workers: int | None = None) -> LayerW
     h, i, e_all = cfg.hidden, cfg.inter, cfg.n_total_experts
     children = np.random.SeedSequence(seed).spawn(1 + e_all)
     router_w, bias = gen_router(cfg, seed)
-    sdt, scales = (np.uint8, _e8m0_scales) if cfg.codec == "mxfp4" else (np.uint16, _scales)
-    gq = np.empty((e_all, i, h // 2), np.uint8)
+    sdt, scales = {"mxfp4": (np.uint8, _e8m0_scales), "int8": (np.uint16, _int8_scales)}.get(
+        cfg.codec, (np.uint16, _scales))
+    cpb = cfg.codes_per_byte
+    gq = np.empty((e_all, i, h // cpb), np.uint8)
     gs = np.empty((e_all, i, h // 32), sdt)
     uq = np.empty_like(gq)
     us = np.empty_like(gs)
-    dq = np.empty((e_all, h, i // 2), np.uint8)
+    dq = np.empty((e_all, h, i // cpb), np.uint8)
     ds = np.empty((e_all, h, i // 32), sdt)
 
     def draw(e):

@@ -551,3 +551,56 @@ def test_mxfp4_generator_dtypes_and_scale_range():
     assert 110 <= int(w.gate_s.min()) and int(w.gate_s.max()) <= 135
     out = oracle.layer_forward(w, synth.gen_tokens(synth.TINY, 3, seed=1))
     assert np.all(np.isfinite(out["y"]))
+
+
+# ----------------------------------------------------------------- int8 codec
+def test_int8_unit_vectors_and_extreme_codes():
+    """x = e_c returns column c of W = scale * q for int8 codes, including
+    -128 and 127, and the scale group each column falls in."""
+    rng = np.random.default_rng(31)
+    rows, cols = 8, 96
+    q = rng.integers(-128, 128, size=(rows, cols))
+    q[0, :] = -128
+    q[1, :] = 127
+    s = f16_bits(np.exp(rng.normal(-3, 0.5, size=(rows, cols // 32))))
+    sc = s.view(np.float16).astype(np.float64)
+    for c in (0, 1, 31, 32, 63, 64, 95):
+        x = np.zeros(cols)
+        x[c] = 1.0
+        y = oracle.matvec(q.astype(np.int8).view(np.uint8), s, x, codec="int8")
+        np.testing.assert_array_equal(y, q[:, c] * sc[:, c // 32])
+    x = rng.normal(size=cols)
+    np.testing.assert_allclose(oracle.matvec(q.astype(np.int8).view(np.uint8), s, x, codec="int8"),
+                               (q * np.repeat(sc, 32, axis=1)) @ x, rtol=1e-13)
+
+
+def test_int8_layer_equals_int4_layer_on_shared_codes():
+    """An int8 layer whose codes lie in [-8, 7] is the int4 layer with the
+    same codes and scales: bit-identical routing and outputs."""
+    import dataclasses
+    base = synth.gen_layer(synth.TINY, seed=4)
+    rng = np.random.default_rng(9)
+    i4, i8 = {}, {}
+    for name in ("gate", "up", "down"):
+        qs = getattr(base, name + "_q")
+        q = rng.integers(-8, 8, size=(qs.shape[0], qs.shape[1], qs.shape[2] * 2))
+        i4[name + "_q"] = np.stack([pack_int4(m) for m in q])
+        i8[name + "_q"] = q.astype(np.int8).view(np.uint8)
+    w4 = dataclasses.replace(base, **i4)
+    w8 = dataclasses.replace(base, cfg=dataclasses.replace(base.cfg, codec="int8"), **i8)
+    x = synth.gen_tokens(synth.TINY, 5, seed=10)
+    a, b = oracle.layer_forward(w4, x), oracle.layer_forward(w8, x)
+    np.testing.assert_array_equal(a["ids"], b["ids"])
+    np.testing.assert_array_equal(a["y"], b["y"])
+    assert np.abs(a["y"]).max() > 0
+
+
+def test_int8_generator_layout():
+    import dataclasses
+    cfg = dataclasses.replace(synth.TINY, codec="int8")
+    w = synth.gen_layer(cfg, seed=0)
+    assert w.gate_q.shape == (cfg.n_total_experts, cfg.inter, cfg.hidden)
+    assert w.down_q.shape == (cfg.n_total_experts, cfg.hidden, cfg.inter)
+    assert cfg.expert_bytes() == 3 * cfg.hidden * cfg.inter + 3 * cfg.hidden * cfg.inter // 16
+    y = oracle.layer_forward(w, synth.gen_tokens(cfg, 2, seed=1))["y"]
+    assert np.all(np.isfinite(y)) and 0.05 < np.abs(y).max() < 1e3

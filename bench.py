@@ -39,6 +39,8 @@ KERNEL_SOURCES = [os.path.join(ROOT, "routed_expert_int4_amd", "csrc", f)
 DTYPES = {
     "int4": "int4 weights x int16 fixed-point activations (two int8 parts), int32 dot, fp32 accumulate",
     "mxfp4": "MXFP4 weights (E2M1, E8M0 scales) x fp16 activation pairs, fp32 dot2 accumulate",
+    "int8": "int8 weights (two nibble planes) x int16 fixed-point activations (two int8 parts), int32 dot, "
+            "fp32 accumulate",
 }
 
 
@@ -54,9 +56,10 @@ def algorithmic_bytes(cfg):
     """
     eb = cfg.expert_bytes()
     n = cfg.top_k + cfg.n_shared
-    sb = cfg.scale_bytes  # 2 (int4, fp16 scales) or 1 (MXFP4, E8M0 scales)
-    gu = 2 * (cfg.hidden * cfg.inter // 2 + cfg.inter * (cfg.hidden // 32) * sb)  # gate + up, codes + scales
-    dn = cfg.hidden * cfg.inter // 2 + cfg.hidden * (cfg.inter // 32) * sb
+    sb = cfg.scale_bytes  # 2 (int4, int8: fp16 scales) or 1 (MXFP4, E8M0 scales)
+    cb = cfg.hidden * cfg.inter // cfg.codes_per_byte  # code bytes of one matrix
+    gu = 2 * (cb + cfg.inter * (cfg.hidden // 32) * sb)  # gate + up, codes + scales
+    dn = cb + cfg.hidden * (cfg.inter // 32) * sb
     router = cfg.n_experts * cfg.hidden * 4 + cfg.n_experts * 4
     io = cfg.hidden * 2 + cfg.hidden * 4
     return {
@@ -135,8 +138,9 @@ def main() -> int:
     ap.add_argument("--pin", type=int, default=-1,
                     help="cache-stack: experts pinned per layer by learned usage (-1: slots - top_k, 0: plain LRU)")
     ap.add_argument("--learn-tokens", type=int, default=128, help="cache-stack: tokens of the learning pass")
-    ap.add_argument("--codec", default="int4", choices=["int4", "mxfp4"],
-                    help="decode and cache-stack: expert weight codec (mxfp4: E2M1 codes, E8M0 scales)")
+    ap.add_argument("--codec", default="int4", choices=["int4", "mxfp4", "int8"],
+                    help="decode and cache-stack: expert weight codec (mxfp4: E2M1 codes, E8M0 scales; int8: one "
+                         "byte per weight, fp16 scales)")
     ap.add_argument("--top-p", type=float, default=1.0,
                     help="decode and cache-stack: adaptive expert top-p (1: plain top-k); decode prices its bytes "
                          "by the experts kept")

@@ -51,7 +51,8 @@ moe_status_t validate_config(const moe_config_t* c) {
     if (!(c->routed_scaling_factor == c->routed_scaling_factor))
         return fail(MOE_EINVAL, "routed_scaling_factor is NaN");
     if (!(c->top_p > 0.0f && c->top_p <= 1.0f)) return fail(MOE_EINVAL, "top_p must be in (0, 1]");
-    if (c->codec != kCodecInt4 && c->codec != kCodecMxfp4) return fail(MOE_EINVAL, "unknown codec %d", c->codec);
+    if (c->codec != kCodecInt4 && c->codec != kCodecMxfp4 && c->codec != kCodecInt8)
+        return fail(MOE_EINVAL, "unknown codec %d", c->codec);
     return MOE_OK;
 }
 
@@ -133,8 +134,8 @@ WorkspaceLayout workspace_layout(const moe_config_t* c, int max_T) {
 // Scale arrays of one expert, permuted into the per-lane packs the kernels
 // read (T = uint16_t fp16 bits or uint8_t E8M0 bytes).
 template <typename T>
-void pack_scale_arrays(uint8_t* dst, const BlobLayout& L, int H, int I, const T* gate_s, const T* up_s,
-                              const T* down_s) {
+void pack_scale_arrays(uint8_t* dst, const BlobLayout& L, int H, int I, int planes, const T* gate_s, const T* up_s,
+                       const T* down_s) {
     const int kh = H / 32, ki = I / 32;
     T* gu = reinterpret_cast<T*>(dst + L.gu_s);
     const int p = gateup_rows(kh);
@@ -144,7 +145,7 @@ void pack_scale_arrays(uint8_t* dst, const BlobLayout& L, int H, int I, const T*
             gu[gateup_scale_index(r, g, 1, kh, p)] = up_s[(size_t)r * kh + g];
         }
     T* dn = reinterpret_cast<T*>(dst + L.down_s);
-    const int pd = down_rows(H, ki);
+    const int pd = down_rows(H, ki, planes);
     for (int r = 0; r < H; ++r)
         for (int g = 0; g < ki; ++g) dn[scale_index(r, g, ki, pd)] = down_s[(size_t)r * ki + g];
 }
@@ -174,7 +175,7 @@ moe_status_t moe_expert_pack(const moe_config_t* cfg, const uint8_t* gate_q, con
     uint8_t* dst = static_cast<uint8_t*>(dst_blob);
     const size_t codes = (size_t)H * I / 2;
     const int kh = H / 32, ki = I / 32;
-    if (I % gateup_rows(kh) || H % down_rows(H, ki))
+    if (I % gateup_rows(kh) || H % down_rows(H, ki, code_planes(cfg->codec)))
         return fail(MOE_EUNSUPPORTED, "moe_expert_pack: rows not a multiple of the scale pack");
     const uint8_t* src_q[3] = {gate_q, up_q, down_q};
     const size_t dst_q[3] = {L.gate_q, L.up_q, L.down_q};
@@ -188,12 +189,24 @@ moe_status_t moe_expert_pack(const moe_config_t* cfg, const uint8_t* gate_q, con
                 if (src_s[m][i] == 255) return fail(MOE_EINVAL, "moe_expert_pack: E8M0 scale 255 (NaN)");
         // codes: E2M1 nibbles as they are
         for (int m = 0; m < 3; ++m) std::memcpy(dst + dst_q[m], src_q[m], codes);
-        pack_scale_arrays(dst, L, H, I, src_s[0], src_s[1], src_s[2]);
+        pack_scale_arrays(dst, L, H, I, 1, src_s[0], src_s[1], src_s[2]);
+    } else if (cfg->codec == kCodecInt8) {
+        // q = 16 hi + lo: high nibbles (signed, stored + 8) in the int4
+        // planes, low nibbles (unsigned) in the low planes
+        const size_t dst_lo[3] = {L.gate_lo, L.up_lo, L.down_lo};
+        for (int m = 0; m < 3; ++m)
+            for (size_t i = 0; i < codes; ++i) {
+                const uint8_t a = src_q[m][2 * i], b = src_q[m][2 * i + 1];
+                dst[dst_q[m] + i] = (uint8_t)((((a >> 4) ^ 8u) & 15u) | ((((b >> 4) ^ 8u) & 15u) << 4));
+                dst[dst_lo[m] + i] = (uint8_t)((a & 15u) | ((b & 15u) << 4));
+            }
+        pack_scale_arrays(dst, L, H, I, 2, static_cast<const uint16_t*>(gate_s), static_cast<const uint16_t*>(up_s),
+                          static_cast<const uint16_t*>(down_s));
     } else {
         // codes: stored as q + 8 (flip bit 3 of every two's complement nibble)
         for (int m = 0; m < 3; ++m)
             for (size_t i = 0; i < codes; ++i) dst[dst_q[m] + i] = src_q[m][i] ^ 0x88u;
-        pack_scale_arrays(dst, L, H, I, static_cast<const uint16_t*>(gate_s), static_cast<const uint16_t*>(up_s),
+        pack_scale_arrays(dst, L, H, I, 1, static_cast<const uint16_t*>(gate_s), static_cast<const uint16_t*>(up_s),
                           static_cast<const uint16_t*>(down_s));
     }
     return MOE_OK;
@@ -421,7 +434,7 @@ BatchArgs batch_args(moe_layer_t* L, const uint16_t* x, int n, int32_t* ids, flo
     b.TG = c.topk_group;
     b.K = c.top_k;
     b.S = c.n_shared;
-    b.down_p = down_rows(c.hidden, c.inter / 32);
+    b.down_p = down_rows(c.hidden, c.inter / 32, 1);
     b.router_splits = batch_router_splits(c.hidden);
     b.rsf = c.routed_scaling_factor;
     return b;
@@ -482,7 +495,8 @@ moe_status_t moe_layer_forward(moe_layer_t* layer, const uint16_t* d_x, int T, f
     float* w_base = d_w ? d_w : reinterpret_cast<float*>(layer->ws + layer->W.w);
     if (T > 1 && !layer->cache) {
         if (c.top_p < 1.0f) return fail(MOE_EUNSUPPORTED, "moe_layer_forward: top_p < 1 needs T = 1 calls");
-        if (c.codec != kCodecInt4) return fail(MOE_EUNSUPPORTED, "moe_layer_forward: MXFP4 experts need T = 1 calls");
+        if (c.codec != kCodecInt4)
+            return fail(MOE_EUNSUPPORTED, "moe_layer_forward: MXFP4 and int8 experts need T = 1 calls");
         // batch union: every distinct expert of a launch sequence is read once
         const int tb = layer->W.batch_tokens;
         for (int t0 = 0; t0 < T; t0 += tb) {

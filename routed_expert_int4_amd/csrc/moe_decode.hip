@@ -158,6 +158,30 @@ __device__ __forceinline__ float dot_chunk_fp4(u32x4 c, const HI8& a) {
     return acc0 + acc1;
 }
 
+// Int8 codes split into two nibble planes, q = 16 hi + lo (hi stored + 8,
+// lo unsigned): both planes take the int4 dot with the same HI8 operands,
+// 16 sum(q a) = 16 (sum((hi + 8) a) - corr) + sum(lo a), exact in int32
+// (|value| < 2^28; the conversion to fp32 rounds once).
+__device__ __forceinline__ float dot_chunk_int8(u32x4 chi, u32x4 clo, const HI8& a) {
+    int h1 = 0, l1 = 0, h2 = 0, l2 = 0;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        const unsigned he = a.he[d], ho = a.ho[d], le = a.le[d], lo_ = a.lo[d];
+        const unsigned w = chi[d], v = clo[d];
+        const int e = (int)(w & 0x0F0F0F0Fu), o = (int)((w >> 4) & 0x0F0F0F0Fu);
+        const int e2 = (int)(v & 0x0F0F0F0Fu), o2 = (int)((v >> 4) & 0x0F0F0F0Fu);
+        h1 = __builtin_amdgcn_sdot4(e, (int)he, h1, false);
+        h1 = __builtin_amdgcn_sdot4(o, (int)ho, h1, false);
+        l1 = (int)__builtin_amdgcn_udot4((unsigned)e, le, (unsigned)l1, false);
+        l1 = (int)__builtin_amdgcn_udot4((unsigned)o, lo_, (unsigned)l1, false);
+        h2 = __builtin_amdgcn_sdot4(e2, (int)he, h2, false);
+        h2 = __builtin_amdgcn_sdot4(o2, (int)ho, h2, false);
+        l2 = (int)__builtin_amdgcn_udot4((unsigned)e2, le, (unsigned)l2, false);
+        l2 = (int)__builtin_amdgcn_udot4((unsigned)o2, lo_, (unsigned)l2, false);
+    }
+    return (float)(16 * (h1 * 256 + l1 - a.corr) + h2 * 256 + l2);
+}
+
 // Codec dispatch of the operand form and the chunk dot.
 template <int F, int CPL>
 __device__ __forceinline__ void to_operands(const float (&hin)[CPL][32], HI8 (&ha)[CPL], float (&hscale)[CPL]) {
@@ -172,6 +196,14 @@ __device__ __forceinline__ float dot_chunk(u32x4 c, const HI8& a) {
         return dot_chunk_fp4(c, a);
     else
         return dot_chunk_i8(c, a);
+}
+// Chunk dot over the codec's planes: c[0] (and c[1] for int8).
+template <int F, int P>
+__device__ __forceinline__ float dot_planes(const u32x4 (&c)[P], const HI8& a) {
+    if constexpr (F == kCodecInt8)
+        return dot_chunk_int8(c[0], c[1], a);
+    else
+        return dot_chunk<F>(c[0], a);
 }
 
 // ---------------------------------------------------------------- gate/up
@@ -341,17 +373,18 @@ __device__ __forceinline__ void load_activations(const unsigned* __restrict__ xq
     }
 }
 
-template <int KG>
+template <int KG, int P>
 struct GateUpBuf {
     using S = GateUpShape<KG>;
-    u32x4 cg[S::NL][S::CPL], cu[S::NL][S::CPL];
+    u32x4 cg[S::NL][S::CPL][P], cu[S::NL][S::CPL][P];  // P code planes (int8: 2)
     unsigned sgu[S::CPL][S::NL];  // halves 0..NL-1 gate, NL..2NL-1 up
 };
 
 template <int KG, int F>
 __device__ __forceinline__ void gateup_issue(const uint8_t* __restrict__ blob, const BlobLayout& L, int rb, int lane,
-                                             GateUpBuf<KG>& b) {
+                                             GateUpBuf<KG, code_planes(F)>& b) {
     using S = GateUpShape<KG>;
+    constexpr int P = code_planes(F);
     const int g0 = KG >= kWave ? lane : (lane & (KG - 1));
     const int row_sub = KG >= kWave ? 0 : (lane / KG);
 #pragma unroll
@@ -360,8 +393,11 @@ __device__ __forceinline__ void gateup_issue(const uint8_t* __restrict__ blob, c
 #pragma unroll
         for (int c = 0; c < S::CPL; ++c) {
             const size_t off = (row * KG + g0 + kWave * c) * 16;
-            b.cg[n][c] = load_stream16(blob + L.gate_q + off);
-            b.cu[n][c] = load_stream16(blob + L.up_q + off);
+#pragma unroll
+            for (int p = 0; p < P; ++p) {
+                b.cg[n][c][p] = load_stream16(blob + (p ? L.gate_lo : L.gate_q) + off);
+                b.cu[n][c][p] = load_stream16(blob + (p ? L.up_lo : L.up_q) + off);
+            }
         }
     }
 #pragma unroll
@@ -397,7 +433,7 @@ __device__ __forceinline__ size_t h_index(int i, int kgi) {
 // Computes one item from its loaded buffer: h = silu(g) * u for rows
 // [rb*R, rb*R + R), written as fp32 at their h_index positions.
 template <int KG, int F>
-__device__ __forceinline__ void gateup_compute(const GateUpBuf<KG>& b, int rb, int lane,
+__device__ __forceinline__ void gateup_compute(const GateUpBuf<KG, code_planes(F)>& b, int rb, int lane,
                                                const HI8 (&xa)[GateUpShape<KG>::CPL],
                                                const float (&xs)[GateUpShape<KG>::CPL], float* __restrict__ h_out,
                                                int kgi, bool store) {
@@ -409,8 +445,8 @@ __device__ __forceinline__ void gateup_compute(const GateUpBuf<KG>& b, int rb, i
         float ag = 0.0f, au = 0.0f;
 #pragma unroll
         for (int c = 0; c < S::CPL; ++c) {
-            ag = fmaf(scale_at<F>(b.sgu[c], n) * xs[c], dot_chunk<F>(b.cg[n][c], xa[c]), ag);
-            au = fmaf(scale_at<F>(b.sgu[c], S::NL + n) * xs[c], dot_chunk<F>(b.cu[n][c], xa[c]), au);
+            ag = fmaf(scale_at<F>(b.sgu[c], n) * xs[c], dot_planes<F>(b.cg[n][c], xa[c]), ag);
+            au = fmaf(scale_at<F>(b.sgu[c], S::NL + n) * xs[c], dot_planes<F>(b.cu[n][c], xa[c]), au);
         }
         v[n] = ag;
         v[S::NL + n] = au;
@@ -486,7 +522,8 @@ __host__ __device__ inline int shared_gateup_blocks(int I) {
 template <int KG, int EPL, int F>
 __global__ void __launch_bounds__(256) router_kernel(DecodeArgs a) {
     using S = GateUpShape<KG>;
-    constexpr int NI = kSharedItemsPerRound;
+    // items per round of the shared expert's waves (two planes: two items)
+    constexpr int NI = code_planes(F) > 1 ? 2 : kSharedItemsPerRound;
     const int lane = threadIdx.x & 63;
     const int wave = wave_in_block();
     const int n_shared_blocks = a.S > 0 ? shared_gateup_blocks<KG>(a.I) : 0;
@@ -508,7 +545,7 @@ __global__ void __launch_bounds__(256) router_kernel(DecodeArgs a) {
         const int n_waves = n_shared_blocks * 4;
         if (wave_id >= per_slot) return;
         const BlobLayout L = blob_layout(a.H, a.I, F);
-        GateUpBuf<KG> buf[NI];
+        GateUpBuf<KG, code_planes(F)> buf[NI];
 #pragma unroll
         for (int k = 0; k < NI; ++k) {
             const int it = wave_id + k * n_waves;
@@ -660,7 +697,7 @@ __global__ void __launch_bounds__(256) gateup_kernel(DecodeArgs a) {
         asm volatile("" : "+v"(xa[c].he), "+v"(xa[c].ho), "+v"(xa[c].le), "+v"(xa[c].lo));
         asm volatile("" : "+v"(xa[c].corr), "+v"(xs[c]));
     }
-    GateUpBuf<KG> b[NI];
+    GateUpBuf<KG, code_planes(F)> b[NI];
 
     // item -> (slot, row block)
     auto slot_of = [&](int item) {
@@ -677,11 +714,11 @@ __global__ void __launch_bounds__(256) gateup_kernel(DecodeArgs a) {
     };
     auto rb_of = [&](int item) { return item % per_slot; };
     auto blob_of = [&](int slot) { return wave_blobs[wave][slot]; };
-    auto issue = [&](int item, GateUpBuf<KG>& buf) {
+    auto issue = [&](int item, GateUpBuf<KG, code_planes(F)>& buf) {
         const int it = item < n_items ? item : n_items - 1;
         gateup_issue<KG, F>(blob_of(slot_of(it)), L, rb_of(it), lane, buf);
     };
-    auto compute = [&](int item, const GateUpBuf<KG>& buf) {
+    auto compute = [&](int item, const GateUpBuf<KG, code_planes(F)>& buf) {
         const int it = item < n_items ? item : n_items - 1;
         gateup_compute<KG, F>(buf, rb_of(it), lane, xa, xs, a.h + (size_t)slot_of(it) * a.I, a.I / 32, item < n_items);
     };
@@ -796,12 +833,16 @@ __global__ void __launch_bounds__(576) down_combine_kernel(DecodeArgs a) {
         };
         float hraw[S::CPL][32];
         load_h<S::CPL, KG>(a.h + (size_t)slot * a.I, g0, hraw);
-        u32x4 code[S::NL][S::CPL];
+        constexpr int P = code_planes(F);
+        u32x4 code[S::NL][S::CPL][P];
         auto issue_round = [&](int r) {
 #pragma unroll
             for (int n = r * WIN; n < (r + 1) * WIN && n < S::NL; ++n)
 #pragma unroll
-                for (int c = 0; c < S::CPL; ++c) code[n][c] = load_stream16(blob + L.down_q + code_off(n, c));
+                for (int c = 0; c < S::CPL; ++c)
+#pragma unroll
+                    for (int p = 0; p < P; ++p)
+                        code[n][c][p] = load_stream16(blob + (p ? L.down_lo : L.down_q) + code_off(n, c));
         };
         __builtin_amdgcn_sched_barrier(0);
         issue_round(0);
@@ -827,7 +868,7 @@ __global__ void __launch_bounds__(576) down_combine_kernel(DecodeArgs a) {
                 float acc = 0.0f;
 #pragma unroll
                 for (int c = 0; c < S::CPL; ++c)
-                    acc = fmaf(scale_at<F>(sc[c], n) * hscale[c], dot_chunk<F>(code[n][c], ha[c]), acc);
+                    acc = fmaf(scale_at<F>(sc[c], n) * hscale[c], dot_planes<F>(code[n][c], ha[c]), acc);
                 v[n] = acc;
             }
             __builtin_amdgcn_sched_barrier(0);
@@ -872,8 +913,9 @@ hipError_t launch_router_c(const DecodeArgs& a, hipStream_t st, const LaunchTimi
 }
 template <int KG>
 hipError_t launch_router(const DecodeArgs& a, hipStream_t st, const LaunchTiming& tm) {
-    return a.codec == kCodecMxfp4 ? launch_router_c<KG, kCodecMxfp4>(a, st, tm)
-                                  : launch_router_c<KG, kCodecInt4>(a, st, tm);
+    if (a.codec == kCodecMxfp4) return launch_router_c<KG, kCodecMxfp4>(a, st, tm);
+    if (a.codec == kCodecInt8) return launch_router_c<KG, kCodecInt8>(a, st, tm);
+    return launch_router_c<KG, kCodecInt4>(a, st, tm);
 }
 
 template <int KG>
@@ -890,27 +932,31 @@ hipError_t launch_gateup(const DecodeArgs& a, hipStream_t st, const LaunchTiming
     waves = (waves + 3) / 4 * 4;
     if (a.codec == kCodecMxfp4)
         return launch_kernel(gateup_kernel<KG, kCodecMxfp4>, dim3(waves / 4), dim3(256), st, tm, a);
+    if (a.codec == kCodecInt8)
+        return launch_kernel(gateup_kernel<KG, kCodecInt8>, dim3(waves / 4), dim3(256), st, tm, a);
     return launch_kernel(gateup_kernel<KG, kCodecInt4>, dim3(waves / 4), dim3(256), st, tm, a);
 }
 
-template <int KG, int NLD>
-hipError_t launch_down_nl(const DecodeArgs& a, hipStream_t st, const LaunchTiming& tm) {
+template <int KG, int NLD, int F>
+hipError_t launch_down_c(const DecodeArgs& a, hipStream_t st, const LaunchTiming& tm) {
     using S = DownShape<KG, NLD>;
-    if constexpr (ilog2(pow2_at_least(S::NL)) <= S::B && S::NL * S::CPL <= kDownMaxLoads) {
+    if constexpr (ilog2(pow2_at_least(S::NL)) <= S::B && S::NL * S::CPL * code_planes(F) <= kDownMaxLoads) {
         const int grid = a.H / S::R;
-        if (a.codec == kCodecMxfp4)
-            return launch_kernel(down_combine_kernel<KG, NLD, kCodecMxfp4>, dim3(grid), dim3((a.K + a.S) * 64), st,
-                                 tm, a);
-        return launch_kernel(down_combine_kernel<KG, NLD, kCodecInt4>, dim3(grid), dim3((a.K + a.S) * 64), st, tm,
-                             a);
+        return launch_kernel(down_combine_kernel<KG, NLD, F>, dim3(grid), dim3((a.K + a.S) * 64), st, tm, a);
     } else {
         return hipErrorInvalidValue;  // never chosen by down_rows
     }
 }
+template <int KG, int NLD>
+hipError_t launch_down_nl(const DecodeArgs& a, hipStream_t st, const LaunchTiming& tm) {
+    if (a.codec == kCodecMxfp4) return launch_down_c<KG, NLD, kCodecMxfp4>(a, st, tm);
+    if (a.codec == kCodecInt8) return launch_down_c<KG, NLD, kCodecInt8>(a, st, tm);
+    return launch_down_c<KG, NLD, kCodecInt4>(a, st, tm);
+}
 
 template <int KG>
 hipError_t launch_down(const DecodeArgs& a, hipStream_t st, const LaunchTiming& tm) {
-    const int nl = down_rows(a.H, KG) / rows_per_load(KG);
+    const int nl = down_rows(a.H, KG, code_planes(a.codec)) / rows_per_load(KG);
     switch (nl) {
         case 1: return launch_down_nl<KG, 1>(a, st, tm);
         case 2: return launch_down_nl<KG, 2>(a, st, tm);
@@ -970,7 +1016,7 @@ bool decode_shape_supported(int hidden, int inter, int top_k, int n_shared) {
     const int kh = hidden / 32, ki = inter / 32;
     const bool h_ok = kh == 8 || kh == 16 || kh == 32 || kh == 64 || kh == 128 || kh == 192 || kh == 256;
     const bool i_ok = ki == 4 || ki == 8 || ki == 16 || ki == 32 || ki == 64 || ki == 128;
-    return h_ok && i_ok && hidden % 256 == 0 && hidden % down_rows(hidden, ki) == 0 &&
+    return h_ok && i_ok && hidden % 256 == 0 && hidden % down_rows(hidden, ki, 1) == 0 && hidden % down_rows(hidden, ki, 2) == 0 &&
            inter % gateup_rows(kh) == 0 && top_k <= 8;
 }
 

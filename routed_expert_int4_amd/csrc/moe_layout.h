@@ -5,11 +5,15 @@
 //   gate codes [I][H/2], up codes [I][H/2], down codes [H][I/2]
 //       the public row-major bytes; int4 nibbles are stored as q + 8
 //       (offset binary, the kernels take the offset off with a per-group
-//       correction), MXFP4 (E2M1) nibbles as they are;
+//       correction), MXFP4 (E2M1) nibbles as they are, int8 codes q as the
+//       int4 planes of their high nibbles q >> 4 (signed, stored + 8);
 //   gate and up scales (interleaved per block of rows), down scales
 //       (fp16 bits for int4, E8M0 bytes for MXFP4), permuted so that each
 //       lane of a wave finds the scales it needs for one work item in
-//       consecutive bytes (see scale_index and gateup_scale_index).
+//       consecutive bytes (see scale_index and gateup_scale_index);
+//   int8 only: gate, up and down planes of the low nibbles q & 15
+//       (unsigned), shaped as the high planes, so q = 16 hi + lo and every
+//       kernel keeps the int4 lane mapping with two loads per chunk.
 // The blob is exactly as large as the public layout.
 #pragma once
 
@@ -24,7 +28,10 @@ constexpr int kWave = 64;
 // Weight codecs (the moe_config_t codec values).
 constexpr int kCodecInt4 = 0;   // int4 codes, fp16 scale per 32 inputs
 constexpr int kCodecMxfp4 = 1;  // E2M1 codes, E8M0 scale per 32 inputs
+constexpr int kCodecInt8 = 2;   // int8 codes, fp16 scale per 32 inputs
 __host__ __device__ constexpr int scale_bytes(int codec) { return codec == kCodecMxfp4 ? 1 : 2; }
+// Nibble planes per matrix in the blob (int8: high and low nibbles).
+__host__ __device__ constexpr int code_planes(int codec) { return codec == kCodecInt8 ? 2 : 1; }
 // Rows of gate (and of up) per gate/up work item when a row fits in one
 // wave load or more.
 constexpr int kGateUpRowsBase = 1;
@@ -53,15 +60,16 @@ __host__ __device__ constexpr int pow2_at_least(int v) { return v <= 1 ? 1 : 2 *
 // divides hidden, with a step count s from down_step_option such that the
 // wave's s x chunks_per_lane code loads stay within kDownMaxLoads and its s
 // row partials, rounded up to a power of two, fit the lanes that share a row
-// (min(inter/32, 64)).
-__host__ __device__ inline int down_rows(int hidden, int kg_i) {
+// (min(inter/32, 64)).  With two nibble planes (int8) every step loads
+// twice as many chunks.
+__host__ __device__ inline int down_rows(int hidden, int kg_i, int planes) {
     const int rpl = rows_per_load(kg_i);
     const int lanes_per_row = kg_i < kWave ? kg_i : kWave;
     const int target = hidden / 256 > rpl ? hidden / 256 : rpl;
     for (int i = 0; i < 7; ++i) {
         const int steps = down_step_option(i);
         const int r = steps * rpl;
-        if (r <= target && hidden % r == 0 && steps * chunks_per_lane(kg_i) <= kDownMaxLoads &&
+        if (r <= target && hidden % r == 0 && steps * chunks_per_lane(kg_i) * planes <= kDownMaxLoads &&
             pow2_at_least(steps) <= lanes_per_row)
             return r;
     }
@@ -89,8 +97,9 @@ __host__ __device__ inline size_t gateup_scale_index(int r, int g, int m, int kg
 }
 
 struct BlobLayout {
-    size_t gate_q, up_q, down_q;  // byte offsets of the code arrays
-    size_t gu_s, down_s;          // byte offsets of the scale arrays
+    size_t gate_q, up_q, down_q;     // byte offsets of the code arrays (int8: high-nibble planes)
+    size_t gu_s, down_s;             // byte offsets of the scale arrays
+    size_t gate_lo, up_lo, down_lo;  // int8 low-nibble planes (0 otherwise)
     size_t total;
 };
 
@@ -104,6 +113,13 @@ __host__ __device__ inline BlobLayout blob_layout(int hidden, int inter, int cod
     L.gu_s = 3 * codes;
     L.down_s = 3 * codes + 2 * scales;
     L.total = 3 * codes + 3 * scales;
+    L.gate_lo = L.up_lo = L.down_lo = 0;
+    if (codec == kCodecInt8) {
+        L.gate_lo = L.total;
+        L.up_lo = L.total + codes;
+        L.down_lo = L.total + 2 * codes;
+        L.total += 3 * codes;
+    }
     return L;
 }
 

@@ -113,6 +113,31 @@ def test_pack_mxfp4_keeps_codes_and_permutes_e8m0_scales():
     assert B.lib().moe_expert_bytes(ctypes.byref(c)) == 0
 
 
+def test_pack_int8_splits_codes_into_nibble_planes():
+    """Int8 blob: high nibbles (offset + 8) where the int4 codes go, low
+    nibbles in planes after the scales; q = 16 hi + lo for every code."""
+    import dataclasses
+    cfg = dataclasses.replace(synth.TINY, codec="int8")
+    w = synth.gen_layer(cfg, seed=0)
+    nb = B.moe_expert_bytes(cfg)
+    assert nb == cfg.expert_bytes() == 3 * cfg.hidden * cfg.inter + 3 * cfg.hidden * cfg.inter // 16
+    blob = np.empty(nb, np.uint8)
+    B.moe_expert_pack(cfg, *w.expert_arrays(2), blob)
+    n = cfg.hidden * cfg.inter // 2
+    s_bytes = 3 * cfg.hidden * cfg.inter // 16
+    for m, q in enumerate((w.gate_q[2], w.up_q[2], w.down_q[2])):
+        hi = blob[m * n:(m + 1) * n]
+        lo = blob[3 * n + s_bytes + m * n:3 * n + s_bytes + (m + 1) * n]
+        hi_n = np.stack([hi & 15, hi >> 4], axis=-1).reshape(-1).astype(np.int64) - 8
+        lo_n = np.stack([lo & 15, lo >> 4], axis=-1).reshape(-1).astype(np.int64)
+        np.testing.assert_array_equal(16 * hi_n + lo_n, q.ravel().view(np.int8).astype(np.int64))
+    sc = blob[3 * n:3 * n + s_bytes].view(np.uint16)
+    m = sc.size // 3
+    gs, us, ds = w.gate_s[2], w.up_s[2], w.down_s[2]
+    np.testing.assert_array_equal(np.sort(sc[:2 * m]), np.sort(np.concatenate([gs.ravel(), us.ravel()])))
+    np.testing.assert_array_equal(np.sort(sc[2 * m:]), np.sort(ds.ravel()))
+
+
 def test_pack_rejects_null():
     code = B.lib().moe_expert_pack(B.MoeConfig.from_cfg(synth.TINY), None, None, None, None, None, None, None)
     assert code == B.MOE_EINVAL

@@ -238,16 +238,17 @@ def test_cache_top_p(torch_cuda):
     cache.close()
 
 
-def test_cache_mxfp4(torch_cuda):
-    """MXFP4 experts behind the cache: outputs equal the resident MXFP4
+@pytest.mark.parametrize("codec", ["mxfp4", "int8"])
+def test_cache_other_codecs(torch_cuda, codec):
+    """MXFP4 and int8 experts behind the cache: outputs equal the resident
     layer's one-token calls bit for bit, and the oracle's within tolerance;
-    copies move MXFP4 blobs (h2d_bytes = misses x MXFP4 blob bytes)."""
+    copies move the codec's blobs (h2d_bytes = misses x blob bytes)."""
     import dataclasses
     torch = torch_cuda
     from routed_expert_int4_amd.layer import DeviceLayer
-    cfg = dataclasses.replace(CFG, codec="mxfp4")
+    cfg = dataclasses.replace(CFG, codec=codec)
     slots = CFG.top_k
-    say(f"[gpu] mxfp4 cache, {slots} slots")
+    say(f"[gpu] {codec} cache, {slots} slots")
     cache, weights, cached, resident = make_stack(torch, slots, n_layers=1, cfg=cfg)
     assert cache.nb == cfg.expert_bytes()
     x_bits = synth.gen_tokens(cfg, N_TOKENS, seed=70)
@@ -261,7 +262,7 @@ def test_cache_mxfp4(torch_cuda):
     st = cache.stats(0)
     assert (st["hits"], st["misses"], st["evictions"]) == lru.replay(idh, slots)
     assert st["h2d_bytes"] == st["misses"] * cache.nb
-    say(f"[gpu] mxfp4 cache: rel err {res['worst_rel']:.3g}, stats {st}")
+    say(f"[gpu] {codec} cache: rel err {res['worst_rel']:.3g}, stats {st}")
     for lay in cached + resident:
         lay.close()
     cache.close()

@@ -290,18 +290,20 @@ def with_codec(cfg, codec="mxfp4"):
     return dataclasses.replace(cfg, codec=codec)
 
 
+@pytest.mark.parametrize("codec", ["mxfp4", "int8"])
 @pytest.mark.parametrize("cfg_name", ["TINY", "MID_A", "MID_B", "MID_C", "MID_D"])
-def test_mxfp4_layer_parity(torch_cuda, cfg_name):
-    """One-token calls of MXFP4 layers against the oracle (E2M1 codes, E8M0
-    scales), every lane mapping of the kernels."""
-    cfg = with_codec({"TINY": synth.TINY, "MID_A": MID_A, "MID_B": MID_B, "MID_C": MID_C, "MID_D": MID_D}[cfg_name])
-    say(f"[gpu] mxfp4 layer parity {cfg_name}")
+def test_codec_layer_parity(torch_cuda, cfg_name, codec):
+    """One-token calls of MXFP4 (E2M1 codes, E8M0 scales) and int8 layers
+    against the oracle, every lane mapping of the kernels."""
+    cfg = with_codec({"TINY": synth.TINY, "MID_A": MID_A, "MID_B": MID_B, "MID_C": MID_C, "MID_D": MID_D}[cfg_name],
+                     codec)
+    say(f"[gpu] {codec} layer parity {cfg_name}")
     weights = synth.gen_layer(cfg, seed=0)
     T = 4 if cfg.hidden * cfg.inter > 2 ** 24 else 13
     x = synth.gen_tokens(cfg, T, seed=1)
     layer, y, ids, w = run_layer(torch_cuda, weights, x)
     res = check_layer(weights, x, y, ids, w)
-    say(f"[gpu] mxfp4 {cfg_name}: worst rel err {res['worst_rel']:.3g}, excused {res['excused']}")
+    say(f"[gpu] {codec} {cfg_name}: worst rel err {res['worst_rel']:.3g}, excused {res['excused']}")
     layer.close()
 
 
@@ -326,9 +328,10 @@ def test_mxfp4_extreme_scales_and_activations(torch_cuda):
             layer.close()
 
 
-def test_mxfp4_batched_call_unsupported(torch_cuda):
+@pytest.mark.parametrize("codec", ["mxfp4", "int8"])
+def test_codec_batched_call_unsupported(torch_cuda, codec):
     from routed_expert_int4_amd.layer import DeviceLayer
-    weights = synth.gen_layer(with_codec(synth.TINY), seed=0)
+    weights = synth.gen_layer(with_codec(synth.TINY, codec), seed=0)
     layer = DeviceLayer(weights, max_T=4)
     x = DeviceLayer.to_device_bf16(synth.gen_tokens(synth.TINY, 4, seed=1))
     with pytest.raises(B.MoeError) as ei:
@@ -365,4 +368,44 @@ def test_glm_mxfp4_decode(torch_cuda):
     torch_cuda.cuda.synchronize()
     res = check_layer(wp, x[:40], y.cpu().numpy(), ids.cpu().numpy(), w.cpu().numpy(), rows=[0, 7, 39])
     say(f"[gpu] GLM mxfp4 top-p 0.7: worst rel err {res['worst_rel']:.3g}")
+    layer.close()
+
+
+def test_int8_extreme_codes_and_activations(torch_cuda):
+    """Int8 codes at -128 and 127 over whole rows and activations of std 1e-3
+    and 300 stay within tolerance (the two nibble planes recombine exactly)."""
+    cfg = with_codec(MID_A, "int8")
+    say("[gpu] int8 extreme codes")
+    base = synth.gen_layer(cfg, seed=3)
+    gq = base.gate_q.copy()
+    gq[:, 0::3, :] = 0x80  # -128
+    gq[:, 1::3, :] = 0x7F  # 127
+    dq = base.down_q.copy()
+    dq[:, 0::2, :] = 0x80
+    weights = dataclasses.replace(base, gate_q=gq, down_q=dq)
+    for std in (1e-3, 300.0):
+        x = synth.gen_tokens(cfg, 3, seed=11, std=std)
+        layer, y, ids, w = run_layer(torch_cuda, weights, x)
+        res = check_layer(weights, x, y, ids, w)
+        say(f"[gpu] int8 extremes std {std}: worst rel err {res['worst_rel']:.3g}")
+        layer.close()
+
+
+def test_glm_int8_decode(torch_cuda):
+    """GLM-shaped int8 layer (twice the int4 code bytes), 200 one-token
+    calls: routing of every token and sampled outputs against the oracle."""
+    cfg = with_codec(synth.GLM, "int8")
+    say("[gpu] generating the GLM-shaped int8 layer (seed 0)")
+    weights = synth.gen_layer(cfg, seed=0)
+    from routed_expert_int4_amd.layer import DeviceLayer
+    layer = DeviceLayer(weights, max_T=1)
+    x = synth.gen_tokens(cfg, 200, seed=1)
+    y, ids, w = layer.forward_each(DeviceLayer.to_device_bf16(x))
+    torch_cuda.cuda.synchronize()
+    y, ids, w = y.cpu().numpy(), ids.cpu().numpy(), w.cpu().numpy()
+    ids_ref, w_ref, gap = oracle.route(weights, x)
+    excused = check_routing(cfg, ids, w, ids_ref, w_ref, gap)
+    rows = sorted(set([0, 1, 100, 199] + list(np.argsort(gap)[:2])))
+    res = check_layer(weights, x, y, ids, w, rows=rows)
+    say(f"[gpu] GLM int8: {len(excused)} excused, sampled worst rel err {res['worst_rel']:.3g}")
     layer.close()

@@ -50,6 +50,11 @@
  *    fp16 scale per 32 inputs as int4; weight = fp32(scale) * q (exact: an
  *    11-bit significand times an 8-bit integer).
  *
+ *  - Int2 format (codec 3), the packed int2 of the same list.  Reading: four
+ *    two's complement 2-bit codes per byte (values -2..1), column 4j + t in
+ *    bits [2t, 2t + 2) of byte j, the same fp16 scale per 32 inputs;
+ *    weight = fp32(scale) * q.
+ *
  *  - Adaptive expert top-p (colibri summary, options list: --topp, an
  *    adaptive expert top-p that cuts the expert reads).  Reading: with
  *    top_p < 1, the selected experts are ranked by their share s_j / sum_sel s
@@ -164,16 +169,37 @@ static void int8_matvec(const uint8_t* q, const uint16_t* s, int rows, int cols,
     }
 }
 
+/* Int2: code of column c in a packed row (two's complement 2-bit field). */
+static int code2_at(const uint8_t* row, int c) {
+    int v = (row[c >> 2] >> ((c & 3) * 2)) & 3;
+    return v >= 2 ? v - 4 : v;
+}
+static void int2_matvec(const uint8_t* q, const uint16_t* s, int rows, int cols, const double* x, double* y) {
+    for (int r = 0; r < rows; ++r) {
+        const uint8_t* qr = q + (size_t)r * (cols / 4);
+        const uint16_t* sr = s + (size_t)r * (cols / 32);
+        double acc = 0.0;
+        for (int g = 0; g < cols / 32; ++g) {
+            float scale = (float)half_to_double(sr[g]);
+            for (int c = 32 * g; c < 32 * g + 32; ++c) acc += (double)(scale * (float)code2_at(qr, c)) * x[c];
+        }
+        y[r] = acc;
+    }
+}
+
 /* Codec 0: int4 codes with fp16 scales; codec 1: MXFP4 (E2M1 codes, E8M0
- * scales); codec 2: int8 codes with fp16 scales.  Scale arrays are uint16
- * (codecs 0 and 2) or uint8 (codec 1); code arrays hold cols/2 bytes per row
- * (codecs 0 and 1) or cols (codec 2). */
+ * scales); codec 2: int8 codes, codec 3: int2 codes, both with fp16 scales.
+ * Scale arrays are uint16 (codecs 0, 2, 3) or uint8 (codec 1); code arrays
+ * hold cols/2 bytes per row (codecs 0 and 1), cols (codec 2) or cols/4
+ * (codec 3). */
 static void codec_matvec(int codec, const uint8_t* q, const void* s, int rows, int cols, const double* x,
                          double* y) {
     if (codec == 1)
         mxfp4_matvec(q, (const uint8_t*)s, rows, cols, x, y);
     else if (codec == 2)
         int8_matvec(q, (const uint16_t*)s, rows, cols, x, y);
+    else if (codec == 3)
+        int2_matvec(q, (const uint16_t*)s, rows, cols, x, y);
     else
         int4_matvec(q, (const uint16_t*)s, rows, cols, x, y);
 }
@@ -332,9 +358,9 @@ int oracle_layer_forward(int codec, int hidden, int inter, int n_experts, int n_
                          const uint16_t* x_bf16, int T, const int32_t* forced_ids,
                          double* y, int32_t* ids, double* w, double* gap, double* pgap, double* logits,
                          int n_threads) {
-    if (hidden % 32 || inter % 32 || T < 0 || n_shared < 0 || codec < 0 || codec > 2) return -1;
-    const size_t ssz = codec == 1 ? 1 : 2;         /* bytes per scale */
-    const size_t cpb = codec == 2 ? 1 : 2;         /* codes per byte */
+    if (hidden % 32 || inter % 32 || T < 0 || n_shared < 0 || codec < 0 || codec > 3) return -1;
+    const size_t ssz = codec == 1 ? 1 : 2;                       /* bytes per scale */
+    const size_t cpb = codec == 2 ? 1 : codec == 3 ? 4 : 2;      /* codes per byte */
     const uint8_t *gs_b = (const uint8_t*)gate_s, *us_b = (const uint8_t*)up_s, *ds_b = (const uint8_t*)down_s;
     const size_t gq_n = (size_t)inter * (hidden / cpb), gs_n = (size_t)inter * (hidden / 32);
     const size_t dq_n = (size_t)hidden * (inter / cpb), ds_n = (size_t)hidden * (inter / 32);

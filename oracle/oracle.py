@@ -73,8 +73,8 @@ def max_threads() -> int:
     return lib().oracle_max_threads()
 
 
-CODECS = {"int4": 0, "mxfp4": 1, "int8": 2}
-CODES_PER_BYTE = {"int4": 2, "mxfp4": 2, "int8": 1}
+CODECS = {"int4": 0, "mxfp4": 1, "int8": 2, "int2": 3}
+CODES_PER_BYTE = {"int4": 2, "mxfp4": 2, "int8": 1, "int2": 4}
 
 
 def _scale_dtype(codec: str):
@@ -95,8 +95,8 @@ def expert_ffn(hidden, inter, gate_q, gate_s, up_q, up_s, down_q, down_s, x: np.
 
 def matvec(q: np.ndarray, s: np.ndarray, x: np.ndarray, codec: str = "int4") -> np.ndarray:
     """y = W x for one quantised matrix: codes q [rows, cols/codes per byte],
-    scales s [rows, cols/32] (fp16 bits for int4 and int8, E8M0 bytes for
-    mxfp4)."""
+    scales s [rows, cols/32] (fp16 bits for int4, int8 and int2, E8M0 bytes
+    for mxfp4)."""
     q = np.ascontiguousarray(q, dtype=np.uint8)
     s = np.ascontiguousarray(s, dtype=_scale_dtype(codec))
     rows, cols = q.shape[0], CODES_PER_BYTE[codec] * q.shape[1]

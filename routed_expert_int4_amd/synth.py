@@ -20,7 +20,9 @@ Public layout of one layer (row-major, little-endian):
 With ``codec="mxfp4"`` the codes are MXFP4 elements (E2M1 nibbles, same
 packing) and every scale array is uint8 E8M0 bytes (one per 32 inputs).
 With ``codec="int8"`` every code is one two's complement byte (code arrays
-``[I, H]`` and ``[H, I]``) with the same fp16 scales.
+``[I, H]`` and ``[H, I]``) with the same fp16 scales; with ``codec="int2"``
+a byte holds four two's complement 2-bit codes, column 4j + t in bits
+[2t, 2t + 2) of byte j (code arrays ``[I, H/4]`` and ``[H, I/4]``).
 
 Value distributions follow the GLM-5.2-shaped layer described on the pages
 (routed experts 256, top-8, ~19 MB of int4 codes per expert): codes are uniform
@@ -31,7 +33,8 @@ MXFP4 layers draw their codes the same way (uniform bytes: every E2M1 code
 equally likely, rms element 2.93) and E8M0 scale bytes 127 + round(N(-5, 0.75))
 (about 2^-5, so the weights have the int4 layer's magnitude).  Int8 layers
 draw uniform code bytes and scales exp(N(-6.77, 0.5)) (the int4 scale times
-4.64 / 73.9, the ratio of the codes' rms values).
+4.64 / 73.9, the ratio of the codes' rms values); int2 layers uniform code
+bytes and scales exp(N(-2.66, 0.5)) (ratio 4.64 / 1.22).
 Streams: SeedSequence(seed).spawn(1 + E + S); the first child draws the
 router weight then the bias; child 1 + e draws expert e (routed experts
 first, shared last) in the order gate codes, gate scales, up codes, up
@@ -55,7 +58,7 @@ class LayerConfig:
     n_shared: int = 1
     routed_scaling_factor: float = 2.5
     top_p: float = 1.0  # adaptive expert top-p over the selected experts (1: plain top-k)
-    codec: str = "int4"  # "int4", "int8" (fp16 scales) or "mxfp4" (E2M1 codes, E8M0 scales)
+    codec: str = "int4"  # "int4", "int8", "int2" (fp16 scales) or "mxfp4" (E2M1 codes, E8M0 scales)
 
     @property
     def n_total_experts(self) -> int:
@@ -67,7 +70,7 @@ class LayerConfig:
 
     @property
     def codes_per_byte(self) -> int:
-        return 1 if self.codec == "int8" else 2
+        return {"int8": 1, "int2": 4}.get(self.codec, 2)
 
     def expert_bytes(self) -> int:
         """Bytes of one expert in the public layout (codes + scales)."""
@@ -129,6 +132,12 @@ def _int8_scales(rng: np.random.Generator, shape) -> np.ndarray:
     return np.exp(z * np.float32(0.5) - np.float32(6.77)).astype(np.float16).view(np.uint16)
 
 
+def _int2_scales(rng: np.random.Generator, shape) -> np.ndarray:
+    """exp(N(-2.66, 0.5)) rounded to fp16 (bits)."""
+    z = rng.standard_normal(size=shape, dtype=np.float32)
+    return np.exp(z * np.float32(0.5) - np.float32(2.66)).astype(np.float16).view(np.uint16)
+
+
 def _e8m0_scales(rng: np.random.Generator, shape) -> np.ndarray:
     """E8M0 bytes 127 + round(N(-5, 0.75))."""
     z = rng.standard_normal(size=shape, dtype=np.float32)
@@ -154,7 +163,8 @@ def gen_layer(cfg: LayerConfig, seed: int, workers: int | None = None) -> LayerW
     h, i, e_all = cfg.hidden, cfg.inter, cfg.n_total_experts
     children = np.random.SeedSequence(seed).spawn(1 + e_all)
     router_w, bias = gen_router(cfg, seed)
-    sdt, scales = {"mxfp4": (np.uint8, _e8m0_scales), "int8": (np.uint16, _int8_scales)}.get(
+    sdt, scales = {"mxfp4": (np.uint8, _e8m0_scales), "int8": (np.uint16, _int8_scales),
+                   "int2": (np.uint16, _int2_scales)}.get(
         cfg.codec, (np.uint16, _scales))
     cpb = cfg.codes_per_byte
     gq = np.empty((e_all, i, h // cpb), np.uint8)

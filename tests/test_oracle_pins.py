@@ -604,3 +604,66 @@ def test_int8_generator_layout():
     assert cfg.expert_bytes() == 3 * cfg.hidden * cfg.inter + 3 * cfg.hidden * cfg.inter // 16
     y = oracle.layer_forward(w, synth.gen_tokens(cfg, 2, seed=1))["y"]
     assert np.all(np.isfinite(y)) and 0.05 < np.abs(y).max() < 1e3
+
+
+# ----------------------------------------------------------------- int2 codec
+def pack_int2(q: np.ndarray) -> np.ndarray:
+    """Test-side packer: integers [R, C] in [-2, 1] -> bytes [R, C/4], column
+    4j + t in bits [2t, 2t + 2) of byte j, two's complement."""
+    q = np.asarray(q, dtype=np.int64)
+    assert q.min() >= -2 and q.max() <= 1 and q.shape[1] % 4 == 0
+    f = (q & 3).astype(np.uint8)
+    return (f[:, 0::4] | (f[:, 1::4] << 2) | (f[:, 2::4] << 4) | (f[:, 3::4] << 6)).astype(np.uint8)
+
+
+def test_int2_unit_vectors_every_field_position():
+    """x = e_c returns column c of W = scale * q: each of the four 2-bit
+    fields of a byte, every code value (-2, -1, 0, 1) and the scale group."""
+    rng = np.random.default_rng(41)
+    rows, cols = 8, 64
+    q = rng.integers(-2, 2, size=(rows, cols))
+    q[0, :] = -2
+    q[1, :] = 1
+    q[2, 0:4] = [-2, -1, 0, 1]
+    q[3, 0:4] = [1, 0, -1, -2]
+    s = f16_bits(np.exp(rng.normal(-1, 0.5, size=(rows, cols // 32))))
+    sc = s.view(np.float16).astype(np.float64)
+    for c in (0, 1, 2, 3, 4, 31, 32, 35, 63):
+        x = np.zeros(cols)
+        x[c] = 1.0
+        np.testing.assert_array_equal(oracle.matvec(pack_int2(q), s, x, codec="int2"), q[:, c] * sc[:, c // 32])
+    x = rng.normal(size=cols)
+    np.testing.assert_allclose(oracle.matvec(pack_int2(q), s, x, codec="int2"),
+                               (q * np.repeat(sc, 32, axis=1)) @ x, rtol=1e-13)
+
+
+def test_int2_layer_equals_int4_layer_on_shared_codes():
+    """An int2 layer is the int4 layer with the same codes (in [-2, 1]) and
+    scales: bit-identical routing and outputs."""
+    import dataclasses
+    base = synth.gen_layer(synth.TINY, seed=6)
+    rng = np.random.default_rng(12)
+    i4, i2 = {}, {}
+    for name in ("gate", "up", "down"):
+        qs = getattr(base, name + "_q")
+        q = rng.integers(-2, 2, size=(qs.shape[0], qs.shape[1], qs.shape[2] * 2))
+        i4[name + "_q"] = np.stack([pack_int4(m) for m in q])
+        i2[name + "_q"] = np.stack([pack_int2(m) for m in q])
+    w4 = dataclasses.replace(base, **i4)
+    w2 = dataclasses.replace(base, cfg=dataclasses.replace(base.cfg, codec="int2"), **i2)
+    x = synth.gen_tokens(synth.TINY, 5, seed=13)
+    a, b = oracle.layer_forward(w4, x), oracle.layer_forward(w2, x)
+    np.testing.assert_array_equal(a["ids"], b["ids"])
+    np.testing.assert_array_equal(a["y"], b["y"])
+    assert np.abs(a["y"]).max() > 0
+
+
+def test_int2_generator_layout():
+    import dataclasses
+    cfg = dataclasses.replace(synth.TINY, codec="int2")
+    w = synth.gen_layer(cfg, seed=0)
+    assert w.gate_q.shape == (cfg.n_total_experts, cfg.inter, cfg.hidden // 4)
+    assert w.down_q.shape == (cfg.n_total_experts, cfg.hidden, cfg.inter // 4)
+    assert cfg.expert_bytes() == 3 * cfg.hidden * cfg.inter // 4 + 3 * cfg.hidden * cfg.inter // 16
+    y = oracle.layer_forward(w, synth.gen_tokens(cfg, 2, seed=1))["y"]
+    assert np.all(np.isfinite(y)) and 0.05 < np.abs(y).max() < 1e3

@@ -41,6 +41,8 @@ DTYPES = {
     "mxfp4": "MXFP4 weights (E2M1, E8M0 scales) x fp16 activation pairs, fp32 dot2 accumulate",
     "int8": "int8 weights (two nibble planes) x int16 fixed-point activations (two int8 parts), int32 dot, "
             "fp32 accumulate",
+    "int2": "int2 weights (two rows per nibble) x int16 fixed-point activations (two int8 parts), int32 dot, "
+            "fp32 accumulate",
 }
 
 
@@ -138,9 +140,9 @@ def main() -> int:
     ap.add_argument("--pin", type=int, default=-1,
                     help="cache-stack: experts pinned per layer by learned usage (-1: slots - top_k, 0: plain LRU)")
     ap.add_argument("--learn-tokens", type=int, default=128, help="cache-stack: tokens of the learning pass")
-    ap.add_argument("--codec", default="int4", choices=["int4", "mxfp4", "int8"],
-                    help="decode and cache-stack: expert weight codec (mxfp4: E2M1 codes, E8M0 scales; int8: one "
-                         "byte per weight, fp16 scales)")
+    ap.add_argument("--codec", default="int4", choices=["int4", "mxfp4", "int8", "int2"],
+                    help="decode and cache-stack: expert weight codec (mxfp4: E2M1 codes, E8M0 scales; int8, "
+                         "int2: one byte or 2 bits per weight, fp16 scales)")
     ap.add_argument("--top-p", type=float, default=1.0,
                     help="decode and cache-stack: adaptive expert top-p (1: plain top-k); decode prices its bytes "
                          "by the experts kept")

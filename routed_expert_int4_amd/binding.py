@@ -41,8 +41,8 @@ class MoeCacheStats(ctypes.Structure):
                 ("evictions", ctypes.c_uint64), ("prefetches", ctypes.c_uint64), ("pinned", ctypes.c_uint64)]
 
 
-MOE_CODEC_INT4, MOE_CODEC_MXFP4, MOE_CODEC_INT8 = 0, 1, 2
-CODECS = {"int4": MOE_CODEC_INT4, "mxfp4": MOE_CODEC_MXFP4, "int8": MOE_CODEC_INT8}
+MOE_CODEC_INT4, MOE_CODEC_MXFP4, MOE_CODEC_INT8, MOE_CODEC_INT2 = 0, 1, 2, 3
+CODECS = {"int4": MOE_CODEC_INT4, "mxfp4": MOE_CODEC_MXFP4, "int8": MOE_CODEC_INT8, "int2": MOE_CODEC_INT2}
 
 
 class MoeError(RuntimeError):

@@ -51,7 +51,7 @@ moe_status_t validate_config(const moe_config_t* c) {
     if (!(c->routed_scaling_factor == c->routed_scaling_factor))
         return fail(MOE_EINVAL, "routed_scaling_factor is NaN");
     if (!(c->top_p > 0.0f && c->top_p <= 1.0f)) return fail(MOE_EINVAL, "top_p must be in (0, 1]");
-    if (c->codec != kCodecInt4 && c->codec != kCodecMxfp4 && c->codec != kCodecInt8)
+    if (c->codec != kCodecInt4 && c->codec != kCodecMxfp4 && c->codec != kCodecInt8 && c->codec != kCodecInt2)
         return fail(MOE_EINVAL, "unknown codec %d", c->codec);
     return MOE_OK;
 }
@@ -134,20 +134,27 @@ WorkspaceLayout workspace_layout(const moe_config_t* c, int max_T) {
 // Scale arrays of one expert, permuted into the per-lane packs the kernels
 // read (T = uint16_t fp16 bits or uint8_t E8M0 bytes).
 template <typename T>
-void pack_scale_arrays(uint8_t* dst, const BlobLayout& L, int H, int I, int planes, const T* gate_s, const T* up_s,
+void pack_scale_arrays(uint8_t* dst, const BlobLayout& L, int H, int I, int codec, const T* gate_s, const T* up_s,
                        const T* down_s) {
-    const int kh = H / 32, ki = I / 32;
-    T* gu = reinterpret_cast<T*>(dst + L.gu_s);
-    const int p = gateup_rows(kh);
-    for (int r = 0; r < I; ++r)
-        for (int g = 0; g < kh; ++g) {
-            gu[gateup_scale_index(r, g, 0, kh, p)] = gate_s[(size_t)r * kh + g];
-            gu[gateup_scale_index(r, g, 1, kh, p)] = up_s[(size_t)r * kh + g];
+    const int kh = H / 32, ki = I / 32, rp = row_pack(codec);
+    const int p = gateup_rows(kh), pd = down_rows(H, ki, codec);
+    // stored row v of half `half` is matrix row rp * v + half (int2: even
+    // rows, then odd rows, each in its own arrays)
+    for (int half = 0; half < rp; ++half) {
+        T* gu = reinterpret_cast<T*>(dst + (half ? L.gu_s2 : L.gu_s));
+        for (int v = 0; v < I / rp; ++v) {
+            const size_t r = (size_t)rp * v + half;
+            for (int g = 0; g < kh; ++g) {
+                gu[gateup_scale_index(v, g, 0, kh, p)] = gate_s[r * kh + g];
+                gu[gateup_scale_index(v, g, 1, kh, p)] = up_s[r * kh + g];
+            }
         }
-    T* dn = reinterpret_cast<T*>(dst + L.down_s);
-    const int pd = down_rows(H, ki, planes);
-    for (int r = 0; r < H; ++r)
-        for (int g = 0; g < ki; ++g) dn[scale_index(r, g, ki, pd)] = down_s[(size_t)r * ki + g];
+        T* dn = reinterpret_cast<T*>(dst + (half ? L.down_s2 : L.down_s));
+        for (int v = 0; v < H / rp; ++v) {
+            const size_t r = (size_t)rp * v + half;
+            for (int g = 0; g < ki; ++g) dn[scale_index(v, g, ki, pd)] = down_s[r * ki + g];
+        }
+    }
 }
 
 }  // namespace moe
@@ -175,7 +182,8 @@ moe_status_t moe_expert_pack(const moe_config_t* cfg, const uint8_t* gate_q, con
     uint8_t* dst = static_cast<uint8_t*>(dst_blob);
     const size_t codes = (size_t)H * I / 2;
     const int kh = H / 32, ki = I / 32;
-    if (I % gateup_rows(kh) || H % down_rows(H, ki, code_planes(cfg->codec)))
+    const int rp = row_pack(cfg->codec);
+    if ((I / rp) % gateup_rows(kh) || (H / rp) % down_rows(H, ki, cfg->codec))
         return fail(MOE_EUNSUPPORTED, "moe_expert_pack: rows not a multiple of the scale pack");
     const uint8_t* src_q[3] = {gate_q, up_q, down_q};
     const size_t dst_q[3] = {L.gate_q, L.up_q, L.down_q};
@@ -189,7 +197,7 @@ moe_status_t moe_expert_pack(const moe_config_t* cfg, const uint8_t* gate_q, con
                 if (src_s[m][i] == 255) return fail(MOE_EINVAL, "moe_expert_pack: E8M0 scale 255 (NaN)");
         // codes: E2M1 nibbles as they are
         for (int m = 0; m < 3; ++m) std::memcpy(dst + dst_q[m], src_q[m], codes);
-        pack_scale_arrays(dst, L, H, I, 1, src_s[0], src_s[1], src_s[2]);
+        pack_scale_arrays(dst, L, H, I, cfg->codec, src_s[0], src_s[1], src_s[2]);
     } else if (cfg->codec == kCodecInt8) {
         // q = 16 hi + lo: high nibbles (signed, stored + 8) in the int4
         // planes, low nibbles (unsigned) in the low planes
@@ -200,14 +208,34 @@ moe_status_t moe_expert_pack(const moe_config_t* cfg, const uint8_t* gate_q, con
                 dst[dst_q[m] + i] = (uint8_t)((((a >> 4) ^ 8u) & 15u) | ((((b >> 4) ^ 8u) & 15u) << 4));
                 dst[dst_lo[m] + i] = (uint8_t)((a & 15u) | ((b & 15u) << 4));
             }
-        pack_scale_arrays(dst, L, H, I, 2, static_cast<const uint16_t*>(gate_s), static_cast<const uint16_t*>(up_s),
-                          static_cast<const uint16_t*>(down_s));
+        pack_scale_arrays(dst, L, H, I, cfg->codec, static_cast<const uint16_t*>(gate_s),
+                          static_cast<const uint16_t*>(up_s), static_cast<const uint16_t*>(down_s));
+    } else if (cfg->codec == kCodecInt2) {
+        // stored row v, column c: nibble (q[2v][c] + 2) | (q[2v + 1][c] + 2) << 2
+        // (flipping the sign bit of a two's complement field adds 2)
+        const int rows[3] = {I, I, H}, cols[3] = {H, H, I};
+        for (int m = 0; m < 3; ++m) {
+            const int C = cols[m];
+            uint8_t* d = dst + dst_q[m];
+            std::memset(d, 0, (size_t)rows[m] / 2 * (C / 2));
+            for (int v = 0; v < rows[m] / 2; ++v) {
+                const uint8_t* r0 = src_q[m] + (size_t)(2 * v) * (C / 4);
+                const uint8_t* r1 = r0 + C / 4;
+                for (int c = 0; c < C; ++c) {
+                    const unsigned f0 = ((r0[c >> 2] >> (2 * (c & 3))) & 3u) ^ 2u;
+                    const unsigned f1 = ((r1[c >> 2] >> (2 * (c & 3))) & 3u) ^ 2u;
+                    d[(size_t)v * (C / 2) + (c >> 1)] |= (uint8_t)((f0 | (f1 << 2)) << (4 * (c & 1)));
+                }
+            }
+        }
+        pack_scale_arrays(dst, L, H, I, cfg->codec, static_cast<const uint16_t*>(gate_s),
+                          static_cast<const uint16_t*>(up_s), static_cast<const uint16_t*>(down_s));
     } else {
         // codes: stored as q + 8 (flip bit 3 of every two's complement nibble)
         for (int m = 0; m < 3; ++m)
             for (size_t i = 0; i < codes; ++i) dst[dst_q[m] + i] = src_q[m][i] ^ 0x88u;
-        pack_scale_arrays(dst, L, H, I, 1, static_cast<const uint16_t*>(gate_s), static_cast<const uint16_t*>(up_s),
-                          static_cast<const uint16_t*>(down_s));
+        pack_scale_arrays(dst, L, H, I, cfg->codec, static_cast<const uint16_t*>(gate_s),
+                          static_cast<const uint16_t*>(up_s), static_cast<const uint16_t*>(down_s));
     }
     return MOE_OK;
 }
@@ -434,7 +462,7 @@ BatchArgs batch_args(moe_layer_t* L, const uint16_t* x, int n, int32_t* ids, flo
     b.TG = c.topk_group;
     b.K = c.top_k;
     b.S = c.n_shared;
-    b.down_p = down_rows(c.hidden, c.inter / 32, 1);
+    b.down_p = down_rows(c.hidden, c.inter / 32, kCodecInt4);
     b.router_splits = batch_router_splits(c.hidden);
     b.rsf = c.routed_scaling_factor;
     return b;
@@ -496,7 +524,7 @@ moe_status_t moe_layer_forward(moe_layer_t* layer, const uint16_t* d_x, int T, f
     if (T > 1 && !layer->cache) {
         if (c.top_p < 1.0f) return fail(MOE_EUNSUPPORTED, "moe_layer_forward: top_p < 1 needs T = 1 calls");
         if (c.codec != kCodecInt4)
-            return fail(MOE_EUNSUPPORTED, "moe_layer_forward: MXFP4 and int8 experts need T = 1 calls");
+            return fail(MOE_EUNSUPPORTED, "moe_layer_forward: MXFP4, int8 and int2 experts need T = 1 calls");
         // batch union: every distinct expert of a launch sequence is read once
         const int tb = layer->W.batch_tokens;
         for (int t0 = 0; t0 < T; t0 += tb) {

@@ -182,6 +182,32 @@ __device__ __forceinline__ float dot_chunk_int8(u32x4 chi, u32x4 clo, const HI8&
     return (float)(16 * (h1 * 256 + l1 - a.corr) + h2 * 256 + l2);
 }
 
+// Int2 chunk: every nibble holds the codes of two rows (bits 0-1: the even
+// row, bits 2-3: the odd row), each + 2; both rows take the int4 dot with the
+// same HI8 operands and the offset correction 2 sum(a) = corr / 4.
+__device__ __forceinline__ void dot_chunk_int2(u32x4 c, const HI8& a, float& r0, float& r1) {
+    int h0 = 0, l0 = 0, h1 = 0, l1 = 0;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        const unsigned he = a.he[d], ho = a.ho[d], le = a.le[d], lo_ = a.lo[d];
+        const unsigned w = c[d];
+        const unsigned e = w & 0x0F0F0F0Fu, o = (w >> 4) & 0x0F0F0F0Fu;
+        const int e0 = (int)(e & 0x03030303u), o0 = (int)(o & 0x03030303u);
+        const int e1 = (int)((e >> 2) & 0x03030303u), o1 = (int)((o >> 2) & 0x03030303u);
+        h0 = __builtin_amdgcn_sdot4(e0, (int)he, h0, false);
+        h0 = __builtin_amdgcn_sdot4(o0, (int)ho, h0, false);
+        l0 = (int)__builtin_amdgcn_udot4((unsigned)e0, le, (unsigned)l0, false);
+        l0 = (int)__builtin_amdgcn_udot4((unsigned)o0, lo_, (unsigned)l0, false);
+        h1 = __builtin_amdgcn_sdot4(e1, (int)he, h1, false);
+        h1 = __builtin_amdgcn_sdot4(o1, (int)ho, h1, false);
+        l1 = (int)__builtin_amdgcn_udot4((unsigned)e1, le, (unsigned)l1, false);
+        l1 = (int)__builtin_amdgcn_udot4((unsigned)o1, lo_, (unsigned)l1, false);
+    }
+    const int corr = a.corr >> 2;
+    r0 = (float)(h0 * 256 + l0 - corr);
+    r1 = (float)(h1 * 256 + l1 - corr);
+}
+
 // Codec dispatch of the operand form and the chunk dot.
 template <int F, int CPL>
 __device__ __forceinline__ void to_operands(const float (&hin)[CPL][32], HI8 (&ha)[CPL], float (&hscale)[CPL]) {
@@ -373,16 +399,17 @@ __device__ __forceinline__ void load_activations(const unsigned* __restrict__ xq
     }
 }
 
-template <int KG, int P>
+template <int KG, int F>
 struct GateUpBuf {
     using S = GateUpShape<KG>;
+    static constexpr int P = code_planes(F), RP = row_pack(F);
     u32x4 cg[S::NL][S::CPL][P], cu[S::NL][S::CPL][P];  // P code planes (int8: 2)
-    unsigned sgu[S::CPL][S::NL];  // halves 0..NL-1 gate, NL..2NL-1 up
+    unsigned sgu[RP][S::CPL][S::NL];  // per row parity (int2): 0..NL-1 gate, NL..2NL-1 up
 };
 
 template <int KG, int F>
 __device__ __forceinline__ void gateup_issue(const uint8_t* __restrict__ blob, const BlobLayout& L, int rb, int lane,
-                                             GateUpBuf<KG, code_planes(F)>& b) {
+                                             GateUpBuf<KG, F>& b) {
     using S = GateUpShape<KG>;
     constexpr int P = code_planes(F);
     const int g0 = KG >= kWave ? lane : (lane & (KG - 1));
@@ -401,19 +428,22 @@ __device__ __forceinline__ void gateup_issue(const uint8_t* __restrict__ blob, c
         }
     }
 #pragma unroll
+    for (int h = 0; h < row_pack(F); ++h)
+#pragma unroll
     for (int c = 0; c < S::CPL; ++c) {
-        const uint8_t* p = blob + L.gu_s + ((size_t)rb * KG + g0 + kWave * c) * 2 * S::R * scale_bytes(F);
+        const uint8_t* p =
+            blob + (h ? L.gu_s2 : L.gu_s) + ((size_t)rb * KG + g0 + kWave * c) * 2 * S::R * scale_bytes(F);
         if constexpr (S::RPL == 1) {
-            load_scales_c<F, 2 * S::NL>(p, b.sgu[c]);
+            load_scales_c<F, 2 * S::NL>(p, b.sgu[h][c]);
         } else if constexpr (F == kCodecMxfp4) {
             const unsigned g = __builtin_nontemporal_load(as_global<uint8_t>(p + row_sub));
             const unsigned u = __builtin_nontemporal_load(as_global<uint8_t>(p + S::R + row_sub));
-            b.sgu[c][0] = g | (u << 8);
+            b.sgu[h][c][0] = g | (u << 8);
         } else {
             const uint16_t* p16 = reinterpret_cast<const uint16_t*>(p);
             const unsigned g = __builtin_nontemporal_load(as_global<uint16_t>(p16 + row_sub));
             const unsigned u = __builtin_nontemporal_load(as_global<uint16_t>(p16 + S::R + row_sub));
-            b.sgu[c][0] = g | (u << 16);
+            b.sgu[h][c][0] = g | (u << 16);
         }
     }
 }
@@ -433,33 +463,58 @@ __device__ __forceinline__ size_t h_index(int i, int kgi) {
 // Computes one item from its loaded buffer: h = silu(g) * u for rows
 // [rb*R, rb*R + R), written as fp32 at their h_index positions.
 template <int KG, int F>
-__device__ __forceinline__ void gateup_compute(const GateUpBuf<KG, code_planes(F)>& b, int rb, int lane,
+__device__ __forceinline__ void gateup_compute(const GateUpBuf<KG, F>& b, int rb, int lane,
                                                const HI8 (&xa)[GateUpShape<KG>::CPL],
                                                const float (&xs)[GateUpShape<KG>::CPL], float* __restrict__ h_out,
                                                int kgi, bool store) {
     using S = GateUpShape<KG>;
+    constexpr int RP = row_pack(F);
+    constexpr int NV = S::NV * RP;  // gate then up; inside each, row parity then step
     const int row_sub = KG >= kWave ? 0 : (lane / KG);
-    float v[S::NV];
+    float v[NV];
 #pragma unroll
     for (int n = 0; n < S::NL; ++n) {
-        float ag = 0.0f, au = 0.0f;
+        if constexpr (F == kCodecInt2) {
+            float ag0 = 0.0f, ag1 = 0.0f, au0 = 0.0f, au1 = 0.0f;
 #pragma unroll
-        for (int c = 0; c < S::CPL; ++c) {
-            ag = fmaf(scale_at<F>(b.sgu[c], n) * xs[c], dot_planes<F>(b.cg[n][c], xa[c]), ag);
-            au = fmaf(scale_at<F>(b.sgu[c], S::NL + n) * xs[c], dot_planes<F>(b.cu[n][c], xa[c]), au);
+            for (int c = 0; c < S::CPL; ++c) {
+                float g0, g1, u0, u1;
+                dot_chunk_int2(b.cg[n][c][0], xa[c], g0, g1);
+                dot_chunk_int2(b.cu[n][c][0], xa[c], u0, u1);
+                ag0 = fmaf(scale_at<F>(b.sgu[0][c], n) * xs[c], g0, ag0);
+                ag1 = fmaf(scale_at<F>(b.sgu[RP - 1][c], n) * xs[c], g1, ag1);
+                au0 = fmaf(scale_at<F>(b.sgu[0][c], S::NL + n) * xs[c], u0, au0);
+                au1 = fmaf(scale_at<F>(b.sgu[RP - 1][c], S::NL + n) * xs[c], u1, au1);
+            }
+            v[n] = ag0;
+            v[S::NL + n] = ag1;
+            v[2 * S::NL + n] = au0;
+            v[3 * S::NL + n] = au1;
+        } else {
+            float ag = 0.0f, au = 0.0f;
+#pragma unroll
+            for (int c = 0; c < S::CPL; ++c) {
+                ag = fmaf(scale_at<F>(b.sgu[0][c], n) * xs[c], dot_planes<F>(b.cg[n][c], xa[c]), ag);
+                au = fmaf(scale_at<F>(b.sgu[0][c], S::NL + n) * xs[c], dot_planes<F>(b.cu[n][c], xa[c]), au);
+            }
+            v[n] = ag;
+            v[S::NL + n] = au;
         }
-        v[n] = ag;
-        v[S::NL + n] = au;
     }
-    const float r = reduce_scatter<S::NV, S::B>(v, lane);
-    // value index: top bit = matrix (0 gate, 1 up), low bits = row step n
-    const float other = partner_value<S::B - 1>(r, lane);
-    const int low_bits = S::B - ilog2(S::NV);
-    const int vi = (lane >> low_bits) & (S::NV - 1);
-    if (store && vi < S::NL && (lane & ((1 << low_bits) - 1)) == 0) {
+    const float r = reduce_scatter<NV, S::B>(v, lane);
+    // value index: top bit = matrix (0 gate, 1 up), then row parity, then step
+    // n.  partner_value may be a DPP mirror, which also flips the lower lane
+    // bits: harmless with one value per matrix, but with two row parities the
+    // up partner must be the exact lane xor.
+    const float other =
+        RP > 1 ? __shfl_xor(r, 1 << (S::B - 1)) : partner_value<S::B - 1>(r, lane);
+    const int low_bits = S::B - ilog2(NV);
+    const int vi = (lane >> low_bits) & (NV - 1);
+    if (store && vi < RP * S::NL && (lane & ((1 << low_bits) - 1)) == 0) {
         const float g = r, u = other;
         const float h = g / (1.0f + expf(-g)) * u;
-        h_out[h_index(rb * S::R + vi * S::RPL + row_sub, kgi)] = h;
+        const int n = vi % S::NL, parity = vi / S::NL;
+        h_out[h_index(RP * (rb * S::R + n * S::RPL + row_sub) + parity, kgi)] = h;
     }
 }
 
@@ -514,7 +569,7 @@ __device__ __forceinline__ void route_token(const DecodeArgs& a, int lane, int* 
 //  * the last block: the activations' integer operands for the routed
 //    experts' kernel.
 template <int KG>
-__host__ __device__ inline int shared_gateup_blocks(int I) {
+__host__ __device__ inline int shared_gateup_blocks(int I) {  // I: stored rows of gate
     const int per_slot = I / GateUpShape<KG>::R;
     return (per_slot + 4 * kSharedItemsPerRound - 1) / (4 * kSharedItemsPerRound);
 }
@@ -526,7 +581,7 @@ __global__ void __launch_bounds__(256) router_kernel(DecodeArgs a) {
     constexpr int NI = code_planes(F) > 1 ? 2 : kSharedItemsPerRound;
     const int lane = threadIdx.x & 63;
     const int wave = wave_in_block();
-    const int n_shared_blocks = a.S > 0 ? shared_gateup_blocks<KG>(a.I) : 0;
+    const int n_shared_blocks = a.S > 0 ? shared_gateup_blocks<KG>(a.I / row_pack(F)) : 0;
     const int n_router_blocks = router_blocks(a.E);
     const int b = blockIdx.x;
     if (b >= n_router_blocks + n_shared_blocks) {
@@ -540,12 +595,12 @@ __global__ void __launch_bounds__(256) router_kernel(DecodeArgs a) {
     }
     if (b >= n_router_blocks) {
         // shared expert gate/up: items of R rows, rounds of NI per wave
-        const int per_slot = a.I / S::R;
+        const int per_slot = a.I / row_pack(F) / S::R;
         const int wave_id = (b - n_router_blocks) * 4 + wave;
         const int n_waves = n_shared_blocks * 4;
         if (wave_id >= per_slot) return;
         const BlobLayout L = blob_layout(a.H, a.I, F);
-        GateUpBuf<KG, code_planes(F)> buf[NI];
+        GateUpBuf<KG, F> buf[NI];
 #pragma unroll
         for (int k = 0; k < NI; ++k) {
             const int it = wave_id + k * n_waves;
@@ -662,7 +717,7 @@ __global__ void __launch_bounds__(256) gateup_kernel(DecodeArgs a) {
     const int wave_id = blockIdx.x * 4 + wave;
     const int n_waves = gridDim.x * 4;
     const BlobLayout L = blob_layout(a.H, a.I, F);
-    const int per_slot = a.I / S::R;
+    const int per_slot = a.I / row_pack(F) / S::R;
     // With the router's kept-slot list (top-p cut) the items cover only the
     // kept slots; the list goes to this wave's LDS row.
     __shared__ int wave_kept[4][17];
@@ -697,7 +752,7 @@ __global__ void __launch_bounds__(256) gateup_kernel(DecodeArgs a) {
         asm volatile("" : "+v"(xa[c].he), "+v"(xa[c].ho), "+v"(xa[c].le), "+v"(xa[c].lo));
         asm volatile("" : "+v"(xa[c].corr), "+v"(xs[c]));
     }
-    GateUpBuf<KG, code_planes(F)> b[NI];
+    GateUpBuf<KG, F> b[NI];
 
     // item -> (slot, row block)
     auto slot_of = [&](int item) {
@@ -714,11 +769,11 @@ __global__ void __launch_bounds__(256) gateup_kernel(DecodeArgs a) {
     };
     auto rb_of = [&](int item) { return item % per_slot; };
     auto blob_of = [&](int slot) { return wave_blobs[wave][slot]; };
-    auto issue = [&](int item, GateUpBuf<KG, code_planes(F)>& buf) {
+    auto issue = [&](int item, GateUpBuf<KG, F>& buf) {
         const int it = item < n_items ? item : n_items - 1;
         gateup_issue<KG, F>(blob_of(slot_of(it)), L, rb_of(it), lane, buf);
     };
-    auto compute = [&](int item, const GateUpBuf<KG, code_planes(F)>& buf) {
+    auto compute = [&](int item, const GateUpBuf<KG, F>& buf) {
         const int it = item < n_items ? item : n_items - 1;
         gateup_compute<KG, F>(buf, rb_of(it), lane, xa, xs, a.h + (size_t)slot_of(it) * a.I, a.I / 32, item < n_items);
     };
@@ -812,7 +867,8 @@ __global__ void __launch_bounds__(576) down_combine_kernel(DecodeArgs a) {
     constexpr int MAXW = 9;
     constexpr int WIN = S::WIN;
     constexpr int NR = (S::NL + WIN - 1) / WIN;  // rounds
-    constexpr int NVP = pow2_at_least(S::NL);
+    constexpr int RP = row_pack(F);                  // matrix rows per stored row (int2: 2)
+    constexpr int NVP = pow2_at_least(S::NL * RP);
     const int lane = threadIdx.x & 63;
     const int slot = wave_in_block();
     const int K = a.K;
@@ -822,10 +878,10 @@ __global__ void __launch_bounds__(576) down_combine_kernel(DecodeArgs a) {
     const BlobLayout L = blob_layout(a.H, a.I, F);
     const uint8_t* blob = slot >= K ? a.shared_blob
                                     : (a.direct ? readlane_ptr(lane_pick(a.blobs, lane), slot) : a.slot_blobs[slot]);
-    __shared__ float part[MAXW][S::R];
+    __shared__ float part[MAXW][RP * S::R];  // [slot][row parity * R + stored row of the block]
     if (blob == nullptr) {
         // a routed slot that the top-p cut dropped: weight 0, nothing read
-        for (int t = lane; t < S::R; t += kWave) part[slot][t] = 0.0f;
+        for (int t = lane; t < RP * S::R; t += kWave) part[slot][t] = 0.0f;
     } else {
         auto code_off = [&](int step, int c) {
             const size_t row = (size_t)rb * S::R + step * S::RPL + row_sub;
@@ -846,12 +902,14 @@ __global__ void __launch_bounds__(576) down_combine_kernel(DecodeArgs a) {
         };
         __builtin_amdgcn_sched_barrier(0);
         issue_round(0);
-        unsigned sc[S::CPL][(S::NL + 1) / 2];
+        unsigned sc[RP][S::CPL][(S::NL + 1) / 2];
 #pragma unroll
-        for (int c = 0; c < S::CPL; ++c) {
-            const size_t si = ((size_t)rb * KG + g0 + kWave * c) * S::R + (size_t)row_sub * S::NL;
-            load_scales_c<F, S::NL>(blob + L.down_s + si * scale_bytes(F), sc[c]);
-        }
+        for (int h = 0; h < RP; ++h)
+#pragma unroll
+            for (int c = 0; c < S::CPL; ++c) {
+                const size_t si = ((size_t)rb * KG + g0 + kWave * c) * S::R + (size_t)row_sub * S::NL;
+                load_scales_c<F, S::NL>(blob + (h ? L.down_s2 : L.down_s) + si * scale_bytes(F), sc[h][c]);
+            }
         if constexpr (NR > 1) issue_round(1);
         __builtin_amdgcn_sched_barrier(0);
         HI8 ha[S::CPL];
@@ -865,11 +923,24 @@ __global__ void __launch_bounds__(576) down_combine_kernel(DecodeArgs a) {
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int n = r * WIN; n < (r + 1) * WIN && n < S::NL; ++n) {
-                float acc = 0.0f;
+                if constexpr (F == kCodecInt2) {
+                    float acc0 = 0.0f, acc1 = 0.0f;
 #pragma unroll
-                for (int c = 0; c < S::CPL; ++c)
-                    acc = fmaf(scale_at<F>(sc[c], n) * hscale[c], dot_planes<F>(code[n][c], ha[c]), acc);
-                v[n] = acc;
+                    for (int c = 0; c < S::CPL; ++c) {
+                        float d0, d1;
+                        dot_chunk_int2(code[n][c][0], ha[c], d0, d1);
+                        acc0 = fmaf(scale_at<F>(sc[0][c], n) * hscale[c], d0, acc0);
+                        acc1 = fmaf(scale_at<F>(sc[RP - 1][c], n) * hscale[c], d1, acc1);
+                    }
+                    v[n] = acc0;
+                    v[S::NL + n] = acc1;
+                } else {
+                    float acc = 0.0f;
+#pragma unroll
+                    for (int c = 0; c < S::CPL; ++c)
+                        acc = fmaf(scale_at<F>(sc[0][c], n) * hscale[c], dot_planes<F>(code[n][c], ha[c]), acc);
+                    v[n] = acc;
+                }
             }
             __builtin_amdgcn_sched_barrier(0);
             if (r + 2 < NR) issue_round(r + 2);
@@ -877,15 +948,17 @@ __global__ void __launch_bounds__(576) down_combine_kernel(DecodeArgs a) {
         const float r = reduce_scatter<NVP, S::B>(v, lane);
         const int low_bits = S::B - ilog2(NVP);
         const int vi = (lane >> low_bits) & (NVP - 1);
-        if ((lane & ((1 << low_bits) - 1)) == 0 && vi < S::NL) part[slot][vi * S::RPL + row_sub] = r;
+        // value index: row parity, then step
+        if ((lane & ((1 << low_bits) - 1)) == 0 && vi < RP * S::NL)
+            part[slot][(vi / S::NL) * S::R + (vi % S::NL) * S::RPL + row_sub] = r;
     }
     __syncthreads();
-    if ((int)threadIdx.x < S::R) {
+    if ((int)threadIdx.x < RP * S::R) {
         const int t = threadIdx.x;
         float y = 0.0f;
         for (int j = 0; j < K; ++j) y = fmaf(a.w[j], part[j][t], y);
         if (a.S > 0) y += part[K][t];
-        a.y[(size_t)rb * S::R + t] = y;
+        a.y[(size_t)RP * (rb * S::R + t % S::R) + t / S::R] = y;
     }
 }
 
@@ -906,7 +979,7 @@ hipError_t launch_kernel(K kernel, dim3 grid, dim3 block, hipStream_t st, const 
 template <int KG, int F>
 hipError_t launch_router_c(const DecodeArgs& a, hipStream_t st, const LaunchTiming& tm) {
     // router blocks, the shared expert's gate/up blocks, one conversion block
-    const dim3 grid(router_blocks(a.E) + (a.S > 0 ? shared_gateup_blocks<KG>(a.I) : 0) + 1);
+    const dim3 grid(router_blocks(a.E) + (a.S > 0 ? shared_gateup_blocks<KG>(a.I / row_pack(F)) : 0) + 1);
     if (a.E <= 64) return launch_kernel(router_kernel<KG, 1, F>, grid, dim3(256), st, tm, a);
     if (a.E <= 128) return launch_kernel(router_kernel<KG, 2, F>, grid, dim3(256), st, tm, a);
     return launch_kernel(router_kernel<KG, 4, F>, grid, dim3(256), st, tm, a);
@@ -915,12 +988,13 @@ template <int KG>
 hipError_t launch_router(const DecodeArgs& a, hipStream_t st, const LaunchTiming& tm) {
     if (a.codec == kCodecMxfp4) return launch_router_c<KG, kCodecMxfp4>(a, st, tm);
     if (a.codec == kCodecInt8) return launch_router_c<KG, kCodecInt8>(a, st, tm);
+    if (a.codec == kCodecInt2) return launch_router_c<KG, kCodecInt2>(a, st, tm);
     return launch_router_c<KG, kCodecInt4>(a, st, tm);
 }
 
 template <int KG>
 hipError_t launch_gateup(const DecodeArgs& a, hipStream_t st, const LaunchTiming& tm) {
-    const int per_slot = a.I / GateUpShape<KG>::R;
+    const int per_slot = a.I / row_pack(a.codec) / GateUpShape<KG>::R;
     const int n_slots = a.use_slot_list ? a.n_slot_list : a.K;
     if (n_slots == 0) return hipSuccess;
     const int items = n_slots * per_slot;
@@ -934,14 +1008,17 @@ hipError_t launch_gateup(const DecodeArgs& a, hipStream_t st, const LaunchTiming
         return launch_kernel(gateup_kernel<KG, kCodecMxfp4>, dim3(waves / 4), dim3(256), st, tm, a);
     if (a.codec == kCodecInt8)
         return launch_kernel(gateup_kernel<KG, kCodecInt8>, dim3(waves / 4), dim3(256), st, tm, a);
+    if (a.codec == kCodecInt2)
+        return launch_kernel(gateup_kernel<KG, kCodecInt2>, dim3(waves / 4), dim3(256), st, tm, a);
     return launch_kernel(gateup_kernel<KG, kCodecInt4>, dim3(waves / 4), dim3(256), st, tm, a);
 }
 
 template <int KG, int NLD, int F>
 hipError_t launch_down_c(const DecodeArgs& a, hipStream_t st, const LaunchTiming& tm) {
     using S = DownShape<KG, NLD>;
-    if constexpr (ilog2(pow2_at_least(S::NL)) <= S::B && S::NL * S::CPL * code_planes(F) <= kDownMaxLoads) {
-        const int grid = a.H / S::R;
+    if constexpr (ilog2(pow2_at_least(S::NL * row_pack(F))) <= S::B &&
+                  S::NL * S::CPL * code_planes(F) <= kDownMaxLoads) {
+        const int grid = a.H / row_pack(F) / S::R;
         return launch_kernel(down_combine_kernel<KG, NLD, F>, dim3(grid), dim3((a.K + a.S) * 64), st, tm, a);
     } else {
         return hipErrorInvalidValue;  // never chosen by down_rows
@@ -951,12 +1028,13 @@ template <int KG, int NLD>
 hipError_t launch_down_nl(const DecodeArgs& a, hipStream_t st, const LaunchTiming& tm) {
     if (a.codec == kCodecMxfp4) return launch_down_c<KG, NLD, kCodecMxfp4>(a, st, tm);
     if (a.codec == kCodecInt8) return launch_down_c<KG, NLD, kCodecInt8>(a, st, tm);
+    if (a.codec == kCodecInt2) return launch_down_c<KG, NLD, kCodecInt2>(a, st, tm);
     return launch_down_c<KG, NLD, kCodecInt4>(a, st, tm);
 }
 
 template <int KG>
 hipError_t launch_down(const DecodeArgs& a, hipStream_t st, const LaunchTiming& tm) {
-    const int nl = down_rows(a.H, KG, code_planes(a.codec)) / rows_per_load(KG);
+    const int nl = down_rows(a.H, KG, a.codec) / rows_per_load(KG);
     switch (nl) {
         case 1: return launch_down_nl<KG, 1>(a, st, tm);
         case 2: return launch_down_nl<KG, 2>(a, st, tm);
@@ -1016,7 +1094,9 @@ bool decode_shape_supported(int hidden, int inter, int top_k, int n_shared) {
     const int kh = hidden / 32, ki = inter / 32;
     const bool h_ok = kh == 8 || kh == 16 || kh == 32 || kh == 64 || kh == 128 || kh == 192 || kh == 256;
     const bool i_ok = ki == 4 || ki == 8 || ki == 16 || ki == 32 || ki == 64 || ki == 128;
-    return h_ok && i_ok && hidden % 256 == 0 && hidden % down_rows(hidden, ki, 1) == 0 && hidden % down_rows(hidden, ki, 2) == 0 &&
+    return h_ok && i_ok && hidden % 256 == 0 && hidden % down_rows(hidden, ki, kCodecInt4) == 0 &&
+           hidden % down_rows(hidden, ki, kCodecInt8) == 0 && (hidden / 2) % down_rows(hidden, ki, kCodecInt2) == 0 &&
+           (inter / 2) % gateup_rows(kh) == 0 &&
            inter % gateup_rows(kh) == 0 && top_k <= 8;
 }
 

@@ -14,6 +14,11 @@
 //   int8 only: gate, up and down planes of the low nibbles q & 15
 //       (unsigned), shaped as the high planes, so q = 16 hi + lo and every
 //       kernel keeps the int4 lane mapping with two loads per chunk.
+// Int2 matrices are stored as int4-shaped planes of half the rows: nibble
+// (virtual row p, column c) holds the codes of rows 2p (bits 0-1) and 2p + 1
+// (bits 2-3), each + 2, and the scales of the even and the odd rows go to
+// two arrays, each packed as an int4 matrix of rows/2 rows would be (the
+// odd rows' arrays follow the even rows' ones).
 // The blob is exactly as large as the public layout.
 #pragma once
 
@@ -29,9 +34,12 @@ constexpr int kWave = 64;
 constexpr int kCodecInt4 = 0;   // int4 codes, fp16 scale per 32 inputs
 constexpr int kCodecMxfp4 = 1;  // E2M1 codes, E8M0 scale per 32 inputs
 constexpr int kCodecInt8 = 2;   // int8 codes, fp16 scale per 32 inputs
+constexpr int kCodecInt2 = 3;   // int2 codes, fp16 scale per 32 inputs
 __host__ __device__ constexpr int scale_bytes(int codec) { return codec == kCodecMxfp4 ? 1 : 2; }
 // Nibble planes per matrix in the blob (int8: high and low nibbles).
 __host__ __device__ constexpr int code_planes(int codec) { return codec == kCodecInt8 ? 2 : 1; }
+// Matrix rows per stored (virtual) row (int2: two rows share a nibble).
+__host__ __device__ constexpr int row_pack(int codec) { return codec == kCodecInt2 ? 2 : 1; }
 // Rows of gate (and of up) per gate/up work item when a row fits in one
 // wave load or more.
 constexpr int kGateUpRowsBase = 1;
@@ -61,16 +69,19 @@ __host__ __device__ constexpr int pow2_at_least(int v) { return v <= 1 ? 1 : 2 *
 // wave's s x chunks_per_lane code loads stay within kDownMaxLoads and its s
 // row partials, rounded up to a power of two, fit the lanes that share a row
 // (min(inter/32, 64)).  With two nibble planes (int8) every step loads
-// twice as many chunks.
-__host__ __device__ inline int down_rows(int hidden, int kg_i, int planes) {
+// twice as many chunks; with two rows per stored row (int2) the rows are
+// stored rows (hidden / 2 of them) and every step yields two partials.
+__host__ __device__ inline int down_rows(int hidden, int kg_i, int codec) {
+    const int planes = code_planes(codec), rp = row_pack(codec);
+    const int vrows = hidden / rp;
     const int rpl = rows_per_load(kg_i);
     const int lanes_per_row = kg_i < kWave ? kg_i : kWave;
-    const int target = hidden / 256 > rpl ? hidden / 256 : rpl;
+    const int target = vrows / 256 > rpl ? vrows / 256 : rpl;
     for (int i = 0; i < 7; ++i) {
         const int steps = down_step_option(i);
         const int r = steps * rpl;
-        if (r <= target && hidden % r == 0 && steps * chunks_per_lane(kg_i) * planes <= kDownMaxLoads &&
-            pow2_at_least(steps) <= lanes_per_row)
+        if (r <= target && vrows % r == 0 && steps * chunks_per_lane(kg_i) * planes <= kDownMaxLoads &&
+            pow2_at_least(steps * rp) <= lanes_per_row)
             return r;
     }
     return rpl;
@@ -98,14 +109,15 @@ __host__ __device__ inline size_t gateup_scale_index(int r, int g, int m, int kg
 
 struct BlobLayout {
     size_t gate_q, up_q, down_q;     // byte offsets of the code arrays (int8: high-nibble planes)
-    size_t gu_s, down_s;             // byte offsets of the scale arrays
+    size_t gu_s, down_s;             // byte offsets of the scale arrays (int2: even rows)
     size_t gate_lo, up_lo, down_lo;  // int8 low-nibble planes (0 otherwise)
+    size_t gu_s2, down_s2;           // int2 scales of the odd rows (0 otherwise)
     size_t total;
 };
 
 __host__ __device__ inline BlobLayout blob_layout(int hidden, int inter, int codec) {
     BlobLayout L;
-    const size_t codes = (size_t)hidden * inter / 2;
+    const size_t codes = (size_t)hidden * inter / 2 / row_pack(codec);
     const size_t scales = (size_t)hidden * (inter / 32) * scale_bytes(codec);
     L.gate_q = 0;
     L.up_q = codes;
@@ -114,6 +126,13 @@ __host__ __device__ inline BlobLayout blob_layout(int hidden, int inter, int cod
     L.down_s = 3 * codes + 2 * scales;
     L.total = 3 * codes + 3 * scales;
     L.gate_lo = L.up_lo = L.down_lo = 0;
+    L.gu_s2 = L.down_s2 = 0;
+    if (codec == kCodecInt2) {
+        // even rows: gate/up then down, then the odd rows' arrays
+        L.down_s = L.gu_s + scales;
+        L.gu_s2 = L.down_s + scales / 2;
+        L.down_s2 = L.gu_s2 + scales;
+    }
     if (codec == kCodecInt8) {
         L.gate_lo = L.total;
         L.up_lo = L.total + codes;

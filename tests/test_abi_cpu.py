@@ -138,6 +138,37 @@ def test_pack_int8_splits_codes_into_nibble_planes():
     np.testing.assert_array_equal(np.sort(sc[2 * m:]), np.sort(ds.ravel()))
 
 
+def test_pack_int2_pairs_rows_in_nibbles():
+    """Int2 blob: stored row v holds rows 2v (bits 0-1) and 2v + 1 (bits 2-3)
+    of every column, each code + 2; the even and odd rows' scales are each a
+    permutation of the public ones."""
+    import dataclasses
+    cfg = dataclasses.replace(synth.TINY, codec="int2")
+    w = synth.gen_layer(cfg, seed=0)
+    nb = B.moe_expert_bytes(cfg)
+    assert nb == cfg.expert_bytes() == 3 * cfg.hidden * cfg.inter // 4 + 3 * cfg.hidden * cfg.inter // 16
+    blob = np.empty(nb, np.uint8)
+    B.moe_expert_pack(cfg, *w.expert_arrays(1), blob)
+    H, I = cfg.hidden, cfg.inter
+    n = H * I // 4
+    for m, (q, rows, cols) in enumerate(((w.gate_q[1], I, H), (w.up_q[1], I, H), (w.down_q[1], H, I))):
+        plane = blob[m * n:(m + 1) * n].reshape(rows // 2, cols // 2)
+        nib = np.stack([plane & 15, plane >> 4], axis=-1).reshape(rows // 2, cols).astype(np.int64)
+        f = np.stack([(q >> (2 * t)) & 3 for t in range(4)], axis=-1).reshape(rows, cols).astype(np.int64)
+        codes = np.where(f >= 2, f - 4, f)
+        np.testing.assert_array_equal((nib & 3) - 2, codes[0::2])
+        np.testing.assert_array_equal((nib >> 2) - 2, codes[1::2])
+    sc = blob[3 * n:].view(np.uint16)
+    gs, us, ds = w.gate_s[1], w.up_s[1], w.down_s[1]
+    g_ev, g_od = np.concatenate([gs[0::2].ravel(), us[0::2].ravel()]), np.concatenate([gs[1::2].ravel(), us[1::2].ravel()])
+    k = g_ev.size
+    d = ds.size // 2
+    np.testing.assert_array_equal(np.sort(sc[:k]), np.sort(g_ev))
+    np.testing.assert_array_equal(np.sort(sc[k:k + d]), np.sort(ds[0::2].ravel()))
+    np.testing.assert_array_equal(np.sort(sc[k + d:2 * k + d]), np.sort(g_od))
+    np.testing.assert_array_equal(np.sort(sc[2 * k + d:]), np.sort(ds[1::2].ravel()))
+
+
 def test_pack_rejects_null():
     code = B.lib().moe_expert_pack(B.MoeConfig.from_cfg(synth.TINY), None, None, None, None, None, None, None)
     assert code == B.MOE_EINVAL

@@ -238,7 +238,7 @@ def test_cache_top_p(torch_cuda):
     cache.close()
 
 
-@pytest.mark.parametrize("codec", ["mxfp4", "int8"])
+@pytest.mark.parametrize("codec", ["mxfp4", "int8", "int2"])
 def test_cache_other_codecs(torch_cuda, codec):
     """MXFP4 and int8 experts behind the cache: outputs equal the resident
     layer's one-token calls bit for bit, and the oracle's within tolerance;

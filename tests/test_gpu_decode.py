@@ -290,11 +290,11 @@ def with_codec(cfg, codec="mxfp4"):
     return dataclasses.replace(cfg, codec=codec)
 
 
-@pytest.mark.parametrize("codec", ["mxfp4", "int8"])
+@pytest.mark.parametrize("codec", ["mxfp4", "int8", "int2"])
 @pytest.mark.parametrize("cfg_name", ["TINY", "MID_A", "MID_B", "MID_C", "MID_D"])
 def test_codec_layer_parity(torch_cuda, cfg_name, codec):
-    """One-token calls of MXFP4 (E2M1 codes, E8M0 scales) and int8 layers
-    against the oracle, every lane mapping of the kernels."""
+    """One-token calls of MXFP4 (E2M1 codes, E8M0 scales), int8 and int2
+    layers against the oracle, every lane mapping of the kernels."""
     cfg = with_codec({"TINY": synth.TINY, "MID_A": MID_A, "MID_B": MID_B, "MID_C": MID_C, "MID_D": MID_D}[cfg_name],
                      codec)
     say(f"[gpu] {codec} layer parity {cfg_name}")
@@ -328,7 +328,7 @@ def test_mxfp4_extreme_scales_and_activations(torch_cuda):
             layer.close()
 
 
-@pytest.mark.parametrize("codec", ["mxfp4", "int8"])
+@pytest.mark.parametrize("codec", ["mxfp4", "int8", "int2"])
 def test_codec_batched_call_unsupported(torch_cuda, codec):
     from routed_expert_int4_amd.layer import DeviceLayer
     weights = synth.gen_layer(with_codec(synth.TINY, codec), seed=0)
@@ -408,4 +408,32 @@ def test_glm_int8_decode(torch_cuda):
     rows = sorted(set([0, 1, 100, 199] + list(np.argsort(gap)[:2])))
     res = check_layer(weights, x, y, ids, w, rows=rows)
     say(f"[gpu] GLM int8: {len(excused)} excused, sampled worst rel err {res['worst_rel']:.3g}")
+    layer.close()
+
+
+def test_glm_int2_decode(torch_cuda):
+    """GLM-shaped int2 layer (half the int4 code bytes, two rows per stored
+    row), 200 one-token calls: routing and sampled outputs against the oracle;
+    then top_p 0.7 on the same layer."""
+    cfg = with_codec(synth.GLM, "int2")
+    say("[gpu] generating the GLM-shaped int2 layer (seed 0)")
+    weights = synth.gen_layer(cfg, seed=0)
+    from routed_expert_int4_amd.layer import DeviceLayer
+    layer = DeviceLayer(weights, max_T=1)
+    x = synth.gen_tokens(cfg, 200, seed=1)
+    y, ids, w = layer.forward_each(DeviceLayer.to_device_bf16(x))
+    torch_cuda.cuda.synchronize()
+    y, ids, w = y.cpu().numpy(), ids.cpu().numpy(), w.cpu().numpy()
+    ids_ref, w_ref, gap = oracle.route(weights, x)
+    excused = check_routing(cfg, ids, w, ids_ref, w_ref, gap)
+    rows = sorted(set([0, 1, 100, 199] + list(np.argsort(gap)[:2])))
+    res = check_layer(weights, x, y, ids, w, rows=rows)
+    say(f"[gpu] GLM int2: {len(excused)} excused, sampled worst rel err {res['worst_rel']:.3g}")
+    layer.close()
+    wp = with_top_p(weights, 0.7)
+    layer = DeviceLayer(wp, max_T=1)
+    y, ids, w = layer.forward_each(DeviceLayer.to_device_bf16(x[:30]))
+    torch_cuda.cuda.synchronize()
+    res = check_layer(wp, x[:30], y.cpu().numpy(), ids.cpu().numpy(), w.cpu().numpy(), rows=[0, 29])
+    say(f"[gpu] GLM int2 top-p 0.7: worst rel err {res['worst_rel']:.3g}")
     layer.close()

@@ -77,10 +77,18 @@ typedef enum {
  *   exponent with bias 1, 1-bit mantissa: 0, 0.5, 1, 1.5, 2, 3, 4, 6 and
  *   their negatives), one E8M0 scale byte b = 2^(b-127) per group (b = 255,
  *   NaN, is refused by moe_expert_pack).  19.125 MiB per expert at hidden
- *   6144, inter 2048.  Served by the one-token path (T = 1 calls, and tokens
- *   behind an expert cache); T > 1 calls of an all-resident layer return
- *   MOE_EUNSUPPORTED. */
-enum { MOE_CODEC_INT4 = 0, MOE_CODEC_MXFP4 = 1 };
+ *   6144, inter 2048.
+ * MOE_CODEC_INT8, MOE_CODEC_INT2: the int8 and packed int2 widths of the
+ *   colibri summary's quantisation kernels ("Principales fonctionnalites"),
+ *   read as two's complement codes with the int4 codec's fp16 scale per 32
+ *   inputs: int8 one byte per weight (code arrays [inter][hidden] and
+ *   [hidden][inter]); int2 four codes per byte, column 4j + t in bits
+ *   [2t, 2t + 2) of byte j (code arrays [inter][hidden/4], [hidden][inter/4]),
+ *   values -2..1.
+ * MXFP4, int8 and int2 are served by the one-token path (T = 1 calls, and
+ * tokens behind an expert cache); T > 1 calls of an all-resident layer
+ * return MOE_EUNSUPPORTED. */
+enum { MOE_CODEC_INT4 = 0, MOE_CODEC_MXFP4 = 1, MOE_CODEC_INT8 = 2, MOE_CODEC_INT2 = 3 };
 
 typedef struct {
     int hidden;
@@ -92,7 +100,7 @@ typedef struct {
     int n_shared;
     float routed_scaling_factor;
     float top_p;
-    int codec; /* MOE_CODEC_INT4 or MOE_CODEC_MXFP4 (layout of the expert weights) */
+    int codec; /* MOE_CODEC_* (layout of the expert weights) */
 } moe_config_t;
 
 typedef struct moe_layer moe_layer_t;
@@ -113,12 +121,14 @@ const char* moe_last_error(void);
  * Weight value = fp32(scale) * code.
  *
  * With codec MOE_CODEC_MXFP4 the codes are E2M1 and the three scale arrays
- * hold uint8 E8M0 bytes with the same shapes.
+ * hold uint8 E8M0 bytes with the same shapes; MOE_CODEC_INT8 and
+ * MOE_CODEC_INT2 change the code arrays' widths as above (fp16 scales).
  *
  * moe_expert_bytes: size of one packed device blob (equal to the public
- * layout's size: 3*hidden*inter/2 + 3*hidden*inter/32 * scale bytes (2 for
- * int4, 1 for MXFP4); 21,233,664 (int4) or 20,054,016 (MXFP4) for hidden
- * 6144, inter 2048).  Returns 0 for an invalid config.
+ * layout's size: 3*hidden*inter * code bits / 8 + 3*hidden*inter/32 * scale
+ * bytes (2, or 1 for MXFP4); for hidden 6144, inter 2048: 21,233,664 (int4),
+ * 20,054,016 (MXFP4), 40,108,032 (int8), 11,796,480 (int2)).  Returns 0 for
+ * an invalid config.
  *
  * moe_expert_pack: host-only repack of one expert from the public layout
  * (host pointers) into the blob format the kernels read (host buffer of

@@ -720,12 +720,15 @@ __global__ void __launch_bounds__(256) gateup_kernel(DecodeArgs a) {
     const int per_slot = a.I / row_pack(F) / S::R;
     // With the router's kept-slot list (top-p cut) the items cover only the
     // kept slots; the list goes to this wave's LDS row.
+    // (the slot count from the arguments first, so that all argument loads
+    // go out together before the kept-list branch)
     __shared__ int wave_kept[4][17];
+    int n_routed_slots = a.use_slot_list ? a.n_slot_list : a.K;
     if (a.kept) {
         if (lane < 17) wave_kept[wave][lane] = lane <= a.K ? a.kept[lane] : 0;
         __builtin_amdgcn_wave_barrier();
+        n_routed_slots = wave_kept[wave][0];
     }
-    const int n_routed_slots = a.kept ? wave_kept[wave][0] : (a.use_slot_list ? a.n_slot_list : a.K);
     const int n_items = n_routed_slots * per_slot;
     if (wave_id >= n_items) return;
 
@@ -879,6 +882,11 @@ __global__ void __launch_bounds__(576) down_combine_kernel(DecodeArgs a) {
     const uint8_t* blob = slot >= K ? a.shared_blob
                                     : (a.direct ? readlane_ptr(lane_pick(a.blobs, lane), slot) : a.slot_blobs[slot]);
     __shared__ float part[MAXW][RP * S::R];  // [slot][row parity * R + stored row of the block]
+    // h does not depend on the blob: its loads go out before the blob
+    // pointer arrives (a dropped slot's h is stale workspace and unused)
+    float hraw[S::CPL][32];
+    load_h<S::CPL, KG>(a.h + (size_t)slot * a.I, g0, hraw);
+    asm volatile("" ::: "memory");  // keeps the h loads here (not sunk into the branch)
     if (blob == nullptr) {
         // a routed slot that the top-p cut dropped: weight 0, nothing read
         for (int t = lane; t < RP * S::R; t += kWave) part[slot][t] = 0.0f;
@@ -887,8 +895,6 @@ __global__ void __launch_bounds__(576) down_combine_kernel(DecodeArgs a) {
             const size_t row = (size_t)rb * S::R + step * S::RPL + row_sub;
             return (row * KG + g0 + kWave * c) * 16;
         };
-        float hraw[S::CPL][32];
-        load_h<S::CPL, KG>(a.h + (size_t)slot * a.I, g0, hraw);
         constexpr int P = code_planes(F);
         u32x4 code[S::NL][S::CPL][P];
         auto issue_round = [&](int r) {

@@ -66,8 +66,8 @@ typedef enum {
  * expert is kept when the shares ranked before it sum to less than top_p,
  * the kept weights are rsf * s_j / sum_kept s, and a dropped slot reports id
  * -1 and weight 0 and is never read.  top_p = 1 is plain top-k.  top_p < 1 is
- * served by the one-token path (T = 1 calls, and tokens behind an expert
- * cache); T > 1 calls of an all-resident layer return MOE_EUNSUPPORTED. */
+ * served by the one-token kernels: a T > 1 call runs as T one-token passes
+ * (no batch union). */
 /* Expert weight codecs.  Both hold 32-input scale groups and two 4-bit codes
  * per byte (even column in the low nibble).
  * MOE_CODEC_INT4: two's complement int4 codes, fp16 scales (the layer's
@@ -85,9 +85,9 @@ typedef enum {
  *   [hidden][inter]); int2 four codes per byte, column 4j + t in bits
  *   [2t, 2t + 2) of byte j (code arrays [inter][hidden/4], [hidden][inter/4]),
  *   values -2..1.
- * MXFP4, int8 and int2 are served by the one-token path (T = 1 calls, and
- * tokens behind an expert cache); T > 1 calls of an all-resident layer
- * return MOE_EUNSUPPORTED. */
+ * MXFP4, int8 and int2 are served by the one-token kernels: a T > 1 call
+ * runs as T one-token passes (no batch union); the batched (batch-union,
+ * matrix-core) kernels are int4 only. */
 enum { MOE_CODEC_INT4 = 0, MOE_CODEC_MXFP4 = 1, MOE_CODEC_INT8 = 2, MOE_CODEC_INT2 = 3 };
 
 typedef struct {

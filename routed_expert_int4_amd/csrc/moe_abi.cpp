@@ -488,8 +488,8 @@ moe_status_t moe_router_topk(moe_layer_t* layer, const uint16_t* d_x, int T, int
     if (T > 0 && (!d_ids || !d_w)) return fail(MOE_EINVAL, "moe_router_topk: NULL ids or w");
     hipStream_t s = static_cast<hipStream_t>(stream);
     const moe_config_t& c = layer->cfg;
-    if (T > 1) {
-        if (c.top_p < 1.0f) return fail(MOE_EUNSUPPORTED, "moe_router_topk: top_p < 1 needs T = 1 calls");
+    if (T > 1 && !(c.top_p < 1.0f)) {
+        // (with the top-p cut the tokens take the one-token router below)
         const int tb = layer->W.batch_tokens;
         for (int t0 = 0; t0 < T; t0 += tb) {
             const int n = T - t0 < tb ? T - t0 : tb;
@@ -521,10 +521,10 @@ moe_status_t moe_layer_forward(moe_layer_t* layer, const uint16_t* d_x, int T, f
     const moe_config_t& c = layer->cfg;
     int32_t* ids_base = d_ids ? d_ids : reinterpret_cast<int32_t*>(layer->ws + layer->W.ids);
     float* w_base = d_w ? d_w : reinterpret_cast<float*>(layer->ws + layer->W.w);
-    if (T > 1 && !layer->cache) {
-        if (c.top_p < 1.0f) return fail(MOE_EUNSUPPORTED, "moe_layer_forward: top_p < 1 needs T = 1 calls");
-        if (c.codec != kCodecInt4)
-            return fail(MOE_EUNSUPPORTED, "moe_layer_forward: MXFP4, int8 and int2 experts need T = 1 calls");
+    // The batched kernels cover int4 experts with plain top-k; T > 1 calls
+    // with the top-p cut or another codec (and every call behind an expert
+    // cache) run as T one-token passes below.
+    if (T > 1 && !layer->cache && !(c.top_p < 1.0f) && c.codec == kCodecInt4) {
         // batch union: every distinct expert of a launch sequence is read once
         const int tb = layer->W.batch_tokens;
         for (int t0 = 0; t0 < T; t0 += tb) {

@@ -245,20 +245,21 @@ def test_top_p_one_is_plain_top_k(torch_cuda):
     l2.close()
 
 
-def test_top_p_batched_call_unsupported(torch_cuda):
-    """T > 1 calls of an all-resident layer with top_p < 1 are refused."""
+def test_top_p_batched_call_runs_per_token(torch_cuda):
+    """A T > 1 call with top_p < 1 runs as T one-token passes: outputs, ids
+    and weights bit-identical to T separate calls, for the layer forward and
+    for router_topk."""
     from routed_expert_int4_amd.layer import DeviceLayer
     weights = with_top_p(synth.gen_layer(synth.TINY, seed=0), 0.5)
     layer = DeviceLayer(weights, max_T=4)
     x = DeviceLayer.to_device_bf16(synth.gen_tokens(synth.TINY, 4, seed=1))
-    with pytest.raises(B.MoeError) as ei:
-        layer.forward(x)
-    assert ei.value.code == B.MOE_EUNSUPPORTED
-    with pytest.raises(B.MoeError) as ei:
-        layer.router_topk(x)
-    assert ei.value.code == B.MOE_EUNSUPPORTED
-    y, ids, w = layer.forward(x[:1])
+    y, ids, w = layer.forward(x)
+    y1, ids1, w1 = layer.forward_each(x)
+    ids_r, w_r = layer.router_topk(x)
     torch_cuda.cuda.synchronize()
+    assert torch_cuda.equal(y, y1) and torch_cuda.equal(ids, ids1) and torch_cuda.equal(w, w1)
+    assert torch_cuda.equal(ids_r, ids1) and torch_cuda.equal(w_r, w1)
+    assert (ids1 < 0).any()
     layer.close()
 
 
@@ -329,16 +330,21 @@ def test_mxfp4_extreme_scales_and_activations(torch_cuda):
 
 
 @pytest.mark.parametrize("codec", ["mxfp4", "int8", "int2"])
-def test_codec_batched_call_unsupported(torch_cuda, codec):
+def test_codec_batched_call_runs_per_token(torch_cuda, codec):
+    """A T > 1 call of an MXFP4, int8 or int2 layer runs as T one-token
+    passes: bit-identical to T separate calls, and within the oracle's
+    tolerance."""
     from routed_expert_int4_amd.layer import DeviceLayer
-    weights = synth.gen_layer(with_codec(synth.TINY, codec), seed=0)
-    layer = DeviceLayer(weights, max_T=4)
-    x = DeviceLayer.to_device_bf16(synth.gen_tokens(synth.TINY, 4, seed=1))
-    with pytest.raises(B.MoeError) as ei:
-        layer.forward(x)
-    assert ei.value.code == B.MOE_EUNSUPPORTED
-    layer.forward(x[:1])
+    cfg = with_codec(synth.TINY, codec)
+    weights = synth.gen_layer(cfg, seed=0)
+    layer = DeviceLayer(weights, max_T=5)
+    xb = synth.gen_tokens(cfg, 5, seed=1)
+    x = DeviceLayer.to_device_bf16(xb)
+    y, ids, w = layer.forward(x)
+    y1, ids1, w1 = layer.forward_each(x)
     torch_cuda.cuda.synchronize()
+    assert torch_cuda.equal(y, y1) and torch_cuda.equal(ids, ids1) and torch_cuda.equal(w, w1)
+    check_layer(weights, xb, y.cpu().numpy(), ids.cpu().numpy(), w.cpu().numpy())
     layer.close()
 
 

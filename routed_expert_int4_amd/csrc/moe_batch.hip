@@ -54,14 +54,26 @@ __device__ __forceinline__ unsigned pack_h2(_Float16 lo, _Float16 hi) {
 
 // 8 offset-binary codes of one dword (columns 8q..8q+7 of a group, column c
 // at bits 4c) -> fp16 values in fragment order (columns 0,4,1,5,2,6,3,7).
-__device__ __forceinline__ f16x8 codes_to_f16x8(unsigned w) {
+// The two exponent patterns OR-ed into the masked codes, held in VGPRs (see
+// magic_exponents) so that each mask-and-or is one v_and_or_b32: a VOP3
+// instruction here can take one scalar or literal operand, not two.
+struct MagicExp {
+    unsigned e1024, e64;  // 0x6400 (1024.0) and 0x5400 (64.0) in both halves
+};
+__device__ __forceinline__ MagicExp magic_exponents() {
+    MagicExp m{0x64006400u, 0x54005400u};
+    asm volatile("" : "+v"(m.e1024), "+v"(m.e64));
+    return m;
+}
+
+__device__ __forceinline__ f16x8 codes_to_f16x8(unsigned w, const MagicExp& mg) {
     const f16x2 k_lo = {(_Float16)1032.0f, (_Float16)1032.0f};  // 1024 + 8
     const f16x2 k_hi = {(_Float16)72.0f, (_Float16)72.0f};      // 64 + 8
     const unsigned w8 = w >> 8;
-    const f16x2 q0 = as_h2((w & 0x000F000Fu) | 0x64006400u) - k_lo;
-    const f16x2 q1 = as_h2((w & 0x00F000F0u) | 0x54005400u) - k_hi;
-    const f16x2 q2 = as_h2((w8 & 0x000F000Fu) | 0x64006400u) - k_lo;
-    const f16x2 q3 = as_h2((w8 & 0x00F000F0u) | 0x54005400u) - k_hi;
+    const f16x2 q0 = as_h2((w & 0x000F000Fu) | mg.e1024) - k_lo;
+    const f16x2 q1 = as_h2((w & 0x00F000F0u) | mg.e64) - k_hi;
+    const f16x2 q2 = as_h2((w8 & 0x000F000Fu) | mg.e1024) - k_lo;
+    const f16x2 q3 = as_h2((w8 & 0x00F000F0u) | mg.e64) - k_hi;
     const u32x4 v = {__builtin_bit_cast(unsigned, q0), __builtin_bit_cast(unsigned, q1),
                      __builtin_bit_cast(unsigned, q2), __builtin_bit_cast(unsigned, q3)};
     return __builtin_bit_cast(f16x8, v);
@@ -363,6 +375,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) b
     const int items = n_tiles * rblocks;
     const BlobLayout L = blob_layout(a.H, a.I, kCodecInt4);  // int4 only
     const int row_bytes = a.H / 2;
+    const MagicExp mg = magic_exponents();
     int gs = 0;  // stages so far: selects the LDS buffer
     for (int item = blockIdx.x; item < items; item += gridDim.x) {
         const int tile = item / rblocks, rb = item - tile * rblocks;
@@ -438,8 +451,8 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) b
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
                     const f16x8 af = __builtin_bit_cast(f16x8, xs[buf][((4 * c + m) * 4 + q) * 16 + i]);
-                    const f32x4 dg = mfma16(af, codes_to_f16x8(cg0[m]), zero);
-                    const f32x4 du = mfma16(af, codes_to_f16x8(cu0[m]), zero);
+                    const f32x4 dg = mfma16(af, codes_to_f16x8(cg0[m], mg), zero);
+                    const f32x4 du = mfma16(af, codes_to_f16x8(cu0[m], mg), zero);
                     const float sg = half_bits_to_float(sc0[m] & 0xFFFFu);
                     const float su = half_bits_to_float(sc0[m] >> 16);
 #pragma unroll
@@ -542,6 +555,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) b
     const int items = n_tiles * rblocks;
     const BlobLayout L = blob_layout(a.H, a.I, kCodecInt4);  // int4 only
     const int row_bytes = a.I / 2;
+    const MagicExp mg = magic_exponents();
     int gs = 0;
     for (int item = blockIdx.x; item < items; item += gridDim.x) {
         const int tile = item / rblocks, rb = item - tile * rblocks;
@@ -594,7 +608,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) b
                     const int slot = ((4 * c + m) * 4 + q) * 16 + i;
                     const f16x8 ah = __builtin_bit_cast(f16x8, hs[buf][slot]);
                     const f16x8 al = __builtin_bit_cast(f16x8, hs[buf][PART + slot]);
-                    const f16x8 bw = codes_to_f16x8(cd0[m]);
+                    const f16x8 bw = codes_to_f16x8(cd0[m], mg);
                     const f32x4 d = mfma16(al, bw, mfma16(ah, bw, zero));
                     const float s = half_bits_to_float(sc0[m]);
 #pragma unroll

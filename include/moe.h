@@ -65,9 +65,8 @@ typedef enum {
  * ranked by their share s_j / sum_selected s (ties to the lower index), an
  * expert is kept when the shares ranked before it sum to less than top_p,
  * the kept weights are rsf * s_j / sum_kept s, and a dropped slot reports id
- * -1 and weight 0 and is never read.  top_p = 1 is plain top-k.  top_p < 1 is
- * served by the one-token kernels: a T > 1 call runs as T one-token passes
- * (no batch union). */
+ * -1 and weight 0 and is never read (the batch-union dispatch gives it no
+ * entry).  top_p = 1 is plain top-k. */
 /* Expert weight codecs.  Both hold 32-input scale groups and two 4-bit codes
  * per byte (even column in the low nibble).
  * MOE_CODEC_INT4: two's complement int4 codes, fp16 scales (the layer's

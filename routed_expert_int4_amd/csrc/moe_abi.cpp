@@ -465,6 +465,7 @@ BatchArgs batch_args(moe_layer_t* L, const uint16_t* x, int n, int32_t* ids, flo
     b.down_p = down_rows(c.hidden, c.inter / 32, kCodecInt4);
     b.router_splits = batch_router_splits(c.hidden);
     b.rsf = c.routed_scaling_factor;
+    b.top_p = c.top_p;
     return b;
 }
 
@@ -488,8 +489,7 @@ moe_status_t moe_router_topk(moe_layer_t* layer, const uint16_t* d_x, int T, int
     if (T > 0 && (!d_ids || !d_w)) return fail(MOE_EINVAL, "moe_router_topk: NULL ids or w");
     hipStream_t s = static_cast<hipStream_t>(stream);
     const moe_config_t& c = layer->cfg;
-    if (T > 1 && !(c.top_p < 1.0f)) {
-        // (with the top-p cut the tokens take the one-token router below)
+    if (T > 1) {
         const int tb = layer->W.batch_tokens;
         for (int t0 = 0; t0 < T; t0 += tb) {
             const int n = T - t0 < tb ? T - t0 : tb;
@@ -521,10 +521,10 @@ moe_status_t moe_layer_forward(moe_layer_t* layer, const uint16_t* d_x, int T, f
     const moe_config_t& c = layer->cfg;
     int32_t* ids_base = d_ids ? d_ids : reinterpret_cast<int32_t*>(layer->ws + layer->W.ids);
     float* w_base = d_w ? d_w : reinterpret_cast<float*>(layer->ws + layer->W.w);
-    // The batched kernels cover int4 experts with plain top-k; T > 1 calls
-    // with the top-p cut or another codec (and every call behind an expert
-    // cache) run as T one-token passes below.
-    if (T > 1 && !layer->cache && !(c.top_p < 1.0f) && c.codec == kCodecInt4) {
+    // The batched kernels cover int4 experts (with or without the top-p
+    // cut); T > 1 calls with another codec, and every call behind an expert
+    // cache, run as T one-token passes below.
+    if (T > 1 && !layer->cache && c.codec == kCodecInt4) {
         // batch union: every distinct expert of a launch sequence is read once
         const int tb = layer->W.batch_tokens;
         for (int t0 = 0; t0 < T; t0 += tb) {

@@ -191,7 +191,7 @@ __global__ void __launch_bounds__(256) batch_topk_kernel(BatchArgs a, int conver
     }
     int id;
     float wt;
-    wave_group_topk_values<EPL>(sv, key, a.E, a.G, a.TG, a.K, a.rsf, 1.0f, lane, &id, &wt);
+    wave_group_topk_values<EPL>(sv, key, a.E, a.G, a.TG, a.K, a.rsf, a.top_p, lane, &id, &wt);
     if (lane < a.K) {
         a.ids[(size_t)t * a.K + lane] = id;
         a.w[(size_t)t * a.K + lane] = wt;
@@ -259,10 +259,13 @@ __global__ void __launch_bounds__(1024) batch_dispatch_kernel(BatchArgs a) {
     const int n = a.T * a.K;
     int n2 = kWave;
     while (n2 < n) n2 <<= 1;
-    for (int i = tid; i < n2; i += 1024) keys[i] = i < n ? (((unsigned)a.ids[i] << 16) | (unsigned)i) : 0xFFFFFFFFu;
+    // a dropped choice (id -1, top-p cut) sorts to the end with the padding
+    for (int i = tid; i < n2; i += 1024)
+        keys[i] = i < n && a.ids[i] >= 0 ? (((unsigned)a.ids[i] << 16) | (unsigned)i) : 0xFFFFFFFFu;
     if (tid < 256) cnt[tid] = 0;
     __syncthreads();
-    for (int i = tid; i < n; i += 1024) atomicAdd(&cnt[a.ids[i]], 1);
+    for (int i = tid; i < n; i += 1024)
+        if (a.ids[i] >= 0) atomicAdd(&cnt[a.ids[i]], 1);
     for (int k = 2; k <= n2; k <<= 1) {
         for (int j = k >> 1; j > 0; j >>= 1) {
             __syncthreads();
@@ -316,10 +319,19 @@ __global__ void __launch_bounds__(1024) batch_dispatch_kernel(BatchArgs a) {
         }
     }
     __syncthreads();
+    // kept entries fill pairs [0, totals[0]); the rest of perm is -1 and a
+    // dropped choice's inv is -1
+    const int n_kept = totals[0];
+    for (int i = tid; i < n; i += 1024)
+        if (a.ids[i] < 0) a.inv[i] = -1;
     for (int p = tid; p < n; p += 1024) {
-        const int idx = (int)(keys[p] & 0xFFFFu);
-        a.perm[p] = idx;
-        a.inv[idx] = p;
+        if (p < n_kept) {
+            const int idx = (int)(keys[p] & 0xFFFFu);
+            a.perm[p] = idx;
+            a.inv[idx] = p;
+        } else {
+            a.perm[p] = -1;
+        }
     }
     for (int e = tid; e < a.E; e += 1024) {
         const int c = cnt[e];
@@ -332,7 +344,7 @@ __global__ void __launch_bounds__(1024) batch_dispatch_kernel(BatchArgs a) {
         }
     }
     if (tid == 0) {
-        a.offsets[a.E] = n;
+        a.offsets[a.E] = n_kept;
         a.n_distinct[0] = totals[2];
         int nt = totals[1];
         for (int s = 0; s < a.S; ++s)
@@ -494,6 +506,7 @@ template <int CPT>
 __global__ void __launch_bounds__(256) batch_hprep_kernel(BatchArgs a) {
     __shared__ unsigned wmax[4];
     const int p = blockIdx.x, tid = threadIdx.x;
+    if (p >= a.offsets[a.E] && p < a.T * a.K) return;  // a pair left empty by the top-p cut
     const int n_el = (a.I / 32) * 4;  // (group, quarter) elements of 8 values
     const float* hr = a.h + (size_t)p * a.I;
     f32x4 v[CPT][2];
@@ -643,15 +656,16 @@ __global__ void __launch_bounds__(256) batch_combine_kernel(BatchArgs a) {
     const float* dj[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-        wj[j] = j < a.K ? a.w[(size_t)t * a.K + j] : 0.0f;
-        dj[j] = j < a.K ? a.d + (size_t)a.inv[(size_t)t * a.K + j] * a.H : nullptr;
+        const int pr = j < a.K ? a.inv[(size_t)t * a.K + j] : -1;  // -1: dropped by top-p
+        wj[j] = pr >= 0 ? a.w[(size_t)t * a.K + j] : 0.0f;
+        dj[j] = pr >= 0 ? a.d + (size_t)pr * a.H : nullptr;
     }
     const float* dsh = a.S > 0 ? a.d + (size_t)(a.T * a.K + t) * a.H : nullptr;
     {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            if (j < a.K) {
+            if (dj[j]) {
                 const f32x4 v = *as_global<f32x4>(dj[j] + r);
 #pragma unroll
                 for (int z = 0; z < 4; ++z) acc[z] = fmaf(wj[j], v[z], acc[z]);

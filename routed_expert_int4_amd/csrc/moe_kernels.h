@@ -94,8 +94,8 @@ struct BatchArgs {
     float* w;                    // [T][K]
     int32_t* counts;             // [E]
     int32_t* offsets;            // [E + 1]
-    int32_t* perm;               // [T*K] pair -> token*K + slot
-    int32_t* inv;                // [T*K] token*K + slot -> pair
+    int32_t* perm;               // [T*K] pair -> token*K + slot (-1 past the kept entries)
+    int32_t* inv;                // [T*K] token*K + slot -> pair (-1 for a dropped choice)
     int32_t* distinct;           // [E] experts with at least one entry, ascending
     int32_t* n_distinct;         // [1]
     Tile* tiles;                 // [max_tiles]
@@ -110,6 +110,7 @@ struct BatchArgs {
     int down_p;                  // row-block size of the down scale packing
     int router_splits;           // column splits of the router (power of two, hidden % (64 * splits) == 0)
     float rsf;
+    float top_p;                 // adaptive expert top-p (1: plain top-k); dropped choices get id -1
 };
 
 // Upper bound of the tiles of a call of T tokens.

@@ -76,7 +76,8 @@ def dispatch_layer(torch_cuda):
 
 
 @pytest.mark.parametrize("T,kind", [(1, "uniform"), (2, "uniform"), (32, "zipf"), (37, "uniform"), (512, "uniform"),
-                                    (1024, "uniform"), (1024, "zipf"), (300, "same")])
+                                    (1024, "uniform"), (1024, "zipf"), (300, "same"), (200, "dropped"),
+                                    (3, "all_dropped_but_one")])
 def test_dispatch_matches_oracle(torch_cuda, dispatch_layer, T, kind):
     say(f"[gpu] dispatch T={T} {kind}")
     E, k = MID_D.n_experts, MID_D.top_k
@@ -88,6 +89,10 @@ def test_dispatch_matches_oracle(torch_cuda, dispatch_layer, T, kind):
         ids = np.stack([rng.choice(E, k, replace=False, p=p / p.sum()) for _ in range(T)]).astype(np.int32)
     else:
         ids = np.stack([rng.choice(E, k, replace=False) for _ in range(T)]).astype(np.int32)
+    if kind == "dropped":  # choices dropped by a top-p cut carry id -1
+        ids[rng.random(ids.shape) < 0.3] = -1
+    if kind == "all_dropped_but_one":
+        ids[:, 1:] = -1
     got = gpu_dispatch(torch_cuda, dispatch_layer, ids)
     ref = oracle_dispatch(ids, E)
     for key in ("counts", "offsets", "perm", "distinct"):
@@ -214,4 +219,33 @@ def test_glm_prefill512(torch_cuda, glm_zipf):
     counts = np.bincount(ids.reshape(-1), minlength=256)
     say(f"[gpu] GLM prefill: {int((counts > 0).sum())} distinct experts, max {counts.max()} tokens/expert, "
         f"{len(excused)} excused, worst rel err {res['worst_rel']:.3g}")
+    layer.close()
+
+
+# ---------------------------------------------------------------- adaptive top-p
+@pytest.mark.parametrize("cfg_name,T,top_p", [("TINY", 13, 0.5), ("MID_A", 37, 0.8), ("MID_B", 16, 0.6),
+                                              ("MID_D", 100, 0.3)])
+def test_batch_top_p_parity(torch_cuda, cfg_name, T, top_p):
+    """Batch-union calls with the top-p cut: ids (-1 where dropped), weights
+    and outputs against the oracle (tokens whose top-p margin is below 1e-6
+    excused and re-checked on the GPU's ids); router_topk gives the same
+    routing as the layer call."""
+    import dataclasses
+    from routed_expert_int4_amd.layer import DeviceLayer
+    cfg = {"TINY": synth.TINY, "MID_A": MID_A, "MID_B": MID_B, "MID_D": MID_D}[cfg_name]
+    cfg = dataclasses.replace(cfg, top_p=top_p)
+    say(f"[gpu] batched top-p {top_p} {cfg_name} T={T}")
+    weights = synth.gen_layer(cfg, seed=0)
+    layer = DeviceLayer(weights, max_T=T)
+    x = synth.gen_tokens(cfg, T, seed=3)
+    y, ids, w = run_batch(torch_cuda, layer, x)
+    res = check_layer(weights, x, y, ids, w)
+    ids_r, w_r = layer.router_topk(DeviceLayer.to_device_bf16(x))
+    torch_cuda.cuda.synchronize()
+    np.testing.assert_array_equal(ids_r.cpu().numpy(), ids)
+    np.testing.assert_array_equal(w_r.cpu().numpy(), w)
+    dropped = int((ids < 0).sum())
+    say(f"[gpu] batched top-p {cfg_name}: dropped {dropped}/{ids.size}, worst rel err {res['worst_rel']:.3g}, "
+        f"excused {res['excused']}")
+    assert dropped > 0
     layer.close()

@@ -245,24 +245,6 @@ def test_top_p_one_is_plain_top_k(torch_cuda):
     l2.close()
 
 
-def test_top_p_batched_call_runs_per_token(torch_cuda):
-    """A T > 1 call with top_p < 1 runs as T one-token passes: outputs, ids
-    and weights bit-identical to T separate calls, for the layer forward and
-    for router_topk."""
-    from routed_expert_int4_amd.layer import DeviceLayer
-    weights = with_top_p(synth.gen_layer(synth.TINY, seed=0), 0.5)
-    layer = DeviceLayer(weights, max_T=4)
-    x = DeviceLayer.to_device_bf16(synth.gen_tokens(synth.TINY, 4, seed=1))
-    y, ids, w = layer.forward(x)
-    y1, ids1, w1 = layer.forward_each(x)
-    ids_r, w_r = layer.router_topk(x)
-    torch_cuda.cuda.synchronize()
-    assert torch_cuda.equal(y, y1) and torch_cuda.equal(ids, ids1) and torch_cuda.equal(w, w1)
-    assert torch_cuda.equal(ids_r, ids1) and torch_cuda.equal(w_r, w1)
-    assert (ids1 < 0).any()
-    layer.close()
-
-
 def test_glm_top_p_decode(torch_cuda, glm):
     """GLM-shaped layer, top_p 0.7, 200 one-token calls: routing of every
     token against the oracle, outputs on a sample."""

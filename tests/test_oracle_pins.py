@@ -378,6 +378,17 @@ def test_dispatch_hand_example():
     assert r["distinct"].tolist() == [0, 2, 3]
 
 
+def test_dispatch_hand_example_with_dropped_choices():
+    from oracle.dispatch import dispatch
+    # the same routing with entries (0,1) and (2,0) dropped by a top-p cut
+    ids = np.array([[2, -1], [0, 3], [-1, 0]])
+    r = dispatch(ids, 4)
+    assert r["counts"].tolist() == [2, 0, 1, 1]
+    assert r["offsets"].tolist() == [0, 2, 2, 3, 4]
+    assert r["perm"].tolist() == [2, 5, 0, 3, -1, -1]
+    assert r["distinct"].tolist() == [0, 2, 3]
+
+
 def test_dispatch_invariants_random():
     from oracle.dispatch import dispatch
     rng = np.random.default_rng(5)

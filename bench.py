@@ -326,7 +326,12 @@ def bench_batched(args) -> int:
     from routed_expert_int4_amd.layer import DeviceLayer
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
-    cfg = synth.GLM
+    import dataclasses
+    if args.codec not in ("int4", "mxfp4"):
+        print(f"bench.py: --workload {args.workload} runs the batched kernels, which serve int4 and mxfp4 experts",
+              file=sys.stderr)
+        return 2
+    cfg = dataclasses.replace(synth.GLM, codec=args.codec, top_p=args.top_p)
     if args.workload == "batch32":
         n_calls, T, seed = 32, 32, 4
         log("generating the GLM-shaped layer (seed 0) with the Zipf(1.1) bias")
@@ -364,11 +369,13 @@ def bench_batched(args) -> int:
     torch.cuda.synchronize()
     ms_per_step = e0.elapsed_time(e1) / args.steps
     ids_h = ids.cpu().numpy().reshape(n_calls, T, k)
-    distinct = [len(np.unique(ids_h[c])) for c in range(n_calls)]
+    # (id -1: a choice the top-p cut dropped; it is neither read nor computed)
+    distinct = [len(np.unique(ids_h[c][ids_h[c] >= 0])) for c in range(n_calls)]
     eb = cfg.expert_bytes()
     router = cfg.n_experts * cfg.hidden * 4 + cfg.n_experts * 4
     bytes_step = sum(router + (d + cfg.n_shared) * eb + T * H * 6 for d in distinct)
-    flops_step = n_calls * T * (k + cfg.n_shared) * 2 * 3 * H * cfg.inter
+    kept_entries = int((ids_h >= 0).sum())
+    flops_step = (kept_entries + n_calls * T * cfg.n_shared) * 2 * 3 * H * cfg.inter
     tokens_per_s = n_calls * T * args.steps / (ms_per_step * args.steps / 1e3)
     gbs = bytes_step / (ms_per_step / 1e3) / 1e9
     tflops = flops_step / (ms_per_step / 1e3) / 1e12
@@ -393,9 +400,10 @@ def bench_batched(args) -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int4 weights x fp16 activations (MFMA), fp32 accumulate",
+        "dtype": f"{cfg.codec} weights x fp16 activations (MFMA), fp32 accumulate",
         "data": f"synthetic (seeded: weights seed 0, tokens seed {seed})",
-        "config": {"workload": workload, "tokens_per_call": T, "calls_per_step": n_calls, "hidden": H,
+        "config": {"workload": workload + (f", {cfg.codec} experts" if cfg.codec != "int4" else "")
+                   + (f", adaptive expert top-p {cfg.top_p}" if cfg.top_p < 1.0 else ""), "tokens_per_call": T, "calls_per_step": n_calls, "hidden": H,
                    "expert_intermediate": cfg.inter, "routed_experts": cfg.n_experts, "top_k": k},
         "tokens_per_s": round(tokens_per_s, 1),
         "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),

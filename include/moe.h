@@ -84,9 +84,8 @@ typedef enum {
  *   [hidden][inter]); int2 four codes per byte, column 4j + t in bits
  *   [2t, 2t + 2) of byte j (code arrays [inter][hidden/4], [hidden][inter/4]),
  *   values -2..1.
- * MXFP4, int8 and int2 are served by the one-token kernels: a T > 1 call
- * runs as T one-token passes (no batch union); the batched (batch-union,
- * matrix-core) kernels are int4 only. */
+ * The batched (batch-union, matrix-core) kernels serve int4 and MXFP4; a
+ * T > 1 call with int8 or int2 experts runs as T one-token passes. */
 enum { MOE_CODEC_INT4 = 0, MOE_CODEC_MXFP4 = 1, MOE_CODEC_INT8 = 2, MOE_CODEC_INT2 = 3 };
 
 typedef struct {

@@ -79,6 +79,34 @@ __device__ __forceinline__ f16x8 codes_to_f16x8(unsigned w, const MagicExp& mg) 
     return __builtin_bit_cast(f16x8, v);
 }
 
+// MXFP4: the same fragment order from eight E2M1 codes (code byte j holds
+// columns 2j and 2j + 1): v_cvt_scalef32_pk_f16_fp4 turns each byte into an
+// exact fp16 pair (scale 1), and byte permutes pair columns c and c + 4.
+__device__ __forceinline__ f16x8 fp4_to_f16x8(unsigned w) {
+    const unsigned p0 = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0));
+    const unsigned p1 = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1));
+    const unsigned p2 = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2));
+    const unsigned p3 = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3));
+    const u32x4 v = {__builtin_amdgcn_perm(p2, p0, 0x05040100u), __builtin_amdgcn_perm(p2, p0, 0x07060302u),
+                     __builtin_amdgcn_perm(p3, p1, 0x05040100u), __builtin_amdgcn_perm(p3, p1, 0x07060302u)};
+    return __builtin_bit_cast(f16x8, v);
+}
+template <int F>
+__device__ __forceinline__ f16x8 dequant_f16x8(unsigned w, const MagicExp& mg) {
+    if constexpr (F == kCodecMxfp4)
+        return fp4_to_f16x8(w);
+    else
+        return codes_to_f16x8(w, mg);
+}
+// A scale held in 16 bits (fp16 bits for int4, the E8M0 byte for MXFP4).
+template <int F>
+__device__ __forceinline__ float scale16(unsigned v) {
+    if constexpr (F == kCodecMxfp4)
+        return e8m0_to_float(v & 0xFFu);
+    else
+        return half_bits_to_float(v & 0xFFFFu);
+}
+
 // Lane (i, q) = (lane & 15, lane >> 4) holds the 4 dwords T[q][0..3] of
 // group g+q of row i; afterwards d[m] holds T[m][q], i.e. dword q (columns
 // 8q..8q+7) of group g+m: the B fragment of group g+m.
@@ -356,24 +384,42 @@ __global__ void __launch_bounds__(1024) batch_dispatch_kernel(BatchArgs a) {
 
 // ---------------------------------------------------------------- gate/up
 // Gate and up scales of row r for groups g..g+3 as dwords (gate | up << 16).
-template <int KG>
-__device__ __forceinline__ u32x4 gateup_scales4(const uint16_t* gus, int r, int g) {
-    if constexpr (KG >= kWave) {
-        return *as_global<u32x4>(gus + gateup_scale_index(r, g, 0, KG, 1));
-    } else {
-        constexpr int p = gateup_rows(KG);
-        u32x4 v;
+// (MXFP4: E8M0 bytes in the same 16-bit places.)
+template <int KG, int F>
+__device__ __forceinline__ u32x4 gateup_scales4(const uint8_t* gus, int r, int g) {
+    if constexpr (F == kCodecMxfp4) {
+        if constexpr (KG >= kWave) {
+            const u32x2 b = *as_global<u32x2>(gus + gateup_scale_index(r, g, 0, KG, 1));
+            return u32x4{(b[0] & 0xFFu) | ((b[0] >> 8 & 0xFFu) << 16), (b[0] >> 16 & 0xFFu) | ((b[0] >> 24) << 16),
+                         (b[1] & 0xFFu) | ((b[1] >> 8 & 0xFFu) << 16), (b[1] >> 16 & 0xFFu) | ((b[1] >> 24) << 16)};
+        } else {
+            constexpr int p = gateup_rows(KG);
+            u32x4 v;
 #pragma unroll
-        for (int m = 0; m < 4; ++m)
-            v[m] = (unsigned)*as_global<uint16_t>(gus + gateup_scale_index(r, g + m, 0, KG, p)) |
-                   ((unsigned)*as_global<uint16_t>(gus + gateup_scale_index(r, g + m, 1, KG, p)) << 16);
-        return v;
+            for (int m = 0; m < 4; ++m)
+                v[m] = (unsigned)*as_global<uint8_t>(gus + gateup_scale_index(r, g + m, 0, KG, p)) |
+                       ((unsigned)*as_global<uint8_t>(gus + gateup_scale_index(r, g + m, 1, KG, p)) << 16);
+            return v;
+        }
+    } else {
+        const uint16_t* gus16 = reinterpret_cast<const uint16_t*>(gus);
+        if constexpr (KG >= kWave) {
+            return *as_global<u32x4>(gus16 + gateup_scale_index(r, g, 0, KG, 1));
+        } else {
+            constexpr int p = gateup_rows(KG);
+            u32x4 v;
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+                v[m] = (unsigned)*as_global<uint16_t>(gus16 + gateup_scale_index(r, g + m, 0, KG, p)) |
+                       ((unsigned)*as_global<uint16_t>(gus16 + gateup_scale_index(r, g + m, 1, KG, p)) << 16);
+            return v;
+        }
     }
 }
 
 // Workgroup = 8 waves over 128 rows of gate and the same 128 rows of up for
 // the (up to) 16 tokens of one tile; wave w owns rows 16w..16w+15.
-template <int KG>
+template <int KG, int F>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) batch_gateup_kernel(BatchArgs a) {
     constexpr int CK = KG < 32 ? KG : 32;   // groups per LDS stage
     constexpr int NST = KG / CK;
@@ -385,7 +431,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) b
     const int n_tiles = a.n_tiles[0];
     const int rblocks = a.I / kBlockRows;
     const int items = n_tiles * rblocks;
-    const BlobLayout L = blob_layout(a.H, a.I, kCodecInt4);  // int4 only
+    const BlobLayout L = blob_layout(a.H, a.I, F);
     const int row_bytes = a.H / 2;
     const MagicExp mg = magic_exponents();
     int gs = 0;  // stages so far: selects the LDS buffer
@@ -396,7 +442,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) b
         const int row = rb * kBlockRows + wv * 16 + i;
         const uint8_t* gq = blob + L.gate_q + (size_t)row * row_bytes;
         const uint8_t* uq = blob + L.up_q + (size_t)row * row_bytes;
-        const uint16_t* gus = reinterpret_cast<const uint16_t*>(blob + L.gu_s);
+        const uint8_t* gus = blob + L.gu_s;
         const int sm = tid & 15;
         const uint16_t* xsrc = sm < td.count ? a.xa + (size_t)pair_token(a, td.first_pair + sm) * a.H : nullptr;
         f32x4 accg = {0.f, 0.f, 0.f, 0.f}, accu = {0.f, 0.f, 0.f, 0.f};
@@ -413,7 +459,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) b
         // lane shuffle
         auto quad_scales = [&](int h) {
             const int s = 4 * h + q;
-            return s < NS ? gateup_scales4<KG>(gus, row, 4 * s) : u32x4{0u, 0u, 0u, 0u};
+            return s < NS ? gateup_scales4<KG, F>(gus, row, 4 * s) : u32x4{0u, 0u, 0u, 0u};
         };
         auto stage_load = [&](int st, u32x4 (&v)[PT]) {
 #pragma unroll
@@ -463,10 +509,10 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) b
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
                     const f16x8 af = __builtin_bit_cast(f16x8, xs[buf][((4 * c + m) * 4 + q) * 16 + i]);
-                    const f32x4 dg = mfma16(af, codes_to_f16x8(cg0[m], mg), zero);
-                    const f32x4 du = mfma16(af, codes_to_f16x8(cu0[m], mg), zero);
-                    const float sg = half_bits_to_float(sc0[m] & 0xFFFFu);
-                    const float su = half_bits_to_float(sc0[m] >> 16);
+                    const f32x4 dg = mfma16(af, dequant_f16x8<F>(cg0[m], mg), zero);
+                    const f32x4 du = mfma16(af, dequant_f16x8<F>(cu0[m], mg), zero);
+                    const float sg = scale16<F>(sc0[m]);
+                    const float su = scale16<F>(sc0[m] >> 16);
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         accg[j] = fmaf(sg, dg[j], accg[j]);
@@ -553,7 +599,7 @@ __global__ void __launch_bounds__(256) batch_hprep_kernel(BatchArgs a) {
 // ---------------------------------------------------------------- down
 // Workgroup = 8 waves over 128 output rows for the (up to) 16 entries of one
 // tile; each group is two MFMAs (hi and lo parts of h) into one result.
-template <int KGI>
+template <int KGI, int F>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) batch_down_kernel(BatchArgs a) {
     constexpr int CK = KGI < 16 ? KGI : 16;
     constexpr int NST = KGI / CK;
@@ -566,7 +612,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) b
     const int n_tiles = a.n_tiles[0];
     const int rblocks = a.H / kBlockRows;
     const int items = n_tiles * rblocks;
-    const BlobLayout L = blob_layout(a.H, a.I, kCodecInt4);  // int4 only
+    const BlobLayout L = blob_layout(a.H, a.I, F);
     const int row_bytes = a.I / 2;
     const MagicExp mg = magic_exponents();
     int gs = 0;
@@ -576,7 +622,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) b
         const uint8_t* blob = td.expert < a.E ? a.table[td.expert] : a.shared_blob;
         const int row = rb * kBlockRows + wv * 16 + i;
         const uint8_t* dq = blob + L.down_q + (size_t)row * row_bytes;
-        const uint16_t* dsc = reinterpret_cast<const uint16_t*>(blob + L.down_s);
+        const uint8_t* dsc = blob + L.down_s;
         const int sm = tid & 15;
         const bool has = sm < td.count;
         const size_t src = (size_t)(td.first_pair + sm) * a.I;
@@ -586,7 +632,13 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) b
         auto load_step = [&](int s, u32x4& c, u32x4& sc) {
             c = *as_global<u32x4>(dq + (4 * s + q) * 16);
 #pragma unroll
-            for (int m = 0; m < 4; ++m) sc[m] = *as_global<uint16_t>(dsc + scale_index(row, 4 * s + m, KGI, a.down_p));
+            for (int m = 0; m < 4; ++m) {
+                const size_t si = scale_index(row, 4 * s + m, KGI, a.down_p);
+                if constexpr (F == kCodecMxfp4)
+                    sc[m] = *as_global<uint8_t>(dsc + si);
+                else
+                    sc[m] = *as_global<uint16_t>(reinterpret_cast<const uint16_t*>(dsc) + si);
+            }
         };
         auto stage_load = [&](int st, u32x4 (&v)[PT]) {
 #pragma unroll
@@ -621,9 +673,9 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) b
                     const int slot = ((4 * c + m) * 4 + q) * 16 + i;
                     const f16x8 ah = __builtin_bit_cast(f16x8, hs[buf][slot]);
                     const f16x8 al = __builtin_bit_cast(f16x8, hs[buf][PART + slot]);
-                    const f16x8 bw = codes_to_f16x8(cd0[m], mg);
+                    const f16x8 bw = dequant_f16x8<F>(cd0[m], mg);
                     const f32x4 d = mfma16(al, bw, mfma16(ah, bw, zero));
-                    const float s = half_bits_to_float(sc0[m]);
+                    const float s = scale16<F>(sc0[m]);
 #pragma unroll
                     for (int j = 0; j < 4; ++j) acc[j] = fmaf(s, d[j], acc[j]);
                     asm volatile("" : "+v"(acc));
@@ -703,13 +755,21 @@ int grouped_grid(const BatchArgs& a, int rblocks) {
 
 template <int KG>
 hipError_t launch_gateup(const BatchArgs& a, hipStream_t st) {
-    hipLaunchKernelGGL((batch_gateup_kernel<KG>), dim3(grouped_grid(a, a.I / kBlockRows)), dim3(512), 0, st, a);
+    const dim3 grid(grouped_grid(a, a.I / kBlockRows));
+    if (a.codec == kCodecMxfp4)
+        hipLaunchKernelGGL((batch_gateup_kernel<KG, kCodecMxfp4>), grid, dim3(512), 0, st, a);
+    else
+        hipLaunchKernelGGL((batch_gateup_kernel<KG, kCodecInt4>), grid, dim3(512), 0, st, a);
     return hipGetLastError();
 }
 
 template <int KGI>
 hipError_t launch_down(const BatchArgs& a, hipStream_t st) {
-    hipLaunchKernelGGL((batch_down_kernel<KGI>), dim3(grouped_grid(a, a.H / kBlockRows)), dim3(512), 0, st, a);
+    const dim3 grid(grouped_grid(a, a.H / kBlockRows));
+    if (a.codec == kCodecMxfp4)
+        hipLaunchKernelGGL((batch_down_kernel<KGI, kCodecMxfp4>), grid, dim3(512), 0, st, a);
+    else
+        hipLaunchKernelGGL((batch_down_kernel<KGI, kCodecInt4>), grid, dim3(512), 0, st, a);
     return hipGetLastError();
 }
 

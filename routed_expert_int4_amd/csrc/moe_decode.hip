@@ -322,12 +322,6 @@ __device__ __forceinline__ void load_scales_c(const uint8_t* p, unsigned (&d)[M]
     }
 }
 
-// E8M0 byte b -> 2^(b - 127) (b = 0 is the subnormal 2^-127; the packer
-// refuses 255).
-__device__ __forceinline__ float e8m0_to_float(unsigned b) {
-    return __builtin_bit_cast(float, b ? b << 23 : 0x00400000u);
-}
-
 // Scale n of a run loaded by load_scales_c.
 template <int F, int N>
 __device__ __forceinline__ float scale_at(const unsigned (&d)[N], int n) {

@@ -37,6 +37,12 @@ __device__ __forceinline__ u32x4 load_stream16(const uint8_t* p) {
     return __builtin_nontemporal_load(as_global<u32x4>(p));
 }
 
+// E8M0 byte b -> 2^(b - 127) (b = 0 is the subnormal 2^-127; the packer
+// refuses 255).
+__device__ __forceinline__ float e8m0_to_float(unsigned b) {
+    return __builtin_bit_cast(float, b ? b << 23 : 0x00400000u);
+}
+
 __device__ __forceinline__ float half_bits_to_float(unsigned bits16) {
     return (float)__builtin_bit_cast(_Float16, (unsigned short)bits16);
 }

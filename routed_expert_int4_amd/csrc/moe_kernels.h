@@ -111,6 +111,7 @@ struct BatchArgs {
     int router_splits;           // column splits of the router (power of two, hidden % (64 * splits) == 0)
     float rsf;
     float top_p;                 // adaptive expert top-p (1: plain top-k); dropped choices get id -1
+    int codec;                   // kCodecInt4 or kCodecMxfp4
 };
 
 // Upper bound of the tiles of a call of T tokens.

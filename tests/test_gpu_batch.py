@@ -249,3 +249,42 @@ def test_batch_top_p_parity(torch_cuda, cfg_name, T, top_p):
         f"excused {res['excused']}")
     assert dropped > 0
     layer.close()
+
+
+# ---------------------------------------------------------------- MXFP4 experts
+@pytest.mark.parametrize("cfg_name,T,top_p", [("TINY", 4, 1.0), ("MID_A", 37, 1.0), ("MID_B", 16, 1.0),
+                                              ("MID_C", 5, 1.0), ("MID_D", 100, 1.0), ("MID_A", 21, 0.7)])
+def test_batch_mxfp4_parity(torch_cuda, cfg_name, T, top_p):
+    """Batch-union calls of MXFP4 layers (E2M1 codes turned into fp16 pairs
+    for the matrix cores, E8M0 scales) against the oracle."""
+    import dataclasses
+    from routed_expert_int4_amd.layer import DeviceLayer
+    cfg = {"TINY": synth.TINY, "MID_A": MID_A, "MID_B": MID_B, "MID_C": MID_C, "MID_D": MID_D}[cfg_name]
+    cfg = dataclasses.replace(cfg, codec="mxfp4", top_p=top_p)
+    say(f"[gpu] batched mxfp4 {cfg_name} T={T} top_p={top_p}")
+    weights = synth.gen_layer(cfg, seed=0)
+    layer = DeviceLayer(weights, max_T=T)
+    x = synth.gen_tokens(cfg, T, seed=4)
+    y, ids, w = run_batch(torch_cuda, layer, x)
+    res = check_layer(weights, x, y, ids, w)
+    say(f"[gpu] batched mxfp4 {cfg_name}: worst rel err {res['worst_rel']:.3g}, excused {res['excused']}")
+    layer.close()
+
+
+def test_glm_mxfp4_prefill_chunk(torch_cuda):
+    """GLM-shaped MXFP4 layer, one 512-token prefill chunk: routing of every
+    token against the oracle, outputs on a sample."""
+    import dataclasses
+    from routed_expert_int4_amd.layer import DeviceLayer
+    cfg = dataclasses.replace(synth.GLM, codec="mxfp4")
+    say("[gpu] GLM mxfp4 prefill chunk of 512")
+    weights = synth.gen_layer(cfg, seed=0)
+    layer = DeviceLayer(weights, max_T=512)
+    x = synth.gen_tokens(cfg, 512, seed=5)
+    y, ids, w = run_batch(torch_cuda, layer, x)
+    ids_ref, w_ref, gap = oracle.route(weights, x)
+    excused = check_routing(cfg, ids, w, ids_ref, w_ref, gap)
+    rows = sorted(set([0, 1, 255, 511] + list(np.argsort(gap)[:2])))
+    res = check_layer(weights, x, y, ids, w, rows=rows)
+    say(f"[gpu] GLM mxfp4 prefill: {len(excused)} excused, sampled worst rel err {res['worst_rel']:.3g}")
+    layer.close()

@@ -164,8 +164,9 @@ void moe_layer_destroy(moe_layer_t* layer);
 
 /* moe_router_topk: router and group-limited top-k for T tokens.
  * d_x bf16 bits [T][hidden]; writes d_ids int32 [T][top_k] (sb descending,
- * ties to the lower index) and d_w fp32 [T][top_k].  T = 0 is a no-op.
- * T must not exceed the workspace's max_T. */
+ * ties to the lower index; -1 for a choice the top-p cut dropped) and d_w
+ * fp32 [T][top_k] (0 for a dropped choice).  T = 0 is a no-op.  T must not
+ * exceed the workspace's max_T. */
 moe_status_t moe_router_topk(moe_layer_t* layer, const uint16_t* d_x, int T, int32_t* d_ids, float* d_w,
                              void* stream);
 
@@ -173,13 +174,15 @@ moe_status_t moe_router_topk(moe_layer_t* layer, const uint16_t* d_x, int T, int
  * [T][hidden]; d_y fp32 [T][hidden] (the block output without residual);
  * d_ids / d_w may be NULL, else receive the routing as in moe_router_topk.
  * T = 1 runs the decode kernels (one token per launch sequence).  T > 1
- * with all experts resident runs the batch-union path (colibrì summary,
+ * with all experts resident and int4 or MXFP4 experts runs the batch-union
+ * path (colibrì summary,
  * fr.news.hada.io topic 31297, "Principales fonctionnalités implémentées":
  * in prefill and batched verification each distinct expert of the batch is
  * read once and applied to every position routed to it): routing of all
  * tokens, a dispatch of the (token, slot) entries by expert, grouped gate/up
  * and down projections on the matrix cores, and the combine; tokens are
- * taken in launch sequences of at most min(max_T, 8192 / top_k).
+ * taken in launch sequences of at most min(max_T, 8192 / top_k); T > 1 with
+ * int8 or int2 experts runs the decode kernels token by token.
  * With all experts resident the call is asynchronous.  With an attached
  * expert cache tokens are processed one at a time; the call blocks the host
  * once per token until its routing is known, issues the copies of missing
@@ -191,12 +194,14 @@ moe_status_t moe_layer_forward(moe_layer_t* layer, const uint16_t* d_x, int T, f
 /* moe_dispatch: the batch-union dispatch of a routing d_ids int32 [T][top_k]
  * (device) on the layer's workspace (T <= min(max_T, 8192 / top_k)):
  * d_counts [n_experts] entries per expert; d_offsets [n_experts + 1] their
- * exclusive prefix sums (d_offsets[n_experts] = T * top_k); d_perm
- * [T * top_k] the entries (token * top_k + slot) sorted by expert, then
- * token, then slot; d_distinct [n_experts] the experts with at least one
- * entry in ascending order, their number in d_n_distinct[0] (entries of
- * d_distinct past it are unspecified).  All device buffers, asynchronous on
- * stream.  Ids outside [0, n_experts) are undefined behaviour. */
+ * exclusive prefix sums (d_offsets[n_experts] = the number of kept entries);
+ * d_perm [T * top_k] the entries (token * top_k + slot) sorted by expert,
+ * then token, then slot, followed by -1 for every id -1 (a choice the top-p
+ * cut dropped, which takes no entry); d_distinct [n_experts] the experts
+ * with at least one entry in ascending order, their number in
+ * d_n_distinct[0] (entries of d_distinct past it are unspecified).  All
+ * device buffers, asynchronous on stream.  Ids outside [-1, n_experts) are
+ * undefined behaviour. */
 moe_status_t moe_dispatch(moe_layer_t* layer, const int32_t* d_ids, int T, int32_t* d_counts, int32_t* d_offsets,
                           int32_t* d_perm, int32_t* d_distinct, int32_t* d_n_distinct, void* stream);
 

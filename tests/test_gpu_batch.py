@@ -288,3 +288,18 @@ def test_glm_mxfp4_prefill_chunk(torch_cuda):
     res = check_layer(weights, x, y, ids, w, rows=rows)
     say(f"[gpu] GLM mxfp4 prefill: {len(excused)} excused, sampled worst rel err {res['worst_rel']:.3g}")
     layer.close()
+
+
+@pytest.mark.parametrize("name", ["no_shared", "top1_one_group", "all_groups"])
+def test_degenerate_configs_batched(torch_cuda, name):
+    from routed_expert_int4_amd.layer import DeviceLayer
+    from tests.test_gpu_decode import DEGENERATE
+    cfg = DEGENERATE[name]
+    say(f"[gpu] degenerate batched {name}")
+    weights = synth.gen_layer(cfg, seed=5)
+    layer = DeviceLayer(weights, max_T=33)
+    x = synth.gen_tokens(cfg, 33, seed=7)
+    y, ids, w = run_batch(torch_cuda, layer, x)
+    res = check_layer(weights, x, y, ids, w)
+    say(f"[gpu] batched {name}: worst rel err {res['worst_rel']:.3g}")
+    layer.close()

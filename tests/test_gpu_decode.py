@@ -424,3 +424,29 @@ def test_glm_int2_decode(torch_cuda):
     res = check_layer(wp, x[:30], y.cpu().numpy(), ids.cpu().numpy(), w.cpu().numpy(), rows=[0, 29])
     say(f"[gpu] GLM int2 top-p 0.7: worst rel err {res['worst_rel']:.3g}")
     layer.close()
+
+
+# ---------------------------------------------------------------- degenerate configurations
+DEGENERATE = {
+    # no shared expert
+    "no_shared": synth.LayerConfig(hidden=1024, inter=256, n_experts=64, n_groups=8, topk_group=4, top_k=6,
+                                   n_shared=0, routed_scaling_factor=1.5),
+    # one group, one expert per token, no shared expert
+    "top1_one_group": synth.LayerConfig(hidden=256, inter=128, n_experts=16, n_groups=1, topk_group=1, top_k=1,
+                                        n_shared=0),
+    # every group kept (group limit inactive), top-8 of 32
+    "all_groups": synth.LayerConfig(hidden=512, inter=128, n_experts=32, n_groups=4, topk_group=4, top_k=8),
+}
+
+
+@pytest.mark.parametrize("name", sorted(DEGENERATE))
+def test_degenerate_configs_decode(torch_cuda, name):
+    cfg = DEGENERATE[name]
+    say(f"[gpu] degenerate decode {name}")
+    weights = synth.gen_layer(cfg, seed=5)
+    x = synth.gen_tokens(cfg, 9, seed=6)
+    layer, y, ids, w = run_layer(torch_cuda, weights, x)
+    res = check_layer(weights, x, y, ids, w)
+    np.testing.assert_allclose(w.sum(axis=1), cfg.routed_scaling_factor, rtol=1e-6)
+    say(f"[gpu] {name}: worst rel err {res['worst_rel']:.3g}")
+    layer.close()

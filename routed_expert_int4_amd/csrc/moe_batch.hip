@@ -421,7 +421,7 @@ __device__ __forceinline__ u32x4 gateup_scales4(const uint8_t* gus, int r, int g
 // the (up to) 16 tokens of one tile; wave w owns rows 16w..16w+15.
 template <int KG, int F>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) batch_gateup_kernel(BatchArgs a) {
-    constexpr int CK = KG < 32 ? KG : 32;   // groups per LDS stage
+    constexpr int CK = KG < 16 ? KG : 16;   // groups per LDS stage (16: no register spills)
     constexpr int NST = KG / CK;
     constexpr int PT = CK * 64 / 512;       // 16-byte staging elements per thread
     static_assert(CK % 4 == 0 && KG % CK == 0 && PT >= 1, "gate/up stage shape");

@@ -291,8 +291,11 @@ __device__ __forceinline__ void load_scale_bytes(const uint8_t* p, unsigned (&d)
         d[0] = __builtin_nontemporal_load(as_global<uint16_t>(p));
     } else if constexpr (NL == 4) {
         d[0] = __builtin_nontemporal_load(as_global<unsigned>(p));
+    } else if constexpr (NL % 8 != 0) {
+        static_assert(NL % 4 == 0, "scale pack");
+#pragma unroll
+        for (int q = 0; q < NL / 4; ++q) d[q] = __builtin_nontemporal_load(as_global<unsigned>(p) + q);
     } else if constexpr (NL % 16 != 0) {
-        static_assert(NL % 8 == 0, "scale pack");
 #pragma unroll
         for (int q = 0; q < NL / 8; ++q) {
             const u32x2 v = __builtin_nontemporal_load(as_global<u32x2>(p) + q);
@@ -1017,7 +1020,7 @@ template <int KG, int NLD, int F>
 hipError_t launch_down_c(const DecodeArgs& a, hipStream_t st, const LaunchTiming& tm) {
     using S = DownShape<KG, NLD>;
     if constexpr (ilog2(pow2_at_least(S::NL * row_pack(F))) <= S::B &&
-                  S::NL * S::CPL * code_planes(F) <= kDownMaxLoads) {
+                  S::NL * S::CPL * code_planes(F) <= down_max_loads(code_planes(F), S::CPL)) {
         const int grid = a.H / row_pack(F) / S::R;
         return launch_kernel(down_combine_kernel<KG, NLD, F>, dim3(grid), dim3((a.K + a.S) * 64), st, tm, a);
     } else {
@@ -1040,6 +1043,7 @@ hipError_t launch_down(const DecodeArgs& a, hipStream_t st, const LaunchTiming& 
         case 2: return launch_down_nl<KG, 2>(a, st, tm);
         case 4: return launch_down_nl<KG, 4>(a, st, tm);
         case 8: return launch_down_nl<KG, 8>(a, st, tm);
+        case 12: return launch_down_nl<KG, 12>(a, st, tm);
         case 16: return launch_down_nl<KG, 16>(a, st, tm);
         case 24: return launch_down_nl<KG, 24>(a, st, tm);
         case 32: return launch_down_nl<KG, 32>(a, st, tm);

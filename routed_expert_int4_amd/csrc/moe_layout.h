@@ -55,11 +55,17 @@ __host__ __device__ constexpr int gateup_rows(int kg_h) {
 // Wave-load steps a down-projection wave may take over its row block; the
 // down kernel is instantiated for each of these counts.
 __host__ __device__ constexpr int down_step_option(int i) {
-    return i == 0 ? 32 : i == 1 ? 24 : i == 2 ? 16 : i == 3 ? 8 : i == 4 ? 4 : i == 5 ? 2 : 1;
+    return i == 0 ? 32 : i == 1 ? 24 : i == 2 ? 16 : i == 3 ? 12 : i == 4 ? 8 : i == 5 ? 4 : i == 6 ? 2 : 1;
 }
+constexpr int kDownStepOptions = 8;
 // Code loads a down-projection wave keeps in registers at most (steps x
-// chunk columns).
+// chunk columns x planes): 24 with one chunk column and one plane, else 16
+// (a second chunk column or nibble plane needs the registers for its own
+// operands and dot chain).
 constexpr int kDownMaxLoads = 24;
+__host__ __device__ constexpr int down_max_loads(int planes, int cpl) {
+    return planes > 1 || cpl > 1 ? 16 : kDownMaxLoads;
+}
 
 __host__ __device__ constexpr int pow2_at_least(int v) { return v <= 1 ? 1 : 2 * pow2_at_least((v + 1) / 2); }
 
@@ -77,10 +83,10 @@ __host__ __device__ inline int down_rows(int hidden, int kg_i, int codec) {
     const int rpl = rows_per_load(kg_i);
     const int lanes_per_row = kg_i < kWave ? kg_i : kWave;
     const int target = vrows / 256 > rpl ? vrows / 256 : rpl;
-    for (int i = 0; i < 7; ++i) {
+    for (int i = 0; i < kDownStepOptions; ++i) {
         const int steps = down_step_option(i);
         const int r = steps * rpl;
-        if (r <= target && vrows % r == 0 && steps * chunks_per_lane(kg_i) * planes <= kDownMaxLoads &&
+        if (r <= target && vrows % r == 0 && steps * chunks_per_lane(kg_i) * planes <= down_max_loads(planes, chunks_per_lane(kg_i)) &&
             pow2_at_least(steps * rp) <= lanes_per_row)
             return r;
     }

@@ -113,6 +113,17 @@ def cpu_baseline(weights, x_bits, n_tokens: int, bytes_per_token: int):
     oracle.layer_forward(weights, sample, n_threads=threads)
     dt = time.perf_counter() - t0
     tps = n_tokens / dt
+    # one thread on a short prefix, for the per-core figure
+    n1 = max(1, min(16, n_tokens))
+    t1 = time.perf_counter()
+    oracle.layer_forward(weights, sample[:n1], n_threads=1)
+    dt1 = time.perf_counter() - t1
+    cpu_model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), "")
+    except OSError:
+        pass
     return {
         "value": round(tps * bytes_per_token / 1e9, 4),
         "unit": "GB/s",
@@ -121,6 +132,8 @@ def cpu_baseline(weights, x_bits, n_tokens: int, bytes_per_token: int):
         "kind": "oracle",
         "sample": f"first {n_tokens} of the 1000 tokens, full layer in fp64 (router, top-k, 8 routed + shared "
                   f"experts, combine), {dt:.1f} s",
+        "tokens_per_s_1_thread": round(n1 / dt1, 3),
+        "cpu_model": cpu_model,
     }
 
 
@@ -133,9 +146,11 @@ def main() -> int:
     ap.add_argument("--cpu-sample", type=int, default=640, help="tokens timed on the CPU oracle (0: skip)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one device copy of 256 MiB (a known-size kernel for HBM counter scaling)")
-    ap.add_argument("--workload", default="decode", choices=["decode", "batch32", "prefill512", "cache-stack"],
+    ap.add_argument("--workload", default="decode",
+                    choices=["decode", "batch32", "prefill512", "cache-stack", "probes"],
                     help="decode: the headline batch-1 line (default); batch32 / prefill512: the batched "
-                         "workloads; cache-stack: 12 layers behind the HBM expert cache; each prints its own line")
+                         "workloads; cache-stack: 12 layers behind the HBM expert cache; probes: the device "
+                         "ceilings (HBM copy, host copies, bf16 GEMM); each prints its own line")
     ap.add_argument("--stack-tokens", type=int, default=256, help="sequential tokens of the cache-stack workload")
     ap.add_argument("--pin", type=int, default=-1,
                     help="cache-stack: experts pinned per layer by learned usage (-1: slots - top_k, 0: plain LRU)")
@@ -155,6 +170,8 @@ def main() -> int:
         return bench_decode(args)
     if args.workload == "cache-stack":
         return bench_cache_stack(args)
+    if args.workload == "probes":
+        return bench_probes(args)
     return bench_batched(args)
 
 
@@ -305,6 +322,59 @@ def bench_cache_stack(args) -> int:
     for lay in layers:
         lay.close()
     cache.close()
+    return 0
+
+
+def bench_probes(args) -> int:
+    """Device ceilings the layer's numbers are read against (one JSON line):
+    HBM GB/s of a device-to-device copy (bytes read + bytes written) over
+    buffers the size of the decode launches (56 MB, 113 MB) and of 1 GiB;
+    pinned host-to-device and device-to-host copy GB/s (256 MiB); bf16 GEMM
+    TFLOP/s (8192^3 through torch.matmul).  Each figure is the best of 10
+    timed repeats after 3 warmups."""
+    import torch
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = "cuda:0"
+
+    def best_ms(fn, reps=10):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        best = float("inf")
+        for _ in range(reps):
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            best = min(best, e0.elapsed_time(e1))
+        return best
+
+    read = {}
+    for label, nbytes in (("56MB", 56_623_104), ("113MB", 113_246_208), ("1GiB", 1 << 30)):
+        src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        ms = best_ms(lambda: dst.copy_(src))
+        read[label] = round(2 * nbytes / (ms / 1e3) / 1e9, 1)
+        del src, dst
+    host = torch.empty(256 << 20, dtype=torch.uint8, pin_memory=True)
+    devb = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+    h2d = (256 << 20) / (best_ms(lambda: devb.copy_(host, non_blocking=True)) / 1e3) / 1e9
+    d2h = (256 << 20) / (best_ms(lambda: host.copy_(devb, non_blocking=True)) / 1e3) / 1e9
+    n = 8192
+    a = torch.randn(n, n, dtype=torch.bfloat16, device=dev)
+    b = torch.randn(n, n, dtype=torch.bfloat16, device=dev)
+    gemm = 2 * n ** 3 / (best_ms(lambda: torch.matmul(a, b)) / 1e3) / 1e12
+    out = {
+        "metric": "device ceilings: HBM copy GB/s (read + write), pinned host copy GB/s, bf16 GEMM TFLOP/s",
+        "value": read["1GiB"], "unit": "GB/s", "n_gpus": 1, "steps": 10, "warmup": 3,
+        "higher_is_better": True, "data": "synthetic",
+        "config": {"workload": "probes: device-to-device copies, pinned 256 MiB copies, 8192^3 bf16 matmul"},
+        "hbm_copy_gbs": read, "h2d_gbs": round(h2d, 1), "d2h_gbs": round(d2h, 1), "bf16_gemm_tflops": round(gemm, 1),
+        "vs_peak": {"hbm_copy_1GiB": round(read["1GiB"] / HBM_PEAK_GBS, 4), "bf16_gemm": round(gemm / 2500.0, 4)},
+    }
+    print(json.dumps(out), flush=True)
     return 0
 
 

@@ -32,6 +32,10 @@
 // fragment as columns (0,4,1,5,2,6,3,7) of its k-block; the activations are
 // stored in that order.  Tokens' activations for a stage of K are staged
 // in LDS (double buffered, one barrier per stage) and read as A fragments.
+// MXFP4 experts take the same kernels: an E2M1 code dword becomes the same
+// fragment through v_cvt_scalef32_pk_f16_fp4 and byte permutes, and the
+// E8M0 byte takes the fp16 scale's place.  With the adaptive top-p cut a
+// dropped choice (id -1) gets no dispatch entry and the combine skips it.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>

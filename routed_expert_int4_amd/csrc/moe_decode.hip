@@ -25,6 +25,16 @@
 // removed with a per-group correction, and the fp16 weight scale and the
 // group's power of two are applied once per chunk in fp32.  Partial sums of
 // the rows a wave visited are reduced across lanes with a reduce-scatter.
+//
+// The kernels are templated on the weight codec; the lane mapping, loads and
+// pipelines stay those of int4.  MXFP4: E2M1 code bytes become exact fp16
+// pairs (v_cvt_scalef32_pk_f16_fp4) dotted with fp16 activation pairs
+// (v_dot2c_f32_f16), E8M0 scale bytes.  Int8: two int4-shaped nibble planes
+// per matrix (q = 16 hi + lo), both dotted with the same 8-bit operands.
+// Int2: int4-shaped planes of half the rows, a nibble holding the codes of
+// two adjacent rows, one chunk dot yielding both rows.  With the adaptive
+// top-p cut the router also writes the kept slots, gate/up covers only
+// those and down skips the dropped slots' waves.
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 

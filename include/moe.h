@@ -279,9 +279,10 @@ moe_status_t expert_cache_autopin(moe_cache_t* cache, int layer, int n);
  * LRU; a miss takes a free slot, else the least recently used unpinned slot
  * not needed by the same token) on a routing trace [n_tokens][top_k] of one
  * layer, with no GPU work.  The n_pinned experts of `pinned` (at most
- * slots - top_k) are resident and pinned before the first token.  Writes the
- * hit, miss and eviction counts the cache would record for the same trace
- * from a cold start. */
+ * slots - top_k) are resident and pinned before the first token.  An id -1
+ * (a choice the top-p cut dropped) is skipped, as the cache skips it.
+ * Writes the hit, miss and eviction counts the cache would record for the
+ * same trace from a cold start. */
 moe_status_t expert_cache_replay(int n_experts, int slots, int top_k, const int32_t* trace, int n_tokens,
                                  const int32_t* pinned, int n_pinned, uint64_t* hits, uint64_t* misses,
                                  uint64_t* evictions);

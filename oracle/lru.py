@@ -9,7 +9,8 @@ Reading used here: a token's experts are looked up in routing order; a hit
 refreshes the expert's recency; a miss takes a free slot, else evicts the
 least recently used expert that the same token does not need.  Pinned
 experts are resident from the start, are never evicted, and leave
-slots - len(pinned) slots to the LRU.  Returns the hit, miss and eviction
+slots - len(pinned) slots to the LRU.  A choice dropped by the adaptive
+top-p cut (id -1) is not looked up.  Returns the hit, miss and eviction
 counts from a cold start (pinned experts loaded beforehand).
 """
 from collections import OrderedDict
@@ -21,9 +22,9 @@ def replay(trace, slots: int, pinned=()):
     resident = OrderedDict()  # unpinned expert -> None, least recently used first
     hits = misses = evictions = 0
     for token in trace:
-        need = set(int(e) for e in token)
+        token = [int(e) for e in token if int(e) >= 0]
+        need = set(token)
         for e in token:
-            e = int(e)
             if e in pinned:
                 hits += 1
                 continue
@@ -45,7 +46,8 @@ def usage(trace, n_experts: int):
     counts = [0] * n_experts
     for token in trace:
         for e in token:
-            counts[int(e)] += 1
+            if int(e) >= 0:
+                counts[int(e)] += 1
     return counts
 
 

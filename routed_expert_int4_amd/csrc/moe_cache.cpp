@@ -401,9 +401,13 @@ moe_status_t expert_cache_replay(int n_experts, int slots, int top_k, const int3
     }
     *hits = *misses = *evictions = 0;
     for (int t = 0; t < n_tokens; ++t) {
-        std::vector<int> ids(trace + (size_t)t * top_k, trace + (size_t)(t + 1) * top_k);
-        for (int e : ids)
-            if (e < 0 || e >= n_experts) return fail(MOE_EINVAL, "expert_cache_replay: id %d out of range", e);
+        // id -1: a choice the top-p cut dropped (no lookup, as in the cache)
+        std::vector<int> ids;
+        for (int j = 0; j < top_k; ++j) {
+            const int e = trace[(size_t)t * top_k + j];
+            if (e < -1 || e >= n_experts) return fail(MOE_EINVAL, "expert_cache_replay: id %d out of range", e);
+            if (e >= 0) ids.push_back(e);
+        }
         for (int e : ids) {
             if (p.slot_of(e) >= 0) {
                 p.touch(e);

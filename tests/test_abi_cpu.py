@@ -221,6 +221,25 @@ def test_cache_policy_matches_lru_replay(slots, skew):
         assert B.expert_cache_replay(E, slots, k, trace, pinned=pins) == lru.replay(trace, slots, pinned=pins)
 
 
+def test_cache_replay_skips_dropped_choices():
+    """Traces with top-p drops (id -1): the library's replay and the oracle's
+    both skip them, and equal the replay of the trace with them removed."""
+    rng = np.random.default_rng(17)
+    E, slots, k = 32, 10, 4
+    trace = np.stack([rng.choice(E, k, replace=False) for _ in range(200)]).astype(np.int32)
+    trace[rng.random(trace.shape) < 0.35] = -1
+    got = B.expert_cache_replay(E, slots, k, trace)
+    assert got == lru.replay(trace, slots)
+    kept = [row[row >= 0] for row in trace]
+    assert lru.replay(kept, slots) == got
+    assert lru.usage(trace, E) == lru.usage(kept, E)
+    bad = trace.copy()
+    bad[0, 0] = -2
+    with pytest.raises(B.MoeError) as e:
+        B.expert_cache_replay(E, slots, k, bad)
+    assert e.value.code == B.MOE_EINVAL
+
+
 def test_cache_replay_rejects_too_many_pins():
     tr = np.zeros((1, 4), np.int32) + np.arange(4, dtype=np.int32)
     with pytest.raises(B.MoeError):

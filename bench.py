@@ -397,8 +397,9 @@ def bench_batched(args) -> int:
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     import dataclasses
-    if args.codec not in ("int4", "mxfp4"):
-        print(f"bench.py: --workload {args.workload} runs the batched kernels, which serve int4 and mxfp4 experts",
+    if args.codec not in ("int4", "mxfp4", "int8"):
+        print(f"bench.py: --workload {args.workload} runs the batched kernels, which serve int4, mxfp4 and int8 "
+              "experts",
               file=sys.stderr)
         return 2
     cfg = dataclasses.replace(synth.GLM, codec=args.codec, top_p=args.top_p)
@@ -460,7 +461,7 @@ def bench_batched(args) -> int:
     log(f"{ms_per_step:.3f} ms/step, {tokens_per_s:.0f} tokens/s, {gbs:.0f} GB/s, {tflops:.1f} TFLOP/s; "
         f"stages ms {stage_ms}; distinct experts per call {min(distinct)}..{max(distinct)}")
     out = {
-        "metric": "MoE-layer tokens/s and HBM GB/s, batched int4 calls",
+        "metric": f"MoE-layer tokens/s and HBM GB/s, batched {cfg.codec} calls",
         "value": round(gbs, 2),
         "unit": "GB/s",
         "n_gpus": 1,

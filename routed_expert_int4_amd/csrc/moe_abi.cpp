@@ -462,7 +462,7 @@ BatchArgs batch_args(moe_layer_t* L, const uint16_t* x, int n, int32_t* ids, flo
     b.TG = c.topk_group;
     b.K = c.top_k;
     b.S = c.n_shared;
-    b.down_p = down_rows(c.hidden, c.inter / 32, kCodecInt4);
+    b.down_p = down_rows(c.hidden, c.inter / 32, c.codec);
     b.router_splits = batch_router_splits(c.hidden);
     b.rsf = c.routed_scaling_factor;
     b.top_p = c.top_p;
@@ -522,10 +522,10 @@ moe_status_t moe_layer_forward(moe_layer_t* layer, const uint16_t* d_x, int T, f
     const moe_config_t& c = layer->cfg;
     int32_t* ids_base = d_ids ? d_ids : reinterpret_cast<int32_t*>(layer->ws + layer->W.ids);
     float* w_base = d_w ? d_w : reinterpret_cast<float*>(layer->ws + layer->W.w);
-    // The batched kernels cover int4 and MXFP4 experts (with or without the
-    // top-p cut); T > 1 calls with the int8 or int2 codecs, and every call
+    // The batched kernels cover int4, MXFP4 and int8 experts (with or
+    // without the top-p cut); T > 1 calls with the int2 codec, and every call
     // behind an expert cache, run as T one-token passes below.
-    if (T > 1 && !layer->cache && (c.codec == kCodecInt4 || c.codec == kCodecMxfp4)) {
+    if (T > 1 && !layer->cache && c.codec != kCodecInt2) {
         // batch union: every distinct expert of a launch sequence is read once
         const int tb = layer->W.batch_tokens;
         for (int t0 = 0; t0 < T; t0 += tb) {

@@ -34,7 +34,9 @@
 // in LDS (double buffered, one barrier per stage) and read as A fragments.
 // MXFP4 experts take the same kernels: an E2M1 code dword becomes the same
 // fragment through v_cvt_scalef32_pk_f16_fp4 and byte permutes, and the
-// E8M0 byte takes the fp16 scale's place.  With the adaptive top-p cut a
+// E8M0 byte takes the fp16 scale's place.  Int8 experts run every group
+// step once per nibble plane: the high plane's codes become 16 (c - 8) and
+// the low plane's c exactly in fp16, two MFMAs under the group's one scale.  With the adaptive top-p cut a
 // dropped choice (id -1) gets no dispatch entry and the combine skips it.
 #include <hip/hip_runtime.h>
 
@@ -70,9 +72,12 @@ __device__ __forceinline__ MagicExp magic_exponents() {
     return m;
 }
 
+// OFF = 8: offset-binary codes c -> c - 8 (int4); OFF = 0: unsigned c (the
+// low-nibble plane of int8 codes).
+template <int OFF = 8>
 __device__ __forceinline__ f16x8 codes_to_f16x8(unsigned w, const MagicExp& mg) {
-    const f16x2 k_lo = {(_Float16)1032.0f, (_Float16)1032.0f};  // 1024 + 8
-    const f16x2 k_hi = {(_Float16)72.0f, (_Float16)72.0f};      // 64 + 8
+    const f16x2 k_lo = {(_Float16)(1024.0f + OFF), (_Float16)(1024.0f + OFF)};
+    const f16x2 k_hi = {(_Float16)(64.0f + OFF), (_Float16)(64.0f + OFF)};
     const unsigned w8 = w >> 8;
     const f16x2 q0 = as_h2((w & 0x000F000Fu) | mg.e1024) - k_lo;
     const f16x2 q1 = as_h2((w & 0x00F000F0u) | mg.e64) - k_hi;
@@ -95,10 +100,27 @@ __device__ __forceinline__ f16x8 fp4_to_f16x8(unsigned w) {
                      __builtin_amdgcn_perm(p3, p1, 0x05040100u), __builtin_amdgcn_perm(p3, p1, 0x07060302u)};
     return __builtin_bit_cast(f16x8, v);
 }
+// High-nibble plane of int8 codes (offset binary c): 16 (c - 8) exactly.
+// Every nibble is moved to bits 4-7 of its half, where under the exponent
+// of 1024 (ulp 1) it reads 1024 + 16c.
+__device__ __forceinline__ f16x8 hi_codes_to_f16x8(unsigned w, const MagicExp& mg) {
+    const f16x2 k = {(_Float16)1152.0f, (_Float16)1152.0f};  // 1024 + 128
+    const f16x2 q0 = as_h2(((w << 4) & 0x00F000F0u) | mg.e1024) - k;
+    const f16x2 q1 = as_h2((w & 0x00F000F0u) | mg.e1024) - k;
+    const f16x2 q2 = as_h2(((w >> 4) & 0x00F000F0u) | mg.e1024) - k;
+    const f16x2 q3 = as_h2(((w >> 8) & 0x00F000F0u) | mg.e1024) - k;
+    const u32x4 v = {__builtin_bit_cast(unsigned, q0), __builtin_bit_cast(unsigned, q1),
+                     __builtin_bit_cast(unsigned, q2), __builtin_bit_cast(unsigned, q3)};
+    return __builtin_bit_cast(f16x8, v);
+}
+// B fragment of one code dword of nibble plane pl (int8: 0 high, 1 low; the
+// two planes' products under one scale sum to the int8 code's product).
 template <int F>
-__device__ __forceinline__ f16x8 dequant_f16x8(unsigned w, const MagicExp& mg) {
+__device__ __forceinline__ f16x8 dequant_f16x8(unsigned w, const MagicExp& mg, int pl = 0) {
     if constexpr (F == kCodecMxfp4)
         return fp4_to_f16x8(w);
+    else if constexpr (F == kCodecInt8)
+        return pl ? codes_to_f16x8<0>(w, mg) : hi_codes_to_f16x8(w, mg);
     else
         return codes_to_f16x8(w, mg);
 }
@@ -446,16 +468,22 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) b
         const int row = rb * kBlockRows + wv * 16 + i;
         const uint8_t* gq = blob + L.gate_q + (size_t)row * row_bytes;
         const uint8_t* uq = blob + L.up_q + (size_t)row * row_bytes;
+        const uint8_t* gql = blob + L.gate_lo + (size_t)row * row_bytes;  // int8 low planes
+        const uint8_t* uql = blob + L.up_lo + (size_t)row * row_bytes;
         const uint8_t* gus = blob + L.gu_s;
         const int sm = tid & 15;
         const uint16_t* xsrc = sm < td.count ? a.xa + (size_t)pair_token(a, td.first_pair + sm) * a.H : nullptr;
         f32x4 accg = {0.f, 0.f, 0.f, 0.f}, accu = {0.f, 0.f, 0.f, 0.f};
         const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
         constexpr int NS = KG / 4;  // steps of 4 groups
-        // codes of a step: lane of quarter q reads group 4s + q
-        auto load_step = [&](int s, u32x4& g, u32x4& u) {
-            g = *as_global<u32x4>(gq + (4 * s + q) * 16);
-            u = *as_global<u32x4>(uq + (4 * s + q) * 16);
+        constexpr int P = code_planes(F);
+        constexpr int NSP = NS * P;  // (step, plane) code loads, plane fastest
+        // codes of load k = (step s, plane pl): lane of quarter q reads group
+        // 4s + q of plane pl
+        auto load_step = [&](int k, u32x4& g, u32x4& u) {
+            const int s = k / P, pl = k - s * P;
+            g = *as_global<u32x4>((pl ? gql : gq) + (4 * s + q) * 16);
+            u = *as_global<u32x4>((pl ? uql : uq) + (4 * s + q) * 16);
         };
         // scales, four steps at a time: for steps 4h .. 4h+3 lane (i, q)
         // fetches step 4h + q of row i (16 bytes, so a wave load covers 16
@@ -480,7 +508,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) b
         u32x4 scl = quad_scales(0), scn = scl;
         u32x4 cg0, cu0, cg1 = {0u, 0u, 0u, 0u}, cu1 = cg1;
         load_step(0, cg0, cu0);
-        if (NS > 1) load_step(1, cg1, cu1);
+        if (NSP > 1) load_step(1, cg1, cu1);
         // fully unrolled over the stages: a loop back-edge here would make
         // the compiler drain the prefetched loads (register rotation copies)
 #pragma unroll
@@ -493,8 +521,6 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) b
 #pragma unroll
             for (int c = 0; c < CK / 4; ++c) {
                 const int sidx = st * (CK / 4) + c;
-                u32x4 cg2 = cg1, cu2 = cu1;
-                if (sidx + 2 < NS) load_step(sidx + 2, cg2, cu2);
                 // the next four steps' scales two steps before they are needed
                 if ((sidx & 3) == 0 && sidx > 0) scl = scn;
                 if ((sidx & 3) == 2 && sidx + 2 < NS) scn = quad_scales(sidx / 4 + 1);
@@ -508,32 +534,38 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) b
                         sc0[d] = (unsigned)__shfl((int)hv, src);
                     }
                 }
-                transpose_quarters(cg0);
-                transpose_quarters(cu0);
 #pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    const f16x8 af = __builtin_bit_cast(f16x8, xs[buf][((4 * c + m) * 4 + q) * 16 + i]);
-                    const f32x4 dg = mfma16(af, dequant_f16x8<F>(cg0[m], mg), zero);
-                    const f32x4 du = mfma16(af, dequant_f16x8<F>(cu0[m], mg), zero);
-                    const float sg = scale16<F>(sc0[m]);
-                    const float su = scale16<F>(sc0[m] >> 16);
+                for (int pl = 0; pl < P; ++pl) {
+                    const int k = sidx * P + pl;
+                    u32x4 cg2 = cg1, cu2 = cu1;
+                    if (k + 2 < NSP) load_step(k + 2, cg2, cu2);
+                    transpose_quarters(cg0);
+                    transpose_quarters(cu0);
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        accg[j] = fmaf(sg, dg[j], accg[j]);
-                        accu[j] = fmaf(su, du[j], accu[j]);
+                    for (int m = 0; m < 4; ++m) {
+                        const f16x8 af = __builtin_bit_cast(f16x8, xs[buf][((4 * c + m) * 4 + q) * 16 + i]);
+                        const f32x4 dg = mfma16(af, dequant_f16x8<F>(cg0[m], mg, pl), zero);
+                        const f32x4 du = mfma16(af, dequant_f16x8<F>(cu0[m], mg, pl), zero);
+                        const float sg = scale16<F>(sc0[m]);
+                        const float su = scale16<F>(sc0[m] >> 16);
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            accg[j] = fmaf(sg, dg[j], accg[j]);
+                            accu[j] = fmaf(su, du[j], accu[j]);
+                        }
+                        // scale and accumulate now: one group's two products
+                        // in flight at a time (otherwise the compiler sinks the
+                        // FMAs to the end of the stage and spills every product)
+                        asm volatile("" : "+v"(accg), "+v"(accu));
+                        __builtin_amdgcn_sched_barrier(0);
                     }
-                    // scale and accumulate now: one group's two products in
-                    // flight at a time (otherwise the compiler sinks the FMAs
-                    // to the end of the stage and spills every product)
-                    asm volatile("" : "+v"(accg), "+v"(accu));
+                    cg0 = cg1;
+                    cu0 = cu1;
+                    cg1 = cg2;
+                    cu1 = cu2;
+                    // keep the prefetch depth, not the whole stage, in flight
                     __builtin_amdgcn_sched_barrier(0);
                 }
-                cg0 = cg1;
-                cu0 = cu1;
-                cg1 = cg2;
-                cu1 = cu2;
-                // keep the prefetch depth, not the whole stage, in flight
-                __builtin_amdgcn_sched_barrier(0);
             }
         }
 #pragma unroll
@@ -626,6 +658,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) b
         const uint8_t* blob = td.expert < a.E ? a.table[td.expert] : a.shared_blob;
         const int row = rb * kBlockRows + wv * 16 + i;
         const uint8_t* dq = blob + L.down_q + (size_t)row * row_bytes;
+        const uint8_t* dql = blob + L.down_lo + (size_t)row * row_bytes;  // int8 low plane
         const uint8_t* dsc = blob + L.down_s;
         const int sm = tid & 15;
         const bool has = sm < td.count;
@@ -633,8 +666,13 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) b
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
         const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
         constexpr int NS = KGI / 4;  // steps of 4 groups
-        auto load_step = [&](int s, u32x4& c, u32x4& sc) {
-            c = *as_global<u32x4>(dq + (4 * s + q) * 16);
+        constexpr int P = code_planes(F);
+        constexpr int NSP = NS * P;  // (step, plane) loads, plane fastest
+        // codes of plane pl and the scales of step s for load k = (s, pl)
+        // (both planes of a step share its scales)
+        auto load_step = [&](int k, u32x4& c, u32x4& sc) {
+            const int s = k / P, pl = k - s * P;
+            c = *as_global<u32x4>((pl ? dql : dq) + (4 * s + q) * 16);
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
                 const size_t si = scale_index(row, 4 * s + m, KGI, a.down_p);
@@ -658,7 +696,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) b
         stage_load(0, v);
         u32x4 cd0, sc0, cd1 = {0u, 0u, 0u, 0u}, sc1 = cd1;
         load_step(0, cd0, sc0);
-        if (NS > 1) load_step(1, cd1, sc1);
+        if (NSP > 1) load_step(1, cd1, sc1);
 #pragma unroll
         for (int st = 0; st < NST; ++st, ++gs) {
             const int buf = gs & 1;
@@ -669,27 +707,31 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) b
 #pragma unroll
             for (int c = 0; c < CK / 4; ++c) {
                 const int sidx = st * (CK / 4) + c;
-                u32x4 cd2 = cd1, sc2 = sc1;
-                if (sidx + 2 < NS) load_step(sidx + 2, cd2, sc2);
-                transpose_quarters(cd0);
 #pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    const int slot = ((4 * c + m) * 4 + q) * 16 + i;
-                    const f16x8 ah = __builtin_bit_cast(f16x8, hs[buf][slot]);
-                    const f16x8 al = __builtin_bit_cast(f16x8, hs[buf][PART + slot]);
-                    const f16x8 bw = dequant_f16x8<F>(cd0[m], mg);
-                    const f32x4 d = mfma16(al, bw, mfma16(ah, bw, zero));
-                    const float s = scale16<F>(sc0[m]);
+                for (int pl = 0; pl < P; ++pl) {
+                    const int k = sidx * P + pl;
+                    u32x4 cd2 = cd1, sc2 = sc1;
+                    if (k + 2 < NSP) load_step(k + 2, cd2, sc2);
+                    transpose_quarters(cd0);
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) acc[j] = fmaf(s, d[j], acc[j]);
-                    asm volatile("" : "+v"(acc));
+                    for (int m = 0; m < 4; ++m) {
+                        const int slot = ((4 * c + m) * 4 + q) * 16 + i;
+                        const f16x8 ah = __builtin_bit_cast(f16x8, hs[buf][slot]);
+                        const f16x8 al = __builtin_bit_cast(f16x8, hs[buf][PART + slot]);
+                        const f16x8 bw = dequant_f16x8<F>(cd0[m], mg, pl);
+                        const f32x4 d = mfma16(al, bw, mfma16(ah, bw, zero));
+                        const float s = scale16<F>(sc0[m]);
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) acc[j] = fmaf(s, d[j], acc[j]);
+                        asm volatile("" : "+v"(acc));
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                    cd0 = cd1;
+                    sc0 = sc1;
+                    cd1 = cd2;
+                    sc1 = sc2;
                     __builtin_amdgcn_sched_barrier(0);
                 }
-                cd0 = cd1;
-                sc0 = sc1;
-                cd1 = cd2;
-                sc1 = sc2;
-                __builtin_amdgcn_sched_barrier(0);
             }
         }
 #pragma unroll
@@ -762,8 +804,12 @@ hipError_t launch_gateup(const BatchArgs& a, hipStream_t st) {
     const dim3 grid(grouped_grid(a, a.I / kBlockRows));
     if (a.codec == kCodecMxfp4)
         hipLaunchKernelGGL((batch_gateup_kernel<KG, kCodecMxfp4>), grid, dim3(512), 0, st, a);
-    else
+    else if (a.codec == kCodecInt8)
+        hipLaunchKernelGGL((batch_gateup_kernel<KG, kCodecInt8>), grid, dim3(512), 0, st, a);
+    else if (a.codec == kCodecInt4)
         hipLaunchKernelGGL((batch_gateup_kernel<KG, kCodecInt4>), grid, dim3(512), 0, st, a);
+    else
+        return hipErrorInvalidValue;
     return hipGetLastError();
 }
 
@@ -772,8 +818,12 @@ hipError_t launch_down(const BatchArgs& a, hipStream_t st) {
     const dim3 grid(grouped_grid(a, a.H / kBlockRows));
     if (a.codec == kCodecMxfp4)
         hipLaunchKernelGGL((batch_down_kernel<KGI, kCodecMxfp4>), grid, dim3(512), 0, st, a);
-    else
+    else if (a.codec == kCodecInt8)
+        hipLaunchKernelGGL((batch_down_kernel<KGI, kCodecInt8>), grid, dim3(512), 0, st, a);
+    else if (a.codec == kCodecInt4)
         hipLaunchKernelGGL((batch_down_kernel<KGI, kCodecInt4>), grid, dim3(512), 0, st, a);
+    else
+        return hipErrorInvalidValue;
     return hipGetLastError();
 }
 

@@ -397,11 +397,6 @@ def bench_batched(args) -> int:
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     import dataclasses
-    if args.codec not in ("int4", "mxfp4", "int8"):
-        print(f"bench.py: --workload {args.workload} runs the batched kernels, which serve int4, mxfp4 and int8 "
-              "experts",
-              file=sys.stderr)
-        return 2
     cfg = dataclasses.replace(synth.GLM, codec=args.codec, top_p=args.top_p)
     if args.workload == "batch32":
         n_calls, T, seed = 32, 32, 4

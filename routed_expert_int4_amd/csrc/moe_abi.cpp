@@ -522,10 +522,10 @@ moe_status_t moe_layer_forward(moe_layer_t* layer, const uint16_t* d_x, int T, f
     const moe_config_t& c = layer->cfg;
     int32_t* ids_base = d_ids ? d_ids : reinterpret_cast<int32_t*>(layer->ws + layer->W.ids);
     float* w_base = d_w ? d_w : reinterpret_cast<float*>(layer->ws + layer->W.w);
-    // The batched kernels cover int4, MXFP4 and int8 experts (with or
-    // without the top-p cut); T > 1 calls with the int2 codec, and every call
-    // behind an expert cache, run as T one-token passes below.
-    if (T > 1 && !layer->cache && c.codec != kCodecInt2) {
+    // The batched kernels cover every codec (with or without the top-p cut;
+    // int2 where hidden and inter are multiples of 256); other T > 1 calls,
+    // and every call behind an expert cache, run as T one-token passes below.
+    if (T > 1 && !layer->cache && batch_codec_supported(c.codec, c.hidden, c.inter)) {
         // batch union: every distinct expert of a launch sequence is read once
         const int tb = layer->W.batch_tokens;
         for (int t0 = 0; t0 < T; t0 += tb) {

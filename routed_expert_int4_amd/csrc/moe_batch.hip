@@ -34,7 +34,9 @@
 // in LDS (double buffered, one barrier per stage) and read as A fragments.
 // MXFP4 experts take the same kernels: an E2M1 code dword becomes the same
 // fragment through v_cvt_scalef32_pk_f16_fp4 and byte permutes, and the
-// E8M0 byte takes the fp16 scale's place.  Int8 experts run every group
+// E8M0 byte takes the fp16 scale's place.  Int2 experts (two rows to a
+// stored nibble) give two fragments per code dword, the even and the odd
+// row's, into accumulators of their own.  Int8 experts run every group
 // step once per nibble plane: the high plane's codes become 16 (c - 8) and
 // the low plane's c exactly in fp16, two MFMAs under the group's one scale.  With the adaptive top-p cut a
 // dropped choice (id -1) gets no dispatch entry and the combine skips it.
@@ -113,14 +115,32 @@ __device__ __forceinline__ f16x8 hi_codes_to_f16x8(unsigned w, const MagicExp& m
                      __builtin_bit_cast(unsigned, q2), __builtin_bit_cast(unsigned, q3)};
     return __builtin_bit_cast(f16x8, v);
 }
+// Int2 codes two rows to a nibble (row 2v in bits 0-1, row 2v + 1 in bits
+// 2-3, each + 2): the fragment of the row in bits 0-1 of every nibble (the
+// other row's is that of w >> 2).
+__device__ __forceinline__ f16x8 codes2_to_f16x8(unsigned w, const MagicExp& mg) {
+    const f16x2 k_lo = {(_Float16)1026.0f, (_Float16)1026.0f};  // 1024 + 2
+    const f16x2 k_hi = {(_Float16)66.0f, (_Float16)66.0f};      // 64 + 2
+    const unsigned w8 = w >> 8;
+    const f16x2 q0 = as_h2((w & 0x00030003u) | mg.e1024) - k_lo;
+    const f16x2 q1 = as_h2((w & 0x00300030u) | mg.e64) - k_hi;
+    const f16x2 q2 = as_h2((w8 & 0x00030003u) | mg.e1024) - k_lo;
+    const f16x2 q3 = as_h2((w8 & 0x00300030u) | mg.e64) - k_hi;
+    const u32x4 v = {__builtin_bit_cast(unsigned, q0), __builtin_bit_cast(unsigned, q1),
+                     __builtin_bit_cast(unsigned, q2), __builtin_bit_cast(unsigned, q3)};
+    return __builtin_bit_cast(f16x8, v);
+}
 // B fragment of one code dword of nibble plane pl (int8: 0 high, 1 low; the
-// two planes' products under one scale sum to the int8 code's product).
+// two planes' products under one scale sum to the int8 code's product) and
+// row parity h (int2: 0 the even row, 1 the odd row of the stored row).
 template <int F>
-__device__ __forceinline__ f16x8 dequant_f16x8(unsigned w, const MagicExp& mg, int pl = 0) {
+__device__ __forceinline__ f16x8 dequant_f16x8(unsigned w, const MagicExp& mg, int pl = 0, int h = 0) {
     if constexpr (F == kCodecMxfp4)
         return fp4_to_f16x8(w);
     else if constexpr (F == kCodecInt8)
         return pl ? codes_to_f16x8<0>(w, mg) : hi_codes_to_f16x8(w, mg);
+    else if constexpr (F == kCodecInt2)
+        return codes2_to_f16x8(h ? w >> 2 : w, mg);
     else
         return codes_to_f16x8(w, mg);
 }
@@ -444,10 +464,15 @@ __device__ __forceinline__ u32x4 gateup_scales4(const uint8_t* gus, int r, int g
 }
 
 // Workgroup = 8 waves over 128 rows of gate and the same 128 rows of up for
-// the (up to) 16 tokens of one tile; wave w owns rows 16w..16w+15.
+// the (up to) 16 tokens of one tile; wave w owns rows 16w..16w+15.  Rows
+// are stored rows: with int2 (two rows per stored row) a workgroup covers
+// 256 matrix rows, with the even and the odd rows in accumulators of their
+// own.
 template <int KG, int F>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) batch_gateup_kernel(BatchArgs a) {
-    constexpr int CK = KG < 16 ? KG : 16;   // groups per LDS stage (16: no register spills)
+    // groups per LDS stage (16 for one fragment per code dword, 8 for two:
+    // int8 planes or int2 rows need the staging registers)
+    constexpr int CK = KG < 16 ? KG : (code_planes(F) > 1 || row_pack(F) > 1 ? 8 : 16);
     constexpr int NST = KG / CK;
     constexpr int PT = CK * 64 / 512;       // 16-byte staging elements per thread
     static_assert(CK % 4 == 0 && KG % CK == 0 && PT >= 1, "gate/up stage shape");
@@ -455,7 +480,8 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) b
     const int tid = threadIdx.x, lane = tid & 63, wv = wave_in_block();
     const int i = lane & 15, q = lane >> 4;
     const int n_tiles = a.n_tiles[0];
-    const int rblocks = a.I / kBlockRows;
+    constexpr int RP = row_pack(F);
+    const int rblocks = a.I / (kBlockRows * RP);
     const int items = n_tiles * rblocks;
     const BlobLayout L = blob_layout(a.H, a.I, F);
     const int row_bytes = a.H / 2;
@@ -471,9 +497,12 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) b
         const uint8_t* gql = blob + L.gate_lo + (size_t)row * row_bytes;  // int8 low planes
         const uint8_t* uql = blob + L.up_lo + (size_t)row * row_bytes;
         const uint8_t* gus = blob + L.gu_s;
+        const uint8_t* gus2 = blob + L.gu_s2;  // int2 odd rows
         const int sm = tid & 15;
         const uint16_t* xsrc = sm < td.count ? a.xa + (size_t)pair_token(a, td.first_pair + sm) * a.H : nullptr;
-        f32x4 accg = {0.f, 0.f, 0.f, 0.f}, accu = {0.f, 0.f, 0.f, 0.f};
+        f32x4 accg[RP], accu[RP];
+#pragma unroll
+        for (int h = 0; h < RP; ++h) accg[h] = accu[h] = f32x4{0.f, 0.f, 0.f, 0.f};
         const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
         constexpr int NS = KG / 4;  // steps of 4 groups
         constexpr int P = code_planes(F);
@@ -489,9 +518,11 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) b
         // fetches step 4h + q of row i (16 bytes, so a wave load covers 16
         // rows x 64 bytes); step s's scales come from lane (i, s % 4) by a
         // lane shuffle
-        auto quad_scales = [&](int h) {
+        auto quad_scales = [&](int h, u32x4 (&v)[RP]) {
             const int s = 4 * h + q;
-            return s < NS ? gateup_scales4<KG, F>(gus, row, 4 * s) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int z = 0; z < RP; ++z)
+                v[z] = s < NS ? gateup_scales4<KG, F>(z ? gus2 : gus, row, 4 * s) : u32x4{0u, 0u, 0u, 0u};
         };
         auto stage_load = [&](int st, u32x4 (&v)[PT]) {
 #pragma unroll
@@ -505,7 +536,10 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) b
         // the next stage's activations in flight during a stage
         u32x4 v[PT];
         stage_load(0, v);
-        u32x4 scl = quad_scales(0), scn = scl;
+        u32x4 scl[RP], scn[RP];
+        quad_scales(0, scl);
+#pragma unroll
+        for (int z = 0; z < RP; ++z) scn[z] = scl[z];
         u32x4 cg0, cu0, cg1 = {0u, 0u, 0u, 0u}, cu1 = cg1;
         load_step(0, cg0, cu0);
         if (NSP > 1) load_step(1, cg1, cu1);
@@ -522,16 +556,20 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) b
             for (int c = 0; c < CK / 4; ++c) {
                 const int sidx = st * (CK / 4) + c;
                 // the next four steps' scales two steps before they are needed
-                if ((sidx & 3) == 0 && sidx > 0) scl = scn;
-                if ((sidx & 3) == 2 && sidx + 2 < NS) scn = quad_scales(sidx / 4 + 1);
-                u32x4 sc0;
-                {
+                if ((sidx & 3) == 0 && sidx > 0) {
+#pragma unroll
+                    for (int z = 0; z < RP; ++z) scl[z] = scn[z];
+                }
+                if ((sidx & 3) == 2 && sidx + 2 < NS) quad_scales(sidx / 4 + 1, scn);
+                u32x4 sc0[RP];
+#pragma unroll
+                for (int z = 0; z < RP; ++z) {
                     const int src = i + 16 * (sidx & 3);
-                    const u32x4 h = scl;
+                    const u32x4 h = scl[z];
 #pragma unroll
                     for (int d = 0; d < 4; ++d) {
                         const unsigned hv = h[d];  // element copied first (bit_cast of an element reads element 0)
-                        sc0[d] = (unsigned)__shfl((int)hv, src);
+                        sc0[z][d] = (unsigned)__shfl((int)hv, src);
                     }
                 }
 #pragma unroll
@@ -544,20 +582,24 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) b
 #pragma unroll
                     for (int m = 0; m < 4; ++m) {
                         const f16x8 af = __builtin_bit_cast(f16x8, xs[buf][((4 * c + m) * 4 + q) * 16 + i]);
-                        const f32x4 dg = mfma16(af, dequant_f16x8<F>(cg0[m], mg, pl), zero);
-                        const f32x4 du = mfma16(af, dequant_f16x8<F>(cu0[m], mg, pl), zero);
-                        const float sg = scale16<F>(sc0[m]);
-                        const float su = scale16<F>(sc0[m] >> 16);
 #pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            accg[j] = fmaf(sg, dg[j], accg[j]);
-                            accu[j] = fmaf(su, du[j], accu[j]);
+                        for (int h = 0; h < RP; ++h) {
+                            const f32x4 dg = mfma16(af, dequant_f16x8<F>(cg0[m], mg, pl, h), zero);
+                            const f32x4 du = mfma16(af, dequant_f16x8<F>(cu0[m], mg, pl, h), zero);
+                            const float sg = scale16<F>(sc0[h][m]);
+                            const float su = scale16<F>(sc0[h][m] >> 16);
+#pragma unroll
+                            for (int j = 0; j < 4; ++j) {
+                                accg[h][j] = fmaf(sg, dg[j], accg[h][j]);
+                                accu[h][j] = fmaf(su, du[j], accu[h][j]);
+                            }
+                            // scale and accumulate now: one group's two
+                            // products in flight at a time (otherwise the
+                            // compiler sinks the FMAs to the end of the stage
+                            // and spills every product)
+                            asm volatile("" : "+v"(accg[h]), "+v"(accu[h]));
+                            __builtin_amdgcn_sched_barrier(0);
                         }
-                        // scale and accumulate now: one group's two products
-                        // in flight at a time (otherwise the compiler sinks the
-                        // FMAs to the end of the stage and spills every product)
-                        asm volatile("" : "+v"(accg), "+v"(accu));
-                        __builtin_amdgcn_sched_barrier(0);
                     }
                     cg0 = cg1;
                     cu0 = cu1;
@@ -574,8 +616,11 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) b
             if (tt < td.count) {
                 const int p = td.first_pair + tt;
                 const int kx = a.kx[pair_token(a, p)];
-                const float g = ldexpf(accg[j], -kx), u = ldexpf(accu[j], -kx);
-                a.h[(size_t)p * a.I + row] = g / (1.0f + expf(-g)) * u;
+#pragma unroll
+                for (int h = 0; h < RP; ++h) {
+                    const float g = ldexpf(accg[h][j], -kx), u = ldexpf(accu[h][j], -kx);
+                    a.h[(size_t)p * a.I + RP * row + h] = g / (1.0f + expf(-g)) * u;
+                }
             }
         }
     }
@@ -635,9 +680,11 @@ __global__ void __launch_bounds__(256) batch_hprep_kernel(BatchArgs a) {
 // ---------------------------------------------------------------- down
 // Workgroup = 8 waves over 128 output rows for the (up to) 16 entries of one
 // tile; each group is two MFMAs (hi and lo parts of h) into one result.
+// Rows are stored rows (int2: 256 output rows, even and odd accumulated
+// apart, the two rows' scales of a group in one dword).
 template <int KGI, int F>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) batch_down_kernel(BatchArgs a) {
-    constexpr int CK = KGI < 16 ? KGI : 16;
+    constexpr int CK = KGI < 16 ? KGI : (code_planes(F) > 1 || row_pack(F) > 1 ? 8 : 16);
     constexpr int NST = KGI / CK;
     constexpr int PART = CK * 64;            // staging elements of one part
     constexpr int PT = 2 * PART / 512;       // per thread (hi and lo)
@@ -646,7 +693,8 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) b
     const int tid = threadIdx.x, lane = tid & 63, wv = wave_in_block();
     const int i = lane & 15, q = lane >> 4;
     const int n_tiles = a.n_tiles[0];
-    const int rblocks = a.H / kBlockRows;
+    constexpr int RP = row_pack(F);
+    const int rblocks = a.H / (kBlockRows * RP);
     const int items = n_tiles * rblocks;
     const BlobLayout L = blob_layout(a.H, a.I, F);
     const int row_bytes = a.I / 2;
@@ -660,10 +708,13 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) b
         const uint8_t* dq = blob + L.down_q + (size_t)row * row_bytes;
         const uint8_t* dql = blob + L.down_lo + (size_t)row * row_bytes;  // int8 low plane
         const uint8_t* dsc = blob + L.down_s;
+        const uint8_t* dsc2 = blob + L.down_s2;  // int2 odd rows
         const int sm = tid & 15;
         const bool has = sm < td.count;
         const size_t src = (size_t)(td.first_pair + sm) * a.I;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        f32x4 acc[RP];
+#pragma unroll
+        for (int h = 0; h < RP; ++h) acc[h] = f32x4{0.f, 0.f, 0.f, 0.f};
         const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
         constexpr int NS = KGI / 4;  // steps of 4 groups
         constexpr int P = code_planes(F);
@@ -678,6 +729,9 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) b
                 const size_t si = scale_index(row, 4 * s + m, KGI, a.down_p);
                 if constexpr (F == kCodecMxfp4)
                     sc[m] = *as_global<uint8_t>(dsc + si);
+                else if constexpr (RP > 1)
+                    sc[m] = (unsigned)*as_global<uint16_t>(reinterpret_cast<const uint16_t*>(dsc) + si) |
+                            ((unsigned)*as_global<uint16_t>(reinterpret_cast<const uint16_t*>(dsc2) + si) << 16);
                 else
                     sc[m] = *as_global<uint16_t>(reinterpret_cast<const uint16_t*>(dsc) + si);
             }
@@ -718,13 +772,16 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) b
                         const int slot = ((4 * c + m) * 4 + q) * 16 + i;
                         const f16x8 ah = __builtin_bit_cast(f16x8, hs[buf][slot]);
                         const f16x8 al = __builtin_bit_cast(f16x8, hs[buf][PART + slot]);
-                        const f16x8 bw = dequant_f16x8<F>(cd0[m], mg, pl);
-                        const f32x4 d = mfma16(al, bw, mfma16(ah, bw, zero));
-                        const float s = scale16<F>(sc0[m]);
 #pragma unroll
-                        for (int j = 0; j < 4; ++j) acc[j] = fmaf(s, d[j], acc[j]);
-                        asm volatile("" : "+v"(acc));
-                        __builtin_amdgcn_sched_barrier(0);
+                        for (int h = 0; h < RP; ++h) {
+                            const f16x8 bw = dequant_f16x8<F>(cd0[m], mg, pl, h);
+                            const f32x4 d = mfma16(al, bw, mfma16(ah, bw, zero));
+                            const float s = scale16<F>(sc0[m] >> (16 * h));
+#pragma unroll
+                            for (int j = 0; j < 4; ++j) acc[h][j] = fmaf(s, d[j], acc[h][j]);
+                            asm volatile("" : "+v"(acc[h]));
+                            __builtin_amdgcn_sched_barrier(0);
+                        }
                     }
                     cd0 = cd1;
                     sc0 = sc1;
@@ -739,7 +796,8 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) b
             const int tt = 4 * q + j;
             if (tt < td.count) {
                 const int p = td.first_pair + tt;
-                a.d[(size_t)p * a.H + row] = ldexpf(acc[j], -a.kh[p]);
+#pragma unroll
+                for (int h = 0; h < RP; ++h) a.d[(size_t)p * a.H + RP * row + h] = ldexpf(acc[h][j], -a.kh[p]);
             }
         }
     }
@@ -801,11 +859,13 @@ int grouped_grid(const BatchArgs& a, int rblocks) {
 
 template <int KG>
 hipError_t launch_gateup(const BatchArgs& a, hipStream_t st) {
-    const dim3 grid(grouped_grid(a, a.I / kBlockRows));
+    const dim3 grid(grouped_grid(a, a.I / (kBlockRows * row_pack(a.codec))));
     if (a.codec == kCodecMxfp4)
         hipLaunchKernelGGL((batch_gateup_kernel<KG, kCodecMxfp4>), grid, dim3(512), 0, st, a);
     else if (a.codec == kCodecInt8)
         hipLaunchKernelGGL((batch_gateup_kernel<KG, kCodecInt8>), grid, dim3(512), 0, st, a);
+    else if (a.codec == kCodecInt2)
+        hipLaunchKernelGGL((batch_gateup_kernel<KG, kCodecInt2>), grid, dim3(512), 0, st, a);
     else if (a.codec == kCodecInt4)
         hipLaunchKernelGGL((batch_gateup_kernel<KG, kCodecInt4>), grid, dim3(512), 0, st, a);
     else
@@ -815,11 +875,13 @@ hipError_t launch_gateup(const BatchArgs& a, hipStream_t st) {
 
 template <int KGI>
 hipError_t launch_down(const BatchArgs& a, hipStream_t st) {
-    const dim3 grid(grouped_grid(a, a.H / kBlockRows));
+    const dim3 grid(grouped_grid(a, a.H / (kBlockRows * row_pack(a.codec))));
     if (a.codec == kCodecMxfp4)
         hipLaunchKernelGGL((batch_down_kernel<KGI, kCodecMxfp4>), grid, dim3(512), 0, st, a);
     else if (a.codec == kCodecInt8)
         hipLaunchKernelGGL((batch_down_kernel<KGI, kCodecInt8>), grid, dim3(512), 0, st, a);
+    else if (a.codec == kCodecInt2)
+        hipLaunchKernelGGL((batch_down_kernel<KGI, kCodecInt2>), grid, dim3(512), 0, st, a);
     else if (a.codec == kCodecInt4)
         hipLaunchKernelGGL((batch_down_kernel<KGI, kCodecInt4>), grid, dim3(512), 0, st, a);
     else
@@ -888,6 +950,11 @@ hipError_t batch_combine(const BatchArgs& a, hipStream_t st) {
 
 bool batch_shape_supported(int hidden, int inter) {
     return hidden % 256 == 0 && inter % kBlockRows == 0 && hidden / 32 <= 256 && inter / 32 <= 128;
+}
+
+bool batch_codec_supported(int codec, int hidden, int inter) {
+    const int rp = row_pack(codec);
+    return batch_shape_supported(hidden, inter) && hidden % (kBlockRows * rp) == 0 && inter % (kBlockRows * rp) == 0;
 }
 
 }  // namespace moe

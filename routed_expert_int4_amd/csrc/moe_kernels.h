@@ -31,7 +31,7 @@ struct DecodeArgs {
     int H, I, E, G, TG, K, S;
     float rsf;
     float top_p;                     // adaptive expert top-p (1: plain top-k)
-    int codec;                       // kCodecInt4 or kCodecMxfp4
+    int codec;                       // weight codec (kCodecInt4 .. kCodecInt2)
     // Expert-cache mode: routed slot j reads blobs[j] instead of
     // table[ids[j]] (the host resolved the routing before the launch).
     int direct;
@@ -111,7 +111,7 @@ struct BatchArgs {
     int router_splits;           // column splits of the router (power of two, hidden % (64 * splits) == 0)
     float rsf;
     float top_p;                 // adaptive expert top-p (1: plain top-k); dropped choices get id -1
-    int codec;                   // kCodecInt4 or kCodecMxfp4
+    int codec;                   // weight codec (kCodecInt4 .. kCodecInt2)
 };
 
 // Upper bound of the tiles of a call of T tokens.
@@ -140,5 +140,8 @@ hipError_t batch_hprep(const BatchArgs& a, hipStream_t st);
 hipError_t batch_down(const BatchArgs& a, hipStream_t st);
 hipError_t batch_combine(const BatchArgs& a, hipStream_t st);
 bool batch_shape_supported(int hidden, int inter);
+// The batched kernels serve this codec at this shape (int2: hidden and
+// inter multiples of 256, a workgroup's 128 stored rows being 256 rows).
+bool batch_codec_supported(int codec, int hidden, int inter);
 
 }  // namespace moe

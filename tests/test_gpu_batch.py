@@ -337,6 +337,69 @@ def test_glm_int8_prefill_chunk(torch_cuda):
     layer.close()
 
 
+# ---------------------------------------------------------------- int2 experts
+@pytest.mark.parametrize("cfg_name,T,top_p", [("MID_A", 37, 1.0), ("MID_B", 16, 1.0), ("MID_C", 5, 1.0),
+                                              ("MID_A", 3, 1.0), ("MID_A", 21, 0.7)])
+def test_batch_int2_parity(torch_cuda, cfg_name, T, top_p):
+    """Batch-union calls of int2 layers (two rows to a stored nibble: two
+    fragments per code dword, even and odd rows accumulated apart, each
+    under its own scale) against the oracle."""
+    import dataclasses
+    from routed_expert_int4_amd.layer import DeviceLayer
+    cfg = {"MID_A": MID_A, "MID_B": MID_B, "MID_C": MID_C}[cfg_name]
+    cfg = dataclasses.replace(cfg, codec="int2", top_p=top_p)
+    say(f"[gpu] batched int2 {cfg_name} T={T} top_p={top_p}")
+    weights = synth.gen_layer(cfg, seed=0)
+    layer = DeviceLayer(weights, max_T=T)
+    x = synth.gen_tokens(cfg, T, seed=4)
+    y, ids, w = run_batch(torch_cuda, layer, x)
+    res = check_layer(weights, x, y, ids, w)
+    say(f"[gpu] batched int2 {cfg_name}: worst rel err {res['worst_rel']:.3g}, excused {res['excused']}")
+    layer.close()
+
+
+def test_batch_int2_extreme_codes(torch_cuda):
+    """Batched int2 calls with whole rows of codes -2 and 1 (every stored
+    nibble 0x0 or 0xF) and activations of std 1e-3 and 300."""
+    import dataclasses
+    from routed_expert_int4_amd.layer import DeviceLayer
+    cfg = dataclasses.replace(MID_A, codec="int2")
+    say("[gpu] batched int2 extreme codes")
+    base = synth.gen_layer(cfg, seed=3)
+    gq = base.gate_q.copy()
+    gq[:, 0::3, :] = 0xAA  # -2 in every 2-bit field
+    gq[:, 1::3, :] = 0x55  # 1
+    dq = base.down_q.copy()
+    dq[:, 0::2, :] = 0xAA
+    weights = dataclasses.replace(base, gate_q=gq, down_q=dq)
+    layer = DeviceLayer(weights, max_T=19)
+    for std in (1e-3, 300.0):
+        x = synth.gen_tokens(cfg, 19, seed=11, std=std)
+        y, ids, w = run_batch(torch_cuda, layer, x)
+        res = check_layer(weights, x, y, ids, w)
+        say(f"[gpu] batched int2 extremes std {std}: worst rel err {res['worst_rel']:.3g}")
+    layer.close()
+
+
+def test_glm_int2_prefill_chunk(torch_cuda):
+    """GLM-shaped int2 layer, one 256-token prefill chunk: routing of every
+    token against the oracle, outputs on a sample."""
+    import dataclasses
+    from routed_expert_int4_amd.layer import DeviceLayer
+    cfg = dataclasses.replace(synth.GLM, codec="int2")
+    say("[gpu] GLM int2 prefill chunk of 256")
+    weights = synth.gen_layer(cfg, seed=0)
+    layer = DeviceLayer(weights, max_T=256)
+    x = synth.gen_tokens(cfg, 256, seed=5)
+    y, ids, w = run_batch(torch_cuda, layer, x)
+    ids_ref, w_ref, gap = oracle.route(weights, x)
+    excused = check_routing(cfg, ids, w, ids_ref, w_ref, gap)
+    rows = sorted(set([0, 1, 128, 255] + list(np.argsort(gap)[:2])))
+    res = check_layer(weights, x, y, ids, w, rows=rows)
+    say(f"[gpu] GLM int2 prefill: {len(excused)} excused, sampled worst rel err {res['worst_rel']:.3g}")
+    layer.close()
+
+
 def test_glm_mxfp4_prefill_chunk(torch_cuda):
     """GLM-shaped MXFP4 layer, one 512-token prefill chunk: routing of every
     token against the oracle, outputs on a sample."""

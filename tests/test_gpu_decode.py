@@ -313,8 +313,9 @@ def test_mxfp4_extreme_scales_and_activations(torch_cuda):
 
 @pytest.mark.parametrize("codec", ["int2"])
 def test_codec_batched_call_runs_per_token(torch_cuda, codec):
-    """A T > 1 call of an int2 layer runs as T one-token passes:
-    bit-identical to T separate calls, and within the oracle's tolerance."""
+    """A T > 1 call of an int2 layer whose inter is not a multiple of 256
+    runs as T one-token passes: bit-identical to T separate calls, and
+    within the oracle's tolerance."""
     from routed_expert_int4_amd.layer import DeviceLayer
     cfg = with_codec(synth.TINY, codec)
     weights = synth.gen_layer(cfg, seed=0)

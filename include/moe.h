@@ -85,8 +85,8 @@ typedef enum {
  *   [2t, 2t + 2) of byte j (code arrays [inter][hidden/4], [hidden][inter/4]),
  *   values -2..1.
  * The batched (batch-union, matrix-core) kernels serve every codec (int2
- * where hidden and inter are multiples of 256; other int2 T > 1 calls run as
- * T one-token passes). */
+ * where hidden is a multiple of 512 and inter of 256; other int2 T > 1 calls
+ * run as T one-token passes). */
 enum { MOE_CODEC_INT4 = 0, MOE_CODEC_MXFP4 = 1, MOE_CODEC_INT8 = 2, MOE_CODEC_INT2 = 3 };
 
 typedef struct {
@@ -183,8 +183,8 @@ moe_status_t moe_router_topk(moe_layer_t* layer, const uint16_t* d_x, int T, int
  * tokens, a dispatch of the (token, slot) entries by expert, grouped gate/up
  * and down projections on the matrix cores, and the combine; tokens are
  * taken in launch sequences of at most min(max_T, 8192 / top_k); T > 1 with
- * int2 experts and hidden or inter not a multiple of 256 runs the decode
- * kernels token by token.
+ * int2 experts, hidden not a multiple of 512 or inter not a multiple of 256
+ * runs the decode kernels token by token.
  * With all experts resident the call is asynchronous.  With an attached
  * expert cache tokens are processed one at a time; the call blocks the host
  * once per token until its routing is known, issues the copies of missing

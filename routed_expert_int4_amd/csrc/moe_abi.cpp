@@ -523,7 +523,7 @@ moe_status_t moe_layer_forward(moe_layer_t* layer, const uint16_t* d_x, int T, f
     int32_t* ids_base = d_ids ? d_ids : reinterpret_cast<int32_t*>(layer->ws + layer->W.ids);
     float* w_base = d_w ? d_w : reinterpret_cast<float*>(layer->ws + layer->W.w);
     // The batched kernels cover every codec (with or without the top-p cut;
-    // int2 where hidden and inter are multiples of 256); other T > 1 calls,
+    // int2 where hidden is a multiple of 512 and inter of 256); other T > 1 calls,
     // and every call behind an expert cache, run as T one-token passes below.
     if (T > 1 && !layer->cache && batch_codec_supported(c.codec, c.hidden, c.inter)) {
         // batch union: every distinct expert of a launch sequence is read once

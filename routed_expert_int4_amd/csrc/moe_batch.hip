@@ -16,7 +16,7 @@
 //      entries of one expert per tile; the shared expert's T tokens last);
 //   4. gate/up: grouped int4 GEMM per (tile, 128 rows) on the matrix cores;
 //   5. h prep: h per entry as scaled fp16 hi + lo parts in MFMA order;
-//   6. down: grouped int4 GEMM per (tile, 128 output rows);
+//   6. down: grouped int4 GEMM per (tile, 256 output rows);
 //   7. combine: y = sum_j w_j d_j + d_shared in slot order (no atomics).
 //
 // Grouped GEMM scheme.  v_mfma_f32_16x16x32_f16 with the 16 tokens of a tile
@@ -678,23 +678,27 @@ __global__ void __launch_bounds__(256) batch_hprep_kernel(BatchArgs a) {
 }
 
 // ---------------------------------------------------------------- down
-// Workgroup = 8 waves over 128 output rows for the (up to) 16 entries of one
-// tile; each group is two MFMAs (hi and lo parts of h) into one result.
-// Rows are stored rows (int2: 256 output rows, even and odd accumulated
-// apart, the two rows' scales of a group in one dword).
+constexpr int kDownThreads = 1024;                   // 16 waves
+constexpr int kDownBlockRows = kDownThreads / 4;     // 16 rows per wave
+// Workgroup = 16 waves over 256 output rows for the (up to) 16 entries of
+// one tile (one workgroup per CU: the staged h, as many bytes per item as
+// 128 rows of codes, serves twice the rows); each group is two MFMAs (hi and
+// lo parts of h) into one result.  Rows are stored rows (int2: 512 output
+// rows, even and odd accumulated apart, the two rows' scales of a group in
+// one dword).
 template <int KGI, int F>
-__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) batch_down_kernel(BatchArgs a) {
+__global__ void __launch_bounds__(kDownThreads) __attribute__((amdgpu_waves_per_eu(4))) batch_down_kernel(BatchArgs a) {
     constexpr int CK = KGI < 16 ? KGI : (code_planes(F) > 1 || row_pack(F) > 1 ? 8 : 16);
     constexpr int NST = KGI / CK;
     constexpr int PART = CK * 64;            // staging elements of one part
-    constexpr int PT = 2 * PART / 512;       // per thread (hi and lo)
+    constexpr int PT = (2 * PART + kDownThreads - 1) / kDownThreads;  // per thread (hi and lo)
     static_assert(CK % 4 == 0 && KGI % CK == 0 && PT >= 1, "down stage shape");
     __shared__ u32x4 hs[2][2 * PART];        // [part * PART + (g * 4 + q) * 16 + token]
     const int tid = threadIdx.x, lane = tid & 63, wv = wave_in_block();
     const int i = lane & 15, q = lane >> 4;
     const int n_tiles = a.n_tiles[0];
     constexpr int RP = row_pack(F);
-    const int rblocks = a.H / (kBlockRows * RP);
+    const int rblocks = a.H / (kDownBlockRows * RP);
     const int items = n_tiles * rblocks;
     const BlobLayout L = blob_layout(a.H, a.I, F);
     const int row_bytes = a.I / 2;
@@ -704,7 +708,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) b
         const int tile = item / rblocks, rb = item - tile * rblocks;
         const Tile td = a.tiles[tile];
         const uint8_t* blob = td.expert < a.E ? a.table[td.expert] : a.shared_blob;
-        const int row = rb * kBlockRows + wv * 16 + i;
+        const int row = rb * kDownBlockRows + wv * 16 + i;
         const uint8_t* dq = blob + L.down_q + (size_t)row * row_bytes;
         const uint8_t* dql = blob + L.down_lo + (size_t)row * row_bytes;  // int8 low plane
         const uint8_t* dsc = blob + L.down_s;
@@ -739,7 +743,8 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) b
         auto stage_load = [&](int st, u32x4 (&v)[PT]) {
 #pragma unroll
             for (int r = 0; r < PT; ++r) {
-                const int e = tid + 512 * r;
+                const int e = tid + kDownThreads * r;
+                if (e >= 2 * PART) break;
                 const int part = e / PART, rest = e - part * PART;
                 const uint16_t* base = part ? a.ha_lo : a.ha_hi;
                 v[r] = has ? *as_global<u32x4>(base + src + (size_t)((st * CK + (rest >> 6)) * 4 + ((rest >> 4) & 3)) * 8)
@@ -755,7 +760,8 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) b
         for (int st = 0; st < NST; ++st, ++gs) {
             const int buf = gs & 1;
 #pragma unroll
-            for (int r = 0; r < PT; ++r) hs[buf][tid + 512 * r] = v[r];
+            for (int r = 0; r < PT; ++r)
+                if (tid + kDownThreads * r < 2 * PART) hs[buf][tid + kDownThreads * r] = v[r];
             __syncthreads();
             if (st + 1 < NST) stage_load(st + 1, v);
 #pragma unroll
@@ -875,15 +881,16 @@ hipError_t launch_gateup(const BatchArgs& a, hipStream_t st) {
 
 template <int KGI>
 hipError_t launch_down(const BatchArgs& a, hipStream_t st) {
-    const dim3 grid(grouped_grid(a, a.H / (kBlockRows * row_pack(a.codec))));
+    const int g = grouped_grid(a, a.H / (kDownBlockRows * row_pack(a.codec)));
+    const dim3 grid(g < kGroupedGrid / 2 ? g : kGroupedGrid / 2);  // one workgroup per CU
     if (a.codec == kCodecMxfp4)
-        hipLaunchKernelGGL((batch_down_kernel<KGI, kCodecMxfp4>), grid, dim3(512), 0, st, a);
+        hipLaunchKernelGGL((batch_down_kernel<KGI, kCodecMxfp4>), grid, dim3(kDownThreads), 0, st, a);
     else if (a.codec == kCodecInt8)
-        hipLaunchKernelGGL((batch_down_kernel<KGI, kCodecInt8>), grid, dim3(512), 0, st, a);
+        hipLaunchKernelGGL((batch_down_kernel<KGI, kCodecInt8>), grid, dim3(kDownThreads), 0, st, a);
     else if (a.codec == kCodecInt2)
-        hipLaunchKernelGGL((batch_down_kernel<KGI, kCodecInt2>), grid, dim3(512), 0, st, a);
+        hipLaunchKernelGGL((batch_down_kernel<KGI, kCodecInt2>), grid, dim3(kDownThreads), 0, st, a);
     else if (a.codec == kCodecInt4)
-        hipLaunchKernelGGL((batch_down_kernel<KGI, kCodecInt4>), grid, dim3(512), 0, st, a);
+        hipLaunchKernelGGL((batch_down_kernel<KGI, kCodecInt4>), grid, dim3(kDownThreads), 0, st, a);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();
@@ -954,7 +961,8 @@ bool batch_shape_supported(int hidden, int inter) {
 
 bool batch_codec_supported(int codec, int hidden, int inter) {
     const int rp = row_pack(codec);
-    return batch_shape_supported(hidden, inter) && hidden % (kBlockRows * rp) == 0 && inter % (kBlockRows * rp) == 0;
+    return batch_shape_supported(hidden, inter) && hidden % (kDownBlockRows * rp) == 0 &&
+           inter % (kBlockRows * rp) == 0;
 }
 
 }  // namespace moe

@@ -63,7 +63,7 @@ hipError_t decode_down_combine(const DecodeArgs& a, hipStream_t st, const Launch
 bool decode_shape_supported(int hidden, int inter, int top_k, int n_shared);
 
 // ------------------------------------------------------------ batched path
-// Tokens per MFMA tile and output rows per workgroup of the grouped kernels.
+// Tokens per MFMA tile and rows per gate/up workgroup of the grouped kernels.
 constexpr int kTileTokens = 16;
 constexpr int kBlockRows = 128;
 // Largest number of (token, routed slot) entries one dispatch sorts in LDS.
@@ -140,8 +140,9 @@ hipError_t batch_hprep(const BatchArgs& a, hipStream_t st);
 hipError_t batch_down(const BatchArgs& a, hipStream_t st);
 hipError_t batch_combine(const BatchArgs& a, hipStream_t st);
 bool batch_shape_supported(int hidden, int inter);
-// The batched kernels serve this codec at this shape (int2: hidden and
-// inter multiples of 256, a workgroup's 128 stored rows being 256 rows).
+// The batched kernels serve this codec at this shape (int2: hidden a
+// multiple of 512 and inter of 256, a workgroup's stored rows being twice
+// as many matrix rows).
 bool batch_codec_supported(int codec, int hidden, int inter);
 
 }  // namespace moe

@@ -467,6 +467,7 @@ BatchArgs batch_args(moe_layer_t* L, const uint16_t* x, int n, int32_t* ids, flo
     b.rsf = c.routed_scaling_factor;
     b.top_p = c.top_p;
     b.codec = c.codec;
+    b.tile_tokens = batch_tile_tokens(c.codec, n, c.top_k, c.n_experts);
     return b;
 }
 

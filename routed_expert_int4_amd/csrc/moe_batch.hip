@@ -364,7 +364,7 @@ __global__ void __launch_bounds__(1024) batch_dispatch_kernel(BatchArgs a) {
         for (int r = 0; r < 4; ++r) {
             const int e = 4 * tid + r;
             c[r] = e < a.E ? cnt[e] : 0;
-            nt[r] = (c[r] + kTileTokens - 1) / kTileTokens;
+            nt[r] = (c[r] + a.tile_tokens - 1) / a.tile_tokens;
             f[r] = c[r] > 0 ? 1 : 0;
             sc += c[r];
             stl += nt[r];
@@ -413,8 +413,8 @@ __global__ void __launch_bounds__(1024) batch_dispatch_kernel(BatchArgs a) {
         a.offsets[e] = off[e];
         if (c > 0) {
             a.distinct[dpos[e]] = e;
-            for (int i = 0; i * kTileTokens < c; ++i)
-                a.tiles[toff[e] + i] = Tile{e, off[e] + kTileTokens * i, min(kTileTokens, c - kTileTokens * i), 0};
+            for (int i = 0; i * a.tile_tokens < c; ++i)
+                a.tiles[toff[e] + i] = Tile{e, off[e] + a.tile_tokens * i, min(a.tile_tokens, c - a.tile_tokens * i), 0};
         }
     }
     if (tid == 0) {
@@ -422,8 +422,8 @@ __global__ void __launch_bounds__(1024) batch_dispatch_kernel(BatchArgs a) {
         a.n_distinct[0] = totals[2];
         int nt = totals[1];
         for (int s = 0; s < a.S; ++s)
-            for (int t0 = 0; t0 < a.T; t0 += kTileTokens)
-                a.tiles[nt++] = Tile{a.E, n + t0, min(kTileTokens, a.T - t0), 0};
+            for (int t0 = 0; t0 < a.T; t0 += a.tile_tokens)
+                a.tiles[nt++] = Tile{a.E, n + t0, min(a.tile_tokens, a.T - t0), 0};
         a.n_tiles[0] = nt;
     }
 }
@@ -468,15 +468,17 @@ __device__ __forceinline__ u32x4 gateup_scales4(const uint8_t* gus, int r, int g
 // are stored rows: with int2 (two rows per stored row) a workgroup covers
 // 256 matrix rows, with the even and the odd rows in accumulators of their
 // own.
-template <int KG, int F>
+template <int KG, int F, int TT>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) batch_gateup_kernel(BatchArgs a) {
-    // groups per LDS stage (16 for one fragment per code dword, 8 for two:
-    // int8 planes or int2 rows need the staging registers)
-    constexpr int CK = KG < 16 ? KG : (code_planes(F) > 1 || row_pack(F) > 1 ? 8 : 16);
+    // groups per LDS stage (8 when a 32-entry tile's two MFMA row blocks or
+    // a two-fragment codec need the staging registers, else 16)
+    static_assert(TT == 16 || TT == 32, "tile entries");
+    constexpr int NB = TT / 16;             // MFMA row blocks (16 tokens each) per tile
+    constexpr int CK = KG < 16 ? KG : (NB > 1 || code_planes(F) > 1 || row_pack(F) > 1 ? 8 : 16);
     constexpr int NST = KG / CK;
-    constexpr int PT = CK * 64 / 512;       // 16-byte staging elements per thread
+    constexpr int PT = CK * 64 * NB / 512;  // 16-byte staging elements per thread
     static_assert(CK % 4 == 0 && KG % CK == 0 && PT >= 1, "gate/up stage shape");
-    __shared__ u32x4 xs[2][CK * 64];        // [(g * 4 + q) * 16 + token]
+    __shared__ u32x4 xs[2][CK * 64 * NB];   // [(g * 4 + q) * TT + token]
     const int tid = threadIdx.x, lane = tid & 63, wv = wave_in_block();
     const int i = lane & 15, q = lane >> 4;
     const int n_tiles = a.n_tiles[0];
@@ -498,11 +500,13 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) b
         const uint8_t* uql = blob + L.up_lo + (size_t)row * row_bytes;
         const uint8_t* gus = blob + L.gu_s;
         const uint8_t* gus2 = blob + L.gu_s2;  // int2 odd rows
-        const int sm = tid & 15;
+        const int sm = tid & (TT - 1);
         const uint16_t* xsrc = sm < td.count ? a.xa + (size_t)pair_token(a, td.first_pair + sm) * a.H : nullptr;
-        f32x4 accg[RP], accu[RP];
+        f32x4 accg[RP][NB], accu[RP][NB];
 #pragma unroll
-        for (int h = 0; h < RP; ++h) accg[h] = accu[h] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int h = 0; h < RP; ++h)
+#pragma unroll
+            for (int z = 0; z < NB; ++z) accg[h][z] = accu[h][z] = f32x4{0.f, 0.f, 0.f, 0.f};
         const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
         constexpr int NS = KG / 4;  // steps of 4 groups
         constexpr int P = code_planes(F);
@@ -528,7 +532,8 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) b
 #pragma unroll
             for (int r = 0; r < PT; ++r) {
                 const int e = tid + 512 * r;
-                v[r] = xsrc ? *as_global<u32x4>(xsrc + (size_t)((st * CK + (e >> 6)) * 4 + ((e >> 4) & 3)) * 8)
+                v[r] = xsrc ? *as_global<u32x4>(xsrc + (size_t)((st * CK + e / (4 * TT)) * 4 +
+                                                        (e / TT) % 4) * 8)
                             : u32x4{0u, 0u, 0u, 0u};
             }
         };
@@ -581,24 +586,30 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) b
                     transpose_quarters(cu0);
 #pragma unroll
                     for (int m = 0; m < 4; ++m) {
-                        const f16x8 af = __builtin_bit_cast(f16x8, xs[buf][((4 * c + m) * 4 + q) * 16 + i]);
 #pragma unroll
                         for (int h = 0; h < RP; ++h) {
-                            const f32x4 dg = mfma16(af, dequant_f16x8<F>(cg0[m], mg, pl, h), zero);
-                            const f32x4 du = mfma16(af, dequant_f16x8<F>(cu0[m], mg, pl, h), zero);
+                            const f16x8 bg = dequant_f16x8<F>(cg0[m], mg, pl, h);
+                            const f16x8 bu = dequant_f16x8<F>(cu0[m], mg, pl, h);
                             const float sg = scale16<F>(sc0[h][m]);
                             const float su = scale16<F>(sc0[h][m] >> 16);
 #pragma unroll
-                            for (int j = 0; j < 4; ++j) {
-                                accg[h][j] = fmaf(sg, dg[j], accg[h][j]);
-                                accu[h][j] = fmaf(su, du[j], accu[h][j]);
+                            for (int z = 0; z < NB; ++z) {
+                                const f16x8 af = __builtin_bit_cast(
+                                    f16x8, xs[buf][((4 * c + m) * 4 + q) * TT + 16 * z + i]);
+                                const f32x4 dg = mfma16(af, bg, zero);
+                                const f32x4 du = mfma16(af, bu, zero);
+#pragma unroll
+                                for (int j = 0; j < 4; ++j) {
+                                    accg[h][z][j] = fmaf(sg, dg[j], accg[h][z][j]);
+                                    accu[h][z][j] = fmaf(su, du[j], accu[h][z][j]);
+                                }
+                                // scale and accumulate now: one group's two
+                                // products in flight at a time (otherwise the
+                                // compiler sinks the FMAs to the end of the
+                                // stage and spills every product)
+                                asm volatile("" : "+v"(accg[h][z]), "+v"(accu[h][z]));
+                                __builtin_amdgcn_sched_barrier(0);
                             }
-                            // scale and accumulate now: one group's two
-                            // products in flight at a time (otherwise the
-                            // compiler sinks the FMAs to the end of the stage
-                            // and spills every product)
-                            asm volatile("" : "+v"(accg[h]), "+v"(accu[h]));
-                            __builtin_amdgcn_sched_barrier(0);
                         }
                     }
                     cg0 = cg1;
@@ -611,18 +622,20 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) b
             }
         }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int tt = 4 * q + j;
-            if (tt < td.count) {
-                const int p = td.first_pair + tt;
-                const int kx = a.kx[pair_token(a, p)];
+        for (int z = 0; z < NB; ++z)
 #pragma unroll
-                for (int h = 0; h < RP; ++h) {
-                    const float g = ldexpf(accg[h][j], -kx), u = ldexpf(accu[h][j], -kx);
-                    a.h[(size_t)p * a.I + RP * row + h] = g / (1.0f + expf(-g)) * u;
+            for (int j = 0; j < 4; ++j) {
+                const int tt = 16 * z + 4 * q + j;
+                if (tt < td.count) {
+                    const int p = td.first_pair + tt;
+                    const int kx = a.kx[pair_token(a, p)];
+#pragma unroll
+                    for (int h = 0; h < RP; ++h) {
+                        const float g = ldexpf(accg[h][z][j], -kx), u = ldexpf(accu[h][z][j], -kx);
+                        a.h[(size_t)p * a.I + RP * row + h] = g / (1.0f + expf(-g)) * u;
+                    }
                 }
             }
-        }
     }
 }
 
@@ -686,14 +699,16 @@ constexpr int kDownBlockRows = kDownThreads / 4;     // 16 rows per wave
 // lo parts of h) into one result.  Rows are stored rows (int2: 512 output
 // rows, even and odd accumulated apart, the two rows' scales of a group in
 // one dword).
-template <int KGI, int F>
+template <int KGI, int F, int TT>
 __global__ void __launch_bounds__(kDownThreads) __attribute__((amdgpu_waves_per_eu(4))) batch_down_kernel(BatchArgs a) {
-    constexpr int CK = KGI < 16 ? KGI : (code_planes(F) > 1 || row_pack(F) > 1 ? 8 : 16);
+    static_assert(TT == 16 || TT == 32, "tile entries");
+    constexpr int NB = TT / 16;              // MFMA row blocks per tile
+    constexpr int CK = KGI < 16 ? KGI : (NB > 1 || code_planes(F) > 1 || row_pack(F) > 1 ? 8 : 16);
     constexpr int NST = KGI / CK;
-    constexpr int PART = CK * 64;            // staging elements of one part
+    constexpr int PART = CK * 64 * NB;       // staging elements of one part
     constexpr int PT = (2 * PART + kDownThreads - 1) / kDownThreads;  // per thread (hi and lo)
     static_assert(CK % 4 == 0 && KGI % CK == 0 && PT >= 1, "down stage shape");
-    __shared__ u32x4 hs[2][2 * PART];        // [part * PART + (g * 4 + q) * 16 + token]
+    __shared__ u32x4 hs[2][2 * PART];        // [part * PART + (g * 4 + q) * TT + token]
     const int tid = threadIdx.x, lane = tid & 63, wv = wave_in_block();
     const int i = lane & 15, q = lane >> 4;
     const int n_tiles = a.n_tiles[0];
@@ -713,12 +728,14 @@ __global__ void __launch_bounds__(kDownThreads) __attribute__((amdgpu_waves_per_
         const uint8_t* dql = blob + L.down_lo + (size_t)row * row_bytes;  // int8 low plane
         const uint8_t* dsc = blob + L.down_s;
         const uint8_t* dsc2 = blob + L.down_s2;  // int2 odd rows
-        const int sm = tid & 15;
+        const int sm = tid & (TT - 1);
         const bool has = sm < td.count;
         const size_t src = (size_t)(td.first_pair + sm) * a.I;
-        f32x4 acc[RP];
+        f32x4 acc[RP][NB];
 #pragma unroll
-        for (int h = 0; h < RP; ++h) acc[h] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int h = 0; h < RP; ++h)
+#pragma unroll
+            for (int z = 0; z < NB; ++z) acc[h][z] = f32x4{0.f, 0.f, 0.f, 0.f};
         const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
         constexpr int NS = KGI / 4;  // steps of 4 groups
         constexpr int P = code_planes(F);
@@ -747,7 +764,8 @@ __global__ void __launch_bounds__(kDownThreads) __attribute__((amdgpu_waves_per_
                 if (e >= 2 * PART) break;
                 const int part = e / PART, rest = e - part * PART;
                 const uint16_t* base = part ? a.ha_lo : a.ha_hi;
-                v[r] = has ? *as_global<u32x4>(base + src + (size_t)((st * CK + (rest >> 6)) * 4 + ((rest >> 4) & 3)) * 8)
+                v[r] = has ? *as_global<u32x4>(base + src + (size_t)((st * CK + rest / (4 * TT)) * 4 +
+                                                                 (rest / TT) % 4) * 8)
                            : u32x4{0u, 0u, 0u, 0u};
             }
         };
@@ -775,18 +793,21 @@ __global__ void __launch_bounds__(kDownThreads) __attribute__((amdgpu_waves_per_
                     transpose_quarters(cd0);
 #pragma unroll
                     for (int m = 0; m < 4; ++m) {
-                        const int slot = ((4 * c + m) * 4 + q) * 16 + i;
-                        const f16x8 ah = __builtin_bit_cast(f16x8, hs[buf][slot]);
-                        const f16x8 al = __builtin_bit_cast(f16x8, hs[buf][PART + slot]);
 #pragma unroll
                         for (int h = 0; h < RP; ++h) {
                             const f16x8 bw = dequant_f16x8<F>(cd0[m], mg, pl, h);
-                            const f32x4 d = mfma16(al, bw, mfma16(ah, bw, zero));
                             const float s = scale16<F>(sc0[m] >> (16 * h));
 #pragma unroll
-                            for (int j = 0; j < 4; ++j) acc[h][j] = fmaf(s, d[j], acc[h][j]);
-                            asm volatile("" : "+v"(acc[h]));
-                            __builtin_amdgcn_sched_barrier(0);
+                            for (int z = 0; z < NB; ++z) {
+                                const int slot = ((4 * c + m) * 4 + q) * TT + 16 * z + i;
+                                const f16x8 ah = __builtin_bit_cast(f16x8, hs[buf][slot]);
+                                const f16x8 al = __builtin_bit_cast(f16x8, hs[buf][PART + slot]);
+                                const f32x4 d = mfma16(al, bw, mfma16(ah, bw, zero));
+#pragma unroll
+                                for (int j = 0; j < 4; ++j) acc[h][z][j] = fmaf(s, d[j], acc[h][z][j]);
+                                asm volatile("" : "+v"(acc[h][z]));
+                                __builtin_amdgcn_sched_barrier(0);
+                            }
                         }
                     }
                     cd0 = cd1;
@@ -798,14 +819,17 @@ __global__ void __launch_bounds__(kDownThreads) __attribute__((amdgpu_waves_per_
             }
         }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int tt = 4 * q + j;
-            if (tt < td.count) {
-                const int p = td.first_pair + tt;
+        for (int z = 0; z < NB; ++z)
 #pragma unroll
-                for (int h = 0; h < RP; ++h) a.d[(size_t)p * a.H + RP * row + h] = ldexpf(acc[h][j], -a.kh[p]);
+            for (int j = 0; j < 4; ++j) {
+                const int tt = 16 * z + 4 * q + j;
+                if (tt < td.count) {
+                    const int p = td.first_pair + tt;
+#pragma unroll
+                    for (int h = 0; h < RP; ++h)
+                        a.d[(size_t)p * a.H + RP * row + h] = ldexpf(acc[h][z][j], -a.kh[p]);
+                }
             }
-        }
     }
 }
 
@@ -863,17 +887,41 @@ int grouped_grid(const BatchArgs& a, int rblocks) {
     return (int)(items < kGroupedGrid ? items : kGroupedGrid);
 }
 
-template <int KG>
-hipError_t launch_gateup(const BatchArgs& a, hipStream_t st) {
+template <int KG, int TT>
+hipError_t launch_gateup_t(const BatchArgs& a, hipStream_t st) {
     const dim3 grid(grouped_grid(a, a.I / (kBlockRows * row_pack(a.codec))));
     if (a.codec == kCodecMxfp4)
-        hipLaunchKernelGGL((batch_gateup_kernel<KG, kCodecMxfp4>), grid, dim3(512), 0, st, a);
-    else if (a.codec == kCodecInt8)
-        hipLaunchKernelGGL((batch_gateup_kernel<KG, kCodecInt8>), grid, dim3(512), 0, st, a);
-    else if (a.codec == kCodecInt2)
-        hipLaunchKernelGGL((batch_gateup_kernel<KG, kCodecInt2>), grid, dim3(512), 0, st, a);
+        hipLaunchKernelGGL((batch_gateup_kernel<KG, kCodecMxfp4, TT>), grid, dim3(512), 0, st, a);
     else if (a.codec == kCodecInt4)
-        hipLaunchKernelGGL((batch_gateup_kernel<KG, kCodecInt4>), grid, dim3(512), 0, st, a);
+        hipLaunchKernelGGL((batch_gateup_kernel<KG, kCodecInt4, TT>), grid, dim3(512), 0, st, a);
+    else if (TT == 16 && a.codec == kCodecInt8)
+        hipLaunchKernelGGL((batch_gateup_kernel<KG, kCodecInt8, 16>), grid, dim3(512), 0, st, a);
+    else if (TT == 16 && a.codec == kCodecInt2)
+        hipLaunchKernelGGL((batch_gateup_kernel<KG, kCodecInt2, 16>), grid, dim3(512), 0, st, a);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+template <int KG>
+hipError_t launch_gateup(const BatchArgs& a, hipStream_t st) {
+    if (a.tile_tokens == 32) return launch_gateup_t<KG, 32>(a, st);
+    if (a.tile_tokens == 16) return launch_gateup_t<KG, 16>(a, st);
+    return hipErrorInvalidValue;
+}
+
+template <int KGI, int TT>
+hipError_t launch_down_t(const BatchArgs& a, hipStream_t st) {
+    const int g = grouped_grid(a, a.H / (kDownBlockRows * row_pack(a.codec)));
+    const dim3 grid(g < kGroupedGrid / 2 ? g : kGroupedGrid / 2);  // one workgroup per CU
+    if (a.codec == kCodecMxfp4)
+        hipLaunchKernelGGL((batch_down_kernel<KGI, kCodecMxfp4, TT>), grid, dim3(kDownThreads), 0, st, a);
+    else if (a.codec == kCodecInt4)
+        hipLaunchKernelGGL((batch_down_kernel<KGI, kCodecInt4, TT>), grid, dim3(kDownThreads), 0, st, a);
+    else if (TT == 16 && a.codec == kCodecInt8)
+        hipLaunchKernelGGL((batch_down_kernel<KGI, kCodecInt8, 16>), grid, dim3(kDownThreads), 0, st, a);
+    else if (TT == 16 && a.codec == kCodecInt2)
+        hipLaunchKernelGGL((batch_down_kernel<KGI, kCodecInt2, 16>), grid, dim3(kDownThreads), 0, st, a);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();
@@ -881,19 +929,9 @@ hipError_t launch_gateup(const BatchArgs& a, hipStream_t st) {
 
 template <int KGI>
 hipError_t launch_down(const BatchArgs& a, hipStream_t st) {
-    const int g = grouped_grid(a, a.H / (kDownBlockRows * row_pack(a.codec)));
-    const dim3 grid(g < kGroupedGrid / 2 ? g : kGroupedGrid / 2);  // one workgroup per CU
-    if (a.codec == kCodecMxfp4)
-        hipLaunchKernelGGL((batch_down_kernel<KGI, kCodecMxfp4>), grid, dim3(kDownThreads), 0, st, a);
-    else if (a.codec == kCodecInt8)
-        hipLaunchKernelGGL((batch_down_kernel<KGI, kCodecInt8>), grid, dim3(kDownThreads), 0, st, a);
-    else if (a.codec == kCodecInt2)
-        hipLaunchKernelGGL((batch_down_kernel<KGI, kCodecInt2>), grid, dim3(kDownThreads), 0, st, a);
-    else if (a.codec == kCodecInt4)
-        hipLaunchKernelGGL((batch_down_kernel<KGI, kCodecInt4>), grid, dim3(kDownThreads), 0, st, a);
-    else
-        return hipErrorInvalidValue;
-    return hipGetLastError();
+    if (a.tile_tokens == 32) return launch_down_t<KGI, 32>(a, st);
+    if (a.tile_tokens == 16) return launch_down_t<KGI, 16>(a, st);
+    return hipErrorInvalidValue;
 }
 
 }  // namespace

@@ -5,6 +5,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include "moe_layout.h"
+
 namespace moe {
 
 // Arguments of the one-token decode path.  Every pointer is device memory.
@@ -63,13 +65,24 @@ hipError_t decode_down_combine(const DecodeArgs& a, hipStream_t st, const Launch
 bool decode_shape_supported(int hidden, int inter, int top_k, int n_shared);
 
 // ------------------------------------------------------------ batched path
-// Tokens per MFMA tile and rows per gate/up workgroup of the grouped kernels.
+// Tokens per MFMA row block (the smallest tile) and rows per gate/up
+// workgroup of the grouped kernels.
 constexpr int kTileTokens = 16;
 constexpr int kBlockRows = 128;
 // Largest number of (token, routed slot) entries one dispatch sorts in LDS.
 constexpr int kMaxDispatchEntries = 8192;
 
-// One tile of the grouped kernels: up to kTileTokens consecutive entries
+// Entries per tile of the grouped kernels for a call of T tokens: 32 (two
+// MFMA row blocks per weight fragment, so an expert with up to 32 entries is
+// read once) when the call averages at least 8 entries per expert and the
+// codec's registers allow it, else 16 (a mostly empty second row block would
+// only add work; the two-fragment codecs, int8 planes and int2 rows, have no
+// registers for it).
+__host__ __device__ constexpr int batch_tile_tokens(int codec, int T, int K, int E) {
+    return codec == kCodecInt8 || codec == kCodecInt2 || T * K < 8 * E ? 16 : 32;
+}
+
+// One tile of the grouped kernels: up to batch_tile_tokens consecutive entries
 // ("pairs") of one expert.  expert == E marks the shared expert.
 struct Tile {
     int expert;
@@ -112,6 +125,7 @@ struct BatchArgs {
     float rsf;
     float top_p;                 // adaptive expert top-p (1: plain top-k); dropped choices get id -1
     int codec;                   // weight codec (kCodecInt4 .. kCodecInt2)
+    int tile_tokens;             // batch_tile_tokens(codec, T, K, E): 16 or 32
 };
 
 // Upper bound of the tiles of a call of T tokens.

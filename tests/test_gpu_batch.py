@@ -271,6 +271,33 @@ def test_batch_mxfp4_parity(torch_cuda, cfg_name, T, top_p):
     layer.close()
 
 
+# ---------------------------------------------------------------- 32-entry tiles
+@pytest.mark.parametrize("cfg_name,T,codec,top_p", [("TINY", 128, "int4", 1.0), ("MID_A", 100, "int4", 1.0),
+                                                    ("MID_A", 100, "mxfp4", 1.0), ("MID_D", 300, "int4", 1.0),
+                                                    ("TINY", 77, "int4", 0.7)])
+def test_batch_wide_tiles_parity(torch_cuda, cfg_name, T, codec, top_p):
+    """Calls averaging at least 8 entries per expert take tiles of up to 32
+    entries (two MFMA row blocks per weight fragment): experts with more
+    than 32 entries, ragged last tiles and the shared expert's tiles,
+    against the oracle on every output."""
+    import dataclasses
+    from routed_expert_int4_amd.layer import DeviceLayer
+    cfg = {"TINY": synth.TINY, "MID_A": MID_A, "MID_D": MID_D}[cfg_name]
+    cfg = dataclasses.replace(cfg, codec=codec, top_p=top_p)
+    assert T * cfg.top_k >= 8 * cfg.n_experts
+    say(f"[gpu] wide tiles {cfg_name} T={T} {codec} top_p={top_p}")
+    weights = synth.gen_layer(cfg, seed=2)
+    layer = DeviceLayer(weights, max_T=T)
+    x = synth.gen_tokens(cfg, T, seed=6)
+    y, ids, w = run_batch(torch_cuda, layer, x)
+    counts = np.bincount(ids[ids >= 0].ravel(), minlength=cfg.n_experts)
+    if cfg_name == "TINY" and top_p == 1.0:
+        assert counts.max() > 32  # several tiles for one expert
+    res = check_layer(weights, x, y, ids, w)
+    say(f"[gpu] wide tiles {cfg_name}: worst rel err {res['worst_rel']:.3g}, max entries {counts.max()}")
+    layer.close()
+
+
 # ---------------------------------------------------------------- int8 experts
 @pytest.mark.parametrize("cfg_name,T,top_p", [("TINY", 4, 1.0), ("MID_A", 37, 1.0), ("MID_B", 16, 1.0),
                                               ("MID_C", 5, 1.0), ("MID_D", 100, 1.0), ("MID_A", 21, 0.7)])

@@ -12,9 +12,11 @@
 //      to scaled fp16 in MFMA operand order;
 //   3. dispatch: one workgroup sorts the T*K (token, slot) entries by
 //      expert then token in LDS, and writes counts, offsets, the permutation
-//      and its inverse, the distinct experts and the tile list (up to 16
+//      and its inverse, the distinct experts and the tile list (up to 16 or 32
 //      entries of one expert per tile; the shared expert's T tokens last);
-//   4. gate/up: grouped int4 GEMM per (tile, 128 rows) on the matrix cores;
+//   4. gate/up: grouped int4 GEMM per (tile, 128 rows) on the matrix cores
+//      (tiles of up to 32 entries when a call averages 8 or more per expert:
+//      two MFMA row blocks share each dequantised weight fragment);
 //   5. h prep: h per entry as scaled fp16 hi + lo parts in MFMA order;
 //   6. down: grouped int4 GEMM per (tile, 256 output rows);
 //   7. combine: y = sum_j w_j d_j + d_shared in slot order (no atomics).

@@ -266,3 +266,59 @@ def test_cache_other_codecs(torch_cuda, codec):
     for lay in cached + resident:
         lay.close()
     cache.close()
+
+
+def glm_stack_layer(l, biases):
+    """Layer l of the GLM-shaped stack: weights seed 100 + l with the
+    committed Zipf(1.1)-calibrated bias of that layer."""
+    wl = synth.gen_layer(synth.GLM, seed=100 + l)
+    wl.bias = np.asarray(biases[l], dtype=np.float32)
+    return wl
+
+
+@pytest.mark.parametrize("slots", [64, 12])
+def test_glm_cache_stack_parity_and_lru(torch_cuda, slots):
+    """The cache-stack workload at full size: two chained GLM-shaped layers
+    (hidden 6144, intermediate 2048, 256 experts, top-8) behind an HBM cache
+    of `slots` slots per layer fed from pinned host stores, 16 sequential
+    tokens.  Every layer's outputs against the oracle on the GPU's own bf16
+    input to that layer; hit / miss / eviction counts equal to the LRU replay
+    of the GPU's routing trace; h2d_bytes = misses x blob bytes.  With 12
+    slots nearly every token evicts experts the previous token read."""
+    import json
+    import os
+    torch = torch_cuda
+    from routed_expert_int4_amd.layer import DeviceLayer, ExpertCache, HostExpertStore
+    n_layers, n_tok = 2, 16
+    with open(os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "zipf_bias_stack.json")) as f:
+        biases = [l["bias"] for l in json.load(f)["layers"]]
+    say(f"[gpu] GLM cache stack: {n_layers} layers, {slots} slots, {n_tok} tokens")
+    cache = ExpertCache(synth.GLM, n_layers, slots)
+    weights, layers = [], []
+    for l in range(n_layers):
+        wl = glm_stack_layer(l, biases)
+        cache.register(l, HostExpertStore(wl))
+        lay = DeviceLayer(wl, max_T=n_tok, resident=False)
+        lay.attach_cache(cache, l)
+        weights.append(wl)
+        layers.append(lay)
+    torch.cuda.synchronize()
+    x_bits = synth.gen_tokens(synth.GLM, n_tok, seed=300)
+    noise = synth.gen_noise(synth.GLM, n_tok * n_layers, seed=400, std=0.1)
+    for l in range(n_layers):
+        y, ids, w = layers[l].forward(DeviceLayer.to_device_bf16(x_bits))
+        torch.cuda.synchronize()
+        yh, idh, wh = y.cpu().numpy(), ids.cpu().numpy(), w.cpu().numpy()
+        res = check_layer(weights[l], x_bits, yh, idh, wh)
+        st = cache.stats(l)
+        want = lru.replay(idh, slots)
+        say(f"[gpu] GLM layer {l}: rel err {res['worst_rel']:.3g}, excused {res['excused']}, stats {st}, "
+            f"replay {want}")
+        assert (st["hits"], st["misses"], st["evictions"]) == want
+        assert st["h2d_bytes"] == st["misses"] * cache.nb
+        if slots == 12:
+            assert st["evictions"] > 0
+        x_bits = chain_input(yh, noise[l * n_tok:(l + 1) * n_tok])
+    for lay in layers:
+        lay.close()
+    cache.close()

@@ -451,3 +451,88 @@ def test_degenerate_configs_decode(torch_cuda, name):
     np.testing.assert_allclose(w.sum(axis=1), cfg.routed_scaling_factor, rtol=1e-6)
     say(f"[gpu] {name}: worst rel err {res['worst_rel']:.3g}")
     layer.close()
+
+
+# ---------------------------------------------------------------- outliers inside a scale group
+def with_group_outliers(cfg, x_bits, seed, lo=1e3, hi=1e4):
+    """x with one element of every 32-input group set to a factor drawn
+    log-uniformly from [lo, hi] times the group's largest magnitude (sign
+    kept), rounded to bf16: the
+    decode kernels round each group to 16-bit integers relative to the
+    group's largest element, so the other 31 lose the most bits here."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    x = synth.bf16_bits_to_f32(x_bits).copy()
+    T, H = x.shape
+    pos = rng.integers(0, 32, size=(T, H // 32)) + 32 * np.arange(H // 32)[None, :]
+    fac = np.exp(rng.uniform(np.log(lo), np.log(hi), size=(T, H // 32))).astype(np.float32)
+    rows = np.arange(T)[:, None]
+    gmax = np.abs(x).reshape(T, H // 32, 32).max(axis=2)
+    x[rows, pos] = np.where(x[rows, pos] < 0, -1.0, 1.0) * fac * gmax
+    return synth.round_to_bf16_bits(x)
+
+
+def with_heavy_tailed_h(weights, factor=1000.0, seed=0):
+    """Up-projection scales of one row in every 32 rows (per expert) raised by
+    `factor`, so that h = silu(g) * u has one element per 32-group of the
+    down projection's input about `factor` times the others."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    cfg = weights.cfg
+    us = weights.up_s.copy()
+    f = us.view(np.float16).astype(np.float32)
+    n_all, I = f.shape[0], f.shape[1]
+    rows = rng.integers(0, 32, size=(n_all, I // 32)) + 32 * np.arange(I // 32)[None, :]
+    for e in range(n_all):
+        f[e, rows[e], :] *= factor
+    assert np.all(np.isfinite(f.astype(np.float16)))
+    return dataclasses.replace(weights, up_s=f.astype(np.float16).view(np.uint16))
+
+
+@pytest.mark.parametrize("cfg_name", ["TINY", "MID_A", "MID_C"])
+def test_activation_outlier_in_every_group(torch_cuda, cfg_name):
+    """One activation per 32-group 1e3..1e4 times the others: decode and
+    batched outputs within 2e-3 of the oracle per token."""
+    cfg = {"TINY": synth.TINY, "MID_A": MID_A, "MID_C": MID_C}[cfg_name]
+    say(f"[gpu] activation outliers in every group, {cfg_name}")
+    weights = synth.gen_layer(cfg, seed=0)
+    T = 4 if cfg.hidden * cfg.inter > 2 ** 24 else 12
+    x = with_group_outliers(cfg, synth.gen_tokens(cfg, T, seed=11), seed=12)
+    layer, y, ids, w = run_layer(torch_cuda, weights, x)
+    res = check_layer(weights, x, y, ids, w)
+    from routed_expert_int4_amd.layer import DeviceLayer
+    yb, idb, wb = layer.forward(DeviceLayer.to_device_bf16(x))
+    torch_cuda.cuda.synchronize()
+    resb = check_layer(weights, x, yb.cpu().numpy(), idb.cpu().numpy(), wb.cpu().numpy())
+    say(f"[gpu] {cfg_name} outliers: decode worst rel err {res['worst_rel']:.3g}, batched {resb['worst_rel']:.3g}")
+    layer.close()
+
+
+@pytest.mark.parametrize("cfg_name", ["TINY", "MID_A", "MID_B"])
+def test_heavy_tailed_h(torch_cuda, cfg_name):
+    """Expert weights that make h heavy-tailed (one element per 32-group of
+    the down projection's input ~1000 times the rest): decode and batched
+    outputs within 2e-3 of the oracle per token."""
+    cfg = {"TINY": synth.TINY, "MID_A": MID_A, "MID_B": MID_B}[cfg_name]
+    say(f"[gpu] heavy-tailed h, {cfg_name}")
+    weights = with_heavy_tailed_h(synth.gen_layer(cfg, seed=0), seed=13)
+    x = synth.gen_tokens(cfg, 10, seed=14)
+    layer, y, ids, w = run_layer(torch_cuda, weights, x)
+    res = check_layer(weights, x, y, ids, w)
+    from routed_expert_int4_amd.layer import DeviceLayer
+    yb, idb, wb = layer.forward(DeviceLayer.to_device_bf16(x))
+    torch_cuda.cuda.synchronize()
+    resb = check_layer(weights, x, yb.cpu().numpy(), idb.cpu().numpy(), wb.cpu().numpy())
+    say(f"[gpu] {cfg_name} heavy-tailed h: decode worst rel err {res['worst_rel']:.3g}, "
+        f"batched {resb['worst_rel']:.3g}")
+    layer.close()
+
+
+def test_glm_activation_outliers(torch_cuda, glm):
+    """GLM-shaped layer, outliers in every activation group, 3 tokens."""
+    weights, layer = glm
+    say("[gpu] GLM activation outliers")
+    x = with_group_outliers(synth.GLM, synth.gen_tokens(synth.GLM, 3, seed=15), seed=16)
+    from routed_expert_int4_amd.layer import DeviceLayer
+    y, ids, w = layer.forward_each(DeviceLayer.to_device_bf16(x))
+    torch_cuda.cuda.synchronize()
+    res = check_layer(weights, x, y.cpu().numpy(), ids.cpu().numpy(), w.cpu().numpy())
+    say(f"[gpu] GLM outliers: worst rel err {res['worst_rel']:.3g}")

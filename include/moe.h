@@ -175,16 +175,16 @@ moe_status_t moe_router_topk(moe_layer_t* layer, const uint16_t* d_x, int T, int
  * [T][hidden]; d_y fp32 [T][hidden] (the block output without residual);
  * d_ids / d_w may be NULL, else receive the routing as in moe_router_topk.
  * T = 1 runs the decode kernels (one token per launch sequence).  T > 1
- * with all experts resident and int4 or MXFP4 experts runs the batch-union
- * path (colibrì summary,
- * fr.news.hada.io topic 31297, "Principales fonctionnalités implémentées":
- * in prefill and batched verification each distinct expert of the batch is
- * read once and applied to every position routed to it): routing of all
- * tokens, a dispatch of the (token, slot) entries by expert, grouped gate/up
- * and down projections on the matrix cores, and the combine; tokens are
- * taken in launch sequences of at most min(max_T, 8192 / top_k); T > 1 with
- * int2 experts, hidden not a multiple of 512 or inter not a multiple of 256
- * runs the decode kernels token by token.
+ * with all experts resident runs the batch-union path for every codec
+ * (colibrì summary, fr.news.hada.io topic 31297, "Principales
+ * fonctionnalités implémentées": in prefill and batched verification each
+ * distinct expert of the batch is read once and applied to every position
+ * routed to it): routing of all tokens, a dispatch of the (token, slot)
+ * entries by expert, grouped gate/up and down projections on the matrix
+ * cores, and the combine; tokens are taken in launch sequences of at most
+ * min(max_T, 8192 / top_k).  Int2 layers take that path where hidden is a
+ * multiple of 512 and inter of 256; other int2 T > 1 calls run the decode
+ * kernels token by token.
  * With all experts resident the call is asynchronous.  With an attached
  * expert cache tokens are processed one at a time; the call blocks the host
  * once per token until its routing is known, issues the copies of missing

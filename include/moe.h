@@ -154,8 +154,8 @@ moe_status_t moe_expert_pack(const moe_config_t* cfg, const uint8_t* gate_q, con
  *
  * moe_layer_set_experts: all-resident mode.  d_blobs is a host array of
  * n_experts device pointers to packed expert blobs; the table is copied into
- * the workspace (synchronously).  A layer with an attached cache must not use
- * this call. */
+ * the workspace (synchronously) now if one is bound, else when one is bound.
+ * A layer with an attached cache must not use this call. */
 size_t moe_workspace_bytes(const moe_config_t* cfg, int max_T);
 moe_status_t moe_layer_create(const moe_config_t* cfg, const float* d_router_w, const float* d_bias,
                               const void* const* d_shared_blobs, moe_layer_t** out);
@@ -192,6 +192,24 @@ moe_status_t moe_router_topk(moe_layer_t* layer, const uint16_t* d_x, int T, int
  * them with events. */
 moe_status_t moe_layer_forward(moe_layer_t* layer, const uint16_t* d_x, int T, float* d_y, int32_t* d_ids,
                                float* d_w, void* stream);
+
+/* moe_layer_forward_noalloc: moe_layer_forward for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops
+ * and harnesses that forbid hipMalloc.  It needs no workspace (none has to be
+ * bound; a bound one is not used) and allocates nothing: its per-call state
+ * lives in a device array of the library, 256 KiB per GPU, held until the
+ * process ends.  Same arguments and results as moe_layer_forward for an
+ * all-resident layer (moe_layer_set_experts called), bit-identical to its
+ * one-token calls: every token runs the decode kernels, one token after the
+ * other, each call starting with one small launch that writes the expert
+ * table into the array.  d_ids / d_w may be NULL.  Errors: MOE_EINVAL for a
+ * layer with an expert cache or without experts, and for a shape whose
+ * per-call state exceeds the array (reported with both sizes; every
+ * supported shape fits).  Every call on a GPU shares that GPU's array: calls
+ * that overlap on one GPU (two streams or two host threads) race; order them
+ * on one stream. */
+moe_status_t moe_layer_forward_noalloc(moe_layer_t* layer, const uint16_t* d_x, int T, float* d_y, int32_t* d_ids,
+                                       float* d_w, void* stream);
 
 /* moe_dispatch: the batch-union dispatch of a routing d_ids int32 [T][top_k]
  * (device) on the layer's workspace (T <= min(max_T, 8192 / top_k)):

@@ -64,6 +64,7 @@ _SIGNATURES = {
     "moe_layer_destroy": ([_vp], None),
     "moe_router_topk": ([_vp, _vp, _i, _vp, _vp, _vp], _i),
     "moe_layer_forward": ([_vp, _vp, _i, _vp, _vp, _vp, _vp], _i),
+    "moe_layer_forward_noalloc": ([_vp, _vp, _i, _vp, _vp, _vp, _vp], _i),
     "moe_layer_profile": ([_vp, _i], _i),
     "moe_layer_profile_read": ([_vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_uint64)], _i),
     "moe_dispatch": ([_vp, _vp, _i, _vp, _vp, _vp, _vp, _vp, _vp], _i),
@@ -174,6 +175,11 @@ def moe_router_topk(layer: int, d_x, T: int, d_ids, d_w, stream=None) -> None:
 def moe_layer_forward(layer: int, d_x, T: int, d_y, d_ids=None, d_w=None, stream=None) -> None:
     check(lib().moe_layer_forward(layer, _ptr(d_x), int(T), _ptr(d_y), _ptr(d_ids), _ptr(d_w),
                                   _stream_handle(stream)))
+
+
+def moe_layer_forward_noalloc(layer: int, d_x, T: int, d_y, d_ids=None, d_w=None, stream=None) -> None:
+    check(lib().moe_layer_forward_noalloc(layer, _ptr(d_x), int(T), _ptr(d_y), _ptr(d_ids), _ptr(d_w),
+                                          _stream_handle(stream)))
 
 
 def moe_dispatch(layer: int, d_ids, T: int, d_counts, d_offsets, d_perm, d_distinct, d_n_distinct,

@@ -294,15 +294,17 @@ moe_status_t moe_layer_set_workspace(moe_layer_t* layer, void* d_ws, size_t byte
 
 moe_status_t moe_layer_set_experts(moe_layer_t* layer, const void* const* d_blobs) {
     if (!layer || !d_blobs) return fail(MOE_EINVAL, "moe_layer_set_experts: NULL argument");
-    if (!layer->ws) return fail(MOE_EINVAL, "moe_layer_set_experts: bind a workspace first");
     if (layer->cache) return fail(MOE_EINVAL, "moe_layer_set_experts: layer uses an expert cache");
-    for (int e = 0; e < layer->cfg.n_experts; ++e) {
+    for (int e = 0; e < layer->cfg.n_experts; ++e)
         if (!d_blobs[e]) return fail(MOE_EINVAL, "moe_layer_set_experts: blob %d is NULL", e);
-        layer->host_table[e] = static_cast<const uint8_t*>(d_blobs[e]);
+    for (int e = 0; e < layer->cfg.n_experts; ++e) layer->host_table[e] = static_cast<const uint8_t*>(d_blobs[e]);
+    // without a workspace the table is copied when one is bound (the
+    // allocation-free entry point carries it in its own launch instead)
+    if (layer->ws) {
+        hipError_t e = hipMemcpy(layer->ws + layer->W.table, layer->host_table.data(),
+                                 sizeof(void*) * layer->host_table.size(), hipMemcpyHostToDevice);
+        if (e != hipSuccess) return hip_fail(e, "hipMemcpy(expert table)");
     }
-    hipError_t e = hipMemcpy(layer->ws + layer->W.table, layer->host_table.data(),
-                             sizeof(void*) * layer->host_table.size(), hipMemcpyHostToDevice);
-    if (e != hipSuccess) return hip_fail(e, "hipMemcpy(expert table)");
     layer->experts_set = true;
     return MOE_OK;
 }
@@ -343,23 +345,24 @@ moe_status_t moe_layer_profile_read(moe_layer_t* layer, double* total_ms, uint64
 
 namespace moe {
 
-DecodeArgs decode_args(moe_layer_t* L, const uint16_t* x, int32_t* ids, float* w, float* y) {
+DecodeArgs decode_args(moe_layer_t* L, uint8_t* ws, const WorkspaceLayout& W, const uint16_t* x, int32_t* ids,
+                       float* w, float* y) {
     DecodeArgs a;
     const moe_config_t& c = L->cfg;
     a.x = x;
     a.router_w = L->router_w;
     a.bias = L->bias;
-    a.table = L->cache ? nullptr : reinterpret_cast<const uint8_t* const*>(L->ws + L->W.table);
-    a.counter = reinterpret_cast<unsigned*>(L->ws + L->W.control);
+    a.table = L->cache ? nullptr : reinterpret_cast<const uint8_t* const*>(ws + W.table);
+    a.counter = reinterpret_cast<unsigned*>(ws + W.control);
     a.shared_blob = c.n_shared > 0 ? L->shared[0] : nullptr;
-    a.s = reinterpret_cast<float*>(L->ws + L->W.s);
-    a.sb = reinterpret_cast<float*>(L->ws + L->W.sb);
-    a.xq = reinterpret_cast<unsigned*>(L->ws + L->W.xq);
-    a.slot_blobs = reinterpret_cast<const uint8_t**>(L->ws + L->W.slot_blobs);
-    a.kept = !L->cache && c.top_p < 1.0f ? reinterpret_cast<int*>(L->ws + L->W.kept) : nullptr;
+    a.s = reinterpret_cast<float*>(ws + W.s);
+    a.sb = reinterpret_cast<float*>(ws + W.sb);
+    a.xq = reinterpret_cast<unsigned*>(ws + W.xq);
+    a.slot_blobs = reinterpret_cast<const uint8_t**>(ws + W.slot_blobs);
+    a.kept = !L->cache && c.top_p < 1.0f ? reinterpret_cast<int*>(ws + W.kept) : nullptr;
     a.ids = ids;
     a.w = w;
-    a.h = reinterpret_cast<float*>(L->ws + L->W.h);
+    a.h = reinterpret_cast<float*>(ws + W.h);
     a.y = y;
     a.H = c.hidden;
     a.I = c.inter;
@@ -504,7 +507,7 @@ moe_status_t moe_router_topk(moe_layer_t* layer, const uint16_t* d_x, int T, int
         return MOE_OK;
     }
     for (int t = 0; t < T; ++t) {
-        DecodeArgs a = decode_args(layer, d_x + (size_t)t * c.hidden, d_ids + (size_t)t * c.top_k,
+        DecodeArgs a = decode_args(layer, layer->ws, layer->W, d_x + (size_t)t * c.hidden, d_ids + (size_t)t * c.top_k,
                                    d_w + (size_t)t * c.top_k, nullptr);
         hipError_t e = decode_router(a, s);
         if (e != hipSuccess) return hip_fail(e, "router kernel launch");
@@ -552,9 +555,20 @@ moe_status_t moe_layer_forward(moe_layer_t* layer, const uint16_t* d_x, int T, f
         }
         return MOE_OK;
     }
+    return decode_tokens(layer, layer->ws, layer->W, d_x, T, d_y, ids_base, c.top_k, w_base, c.top_k, s);
+}
+
+}  // extern "C"
+
+namespace moe {
+
+moe_status_t decode_tokens(moe_layer_t* layer, uint8_t* ws, const WorkspaceLayout& W, const uint16_t* d_x, int T,
+                           float* d_y, int32_t* ids_base, int ids_stride, float* w_base, int w_stride, hipStream_t s) {
+    const moe_config_t& c = layer->cfg;
+    moe_status_t st = MOE_OK;
     for (int t = 0; t < T; ++t) {
-        DecodeArgs a = decode_args(layer, d_x + (size_t)t * c.hidden, ids_base + (size_t)t * c.top_k,
-                                   w_base + (size_t)t * c.top_k, d_y + (size_t)t * c.hidden);
+        DecodeArgs a = decode_args(layer, ws, W, d_x + (size_t)t * c.hidden, ids_base + (size_t)t * ids_stride,
+                                   w_base + (size_t)t * w_stride, d_y + (size_t)t * c.hidden);
         ProfileScope p0(layer, 0, s, ProfileScope::kKernel);
         hipError_t e = decode_router(a, s, p0.timing());
         if (e != hipSuccess) return hip_fail(e, "router kernel launch");
@@ -582,6 +596,10 @@ moe_status_t moe_layer_forward(moe_layer_t* layer, const uint16_t* d_x, int T, f
     }
     return MOE_OK;
 }
+
+}  // namespace moe
+
+extern "C" {
 
 moe_status_t moe_dispatch(moe_layer_t* layer, const int32_t* d_ids, int T, int32_t* d_counts, int32_t* d_offsets,
                           int32_t* d_perm, int32_t* d_distinct, int32_t* d_n_distinct, void* stream) {

@@ -44,6 +44,13 @@ moe_status_t hip_fail(hipError_t e, const char* what);
 moe_status_t validate_config(const moe_config_t* c);
 moe_status_t validate_supported(const moe_config_t* c);
 
+// The one-token decode path over T tokens with the per-call state at ws
+// (laid out as W): token t reads x[t], writes y[t] and its routing to
+// ids_base + t * ids_stride and w_base + t * w_stride.
+moe_status_t decode_tokens(moe_layer* L, uint8_t* ws, const WorkspaceLayout& W, const uint16_t* d_x, int T,
+                           float* d_y, int32_t* ids_base, int ids_stride, float* w_base, int w_stride,
+                           hipStream_t s);
+
 }  // namespace moe
 
 struct moe_layer {

@@ -31,6 +31,8 @@ def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+# HBM counter record (rocprofv3 FETCH_SIZE / WRITE_SIZE) of the dominant
+# decode kernel, the routed gate/up launch
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "gateup_kernel_glm_decode_traffic.md")
 KERNEL_SOURCES = [os.path.join(ROOT, "routed_expert_int4_amd", "csrc", f)
                   for f in ("moe_decode.hip", "moe_device.h", "moe_kernels.h", "moe_layout.h")]
@@ -85,17 +87,19 @@ def source_digest() -> str:
 
 
 def measured_traffic():
-    """HBM bytes per gate/up launch from the committed rocprofv3 counter record.
+    """HBM bytes per launch of the dominant decode kernel from the committed
+    rocprofv3 counter record.
 
-    The record holds FETCH_SIZE and WRITE_SIZE per dispatch of the gate/up
-    kernel, each scaled by what the counter reads for a device copy of known
-    size, and the digest of the kernel sources they were taken on.  Returns
-    None when there is no record or the kernel source has changed since.
+    The record holds FETCH_SIZE and WRITE_SIZE per dispatch of the kernel,
+    each scaled by what the counter reads for a device copy of known size,
+    and the digest of the kernel sources they were taken on.  Returns None
+    when there is no record or the kernel source has changed since.
     """
-    if not os.path.exists(TRAFFIC_RECORD):
+    path = TRAFFIC_RECORD
+    if not os.path.exists(path):
         return None
     rec = None
-    with open(TRAFFIC_RECORD) as f:
+    with open(path) as f:
         for line in f:
             if line.startswith("traffic-record:"):
                 rec = json.loads(line.split(":", 1)[1])
@@ -327,8 +331,9 @@ def bench_cache_stack(args) -> int:
 
 def bench_probes(args) -> int:
     """Device ceilings the layer's numbers are read against (one JSON line):
-    HBM GB/s of a device-to-device copy (bytes read + bytes written) over
-    buffers the size of the decode launches (56 MB, 113 MB) and of 1 GiB;
+    HBM GB/s of the library's read-only streaming kernel (moe_hbm_read_probe)
+    and of a device-to-device copy (bytes read + bytes written) over buffers
+    the size of the decode launches (56 MB, 113 MB, 197 MB) and of 1 GiB;
     pinned host-to-device and device-to-host copy GB/s (256 MiB); bf16 GEMM
     TFLOP/s (8192^3 through torch.matmul).  Each figure is the best of 10
     timed repeats after 3 warmups."""
@@ -351,6 +356,7 @@ def bench_probes(args) -> int:
             best = min(best, e0.elapsed_time(e1))
         return best
 
+    from routed_expert_int4_amd import binding as B
     read = {}
     for label, nbytes in (("56MB", 56_623_104), ("113MB", 113_246_208), ("1GiB", 1 << 30)):
         src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
@@ -358,6 +364,21 @@ def bench_probes(args) -> int:
         ms = best_ms(lambda: dst.copy_(src))
         read[label] = round(2 * nbytes / (ms / 1e3) / 1e9, 1)
         del src, dst
+    # read-only streaming (the library's probe kernel) at the decode launches'
+    # sizes (56.6 MB down, 113 MB routed gate/up, 197 MB one layer-token) and
+    # 1 GiB; best over workgroup counts of 1 to 16 per CU
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    read_only = {}
+    for label, nbytes in (("56MB", 56_623_104), ("113MB", 113_246_208), ("197MB", 197_432_320), ("1GiB", 1 << 30)):
+        buf = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+        sink = torch.empty(16 * n_cu, dtype=torch.int32, device=dev)
+        best = None
+        for per_cu in (1, 2, 4, 8, 16):
+            ms = best_ms(lambda: B.moe_hbm_read_probe(buf, nbytes, sink, per_cu * n_cu))
+            if best is None or ms < best[0]:
+                best = (ms, per_cu)
+        read_only[label] = {"gbs": round(nbytes / (best[0] / 1e3) / 1e9, 1), "workgroups_per_cu": best[1]}
+        del buf, sink
     host = torch.empty(256 << 20, dtype=torch.uint8, pin_memory=True)
     devb = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
     h2d = (256 << 20) / (best_ms(lambda: devb.copy_(host, non_blocking=True)) / 1e3) / 1e9
@@ -367,12 +388,15 @@ def bench_probes(args) -> int:
     b = torch.randn(n, n, dtype=torch.bfloat16, device=dev)
     gemm = 2 * n ** 3 / (best_ms(lambda: torch.matmul(a, b)) / 1e3) / 1e12
     out = {
-        "metric": "device ceilings: HBM copy GB/s (read + write), pinned host copy GB/s, bf16 GEMM TFLOP/s",
-        "value": read["1GiB"], "unit": "GB/s", "n_gpus": 1, "steps": 10, "warmup": 3,
+        "metric": "device ceilings: HBM read-only and copy GB/s, pinned host copy GB/s, bf16 GEMM TFLOP/s",
+        "value": read_only["1GiB"]["gbs"], "unit": "GB/s", "n_gpus": 1, "steps": 10, "warmup": 3,
         "higher_is_better": True, "data": "synthetic",
-        "config": {"workload": "probes: device-to-device copies, pinned 256 MiB copies, 8192^3 bf16 matmul"},
-        "hbm_copy_gbs": read, "h2d_gbs": round(h2d, 1), "d2h_gbs": round(d2h, 1), "bf16_gemm_tflops": round(gemm, 1),
-        "vs_peak": {"hbm_copy_1GiB": round(read["1GiB"] / HBM_PEAK_GBS, 4), "bf16_gemm": round(gemm / 2500.0, 4)},
+        "config": {"workload": "probes: read-only streaming kernel (moe_hbm_read_probe), device-to-device copies, "
+                               "pinned 256 MiB copies, 8192^3 bf16 matmul"},
+        "hbm_read_only_gbs": read_only, "hbm_copy_gbs": read, "h2d_gbs": round(h2d, 1), "d2h_gbs": round(d2h, 1),
+        "bf16_gemm_tflops": round(gemm, 1),
+        "vs_peak": {"hbm_read_only_1GiB": round(read_only["1GiB"]["gbs"] / HBM_PEAK_GBS, 4),
+                    "hbm_copy_1GiB": round(read["1GiB"] / HBM_PEAK_GBS, 4), "bf16_gemm": round(gemm / 2500.0, 4)},
     }
     print(json.dumps(out), flush=True)
     return 0
@@ -566,18 +590,46 @@ def bench_decode(args) -> int:
     layer_gbs = tokens_per_s * nbytes["layer_per_token"] / 1e9
     log(f"{ms_per_step:.3f} ms/step, {tokens_per_s:.0f} tokens/s, routed {routed_gbs:.0f} GB/s (wall {wall:.2f} s)")
 
-    # per-kernel durations with HIP events on the launch stream (one step)
-    B.moe_layer_profile(layer.handle, True)
-    step()
+    def kernel_avg_us():
+        """Per-kind average launch duration (us) over one step, from HIP
+        events stamped with each kernel's own begin and end on the launch
+        stream: router, gate/up, down + combine, fused one-token launch."""
+        B.moe_layer_profile(layer.handle, True)
+        step()
+        torch.cuda.synchronize()
+        kms, kn = B.moe_layer_profile_read(layer.handle)
+        B.moe_layer_profile(layer.handle, False)
+        return [1e3 * kms[k] / kn[k] if kn[k] else None for k in range(4)]
+
+    avg3 = kernel_avg_us()
+    gateup_gbs = nbytes["gateup_launch"] / (avg3[1] * 1e-6) / 1e9
+    down_gbs = nbytes["down_launch"] / (avg3[2] * 1e-6) / 1e9
+    router_gbs = nbytes["router_launch"] / (avg3[0] * 1e-6) / 1e9
+    log(f"kernel avg us: router {avg3[0]:.2f} ({router_gbs:.0f} GB/s), gate/up {avg3[1]:.2f} ({gateup_gbs:.0f} GB/s), "
+        f"down+combine {avg3[2]:.2f} ({down_gbs:.0f} GB/s)")
+    # the fused one-token launch on the same tokens, for comparison (opt-in:
+    # moe_layer_set_decode(layer, 1); bit-identical results)
+    fused = None
+    B.moe_layer_set_decode(layer.handle, 1)
+    for _ in range(max(1, args.warmup)):
+        step()
     torch.cuda.synchronize()
-    kms, kn = B.moe_layer_profile_read(layer.handle)
-    B.moe_layer_profile(layer.handle, False)
-    avg_us = [1e3 * kms[k] / max(kn[k], 1) for k in range(3)]
-    gateup_gbs = nbytes["gateup_launch"] / (avg_us[1] * 1e-6) / 1e9
-    down_gbs = nbytes["down_launch"] / (avg_us[2] * 1e-6) / 1e9
-    router_gbs = nbytes["router_launch"] / (avg_us[0] * 1e-6) / 1e9
-    log(f"kernel avg us: router {avg_us[0]:.2f} ({router_gbs:.0f} GB/s), gate/up {avg_us[1]:.2f} "
-        f"({gateup_gbs:.0f} GB/s), down+combine {avg_us[2]:.2f} ({down_gbs:.0f} GB/s)")
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms1 = e0.elapsed_time(e1) / args.steps
+    avg1 = kernel_avg_us()
+    B.moe_layer_set_decode(layer.handle, 3)
+    if avg1[3] is not None:
+        fused = {
+            "ms_per_step": round(ms1, 4),
+            "tokens_per_s": round(args.tokens / (ms1 / 1e3), 1),
+            "avg_launch_us": round(avg1[3], 3),
+            "layer_gbs": round(nbytes["layer_per_token"] / (avg1[3] * 1e-6) / 1e9, 1),
+        }
+        log(f"fused one-token launch: {ms1:.3f} ms/step, launch avg {avg1[3]:.2f} us")
 
     cpu = None
     if args.cpu_sample > 0:
@@ -611,10 +663,12 @@ def bench_decode(args) -> int:
         "pct_of_hbm_peak": round(100 * routed_gbs / HBM_PEAK_GBS, 2),
         "layer_gbs": round(layer_gbs, 2),
         "bytes_per_token": {"routed": nbytes["routed_per_token"], "layer": nbytes["layer_per_token"]},
-        "kernels_avg_us": {"router_shared_gateup": round(avg_us[0], 3), "gateup_swiglu": round(avg_us[1], 3),
-                           "down_combine": round(avg_us[2], 3)},
+        "decode_launches_per_token": 3,
+        "kernels_avg_us": {"router_shared_gateup": round(avg3[0], 3), "gateup_swiglu": round(avg3[1], 3),
+                           "down_combine": round(avg3[2], 3)},
         "kernels_gbs": {"router_shared_gateup": round(router_gbs, 1), "gateup_swiglu": round(gateup_gbs, 1),
                         "down_combine": round(down_gbs, 1)},
+        "fused_single_launch": fused,
         "roofline": {
             "kernel": "gate/up + SwiGLU of the 8 routed experts (gateup_kernel<192>)",
             "bound": "hbm",
@@ -624,7 +678,7 @@ def bench_decode(args) -> int:
             "frac": round(gateup_gbs / HBM_PEAK_GBS, 4),
             "traffic": measured_traffic() if cfg.top_p >= 1.0 and cfg.codec == "int4" else None,
             "bytes_per_launch": nbytes["gateup_launch"],
-            "avg_launch_us": round(avg_us[1], 3),
+            "avg_launch_us": round(avg3[1], 3),
         },
         "cpu_baseline": cpu,
     }

@@ -174,7 +174,8 @@ moe_status_t moe_router_topk(moe_layer_t* layer, const uint16_t* d_x, int T, int
 /* moe_layer_forward: the whole layer for T tokens.  d_x bf16 bits
  * [T][hidden]; d_y fp32 [T][hidden] (the block output without residual);
  * d_ids / d_w may be NULL, else receive the routing as in moe_router_topk.
- * T = 1 runs the decode kernels (one token per launch sequence).  T > 1
+ * T = 1 runs the decode kernels (three launches per token, or one fused
+ * launch: moe_layer_set_decode).  T > 1
  * with all experts resident runs the batch-union path for every codec
  * (colibrì summary, fr.news.hada.io topic 31297, "Principales
  * fonctionnalités implémentées": in prefill and batched verification each
@@ -211,6 +212,15 @@ moe_status_t moe_layer_forward(moe_layer_t* layer, const uint16_t* d_x, int T, f
 moe_status_t moe_layer_forward_noalloc(moe_layer_t* layer, const uint16_t* d_x, int T, float* d_y, int32_t* d_ids,
                                        float* d_w, void* stream);
 
+/* moe_hbm_read_probe: device read ceiling the streaming kernels are
+ * measured against (the analogue of the disk read benchmark in the colibri
+ * repository, fr.news.hada.io topic 31297, "Structure du depot et
+ * licence"): one launch of `blocks` workgroups of 256 threads reads the
+ * `bytes` (a multiple of 16, 16-byte aligned) at d_buf once with
+ * non-temporal 16-byte loads and writes one word per workgroup to d_sink
+ * (device, `blocks` words).  Asynchronous on stream; time it with events. */
+moe_status_t moe_hbm_read_probe(const void* d_buf, size_t bytes, unsigned* d_sink, int blocks, void* stream);
+
 /* moe_dispatch: the batch-union dispatch of a routing d_ids int32 [T][top_k]
  * (device) on the layer's workspace (T <= min(max_T, 8192 / top_k)):
  * d_counts [n_experts] entries per expert; d_offsets [n_experts + 1] their
@@ -225,6 +235,25 @@ moe_status_t moe_layer_forward_noalloc(moe_layer_t* layer, const uint16_t* d_x, 
 moe_status_t moe_dispatch(moe_layer_t* layer, const int32_t* d_ids, int T, int32_t* d_counts, int32_t* d_offsets,
                           int32_t* d_perm, int32_t* d_distinct, int32_t* d_n_distinct, void* stream);
 
+/* moe_layer_set_decode: how one-token calls run.  launches = 3 (the
+ * default): three launches per token (router + shared gate/up, routed
+ * gate/up, down + combine).  launches = 1: one fused launch per token, in
+ * which co-resident workgroups run the router, the top-k, the routed and
+ * shared gate/up, the down projections and the combine with the hand-offs
+ * between them done inside the kernel, used when the kernel has an instance
+ * for the layer's shape and codec (int4 experts), the layer has no expert
+ * cache and all of its workgroups fit on the device at once (checked once
+ * per layer with the occupancy API); otherwise three launches.  On the
+ * GLM-shaped layer the fused launch takes longer than the three (with one
+ * workgroup per CU its gate/up streaming keeps fewer loads in flight than
+ * the dedicated kernel's), hence the default.  Both give bit-identical
+ * results.  spin_limit: polls of an in-kernel wait before
+ * it gives up (0: the default, about one second); a wait that gives up lets
+ * the launch finish, and every later moe_layer_forward,
+ * moe_layer_forward_noalloc or moe_layer_profile_read of the layer returns
+ * MOE_EHIP until a workspace is bound again (moe_layer_set_workspace). */
+moe_status_t moe_layer_set_decode(moe_layer_t* layer, int launches, unsigned spin_limit);
+
 /* moe_layer_profile: when enable != 0, moe_layer_forward times each of its
  * kernel launches with HIP events on the call's stream until profiling is
  * disabled: the events are stamped with the kernel's own begin and end
@@ -233,10 +262,10 @@ moe_status_t moe_dispatch(moe_layer_t* layer, const int32_t* d_ids, int T, int32
  * routing, the copies' ordering and the gate/up launches.
  * moe_layer_profile_read synchronises on the recorded events and returns,
  * per kernel kind (0 router, 1 gate/up + SwiGLU of the shared and routed
- * experts, 2 down + combine), the summed duration in milliseconds and the
- * number of launches since profiling was enabled; arrays of 3 entries.
- * Timings taken with profiling enabled are per-kernel durations, not
- * end-to-end throughput. */
+ * experts, 2 down + combine, 3 fused one-token launch), the summed duration
+ * in milliseconds and the number of launches since profiling was enabled;
+ * arrays of 4 entries.  Timings taken with profiling enabled are per-kernel
+ * durations, not end-to-end throughput. */
 moe_status_t moe_layer_profile(moe_layer_t* layer, int enable);
 moe_status_t moe_layer_profile_read(moe_layer_t* layer, double* total_ms, uint64_t* launches);
 

@@ -66,8 +66,10 @@ _SIGNATURES = {
     "moe_layer_forward": ([_vp, _vp, _i, _vp, _vp, _vp, _vp], _i),
     "moe_layer_forward_noalloc": ([_vp, _vp, _i, _vp, _vp, _vp, _vp], _i),
     "moe_layer_profile": ([_vp, _i], _i),
+    "moe_layer_set_decode": ([_vp, _i, ctypes.c_uint], _i),
     "moe_layer_profile_read": ([_vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_uint64)], _i),
     "moe_dispatch": ([_vp, _vp, _i, _vp, _vp, _vp, _vp, _vp, _vp], _i),
+    "moe_hbm_read_probe": ([_vp, _sz, _vp, _i, _vp], _i),
     "expert_cache_create": ([ctypes.POINTER(MoeConfig), _i, _i, _vp, _sz, _vp, ctypes.POINTER(_vp)], _i),
     "expert_cache_register": ([_vp, _i, _i, _vp, _sz], _i),
     "expert_cache_prefetch": ([_vp, _i, _vp, _i], _i),
@@ -188,14 +190,22 @@ def moe_dispatch(layer: int, d_ids, T: int, d_counts, d_offsets, d_perm, d_disti
                              _ptr(d_distinct), _ptr(d_n_distinct), _stream_handle(stream)))
 
 
+def moe_hbm_read_probe(d_buf, nbytes: int, d_sink, blocks: int, stream=None) -> None:
+    check(lib().moe_hbm_read_probe(_ptr(d_buf), int(nbytes), _ptr(d_sink), int(blocks), _stream_handle(stream)))
+
+
 def moe_layer_profile(layer: int, enable: bool) -> None:
     check(lib().moe_layer_profile(layer, 1 if enable else 0))
 
 
+def moe_layer_set_decode(layer: int, launches: int, spin_limit: int = 0) -> None:
+    check(lib().moe_layer_set_decode(layer, int(launches), int(spin_limit)))
+
+
 def moe_layer_profile_read(layer: int):
-    """-> (total_ms[3], launches[3]) for router, gate/up + SwiGLU, down + combine."""
-    ms = (ctypes.c_double * 3)()
-    n = (ctypes.c_uint64 * 3)()
+    """-> (total_ms[4], launches[4]) for router, gate/up + SwiGLU, down + combine, fused one-token launch."""
+    ms = (ctypes.c_double * 4)()
+    n = (ctypes.c_uint64 * 4)()
     check(lib().moe_layer_profile_read(layer, ms, n))
     return [float(v) for v in ms], [int(v) for v in n]
 

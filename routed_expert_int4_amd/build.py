@@ -14,7 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OBJ_DIR = os.path.join(os.path.dirname(HERE), "_build")
 LIB = os.path.join(HERE, "libmoe_int4.so")
-SOURCES = ["moe_decode.hip", "moe_batch.hip", "moe_abi.cpp", "moe_cache.cpp", "moe_static.hip"]
+SOURCES = ["moe_decode.hip", "moe_batch.hip", "moe_abi.cpp", "moe_cache.cpp", "moe_static.hip", "moe_probe.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",

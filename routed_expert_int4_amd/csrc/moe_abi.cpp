@@ -85,6 +85,8 @@ WorkspaceLayout workspace_layout(const moe_config_t* c, int max_T) {
     W.control = o;
     o = align256(o + 256);
     W.control_bytes = 256;
+    W.sync = o;
+    o = align256(o + kSyncBytes);
     W.s = o;
     o = align256(o + sizeof(float) * (size_t)c->n_experts);
     W.sb = o;
@@ -266,6 +268,13 @@ moe_status_t moe_layer_create(const moe_config_t* cfg, const float* d_router_w, 
         L->shared.push_back(static_cast<const uint8_t*>(d_shared_blobs[s]));
     }
     L->host_table.assign((size_t)cfg->n_experts, nullptr);
+    // host-visible status word of the fused decode launch (pinned, mapped)
+    hipError_t e = hipHostMalloc(reinterpret_cast<void**>(&L->status), 64, hipHostMallocDefault);
+    if (e != hipSuccess) {
+        delete L;
+        return hip_fail(e, "moe_layer_create: hipHostMalloc(status word)");
+    }
+    *L->status = 0u;
     *out = L;
     return MOE_OK;
 }
@@ -279,11 +288,14 @@ moe_status_t moe_layer_set_workspace(moe_layer_t* layer, void* d_ws, size_t byte
         return fail(MOE_EINVAL, "workspace too small: %zu bytes given, %zu needed for max_T=%d", bytes, W.total,
                     max_T);
     hipError_t e = hipMemset(static_cast<uint8_t*>(d_ws) + W.control, 0, W.control_bytes);
+    if (e == hipSuccess) e = hipMemset(static_cast<uint8_t*>(d_ws) + W.sync, 0, kSyncBytes);
     if (e != hipSuccess) return hip_fail(e, "hipMemset(workspace control)");
     layer->ws = static_cast<uint8_t*>(d_ws);
     layer->ws_bytes = bytes;
     layer->max_T = max_T;
     layer->W = W;
+    layer->fused_seq = 0;  // the control words were just cleared
+    *layer->status = 0u;
     if (layer->experts_set) {
         e = hipMemcpy(layer->ws + W.table, layer->host_table.data(), sizeof(void*) * layer->host_table.size(),
                       hipMemcpyHostToDevice);
@@ -312,6 +324,7 @@ moe_status_t moe_layer_set_experts(moe_layer_t* layer, const void* const* d_blob
 void moe_layer_destroy(moe_layer_t* layer) {
     if (!layer) return;
     for (hipEvent_t e : layer->prof_events) (void)hipEventDestroy(e);
+    if (layer->status) (void)hipHostFree(layer->status);
     delete layer;
 }
 
@@ -325,7 +338,7 @@ moe_status_t moe_layer_profile(moe_layer_t* layer, int enable) {
 
 moe_status_t moe_layer_profile_read(moe_layer_t* layer, double* total_ms, uint64_t* launches) {
     if (!layer || !total_ms || !launches) return fail(MOE_EINVAL, "moe_layer_profile_read: NULL argument");
-    for (int k = 0; k < 3; ++k) {
+    for (int k = 0; k < kProfileKinds; ++k) {
         total_ms[k] = 0.0;
         launches[k] = 0;
     }
@@ -338,6 +351,14 @@ moe_status_t moe_layer_profile_read(moe_layer_t* layer, double* total_ms, uint64
         total_ms[m.first] += ms;
         launches[m.first] += 1;
     }
+    return check_layer_status(layer, "moe_layer_profile_read");
+}
+
+moe_status_t moe_layer_set_decode(moe_layer_t* layer, int launches, unsigned spin_limit) {
+    if (!layer) return fail(MOE_EINVAL, "moe_layer_set_decode: layer is NULL");
+    if (launches != 1 && launches != 3) return fail(MOE_EINVAL, "moe_layer_set_decode: launches must be 1 or 3");
+    layer->decode_launches = launches;
+    layer->spin_limit = spin_limit ? spin_limit : kDefaultSpinLimit;
     return MOE_OK;
 }
 
@@ -519,6 +540,8 @@ moe_status_t moe_layer_forward(moe_layer_t* layer, const uint16_t* d_x, int T, f
                                float* d_w, void* stream) {
     moe_status_t st = check_call(layer, d_x, T, "moe_layer_forward");
     if (st != MOE_OK) return st;
+    st = check_layer_status(layer, "moe_layer_forward");
+    if (st != MOE_OK) return st;
     if (T > 0 && !d_y) return fail(MOE_EINVAL, "moe_layer_forward: y is NULL");
     if (!layer->cache && !layer->experts_set)
         return fail(MOE_EINVAL, "moe_layer_forward: no experts set and no cache attached");
@@ -555,20 +578,63 @@ moe_status_t moe_layer_forward(moe_layer_t* layer, const uint16_t* d_x, int T, f
         }
         return MOE_OK;
     }
-    return decode_tokens(layer, layer->ws, layer->W, d_x, T, d_y, ids_base, c.top_k, w_base, c.top_k, s);
+    return decode_tokens(layer, layer->ws, layer->W, d_x, T, d_y, ids_base, c.top_k, w_base, c.top_k,
+                         &layer->fused_seq, s);
 }
 
 }  // extern "C"
 
 namespace moe {
 
+moe_status_t check_layer_status(const moe_layer* L, const char* who) {
+    if (L->status && __atomic_load_n(L->status, __ATOMIC_ACQUIRE) != 0u)
+        return fail(MOE_EHIP, "%s: a wait inside the fused decode launch gave up (its workgroups were not all "
+                    "resident at once); outputs since then are not valid; bind the workspace again to reset", who);
+    return MOE_OK;
+}
+
+// Whether the fused one-token launch serves this layer: not behind an expert
+// cache (the host must see each token's routing), an instance for the shape
+// and codec, and every workgroup resident at once (occupancy per CU times
+// the CU count covers the grid; checked once per layer).
+static bool use_fused(moe_layer_t* L, const DecodeArgs& a) {
+    if (L->cache || L->decode_launches != 1) return false;
+    if (L->fused_fits < 0) {
+        L->fused_fits = 0;
+        int threads = 0, per_cu = 0, dev = 0, cus = 0;
+        const int grid = fused_grid(a, &threads);
+        const void* fn = fused_kernel_function(a);
+        if (grid > 0 && fn && hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, threads, 0) == hipSuccess)
+            L->fused_fits = (long long)per_cu * cus >= grid ? 1 : 0;
+        (void)hipGetLastError();
+    }
+    return L->fused_fits == 1;
+}
+
 moe_status_t decode_tokens(moe_layer_t* layer, uint8_t* ws, const WorkspaceLayout& W, const uint16_t* d_x, int T,
-                           float* d_y, int32_t* ids_base, int ids_stride, float* w_base, int w_stride, hipStream_t s) {
+                           float* d_y, int32_t* ids_base, int ids_stride, float* w_base, int w_stride,
+                           unsigned* fused_seq, hipStream_t s) {
     const moe_config_t& c = layer->cfg;
     moe_status_t st = MOE_OK;
     for (int t = 0; t < T; ++t) {
         DecodeArgs a = decode_args(layer, ws, W, d_x + (size_t)t * c.hidden, ids_base + (size_t)t * ids_stride,
                                    w_base + (size_t)t * w_stride, d_y + (size_t)t * c.hidden);
+        if (use_fused(layer, a)) {
+            FusedArgs f;
+            f.h_done = reinterpret_cast<unsigned*>(ws + W.sync);
+            f.shared_done = reinterpret_cast<unsigned*>(ws + W.sync + kSyncCounterBytes);
+            f.s_rec = reinterpret_cast<unsigned long long*>(ws + W.sync + 2 * kSyncCounterBytes);
+            f.sb_rec = f.s_rec + kSyncMaxExperts;
+            f.status = layer->status;
+            f.seq = ++*fused_seq;
+            f.spin_limit = layer->spin_limit;
+            ProfileScope pf(layer, 3, s, ProfileScope::kKernel);
+            hipError_t e = decode_fused(a, f, s, pf.timing());
+            if (e != hipSuccess) return hip_fail(e, "fused decode launch");
+            continue;
+        }
         ProfileScope p0(layer, 0, s, ProfileScope::kKernel);
         hipError_t e = decode_router(a, s, p0.timing());
         if (e != hipSuccess) return hip_fail(e, "router kernel launch");

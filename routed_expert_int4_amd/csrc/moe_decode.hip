@@ -469,11 +469,14 @@ __device__ __forceinline__ size_t h_index(int i, int kgi) {
 
 // Computes one item from its loaded buffer: h = silu(g) * u for rows
 // [rb*R, rb*R + R), written as fp32 at their h_index positions.
-template <int KG, int F>
-__device__ __forceinline__ void gateup_compute(const GateUpBuf<KG, F>& b, int rb, int lane,
-                                               const HI8 (&xa)[GateUpShape<KG>::CPL],
-                                               const float (&xs)[GateUpShape<KG>::CPL], float* __restrict__ h_out,
-                                               int kgi, bool store) {
+// With SC the h values are stored with device-scope atomic stores, so that
+// workgroups of the same launch on other XCDs can read them (the fused
+// decode kernel); otherwise with plain stores, read after the launch ends.
+// The activation operands come from xsrc(c, operands, factor) for chunk
+// column c (registers, or LDS in the fused kernel).
+template <int KG, int F, bool SC = false, typename XSrc>
+__device__ __forceinline__ void gateup_compute_src(const GateUpBuf<KG, F>& b, int rb, int lane, const XSrc& xsrc,
+                                                   float* __restrict__ h_out, int kgi, bool store) {
     using S = GateUpShape<KG>;
     constexpr int RP = row_pack(F);
     constexpr int NV = S::NV * RP;  // gate then up; inside each, row parity then step
@@ -485,13 +488,16 @@ __device__ __forceinline__ void gateup_compute(const GateUpBuf<KG, F>& b, int rb
             float ag0 = 0.0f, ag1 = 0.0f, au0 = 0.0f, au1 = 0.0f;
 #pragma unroll
             for (int c = 0; c < S::CPL; ++c) {
+                HI8 xc;
+                float xsc;
+                xsrc(c, xc, xsc);
                 float g0, g1, u0, u1;
-                dot_chunk_int2(b.cg[n][c][0], xa[c], g0, g1);
-                dot_chunk_int2(b.cu[n][c][0], xa[c], u0, u1);
-                ag0 = fmaf(scale_at<F>(b.sgu[0][c], n) * xs[c], g0, ag0);
-                ag1 = fmaf(scale_at<F>(b.sgu[RP - 1][c], n) * xs[c], g1, ag1);
-                au0 = fmaf(scale_at<F>(b.sgu[0][c], S::NL + n) * xs[c], u0, au0);
-                au1 = fmaf(scale_at<F>(b.sgu[RP - 1][c], S::NL + n) * xs[c], u1, au1);
+                dot_chunk_int2(b.cg[n][c][0], xc, g0, g1);
+                dot_chunk_int2(b.cu[n][c][0], xc, u0, u1);
+                ag0 = fmaf(scale_at<F>(b.sgu[0][c], n) * xsc, g0, ag0);
+                ag1 = fmaf(scale_at<F>(b.sgu[RP - 1][c], n) * xsc, g1, ag1);
+                au0 = fmaf(scale_at<F>(b.sgu[0][c], S::NL + n) * xsc, u0, au0);
+                au1 = fmaf(scale_at<F>(b.sgu[RP - 1][c], S::NL + n) * xsc, u1, au1);
             }
             v[n] = ag0;
             v[S::NL + n] = ag1;
@@ -501,8 +507,11 @@ __device__ __forceinline__ void gateup_compute(const GateUpBuf<KG, F>& b, int rb
             float ag = 0.0f, au = 0.0f;
 #pragma unroll
             for (int c = 0; c < S::CPL; ++c) {
-                ag = fmaf(scale_at<F>(b.sgu[0][c], n) * xs[c], dot_planes<F>(b.cg[n][c], xa[c]), ag);
-                au = fmaf(scale_at<F>(b.sgu[0][c], S::NL + n) * xs[c], dot_planes<F>(b.cu[n][c], xa[c]), au);
+                HI8 xc;
+                float xsc;
+                xsrc(c, xc, xsc);
+                ag = fmaf(scale_at<F>(b.sgu[0][c], n) * xsc, dot_planes<F>(b.cg[n][c], xc), ag);
+                au = fmaf(scale_at<F>(b.sgu[0][c], S::NL + n) * xsc, dot_planes<F>(b.cu[n][c], xc), au);
             }
             v[n] = ag;
             v[S::NL + n] = au;
@@ -521,8 +530,27 @@ __device__ __forceinline__ void gateup_compute(const GateUpBuf<KG, F>& b, int rb
         const float g = r, u = other;
         const float h = g / (1.0f + expf(-g)) * u;
         const int n = vi % S::NL, parity = vi / S::NL;
-        h_out[h_index(RP * (rb * S::R + n * S::RPL + row_sub) + parity, kgi)] = h;
+        float* dst = h_out + h_index(RP * (rb * S::R + n * S::RPL + row_sub) + parity, kgi);
+        if constexpr (SC)
+            __hip_atomic_store(dst, h, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        else
+            *dst = h;
     }
+}
+
+// Operands held in registers.
+template <int KG, int F, bool SC = false>
+__device__ __forceinline__ void gateup_compute(const GateUpBuf<KG, F>& b, int rb, int lane,
+                                               const HI8 (&xa)[GateUpShape<KG>::CPL],
+                                               const float (&xs)[GateUpShape<KG>::CPL], float* __restrict__ h_out,
+                                               int kgi, bool store) {
+    gateup_compute_src<KG, F, SC>(
+        b, rb, lane,
+        [&](int c, HI8& o, float& f) {
+            o = xa[c];
+            f = xs[c];
+        },
+        h_out, kgi, store);
 }
 
 // Group-limited top-k of the token from s and sb (written by the router
@@ -531,17 +559,12 @@ __device__ __forceinline__ void gateup_compute(const GateUpBuf<KG, F>& b, int rb
 // its blob from the table (null without a table, and in lanes >= K).  The
 // table entries of the lane's own experts are fetched beside its scores, so
 // resolving the blobs costs no dependent load.
+// The top-k of route_token from the lane's scores and table entries
+// (experts lane * EPL .. lane * EPL + EPL - 1).
 template <int EPL>
-__device__ __forceinline__ void route_token(const DecodeArgs& a, int lane, int* id, float* w, const uint8_t** blob) {
-    float sv[EPL], key[EPL];
-    const uint8_t* tab[EPL];
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) {
-        const int e = lane * EPL + i;
-        sv[i] = e < a.E ? __hip_atomic_load(a.s + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0.0f;
-        key[i] = e < a.E ? __hip_atomic_load(a.sb + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : -__builtin_inff();
-        tab[i] = a.table && e < a.E ? a.table[e] : nullptr;
-    }
+__device__ __forceinline__ void route_values(const DecodeArgs& a, int lane, const float (&sv)[EPL],
+                                             const float (&key)[EPL], const uint8_t* const (&tab)[EPL], int* id,
+                                             float* w, const uint8_t** blob) {
     wave_group_topk_values<EPL>(sv, key, a.E, a.G, a.TG, a.K, a.rsf, a.top_p, lane, id, w);
     // lane j < K: the blob of its choice, held by lane id / EPL (none for a
     // choice the top-p cut dropped)
@@ -560,6 +583,20 @@ __device__ __forceinline__ void route_token(const DecodeArgs& a, int lane, int* 
         if (chosen) a.kept[1 + __popcll(m & ((1ull << lane) - 1))] = lane;
         if (lane == 0) a.kept[0] = __popcll(m);
     }
+}
+
+template <int EPL>
+__device__ __forceinline__ void route_token(const DecodeArgs& a, int lane, int* id, float* w, const uint8_t** blob) {
+    float sv[EPL], key[EPL];
+    const uint8_t* tab[EPL];
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+        const int e = lane * EPL + i;
+        sv[i] = e < a.E ? __hip_atomic_load(a.s + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0.0f;
+        key[i] = e < a.E ? __hip_atomic_load(a.sb + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : -__builtin_inff();
+        tab[i] = a.table && e < a.E ? a.table[e] : nullptr;
+    }
+    route_values<EPL>(a, lane, sv, key, tab, id, w, blob);
 }
 
 // ---------------------------------------------------------------- kernel 1
@@ -866,6 +903,118 @@ __device__ __forceinline__ void load_h(const float* __restrict__ h, int g0, floa
     }
 }
 
+// Down-projection work of one wave: one slot's blob over the R rows of row
+// block rb.  Code loads go in rounds of WIN steps; compute_round folds a
+// round into the per-step partials v, store_part reduces them over the
+// lanes into the workgroup's part row of this slot.
+template <int KG, int NLD, int F>
+struct DownWork {
+    using S = DownShape<KG, NLD>;
+    static constexpr int WIN = S::WIN;
+    static constexpr int NR = (S::NL + WIN - 1) / WIN;  // rounds
+    static constexpr int RP = row_pack(F);               // matrix rows per stored row (int2: 2)
+    static constexpr int P = code_planes(F);
+    static constexpr int NVP = pow2_at_least(S::NL * RP);
+    const uint8_t* blob;
+    BlobLayout L;
+    int rb, g0, row_sub;
+    u32x4 code[S::NL][S::CPL][P];
+    unsigned sc[RP][S::CPL][(S::NL + 1) / 2];
+
+    __device__ __forceinline__ void init(const uint8_t* b, const DecodeArgs& a, int block, int lane) {
+        blob = b;
+        L = blob_layout(a.H, a.I, F);
+        rb = block;
+        g0 = KG >= kWave ? lane : (lane & (KG - 1));
+        row_sub = KG >= kWave ? 0 : (lane / KG);
+    }
+    __device__ __forceinline__ size_t code_off(int step, int c) const {
+        const size_t row = (size_t)rb * S::R + step * S::RPL + row_sub;
+        return (row * KG + g0 + kWave * c) * 16;
+    }
+    __device__ __forceinline__ void issue_round(int r) {
+#pragma unroll
+        for (int n = r * WIN; n < (r + 1) * WIN && n < S::NL; ++n)
+#pragma unroll
+            for (int c = 0; c < S::CPL; ++c)
+#pragma unroll
+                for (int p = 0; p < P; ++p)
+                    code[n][c][p] = load_stream16(blob + (p ? L.down_lo : L.down_q) + code_off(n, c));
+    }
+    __device__ __forceinline__ void load_scales() {
+#pragma unroll
+        for (int h = 0; h < RP; ++h)
+#pragma unroll
+            for (int c = 0; c < S::CPL; ++c) {
+                const size_t si = ((size_t)rb * KG + g0 + kWave * c) * S::R + (size_t)row_sub * S::NL;
+                load_scales_c<F, S::NL>(blob + (h ? L.down_s2 : L.down_s) + si * scale_bytes(F), sc[h][c]);
+            }
+    }
+    __device__ __forceinline__ void compute_round(int r, const HI8 (&ha)[S::CPL], const float (&hscale)[S::CPL],
+                                                  float (&v)[NVP]) const {
+#pragma unroll
+        for (int n = r * WIN; n < (r + 1) * WIN && n < S::NL; ++n) {
+            if constexpr (F == kCodecInt2) {
+                float acc0 = 0.0f, acc1 = 0.0f;
+#pragma unroll
+                for (int c = 0; c < S::CPL; ++c) {
+                    float d0, d1;
+                    dot_chunk_int2(code[n][c][0], ha[c], d0, d1);
+                    acc0 = fmaf(scale_at<F>(sc[0][c], n) * hscale[c], d0, acc0);
+                    acc1 = fmaf(scale_at<F>(sc[RP - 1][c], n) * hscale[c], d1, acc1);
+                }
+                v[n] = acc0;
+                v[S::NL + n] = acc1;
+            } else {
+                float acc = 0.0f;
+#pragma unroll
+                for (int c = 0; c < S::CPL; ++c)
+                    acc = fmaf(scale_at<F>(sc[0][c], n) * hscale[c], dot_planes<F>(code[n][c], ha[c]), acc);
+                v[n] = acc;
+            }
+        }
+    }
+    // part[row parity * R + stored row of the block]
+    __device__ __forceinline__ void store_part(float (&v)[NVP], int lane, float* part) const {
+        const float r = reduce_scatter<NVP, S::B>(v, lane);
+        const int low_bits = S::B - ilog2(NVP);
+        const int vi = (lane >> low_bits) & (NVP - 1);
+        // value index: row parity, then step
+        if ((lane & ((1 << low_bits) - 1)) == 0 && vi < RP * S::NL)
+            part[(vi / S::NL) * S::R + (vi % S::NL) * S::RPL + row_sub] = r;
+    }
+    // Every round already issued: h to operands, the rounds computed in order.
+    __device__ __forceinline__ void finish_issued(const float (&hraw)[S::CPL][32], int lane, float* part) {
+        HI8 ha[S::CPL];
+        float hscale[S::CPL];
+        to_operands<F, S::CPL>(hraw, ha, hscale);
+        float v[NVP];
+#pragma unroll
+        for (int n = 0; n < NVP; ++n) v[n] = 0.0f;
+#pragma unroll
+        for (int r = 0; r < NR; ++r) compute_round(r, ha, hscale, v);
+        store_part(v, lane, part);
+    }
+    // The whole row block after the first rounds were issued: h to operands,
+    // the rounds computed in order with round r + 2 issued after round r.
+    __device__ __forceinline__ void finish(const float (&hraw)[S::CPL][32], int lane, float* part) {
+        HI8 ha[S::CPL];
+        float hscale[S::CPL];
+        to_operands<F, S::CPL>(hraw, ha, hscale);
+        float v[NVP];
+#pragma unroll
+        for (int n = 0; n < NVP; ++n) v[n] = 0.0f;
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+            __builtin_amdgcn_sched_barrier(0);
+            compute_round(r, ha, hscale, v);
+            __builtin_amdgcn_sched_barrier(0);
+            if (r + 2 < NR) issue_round(r + 2);
+        }
+        store_part(v, lane, part);
+    }
+};
+
 // One workgroup = one wave per slot (the routed slots, then the shared
 // expert) over a block of R output rows.  Row loads go in rounds of WIN
 // steps, the next round issued before the current one is computed
@@ -874,18 +1023,14 @@ __device__ __forceinline__ void load_h(const float* __restrict__ h, int g0, floa
 template <int KG, int NLD, int F>
 __global__ void __launch_bounds__(576) down_combine_kernel(DecodeArgs a) {
     using S = DownShape<KG, NLD>;
+    using D = DownWork<KG, NLD, F>;
     constexpr int MAXW = 9;
-    constexpr int WIN = S::WIN;
-    constexpr int NR = (S::NL + WIN - 1) / WIN;  // rounds
-    constexpr int RP = row_pack(F);                  // matrix rows per stored row (int2: 2)
-    constexpr int NVP = pow2_at_least(S::NL * RP);
+    constexpr int RP = D::RP;
     const int lane = threadIdx.x & 63;
     const int slot = wave_in_block();
     const int K = a.K;
     const int g0 = KG >= kWave ? lane : (lane & (KG - 1));
-    const int row_sub = KG >= kWave ? 0 : (lane / KG);
     const int rb = blockIdx.x;
-    const BlobLayout L = blob_layout(a.H, a.I, F);
     const uint8_t* blob = slot >= K ? a.shared_blob
                                     : (a.direct ? readlane_ptr(lane_pick(a.blobs, lane), slot) : a.slot_blobs[slot]);
     __shared__ float part[MAXW][RP * S::R];  // [slot][row parity * R + stored row of the block]
@@ -898,72 +1043,14 @@ __global__ void __launch_bounds__(576) down_combine_kernel(DecodeArgs a) {
         // a routed slot that the top-p cut dropped: weight 0, nothing read
         for (int t = lane; t < RP * S::R; t += kWave) part[slot][t] = 0.0f;
     } else {
-        auto code_off = [&](int step, int c) {
-            const size_t row = (size_t)rb * S::R + step * S::RPL + row_sub;
-            return (row * KG + g0 + kWave * c) * 16;
-        };
-        constexpr int P = code_planes(F);
-        u32x4 code[S::NL][S::CPL][P];
-        auto issue_round = [&](int r) {
-#pragma unroll
-            for (int n = r * WIN; n < (r + 1) * WIN && n < S::NL; ++n)
-#pragma unroll
-                for (int c = 0; c < S::CPL; ++c)
-#pragma unroll
-                    for (int p = 0; p < P; ++p)
-                        code[n][c][p] = load_stream16(blob + (p ? L.down_lo : L.down_q) + code_off(n, c));
-        };
+        D d;
+        d.init(blob, a, rb, lane);
         __builtin_amdgcn_sched_barrier(0);
-        issue_round(0);
-        unsigned sc[RP][S::CPL][(S::NL + 1) / 2];
-#pragma unroll
-        for (int h = 0; h < RP; ++h)
-#pragma unroll
-            for (int c = 0; c < S::CPL; ++c) {
-                const size_t si = ((size_t)rb * KG + g0 + kWave * c) * S::R + (size_t)row_sub * S::NL;
-                load_scales_c<F, S::NL>(blob + (h ? L.down_s2 : L.down_s) + si * scale_bytes(F), sc[h][c]);
-            }
-        if constexpr (NR > 1) issue_round(1);
+        d.issue_round(0);
+        d.load_scales();
+        if constexpr (D::NR > 1) d.issue_round(1);
         __builtin_amdgcn_sched_barrier(0);
-        HI8 ha[S::CPL];
-        float hscale[S::CPL];
-        to_operands<F, S::CPL>(hraw, ha, hscale);
-        float v[NVP];
-#pragma unroll
-        for (int n = 0; n < NVP; ++n) v[n] = 0.0f;
-#pragma unroll
-        for (int r = 0; r < NR; ++r) {
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int n = r * WIN; n < (r + 1) * WIN && n < S::NL; ++n) {
-                if constexpr (F == kCodecInt2) {
-                    float acc0 = 0.0f, acc1 = 0.0f;
-#pragma unroll
-                    for (int c = 0; c < S::CPL; ++c) {
-                        float d0, d1;
-                        dot_chunk_int2(code[n][c][0], ha[c], d0, d1);
-                        acc0 = fmaf(scale_at<F>(sc[0][c], n) * hscale[c], d0, acc0);
-                        acc1 = fmaf(scale_at<F>(sc[RP - 1][c], n) * hscale[c], d1, acc1);
-                    }
-                    v[n] = acc0;
-                    v[S::NL + n] = acc1;
-                } else {
-                    float acc = 0.0f;
-#pragma unroll
-                    for (int c = 0; c < S::CPL; ++c)
-                        acc = fmaf(scale_at<F>(sc[0][c], n) * hscale[c], dot_planes<F>(code[n][c], ha[c]), acc);
-                    v[n] = acc;
-                }
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            if (r + 2 < NR) issue_round(r + 2);
-        }
-        const float r = reduce_scatter<NVP, S::B>(v, lane);
-        const int low_bits = S::B - ilog2(NVP);
-        const int vi = (lane >> low_bits) & (NVP - 1);
-        // value index: row parity, then step
-        if ((lane & ((1 << low_bits) - 1)) == 0 && vi < RP * S::NL)
-            part[slot][(vi / S::NL) * S::R + (vi % S::NL) * S::RPL + row_sub] = r;
+        d.finish(hraw, lane, part[slot]);
     }
     __syncthreads();
     if ((int)threadIdx.x < RP * S::R) {
@@ -973,6 +1060,556 @@ __global__ void __launch_bounds__(576) down_combine_kernel(DecodeArgs a) {
         if (a.S > 0) y += part[K][t];
         a.y[(size_t)RP * (rb * S::R + t % S::R) + t / S::R] = y;
     }
+}
+
+// ---------------------------------------------------------------- fused decode
+// One launch per token running the three stages above on workgroups that
+// are all resident at once, with the two hand-offs done inside the kernel.
+// A workgroup has one wave per routed slot (K waves, two per SIMD for
+// K = 8) and owns the down rows of one row block:
+//   phase 0  router rows (one W_r row per wave, as router_kernel), each
+//            score published as a (value, call number) record, and the
+//            shared expert's gate/up items, spread over every wave; the
+//            token's activation operands are converted once per
+//            workgroup into LDS;
+//   routing  wave 0 polls the score records until all E carry this call's
+//            number and runs the group-limited top-k (every workgroup
+//            derives the same routing); workgroup 0 writes ids and w;
+//   phase 1  the routed gate/up items, the same number per wave;
+//   phase 2  wave w: the down rows of slot w over the block, and the shared
+//            expert's rows of the block congruent to w modulo K; all code
+//            loads are issued, then the workgroup waits until every
+//            workgroup has published its h values, reads h and finishes.
+// Hand-off data (score records, h) is written with device-scope atomic
+// stores; h writers wait for the stores' acknowledgement (s_waitcnt) before
+// a device-scope counter increment, and readers poll, then read with
+// device-scope loads.  Every value is computed exactly as on the
+// three-launch path (the shared expert's rows sit at the same places of the
+// same wave reduction), so both paths give bit-identical results.
+//
+// Global wave index gw = wave * grid + block: consecutive work units land on
+// different workgroups (and CUs), so a ragged last round spreads over the
+// chip.
+
+// Adds one to a spread count (contribution index i).
+__device__ __forceinline__ void count_up(unsigned* ctr, int i) {
+    __hip_atomic_fetch_add(ctr + (i % kSyncCounters) * kSyncStride, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Polls a spread count until its words sum to target (one device-scope load
+// per lane, a wave sum); false after limit polls.  Called by a whole wave.
+__device__ __forceinline__ bool wait_count(const unsigned* ctr, unsigned target, unsigned limit, int lane) {
+    for (unsigned i = 0; i < limit; ++i) {
+        unsigned v = lane < kSyncCounters
+                         ? __hip_atomic_load(ctr + lane * kSyncStride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                         : 0u;
+#pragma unroll
+        for (int o = 1; o < kSyncCounters; o <<= 1) v += __shfl_xor(v, o);
+        if (__builtin_amdgcn_readfirstlane(v) == target) return true;
+        __builtin_amdgcn_s_sleep(1);
+    }
+    return false;
+}
+
+// Chunk column c of the token's activation operands (the values
+// convert_activations gives), converted by one wave into LDS in
+// structure-of-arrays order: xo[c][q][lane] (he, ho, le, lo) and
+// xm[c][lane] (corr, factor).
+template <int KG, int F>
+__device__ __forceinline__ void convert_column_to_lds(const uint16_t* __restrict__ x, int lane, int c, u32x4* xo,
+                                                      u32x2* xm) {
+    const int g0 = KG >= kWave ? lane : (lane & (KG - 1));
+    const uint16_t* xg = x + 32 * (g0 + kWave * c);
+    float xv[1][32];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const u32x4 raw = *reinterpret_cast<const u32x4*>(xg + 8 * q);
+#pragma unroll
+        for (int z = 0; z < 4; ++z) {
+            const unsigned d = raw[z];
+            xv[0][8 * q + 2 * z] = __builtin_bit_cast(float, d << 16);
+            xv[0][8 * q + 2 * z + 1] = __builtin_bit_cast(float, d & 0xFFFF0000u);
+        }
+    }
+    HI8 one[1];
+    float one_s[1];
+    to_operands<F, 1>(xv, one, one_s);
+    xo[(c * 4 + 0) * kWave + lane] = one[0].he;
+    xo[(c * 4 + 1) * kWave + lane] = one[0].ho;
+    xo[(c * 4 + 2) * kWave + lane] = one[0].le;
+    xo[(c * 4 + 3) * kWave + lane] = one[0].lo;
+    xm[c * kWave + lane] = u32x2{(unsigned)one[0].corr, __builtin_bit_cast(unsigned, one_s[0])};
+}
+
+// Operand source reading column c of the LDS copy (gateup_compute_src).
+struct LdsOperands {
+    const u32x4* xo;
+    const u32x2* xm;
+    int lane;
+    __device__ __forceinline__ void operator()(int c, HI8& o, float& f) const {
+        o.he = xo[(c * 4 + 0) * kWave + lane];
+        o.ho = xo[(c * 4 + 1) * kWave + lane];
+        o.le = xo[(c * 4 + 2) * kWave + lane];
+        o.lo = xo[(c * 4 + 3) * kWave + lane];
+        const u32x2 m = xm[c * kWave + lane];
+        // elements go through named scalars: this compiler bit-casts a vector
+        // element operand (m[1]) as element 0
+        const unsigned m0 = m[0], m1 = m[1];
+        o.corr = (int)m0;
+        f = __builtin_bit_cast(float, m1);
+    }
+};
+
+// A score record: the value's bits in the low word, the call number in the
+// high word, written and read as one 8-byte device-scope atomic.
+__device__ __forceinline__ unsigned long long score_record(float v, unsigned seq) {
+    return ((unsigned long long)seq << 32) | __builtin_bit_cast(unsigned, v);
+}
+
+// One router row as in router_kernel (one wave per row): the loads, then
+// the fixed-order sum, published as records of s and sb.
+template <int KG>
+struct RouterRow {
+    static constexpr int CR = KG / 8;  // 16-byte chunks per lane of a row
+    f32x4 wv[CR];
+    __device__ __forceinline__ void issue(const DecodeArgs& a, int e, int lane) {
+        const float* row = a.router_w + (size_t)e * a.H;
+#pragma unroll
+        for (int c = 0; c < CR; ++c)
+            wv[c] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(row + 4 * lane + 256 * c));
+    }
+    __device__ __forceinline__ void finish(const DecodeArgs& a, const FusedArgs& f, int e, int lane) {
+        float acc = 0.0f;
+#pragma unroll
+        for (int c = 0; c < CR; ++c) {
+            const u32x2 xb = *reinterpret_cast<const u32x2*>(a.x + 4 * lane + 256 * c);
+            acc = fmaf(wv[c][0], __builtin_bit_cast(float, xb[0] << 16), acc);
+            acc = fmaf(wv[c][1], __builtin_bit_cast(float, xb[0] & 0xFFFF0000u), acc);
+            acc = fmaf(wv[c][2], __builtin_bit_cast(float, xb[1] << 16), acc);
+            acc = fmaf(wv[c][3], __builtin_bit_cast(float, xb[1] & 0xFFFF0000u), acc);
+        }
+        acc = wave_sum(acc);
+        if (lane == 0) {
+            const float sv = 1.0f / (1.0f + expf(-acc));
+            // system scope on both sides: the record goes past every cache
+            // and the polls read it there
+            __hip_atomic_store(f.s_rec + e, score_record(sv, f.seq), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+            __hip_atomic_store(f.sb_rec + e, score_record(sv + a.bias[e], f.seq), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_SYSTEM);
+        }
+    }
+};
+
+// The token's routing on one wave from the score records: polls until every
+// record of the lane's experts carries this call's number (system-scope
+// loads, which no cache line of an earlier poll can satisfy), then runs the
+// top-k.  False if the records were not all there within the spin limit.
+template <int EPL>
+__device__ __forceinline__ bool route_from_records(const DecodeArgs& a, const FusedArgs& f, int lane, int* id,
+                                                   float* w, const uint8_t** blob) {
+    const uint8_t* tab[EPL];
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+        const int e = lane * EPL + i;
+        tab[i] = e < a.E ? a.table[e] : nullptr;
+    }
+    float sv[EPL], key[EPL];
+    bool ok = false;
+    for (unsigned it = 0; it < f.spin_limit && !ok; ++it) {
+        bool mine = true;
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) {
+            const int e = lane * EPL + i;
+            if (e < a.E) {
+                const unsigned long long rs = __hip_atomic_load(f.s_rec + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+                const unsigned long long rb = __hip_atomic_load(f.sb_rec + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+                mine = mine && (unsigned)(rs >> 32) == f.seq && (unsigned)(rb >> 32) == f.seq;
+                sv[i] = __builtin_bit_cast(float, (unsigned)rs);
+                key[i] = __builtin_bit_cast(float, (unsigned)rb);
+            } else {
+                sv[i] = 0.0f;
+                key[i] = -__builtin_inff();
+            }
+        }
+        ok = __ballot(!mine) == 0ull;
+        if (!ok) __builtin_amdgcn_s_sleep(1);
+    }
+    DecodeArgs ar = a;
+    ar.kept = nullptr;
+    route_values<EPL>(ar, lane, sv, key, tab, id, w, blob);
+    return ok;
+}
+
+// h of one slot read with device-scope atomic loads of 8 bytes (written in
+// this launch by workgroups on other XCDs), in the order of load_h.
+template <int CPL, int KG>
+__device__ __forceinline__ void load_h_device_scope(const float* h, int g0, float (&hv)[CPL][32]) {
+    constexpr int G = KG < kWave ? KG : kWave;
+    const uint64_t* h64 = reinterpret_cast<const uint64_t*>(h);
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                const uint64_t v = __hip_atomic_load(h64 + ((size_t)(c * 8 + q) * G + g0) * 2 + half, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT);
+                hv[c][4 * q + 2 * half] = __builtin_bit_cast(float, (unsigned)v);
+                hv[c][4 * q + 2 * half + 1] = __builtin_bit_cast(float, (unsigned)(v >> 32));
+            }
+        }
+    }
+}
+
+// Down rows of one slot over block rb owned by owner m of M (steps n with
+// n mod M == m): their code loads, and their dot products placed at the
+// value indices down_combine_kernel's wave for that slot uses, so that the
+// same wave reduction gives the same sums (the other indices hold zeros,
+// which leave every row's sum unchanged).
+template <int KG, int NLD, int F, int M>
+struct DownSteps {
+    using S = DownShape<KG, NLD>;
+    using D = DownWork<KG, NLD, F>;
+    static constexpr int MAXOWN = (S::NL + M - 1) / M;
+    static constexpr int P = code_planes(F);
+    static_assert(row_pack(F) == 1, "one matrix row per stored row");
+    u32x4 code[MAXOWN][S::CPL][P];
+    unsigned sc[MAXOWN][S::CPL];
+    __device__ __forceinline__ void issue(const uint8_t* blob, const BlobLayout& L, int rb, int lane, int m) {
+        const int g0 = KG >= kWave ? lane : (lane & (KG - 1));
+        const int row_sub = KG >= kWave ? 0 : (lane / KG);
+#pragma unroll
+        for (int i = 0; i < MAXOWN; ++i) {
+            const int step = m + i * M;
+            if (step < S::NL) {
+                const size_t row = (size_t)rb * S::R + step * S::RPL + row_sub;
+#pragma unroll
+                for (int c = 0; c < S::CPL; ++c) {
+#pragma unroll
+                    for (int p = 0; p < P; ++p)
+                        code[i][c][p] = load_stream16(blob + (p ? L.down_lo : L.down_q) + (row * KG + g0 + kWave * c) * 16);
+                    // the step's scale inside the lane's run of NL scales
+                    const size_t si = ((size_t)rb * KG + g0 + kWave * c) * S::R + (size_t)row_sub * S::NL + step;
+                    if constexpr (F == kCodecMxfp4)
+                        sc[i][c] = __builtin_nontemporal_load(as_global<uint8_t>(blob + L.down_s + si));
+                    else
+                        sc[i][c] = __builtin_nontemporal_load(as_global<uint16_t>(blob + L.down_s + 2 * si));
+                }
+            }
+        }
+    }
+    __device__ __forceinline__ void finish(const float (&hraw)[S::CPL][32], int lane, int m, float* part) {
+        HI8 ha[S::CPL];
+        float hscale[S::CPL];
+        to_operands<F, S::CPL>(hraw, ha, hscale);
+        float acc[MAXOWN];
+#pragma unroll
+        for (int i = 0; i < MAXOWN; ++i) {
+            acc[i] = 0.0f;
+            if (m + i * M < S::NL) {
+#pragma unroll
+                for (int c = 0; c < S::CPL; ++c) {
+                    const float scale = F == kCodecMxfp4 ? e8m0_to_float(sc[i][c]) : half_bits_to_float(sc[i][c]);
+                    acc[i] = fmaf(scale * hscale[c], dot_planes<F>(code[i][c], ha[c]), acc[i]);
+                }
+            }
+        }
+        // value j is step j: owned when j mod M == m
+        float v[D::NVP];
+#pragma unroll
+        for (int j = 0; j < D::NVP; ++j) v[j] = (j < S::NL && j % M == m) ? acc[j / M] : 0.0f;
+        const float r = reduce_scatter<D::NVP, S::B>(v, lane);
+        const int low_bits = S::B - ilog2(D::NVP);
+        const int vi = (lane >> low_bits) & (D::NVP - 1);
+        const int row_sub = KG >= kWave ? 0 : (lane / KG);
+        if ((lane & ((1 << low_bits) - 1)) == 0 && vi < S::NL && vi % M == m) part[vi * S::RPL + row_sub] = r;
+    }
+};
+
+// gateup_issue through buffer loads on a resource over the blob; with live
+// false the resource has no records, so every load returns zeros without
+// touching memory (the same loads are issued either way, which keeps the
+// compiler's load counts exact when a wave may run out of items).  For
+// shapes whose rows span whole wave loads (one row per load) with one code
+// plane and one row per stored row.
+constexpr int kLoadNonTemporal = 2;  // cache-policy bits: nt
+template <int KG, int F>
+__device__ __forceinline__ void gateup_issue_buf(const uint8_t* blob, bool live, const BlobLayout& L, int rb, int lane,
+                                                 GateUpBuf<KG, F>& b) {
+    using S = GateUpShape<KG>;
+    static_assert(S::RPL == 1 && code_planes(F) == 1 && row_pack(F) == 1, "one row per wave load");
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(blob), (short)0, live ? 0x7FFFFFF0 : 0, 0x00020000);
+    const int g0 = lane;
+#pragma unroll
+    for (int n = 0; n < S::NL; ++n) {
+        const int row = rb * S::R + n;
+#pragma unroll
+        for (int c = 0; c < S::CPL; ++c) {
+            const int off = (row * KG + g0 + kWave * c) * 16;
+            b.cg[n][c][0] = __builtin_amdgcn_raw_buffer_load_b128(r, (int)L.gate_q + off, 0, kLoadNonTemporal);
+            b.cu[n][c][0] = __builtin_amdgcn_raw_buffer_load_b128(r, (int)L.up_q + off, 0, kLoadNonTemporal);
+        }
+    }
+#pragma unroll
+    for (int c = 0; c < S::CPL; ++c) {
+        // the 2 NL gate and up scales of the lane's group, as in gateup_issue
+        const int p = (int)L.gu_s + (rb * KG + g0 + kWave * c) * 2 * S::R * scale_bytes(F);
+        static_assert(2 * S::NL * (F == kCodecMxfp4 ? 1 : 2) == 4, "one scale dword per chunk column");
+        b.sgu[0][c][0] = __builtin_amdgcn_raw_buffer_load_b32(r, p, 0, kLoadNonTemporal);
+    }
+}
+
+// A wave's N items with up to NB items' loads in flight: item k + NB is
+// issued once item k is computed, in straight-line code (compile-time buffer
+// choice keeps the compiler's load waits exact); nothing beyond the wave's
+// own items is loaded.
+template <int N, int NB, typename Issue, typename Compute, typename Buf>
+__device__ __forceinline__ void run_items(const Issue& issue, const Compute& compute, Buf (&b)[NB]) {
+#pragma unroll
+    for (int k = 0; k < (N < NB ? N : NB); ++k) issue(k, b[k]);
+#pragma unroll
+    for (int k = 0; k < N; ++k) {
+        compute(k, b[k % NB]);
+        if (k + NB < N) issue(k + NB, b[k % NB]);
+    }
+}
+
+// More items than the straight-line cases cover: two buffers in a loop;
+// the pair after the last is clamped by the caller's issue (loads repeated,
+// results not stored).
+template <int NB, typename Issue, typename Compute, typename Buf>
+__device__ __forceinline__ void run_items_loop(int n, const Issue& issue, const Compute& compute, Buf (&b)[NB]) {
+    static_assert(NB >= 2, "two buffers");
+    issue(0, b[0]);
+    issue(1, b[1]);
+#pragma unroll 1
+    for (int k = 0; k < n; k += 2) {
+        compute(k, b[0]);
+        issue(k + 2, b[0]);
+        compute(k + 1, b[1]);
+        issue(k + 3, b[1]);
+    }
+}
+
+constexpr int kFusedMaxSlots = 8;        // routed slots (top_k <= 8)
+constexpr int kFusedWavesPerSlot = 1;    // waves per routed slot (one wave per slot: two per SIMD at top_k 8)
+constexpr int kFusedItemsInFlight = 4;   // gate/up items per wave with loads in flight
+
+template <int KG, int KGI, int NLD, int EPL, int F, int NK>
+__global__ void __launch_bounds__(64 * kFusedWavesPerSlot * NK) fused_decode_kernel(DecodeArgs a, FusedArgs f) {
+    using SG = GateUpShape<KG>;
+    using SD = DownShape<KGI, NLD>;
+    using D = DownWork<KGI, NLD, F>;
+    const int lane = threadIdx.x & 63;
+    const int wave = wave_in_block();
+    constexpr int nw = kFusedWavesPerSlot * NK;  // waves per workgroup
+    const int G = gridDim.x;
+    const int b = blockIdx.x;
+    const int gw = wave * G + b;
+    const int NW = nw * G;
+    const BlobLayout L = blob_layout(a.H, a.I, F);
+    const int per_slot = a.I / row_pack(F) / SG::R;  // gate/up items per slot
+    const int n_shared = a.S > 0 ? per_slot : 0;
+    float* const h_shared = a.h + (size_t)a.K * a.I;
+
+    __shared__ const uint8_t* s_blob[16];  // routed slot -> blob (null: dropped)
+    __shared__ float s_w[16];
+    __shared__ int s_kept[17];             // kept routed slots: count, then slots ascending
+    __shared__ int s_fail;
+    __shared__ int s_next;                 // next unclaimed gate/up item of this workgroup
+    __shared__ float part[kFusedMaxSlots + 1][D::RP * SD::R];
+    __shared__ u32x4 xo[SG::CPL * 4 * kWave];  // activation operands, converted once per workgroup
+    __shared__ u32x2 xm[SG::CPL * kWave];
+    const LdsOperands xsrc{xo, xm, lane};
+
+    // ---- phase 0: a router row (waves with gw < E), shared gate/up items;
+    // the loads go out before the activation columns are converted into LDS
+    // (column c by wave nw - 1 - c mod nw: the last waves, which have no
+    // phase-0 unit when units are fewer than waves)
+    if (threadIdx.x == 0) {
+        s_fail = 0;
+        s_next = 0;
+    }
+    {
+        // A router-row wave and an item wave keep their loads in separate
+        // code paths (each with the workgroup's one barrier: a workgroup
+        // barrier counts every wave that reaches any barrier instruction), so
+        // the row's registers and the item's never overlap.
+        const int n_units = a.E + n_shared;
+        int u = gw;
+        if (u < a.E) {
+            RouterRow<KG> row;
+            row.issue(a, u, lane);
+            for (int c = nw - 1 - wave; c >= 0; c -= nw)
+                if (c < SG::CPL) convert_column_to_lds<KG, F>(a.x, lane, c, xo, xm);
+            __syncthreads();
+            row.finish(a, f, u, lane);
+            // further router rows (shapes with more rows than waves)
+            for (u += NW; u < a.E; u += NW) {
+                row.issue(a, u, lane);
+                row.finish(a, f, u, lane);
+            }
+        } else {
+            GateUpBuf<KG, F> buf;
+            if (u < n_units) gateup_issue<KG, F>(a.shared_blob, L, u - a.E, lane, buf);
+            for (int c = nw - 1 - wave; c >= 0; c -= nw)
+                if (c < SG::CPL) convert_column_to_lds<KG, F>(a.x, lane, c, xo, xm);
+            __syncthreads();
+            if (u < n_units) {
+                gateup_compute_src<KG, F, true>(buf, u - a.E, lane, xsrc, h_shared, a.I / 32, true);
+                u += NW;
+            }
+        }
+        // further shared items (shapes with more units than waves)
+        for (; u < n_units; u += NW) {
+            GateUpBuf<KG, F> buf;
+            gateup_issue<KG, F>(a.shared_blob, L, u - a.E, lane, buf);
+            gateup_compute_src<KG, F, true>(buf, u - a.E, lane, xsrc, h_shared, a.I / 32, true);
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's shared h stores are acknowledged
+
+    // ---- routing on wave 0
+    if (wave == 0) {
+        int id;
+        float w;
+        const uint8_t* blob;
+        if (!route_from_records<EPL>(a, f, lane, &id, &w, &blob) && lane == 0) s_fail = 1;
+        const bool chosen = lane < a.K && id >= 0;
+        const unsigned long long m = __ballot(chosen);
+        if (lane < 16) {
+            s_blob[lane] = lane < a.K ? blob : nullptr;
+            s_w[lane] = lane < a.K ? w : 0.0f;
+        }
+        if (chosen) s_kept[1 + __popcll(m & ((1ull << lane) - 1))] = lane;
+        if (lane == 0) s_kept[0] = __popcll(m);
+        if (b == 0 && lane < a.K) {
+            a.ids[lane] = id;
+            a.w[lane] = w;
+        }
+    }
+    __syncthreads();
+    // this workgroup's shared expert h values are all published
+    if (threadIdx.x == 0 && a.S > 0) count_up(f.shared_done, b);
+
+    // ---- phase 1: routed gate/up items
+    if constexpr (SG::RPL == 1 && code_planes(F) == 1 && row_pack(F) == 1) {
+        // items b, b + G, b + 2G, ... belong to this workgroup; its waves
+        // claim them one at a time from an LDS counter, so faster waves take
+        // more of them and all finish together
+        const int n_items = s_kept[0] * per_slot;
+        const int n_wg = b < n_items ? (n_items - 1 - b) / G + 1 : 0;
+        auto claim = [&]() {
+            int j = 0;
+            if (lane == 0) j = atomicAdd(&s_next, 1);
+            return __builtin_amdgcn_readfirstlane(j);
+        };
+        constexpr int NB = kFusedItemsInFlight;
+        GateUpBuf<KG, F> bufs[NB];
+        int item[NB];
+        auto issue = [&](int i) {
+            const int j = claim();
+            const bool live = j < n_wg;
+            item[i] = live ? b + j * G : -1;
+            const int it = live ? item[i] : 0;
+            const int slot = __builtin_amdgcn_readfirstlane(s_kept[1 + it / per_slot]);
+            gateup_issue_buf<KG, F>(readlane_ptr(s_blob[slot], 0), live, L, it % per_slot, lane, bufs[i]);
+        };
+#pragma unroll
+        for (int i = 0; i < NB; ++i) issue(i);
+        bool more = true;
+        while (more) {
+            more = false;
+#pragma unroll
+            for (int i = 0; i < NB; ++i) {
+                if (item[i] >= 0) {
+                    const int it = item[i];
+                    const int slot = __builtin_amdgcn_readfirstlane(s_kept[1 + it / per_slot]);
+                    gateup_compute_src<KG, F, true>(bufs[i], it % per_slot, lane, xsrc, a.h + (size_t)slot * a.I,
+                                                    a.I / 32, true);
+                    more = true;
+                }
+                issue(i);
+            }
+        }
+    } else {
+        const int n_items = s_kept[0] * per_slot;
+        const int n_mine = gw < n_items ? (n_items - 1 - gw) / NW + 1 : 0;
+        auto item_of = [&](int k) {
+            const int item = gw + k * NW;
+            return item < n_items ? item : n_items - 1;
+        };
+        // slot and blob of an item as wave-uniform values (scalar
+        // registers), so the loads take a scalar base and one lane offset
+        auto slot_of = [&](int it) { return __builtin_amdgcn_readfirstlane(s_kept[1 + it / per_slot]); };
+        auto issue = [&](int k, GateUpBuf<KG, F>& buf) {
+            const int it = item_of(k);
+            gateup_issue<KG, F>(readlane_ptr(s_blob[slot_of(it)], 0), L, it % per_slot, lane, buf);
+        };
+        auto compute = [&](int k, const GateUpBuf<KG, F>& buf) {
+            const int it = item_of(k);
+            gateup_compute_src<KG, F, true>(buf, it % per_slot, lane, xsrc, a.h + (size_t)slot_of(it) * a.I, a.I / 32,
+                                            k < n_mine);
+        };
+        constexpr int NB = kFusedItemsInFlight;
+        GateUpBuf<KG, F> bufs[NB];
+        switch (n_mine) {
+            case 0: break;
+            case 1: run_items<1, NB>(issue, compute, bufs); break;
+            case 2: run_items<2, NB>(issue, compute, bufs); break;
+            case 3: run_items<3, NB>(issue, compute, bufs); break;
+            case 4: run_items<4, NB>(issue, compute, bufs); break;
+            case 5: run_items<5, NB>(issue, compute, bufs); break;
+            case 6: run_items<6, NB>(issue, compute, bufs); break;
+            case 7: run_items<7, NB>(issue, compute, bufs); break;
+            case 8: run_items<8, NB>(issue, compute, bufs); break;
+            default: run_items_loop<NB>(n_mine, issue, compute, bufs); break;
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's h stores are acknowledged
+
+    // ---- phase 2: wave w takes the steps of routed slot w / P congruent to
+    // w mod P (P = kFusedWavesPerSlot) and the shared expert's steps
+    // congruent to w modulo the wave count, over row block b
+    const int slot = wave / kFusedWavesPerSlot;
+    const uint8_t* dblob = s_blob[slot];
+    DownSteps<KGI, NLD, F, kFusedWavesPerSlot> d;
+    if (dblob) d.issue(dblob, L, b, lane, wave % kFusedWavesPerSlot);
+    const int g0i = KGI >= kWave ? lane : (lane & (KGI - 1));
+    if (a.S > 0) {
+        // the shared expert's h was complete long ago (phase 0): its rows go
+        // before the wait for the routed experts' h
+        DownSteps<KGI, NLD, F, kFusedWavesPerSlot * NK> sh;
+        sh.issue(a.shared_blob, L, b, lane, wave);
+        if (!wait_count(f.shared_done, f.seq * (unsigned)G, f.spin_limit, lane) && lane == 0) s_fail = 1;
+        float hraw[SD::CPL][32];
+        load_h_device_scope<SD::CPL, KGI>(h_shared, g0i, hraw);
+        sh.finish(hraw, lane, wave, part[a.K]);
+    }
+    __syncthreads();
+    if (wave == 0) {
+        if (lane == 0) count_up(f.h_done, b);
+        if (!wait_count(f.h_done, f.seq * (unsigned)G, f.spin_limit, lane) && lane == 0) s_fail = 1;
+    }
+    __syncthreads();
+    if (dblob) {
+        float hraw[SD::CPL][32];
+        load_h_device_scope<SD::CPL, KGI>(a.h + (size_t)slot * a.I, g0i, hraw);
+        d.finish(hraw, lane, wave % kFusedWavesPerSlot, part[slot]);
+    } else if (wave % kFusedWavesPerSlot == 0) {
+        // a routed slot that the top-p cut dropped: weight 0, nothing read
+        for (int t = lane; t < D::RP * SD::R; t += kWave) part[slot][t] = 0.0f;
+    }
+    __syncthreads();
+    if ((int)threadIdx.x < D::RP * SD::R) {
+        const int t = threadIdx.x;
+        float y = 0.0f;
+        for (int j = 0; j < a.K; ++j) y = fmaf(s_w[j], part[j][t], y);
+        if (a.S > 0) y += part[a.K][t];
+        a.y[(size_t)D::RP * (b * SD::R + t % SD::R) + t / SD::R] = y;
+    }
+    if (threadIdx.x == 0 && s_fail) __hip_atomic_store(f.status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
 // ---------------------------------------------------------------- launchers
@@ -1062,6 +1699,30 @@ hipError_t launch_down(const DecodeArgs& a, hipStream_t st, const LaunchTiming& 
 }
 
 
+// Fused kernel instances: (hidden/32, inter/32, experts per router lane)
+// of the GLM-5.2-shaped layer and of the smaller parity shapes, int4
+// experts; other shapes and codecs take the three launches.
+template <int KG, int KGI, int EPL, int F, int NK>
+const void* fused_fn_shape() {
+    // the down step count down_rows gives at hidden = 32 KG
+    constexpr int NLD = down_rows(32 * KG, KGI, F) / rows_per_load(KGI);
+    return reinterpret_cast<const void*>(fused_decode_kernel<KG, KGI, NLD, EPL, F, NK>);
+}
+
+const void* fused_fn(const DecodeArgs& a) {
+    const int kg = a.H / 32, kgi = a.I / 32;
+    const int epl = a.E <= 64 ? 1 : (a.E <= 128 ? 2 : 4);
+    if (a.S > 1) return nullptr;
+    // int4 only: the instances are sized for its registers
+    if (a.codec != kCodecInt4) return nullptr;
+    if (kg == 192 && kgi == 64 && epl == 4 && a.K == 8) return fused_fn_shape<192, 64, 4, kCodecInt4, 8>();
+    if (kg == 8 && kgi == 4 && epl == 1 && a.K == 4) return fused_fn_shape<8, 4, 1, kCodecInt4, 4>();
+    if (kg == 32 && kgi == 8 && epl == 1 && a.K == 6) return fused_fn_shape<32, 8, 1, kCodecInt4, 6>();
+    if (kg == 128 && kgi == 32 && epl == 2 && a.K == 8) return fused_fn_shape<128, 32, 2, kCodecInt4, 8>();
+    if (kg == 16 && kgi == 4 && epl == 4 && a.K == 8) return fused_fn_shape<16, 4, 4, kCodecInt4, 8>();
+    return nullptr;
+}
+
 }  // namespace
 
 // Kernels are instantiated for H/32 in {8,16,32,64,128,192,256} and
@@ -1102,6 +1763,27 @@ hipError_t decode_down_combine(const DecodeArgs& a, hipStream_t st, const Launch
         case 128: return launch_down<128>(a, st, tm);
         default: return hipErrorInvalidValue;
     }
+}
+
+int fused_grid(const DecodeArgs& a, int* threads) {
+    if (!fused_fn(a)) return 0;
+    *threads = 64 * kFusedWavesPerSlot * a.K;
+    return a.H / row_pack(a.codec) / down_rows(a.H, a.I / 32, a.codec);
+}
+
+const void* fused_kernel_function(const DecodeArgs& a) { return fused_fn(a); }
+
+hipError_t decode_fused(const DecodeArgs& a, const FusedArgs& f, hipStream_t st, const LaunchTiming& tm) {
+    const void* fn = fused_fn(a);
+    int threads = 0;
+    const int grid = fused_grid(a, &threads);
+    if (!fn || grid == 0) return hipErrorInvalidValue;
+    DecodeArgs args = a;
+    FusedArgs fargs = f;
+    void* params[] = {&args, &fargs};
+    if (tm.start)
+        return hipExtLaunchKernel(fn, dim3(grid), dim3(threads), params, 0, st, tm.start, tm.stop, 0);
+    return hipLaunchKernel(fn, dim3(grid), dim3(threads), params, 0, st);
 }
 
 bool decode_shape_supported(int hidden, int inter, int top_k, int n_shared) {

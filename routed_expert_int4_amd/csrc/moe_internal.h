@@ -16,6 +16,7 @@ struct WorkspaceLayout {
     size_t table = 0;          // [E] device blob pointers of the routed experts
     size_t control = 0;        // control words (cleared when bound)
     size_t control_bytes = 0;
+    size_t sync = 0;           // counters of the fused launch (kSyncBytes, cleared when bound)
     size_t s = 0;              // [E] router affinities of the token in flight
     size_t sb = 0;             // [E] biased scores
     size_t xq = 0;             // activation operands of the token in flight
@@ -47,9 +48,17 @@ moe_status_t validate_supported(const moe_config_t* c);
 // The one-token decode path over T tokens with the per-call state at ws
 // (laid out as W): token t reads x[t], writes y[t] and its routing to
 // ids_base + t * ids_stride and w_base + t * w_stride.
+// fused_seq counts the fused launches made on ws since its control words
+// were cleared (the fused kernel's counters count up across calls).
 moe_status_t decode_tokens(moe_layer* L, uint8_t* ws, const WorkspaceLayout& W, const uint16_t* d_x, int T,
                            float* d_y, int32_t* ids_base, int ids_stride, float* w_base, int w_stride,
-                           hipStream_t s);
+                           unsigned* fused_seq, hipStream_t s);
+// MOE_EHIP if a fused launch of this layer reported a wait that gave up.
+moe_status_t check_layer_status(const moe_layer* L, const char* who);
+
+constexpr unsigned kDefaultSpinLimit = 1u << 20;  // polls, about a second
+// moe_layer_profile kinds: router, gate/up, down + combine, fused one-token launch
+constexpr int kProfileKinds = 4;
 
 }  // namespace moe
 
@@ -66,6 +75,13 @@ struct moe_layer {
     moe::WorkspaceLayout W;
     moe_cache* cache = nullptr;
     int cache_layer = -1;
+    // one-token calls: 3 = three launches (the default), 1 = one fused
+    // launch when its workgroups fit on the device at once (moe_layer_set_decode)
+    int decode_launches = 3;
+    unsigned spin_limit = moe::kDefaultSpinLimit;
+    int fused_fits = -1;           // occupancy check of the fused launch (-1: not yet made)
+    unsigned fused_seq = 0;        // fused launches on the bound workspace
+    unsigned* status = nullptr;    // host-visible word the fused kernel sets when a wait gives up
     // per-kernel event timing (moe_layer_profile)
     bool profiling = false;
     std::vector<hipEvent_t> prof_events;          // pool

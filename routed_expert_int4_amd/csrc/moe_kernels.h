@@ -53,6 +53,34 @@ struct LaunchTiming {
     hipEvent_t stop = nullptr;
 };
 
+// Control of the fused one-token decode launch (decode_fused), in the
+// workspace's sync region (cleared when a workspace is bound).  The router
+// rows publish s and sb as records (value bits, call number) that the
+// routing waves poll.  The counts of workgroups whose shared expert h, and
+// whose routed h, values are published are each spread over kSyncCounters words kSyncStride words apart (one cache line
+// each): workgroup b increments word b mod kSyncCounters, and a waiting wave
+// reads all of them at once and sums them (device-scope atomics on one
+// address are serialised where they execute, so hundreds of increments of
+// a single word would take microseconds).  Nothing is reset between calls:
+// the call with number seq (1, 2, ... since the workspace was bound) looks
+// for records carrying seq and waits for the sums seq * grid.  A wait that
+// does not succeed within spin_limit polls gives up, sets *status
+// (host-visible memory) to 1 and the launch finishes without blocking.
+constexpr int kSyncCounters = 32;
+constexpr int kSyncStride = 64;  // words (256 bytes)
+constexpr int kSyncMaxExperts = 256;
+constexpr size_t kSyncCounterBytes = kSyncCounters * kSyncStride * sizeof(unsigned);
+constexpr size_t kSyncBytes = 2 * kSyncCounterBytes + 2 * kSyncMaxExperts * sizeof(unsigned long long);
+struct FusedArgs {
+    unsigned* h_done;               // kSyncCounters words
+    unsigned* shared_done;          // kSyncCounters words: workgroups whose shared expert h is published
+    unsigned long long* s_rec;      // [E] records of s
+    unsigned long long* sb_rec;     // [E] records of sb
+    unsigned* status;               // set to 1 when a wait gives up
+    unsigned seq;
+    unsigned spin_limit;
+};
+
 // Router logits -> s, sb; group-limited top-k -> ids, w (and slot_blobs
 // from table when it is set); gate/up + SwiGLU of the shared expert;
 // activation pairs.
@@ -63,6 +91,15 @@ hipError_t decode_routed_gateup(const DecodeArgs& a, hipStream_t st, const Launc
 // Down projection of every slot and the weighted combine into y.
 hipError_t decode_down_combine(const DecodeArgs& a, hipStream_t st, const LaunchTiming& tm = {});
 bool decode_shape_supported(int hidden, int inter, int top_k, int n_shared);
+// The whole one-token layer in one launch of co-resident workgroups (router
+// and shared gate/up, the top-k, routed gate/up, down and combine, with the
+// hand-offs done in the kernel).  fused_grid returns the launch's workgroups
+// and threads per workgroup for this shape, or 0 when the fused kernel has
+// no instance for it; fused_kernel_function returns the kernel (for the
+// occupancy query).
+int fused_grid(const DecodeArgs& a, int* threads);
+const void* fused_kernel_function(const DecodeArgs& a);
+hipError_t decode_fused(const DecodeArgs& a, const FusedArgs& f, hipStream_t st, const LaunchTiming& tm = {});
 
 // ------------------------------------------------------------ batched path
 // Tokens per MFMA row block (the smallest tile) and rows per gate/up

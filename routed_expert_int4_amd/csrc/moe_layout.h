@@ -77,7 +77,7 @@ __host__ __device__ constexpr int pow2_at_least(int v) { return v <= 1 ? 1 : 2 *
 // (min(inter/32, 64)).  With two nibble planes (int8) every step loads
 // twice as many chunks; with two rows per stored row (int2) the rows are
 // stored rows (hidden / 2 of them) and every step yields two partials.
-__host__ __device__ inline int down_rows(int hidden, int kg_i, int codec) {
+__host__ __device__ constexpr int down_rows(int hidden, int kg_i, int codec) {
     const int planes = code_planes(codec), rp = row_pack(codec);
     const int vrows = hidden / rp;
     const int rpl = rows_per_load(kg_i);

@@ -25,7 +25,7 @@ namespace {
 
 // Largest per-call state the variant serves: the one-token decode layout of
 // the biggest supported shape (hidden 8192, intermediate 4096, 256 experts,
-// top-8 + 1 shared) needs about 170 KiB.
+// top-8 + 1 shared) needs about 186 KiB.
 constexpr size_t kScratchBytes = 256 * 1024;
 constexpr int kMaxDevices = 64;
 
@@ -37,13 +37,15 @@ struct TableArg {
     const uint8_t* p[256];
 };
 
-// Writes the layer's table into the array and clears the control words the
-// decode kernels expect to find at zero.
+// Writes the layer's table into the array and clears the control and sync
+// words the decode kernels expect to find at zero.
 __global__ void __launch_bounds__(256) noalloc_setup_kernel(TableArg t, int n, const uint8_t** table,
-                                                            unsigned* control, int n_control) {
+                                                            unsigned* control, int n_control, unsigned* sync,
+                                                            int n_sync) {
     const int i = threadIdx.x;
     if (i < n) table[i] = t.p[i];
     if (i < n_control) control[i] = 0u;
+    for (int k = i; k < n_sync; k += blockDim.x) sync[k] = 0u;
 }
 
 std::mutex g_mutex;
@@ -81,6 +83,8 @@ moe_status_t moe_layer_forward_noalloc(moe_layer_t* layer, const uint16_t* d_x, 
     if (!d_x || !d_y) return fail(MOE_EINVAL, "moe_layer_forward_noalloc: NULL x or y");
     if (layer->cache) return fail(MOE_EINVAL, "moe_layer_forward_noalloc: the layer uses an expert cache");
     if (!layer->experts_set) return fail(MOE_EINVAL, "moe_layer_forward_noalloc: no experts set");
+    moe_status_t st0 = check_layer_status(layer, "moe_layer_forward_noalloc");
+    if (st0 != MOE_OK) return st0;
     const moe_config_t& c = layer->cfg;
     if (c.n_experts > 256) return fail(MOE_EINVAL, "moe_layer_forward_noalloc: more than 256 experts");
     const WorkspaceLayout W = workspace_layout(&c, 1);
@@ -96,14 +100,17 @@ moe_status_t moe_layer_forward_noalloc(moe_layer_t* layer, const uint16_t* d_x, 
     for (int e = 0; e < c.n_experts; ++e) t.p[e] = layer->host_table[e];
     hipLaunchKernelGGL(noalloc_setup_kernel, dim3(1), dim3(256), 0, s, t, c.n_experts,
                        reinterpret_cast<const uint8_t**>(base + W.table), reinterpret_cast<unsigned*>(base + W.control),
-                       (int)(W.control_bytes / sizeof(unsigned)));
+                       (int)(W.control_bytes / sizeof(unsigned)), reinterpret_cast<unsigned*>(base + W.sync),
+                       (int)(kSyncBytes / sizeof(unsigned)));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(e, "moe_layer_forward_noalloc: setup launch");
     // routing outputs the caller does not want go to the array's one-token
     // slots, overwritten token after token
     int32_t* ids = d_ids ? d_ids : reinterpret_cast<int32_t*>(base + W.ids);
     float* w = d_w ? d_w : reinterpret_cast<float*>(base + W.w);
-    return decode_tokens(layer, base, W, d_x, T, d_y, ids, d_ids ? c.top_k : 0, w, d_w ? c.top_k : 0, s);
+    // the setup launch cleared the control words: fused launches count from 0
+    unsigned fused_seq = 0;
+    return decode_tokens(layer, base, W, d_x, T, d_y, ids, d_ids ? c.top_k : 0, w, d_w ? c.top_k : 0, &fused_seq, s);
 }
 
 }  // extern "C"

@@ -204,6 +204,53 @@ def test_lru_oracle_pinned_hand_worked():
     assert lru.hottest(lru.usage(tr, 5), 3) == [1, 0, 2]
 
 
+def test_lru_prefetch_oracle_hand_worked():
+    # Worked by hand: 3 slots, top-2 routing, at most 2 prefetch copies.
+    #   t0 [0,1], no prediction: 0 miss, 1 miss              LRU [0,1]
+    #   t1 predicted [2,4]: 2 in; 4 in evicts 0              LRU [1,2,4]
+    #      [2,3]: 2 hit (prefetched); 3 miss evicts 1         LRU [4,2,3]
+    #   t2 predicted [0,1]: 0 in evicts 4 (never used); 1 in evicts 2
+    #      [0,2]: 0 hit (prefetched); 2 miss evicts 3         LRU [1,0,2]
+    r = lru.replay_prefetch([[0, 1], [2, 3], [0, 2]], [None, [2, 4], [0, 1]], 3, max_prefetch=2)
+    assert r == dict(hits=2, misses=4, evictions=5, prefetches=4, prefetch_hits=2, predicted_uses=4,
+                     predicted_hits=2)
+    # a limit of one copy per token:
+    #   t1 predicted [2,4]: 2 in (free slot), 4 over the limit     LRU [0,1,2]
+    #      [2,3]: 2 hit (prefetched); 3 miss evicts 0               LRU [1,2,3]
+    #   t2 predicted [0,1]: 0 in evicts 2 (1 is predicted itself); 1 resident
+    #                                                               LRU [1,3,0]
+    #      [0,2]: 0 hit (prefetched); 2 miss evicts 1               LRU [3,0,2]
+    r = lru.replay_prefetch([[0, 1], [2, 3], [0, 2]], [None, [2, 4], [0, 1]], 3, max_prefetch=1)
+    assert r == dict(hits=2, misses=4, evictions=3, prefetches=2, prefetch_hits=2, predicted_uses=4,
+                     predicted_hits=2)
+
+
+@pytest.mark.parametrize("slots,n_pin", [(8, 0), (16, 0), (16, 6), (64, 56)])
+def test_lru_prefetch_oracle_reductions(slots, n_pin):
+    """No prediction, or a limit of zero copies, reduces to plain replay; a
+    perfect prediction leaves no miss; the counts stay consistent."""
+    rng = np.random.default_rng(slots + n_pin)
+    E, k = 256, 8
+    p = 1.0 / np.arange(1, E + 1) ** 1.1
+    p /= p.sum()
+    trace = np.array([rng.choice(E, k, replace=False, p=p) for _ in range(300)], np.int32)
+    pins = lru.hottest(lru.usage(trace[:100], E), n_pin)
+    base = lru.replay(trace, slots, pinned=pins)
+    none = lru.replay_prefetch(trace, [None] * len(trace), slots, pinned=pins)
+    assert (none["hits"], none["misses"], none["evictions"]) == base and none["prefetches"] == 0
+    guess = [rng.choice(E, k, replace=False, p=p) for _ in range(len(trace))]
+    zero = lru.replay_prefetch(trace, guess, slots, pinned=pins, max_prefetch=0)
+    assert (zero["hits"], zero["misses"], zero["evictions"]) == base and zero["prefetches"] == 0
+    perfect = lru.replay_prefetch(trace, trace, slots, pinned=pins)
+    assert perfect["misses"] == 0 and perfect["hits"] == trace.size
+    assert perfect["predicted_hits"] == perfect["predicted_uses"] == trace.size
+    r = lru.replay_prefetch(trace, guess, slots, pinned=pins, max_prefetch=4)
+    assert r["hits"] + r["misses"] == trace.size
+    assert r["prefetch_hits"] <= r["prefetches"] and r["predicted_hits"] <= r["predicted_uses"] == trace.size
+    overlap = sum(len(set(a) & set(b)) for a, b in zip(trace, guess))
+    assert r["predicted_hits"] == overlap
+
+
 @pytest.mark.parametrize("slots,skew", [(8, 0.0), (16, 1.1), (64, 1.1), (64, 0.0)])
 def test_cache_policy_matches_lru_replay(slots, skew):
     rng = np.random.default_rng(slots)

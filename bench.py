@@ -108,17 +108,16 @@ def measured_traffic():
     return int(rec["hbm_bytes_per_launch"])
 
 
-def cpu_baseline(weights, x_bits, n_tokens: int, bytes_per_token: int):
+def time_oracle(weights, sample):
+    """Tokens/s of the fp64 oracle's full layer over sample (bf16 bits) on
+    every host thread, and on one thread over a short prefix."""
     from oracle import oracle
     threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
-    sample = x_bits[:n_tokens]
     oracle.layer_forward(weights, sample[:1], n_threads=threads)  # load + warm
     t0 = time.perf_counter()
     oracle.layer_forward(weights, sample, n_threads=threads)
     dt = time.perf_counter() - t0
-    tps = n_tokens / dt
-    # one thread on a short prefix, for the per-core figure
-    n1 = max(1, min(16, n_tokens))
+    n1 = max(1, min(16, sample.shape[0]))
     t1 = time.perf_counter()
     oracle.layer_forward(weights, sample[:n1], n_threads=1)
     dt1 = time.perf_counter() - t1
@@ -128,16 +127,22 @@ def cpu_baseline(weights, x_bits, n_tokens: int, bytes_per_token: int):
             cpu_model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), "")
     except OSError:
         pass
+    return {"tokens_per_s": sample.shape[0] / dt, "seconds": dt, "cores": threads,
+            "tokens_per_s_1_thread": n1 / dt1, "cpu_model": cpu_model}
+
+
+def cpu_baseline(weights, x_bits, n_tokens: int, bytes_per_token: int):
+    r = time_oracle(weights, x_bits[:n_tokens])
     return {
-        "value": round(tps * bytes_per_token / 1e9, 4),
+        "value": round(r["tokens_per_s"] * bytes_per_token / 1e9, 4),
         "unit": "GB/s",
-        "tokens_per_s": round(tps, 3),
-        "cores": threads,
+        "tokens_per_s": round(r["tokens_per_s"], 3),
+        "cores": r["cores"],
         "kind": "oracle",
         "sample": f"first {n_tokens} of the 1000 tokens, full layer in fp64 (router, top-k, 8 routed + shared "
-                  f"experts, combine), {dt:.1f} s",
-        "tokens_per_s_1_thread": round(n1 / dt1, 3),
-        "cpu_model": cpu_model,
+                  f"experts, combine), {r['seconds']:.1f} s",
+        "tokens_per_s_1_thread": round(r["tokens_per_s_1_thread"], 3),
+        "cpu_model": r["cpu_model"],
     }
 
 
@@ -159,6 +164,12 @@ def main() -> int:
     ap.add_argument("--pin", type=int, default=-1,
                     help="cache-stack: experts pinned per layer by learned usage (-1: slots - top_k, 0: plain LRU)")
     ap.add_argument("--learn-tokens", type=int, default=128, help="cache-stack: tokens of the learning pass")
+    ap.add_argument("--max-prefetch", type=int, default=0,
+                    help="cache-stack: experts copied per call by the next-layer prefetch (0: top_k)")
+    ap.add_argument("--chain", default="noise", choices=["noise", "residual"],
+                    help="cache-stack: next layer input = bf16(y / rms(y) + N(0, 0.1)) (noise, the workload's "
+                         "chaining) or the RMS-normalised running sum of those terms and the first input "
+                         "(residual: a residual stream, which makes consecutive layers' inputs correlated)")
     ap.add_argument("--codec", default="int4", choices=["int4", "mxfp4", "int8", "int2"],
                     help="decode and cache-stack: expert weight codec (mxfp4: E2M1 codes, E8M0 scales; int8, "
                          "int2: one byte or 2 bits per weight, fp16 scales)")
@@ -197,7 +208,11 @@ def bench_cache_stack(args) -> int:
     start-up) and keeps the other slots as an LRU.  The timed run decodes
     --stack-tokens tokens (x0 seed 300, noise seed 400) with the LRU part
     empty.  The same tokens are then run again with plain LRU over all slots
-    from a cold start (reported as lru_only).  --pin 0 times plain LRU only."""
+    from a cold start.  Each configuration also runs with the speculative
+    next-layer prefetch (layer l + 1's router on layer l's input, at most
+    --max-prefetch copies per call), and each run records a copy/compute
+    timeline over its second half (fraction of the copy engine's busy time
+    during which a kernel ran).  --pin 0 times plain LRU only."""
     import numpy as np
     import torch
 
@@ -214,6 +229,7 @@ def bench_cache_stack(args) -> int:
         biases = [np.asarray(l["bias"], dtype=np.float32) for l in json.load(f)["layers"]]
     cache = ExpertCache(cfg, n_layers, slots)
     layers = []
+    w0 = None
     t0 = time.perf_counter()
     for l in range(n_layers):
         w = synth.gen_layer(cfg, seed=100 + l)
@@ -222,6 +238,8 @@ def bench_cache_stack(args) -> int:
         lay = DeviceLayer(w, max_T=1, resident=False)
         lay.attach_cache(cache, l)
         layers.append(lay)
+        if l == 0:
+            w0 = w  # kept for the CPU oracle's sample
         del w
         log(f"layer {l} ready ({time.perf_counter() - t0:.0f} s)")
     H = cfg.hidden
@@ -230,8 +248,9 @@ def bench_cache_stack(args) -> int:
     w = torch.empty((1, cfg.top_k), dtype=torch.float32, device="cuda:0")
     stream = torch.cuda.current_stream()
 
-    def decode(x_seed, noise_seed, n):
-        """n sequential tokens through the stack; returns (ms, stats at n/2)."""
+    def decode(x_seed, noise_seed, n, timeline_from=None):
+        """n sequential tokens through the stack; returns (ms, stats at n/2,
+        copy/compute timeline from token timeline_from on, or None)."""
         x0 = DeviceLayer.to_device_bf16(synth.gen_tokens(cfg, n, seed=x_seed))
         noise = torch.from_numpy(synth.gen_noise(cfg, n * n_layers, seed=noise_seed, std=0.1)).to("cuda:0")
         half = None
@@ -241,34 +260,37 @@ def bench_cache_stack(args) -> int:
         for t in range(n):
             if t == n // 2:
                 half = [cache.stats(l) for l in range(n_layers)]
+            if t == timeline_from:
+                cache.timeline(True)
             x = x0[t:t + 1]
+            r = x.float() if args.chain == "residual" else None
             for l in range(n_layers):
                 B.moe_layer_forward(layers[l].handle, x, 1, y, ids, w, stream)
                 rms = torch.sqrt(torch.mean(y * y, dim=1, keepdim=True))
-                x = (y / rms + noise[t * n_layers + l:t * n_layers + l + 1]).to(torch.bfloat16)
+                z = y / rms + noise[t * n_layers + l:t * n_layers + l + 1]
+                if args.chain == "residual":
+                    # a residual stream: the layer's normalised output is added
+                    # to the running sum, whose RMS-normalised value is the next input
+                    r = r + z
+                    z = r / torch.sqrt(torch.mean(r * r, dim=1, keepdim=True))
+                x = z.to(torch.bfloat16)
         e1.record(stream)
         torch.cuda.synchronize()
-        return e0.elapsed_time(e1), half
+        tl = None
+        if timeline_from is not None:
+            tl = cache.timeline_read()
+            cache.timeline(False)
+        return e0.elapsed_time(e1), half, tl
+
+    keys = ("hits", "misses", "h2d_bytes", "prefetches", "prefetch_hits", "predicted_uses", "predicted_hits")
 
     def totals(stats):
-        return {k: sum(st[k] for st in stats) for k in ("hits", "misses", "h2d_bytes")}
+        return {k: sum(st[k] for st in stats) for k in keys}
 
-    def measured(label):
-        before = totals([cache.stats(l) for l in range(n_layers)])
-        log(f"{label}: decoding {n_tok} tokens through {n_layers} cached layers")
-        ms, half = decode(300, 400, n_tok)
-        after = totals([cache.stats(l) for l in range(n_layers)])
-        mid = totals(half)
-        d = {k: after[k] - before[k] for k in after}
-        d2 = {k: after[k] - mid[k] for k in after}
-        r = {"tokens_per_s": n_tok / (ms / 1e3), "ms": ms, "routed_uses_per_token_layer":
-             (d["hits"] + d["misses"]) / (n_tok * n_layers),
-             "hit_rate": d["hits"] / max(d["hits"] + d["misses"], 1),
-             "hit_rate_second_half": d2["hits"] / max(d2["hits"] + d2["misses"], 1),
-             "h2d_bytes": d["h2d_bytes"], "h2d_gbs": d["h2d_bytes"] / (ms / 1e3) / 1e9}
-        log(f"{label}: {r['tokens_per_s']:.1f} tokens/s, hit rate {r['hit_rate']:.4f}, "
-            f"H2D {r['h2d_bytes'] / 1e9:.1f} GB at {r['h2d_gbs']:.1f} GB/s")
-        return r
+    def link(on):
+        """Speculative next-layer prefetch: layer l predicts layer l + 1."""
+        for l in range(n_layers - 1):
+            layers[l].set_next(layers[l + 1] if on else None, args.max_prefetch)
 
     def empty_cache():
         for l in range(n_layers):
@@ -276,21 +298,88 @@ def bench_cache_stack(args) -> int:
             for e in range(cfg.n_experts):
                 cache.evict(l, e)
 
-    pinned = None
+    def reset(pins):
+        """Empty slots, then the pinned experts loaded (as at start-up)."""
+        empty_cache()
+        p0 = time.perf_counter()
+        if pins is not None:
+            for l in range(n_layers):
+                cache.pin(l, pins[l])
+        torch.cuda.synchronize()
+        return time.perf_counter() - p0
+
+    def measured(label, prefetch, pins):
+        """One timed run from the reset state, then a replica of it (same
+        state, seeds and therefore the same cache decisions) with the
+        copy/compute timeline recorded over its second half (its event
+        stamps are kept out of the timed run)."""
+        reset(pins)
+        before = totals([cache.stats(l) for l in range(n_layers)])
+        link(prefetch)
+        log(f"{label}: decoding {n_tok} tokens through {n_layers} cached layers")
+        ms, half, _ = decode(300, 400, n_tok)
+        after = totals([cache.stats(l) for l in range(n_layers)])
+        reset(pins)
+        _, _, tl = decode(300, 400, n_tok, timeline_from=n_tok // 2)
+        link(False)
+        mid = totals(half)
+        d = {k: after[k] - before[k] for k in after}
+        d2 = {k: after[k] - mid[k] for k in after}
+        r = {"tokens_per_s": n_tok / (ms / 1e3), "ms": ms, "routed_uses_per_token_layer":
+             (d["hits"] + d["misses"]) / (n_tok * n_layers),
+             "hit_rate": d["hits"] / max(d["hits"] + d["misses"], 1),
+             "hit_rate_second_half": d2["hits"] / max(d2["hits"] + d2["misses"], 1),
+             "h2d_bytes": d["h2d_bytes"], "h2d_gbs": d["h2d_bytes"] / (ms / 1e3) / 1e9,
+             "misses": d["misses"], "prefetches": d["prefetches"], "prefetch_hits": d["prefetch_hits"],
+             "prediction_accuracy": d["predicted_hits"] / d["predicted_uses"] if d["predicted_uses"] else None,
+             "timeline_second_half": {
+                 "copy_ms": tl["copy_ms"], "kernel_ms": tl["kernel_ms"], "overlap_ms": tl["overlap_ms"],
+                 "span_ms": tl["span_ms"], "copies": tl["copies"], "kernels": tl["kernels"],
+                 "truncated": tl["truncated"],
+                 "copy_busy_frac": tl["copy_ms"] / tl["span_ms"] if tl["span_ms"] else None,
+                 "copy_overlapped_frac": tl["overlap_ms"] / tl["copy_ms"] if tl["copy_ms"] else None}}
+        acc = r["prediction_accuracy"]
+        log(f"{label}: {r['tokens_per_s']:.1f} tokens/s, hit rate {r['hit_rate']:.4f}, "
+            f"H2D {r['h2d_bytes'] / 1e9:.1f} GB at {r['h2d_gbs']:.1f} GB/s, prefetches {d['prefetches']} "
+            f"(used {d['prefetch_hits']}), prediction accuracy {acc if acc is None else round(acc, 4)}, "
+            f"copy busy {r['timeline_second_half']['copy_busy_frac']}, "
+            f"overlapped {r['timeline_second_half']['copy_overlapped_frac']}")
+        return r
+
+    runs = {}
     pin_load_s = 0.0
     if n_pin > 0:
         log(f"learning pass: {args.learn_tokens} tokens")
         decode(310, 410, args.learn_tokens)
-        empty_cache()
-        p0 = time.perf_counter()
-        for l in range(n_layers):
-            cache.autopin(l, n_pin)
-        torch.cuda.synchronize()
-        pin_load_s = time.perf_counter() - p0
-        pinned = measured(f"autopin {n_pin}")
-        empty_cache()
-    lru_only = measured("plain LRU")
-    main_run = pinned if pinned else lru_only
+        # the n most used experts of each layer, ties to the lower index,
+        # fixed now so that every run pins the same ones
+        hot = [list(np.argsort(-cache.usage(l).astype(np.int64), kind="stable")[:n_pin]) for l in range(n_layers)]
+        pin_load_s = reset(hot)
+        for prefetch in (False, True):
+            runs[("pinned", prefetch)] = measured(f"pinned {n_pin}" + (" + prefetch" if prefetch else ""),
+                                                  prefetch, hot)
+    for prefetch in (False, True):
+        runs[("lru", prefetch)] = measured("plain LRU" + (" + prefetch" if prefetch else ""), prefetch, None)
+    main_key = ("pinned", False) if n_pin > 0 else ("lru", False)
+    main_run = runs[main_key]
+    cpu = None
+    if args.cpu_sample > 0:
+        n = min(args.cpu_sample, 128)
+        log(f"timing the CPU oracle on layer 0 for {n} tokens")
+        r = time_oracle(w0, synth.gen_tokens(cfg, n, seed=300))
+        cpu = {"value": round(r["tokens_per_s"] / n_layers, 4), "unit": "tokens/s",
+               "tokens_per_s_one_layer": round(r["tokens_per_s"], 3), "cores": r["cores"], "kind": "oracle",
+               "sample": f"layer 0 of the stack on the first {n} stack inputs (x0 seed 300), full layer in fp64 "
+                         f"with every expert in host memory (no cache, no copies), {r['seconds']:.1f} s; "
+                         f"through the stack = one layer's rate / {n_layers}",
+               "tokens_per_s_1_thread": round(r["tokens_per_s_1_thread"] / n_layers, 4), "cpu_model": r["cpu_model"]}
+        log(f"oracle: {cpu['value']} stack tokens/s on {cpu['cores']} threads")
+
+    def rounded(r):
+        return {k: (round(v, 4) if isinstance(v, float) else
+                    ({kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
+                     if isinstance(v, dict) else v)) for k, v in r.items()}
+
     out = {
         "metric": "MoE-layer tokens/s through a 12-layer stack behind the HBM expert cache",
         "value": round(main_run["tokens_per_s"], 3),
@@ -308,7 +397,9 @@ def bench_cache_stack(args) -> int:
         "config": {"workload": f"12 GLM-5.2-shaped MoE layers, {n_tok} sequential decode tokens, 64 HBM slots "
                                f"per layer ({n_pin} pinned by learned usage, the rest LRU), pinned host expert "
                                "store" + (f", adaptive expert top-p {cfg.top_p}" if cfg.top_p < 1.0 else "")
-                               + (f", {cfg.codec} experts" if cfg.codec != "int4" else ""),
+                               + (f", {cfg.codec} experts" if cfg.codec != "int4" else "")
+                               + (", residual-stream chaining" if args.chain == "residual" else ""),
+                   "chain": args.chain, "max_prefetch": args.max_prefetch or cfg.top_k,
                    "layers": n_layers, "slots_per_layer": slots, "pinned_per_layer": n_pin,
                    "learning_tokens": args.learn_tokens if n_pin > 0 else 0, "tokens": n_tok},
         "hit_rate": round(main_run["hit_rate"], 4),
@@ -316,11 +407,12 @@ def bench_cache_stack(args) -> int:
         "h2d_gbytes": round(main_run["h2d_bytes"] / 1e9, 3),
         "h2d_gbs": round(main_run["h2d_gbs"], 2),
         "pin_load_s": round(pin_load_s, 3),
-        "lru_only": {k: round(v, 4) for k, v in lru_only.items()},
+        "timeline_second_half": rounded(main_run["timeline_second_half"]),
+        "runs": {f"{kind}{'_prefetch' if pf else ''}": rounded(r) for (kind, pf), r in runs.items()},
         "roofline": {"kernel": "host-to-device expert copies (hipMemcpyAsync, pinned host)", "bound": "pcie",
                      "achieved": round(main_run["h2d_gbs"], 2), "peak": 64.0, "unit": "GB/s",
                      "frac": round(main_run["h2d_gbs"] / 64.0, 4), "traffic": None},
-        "cpu_baseline": None,
+        "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
     for lay in layers:
@@ -469,16 +561,45 @@ def bench_batched(args) -> int:
     tokens_per_s = n_calls * T * args.steps / (ms_per_step * args.steps / 1e3)
     gbs = bytes_step / (ms_per_step / 1e3) / 1e9
     tflops = flops_step / (ms_per_step / 1e3) / 1e12
-    # per-stage durations (events around each stage of each call)
+    # per-stage spans, and the two grouped kernels stamped with their own
+    # begin and end (HIP events on the launch stream), over one more step
     B.moe_layer_profile(layer.handle, True)
     step()
     torch.cuda.synchronize()
     kms, kn = B.moe_layer_profile_read(layer.handle)
     B.moe_layer_profile(layer.handle, False)
     stage_ms = [kms[i] for i in range(3)]
-    grouped_ms = stage_ms[1] + stage_ms[2]
+    gu_ms, dn_ms = kms[4], kms[5]
+    # algorithmic bytes of the two grouped kernels per step: the distinct
+    # routed experts' and the shared expert's weights once per call, plus the
+    # activations they read and the results they write
+    sb = cfg.scale_bytes
+    cb = H * cfg.inter // cfg.codes_per_byte
+    gu_w = 2 * (cb + cfg.inter * (H // 32) * sb)
+    dn_w = cb + H * (cfg.inter // 32) * sb
+    pairs_step = kept_entries + n_calls * T * cfg.n_shared
+    gu_bytes = sum((d + cfg.n_shared) * gu_w for d in distinct) + n_calls * T * H * 2 + pairs_step * cfg.inter * 4
+    dn_bytes = sum((d + cfg.n_shared) * dn_w for d in distinct) + pairs_step * cfg.inter * 4 + pairs_step * H * 4
+    gu_gbs = gu_bytes / (gu_ms / 1e3) / 1e9
+    dn_gbs = dn_bytes / (dn_ms / 1e3) / 1e9
+    gu_tf = pairs_step * 2 * 2 * H * cfg.inter / (gu_ms / 1e3) / 1e12
+    dn_tf = pairs_step * 2 * H * cfg.inter / (dn_ms / 1e3) / 1e12
     log(f"{ms_per_step:.3f} ms/step, {tokens_per_s:.0f} tokens/s, {gbs:.0f} GB/s, {tflops:.1f} TFLOP/s; "
-        f"stages ms {stage_ms}; distinct experts per call {min(distinct)}..{max(distinct)}")
+        f"stages ms {stage_ms}; grouped gate/up {1e3 * gu_ms / kn[4]:.1f} us x {kn[4]} ({gu_gbs:.0f} GB/s), "
+        f"down {1e3 * dn_ms / kn[5]:.1f} us x {kn[5]} ({dn_gbs:.0f} GB/s); distinct experts per call "
+        f"{min(distinct)}..{max(distinct)}")
+    cpu = None
+    if args.cpu_sample > 0:
+        n = min(args.cpu_sample, 256)
+        log(f"timing the CPU oracle on {n} tokens")
+        r = time_oracle(weights, x_bits[:n])
+        cpu = {"value": round(r["tokens_per_s"] * bytes_step / (n_calls * T) / 1e9, 4), "unit": "GB/s",
+               "tokens_per_s": round(r["tokens_per_s"], 3), "cores": r["cores"], "kind": "oracle",
+               "sample": f"first {n} tokens of the step, full layer in fp64 token by token (the oracle reads each "
+                         f"token's experts itself), {r['seconds']:.1f} s; GB/s = tokens/s x the step's "
+                         "algorithmic bytes per token",
+               "tokens_per_s_1_thread": round(r["tokens_per_s_1_thread"], 3), "cpu_model": r["cpu_model"]}
+        log(f"oracle: {cpu['tokens_per_s']} tokens/s on {cpu['cores']} threads")
     out = {
         "metric": f"MoE-layer tokens/s and HBM GB/s, batched {cfg.codec} calls",
         "value": round(gbs, 2),
@@ -493,8 +614,9 @@ def bench_batched(args) -> int:
         "dtype": f"{cfg.codec} weights x fp16 activations (MFMA), fp32 accumulate",
         "data": f"synthetic (seeded: weights seed 0, tokens seed {seed})",
         "config": {"workload": workload + (f", {cfg.codec} experts" if cfg.codec != "int4" else "")
-                   + (f", adaptive expert top-p {cfg.top_p}" if cfg.top_p < 1.0 else ""), "tokens_per_call": T, "calls_per_step": n_calls, "hidden": H,
-                   "expert_intermediate": cfg.inter, "routed_experts": cfg.n_experts, "top_k": k},
+                   + (f", adaptive expert top-p {cfg.top_p}" if cfg.top_p < 1.0 else ""), "tokens_per_call": T,
+                   "calls_per_step": n_calls, "hidden": H, "expert_intermediate": cfg.inter,
+                   "routed_experts": cfg.n_experts, "top_k": k},
         "tokens_per_s": round(tokens_per_s, 1),
         "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "distinct_experts_per_call": {"min": min(distinct), "max": max(distinct),
@@ -502,18 +624,26 @@ def bench_batched(args) -> int:
         "tflops": round(tflops, 2),
         "stage_ms_per_step": {"routing_dispatch": round(stage_ms[0], 4), "gateup_hprep": round(stage_ms[1], 4),
                               "down_combine": round(stage_ms[2], 4)},
+        "grouped_kernels": {
+            "gateup": {"avg_launch_us": round(1e3 * gu_ms / kn[4], 3), "launches_per_step": kn[4],
+                       "bytes_per_step": gu_bytes, "gbs": round(gu_gbs, 1), "tflops": round(gu_tf, 2)},
+            "down": {"avg_launch_us": round(1e3 * dn_ms / kn[5], 3), "launches_per_step": kn[5],
+                     "bytes_per_step": dn_bytes, "gbs": round(dn_gbs, 1), "tflops": round(dn_tf, 2)},
+        },
         "roofline": {
-            "kernel": "grouped gate/up + down (batch_gateup_kernel, batch_down_kernel)",
+            "kernel": "grouped gate/up + SwiGLU (batch_gateup_kernel)",
             "bound": "hbm",
-            "achieved": round(bytes_step / (grouped_ms / 1e3) / 1e9, 1),
+            "achieved": round(gu_gbs, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
-            "frac": round(bytes_step / (grouped_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+            "frac": round(gu_gbs / HBM_PEAK_GBS, 4),
             "traffic": None,
-            "mfma_tflops": round(flops_step / (grouped_ms / 1e3) / 1e12, 2),
-            "mfma_frac_of_fp16_dense_peak": round(flops_step / (grouped_ms / 1e3) / 1e12 / 2500.0, 4),
+            "bytes_per_launch": int(round(gu_bytes / kn[4])),
+            "avg_launch_us": round(1e3 * gu_ms / kn[4], 3),
+            "mfma_tflops": round(gu_tf, 2),
+            "mfma_frac_of_fp16_dense_peak": round(gu_tf / 2500.0, 4),
         },
-        "cpu_baseline": None,
+        "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
     layer.close()

@@ -260,12 +260,17 @@ moe_status_t moe_layer_set_decode(moe_layer_t* layer, int launches, unsigned spi
  * (hipExtLaunchKernelGGL), except for the gate/up step of a layer with an
  * attached cache, whose events span the top-k launch, the wait for the
  * routing, the copies' ordering and the gate/up launches.
+ * T > 1 calls on the batched kernels record kinds 0-2 as spans of their
+ * stages and stamp the two grouped kernels themselves as kinds 4 and 5.
  * moe_layer_profile_read synchronises on the recorded events and returns,
- * per kernel kind (0 router, 1 gate/up + SwiGLU of the shared and routed
- * experts, 2 down + combine, 3 fused one-token launch), the summed duration
- * in milliseconds and the number of launches since profiling was enabled;
- * arrays of 4 entries.  Timings taken with profiling enabled are per-kernel
- * durations, not end-to-end throughput. */
+ * per kind (0 router, or the batched routing + dispatch; 1 gate/up + SwiGLU
+ * of the shared and routed experts, or the batched grouped gate/up + h
+ * preparation; 2 down + combine, or the batched grouped down + combine; 3
+ * fused one-token launch; 4 batched grouped gate/up kernel; 5 batched
+ * grouped down kernel), the summed duration in milliseconds and the number
+ * of launches since profiling was enabled; arrays of 6 entries.  Timings
+ * taken with profiling enabled are per-kernel durations, not end-to-end
+ * throughput. */
 moe_status_t moe_layer_profile(moe_layer_t* layer, int enable);
 moe_status_t moe_layer_profile_read(moe_layer_t* layer, double* total_ms, uint64_t* launches);
 
@@ -292,8 +297,11 @@ typedef struct {
     uint64_t misses;
     uint64_t h2d_bytes;
     uint64_t evictions;
-    uint64_t prefetches;  /* experts copied by prefetch or pin */
-    uint64_t pinned;      /* experts pinned now */
+    uint64_t prefetches;      /* experts copied by prefetch or pin */
+    uint64_t pinned;          /* experts pinned now */
+    uint64_t prefetch_hits;   /* routed uses that found an expert a prefetch brought in, unused since */
+    uint64_t predicted_uses;  /* routed uses of tokens for which the previous layer predicted this layer */
+    uint64_t predicted_hits;  /* of those, uses whose expert was in the prediction */
 } moe_cache_stats_t;
 
 moe_status_t expert_cache_create(const moe_config_t* cfg, int n_layers, int slots_per_layer, void* d_slot_pool,
@@ -335,6 +343,61 @@ moe_status_t expert_cache_autopin(moe_cache_t* cache, int layer, int n);
 moe_status_t expert_cache_replay(int n_experts, int slots, int top_k, const int32_t* trace, int n_tokens,
                                  const int32_t* pinned, int n_pinned, uint64_t* hits, uint64_t* misses,
                                  uint64_t* evictions);
+
+/* Speculative next-layer prefetch (the expert readahead of the colibri
+ * summary, "Principales fonctionnalites implementees": the next expert block
+ * is fetched while the current one is being multiplied; the pages name no
+ * predictor, and the one used here is the next layer's own router applied
+ * to the current layer's input).
+ * moe_layer_set_next: with next != NULL, every one-token call of `layer`
+ * (both attached to the same expert cache, next with a bound workspace) also
+ * runs next's router and top-k on this call's input, on the call's stream
+ * right after this layer's router (no shared expert work, next's workspace as
+ * scratch), reads the prediction back in the same host wait as this layer's
+ * routing, and once this layer's own misses are queued, copies the predicted
+ * experts of next that are not resident, in routing order, at most
+ * max_prefetch of them (0: top_k), on the cache's copy stream.  The slot
+ * choice of such a copy is a miss's, except that no predicted expert is
+ * evicted for another.  next's following call counts predicted_uses /
+ * predicted_hits and prefetch_hits.  next = NULL turns prediction off.
+ * MOE_EINVAL if either layer has no cache, they use different caches, next
+ * is layer itself, or next has no workspace or one that overlaps layer's
+ * (checked again at each call).  The link is not owned: unlink (next = NULL)
+ * before destroying next. */
+moe_status_t moe_layer_set_next(moe_layer_t* layer, moe_layer_t* next, int max_prefetch);
+
+/* expert_cache_replay_prefetch: expert_cache_replay with the prefetch above
+ * before each token's lookup: predicted [n_tokens][top_k] holds token t's
+ * prediction for this layer (a row of -1 only: no prediction for t; other
+ * -1 entries are skipped), max_prefetch as in moe_layer_set_next (0:
+ * top_k).  counts [7] receives hits, misses, evictions, prefetches,
+ * prefetch_hits, predicted_uses, predicted_hits. */
+moe_status_t expert_cache_replay_prefetch(int n_experts, int slots, int top_k, const int32_t* trace,
+                                          const int32_t* predicted, int n_tokens, int max_prefetch,
+                                          const int32_t* pinned, int n_pinned, uint64_t* counts);
+
+/* Copy/compute overlap timeline of a cache.  expert_cache_timeline: with
+ * enable != 0, every expert copy the cache makes (misses, prefetches, pins)
+ * is bracketed by timing events on the copy stream, and every kernel that a
+ * layer attached to the cache launches for a one-token call is stamped with
+ * its own begin and end (unless moe_layer_profile already times it), up to
+ * max_marks intervals (0: 65536; later ones are not recorded and
+ * `truncated` is set); enabling clears the recorded intervals.
+ * expert_cache_timeline_read synchronises on the recorded events, measures
+ * the union of the copy intervals, the union of the kernel intervals and
+ * their intersection (time during which a copy and a kernel both ran) over
+ * the recorded window, and clears the intervals. */
+typedef struct {
+    double copy_ms;      /* union of the copy intervals */
+    double kernel_ms;    /* union of the kernel intervals */
+    double overlap_ms;   /* time with a copy and a kernel in flight */
+    double span_ms;      /* first recorded begin to last recorded end */
+    uint64_t copies;
+    uint64_t kernels;
+    int truncated;
+} moe_cache_timeline_t;
+moe_status_t expert_cache_timeline(moe_cache_t* cache, int enable, int max_marks);
+moe_status_t expert_cache_timeline_read(moe_cache_t* cache, moe_cache_timeline_t* out);
 
 #ifdef __cplusplus
 }

@@ -38,7 +38,15 @@ class MoeConfig(ctypes.Structure):
 
 class MoeCacheStats(ctypes.Structure):
     _fields_ = [("hits", ctypes.c_uint64), ("misses", ctypes.c_uint64), ("h2d_bytes", ctypes.c_uint64),
-                ("evictions", ctypes.c_uint64), ("prefetches", ctypes.c_uint64), ("pinned", ctypes.c_uint64)]
+                ("evictions", ctypes.c_uint64), ("prefetches", ctypes.c_uint64), ("pinned", ctypes.c_uint64),
+                ("prefetch_hits", ctypes.c_uint64), ("predicted_uses", ctypes.c_uint64),
+                ("predicted_hits", ctypes.c_uint64)]
+
+
+class MoeCacheTimeline(ctypes.Structure):
+    _fields_ = [("copy_ms", ctypes.c_double), ("kernel_ms", ctypes.c_double), ("overlap_ms", ctypes.c_double),
+                ("span_ms", ctypes.c_double), ("copies", ctypes.c_uint64), ("kernels", ctypes.c_uint64),
+                ("truncated", ctypes.c_int)]
 
 
 MOE_CODEC_INT4, MOE_CODEC_MXFP4, MOE_CODEC_INT8, MOE_CODEC_INT2 = 0, 1, 2, 3
@@ -83,6 +91,10 @@ _SIGNATURES = {
     "expert_cache_autopin": ([_vp, _i, _i], _i),
     "expert_cache_replay": ([_i, _i, _i, _vp, _i, _vp, _i, ctypes.POINTER(ctypes.c_uint64),
                              ctypes.POINTER(ctypes.c_uint64), ctypes.POINTER(ctypes.c_uint64)], _i),
+    "moe_layer_set_next": ([_vp, _vp, _i], _i),
+    "expert_cache_replay_prefetch": ([_i, _i, _i, _vp, _vp, _i, _i, _vp, _i, ctypes.POINTER(ctypes.c_uint64)], _i),
+    "expert_cache_timeline": ([_vp, _i, _i], _i),
+    "expert_cache_timeline_read": ([_vp, ctypes.POINTER(MoeCacheTimeline)], _i),
 }
 
 
@@ -203,9 +215,10 @@ def moe_layer_set_decode(layer: int, launches: int, spin_limit: int = 0) -> None
 
 
 def moe_layer_profile_read(layer: int):
-    """-> (total_ms[4], launches[4]) for router, gate/up + SwiGLU, down + combine, fused one-token launch."""
-    ms = (ctypes.c_double * 4)()
-    n = (ctypes.c_uint64 * 4)()
+    """-> (total_ms[6], launches[6]) for router, gate/up + SwiGLU, down + combine, fused one-token launch,
+    batched grouped gate/up kernel, batched grouped down kernel."""
+    ms = (ctypes.c_double * 6)()
+    n = (ctypes.c_uint64 * 6)()
     check(lib().moe_layer_profile_read(layer, ms, n))
     return [float(v) for v in ms], [int(v) for v in n]
 
@@ -273,3 +286,34 @@ def expert_cache_replay(n_experts: int, slots: int, top_k: int, trace: np.ndarra
                                     p.ctypes.data if p.size else None, int(p.size), ctypes.byref(h), ctypes.byref(m),
                                     ctypes.byref(e)))
     return int(h.value), int(m.value), int(e.value)
+
+
+def moe_layer_set_next(layer: int, next_layer, max_prefetch: int = 0) -> None:
+    check(lib().moe_layer_set_next(layer, next_layer, int(max_prefetch)))
+
+
+REPLAY_PREFETCH_KEYS = ("hits", "misses", "evictions", "prefetches", "prefetch_hits", "predicted_uses",
+                        "predicted_hits")
+
+
+def expert_cache_replay_prefetch(n_experts: int, slots: int, top_k: int, trace: np.ndarray, predicted: np.ndarray,
+                                 max_prefetch: int = 0, pinned=()) -> dict:
+    t = np.ascontiguousarray(trace, dtype=np.int32)
+    q = np.ascontiguousarray(predicted, dtype=np.int32)
+    assert t.shape == q.shape
+    p = np.ascontiguousarray(np.asarray(pinned, dtype=np.int32))
+    out = (ctypes.c_uint64 * 7)()
+    check(lib().expert_cache_replay_prefetch(int(n_experts), int(slots), int(top_k), t.ctypes.data, q.ctypes.data,
+                                             int(t.shape[0]), int(max_prefetch), p.ctypes.data if p.size else None,
+                                             int(p.size), out))
+    return {k: int(out[i]) for i, k in enumerate(REPLAY_PREFETCH_KEYS)}
+
+
+def expert_cache_timeline(cache: int, enable: bool, max_marks: int = 0) -> None:
+    check(lib().expert_cache_timeline(cache, int(bool(enable)), int(max_marks)))
+
+
+def expert_cache_timeline_read(cache: int) -> dict:
+    t = MoeCacheTimeline()
+    check(lib().expert_cache_timeline_read(cache, ctypes.byref(t)))
+    return {k: (float(getattr(t, k)) if k.endswith("_ms") else int(getattr(t, k))) for k, _ in MoeCacheTimeline._fields_}

@@ -566,12 +566,18 @@ moe_status_t moe_layer_forward(moe_layer_t* layer, const uint16_t* d_x, int T, f
             if (e != hipSuccess) return hip_fail(e, "batched routing launch");
             p0.end();
             ProfileScope p1(layer, 1, s, ProfileScope::kSpan);
-            e = batch_gateup(b, s);
+            {
+                ProfileScope k4(layer, 4, s, ProfileScope::kKernel);
+                e = batch_gateup(b, s, k4.timing());
+            }
             if (e == hipSuccess) e = batch_hprep(b, s);
             if (e != hipSuccess) return hip_fail(e, "batched gate/up launch");
             p1.end();
             ProfileScope p2(layer, 2, s, ProfileScope::kSpan);
-            e = batch_down(b, s);
+            {
+                ProfileScope k5(layer, 5, s, ProfileScope::kKernel);
+                e = batch_down(b, s, k5.timing());
+            }
             if (e == hipSuccess) e = batch_combine(b, s);
             if (e != hipSuccess) return hip_fail(e, "batched down/combine launch");
             p2.end();
@@ -618,6 +624,13 @@ moe_status_t decode_tokens(moe_layer_t* layer, uint8_t* ws, const WorkspaceLayou
                            unsigned* fused_seq, hipStream_t s) {
     const moe_config_t& c = layer->cfg;
     moe_status_t st = MOE_OK;
+    if (layer->cache && layer->next) {
+        // the prediction runs on the next layer's workspace, which must not
+        // hold this call's state
+        const moe_layer* nx = layer->next;
+        if (!nx->ws || (nx->ws < ws + W.total && ws < nx->ws + nx->W.total))
+            return fail(MOE_EINVAL, "moe_layer_forward: the linked next layer needs a workspace of its own");
+    }
     for (int t = 0; t < T; ++t) {
         DecodeArgs a = decode_args(layer, ws, W, d_x + (size_t)t * c.hidden, ids_base + (size_t)t * ids_stride,
                                    w_base + (size_t)t * w_stride, d_y + (size_t)t * c.hidden);
@@ -635,16 +648,35 @@ moe_status_t decode_tokens(moe_layer_t* layer, uint8_t* ws, const WorkspaceLayou
             if (e != hipSuccess) return hip_fail(e, "fused decode launch");
             continue;
         }
+        // a kernel that moe_layer_profile does not time is stamped for the
+        // cache's copy/compute timeline when that is on
+        auto stamp = [&](const ProfileScope& p) {
+            LaunchTiming t = p.timing();
+            return t.start || !layer->cache ? t : cache_kernel_timing(layer->cache);
+        };
         ProfileScope p0(layer, 0, s, ProfileScope::kKernel);
-        hipError_t e = decode_router(a, s, p0.timing());
+        hipError_t e = decode_router(a, s, stamp(p0));
         if (e != hipSuccess) return hip_fail(e, "router kernel launch");
         p0.end();
+        // speculative prefetch: the linked next layer's router and top-k on
+        // this token's input (no shared expert work), into that layer's
+        // one-token routing slots
+        const int32_t* d_pred = nullptr;
+        if (layer->cache && layer->next) {
+            moe_layer* nx = layer->next;
+            DecodeArgs pa = decode_args(nx, nx->ws, nx->W, a.x, reinterpret_cast<int32_t*>(nx->ws + nx->W.ids),
+                                        reinterpret_cast<float*>(nx->ws + nx->W.w), nullptr);
+            pa.S = 0;
+            e = decode_router(pa, s, cache_kernel_timing(layer->cache));
+            if (e != hipSuccess) return hip_fail(e, "next-layer router launch");
+            d_pred = pa.ids;
+        }
         ProfileScope p1(layer, 1, s, layer->cache ? ProfileScope::kSpan : ProfileScope::kKernel);
         if (layer->cache) {
             // the host needs the routing: the cache reads it back, resolves
             // it, copies missing experts and enqueues the routed gate/up
             // (hits first)
-            st = cache_prepare_token(layer, a, s);
+            st = cache_prepare_token(layer, a, s, d_pred);
             if (st != MOE_OK) return st;
         } else {
             e = decode_routed_gateup(a, s, p1.timing());
@@ -652,7 +684,7 @@ moe_status_t decode_tokens(moe_layer_t* layer, uint8_t* ws, const WorkspaceLayou
         }
         p1.end();
         ProfileScope p2(layer, 2, s, ProfileScope::kKernel);
-        e = decode_down_combine(a, s, p2.timing());
+        e = decode_down_combine(a, s, stamp(p2));
         if (e != hipSuccess) return hip_fail(e, "down/combine kernel launch");
         p2.end();
         if (layer->cache) {

@@ -42,6 +42,7 @@
 // step once per nibble plane: the high plane's codes become 16 (c - 8) and
 // the low plane's c exactly in fp16, two MFMAs under the group's one scale.  With the adaptive top-p cut a
 // dropped choice (id -1) gets no dispatch entry and the combine skips it.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -884,55 +885,59 @@ hipError_t launch_topk(const BatchArgs& a, bool convert, hipStream_t st) {
     return hipGetLastError();
 }
 
+// With timing events the launch goes through hipExtLaunchKernelGGL, which
+// stamps them with the kernel's own start and end.
+template <typename K>
+hipError_t launch_timed(K kernel, dim3 grid, dim3 block, hipStream_t st, const LaunchTiming& tm, const BatchArgs& a) {
+    if (tm.start)
+        hipExtLaunchKernelGGL(kernel, grid, block, 0, st, tm.start, tm.stop, 0, a);
+    else
+        hipLaunchKernelGGL(kernel, grid, block, 0, st, a);
+    return hipGetLastError();
+}
+
 int grouped_grid(const BatchArgs& a, int rblocks) {
     const long items = (long)batch_max_tiles(a.T, a.K, a.E, a.S) * rblocks;
     return (int)(items < kGroupedGrid ? items : kGroupedGrid);
 }
 
 template <int KG, int TT>
-hipError_t launch_gateup_t(const BatchArgs& a, hipStream_t st) {
+hipError_t launch_gateup_t(const BatchArgs& a, hipStream_t st, const LaunchTiming& tm) {
     const dim3 grid(grouped_grid(a, a.I / (kBlockRows * row_pack(a.codec))));
-    if (a.codec == kCodecMxfp4)
-        hipLaunchKernelGGL((batch_gateup_kernel<KG, kCodecMxfp4, TT>), grid, dim3(512), 0, st, a);
-    else if (a.codec == kCodecInt4)
-        hipLaunchKernelGGL((batch_gateup_kernel<KG, kCodecInt4, TT>), grid, dim3(512), 0, st, a);
-    else if (TT == 16 && a.codec == kCodecInt8)
-        hipLaunchKernelGGL((batch_gateup_kernel<KG, kCodecInt8, 16>), grid, dim3(512), 0, st, a);
-    else if (TT == 16 && a.codec == kCodecInt2)
-        hipLaunchKernelGGL((batch_gateup_kernel<KG, kCodecInt2, 16>), grid, dim3(512), 0, st, a);
-    else
-        return hipErrorInvalidValue;
-    return hipGetLastError();
+    if (a.codec == kCodecMxfp4) return launch_timed(batch_gateup_kernel<KG, kCodecMxfp4, TT>, grid, dim3(512), st, tm, a);
+    if (a.codec == kCodecInt4) return launch_timed(batch_gateup_kernel<KG, kCodecInt4, TT>, grid, dim3(512), st, tm, a);
+    if (TT == 16 && a.codec == kCodecInt8)
+        return launch_timed(batch_gateup_kernel<KG, kCodecInt8, 16>, grid, dim3(512), st, tm, a);
+    if (TT == 16 && a.codec == kCodecInt2)
+        return launch_timed(batch_gateup_kernel<KG, kCodecInt2, 16>, grid, dim3(512), st, tm, a);
+    return hipErrorInvalidValue;
 }
 
 template <int KG>
-hipError_t launch_gateup(const BatchArgs& a, hipStream_t st) {
-    if (a.tile_tokens == 32) return launch_gateup_t<KG, 32>(a, st);
-    if (a.tile_tokens == 16) return launch_gateup_t<KG, 16>(a, st);
+hipError_t launch_gateup(const BatchArgs& a, hipStream_t st, const LaunchTiming& tm) {
+    if (a.tile_tokens == 32) return launch_gateup_t<KG, 32>(a, st, tm);
+    if (a.tile_tokens == 16) return launch_gateup_t<KG, 16>(a, st, tm);
     return hipErrorInvalidValue;
 }
 
 template <int KGI, int TT>
-hipError_t launch_down_t(const BatchArgs& a, hipStream_t st) {
+hipError_t launch_down_t(const BatchArgs& a, hipStream_t st, const LaunchTiming& tm) {
     const int g = grouped_grid(a, a.H / (kDownBlockRows * row_pack(a.codec)));
     const dim3 grid(g < kGroupedGrid / 2 ? g : kGroupedGrid / 2);  // one workgroup per CU
-    if (a.codec == kCodecMxfp4)
-        hipLaunchKernelGGL((batch_down_kernel<KGI, kCodecMxfp4, TT>), grid, dim3(kDownThreads), 0, st, a);
-    else if (a.codec == kCodecInt4)
-        hipLaunchKernelGGL((batch_down_kernel<KGI, kCodecInt4, TT>), grid, dim3(kDownThreads), 0, st, a);
-    else if (TT == 16 && a.codec == kCodecInt8)
-        hipLaunchKernelGGL((batch_down_kernel<KGI, kCodecInt8, 16>), grid, dim3(kDownThreads), 0, st, a);
-    else if (TT == 16 && a.codec == kCodecInt2)
-        hipLaunchKernelGGL((batch_down_kernel<KGI, kCodecInt2, 16>), grid, dim3(kDownThreads), 0, st, a);
-    else
-        return hipErrorInvalidValue;
-    return hipGetLastError();
+    const dim3 block(kDownThreads);
+    if (a.codec == kCodecMxfp4) return launch_timed(batch_down_kernel<KGI, kCodecMxfp4, TT>, grid, block, st, tm, a);
+    if (a.codec == kCodecInt4) return launch_timed(batch_down_kernel<KGI, kCodecInt4, TT>, grid, block, st, tm, a);
+    if (TT == 16 && a.codec == kCodecInt8)
+        return launch_timed(batch_down_kernel<KGI, kCodecInt8, 16>, grid, block, st, tm, a);
+    if (TT == 16 && a.codec == kCodecInt2)
+        return launch_timed(batch_down_kernel<KGI, kCodecInt2, 16>, grid, block, st, tm, a);
+    return hipErrorInvalidValue;
 }
 
 template <int KGI>
-hipError_t launch_down(const BatchArgs& a, hipStream_t st) {
-    if (a.tile_tokens == 32) return launch_down_t<KGI, 32>(a, st);
-    if (a.tile_tokens == 16) return launch_down_t<KGI, 16>(a, st);
+hipError_t launch_down(const BatchArgs& a, hipStream_t st, const LaunchTiming& tm) {
+    if (a.tile_tokens == 32) return launch_down_t<KGI, 32>(a, st, tm);
+    if (a.tile_tokens == 16) return launch_down_t<KGI, 16>(a, st, tm);
     return hipErrorInvalidValue;
 }
 
@@ -956,15 +961,15 @@ hipError_t batch_dispatch(const BatchArgs& a, hipStream_t st) {
     return hipGetLastError();
 }
 
-hipError_t batch_gateup(const BatchArgs& a, hipStream_t st) {
+hipError_t batch_gateup(const BatchArgs& a, hipStream_t st, const LaunchTiming& tm) {
     switch (a.H / 32) {
-        case 8: return launch_gateup<8>(a, st);
-        case 16: return launch_gateup<16>(a, st);
-        case 32: return launch_gateup<32>(a, st);
-        case 64: return launch_gateup<64>(a, st);
-        case 128: return launch_gateup<128>(a, st);
-        case 192: return launch_gateup<192>(a, st);
-        case 256: return launch_gateup<256>(a, st);
+        case 8: return launch_gateup<8>(a, st, tm);
+        case 16: return launch_gateup<16>(a, st, tm);
+        case 32: return launch_gateup<32>(a, st, tm);
+        case 64: return launch_gateup<64>(a, st, tm);
+        case 128: return launch_gateup<128>(a, st, tm);
+        case 192: return launch_gateup<192>(a, st, tm);
+        case 256: return launch_gateup<256>(a, st, tm);
         default: return hipErrorInvalidValue;
     }
 }
@@ -978,14 +983,14 @@ hipError_t batch_hprep(const BatchArgs& a, hipStream_t st) {
     return hipGetLastError();
 }
 
-hipError_t batch_down(const BatchArgs& a, hipStream_t st) {
+hipError_t batch_down(const BatchArgs& a, hipStream_t st, const LaunchTiming& tm) {
     switch (a.I / 32) {
-        case 4: return launch_down<4>(a, st);
-        case 8: return launch_down<8>(a, st);
-        case 16: return launch_down<16>(a, st);
-        case 32: return launch_down<32>(a, st);
-        case 64: return launch_down<64>(a, st);
-        case 128: return launch_down<128>(a, st);
+        case 4: return launch_down<4>(a, st, tm);
+        case 8: return launch_down<8>(a, st, tm);
+        case 16: return launch_down<16>(a, st, tm);
+        case 32: return launch_down<32>(a, st, tm);
+        case 64: return launch_down<64>(a, st, tm);
+        case 128: return launch_down<128>(a, st, tm);
         default: return hipErrorInvalidValue;
     }
 }

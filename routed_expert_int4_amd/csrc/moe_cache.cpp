@@ -11,7 +11,8 @@
 //  - the compute stream waits for the slot's copy event before a kernel
 //    reads it.
 // The one host wait per token is for the token's routing (a small
-// device-to-host copy of the expert ids).
+// device-to-host copy of the expert ids, with the next layer's predicted ids
+// beside them when a next layer is linked).
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -37,6 +38,9 @@ struct LayerSlots {
     std::vector<char> use_recorded;        // [slots]
     std::vector<char> copy_recorded;       // [slots]
     std::vector<uint64_t> usage;           // [E] routed uses (the learning cache's counts)
+    std::vector<char> fresh;               // [E] brought in by a prefetch and not used since
+    std::vector<int> prediction;           // experts predicted for this layer's next call
+    bool has_prediction = false;
     moe_cache_stats_t stats{};
 };
 
@@ -50,10 +54,19 @@ struct moe_cache {
     size_t expert_bytes = 0;
     hipStream_t copy_stream = nullptr;
     std::vector<moe::LayerSlots*> layers;
-    int32_t* pinned_ids = nullptr;   // host-pinned staging of one token's ids
+    int32_t* pinned_ids = nullptr;   // host-pinned staging of one token's ids [0, 16) and prediction [16, 32)
     hipEvent_t ids_ready = nullptr;
     std::vector<int> pending_slots;  // slots read by the token being enqueued
     int pending_layer = -1;
+    // copy/compute timeline (expert_cache_timeline): a pool of timing events
+    // and the recorded intervals (kind 0 copy, 1 kernel; index of the begin
+    // event, the end event follows it)
+    bool timeline = false;
+    int max_marks = 0;
+    int truncated = 0;
+    std::vector<hipEvent_t> tl_events;
+    size_t tl_used = 0;
+    std::vector<std::pair<int, int>> tl_marks;
 
     uint8_t* slot_ptr(int layer, int s) const {
         return pool + ((size_t)layer * slots + (size_t)s) * expert_bytes;
@@ -72,9 +85,44 @@ static void destroy_cache(moe_cache* c) {
             if (e) (void)hipEventDestroy(e);
         delete L;
     }
+    for (hipEvent_t e : c->tl_events) (void)hipEventDestroy(e);
     if (c->ids_ready) (void)hipEventDestroy(c->ids_ready);
     if (c->pinned_ids) (void)hipHostFree(c->pinned_ids);
     delete c;
+}
+
+// Two timing events for one interval of the timeline (kind 0 copy, 1
+// kernel), or false when the timeline is off or full.
+static bool timeline_pair(moe_cache* c, int kind, hipEvent_t* begin, hipEvent_t* end) {
+    if (!c->timeline) return false;
+    if ((int)c->tl_marks.size() >= c->max_marks) {
+        c->truncated = 1;
+        return false;
+    }
+    while (c->tl_events.size() < c->tl_used + 2) {
+        hipEvent_t ev;
+        if (hipEventCreate(&ev) != hipSuccess) {
+            (void)hipGetLastError();
+            c->truncated = 1;
+            return false;
+        }
+        c->tl_events.push_back(ev);
+    }
+    *begin = c->tl_events[c->tl_used];
+    *end = c->tl_events[c->tl_used + 1];
+    c->tl_marks.emplace_back(kind, (int)c->tl_used);
+    c->tl_used += 2;
+    return true;
+}
+
+LaunchTiming cache_kernel_timing(moe_cache* c) {
+    LaunchTiming t;
+    hipEvent_t b, e;
+    if (c && timeline_pair(c, 1, &b, &e)) {
+        t.start = b;
+        t.stop = e;
+    }
+    return t;
 }
 
 // Makes expert e of layer l resident; `protect` lists experts that must not
@@ -93,12 +141,19 @@ static moe_status_t make_resident(moe_cache* c, int l, int e, const std::vector<
     int evicted = -1;
     s = L.policy.assign(e, protect, &evicted);
     if (s < 0) return fail(MOE_ENOSLOT, "expert cache: no slot of layer %d can be freed", l);
-    if (evicted >= 0) ++L.stats.evictions;
+    if (evicted >= 0) {
+        ++L.stats.evictions;
+        L.fresh[evicted] = 0;
+    }
+    hipEvent_t tb = nullptr, te = nullptr;
+    const bool stamp = timeline_pair(c, 0, &tb, &te);
     hipError_t err = hipSuccess;
     if (L.use_recorded[s]) err = hipStreamWaitEvent(c->copy_stream, L.last_use[s], 0);
+    if (err == hipSuccess && stamp) err = hipEventRecord(tb, c->copy_stream);
     if (err == hipSuccess)
         err = hipMemcpyAsync(c->slot_ptr(l, s), L.host_blob[e], c->expert_bytes, hipMemcpyHostToDevice,
                              c->copy_stream);
+    if (err == hipSuccess && stamp) err = hipEventRecord(te, c->copy_stream);
     if (err == hipSuccess) err = hipEventRecord(L.copy_done[s], c->copy_stream);
     if (err != hipSuccess) {
         L.policy.release(e);
@@ -111,12 +166,36 @@ static moe_status_t make_resident(moe_cache* c, int l, int e, const std::vector<
     return MOE_OK;
 }
 
-moe_status_t cache_prepare_token(moe_layer* layer, DecodeArgs& a, hipStream_t st) {
+// Brings in the experts of `want` (ids -1 skipped) that are not resident, in
+// order, at most max_copies of them (< 0: no limit); the slot of each is
+// chosen as for a miss with the whole list protected, so no expert of the
+// list is evicted for another.  Each copy counts as a prefetch and the
+// expert is marked fresh until its first use or its eviction.
+static moe_status_t prefetch_experts(moe_cache* c, int l, const std::vector<int>& want, int max_copies) {
+    LayerSlots& L = *c->layers[l];
+    int copies = 0;
+    for (int e : want) {
+        if (e < 0 || L.policy.slot_of(e) >= 0) continue;
+        if (max_copies >= 0 && copies >= max_copies) break;
+        int s = -1;
+        bool missed = false;
+        moe_status_t r = make_resident(c, l, e, want, &s, &missed);
+        if (r != MOE_OK) return r;
+        ++L.stats.prefetches;
+        L.fresh[e] = 1;
+        ++copies;
+    }
+    return MOE_OK;
+}
+
+moe_status_t cache_prepare_token(moe_layer* layer, DecodeArgs& a, hipStream_t st, const int32_t* d_pred) {
     moe_cache* c = layer->cache;
     const int l = layer->cache_layer;
     LayerSlots& L = *c->layers[l];
     const int K = a.K;
     hipError_t err = hipMemcpyAsync(c->pinned_ids, a.ids, sizeof(int32_t) * K, hipMemcpyDeviceToHost, st);
+    if (err == hipSuccess && d_pred)
+        err = hipMemcpyAsync(c->pinned_ids + 16, d_pred, sizeof(int32_t) * K, hipMemcpyDeviceToHost, st);
     if (err == hipSuccess) err = hipEventRecord(c->ids_ready, st);
     if (err == hipSuccess) err = hipEventSynchronize(c->ids_ready);
     if (err != hipSuccess) return hip_fail(err, "expert cache: reading the routing");
@@ -125,12 +204,28 @@ moe_status_t cache_prepare_token(moe_layer* layer, DecodeArgs& a, hipStream_t st
     for (int e : ids)
         if (e < -1 || e >= c->cfg.n_experts || (e == -1 && !(layer->cfg.top_p < 1.0f)))
             return fail(MOE_EINVAL, "expert cache: routed id %d out of range", e);
+    std::vector<int> guess;
+    if (d_pred) {
+        for (int j = 0; j < K; ++j) {
+            const int e = c->pinned_ids[16 + j];
+            if (e < -1 || e >= c->cfg.n_experts) return fail(MOE_EINVAL, "expert cache: predicted id %d out of range", e);
+            if (e >= 0) guess.push_back(e);
+        }
+    }
     std::vector<int> needed;
     for (int e : ids)
         if (e >= 0) {
             ++L.usage[e];
             needed.push_back(e);
         }
+    // how well the previous layer predicted this token's experts
+    if (L.has_prediction) {
+        for (int e : needed) {
+            ++L.stats.predicted_uses;
+            if (std::find(L.prediction.begin(), L.prediction.end(), e) != L.prediction.end()) ++L.stats.predicted_hits;
+        }
+        L.has_prediction = false;
+    }
     std::vector<int> hit_slots, miss_slots, slot_of_j(K, -1);
     for (int j = 0; j < K; ++j) {
         a.blobs[j] = nullptr;
@@ -141,14 +236,29 @@ moe_status_t cache_prepare_token(moe_layer* layer, DecodeArgs& a, hipStream_t st
         if (r != MOE_OK) return r;
         slot_of_j[j] = s;
         a.blobs[j] = c->slot_ptr(l, s);
-        // a hit on a slot whose (prefetch) copy may still run also waits
         if (missed) {
             ++L.stats.misses;
             miss_slots.push_back(j);
-        } else {
-            ++L.stats.hits;
-            hit_slots.push_back(j);
+            continue;
         }
+        ++L.stats.hits;
+        if (L.fresh[ids[j]]) {
+            ++L.stats.prefetch_hits;
+            L.fresh[ids[j]] = 0;
+        }
+        // a hit whose (prefetch) copy is still running goes with the misses,
+        // so that it does not hold back the hits that are ready
+        bool copying = false;
+        if (L.copy_recorded[s]) {
+            const hipError_t q = hipEventQuery(L.copy_done[s]);
+            if (q == hipErrorNotReady) {
+                copying = true;
+                (void)hipGetLastError();
+            } else if (q != hipSuccess) {
+                return hip_fail(q, "expert cache: copy event query");
+            }
+        }
+        (copying ? miss_slots : hit_slots).push_back(j);
     }
     a.direct = 1;
     // gate/up of the hit experts first, then of the misses once copied (the
@@ -166,7 +276,7 @@ moe_status_t cache_prepare_token(moe_layer* layer, DecodeArgs& a, hipStream_t st
         a.use_slot_list = 1;
         a.n_slot_list = (int)js.size();
         for (size_t i = 0; i < js.size(); ++i) a.slot_list[i] = js[i];
-        err = decode_routed_gateup(a, st);
+        err = decode_routed_gateup(a, st, cache_kernel_timing(c));
         if (err != hipSuccess) return hip_fail(err, "gate/up kernel launch");
     }
     a.use_slot_list = 0;
@@ -175,6 +285,16 @@ moe_status_t cache_prepare_token(moe_layer* layer, DecodeArgs& a, hipStream_t st
     for (int s : slot_of_j)
         if (s >= 0) c->pending_slots.push_back(s);
     c->pending_layer = l;
+    // the next layer's predicted experts, queued behind this token's misses
+    if (d_pred) {
+        const int nl = layer->next->cache_layer;
+        LayerSlots& N = *c->layers[nl];
+        N.prediction = guess;
+        N.has_prediction = true;
+        const int limit = layer->max_prefetch > 0 ? layer->max_prefetch : K;
+        moe_status_t r = prefetch_experts(c, nl, guess, limit);
+        if (r != MOE_OK) return r;
+    }
     return MOE_OK;
 }
 
@@ -221,7 +341,7 @@ moe_status_t expert_cache_create(const moe_config_t* cfg, int n_layers, int slot
     c->pool = static_cast<uint8_t*>(d_slot_pool);
     c->expert_bytes = eb;
     c->copy_stream = static_cast<hipStream_t>(copy_stream);
-    hipError_t err = hipHostMalloc(reinterpret_cast<void**>(&c->pinned_ids), sizeof(int32_t) * 16);
+    hipError_t err = hipHostMalloc(reinterpret_cast<void**>(&c->pinned_ids), sizeof(int32_t) * 32);
     if (err == hipSuccess) err = hipEventCreateWithFlags(&c->ids_ready, hipEventDisableTiming);
     for (int l = 0; l < n_layers && err == hipSuccess; ++l) {
         LayerSlots* L = new (std::nothrow) LayerSlots(cfg->n_experts, slots_per_layer);
@@ -236,6 +356,7 @@ moe_status_t expert_cache_create(const moe_config_t* cfg, int n_layers, int slot
         L->use_recorded.assign(slots_per_layer, 0);
         L->copy_recorded.assign(slots_per_layer, 0);
         L->usage.assign(cfg->n_experts, 0);
+        L->fresh.assign(cfg->n_experts, 0);
         for (int s = 0; s < slots_per_layer && err == hipSuccess; ++s) {
             err = hipEventCreateWithFlags(&L->copy_done[s], hipEventDisableTiming);
             if (err == hipSuccess) err = hipEventCreateWithFlags(&L->last_use[s], hipEventDisableTiming);
@@ -271,16 +392,7 @@ moe_status_t expert_cache_prefetch(moe_cache_t* cache, int layer, const int32_t*
     std::vector<int> want(h_experts, h_experts + n);
     for (int e : want)
         if (e < 0 || e >= cache->cfg.n_experts) return fail(MOE_EINVAL, "expert_cache_prefetch: expert %d", e);
-    LayerSlots& L = *cache->layers[layer];
-    for (int e : want) {
-        if (L.policy.slot_of(e) >= 0) continue;
-        int s = -1;
-        bool missed = false;
-        moe_status_t r = make_resident(cache, layer, e, want, &s, &missed);
-        if (r != MOE_OK) return r;
-        ++L.stats.prefetches;
-    }
-    return MOE_OK;
+    return prefetch_experts(cache, layer, want, -1);
 }
 
 moe_status_t expert_cache_evict(moe_cache_t* cache, int layer, int expert) {
@@ -290,6 +402,7 @@ moe_status_t expert_cache_evict(moe_cache_t* cache, int layer, int expert) {
     LayerSlots& L = *cache->layers[layer];
     // The slot's next copy waits on its last-use event, so freeing it now is safe.
     if (L.policy.release(expert) >= 0) ++L.stats.evictions;
+    L.fresh[expert] = 0;
     return MOE_OK;
 }
 
@@ -420,6 +533,191 @@ moe_status_t expert_cache_replay(int n_experts, int slots, int top_k, const int3
             }
         }
     }
+    return MOE_OK;
+}
+
+moe_status_t expert_cache_replay_prefetch(int n_experts, int slots, int top_k, const int32_t* trace,
+                                          const int32_t* predicted, int n_tokens, int max_prefetch,
+                                          const int32_t* pinned, int n_pinned, uint64_t* counts) {
+    if (n_experts < 1 || slots < top_k || top_k < 1 || n_tokens < 0 || (n_tokens > 0 && (!trace || !predicted)) ||
+        !counts || n_pinned < 0 || (n_pinned > 0 && !pinned) || n_pinned > slots - top_k || max_prefetch < 0)
+        return fail(MOE_EINVAL, "expert_cache_replay_prefetch: bad arguments");
+    SlotPolicy p(n_experts, slots);
+    for (int i = 0; i < n_pinned; ++i) {
+        const int e = pinned[i];
+        if (e < 0 || e >= n_experts)
+            return fail(MOE_EINVAL, "expert_cache_replay_prefetch: pinned id %d out of range", e);
+        if (p.slot_of(e) < 0) {
+            int ev = -1;
+            if (p.assign(e, {}, &ev) < 0) return fail(MOE_ENOSLOT, "expert_cache_replay_prefetch: no slot to pin");
+        }
+        p.pin(e);
+    }
+    uint64_t hits = 0, misses = 0, evictions = 0, prefetches = 0, prefetch_hits = 0, pred_uses = 0, pred_hits = 0;
+    std::vector<char> fresh(n_experts, 0);
+    const int limit = max_prefetch > 0 ? max_prefetch : top_k;
+    for (int t = 0; t < n_tokens; ++t) {
+        std::vector<int> ids, guess;
+        bool any = false;
+        for (int j = 0; j < top_k; ++j) {
+            const int e = trace[(size_t)t * top_k + j];
+            const int g = predicted[(size_t)t * top_k + j];
+            if (e < -1 || e >= n_experts || g < -1 || g >= n_experts)
+                return fail(MOE_EINVAL, "expert_cache_replay_prefetch: id out of range at token %d", t);
+            if (e >= 0) ids.push_back(e);
+            if (g >= 0) guess.push_back(g);
+            any = any || g != -1;
+        }
+        if (any) {
+            // the prefetch the previous layer's call makes before this lookup
+            int copies = 0;
+            for (int e : guess) {
+                if (p.slot_of(e) >= 0) continue;
+                if (copies >= limit) break;
+                int ev = -1;
+                if (p.assign(e, guess, &ev) < 0) return fail(MOE_ENOSLOT, "expert_cache_replay_prefetch: no slot");
+                if (ev >= 0) {
+                    ++evictions;
+                    fresh[ev] = 0;
+                }
+                fresh[e] = 1;
+                ++prefetches;
+                ++copies;
+            }
+            for (int e : ids) {
+                ++pred_uses;
+                if (std::find(guess.begin(), guess.end(), e) != guess.end()) ++pred_hits;
+            }
+        }
+        for (int e : ids) {
+            if (p.slot_of(e) >= 0) {
+                p.touch(e);
+                ++hits;
+                if (fresh[e]) {
+                    ++prefetch_hits;
+                    fresh[e] = 0;
+                }
+            } else {
+                int ev = -1;
+                if (p.assign(e, ids, &ev) < 0) return fail(MOE_ENOSLOT, "expert_cache_replay_prefetch: no slot");
+                ++misses;
+                if (ev >= 0) {
+                    ++evictions;
+                    fresh[ev] = 0;
+                }
+            }
+        }
+    }
+    counts[0] = hits;
+    counts[1] = misses;
+    counts[2] = evictions;
+    counts[3] = prefetches;
+    counts[4] = prefetch_hits;
+    counts[5] = pred_uses;
+    counts[6] = pred_hits;
+    return MOE_OK;
+}
+
+moe_status_t moe_layer_set_next(moe_layer_t* layer, moe_layer_t* next, int max_prefetch) {
+    if (!layer) return fail(MOE_EINVAL, "moe_layer_set_next: layer is NULL");
+    if (max_prefetch < 0) return fail(MOE_EINVAL, "moe_layer_set_next: max_prefetch < 0");
+    if (!next) {
+        layer->next = nullptr;
+        layer->max_prefetch = 0;
+        return MOE_OK;
+    }
+    if (!layer->cache || !next->cache || layer->cache != next->cache)
+        return fail(MOE_EINVAL, "moe_layer_set_next: both layers must be attached to the same expert cache");
+    if (next == layer || next->cache_layer == layer->cache_layer)
+        return fail(MOE_EINVAL, "moe_layer_set_next: the next layer must be another cache layer");
+    if (!next->ws) return fail(MOE_EINVAL, "moe_layer_set_next: the next layer has no workspace");
+    if (layer->ws && next->ws < layer->ws + layer->W.total && layer->ws < next->ws + next->W.total)
+        return fail(MOE_EINVAL, "moe_layer_set_next: the layers' workspaces overlap");
+    const moe_config_t &a = layer->cfg, &b = next->cfg;
+    if (a.hidden != b.hidden || a.top_k != b.top_k)
+        return fail(MOE_EINVAL, "moe_layer_set_next: the layers' hidden sizes or top_k differ");
+    layer->next = next;
+    layer->max_prefetch = max_prefetch;
+    return MOE_OK;
+}
+
+moe_status_t expert_cache_timeline(moe_cache_t* cache, int enable, int max_marks) {
+    if (!cache) return fail(MOE_EINVAL, "expert_cache_timeline: cache is NULL");
+    if (max_marks < 0) return fail(MOE_EINVAL, "expert_cache_timeline: max_marks < 0");
+    cache->timeline = enable != 0;
+    cache->max_marks = max_marks > 0 ? max_marks : 65536;
+    cache->tl_marks.clear();
+    cache->tl_used = 0;
+    cache->truncated = 0;
+    return MOE_OK;
+}
+
+// Total length of a set of intervals' union; sorts and merges them in place.
+static double merge_union(std::vector<std::pair<double, double>>& v) {
+    std::sort(v.begin(), v.end());
+    std::vector<std::pair<double, double>> m;
+    for (const auto& iv : v) {
+        if (!m.empty() && iv.first <= m.back().second)
+            m.back().second = std::max(m.back().second, iv.second);
+        else
+            m.push_back(iv);
+    }
+    v.swap(m);
+    double t = 0.0;
+    for (const auto& iv : v) t += iv.second - iv.first;
+    return t;
+}
+
+moe_status_t expert_cache_timeline_read(moe_cache_t* cache, moe_cache_timeline_t* out) {
+    if (!cache || !out) return fail(MOE_EINVAL, "expert_cache_timeline_read: NULL argument");
+    std::memset(out, 0, sizeof *out);
+    out->truncated = cache->truncated;
+    std::vector<std::pair<double, double>> iv[2];
+    if (!cache->tl_marks.empty()) {
+        hipEvent_t ref = cache->tl_events[cache->tl_marks[0].second];
+        for (const auto& m : cache->tl_marks) {
+            hipEvent_t b = cache->tl_events[m.second], e = cache->tl_events[m.second + 1];
+            hipError_t err = hipEventSynchronize(e);
+            float tb = 0.0f, te = 0.0f;
+            if (err == hipSuccess) err = hipEventElapsedTime(&tb, ref, b);
+            if (err == hipSuccess) err = hipEventElapsedTime(&te, ref, e);
+            if (err != hipSuccess) {
+                // an interval whose launch or copy was never enqueued
+                (void)hipGetLastError();
+                continue;
+            }
+            iv[m.first].emplace_back(tb, te);
+        }
+    }
+    out->copies = iv[0].size();
+    out->kernels = iv[1].size();
+    double lo = 0.0, hi = 0.0;
+    bool first = true;
+    for (int k = 0; k < 2; ++k)
+        for (const auto& x : iv[k]) {
+            lo = first ? x.first : std::min(lo, x.first);
+            hi = first ? x.second : std::max(hi, x.second);
+            first = false;
+        }
+    out->copy_ms = merge_union(iv[0]);
+    out->kernel_ms = merge_union(iv[1]);
+    out->span_ms = first ? 0.0 : hi - lo;
+    // intersection of the two unions (both sorted and disjoint now)
+    double both = 0.0;
+    size_t i = 0, j = 0;
+    while (i < iv[0].size() && j < iv[1].size()) {
+        const double a0 = std::max(iv[0][i].first, iv[1][j].first);
+        const double a1 = std::min(iv[0][i].second, iv[1][j].second);
+        if (a1 > a0) both += a1 - a0;
+        if (iv[0][i].second < iv[1][j].second)
+            ++i;
+        else
+            ++j;
+    }
+    out->overlap_ms = both;
+    cache->tl_marks.clear();
+    cache->tl_used = 0;
+    cache->truncated = 0;
     return MOE_OK;
 }
 

@@ -57,8 +57,9 @@ moe_status_t decode_tokens(moe_layer* L, uint8_t* ws, const WorkspaceLayout& W, 
 moe_status_t check_layer_status(const moe_layer* L, const char* who);
 
 constexpr unsigned kDefaultSpinLimit = 1u << 20;  // polls, about a second
-// moe_layer_profile kinds: router, gate/up, down + combine, fused one-token launch
-constexpr int kProfileKinds = 4;
+// moe_layer_profile kinds: router, gate/up, down + combine, fused one-token
+// launch, and the batched path's grouped gate/up and down kernels alone
+constexpr int kProfileKinds = 6;
 
 }  // namespace moe
 
@@ -75,6 +76,10 @@ struct moe_layer {
     moe::WorkspaceLayout W;
     moe_cache* cache = nullptr;
     int cache_layer = -1;
+    // speculative next-layer prefetch (moe_layer_set_next): the linked layer
+    // whose experts one-token calls predict and prefetch, and the copy limit
+    moe_layer* next = nullptr;
+    int max_prefetch = 0;
     // one-token calls: 3 = three launches (the default), 1 = one fused
     // launch when its workgroups fit on the device at once (moe_layer_set_decode)
     int decode_launches = 3;

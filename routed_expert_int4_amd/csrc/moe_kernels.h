@@ -186,9 +186,9 @@ hipError_t batch_router(const BatchArgs& a, hipStream_t st);
 hipError_t batch_topk(const BatchArgs& a, bool convert, hipStream_t st);
 // counts, offsets, perm, inv, distinct, tiles from ids (T*K <= kMaxDispatchEntries).
 hipError_t batch_dispatch(const BatchArgs& a, hipStream_t st);
-hipError_t batch_gateup(const BatchArgs& a, hipStream_t st);
+hipError_t batch_gateup(const BatchArgs& a, hipStream_t st, const LaunchTiming& tm = {});
 hipError_t batch_hprep(const BatchArgs& a, hipStream_t st);
-hipError_t batch_down(const BatchArgs& a, hipStream_t st);
+hipError_t batch_down(const BatchArgs& a, hipStream_t st, const LaunchTiming& tm = {});
 hipError_t batch_combine(const BatchArgs& a, hipStream_t st);
 bool batch_shape_supported(int hidden, int inter);
 // The batched kernels serve this codec at this shape (int2: hidden a

@@ -109,6 +109,12 @@ class ExpertCache:
     def autopin(self, layer: int, n: int) -> None:
         B.expert_cache_autopin(self.handle, layer, n)
 
+    def timeline(self, enable: bool, max_marks: int = 0) -> None:
+        B.expert_cache_timeline(self.handle, enable, max_marks)
+
+    def timeline_read(self) -> dict:
+        return B.expert_cache_timeline_read(self.handle)
+
     def close(self) -> None:
         if getattr(self, "handle", None):
             B.expert_cache_destroy(self.handle)
@@ -165,10 +171,17 @@ class DeviceLayer:
         B.moe_layer_attach_cache(self.handle, cache.handle, layer_id)
         self.cache = cache  # the cache outlives the layer's use of it
 
+    def set_next(self, next_layer: "DeviceLayer | None", max_prefetch: int = 0) -> None:
+        """Speculative prefetch of next_layer's experts on this layer's input
+        (None: off)."""
+        B.moe_layer_set_next(self.handle, next_layer.handle if next_layer is not None else None, max_prefetch)
+        self.next_layer = next_layer  # kept alive while linked
+
     def close(self):
         if getattr(self, "handle", None):
             B.moe_layer_destroy(self.handle)
             self.handle = None
+        self.next_layer = None
 
     def __del__(self):
         try:

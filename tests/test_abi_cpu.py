@@ -268,6 +268,50 @@ def test_cache_policy_matches_lru_replay(slots, skew):
         assert B.expert_cache_replay(E, slots, k, trace, pinned=pins) == lru.replay(trace, slots, pinned=pins)
 
 
+@pytest.mark.parametrize("slots,n_pin,max_prefetch", [(16, 0, 0), (16, 6, 3), (64, 56, 8), (12, 4, 1), (8, 0, 2)])
+def test_cache_replay_prefetch_matches_oracle(slots, n_pin, max_prefetch):
+    """The library's host replay of the prefetching cache equals the oracle's
+    on Zipf traces, with predictions drawn from the same prior, rows without a
+    prediction and top-p drops (id -1) in both."""
+    rng = np.random.default_rng(100 + slots + n_pin)
+    E, k = 256, 8
+    p = 1.0 / np.arange(1, E + 1) ** 1.1
+    p /= p.sum()
+    trace = np.array([rng.choice(E, k, replace=False, p=p) for _ in range(300)], np.int32)
+    guess = np.array([rng.choice(E, k, replace=False, p=p) for _ in range(300)], np.int32)
+    trace[rng.random(trace.shape) < 0.1] = -1
+    guess[rng.random(guess.shape) < 0.1] = -1
+    guess[::7] = -1  # no prediction for these tokens
+    pins = lru.hottest(lru.usage(trace[:100], E), n_pin)
+    got = B.expert_cache_replay_prefetch(E, slots, k, trace, guess, max_prefetch, pins)
+    predicted = [None if (row == -1).all() else row for row in guess]
+    ref = lru.replay_prefetch(trace, predicted, slots, pinned=pins, max_prefetch=max_prefetch or k)
+    assert got == ref
+    assert ref["prefetches"] > 0 and ref["predicted_uses"] > 0
+
+
+def test_cache_replay_prefetch_rejects_bad_arguments():
+    trace = np.zeros((2, 4), np.int32)
+    guess = np.full((2, 4), -1, np.int32)
+    for bad in (dict(slots=3), dict(max_prefetch=-1)):
+        kw = dict(slots=8, max_prefetch=0)
+        kw.update(bad)
+        with pytest.raises(B.MoeError) as e:
+            B.expert_cache_replay_prefetch(16, kw["slots"], 4, trace, guess, kw["max_prefetch"])
+        assert e.value.code == B.MOE_EINVAL
+    g = guess.copy()
+    g[1, 2] = 16
+    with pytest.raises(B.MoeError) as e:
+        B.expert_cache_replay_prefetch(16, 8, 4, trace, g)
+    assert e.value.code == B.MOE_EINVAL
+    with pytest.raises(B.MoeError) as e:
+        B.moe_layer_set_next(None, None, 0)
+    assert e.value.code == B.MOE_EINVAL
+    with pytest.raises(B.MoeError) as e:
+        B.expert_cache_timeline(None, True)
+    assert e.value.code == B.MOE_EINVAL
+
+
 def test_cache_replay_skips_dropped_choices():
     """Traces with top-p drops (id -1): the library's replay and the oracle's
     both skip them, and equal the replay of the trace with them removed."""

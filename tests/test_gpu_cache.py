@@ -14,7 +14,11 @@ the C ABI:
     routing trace (oracle/lru.py), and h2d_bytes = misses x blob bytes;
   * copy/compute ordering with the minimum slot count (every token evicts
     experts the previous token read);
-  * prefetch and evict semantics and their errors.
+  * prefetch and evict semantics and their errors;
+  * speculative next-layer prefetch (the next layer's router on the current
+    layer's input): outputs unchanged, the predictions equal to the oracle's
+    routing, and every count equal to the oracle's prefetching replay; the
+    copy/compute timeline sees every copy.
 """
 import sys
 
@@ -322,3 +326,123 @@ def test_glm_cache_stack_parity_and_lru(torch_cuda, slots):
     for lay in layers:
         lay.close()
     cache.close()
+
+
+def run_token_major(torch, cached, x0_bits, noise_seed):
+    """Every token through all layers before the next one starts (the order
+    in which layer l's prediction is used by layer l + 1's call for the same
+    token).  Returns per layer its inputs (bf16 bits) and outputs, ids, w."""
+    from routed_expert_int4_amd.layer import DeviceLayer
+    n_layers, (T, H), k = len(cached), x0_bits.shape, CFG.top_k
+    xs = [np.empty((T, H), np.uint16) for _ in range(n_layers)]
+    ys = [np.empty((T, H), np.float32) for _ in range(n_layers)]
+    ids = [np.empty((T, k), np.int32) for _ in range(n_layers)]
+    ws = [np.empty((T, k), np.float32) for _ in range(n_layers)]
+    noise = synth.gen_noise(CFG, T * n_layers, seed=noise_seed, std=0.1)
+    for t in range(T):
+        xb = x0_bits[t:t + 1]
+        for l in range(n_layers):
+            xs[l][t] = xb[0]
+            y, i, w = cached[l].forward(DeviceLayer.to_device_bf16(xb))
+            torch.cuda.synchronize()
+            ys[l][t], ids[l][t], ws[l][t] = y.cpu().numpy()[0], i.cpu().numpy()[0], w.cpu().numpy()[0]
+            xb = chain_input(ys[l][t:t + 1], noise[t * n_layers + l:t * n_layers + l + 1])
+    return xs, ys, ids, ws
+
+
+@pytest.mark.parametrize("slots,max_prefetch", [(12, 0), (8, 2), (CFG.top_k + 1, 1)])
+def test_cache_next_layer_prefetch(torch_cuda, slots, max_prefetch):
+    torch = torch_cuda
+    from oracle import oracle
+    from routed_expert_int4_amd.layer import DeviceLayer
+    from tests.helpers import check_routing
+    T = 24
+    say(f"[gpu] next-layer prefetch: {N_LAYERS} layers, {slots} slots, max_prefetch {max_prefetch}, {T} tokens")
+    cache, weights, cached, resident = make_stack(torch, slots, max_T=1)
+    for l in range(N_LAYERS - 1):
+        cached[l].set_next(cached[l + 1], max_prefetch)
+    cache.timeline(True)
+    xs, ys, ids, ws = run_token_major(torch, cached, synth.gen_tokens(CFG, T, seed=36), noise_seed=37)
+    tl = cache.timeline_read()
+    copies = 0
+    for l in range(N_LAYERS):
+        res = check_layer(weights[l], xs[l], ys[l], ids[l], ws[l])
+        y_res, ids_res, _ = resident[l].forward_each(DeviceLayer.to_device_bf16(xs[l]))
+        torch.cuda.synchronize()
+        assert np.array_equal(ids_res.cpu().numpy(), ids[l]), "prefetching changed the routing"
+        assert np.array_equal(y_res.cpu().numpy(), ys[l]), "prefetching changed the outputs"
+        predicted = [None] * T
+        if l > 0:
+            # layer l's router on layer l - 1's input, one token at a time
+            # as the predictor runs it, checked against the oracle's routing
+            x_prev = DeviceLayer.to_device_bf16(xs[l - 1])
+            pr, pw = zip(*(resident[l].router_topk(x_prev[t:t + 1]) for t in range(T)))
+            pr = np.concatenate([v.cpu().numpy() for v in pr])
+            pw = np.concatenate([v.cpu().numpy() for v in pw])
+            ref_ids, ref_w, gap = oracle.route(weights[l], xs[l - 1])
+            check_routing(CFG, pr, pw, ref_ids, ref_w, gap)
+            predicted = list(pr)
+        ref = lru.replay_prefetch(ids[l], predicted, slots, max_prefetch=max_prefetch or CFG.top_k)
+        st = cache.stats(l)
+        say(f"[gpu] layer {l}: rel err {res['worst_rel']:.3g}, stats {st}")
+        assert {k: st[k] for k in ref} == ref
+        assert st["h2d_bytes"] == (st["misses"] + st["prefetches"]) * cache.nb
+        copies += st["misses"] + st["prefetches"]
+    calls, preds = T * N_LAYERS, T * (N_LAYERS - 1)
+    say(f"[gpu] timeline {tl}")
+    assert not tl["truncated"] and tl["copies"] == copies
+    # router + down per call, one or two gate/up launches, one predictor launch per linked call
+    assert 3 * calls + preds <= tl["kernels"] <= 4 * calls + preds
+    assert 0.0 <= tl["overlap_ms"] <= min(tl["copy_ms"], tl["kernel_ms"]) + 1e-6
+    assert tl["span_ms"] >= max(tl["copy_ms"], tl["kernel_ms"]) - 1e-6 and tl["copy_ms"] > 0.0
+    for l in range(N_LAYERS - 1):
+        cached[l].set_next(None)
+    for lay in cached + resident:
+        lay.close()
+    cache.close()
+
+
+def test_cache_prefetch_link_errors_and_timeline_limit(torch_cuda):
+    torch = torch_cuda
+    from routed_expert_int4_amd.layer import DeviceLayer
+    say("[gpu] next-layer link errors and timeline limit")
+    cache, weights, cached, resident = make_stack(torch, slots=8, n_layers=2, max_T=1)
+    other, _, other_cached, other_resident = make_stack(torch, slots=8, n_layers=1, max_T=1)
+    for a, b in [(cached[0], cached[0]), (cached[0], resident[1]), (resident[0], cached[1]),
+                 (cached[0], other_cached[0])]:
+        with pytest.raises(B.MoeError) as err:
+            a.set_next(b)
+        assert err.value.code == B.MOE_EINVAL
+    with pytest.raises(B.MoeError) as err:
+        B.moe_layer_set_next(cached[0].handle, cached[1].handle, -1)
+    assert err.value.code == B.MOE_EINVAL
+    # a next layer bound to the same workspace is refused, at link time and at call time
+    B.moe_layer_set_workspace(cached[1].handle, cached[0].ws, cached[0].ws_bytes, 1)
+    with pytest.raises(B.MoeError) as err:
+        cached[0].set_next(cached[1])
+    assert err.value.code == B.MOE_EINVAL
+    B.moe_layer_set_workspace(cached[1].handle, cached[1].ws, cached[1].ws_bytes, 1)
+    cached[0].set_next(cached[1])
+    x = DeviceLayer.to_device_bf16(synth.gen_tokens(CFG, 2, seed=38))
+    B.moe_layer_set_workspace(cached[1].handle, cached[0].ws, cached[0].ws_bytes, 1)
+    with pytest.raises(B.MoeError) as err:
+        cached[0].forward(x[0:1])
+    assert err.value.code == B.MOE_EINVAL and "workspace" in B.last_error()
+    torch.cuda.synchronize()
+    B.moe_layer_set_workspace(cached[1].handle, cached[1].ws, cached[1].ws_bytes, 1)
+    # a timeline limited to three intervals: truncated, and no more recorded
+    cache.timeline(True, max_marks=3)
+    cached[0].forward(x[1:2])
+    torch.cuda.synchronize()
+    tl = cache.timeline_read()
+    assert tl["truncated"] == 1 and tl["copies"] + tl["kernels"] <= 3
+    cache.timeline(False)
+    cached[1].forward(x[1:2])
+    torch.cuda.synchronize()
+    tl = cache.timeline_read()
+    assert tl["copies"] == tl["kernels"] == 0 and not tl["truncated"]
+    cached[0].set_next(None)
+    for lay in cached + resident + other_cached + other_resident:
+        lay.close()
+    cache.close()
+    other.close()

@@ -175,9 +175,8 @@ moe_status_t moe_router_topk(moe_layer_t* layer, const uint16_t* d_x, int T, int
  * [T][hidden]; d_y fp32 [T][hidden] (the block output without residual);
  * d_ids / d_w may be NULL, else receive the routing as in moe_router_topk.
  * T = 1 runs the decode kernels (three launches per token, or one fused
- * launch: moe_layer_set_decode).  T > 1
- * with all experts resident runs the batch-union path for every codec
- * (colibrì summary, fr.news.hada.io topic 31297, "Principales
+ * launch: moe_layer_set_decode).  T > 1 runs the batch-union path for
+ * every codec (colibrì summary, fr.news.hada.io topic 31297, "Principales
  * fonctionnalités implémentées": in prefill and batched verification each
  * distinct expert of the batch is read once and applied to every position
  * routed to it): routing of all tokens, a dispatch of the (token, slot)
@@ -187,10 +186,15 @@ moe_status_t moe_router_topk(moe_layer_t* layer, const uint16_t* d_x, int T, int
  * multiple of 512 and inter of 256; other int2 T > 1 calls run the decode
  * kernels token by token.
  * With all experts resident the call is asynchronous.  With an attached
- * expert cache tokens are processed one at a time; the call blocks the host
- * once per token until its routing is known, issues the copies of missing
- * experts on the cache's copy stream and orders the expert kernels after
- * them with events. */
+ * expert cache the call blocks the host until the routing is known, issues
+ * the copies of missing experts on the cache's copy stream and orders the
+ * expert kernels after them with events: a one-token call once per token
+ * (each routed expert one cache lookup, in routing order); a batched call
+ * once per launch sequence, whose tokens are then taken in consecutive groups
+ * (as many tokens as fit, in order, while the group's distinct experts that
+ * are not pinned number at most the layer's unpinned slots) and each group's
+ * distinct experts are looked up once, in ascending id order, and stay
+ * resident until the group's kernels have read them. */
 moe_status_t moe_layer_forward(moe_layer_t* layer, const uint16_t* d_x, int T, float* d_y, int32_t* d_ids,
                                float* d_w, void* stream);
 

@@ -995,6 +995,19 @@ hipError_t batch_down(const BatchArgs& a, hipStream_t st, const LaunchTiming& tm
     }
 }
 
+// The expert table of a launch sequence whose blobs sit in cache slots: the
+// pointers travel as the kernel's argument (no host staging to keep alive).
+__global__ void __launch_bounds__(256) batch_table_kernel(ExpertTable t, int n, const uint8_t** table) {
+    const int i = threadIdx.x;
+    if (i < n) table[i] = t.p[i];
+}
+
+hipError_t batch_set_table(const ExpertTable& t, int n, const uint8_t** table, hipStream_t st) {
+    if (n < 0 || n > 256) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(batch_table_kernel, dim3(1), dim3(256), 0, st, t, n, table);
+    return hipGetLastError();
+}
+
 hipError_t batch_combine(const BatchArgs& a, hipStream_t st) {
     hipLaunchKernelGGL(batch_combine_kernel, dim3(a.T, (a.H + 1023) / 1024), dim3(256), 0, st, a);
     return hipGetLastError();

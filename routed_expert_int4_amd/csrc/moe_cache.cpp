@@ -55,6 +55,7 @@ struct moe_cache {
     hipStream_t copy_stream = nullptr;
     std::vector<moe::LayerSlots*> layers;
     int32_t* pinned_ids = nullptr;   // host-pinned staging of one token's ids [0, 16) and prediction [16, 32)
+    int32_t* pinned_batch = nullptr; // host-pinned staging of a launch sequence's ids (kMaxDispatchEntries)
     hipEvent_t ids_ready = nullptr;
     std::vector<int> pending_slots;  // slots read by the token being enqueued
     int pending_layer = -1;
@@ -88,6 +89,7 @@ static void destroy_cache(moe_cache* c) {
     for (hipEvent_t e : c->tl_events) (void)hipEventDestroy(e);
     if (c->ids_ready) (void)hipEventDestroy(c->ids_ready);
     if (c->pinned_ids) (void)hipHostFree(c->pinned_ids);
+    if (c->pinned_batch) (void)hipHostFree(c->pinned_batch);
     delete c;
 }
 
@@ -298,6 +300,119 @@ moe_status_t cache_prepare_token(moe_layer* layer, DecodeArgs& a, hipStream_t st
     return MOE_OK;
 }
 
+// One group of a batched call: tokens [g0, g1) of the launch sequence b,
+// whose experts (routed ids in ids) are made resident first.
+static moe_status_t run_group(moe_layer* layer, const BatchArgs& b, const int32_t* ids, int g0, int g1,
+                              hipStream_t st) {
+    moe_cache* c = layer->cache;
+    const int l = layer->cache_layer;
+    LayerSlots& L = *c->layers[l];
+    const int K = b.K, E = b.E;
+    std::vector<char> in(E, 0);
+    for (int i = g0 * K; i < g1 * K; ++i)
+        if (ids[i] >= 0) in[ids[i]] = 1;
+    std::vector<int> distinct;
+    for (int e = 0; e < E; ++e)
+        if (in[e]) distinct.push_back(e);
+    ExpertTable table;
+    std::memset(&table, 0, sizeof table);
+    std::vector<int> slots;
+    for (int e : distinct) {
+        int s = -1;
+        bool missed = false;
+        moe_status_t r = make_resident(c, l, e, distinct, &s, &missed);
+        if (r != MOE_OK) return r;
+        if (missed) {
+            ++L.stats.misses;
+        } else {
+            ++L.stats.hits;
+            if (L.fresh[e]) ++L.stats.prefetch_hits;
+        }
+        L.fresh[e] = 0;
+        table.p[e] = c->slot_ptr(l, s);
+        slots.push_back(s);
+        if (L.copy_recorded[s]) {
+            hipError_t err = hipStreamWaitEvent(st, L.copy_done[s], 0);
+            if (err != hipSuccess) return hip_fail(err, "expert cache: stream wait");
+        }
+    }
+    BatchArgs g = b;
+    const int n = g1 - g0;
+    g.x = b.x + (size_t)g0 * b.H;
+    g.xa = b.xa + (size_t)g0 * b.H;
+    g.kx = b.kx + g0;
+    g.ids = b.ids + (size_t)g0 * K;
+    g.w = b.w + (size_t)g0 * K;
+    g.y = b.y + (size_t)g0 * b.H;
+    g.T = n;
+    g.tile_tokens = batch_tile_tokens(b.codec, n, K, E);
+    hipError_t err = batch_set_table(table, E, const_cast<const uint8_t**>(b.table), st);
+    if (err == hipSuccess) err = batch_dispatch(g, st);
+    if (err == hipSuccess) err = batch_gateup(g, st);
+    if (err == hipSuccess) err = batch_hprep(g, st);
+    if (err == hipSuccess) err = batch_down(g, st);
+    if (err == hipSuccess) err = batch_combine(g, st);
+    if (err != hipSuccess) return hip_fail(err, "batched launch behind the expert cache");
+    for (int s : slots) {
+        err = hipEventRecord(L.last_use[s], st);
+        if (err != hipSuccess) return hip_fail(err, "expert cache: last-use event");
+        L.use_recorded[s] = 1;
+    }
+    return MOE_OK;
+}
+
+moe_status_t cache_batch_forward(moe_layer* layer, const uint16_t* d_x, int T, float* d_y, int32_t* ids_base,
+                                 float* w_base, hipStream_t st) {
+    moe_cache* c = layer->cache;
+    LayerSlots& L = *c->layers[layer->cache_layer];
+    const moe_config_t& cfg = layer->cfg;
+    const int K = cfg.top_k, E = cfg.n_experts, H = cfg.hidden;
+    const int tb = layer->W.batch_tokens;
+    L.has_prediction = false;  // a one-token prediction does not carry over to a batched call
+    for (int t0 = 0; t0 < T; t0 += tb) {
+        const int n = T - t0 < tb ? T - t0 : tb;
+        BatchArgs b = batch_args(layer, d_x + (size_t)t0 * H, n, ids_base + (size_t)t0 * K, w_base + (size_t)t0 * K,
+                                 d_y + (size_t)t0 * H);
+        hipError_t err = batch_router(b, st);
+        if (err == hipSuccess) err = batch_topk(b, true, st);
+        if (err == hipSuccess)
+            err = hipMemcpyAsync(c->pinned_batch, b.ids, sizeof(int32_t) * n * K, hipMemcpyDeviceToHost, st);
+        if (err == hipSuccess) err = hipEventRecord(c->ids_ready, st);
+        if (err == hipSuccess) err = hipEventSynchronize(c->ids_ready);
+        if (err != hipSuccess) return hip_fail(err, "expert cache: batched routing");
+        const int32_t* ids = c->pinned_batch;
+        for (int i = 0; i < n * K; ++i) {
+            const int e = ids[i];
+            if (e < -1 || e >= E || (e == -1 && !(cfg.top_p < 1.0f)))
+                return fail(MOE_EINVAL, "expert cache: routed id %d out of range", e);
+            if (e >= 0) ++L.usage[e];
+        }
+        // consecutive groups of tokens whose unpinned experts fit the
+        // unpinned slots together (one token always fits: pins leave top_k)
+        const int room = c->slots - L.policy.n_pinned();
+        std::vector<char> in(E);
+        for (int g0 = 0; g0 < n;) {
+            std::fill(in.begin(), in.end(), 0);
+            int used = 0, t = g0;
+            for (; t < n; ++t) {
+                int add = 0;
+                for (int j = 0; j < K; ++j) {
+                    const int e = ids[t * K + j];
+                    if (e >= 0 && !in[e] && !L.policy.is_pinned(e)) ++add;
+                }
+                if (t > g0 && used + add > room) break;
+                used += add;
+                for (int j = 0; j < K; ++j)
+                    if (ids[t * K + j] >= 0) in[ids[t * K + j]] = 1;
+            }
+            moe_status_t r = run_group(layer, b, ids, g0, t, st);
+            if (r != MOE_OK) return r;
+            g0 = t;
+        }
+    }
+    return MOE_OK;
+}
+
 moe_status_t cache_finish_token(moe_layer* layer, hipStream_t st) {
     moe_cache* c = layer->cache;
     LayerSlots& L = *c->layers[c->pending_layer];
@@ -342,6 +457,8 @@ moe_status_t expert_cache_create(const moe_config_t* cfg, int n_layers, int slot
     c->expert_bytes = eb;
     c->copy_stream = static_cast<hipStream_t>(copy_stream);
     hipError_t err = hipHostMalloc(reinterpret_cast<void**>(&c->pinned_ids), sizeof(int32_t) * 32);
+    if (err == hipSuccess)
+        err = hipHostMalloc(reinterpret_cast<void**>(&c->pinned_batch), sizeof(int32_t) * kMaxDispatchEntries);
     if (err == hipSuccess) err = hipEventCreateWithFlags(&c->ids_ready, hipEventDisableTiming);
     for (int l = 0; l < n_layers && err == hipSuccess; ++l) {
         LayerSlots* L = new (std::nothrow) LayerSlots(cfg->n_experts, slots_per_layer);

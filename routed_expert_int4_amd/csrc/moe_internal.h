@@ -53,6 +53,11 @@ moe_status_t validate_supported(const moe_config_t* c);
 moe_status_t decode_tokens(moe_layer* L, uint8_t* ws, const WorkspaceLayout& W, const uint16_t* d_x, int T,
                            float* d_y, int32_t* ids_base, int ids_stride, float* w_base, int w_stride,
                            unsigned* fused_seq, hipStream_t s);
+// Kernel arguments of one token's decode launches, and of one batched launch
+// sequence over n tokens starting at x (outputs at ids / w / y).
+DecodeArgs decode_args(moe_layer* L, uint8_t* ws, const WorkspaceLayout& W, const uint16_t* x, int32_t* ids,
+                       float* w, float* y);
+BatchArgs batch_args(moe_layer* L, const uint16_t* x, int n, int32_t* ids, float* w, float* y);
 // MOE_EHIP if a fused launch of this layer reported a wait that gave up.
 moe_status_t check_layer_status(const moe_layer* L, const char* who);
 

@@ -190,6 +190,11 @@ hipError_t batch_gateup(const BatchArgs& a, hipStream_t st, const LaunchTiming& 
 hipError_t batch_hprep(const BatchArgs& a, hipStream_t st);
 hipError_t batch_down(const BatchArgs& a, hipStream_t st, const LaunchTiming& tm = {});
 hipError_t batch_combine(const BatchArgs& a, hipStream_t st);
+// Writes n (<= 256) expert blob pointers into a device table, in stream order.
+struct ExpertTable {
+    const uint8_t* p[256];
+};
+hipError_t batch_set_table(const ExpertTable& t, int n, const uint8_t** table, hipStream_t st);
 bool batch_shape_supported(int hidden, int inter);
 // The batched kernels serve this codec at this shape (int2: hidden a
 // multiple of 512 and inter of 256, a workgroup's stored rows being twice

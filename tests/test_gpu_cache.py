@@ -15,11 +15,15 @@ the C ABI:
   * copy/compute ordering with the minimum slot count (every token evicts
     experts the previous token read);
   * prefetch and evict semantics and their errors;
+  * batched calls (T > 1) behind the cache: outputs bit-identical to the
+    resident batched path, one lookup per distinct expert and token group,
+    the counts equal to the LRU replay of those groups;
   * speculative next-layer prefetch (the next layer's router on the current
     layer's input): outputs unchanged, the predictions equal to the oracle's
     routing, and every count equal to the oracle's prefetching replay; the
     copy/compute timeline sees every copy.
 """
+import dataclasses
 import sys
 
 import numpy as np
@@ -81,7 +85,7 @@ def test_cache_stack_parity_and_lru(torch_cuda, slots):
     x_bits = synth.gen_tokens(CFG, N_TOKENS, seed=30)
     for l in range(N_LAYERS):
         x = DeviceLayer.to_device_bf16(x_bits)
-        y, ids, w = cached[l].forward(x)
+        y, ids, w = cached[l].forward_each(x)
         y_res, ids_res, w_res = resident[l].forward_each(x)
         torch.cuda.synchronize()
         yh, idh, wh = y.cpu().numpy(), ids.cpu().numpy(), w.cpu().numpy()
@@ -165,7 +169,7 @@ def test_cache_learning_autopin(torch_cuda):
     say(f"[gpu] learning cache: {slots} slots, autopin {n_pin}")
     cache, weights, cached, resident = make_stack(torch, slots, n_layers=1)
     x1 = synth.gen_tokens(CFG, N_TOKENS, seed=50)
-    _, ids1, _ = cached[0].forward(DeviceLayer.to_device_bf16(x1))
+    _, ids1, _ = cached[0].forward_each(DeviceLayer.to_device_bf16(x1))
     torch.cuda.synchronize()
     trace1 = ids1.cpu().numpy()
     counts = cache.usage(0)
@@ -180,7 +184,7 @@ def test_cache_learning_autopin(torch_cuda):
     assert st0["pinned"] == n_pin
     x2 = synth.gen_tokens(CFG, N_TOKENS, seed=51)
     x = DeviceLayer.to_device_bf16(x2)
-    y, ids, w = cached[0].forward(x)
+    y, ids, w = cached[0].forward_each(x)
     y_res, ids_res, w_res = resident[0].forward_each(x)
     torch.cuda.synchronize()
     idh = ids.cpu().numpy()
@@ -223,7 +227,7 @@ def test_cache_top_p(torch_cuda):
     cache, weights, cached, resident = make_stack(torch, slots, n_layers=1, cfg=cfg)
     x_bits = synth.gen_tokens(cfg, N_TOKENS, seed=60)
     x = DeviceLayer.to_device_bf16(x_bits)
-    y, ids, w = cached[0].forward(x)
+    y, ids, w = cached[0].forward_each(x)
     y_res, ids_res, w_res = resident[0].forward_each(x)
     torch.cuda.synchronize()
     idh = ids.cpu().numpy()
@@ -257,7 +261,7 @@ def test_cache_other_codecs(torch_cuda, codec):
     assert cache.nb == cfg.expert_bytes()
     x_bits = synth.gen_tokens(cfg, N_TOKENS, seed=70)
     x = DeviceLayer.to_device_bf16(x_bits)
-    y, ids, w = cached[0].forward(x)
+    y, ids, w = cached[0].forward_each(x)
     y_res, ids_res, w_res = resident[0].forward_each(x)
     torch.cuda.synchronize()
     assert torch.equal(ids, ids_res) and torch.equal(w, w_res) and torch.equal(y, y_res)
@@ -310,7 +314,7 @@ def test_glm_cache_stack_parity_and_lru(torch_cuda, slots):
     x_bits = synth.gen_tokens(synth.GLM, n_tok, seed=300)
     noise = synth.gen_noise(synth.GLM, n_tok * n_layers, seed=400, std=0.1)
     for l in range(n_layers):
-        y, ids, w = layers[l].forward(DeviceLayer.to_device_bf16(x_bits))
+        y, ids, w = layers[l].forward_each(DeviceLayer.to_device_bf16(x_bits))
         torch.cuda.synchronize()
         yh, idh, wh = y.cpu().numpy(), ids.cpu().numpy(), w.cpu().numpy()
         res = check_layer(weights[l], x_bits, yh, idh, wh)
@@ -446,3 +450,97 @@ def test_cache_prefetch_link_errors_and_timeline_limit(torch_cuda):
         lay.close()
     cache.close()
     other.close()
+
+
+def token_groups(ids, slots, pinned):
+    """The consecutive token groups of a batched call behind the cache: as
+    many tokens as fit, in order, while the group's distinct experts that are
+    not pinned number at most slots - len(pinned); each group is looked up as
+    its distinct experts in ascending order."""
+    pinned, room = set(int(e) for e in pinned), slots - len(pinned)
+    groups, g0, n = [], 0, len(ids)
+    while g0 < n:
+        seen, used, t = set(), 0, g0
+        while t < n:
+            row = [int(e) for e in ids[t] if e >= 0]
+            add = len({e for e in row if e not in seen and e not in pinned})
+            if t > g0 and used + add > room:
+                break
+            used += add
+            seen.update(row)
+            t += 1
+        groups.append(sorted(seen))
+        g0 = t
+    return groups
+
+
+@pytest.mark.parametrize("slots,n_pin,top_p", [(64, 0, 1.0), (16, 0, 1.0), (12, 4, 1.0), (16, 0, 0.6)])
+def test_cache_batched_call(torch_cuda, slots, n_pin, top_p):
+    torch = torch_cuda
+    from routed_expert_int4_amd.layer import DeviceLayer
+    cfg = dataclasses.replace(CFG, top_p=top_p)
+    T = 40
+    say(f"[gpu] batched call behind the cache: {slots} slots, {n_pin} pinned, top-p {top_p}, T={T}")
+    cache, weights, cached, resident = make_stack(torch, slots, n_layers=1, max_T=T, cfg=cfg)
+    x_bits = synth.gen_tokens(cfg, T, seed=39)
+    x = DeviceLayer.to_device_bf16(x_bits)
+    y_r, ids_r, w_r = resident[0].forward(x)
+    torch.cuda.synchronize()
+    idh = ids_r.cpu().numpy()
+    pins = lru.hottest(lru.usage(idh, cfg.n_experts), n_pin)
+    if pins:
+        cache.pin(0, pins)
+    for call in range(2):  # the second call finds the last group's experts resident
+        y, ids, w = cached[0].forward(x)
+        torch.cuda.synchronize()
+        assert torch.equal(ids, ids_r) and torch.equal(w, w_r), "routing differs from the resident batched path"
+        assert torch.equal(y, y_r), "outputs differ from the resident batched path"
+    res = check_layer(weights[0], x_bits, y.cpu().numpy(), idh, w.cpu().numpy())
+    groups = token_groups(idh, slots, pins)
+    hits, misses, evictions = lru.replay(groups + groups, slots, pinned=pins)
+    st = cache.stats(0)
+    say(f"[gpu] {len(groups)} groups, rel err {res['worst_rel']:.3g}, stats {st}, replay {(hits, misses, evictions)}")
+    assert (st["hits"], st["misses"], st["evictions"]) == (hits, misses, evictions)
+    assert st["h2d_bytes"] == (misses + len(pins)) * cache.nb
+    assert list(cache.usage(0)) == lru.usage(np.concatenate([idh, idh]), cfg.n_experts)
+    if slots < cfg.n_experts and top_p == 1.0:
+        assert len(groups) > 1, "the call should need several groups"
+    for lay in cached + resident:
+        lay.close()
+    cache.close()
+
+
+def test_glm_cache_batched_call(torch_cuda):
+    """A 32-token call of the GLM-shaped layer with the Zipf(1.1) bias behind
+    a 64-slot cache (about 90 distinct experts per call, so several token
+    groups): outputs bit-identical to the resident batched path, sampled
+    tokens against the oracle, counts equal to the LRU replay of the groups."""
+    torch = torch_cuda
+    from routed_expert_int4_amd.layer import DeviceLayer, ExpertCache, HostExpertStore
+    from tests.helpers import zipf_glm_weights
+    slots, T = 64, 32
+    say(f"[gpu] GLM batched call behind a {slots}-slot cache, T={T}")
+    weights, _ = zipf_glm_weights()
+    cache = ExpertCache(synth.GLM, 1, slots)
+    cache.register(0, HostExpertStore(weights))
+    cached = DeviceLayer(weights, max_T=T, resident=False)
+    cached.attach_cache(cache, 0)
+    resident = DeviceLayer(weights, max_T=T)
+    x_bits = synth.gen_tokens(synth.GLM, T, seed=4)
+    x = DeviceLayer.to_device_bf16(x_bits)
+    y_r, ids_r, w_r = resident.forward(x)
+    y, ids, w = cached.forward(x)
+    torch.cuda.synchronize()
+    assert torch.equal(ids, ids_r) and torch.equal(w, w_r) and torch.equal(y, y_r)
+    idh = ids.cpu().numpy()
+    res = check_layer(weights, x_bits, y.cpu().numpy(), idh, w.cpu().numpy(), rows=[0, 9, 31])
+    groups = token_groups(idh, slots, [])
+    st = cache.stats(0)
+    say(f"[gpu] GLM batched cache: {len(groups)} groups of {[len(g) for g in groups]} experts, "
+        f"rel err {res['worst_rel']:.3g}, stats {st}")
+    assert len(groups) > 1
+    assert (st["hits"], st["misses"], st["evictions"]) == lru.replay(groups, slots)
+    assert st["h2d_bytes"] == st["misses"] * cache.nb
+    cached.close()
+    resident.close()
+    cache.close()

@@ -16,16 +16,19 @@
 //      entries of one expert per tile; the shared expert's T tokens last);
 //   4. gate/up: grouped int4 GEMM per (tile, 128 rows) on the matrix cores
 //      (tiles of up to 32 entries when a call averages 8 or more per expert:
-//      two MFMA row blocks share each dequantised weight fragment);
+//      two MFMA row blocks share each dequantised weight fragment, and a
+//      workgroup of 16 waves covers 256 rows);
 //   5. h prep: h per entry as scaled fp16 hi + lo parts in MFMA order;
 //   6. down: grouped int4 GEMM per (tile, 256 output rows);
 //   7. combine: y = sum_j w_j d_j + d_shared in slot order (no atomics).
 //
 // Grouped GEMM scheme.  v_mfma_f32_16x16x32_f16 with the 16 tokens of a tile
 // as its A rows and 16 weight rows as its B columns; K = 32 is exactly one
-// scale group, so each MFMA's 16x16 result is scaled by the fp16 group scale
-// of its weight row and accumulated in fp32 (the int4 values enter the MFMA
-// exactly as fp16, the scale is applied in fp32: no rounding of weights).
+// scale group.  Int4 weights are dequantised in registers to fp16(code x
+// scale), one rounding of relative size at most 2^-11, and the MFMAs
+// accumulate over K in fp32.  The other codecs keep exact fragments (codes
+// as fp16 integers or E2M1 values) and scale each MFMA's 16x16 group result
+// by its row's group scale in fp32.
 // A lane of quarter q loads 16 contiguous code bytes (one group of one row);
 // a 4x4 exchange of dwords between the four quarters (permlane32/16 swaps)
 // turns the four loads of a quarter-row into the B fragments of four
@@ -168,6 +171,12 @@ __device__ __forceinline__ void transpose_quarters(u32x4& d) {
     d[1] = r01[1];
     d[2] = r23[0];
     d[3] = r23[1];
+}
+
+// The fp16 scale in the low 16 bits of v in all eight lanes of a fragment.
+__device__ __forceinline__ f16x8 splat_h8(unsigned v) {
+    const _Float16 s = __builtin_bit_cast(_Float16, (unsigned short)(v & 0xFFFFu));
+    return f16x8{s, s, s, s, s, s, s, s};
 }
 
 __device__ __forceinline__ f32x4 mfma16(f16x8 a, f16x8 b, f32x4 c) {
@@ -431,6 +440,21 @@ __global__ void __launch_bounds__(1024) batch_dispatch_kernel(BatchArgs a) {
     }
 }
 
+// ---------------------------------------------------------------- item order
+// Item k of workgroup b in the grouped kernels.  A launch's workgroups are
+// dealt to the chip's 8 XCDs round robin (workgroup b runs on XCD b % 8, each
+// XCD with an L2 of its own), so with a grid that is a multiple of 8 the item
+// range is cut into 8 consecutive parts and XCD x's workgroups walk part x in
+// order: the row blocks of one tile, which stage the same activations, then
+// run side by side on one XCD and read them through its L2 once, instead of
+// once on every XCD.  Returns a value >= items past the workgroup's last item.
+__device__ __forceinline__ int grouped_item(int b, int grid, int k, int items) {
+    if (grid & 7) return b + k * grid;
+    const int per = (items + 7) >> 3;
+    const int i = (b >> 3) + k * (grid >> 3);
+    return i < per ? (b & 7) * per + i : items;
+}
+
 // ---------------------------------------------------------------- gate/up
 // Gate and up scales of row r for groups g..g+3 as dwords (gate | up << 16).
 // (MXFP4: E8M0 bytes in the same 16-bit places.)
@@ -466,37 +490,45 @@ __device__ __forceinline__ u32x4 gateup_scales4(const uint8_t* gus, int r, int g
     }
 }
 
-// Workgroup = 8 waves over 128 rows of gate and the same 128 rows of up for
-// the (up to) 16 tokens of one tile; wave w owns rows 16w..16w+15.  Rows
+// Workgroup = W waves over 16 W rows of gate and the same rows of up for
+// the (up to) TT tokens of one tile; wave w owns rows 16w..16w+15.  Rows
 // are stored rows: with int2 (two rows per stored row) a workgroup covers
-// 256 matrix rows, with the even and the odd rows in accumulators of their
-// own.
-template <int KG, int F, int TT>
-__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) batch_gateup_kernel(BatchArgs a) {
+// twice as many matrix rows, with the even and the odd rows in accumulators
+// of their own.  W = 8 (two workgroups per CU), or 16 (one per CU) for
+// 32-entry tiles: a prefill item then stages its tile's activations once per
+// 256 rows instead of once per 128 (prefill gate/up 0.93 ms to 0.88 ms per
+// 512-token call); calls with few entries per expert keep 8 waves, whose
+// twice as many items balance better over the CUs.
+template <int KG, int F, int TT, int W>
+__global__ void __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(4))) batch_gateup_kernel(BatchArgs a) {
     // groups per LDS stage (8 when a 32-entry tile's two MFMA row blocks or
     // a two-fragment codec need the staging registers, else 16)
     static_assert(TT == 16 || TT == 32, "tile entries");
+    static_assert(W == 8 || W == 16, "waves per workgroup");
+    constexpr int NT = 64 * W;              // threads
     constexpr int NB = TT / 16;             // MFMA row blocks (16 tokens each) per tile
     constexpr int CK = KG < 16 ? KG : (NB > 1 || code_planes(F) > 1 || row_pack(F) > 1 ? 8 : 16);
     constexpr int NST = KG / CK;
-    constexpr int PT = CK * 64 * NB / 512;  // 16-byte staging elements per thread
-    static_assert(CK % 4 == 0 && KG % CK == 0 && PT >= 1, "gate/up stage shape");
+    constexpr int NX = CK * 64 * NB;        // 16-byte staging elements of a stage
+    constexpr int PT = (NX + NT - 1) / NT;  // per thread
+    static_assert(CK % 4 == 0 && KG % CK == 0, "gate/up stage shape");
     __shared__ u32x4 xs[2][CK * 64 * NB];   // [(g * 4 + q) * TT + token]
     const int tid = threadIdx.x, lane = tid & 63, wv = wave_in_block();
     const int i = lane & 15, q = lane >> 4;
     const int n_tiles = a.n_tiles[0];
     constexpr int RP = row_pack(F);
-    const int rblocks = a.I / (kBlockRows * RP);
+    const int rblocks = a.I / (16 * W * RP);
     const int items = n_tiles * rblocks;
     const BlobLayout L = blob_layout(a.H, a.I, F);
     const int row_bytes = a.H / 2;
     const MagicExp mg = magic_exponents();
     int gs = 0;  // stages so far: selects the LDS buffer
-    for (int item = blockIdx.x; item < items; item += gridDim.x) {
+    for (int ik = 0, item = grouped_item(blockIdx.x, gridDim.x, 0, items); item < items;
+         item = grouped_item(blockIdx.x, gridDim.x, ++ik, items)) {
         const int tile = item / rblocks, rb = item - tile * rblocks;
         const Tile td = a.tiles[tile];
         const uint8_t* blob = td.expert < a.E ? a.table[td.expert] : a.shared_blob;
-        const int row = rb * kBlockRows + wv * 16 + i;
+        const int row = rb * 16 * W + wv * 16 + i;
         const uint8_t* gq = blob + L.gate_q + (size_t)row * row_bytes;
         const uint8_t* uq = blob + L.up_q + (size_t)row * row_bytes;
         const uint8_t* gql = blob + L.gate_lo + (size_t)row * row_bytes;  // int8 low planes
@@ -534,8 +566,8 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) b
         auto stage_load = [&](int st, u32x4 (&v)[PT]) {
 #pragma unroll
             for (int r = 0; r < PT; ++r) {
-                const int e = tid + 512 * r;
-                v[r] = xsrc ? *as_global<u32x4>(xsrc + (size_t)((st * CK + e / (4 * TT)) * 4 +
+                const int e = tid + NT * r;
+                v[r] = xsrc && e < NX ? *as_global<u32x4>(xsrc + (size_t)((st * CK + e / (4 * TT)) * 4 +
                                                         (e / TT) % 4) * 8)
                             : u32x4{0u, 0u, 0u, 0u};
             }
@@ -557,7 +589,8 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) b
         for (int st = 0; st < NST; ++st, ++gs) {
             const int buf = gs & 1;
 #pragma unroll
-            for (int r = 0; r < PT; ++r) xs[buf][tid + 512 * r] = v[r];
+            for (int r = 0; r < PT; ++r)
+                if (tid + NT * r < NX) xs[buf][tid + NT * r] = v[r];
             __syncthreads();
             if (st + 1 < NST) stage_load(st + 1, v);
 #pragma unroll
@@ -587,6 +620,26 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) b
                     if (k + 2 < NSP) load_step(k + 2, cg2, cu2);
                     transpose_quarters(cg0);
                     transpose_quarters(cu0);
+                    if constexpr (F == kCodecInt4) {
+                        // int4: each weight enters the MFMA as fp16(code x
+                        // scale), one rounding (relative 2^-11), and the
+                        // products accumulate in the MFMA's fp32 accumulator
+#pragma unroll
+                        for (int m = 0; m < 4; ++m) {
+                            const unsigned sv = sc0[0][m];
+                            const f16x8 bg = codes_to_f16x8(cg0[m], mg) * splat_h8(sv);
+                            const f16x8 bu = codes_to_f16x8(cu0[m], mg) * splat_h8(sv >> 16);
+#pragma unroll
+                            for (int z = 0; z < NB; ++z) {
+                                const f16x8 af =
+                                    __builtin_bit_cast(f16x8, xs[buf][((4 * c + m) * 4 + q) * TT + 16 * z + i]);
+                                accg[0][z] = mfma16(af, bg, accg[0][z]);
+                                accu[0][z] = mfma16(af, bu, accu[0][z]);
+                            }
+                        }
+                    } else {
+                    // other codecs: exact fragments, each group's product
+                    // scaled in fp32
 #pragma unroll
                     for (int m = 0; m < 4; ++m) {
 #pragma unroll
@@ -614,6 +667,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) b
                                 __builtin_amdgcn_sched_barrier(0);
                             }
                         }
+                    }
                     }
                     cg0 = cg1;
                     cu0 = cu1;
@@ -722,7 +776,8 @@ __global__ void __launch_bounds__(kDownThreads) __attribute__((amdgpu_waves_per_
     const int row_bytes = a.I / 2;
     const MagicExp mg = magic_exponents();
     int gs = 0;
-    for (int item = blockIdx.x; item < items; item += gridDim.x) {
+    for (int ik = 0, item = grouped_item(blockIdx.x, gridDim.x, 0, items); item < items;
+         item = grouped_item(blockIdx.x, gridDim.x, ++ik, items)) {
         const int tile = item / rblocks, rb = item - tile * rblocks;
         const Tile td = a.tiles[tile];
         const uint8_t* blob = td.expert < a.E ? a.table[td.expert] : a.shared_blob;
@@ -794,6 +849,20 @@ __global__ void __launch_bounds__(kDownThreads) __attribute__((amdgpu_waves_per_
                     u32x4 cd2 = cd1, sc2 = sc1;
                     if (k + 2 < NSP) load_step(k + 2, cd2, sc2);
                     transpose_quarters(cd0);
+                    if constexpr (F == kCodecInt4) {
+                        // int4: fp16(code x scale) fragments, as in gate/up
+#pragma unroll
+                        for (int m = 0; m < 4; ++m) {
+                            const f16x8 bw = codes_to_f16x8(cd0[m], mg) * splat_h8(sc0[m]);
+#pragma unroll
+                            for (int z = 0; z < NB; ++z) {
+                                const int slot = ((4 * c + m) * 4 + q) * TT + 16 * z + i;
+                                const f16x8 ah = __builtin_bit_cast(f16x8, hs[buf][slot]);
+                                const f16x8 al = __builtin_bit_cast(f16x8, hs[buf][PART + slot]);
+                                acc[0][z] = mfma16(al, bw, mfma16(ah, bw, acc[0][z]));
+                            }
+                        }
+                    } else {
 #pragma unroll
                     for (int m = 0; m < 4; ++m) {
 #pragma unroll
@@ -812,6 +881,7 @@ __global__ void __launch_bounds__(kDownThreads) __attribute__((amdgpu_waves_per_
                                 __builtin_amdgcn_sched_barrier(0);
                             }
                         }
+                    }
                     }
                     cd0 = cd1;
                     sc0 = sc1;
@@ -903,13 +973,25 @@ int grouped_grid(const BatchArgs& a, int rblocks) {
 
 template <int KG, int TT>
 hipError_t launch_gateup_t(const BatchArgs& a, hipStream_t st, const LaunchTiming& tm) {
+    if constexpr (TT == 32) {
+        if (a.I % (16 * 16 * row_pack(a.codec)) == 0) {
+            // 16 waves over 256 rows, one workgroup per CU
+            const int g = grouped_grid(a, a.I / (16 * 16 * row_pack(a.codec)));
+            const dim3 grid(g < kGroupedGrid / 2 ? g : kGroupedGrid / 2);
+            if (a.codec == kCodecMxfp4)
+                return launch_timed(batch_gateup_kernel<KG, kCodecMxfp4, TT, 16>, grid, dim3(1024), st, tm, a);
+            if (a.codec == kCodecInt4)
+                return launch_timed(batch_gateup_kernel<KG, kCodecInt4, TT, 16>, grid, dim3(1024), st, tm, a);
+            return hipErrorInvalidValue;
+        }
+    }
     const dim3 grid(grouped_grid(a, a.I / (kBlockRows * row_pack(a.codec))));
-    if (a.codec == kCodecMxfp4) return launch_timed(batch_gateup_kernel<KG, kCodecMxfp4, TT>, grid, dim3(512), st, tm, a);
-    if (a.codec == kCodecInt4) return launch_timed(batch_gateup_kernel<KG, kCodecInt4, TT>, grid, dim3(512), st, tm, a);
+    if (a.codec == kCodecMxfp4) return launch_timed(batch_gateup_kernel<KG, kCodecMxfp4, TT, 8>, grid, dim3(512), st, tm, a);
+    if (a.codec == kCodecInt4) return launch_timed(batch_gateup_kernel<KG, kCodecInt4, TT, 8>, grid, dim3(512), st, tm, a);
     if (TT == 16 && a.codec == kCodecInt8)
-        return launch_timed(batch_gateup_kernel<KG, kCodecInt8, 16>, grid, dim3(512), st, tm, a);
+        return launch_timed(batch_gateup_kernel<KG, kCodecInt8, 16, 8>, grid, dim3(512), st, tm, a);
     if (TT == 16 && a.codec == kCodecInt2)
-        return launch_timed(batch_gateup_kernel<KG, kCodecInt2, 16>, grid, dim3(512), st, tm, a);
+        return launch_timed(batch_gateup_kernel<KG, kCodecInt2, 16, 8>, grid, dim3(512), st, tm, a);
     return hipErrorInvalidValue;
 }
 

@@ -36,6 +36,13 @@ def log(msg: str) -> None:
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "gateup_kernel_glm_decode_traffic.md")
 KERNEL_SOURCES = [os.path.join(ROOT, "routed_expert_int4_amd", "csrc", f)
                   for f in ("moe_decode.hip", "moe_device.h", "moe_kernels.h", "moe_layout.h")]
+# Counter records of the grouped gate/up kernel per batched workload: HBM
+# traffic (FETCH_SIZE / WRITE_SIZE) and matrix-core work (MFMA ops and busy
+# cycles)
+BATCH_TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "batched_kernels_glm_hbm_counters.md")
+BATCH_MFMA_RECORD = os.path.join(ROOT, "profiles", "batched_kernels_glm_mfma_counters.md")
+BATCH_KERNEL_SOURCES = [os.path.join(ROOT, "routed_expert_int4_amd", "csrc", f)
+                        for f in ("moe_batch.hip", "moe_device.h", "moe_kernels.h", "moe_layout.h")]
 
 
 DTYPES = {
@@ -77,13 +84,31 @@ def algorithmic_bytes(cfg):
     }
 
 
-def source_digest() -> str:
+def source_digest(sources=None) -> str:
     import hashlib
     h = hashlib.sha256()
-    for path in KERNEL_SOURCES:
+    for path in sources or KERNEL_SOURCES:
         with open(path, "rb") as f:
             h.update(f.read())
     return h.hexdigest()
+
+
+def read_record(path, tag, sources, **match):
+    """The last `tag:` JSON line of a committed counter record whose fields
+    equal match, or None when there is none or the kernel sources' digest
+    differs from the one the counters were taken on."""
+    if not os.path.exists(path):
+        return None
+    rec = None
+    with open(path) as f:
+        for line in f:
+            if line.startswith(tag + ":"):
+                r = json.loads(line.split(":", 1)[1])
+                if all(r.get(k) == v for k, v in match.items()):
+                    rec = r
+    if not rec or rec.get("source_sha256") != source_digest(sources):
+        return None
+    return rec
 
 
 def measured_traffic():
@@ -95,17 +120,8 @@ def measured_traffic():
     and the digest of the kernel sources they were taken on.  Returns None
     when there is no record or the kernel source has changed since.
     """
-    path = TRAFFIC_RECORD
-    if not os.path.exists(path):
-        return None
-    rec = None
-    with open(path) as f:
-        for line in f:
-            if line.startswith("traffic-record:"):
-                rec = json.loads(line.split(":", 1)[1])
-    if not rec or rec.get("source_sha256") != source_digest():
-        return None
-    return int(rec["hbm_bytes_per_launch"])
+    rec = read_record(TRAFFIC_RECORD, "traffic-record", KERNEL_SOURCES)
+    return int(rec["hbm_bytes_per_launch"]) if rec else None
 
 
 def time_oracle(weights, sample):
@@ -458,18 +474,22 @@ def bench_probes(args) -> int:
         del src, dst
     # read-only streaming (the library's probe kernel) at the decode launches'
     # sizes (56.6 MB down, 113 MB routed gate/up, 197 MB one layer-token) and
-    # 1 GiB; best over workgroup counts of 1 to 16 per CU
+    # 1 GiB; best over workgroup counts of 1 to 16 per CU and one workgroup
+    # per 32 KiB tile (one pass)
     n_cu = torch.cuda.get_device_properties(0).multi_processor_count
     read_only = {}
     for label, nbytes in (("56MB", 56_623_104), ("113MB", 113_246_208), ("197MB", 197_432_320), ("1GiB", 1 << 30)):
         buf = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
-        sink = torch.empty(16 * n_cu, dtype=torch.int32, device=dev)
+        one_pass = (nbytes + 32767) // 32768  # one workgroup per 32 KiB tile
+        sink = torch.empty(max(16 * n_cu, one_pass), dtype=torch.int32, device=dev)
         best = None
-        for per_cu in (1, 2, 4, 8, 16):
-            ms = best_ms(lambda: B.moe_hbm_read_probe(buf, nbytes, sink, per_cu * n_cu))
+        for per_cu in (1, 2, 4, 8, 16, "one pass"):
+            blocks = one_pass if per_cu == "one pass" else per_cu * n_cu
+            ms = best_ms(lambda: B.moe_hbm_read_probe(buf, nbytes, sink, blocks))
             if best is None or ms < best[0]:
                 best = (ms, per_cu)
-        read_only[label] = {"gbs": round(nbytes / (best[0] / 1e3) / 1e9, 1), "workgroups_per_cu": best[1]}
+        read_only[label] = {"gbs": round(nbytes / (best[0] / 1e3) / 1e9, 1), "workgroups_per_cu": best[1],
+                            "us": round(best[0] * 1e3, 2)}
         del buf, sink
     host = torch.empty(256 << 20, dtype=torch.uint8, pin_memory=True)
     devb = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
@@ -588,6 +608,21 @@ def bench_batched(args) -> int:
         f"stages ms {stage_ms}; grouped gate/up {1e3 * gu_ms / kn[4]:.1f} us x {kn[4]} ({gu_gbs:.0f} GB/s), "
         f"down {1e3 * dn_ms / kn[5]:.1f} us x {kn[5]} ({dn_gbs:.0f} GB/s); distinct experts per call "
         f"{min(distinct)}..{max(distinct)}")
+    # counter records of this workload's grouped gate/up kernel (int4, plain
+    # top-k), taken on the current kernel sources
+    traffic, mfma = None, None
+    if cfg.codec == "int4" and cfg.top_p >= 1.0:
+        rec = read_record(BATCH_TRAFFIC_RECORD, "traffic-record", BATCH_KERNEL_SOURCES, workload=args.workload)
+        if rec:
+            traffic = int(rec["hbm_bytes_per_launch"])
+        rec = read_record(BATCH_MFMA_RECORD, "mfma-record", BATCH_KERNEL_SOURCES, workload=args.workload)
+        if rec:
+            # matrix-core work the counters saw (zero-padded tile rows
+            # included) over the bench's own launch time, and the MFMA
+            # units' busy fraction over the launch
+            mfma = {"flops_per_launch": rec["mfma_flops_per_dispatch"],
+                    "tflops": round(rec["mfma_flops_per_dispatch"] / (gu_ms / kn[4] / 1e3) / 1e12, 2),
+                    "busy_frac": rec["mfma_busy_frac"]}
     cpu = None
     if args.cpu_sample > 0:
         n = min(args.cpu_sample, 256)
@@ -637,11 +672,12 @@ def bench_batched(args) -> int:
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(gu_gbs / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": traffic,
             "bytes_per_launch": int(round(gu_bytes / kn[4])),
             "avg_launch_us": round(1e3 * gu_ms / kn[4], 3),
             "mfma_tflops": round(gu_tf, 2),
             "mfma_frac_of_fp16_dense_peak": round(gu_tf / 2500.0, 4),
+            "mfma_counters": mfma,
         },
         "cpu_baseline": cpu,
     }

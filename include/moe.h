@@ -184,7 +184,12 @@ moe_status_t moe_router_topk(moe_layer_t* layer, const uint16_t* d_x, int T, int
  * cores, and the combine; tokens are taken in launch sequences of at most
  * min(max_T, 8192 / top_k).  Int2 layers take that path where hidden is a
  * multiple of 512 and inter of 256; other int2 T > 1 calls run the decode
- * kernels token by token.
+ * kernels token by token.  Numerics of the batched int4 calls: each weight
+ * enters the matrix cores as fp16(code x scale), one rounding of at most
+ * 2^-11 of itself, accumulated in fp32; this assumes every int4 group scale
+ * lies in [2^-14, 2^12] (below, small codes give fp16 subnormals with fewer
+ * bits; above, 8 x scale overflows fp16).  One-token calls and the other
+ * codecs have no such range limit.
  * With all experts resident the call is asynchronous.  With an attached
  * expert cache the call blocks the host until the routing is known, issues
  * the copies of missing experts on the cache's copy stream and orders the
@@ -221,8 +226,12 @@ moe_status_t moe_layer_forward_noalloc(moe_layer_t* layer, const uint16_t* d_x, 
  * repository, fr.news.hada.io topic 31297, "Structure du depot et
  * licence"): one launch of `blocks` workgroups of 256 threads reads the
  * `bytes` (a multiple of 16, 16-byte aligned) at d_buf once with
- * non-temporal 16-byte loads and writes one word per workgroup to d_sink
- * (device, `blocks` words).  Asynchronous on stream; time it with events. */
+ * non-temporal 16-byte loads, in tiles of 32 KiB taken by the workgroups in
+ * turn (each thread holds 8 loads of a tile in flight; blocks = bytes / 32 KiB
+ * rounded up reads the buffer in one pass), and writes one word per
+ * workgroup to d_sink (device, `blocks` words).  Asynchronous on stream;
+ * time it with events.  Errors: MOE_EINVAL for a NULL pointer, a size or
+ * address that is not a multiple of 16, or blocks < 1. */
 moe_status_t moe_hbm_read_probe(const void* d_buf, size_t bytes, unsigned* d_sink, int blocks, void* stream);
 
 /* moe_dispatch: the batch-union dispatch of a routing d_ids int32 [T][top_k]

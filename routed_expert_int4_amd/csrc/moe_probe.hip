@@ -1,10 +1,13 @@
 // Read-only HBM streaming probe: the device's read ceiling that the layer's
 // streaming kernels are measured against (the analogue of the disk read
 // benchmark the colibri repository ships, fr.news.hada.io topic 31297,
-// "Structure du depot et licence").  Every lane reads 16-byte chunks with
-// non-temporal loads in a grid-stride loop, four chunks in flight, and folds
-// them into one word so that no load is dead; one word per workgroup is
-// written to the sink.
+// "Structure du depot et licence").  The buffer is cut into tiles of 32 KiB
+// (256 threads x 8 chunks of 16 bytes); a workgroup takes tiles b, b + grid,
+// ...  and each thread issues all 8 non-temporal loads of a tile before it
+// uses any (a wave load covers 1 KiB of contiguous bytes, as in the decode
+// kernels), folding them into one word so that no load is dead; one word per
+// workgroup is written to the sink.  A grid of one workgroup per tile reads
+// the buffer in one pass.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -18,19 +21,19 @@ namespace {
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 __global__ void __launch_bounds__(256) hbm_read_kernel(const u32x4* __restrict__ src, size_t n16, unsigned* sink) {
-    const size_t stride = (size_t)gridDim.x * blockDim.x;
-    size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    constexpr int U = 8;  // chunks in flight per thread
+    const size_t n_tiles = (n16 + 256 * U - 1) / (256 * U);
     unsigned acc = 0u;
-    for (; i + 3 * stride < n16; i += 4 * stride) {
-        const u32x4 a = __builtin_nontemporal_load(src + i);
-        const u32x4 b = __builtin_nontemporal_load(src + i + stride);
-        const u32x4 c = __builtin_nontemporal_load(src + i + 2 * stride);
-        const u32x4 d = __builtin_nontemporal_load(src + i + 3 * stride);
-        acc ^= (a.x ^ a.y ^ a.z ^ a.w) ^ (b.x ^ b.y ^ b.z ^ b.w) ^ (c.x ^ c.y ^ c.z ^ c.w) ^ (d.x ^ d.y ^ d.z ^ d.w);
-    }
-    for (; i < n16; i += stride) {
-        const u32x4 a = __builtin_nontemporal_load(src + i);
-        acc ^= a.x ^ a.y ^ a.z ^ a.w;
+    for (size_t t = blockIdx.x; t < n_tiles; t += gridDim.x) {
+        const size_t base = t * 256 * U + threadIdx.x;
+        u32x4 v[U];
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            const size_t i = base + (size_t)k * 256;
+            v[k] = i < n16 ? __builtin_nontemporal_load(src + i) : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int k = 0; k < U; ++k) acc ^= v[k].x ^ v[k].y ^ v[k].z ^ v[k].w;
     }
     __shared__ unsigned part[256];
     part[threadIdx.x] = acc;

@@ -42,7 +42,7 @@ KERNEL_SOURCES = [os.path.join(ROOT, "routed_expert_int4_amd", "csrc", f)
 BATCH_TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "batched_kernels_glm_hbm_counters.md")
 BATCH_MFMA_RECORD = os.path.join(ROOT, "profiles", "batched_kernels_glm_mfma_counters.md")
 BATCH_KERNEL_SOURCES = [os.path.join(ROOT, "routed_expert_int4_amd", "csrc", f)
-                        for f in ("moe_batch.hip", "moe_device.h", "moe_kernels.h", "moe_layout.h")]
+                        for f in ("moe_batch.hip", "moe_decode.hip", "moe_device.h", "moe_kernels.h", "moe_layout.h")]
 
 
 DTYPES = {
@@ -573,6 +573,9 @@ def bench_batched(args) -> int:
     ids_h = ids.cpu().numpy().reshape(n_calls, T, k)
     # (id -1: a choice the top-p cut dropped; it is neither read nor computed)
     distinct = [len(np.unique(ids_h[c][ids_h[c] >= 0])) for c in range(n_calls)]
+    single_max = 1 if T * k < 8 * cfg.n_experts or cfg.codec in ("int8", "int2") else 0
+    singles = [int((np.unique(ids_h[c][ids_h[c] >= 0], return_counts=True)[1] <= single_max).sum())
+               for c in range(n_calls)]
     eb = cfg.expert_bytes()
     router = cfg.n_experts * cfg.hidden * 4 + cfg.n_experts * 4
     bytes_step = sum(router + (d + cfg.n_shared) * eb + T * H * 6 for d in distinct)
@@ -589,7 +592,9 @@ def bench_batched(args) -> int:
     kms, kn = B.moe_layer_profile_read(layer.handle)
     B.moe_layer_profile(layer.handle, False)
     stage_ms = [kms[i] for i in range(3)]
-    gu_ms, dn_ms = kms[4], kms[5]
+    # per call: the grouped MFMA kernel plus, in calls with 16-entry tiles,
+    # the GEMV kernel of the experts with a single entry
+    gu_ms, dn_ms = kms[4] + kms[6], kms[5] + kms[7]
     # algorithmic bytes of the two grouped kernels per step: the distinct
     # routed experts' and the shared expert's weights once per call, plus the
     # activations they read and the results they write
@@ -661,12 +666,18 @@ def bench_batched(args) -> int:
                               "down_combine": round(stage_ms[2], 4)},
         "grouped_kernels": {
             "gateup": {"avg_launch_us": round(1e3 * gu_ms / kn[4], 3), "launches_per_step": kn[4],
-                       "bytes_per_step": gu_bytes, "gbs": round(gu_gbs, 1), "tflops": round(gu_tf, 2)},
+                       "bytes_per_step": gu_bytes, "gbs": round(gu_gbs, 1), "tflops": round(gu_tf, 2),
+                       "mfma_kernel_us": round(1e3 * kms[4] / kn[4], 3),
+                       "single_entry_gemv_us": round(1e3 * kms[6] / kn[6], 3) if kn[6] else None},
             "down": {"avg_launch_us": round(1e3 * dn_ms / kn[5], 3), "launches_per_step": kn[5],
-                     "bytes_per_step": dn_bytes, "gbs": round(dn_gbs, 1), "tflops": round(dn_tf, 2)},
+                     "bytes_per_step": dn_bytes, "gbs": round(dn_gbs, 1), "tflops": round(dn_tf, 2),
+                     "mfma_kernel_us": round(1e3 * kms[5] / kn[5], 3),
+                     "single_entry_gemv_us": round(1e3 * kms[7] / kn[7], 3) if kn[7] else None},
+            "single_entry_experts_per_call": round(float(np.mean(singles)), 2),
         },
         "roofline": {
-            "kernel": "grouped gate/up + SwiGLU (batch_gateup_kernel)",
+            "kernel": "grouped gate/up + SwiGLU per call (batch_gateup_kernel, plus pair_gateup_kernel for the "
+                      "experts with a single entry in calls with 16-entry tiles)",
             "bound": "hbm",
             "achieved": round(gu_gbs, 1),
             "peak": HBM_PEAK_GBS,

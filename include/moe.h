@@ -274,16 +274,18 @@ moe_status_t moe_layer_set_decode(moe_layer_t* layer, int launches, unsigned spi
  * attached cache, whose events span the top-k launch, the wait for the
  * routing, the copies' ordering and the gate/up launches.
  * T > 1 calls on the batched kernels record kinds 0-2 as spans of their
- * stages and stamp the two grouped kernels themselves as kinds 4 and 5.
+ * stages and stamp the two grouped kernels themselves as kinds 4 and 5, and
+ * the GEMV kernels of the experts with a single entry as kinds 6 and 7.
  * moe_layer_profile_read synchronises on the recorded events and returns,
  * per kind (0 router, or the batched routing + dispatch; 1 gate/up + SwiGLU
  * of the shared and routed experts, or the batched grouped gate/up + h
  * preparation; 2 down + combine, or the batched grouped down + combine; 3
  * fused one-token launch; 4 batched grouped gate/up kernel; 5 batched
- * grouped down kernel), the summed duration in milliseconds and the number
- * of launches since profiling was enabled; arrays of 6 entries.  Timings
- * taken with profiling enabled are per-kernel durations, not end-to-end
- * throughput. */
+ * grouped down kernel; 6 batched gate/up of single-entry experts; 7 batched
+ * down of single-entry experts), the summed duration in milliseconds and
+ * the number of launches since profiling was enabled; arrays of 8 entries.
+ * Timings taken with profiling enabled are per-kernel durations, not
+ * end-to-end throughput. */
 moe_status_t moe_layer_profile(moe_layer_t* layer, int enable);
 moe_status_t moe_layer_profile_read(moe_layer_t* layer, double* total_ms, uint64_t* launches);
 

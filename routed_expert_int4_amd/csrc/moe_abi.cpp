@@ -123,6 +123,8 @@ WorkspaceLayout workspace_layout(const moe_config_t* c, int max_T) {
         take(W.b_n_distinct, sizeof(int32_t));
         take(W.b_tiles, sizeof(Tile) * (size_t)batch_max_tiles(tb, c->top_k, c->n_experts, c->n_shared));
         take(W.b_n_tiles, sizeof(int32_t));
+        take(W.b_singles, sizeof(Tile) * (n < E ? n : E));
+        take(W.b_n_singles, sizeof(int32_t));
         take(W.b_h, sizeof(float) * P * I);
         take(W.b_ha_hi, 2 * P * I);
         take(W.b_ha_lo, 2 * P * I);
@@ -472,6 +474,8 @@ BatchArgs batch_args(moe_layer_t* L, const uint16_t* x, int n, int32_t* ids, flo
     b.n_distinct = reinterpret_cast<int32_t*>(ws + W.b_n_distinct);
     b.tiles = reinterpret_cast<Tile*>(ws + W.b_tiles);
     b.n_tiles = reinterpret_cast<int32_t*>(ws + W.b_n_tiles);
+    b.singles = reinterpret_cast<Tile*>(ws + W.b_singles);
+    b.n_singles = reinterpret_cast<int32_t*>(ws + W.b_n_singles);
     b.h = reinterpret_cast<float*>(ws + W.b_h);
     b.ha_hi = reinterpret_cast<uint16_t*>(ws + W.b_ha_hi);
     b.ha_lo = reinterpret_cast<uint16_t*>(ws + W.b_ha_lo);
@@ -492,6 +496,7 @@ BatchArgs batch_args(moe_layer_t* L, const uint16_t* x, int n, int32_t* ids, flo
     b.top_p = c.top_p;
     b.codec = c.codec;
     b.tile_tokens = batch_tile_tokens(c.codec, n, c.top_k, c.n_experts);
+    b.single_max = batch_single_max(b.tile_tokens);
     return b;
 }
 
@@ -572,6 +577,10 @@ moe_status_t moe_layer_forward(moe_layer_t* layer, const uint16_t* d_x, int T, f
                 ProfileScope k4(layer, 4, s, ProfileScope::kKernel);
                 e = batch_gateup(b, s, k4.timing());
             }
+            if (e == hipSuccess && b.single_max > 0) {
+                ProfileScope k6(layer, 6, s, ProfileScope::kKernel);
+                e = batch_pair_gateup(b, s, k6.timing());
+            }
             if (e == hipSuccess) e = batch_hprep(b, s);
             if (e != hipSuccess) return hip_fail(e, "batched gate/up launch");
             p1.end();
@@ -579,6 +588,10 @@ moe_status_t moe_layer_forward(moe_layer_t* layer, const uint16_t* d_x, int T, f
             {
                 ProfileScope k5(layer, 5, s, ProfileScope::kKernel);
                 e = batch_down(b, s, k5.timing());
+            }
+            if (e == hipSuccess && b.single_max > 0) {
+                ProfileScope k7(layer, 7, s, ProfileScope::kKernel);
+                e = batch_pair_down(b, s, k7.timing());
             }
             if (e == hipSuccess) e = batch_combine(b, s);
             if (e != hipSuccess) return hip_fail(e, "batched down/combine launch");

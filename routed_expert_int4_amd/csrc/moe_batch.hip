@@ -339,8 +339,8 @@ __device__ __forceinline__ int wave_exclusive_scan(int v, int lane, int* total) 
 // sort gives the stable order by expert, then token, then slot.
 __global__ void __launch_bounds__(1024) batch_dispatch_kernel(BatchArgs a) {
     __shared__ unsigned keys[kMaxDispatchEntries];
-    __shared__ int cnt[256], off[256], toff[256], dpos[256];
-    __shared__ int totals[3];
+    __shared__ int cnt[256], off[256], toff[256], dpos[256], spos[256];
+    __shared__ int totals[4];
     const int tid = threadIdx.x;
     const int n = a.T * a.K;
     int n2 = kWave;
@@ -370,22 +370,27 @@ __global__ void __launch_bounds__(1024) batch_dispatch_kernel(BatchArgs a) {
     }
     __syncthreads();
     if (tid < kWave) {
-        int c[4], nt[4], f[4];
-        int sc = 0, stl = 0, sf = 0;
+        // per expert: entries, MFMA tiles (none for a single), distinct
+        // flag, single flag (1 to single_max entries: the GEMV path)
+        int c[4], nt[4], f[4], g[4];
+        int sc = 0, stl = 0, sf = 0, sg = 0;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int e = 4 * tid + r;
             c[r] = e < a.E ? cnt[e] : 0;
-            nt[r] = (c[r] + a.tile_tokens - 1) / a.tile_tokens;
+            g[r] = c[r] > 0 && c[r] <= a.single_max ? 1 : 0;
+            nt[r] = g[r] ? 0 : (c[r] + a.tile_tokens - 1) / a.tile_tokens;
             f[r] = c[r] > 0 ? 1 : 0;
             sc += c[r];
             stl += nt[r];
             sf += f[r];
+            sg += g[r];
         }
-        int tc, tt, tf;
+        int tc, tt, tf, tg;
         int bc = wave_exclusive_scan(sc, tid, &tc);
         int bt = wave_exclusive_scan(stl, tid, &tt);
         int bf = wave_exclusive_scan(sf, tid, &tf);
+        int bg = wave_exclusive_scan(sg, tid, &tg);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int e = 4 * tid + r;
@@ -393,15 +398,18 @@ __global__ void __launch_bounds__(1024) batch_dispatch_kernel(BatchArgs a) {
                 off[e] = bc;
                 toff[e] = bt;
                 dpos[e] = bf;
+                spos[e] = g[r] ? bg : -1;
             }
             bc += c[r];
             bt += nt[r];
             bf += f[r];
+            bg += g[r];
         }
         if (tid == 0) {
             totals[0] = tc;
             totals[1] = tt;
             totals[2] = tf;
+            totals[3] = tg;
         }
     }
     __syncthreads();
@@ -425,8 +433,12 @@ __global__ void __launch_bounds__(1024) batch_dispatch_kernel(BatchArgs a) {
         a.offsets[e] = off[e];
         if (c > 0) {
             a.distinct[dpos[e]] = e;
-            for (int i = 0; i * a.tile_tokens < c; ++i)
-                a.tiles[toff[e] + i] = Tile{e, off[e] + a.tile_tokens * i, min(a.tile_tokens, c - a.tile_tokens * i), 0};
+            if (spos[e] >= 0)
+                a.singles[spos[e]] = Tile{e, off[e], c, 0};
+            else
+                for (int i = 0; i * a.tile_tokens < c; ++i)
+                    a.tiles[toff[e] + i] =
+                        Tile{e, off[e] + a.tile_tokens * i, min(a.tile_tokens, c - a.tile_tokens * i), 0};
         }
     }
     if (tid == 0) {
@@ -437,6 +449,7 @@ __global__ void __launch_bounds__(1024) batch_dispatch_kernel(BatchArgs a) {
             for (int t0 = 0; t0 < a.T; t0 += a.tile_tokens)
                 a.tiles[nt++] = Tile{a.E, n + t0, min(a.tile_tokens, a.T - t0), 0};
         a.n_tiles[0] = nt;
+        if (a.n_singles) a.n_singles[0] = totals[3];
     }
 }
 

@@ -346,11 +346,14 @@ static moe_status_t run_group(moe_layer* layer, const BatchArgs& b, const int32_
     g.y = b.y + (size_t)g0 * b.H;
     g.T = n;
     g.tile_tokens = batch_tile_tokens(b.codec, n, K, E);
+    g.single_max = batch_single_max(g.tile_tokens);
     hipError_t err = batch_set_table(table, E, const_cast<const uint8_t**>(b.table), st);
     if (err == hipSuccess) err = batch_dispatch(g, st);
     if (err == hipSuccess) err = batch_gateup(g, st);
+    if (err == hipSuccess && g.single_max > 0) err = batch_pair_gateup(g, st);
     if (err == hipSuccess) err = batch_hprep(g, st);
     if (err == hipSuccess) err = batch_down(g, st);
+    if (err == hipSuccess && g.single_max > 0) err = batch_pair_down(g, st);
     if (err == hipSuccess) err = batch_combine(g, st);
     if (err != hipSuccess) return hip_fail(err, "batched launch behind the expert cache");
     for (int s : slots) {

@@ -369,6 +369,36 @@ __device__ __forceinline__ void convert_activations(const uint16_t* __restrict__
     to_operands<F, S::CPL>(xv, xa, xs);
 }
 
+// The same conversion one chunk column at a time (32 floats live instead of
+// 32 per column), for kernels that keep many other registers.
+template <int KG, int F>
+__device__ __forceinline__ void convert_activations_by_column(const uint16_t* __restrict__ x, int lane,
+                                                              HI8 (&xa)[GateUpShape<KG>::CPL],
+                                                              float (&xs)[GateUpShape<KG>::CPL]) {
+    using S = GateUpShape<KG>;
+    const int g0 = KG >= kWave ? lane : (lane & (KG - 1));
+#pragma unroll
+    for (int c = 0; c < S::CPL; ++c) {
+        float xv[1][32];
+        const uint16_t* xg = x + 32 * (g0 + kWave * c);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const u32x4 raw = *reinterpret_cast<const u32x4*>(xg + 8 * q);
+#pragma unroll
+            for (int z = 0; z < 4; ++z) {
+                const unsigned d = raw[z];
+                xv[0][8 * q + 2 * z] = __builtin_bit_cast(float, d << 16);
+                xv[0][8 * q + 2 * z + 1] = __builtin_bit_cast(float, d & 0xFFFF0000u);
+            }
+        }
+        HI8 a1[1];
+        float s1[1];
+        to_operands<F, 1>(xv, a1, s1);
+        xa[c] = a1[0];
+        xs[c] = s1[0];
+    }
+}
+
 // Converted activations in the workspace: lane l, chunk column c holds the
 // 16 byte dwords at [(c*64 + l)*16, +16) and (corr, factor) at
 // meta + (c*64 + l)*2, meta = 16*64*CPL dwords on.
@@ -921,12 +951,15 @@ struct DownWork {
     u32x4 code[S::NL][S::CPL][P];
     unsigned sc[RP][S::CPL][(S::NL + 1) / 2];
 
-    __device__ __forceinline__ void init(const uint8_t* b, const DecodeArgs& a, int block, int lane) {
+    __device__ __forceinline__ void init(const uint8_t* b, int H, int I, int block, int lane) {
         blob = b;
-        L = blob_layout(a.H, a.I, F);
+        L = blob_layout(H, I, F);
         rb = block;
         g0 = KG >= kWave ? lane : (lane & (KG - 1));
         row_sub = KG >= kWave ? 0 : (lane / KG);
+    }
+    __device__ __forceinline__ void init(const uint8_t* b, const DecodeArgs& a, int block, int lane) {
+        init(b, a.H, a.I, block, lane);
     }
     __device__ __forceinline__ size_t code_off(int step, int c) const {
         const size_t row = (size_t)rb * S::R + step * S::RPL + row_sub;
@@ -1059,6 +1092,94 @@ __global__ void __launch_bounds__(576) down_combine_kernel(DecodeArgs a) {
         for (int j = 0; j < K; ++j) y = fmaf(a.w[j], part[j][t], y);
         if (a.S > 0) y += part[K][t];
         a.y[(size_t)RP * (rb * S::R + t % S::R) + t / S::R] = y;
+    }
+}
+
+// ---------------------------------------------------------------- single-entry experts of batched calls
+// An expert that exactly one entry of a batched call routes to (the
+// dispatch's singles list, calls with 16-entry tiles) skips the grouped MFMA
+// kernels, whose tile it would fill to one sixteenth: its gate/up and down
+// run as the GEMVs above, one (token, expert) pair at a time.
+
+// Gate/up + SwiGLU of the singles: the grid's waves are spread evenly over
+// the pairs (waves_per_pair = waves / pairs); wave sub of a pair takes items
+// (blocks of R rows) sub, sub + waves_per_pair, ... with two items' loads in
+// flight, after converting the pair's token into integer operands itself.
+// h goes to the pair's row of the batched h buffer in the order
+// pair_down_kernel's lanes read it (h_index).
+template <int KG, int F>
+__global__ void __launch_bounds__(256) pair_gateup_kernel(BatchArgs a) {
+    using S = GateUpShape<KG>;
+    const int n = a.n_singles[0];
+    if (n == 0) return;
+    const int lane = threadIdx.x & 63;
+    const int wave_id = blockIdx.x * 4 + wave_in_block();
+    const int n_waves = gridDim.x * 4;
+    const int wpp = n_waves >= n ? n_waves / n : 1;
+    const int j = wave_id / wpp, sub = wave_id - j * wpp;
+    const int per_slot = a.I / row_pack(F) / S::R;
+    if (j >= n || sub >= per_slot) return;
+    const int n_mine = (per_slot - sub + wpp - 1) / wpp;
+    const Tile t = a.singles[j];
+    const int p = t.first_pair;
+    const uint8_t* blob = a.table[t.expert];
+    const BlobLayout L = blob_layout(a.H, a.I, F);
+    HI8 xa[S::CPL];
+    float xs[S::CPL];
+    convert_activations_by_column<KG, F>(a.x + (size_t)(a.perm[p] / a.K) * a.H, lane, xa, xs);
+    // settle the operands once (as in gateup_kernel), so that no later
+    // weight load waits on them
+#pragma unroll
+    for (int c = 0; c < S::CPL; ++c) {
+        asm volatile("" : "+v"(xa[c].he), "+v"(xa[c].ho), "+v"(xa[c].le), "+v"(xa[c].lo));
+        asm volatile("" : "+v"(xa[c].corr), "+v"(xs[c]));
+    }
+    float* h = a.h + (size_t)p * a.I;
+    GateUpBuf<KG, F> b[2];
+    // items past the wave's last repeat its last item (loads from L2, nothing stored)
+    auto rb_of = [&](int k) { return sub + (k < n_mine ? k : n_mine - 1) * wpp; };
+    run_items_loop<2>(
+        n_mine, [&](int k, GateUpBuf<KG, F>& buf) { gateup_issue<KG, F>(blob, L, rb_of(k), lane, buf); },
+        [&](int k, const GateUpBuf<KG, F>& buf) {
+            gateup_compute<KG, F>(buf, rb_of(k), lane, xa, xs, h, a.I / 32, k < n_mine);
+        },
+        b);
+}
+
+// Down projection of the singles: one wave per (pair, block of R output
+// rows) item, taken in turn by the grid's waves; the wave loads the pair's h
+// and converts it to integer operands, streams the block's rows as
+// down_combine_kernel does, and writes the R results to the pair's row of
+// the per-entry output d (the batched combine applies the routing weight).
+template <int KG, int NLD, int F>
+__global__ void __launch_bounds__(256) pair_down_kernel(BatchArgs a) {
+    using S = DownShape<KG, NLD>;
+    using D = DownWork<KG, NLD, F>;
+    constexpr int RP = D::RP;
+    __shared__ float part[4][RP * S::R];
+    const int n = a.n_singles[0];
+    const int lane = threadIdx.x & 63, wv = wave_in_block();
+    const int g0 = KG >= kWave ? lane : (lane & (KG - 1));
+    const int rblocks = a.H / RP / S::R;
+    const int items = n * rblocks;
+    for (int it = blockIdx.x * 4 + wv; it < items; it += gridDim.x * 4) {
+        const int j = it / rblocks, rb = it - j * rblocks;
+        const Tile t = a.singles[j];
+        const int p = t.first_pair;
+        float hraw[S::CPL][32];
+        load_h<S::CPL, KG>(a.h + (size_t)p * a.I, g0, hraw);
+        D d;
+        d.init(a.table[t.expert], a.H, a.I, rb, lane);
+        __builtin_amdgcn_sched_barrier(0);
+        d.issue_round(0);
+        d.load_scales();
+        if constexpr (D::NR > 1) d.issue_round(1);
+        __builtin_amdgcn_sched_barrier(0);
+        d.finish(hraw, lane, part[wv]);
+        __builtin_amdgcn_wave_barrier();
+        for (int q = lane; q < RP * S::R; q += kWave)
+            a.d[(size_t)p * a.H + (size_t)RP * (rb * S::R + q % S::R) + q / S::R] = part[wv][q];
+        __builtin_amdgcn_wave_barrier();
     }
 }
 
@@ -1723,6 +1844,61 @@ const void* fused_fn(const DecodeArgs& a) {
     return nullptr;
 }
 
+template <typename K>
+hipError_t launch_batch_kernel(K kernel, dim3 grid, dim3 block, hipStream_t st, const LaunchTiming& tm,
+                               const BatchArgs& a) {
+    if (tm.start)
+        hipExtLaunchKernelGGL(kernel, grid, block, 0, st, tm.start, tm.stop, 0, a);
+    else
+        hipLaunchKernelGGL(kernel, grid, block, 0, st, a);
+    return hipGetLastError();
+}
+
+// 4096 waves (16 per CU) for the singles' gate/up, spread over the pairs;
+// the same for their down items.
+constexpr int kPairGrid = 1024;
+
+template <int KG>
+hipError_t launch_pair_gateup(const BatchArgs& a, hipStream_t st, const LaunchTiming& tm) {
+    const dim3 g(kPairGrid), b(256);
+    if (a.codec == kCodecMxfp4) return launch_batch_kernel(pair_gateup_kernel<KG, kCodecMxfp4>, g, b, st, tm, a);
+    if (a.codec == kCodecInt8) return launch_batch_kernel(pair_gateup_kernel<KG, kCodecInt8>, g, b, st, tm, a);
+    if (a.codec == kCodecInt2) return launch_batch_kernel(pair_gateup_kernel<KG, kCodecInt2>, g, b, st, tm, a);
+    return launch_batch_kernel(pair_gateup_kernel<KG, kCodecInt4>, g, b, st, tm, a);
+}
+
+template <int KG, int NLD, int F>
+hipError_t launch_pair_down_c(const BatchArgs& a, hipStream_t st, const LaunchTiming& tm) {
+    using S = DownShape<KG, NLD>;
+    if constexpr (ilog2(pow2_at_least(S::NL * row_pack(F))) <= S::B &&
+                  S::NL * S::CPL * code_planes(F) <= down_max_loads(code_planes(F), S::CPL)) {
+        return launch_batch_kernel(pair_down_kernel<KG, NLD, F>, dim3(kPairGrid), dim3(256), st, tm, a);
+    } else {
+        return hipErrorInvalidValue;  // never chosen by down_rows
+    }
+}
+template <int KG, int NLD>
+hipError_t launch_pair_down_nl(const BatchArgs& a, hipStream_t st, const LaunchTiming& tm) {
+    if (a.codec == kCodecMxfp4) return launch_pair_down_c<KG, NLD, kCodecMxfp4>(a, st, tm);
+    if (a.codec == kCodecInt8) return launch_pair_down_c<KG, NLD, kCodecInt8>(a, st, tm);
+    if (a.codec == kCodecInt2) return launch_pair_down_c<KG, NLD, kCodecInt2>(a, st, tm);
+    return launch_pair_down_c<KG, NLD, kCodecInt4>(a, st, tm);
+}
+template <int KG>
+hipError_t launch_pair_down(const BatchArgs& a, hipStream_t st, const LaunchTiming& tm) {
+    switch (down_rows(a.H, KG, a.codec) / rows_per_load(KG)) {
+        case 1: return launch_pair_down_nl<KG, 1>(a, st, tm);
+        case 2: return launch_pair_down_nl<KG, 2>(a, st, tm);
+        case 4: return launch_pair_down_nl<KG, 4>(a, st, tm);
+        case 8: return launch_pair_down_nl<KG, 8>(a, st, tm);
+        case 12: return launch_pair_down_nl<KG, 12>(a, st, tm);
+        case 16: return launch_pair_down_nl<KG, 16>(a, st, tm);
+        case 24: return launch_pair_down_nl<KG, 24>(a, st, tm);
+        case 32: return launch_pair_down_nl<KG, 32>(a, st, tm);
+        default: return hipErrorInvalidValue;
+    }
+}
+
 }  // namespace
 
 // Kernels are instantiated for H/32 in {8,16,32,64,128,192,256} and
@@ -1749,6 +1925,31 @@ hipError_t decode_routed_gateup(const DecodeArgs& a, hipStream_t st, const Launc
         case 128: return launch_gateup<128>(a, st, tm);
         case 192: return launch_gateup<192>(a, st, tm);
         case 256: return launch_gateup<256>(a, st, tm);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t batch_pair_gateup(const BatchArgs& a, hipStream_t st, const LaunchTiming& tm) {
+    switch (a.H / 32) {
+        case 8: return launch_pair_gateup<8>(a, st, tm);
+        case 16: return launch_pair_gateup<16>(a, st, tm);
+        case 32: return launch_pair_gateup<32>(a, st, tm);
+        case 64: return launch_pair_gateup<64>(a, st, tm);
+        case 128: return launch_pair_gateup<128>(a, st, tm);
+        case 192: return launch_pair_gateup<192>(a, st, tm);
+        case 256: return launch_pair_gateup<256>(a, st, tm);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t batch_pair_down(const BatchArgs& a, hipStream_t st, const LaunchTiming& tm) {
+    switch (a.I / 32) {
+        case 4: return launch_pair_down<4>(a, st, tm);
+        case 8: return launch_pair_down<8>(a, st, tm);
+        case 16: return launch_pair_down<16>(a, st, tm);
+        case 32: return launch_pair_down<32>(a, st, tm);
+        case 64: return launch_pair_down<64>(a, st, tm);
+        case 128: return launch_pair_down<128>(a, st, tm);
         default: return hipErrorInvalidValue;
     }
 }

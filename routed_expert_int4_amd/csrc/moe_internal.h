@@ -31,7 +31,7 @@ struct WorkspaceLayout {
     size_t b_xa = 0;           // [Tb][H] fp16
     size_t b_kx = 0;           // [Tb]
     size_t b_counts = 0, b_offsets = 0, b_perm = 0, b_inv = 0, b_distinct = 0, b_n_distinct = 0;
-    size_t b_tiles = 0, b_n_tiles = 0;
+    size_t b_tiles = 0, b_n_tiles = 0, b_singles = 0, b_n_singles = 0;
     size_t b_h = 0;            // [P][I] fp32, P = Tb * (K + S)
     size_t b_ha_hi = 0, b_ha_lo = 0;  // [P][I] fp16
     size_t b_kh = 0;           // [P]
@@ -64,7 +64,7 @@ moe_status_t check_layer_status(const moe_layer* L, const char* who);
 constexpr unsigned kDefaultSpinLimit = 1u << 20;  // polls, about a second
 // moe_layer_profile kinds: router, gate/up, down + combine, fused one-token
 // launch, and the batched path's grouped gate/up and down kernels alone
-constexpr int kProfileKinds = 6;
+constexpr int kProfileKinds = 8;
 
 }  // namespace moe
 

@@ -150,6 +150,8 @@ struct BatchArgs {
     int32_t* n_distinct;         // [1]
     Tile* tiles;                 // [max_tiles]
     int32_t* n_tiles;            // [1]
+    Tile* singles;               // [min(T*K, E)] experts with 1..single_max entries (GEMV path)
+    int32_t* n_singles;          // [1]
     float* h;                    // [P][I] SwiGLU outputs
     uint16_t* ha_hi;             // [P][I/32][4][8] h as scaled fp16 hi part, MFMA order
     uint16_t* ha_lo;             // [P][I/32][4][8] lo part
@@ -163,7 +165,14 @@ struct BatchArgs {
     float top_p;                 // adaptive expert top-p (1: plain top-k); dropped choices get id -1
     int codec;                   // weight codec (kCodecInt4 .. kCodecInt2)
     int tile_tokens;             // batch_tile_tokens(codec, T, K, E): 16 or 32
+    int single_max;              // batch_single_max(tile_tokens): entries of an expert that takes the GEMV path
 };
+
+// Experts with at most this many entries in a call skip the grouped MFMA
+// kernels and run the one-token GEMVs per (token, expert) pair: 1 in calls
+// with 16-entry tiles (a single entry fills a sixteenth of its tile; two or
+// more would read the expert once per pair), none with 32-entry tiles.
+__host__ __device__ constexpr int batch_single_max(int tile_tokens) { return tile_tokens == 16 ? 1 : 0; }
 
 // Upper bound of the tiles of a call of T tokens.
 inline int batch_max_tiles(int T, int K, int E, int S) {
@@ -188,6 +197,10 @@ hipError_t batch_topk(const BatchArgs& a, bool convert, hipStream_t st);
 hipError_t batch_dispatch(const BatchArgs& a, hipStream_t st);
 hipError_t batch_gateup(const BatchArgs& a, hipStream_t st, const LaunchTiming& tm = {});
 hipError_t batch_hprep(const BatchArgs& a, hipStream_t st);
+// Gate/up + SwiGLU and down of the singles (one-token GEMVs per pair; no-ops
+// when the dispatch found none).
+hipError_t batch_pair_gateup(const BatchArgs& a, hipStream_t st, const LaunchTiming& tm = {});
+hipError_t batch_pair_down(const BatchArgs& a, hipStream_t st, const LaunchTiming& tm = {});
 hipError_t batch_down(const BatchArgs& a, hipStream_t st, const LaunchTiming& tm = {});
 hipError_t batch_combine(const BatchArgs& a, hipStream_t st);
 // Writes n (<= 256) expert blob pointers into a device table, in stream order.

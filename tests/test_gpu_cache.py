@@ -16,7 +16,9 @@ the C ABI:
     experts the previous token read);
   * prefetch and evict semantics and their errors;
   * batched calls (T > 1) behind the cache: outputs bit-identical to the
-    resident batched path, one lookup per distinct expert and token group,
+    resident batched path run on the same token groups (one group: the whole
+    call; groups of one token, which a resident call would run on the decode
+    kernels, against the oracle), one lookup per distinct expert and token group,
     the counts equal to the LRU replay of those groups;
   * speculative next-layer prefetch (the next layer's router on the current
     layer's input): outputs unchanged, the predictions equal to the oracle's
@@ -452,13 +454,14 @@ def test_cache_prefetch_link_errors_and_timeline_limit(torch_cuda):
     other.close()
 
 
-def token_groups(ids, slots, pinned):
+def token_groups(ids, slots, pinned, ranges=False):
     """The consecutive token groups of a batched call behind the cache: as
     many tokens as fit, in order, while the group's distinct experts that are
     not pinned number at most slots - len(pinned); each group is looked up as
-    its distinct experts in ascending order."""
+    its distinct experts in ascending order.  With ranges, also the groups'
+    token ranges [t0, t1)."""
     pinned, room = set(int(e) for e in pinned), slots - len(pinned)
-    groups, g0, n = [], 0, len(ids)
+    groups, spans, g0, n = [], [], 0, len(ids)
     while g0 < n:
         seen, used, t = set(), 0, g0
         while t < n:
@@ -470,8 +473,24 @@ def token_groups(ids, slots, pinned):
             seen.update(row)
             t += 1
         groups.append(sorted(seen))
+        spans.append((g0, t))
         g0 = t
-    return groups
+    return (groups, spans) if ranges else groups
+
+
+def resident_by_groups(torch, resident, x, spans):
+    """The resident layer's batched outputs over each token group on its
+    own: the reference of a cached batched call, which runs its groups as
+    separate launch sequences (an expert's entries in a group decide its
+    kernel, the grouped MFMA or, with a single entry, the GEMV).  A resident
+    call of one token takes the decode kernels instead, so one-token groups
+    have no bit-exact reference: returns (reference rows, mask of the tokens
+    in groups of two or more)."""
+    ys, keep = [], []
+    for t0, t1 in spans:
+        ys.append(resident.forward(x[t0:t1])[0])
+        keep += [t1 - t0 > 1] * (t1 - t0)
+    return torch.cat(ys), torch.tensor(keep, device=x.device)
 
 
 @pytest.mark.parametrize("slots,n_pin,top_p", [(64, 0, 1.0), (16, 0, 1.0), (12, 4, 1.0), (16, 0, 0.6)])
@@ -490,13 +509,18 @@ def test_cache_batched_call(torch_cuda, slots, n_pin, top_p):
     pins = lru.hottest(lru.usage(idh, cfg.n_experts), n_pin)
     if pins:
         cache.pin(0, pins)
+    groups, spans = token_groups(idh, slots, pins, ranges=True)
+    y_g, multi = resident_by_groups(torch, resident[0], x, spans)
+    if len(spans) == 1:
+        assert torch.equal(y_g, y_r)
     for call in range(2):  # the second call finds the last group's experts resident
         y, ids, w = cached[0].forward(x)
         torch.cuda.synchronize()
         assert torch.equal(ids, ids_r) and torch.equal(w, w_r), "routing differs from the resident batched path"
-        assert torch.equal(y, y_r), "outputs differ from the resident batched path"
+        assert torch.equal(y[multi], y_g[multi]), \
+            "outputs differ from the resident batched path over the same token groups"
+    # every token (one-token groups included) against the oracle
     res = check_layer(weights[0], x_bits, y.cpu().numpy(), idh, w.cpu().numpy())
-    groups = token_groups(idh, slots, pins)
     hits, misses, evictions = lru.replay(groups + groups, slots, pinned=pins)
     st = cache.stats(0)
     say(f"[gpu] {len(groups)} groups, rel err {res['worst_rel']:.3g}, stats {st}, replay {(hits, misses, evictions)}")
@@ -513,8 +537,9 @@ def test_cache_batched_call(torch_cuda, slots, n_pin, top_p):
 def test_glm_cache_batched_call(torch_cuda):
     """A 32-token call of the GLM-shaped layer with the Zipf(1.1) bias behind
     a 64-slot cache (about 90 distinct experts per call, so several token
-    groups): outputs bit-identical to the resident batched path, sampled
-    tokens against the oracle, counts equal to the LRU replay of the groups."""
+    groups): outputs bit-identical to the resident batched path over the
+    same token groups, sampled tokens against the oracle, counts equal to the
+    LRU replay of the groups."""
     torch = torch_cuda
     from routed_expert_int4_amd.layer import DeviceLayer, ExpertCache, HostExpertStore
     from tests.helpers import zipf_glm_weights
@@ -531,10 +556,12 @@ def test_glm_cache_batched_call(torch_cuda):
     y_r, ids_r, w_r = resident.forward(x)
     y, ids, w = cached.forward(x)
     torch.cuda.synchronize()
-    assert torch.equal(ids, ids_r) and torch.equal(w, w_r) and torch.equal(y, y_r)
     idh = ids.cpu().numpy()
-    res = check_layer(weights, x_bits, y.cpu().numpy(), idh, w.cpu().numpy(), rows=[0, 9, 31])
-    groups = token_groups(idh, slots, [])
+    groups, spans = token_groups(idh, slots, [], ranges=True)
+    y_g, multi = resident_by_groups(torch, resident, x, spans)
+    assert torch.equal(ids, ids_r) and torch.equal(w, w_r) and torch.equal(y[multi], y_g[multi])
+    single = [t for t, m in enumerate(multi.cpu().tolist()) if not m]  # one-token groups: the oracle only
+    res = check_layer(weights, x_bits, y.cpu().numpy(), idh, w.cpu().numpy(), rows=sorted({0, 9, 31, *single}))
     st = cache.stats(0)
     say(f"[gpu] GLM batched cache: {len(groups)} groups of {[len(g) for g in groups]} experts, "
         f"rel err {res['worst_rel']:.3g}, stats {st}")

@@ -74,7 +74,7 @@ def test_fused_matches_three_launches(torch_cuda, cfg_name):
     (y1, ids1, w1, n1), (y3, ids3, w3, n3) = run_both(torch, layer, x)
     say(f"[gpu] {cfg_name}: launches fused path {n1}, three-launch path {n3}")
     assert n1[3] == T and n1[:3] == [0, 0, 0], "the fused launch did not run"
-    assert n3[3] == 0 and n3[:3] == [T, T, T] and n1[4:] == n3[4:] == [0, 0]
+    assert n3[3] == 0 and n3[:3] == [T, T, T] and n1[4:] == n3[4:] == [0, 0, 0, 0]
     assert torch.equal(ids1, ids3) and torch.equal(w1, w3), "routing differs between the paths"
     assert torch.equal(y1, y3), "outputs differ between the fused and the three-launch path"
     assert torch.all(y1[5] == 0.0)
@@ -120,7 +120,7 @@ def test_fused_falls_back_without_instance(torch_cuda):
     torch.cuda.synchronize()
     _, n = B.moe_layer_profile_read(layer.handle)
     B.moe_layer_profile(layer.handle, False)
-    assert n == [2, 2, 2, 0, 0, 0]
+    assert n == [2, 2, 2, 0, 0, 0, 0, 0]
     check_layer(weights, x_bits, y.cpu().numpy(), ids.cpu().numpy(), w.cpu().numpy())
     layer.close()
 

@@ -243,8 +243,8 @@ moe_status_t moe_hbm_read_probe(const void* d_buf, size_t bytes, unsigned* d_sin
  * cut dropped, which takes no entry); d_distinct [n_experts] the experts
  * with at least one entry in ascending order, their number in
  * d_n_distinct[0] (entries of d_distinct past it are unspecified).  All
- * device buffers, asynchronous on stream.  Ids outside [-1, n_experts) are
- * undefined behaviour. */
+ * device buffers, asynchronous on stream.  An id outside [-1, n_experts)
+ * is treated as -1 (no entry). */
 moe_status_t moe_dispatch(moe_layer_t* layer, const int32_t* d_ids, int T, int32_t* d_counts, int32_t* d_offsets,
                           int32_t* d_perm, int32_t* d_distinct, int32_t* d_n_distinct, void* stream);
 

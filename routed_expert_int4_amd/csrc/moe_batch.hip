@@ -18,7 +18,8 @@
 //      (tiles of up to 32 entries when a call averages 8 or more per expert:
 //      two MFMA row blocks share each dequantised weight fragment, and a
 //      workgroup of 16 waves covers 256 rows);
-//   5. h prep: h per entry as scaled fp16 hi + lo parts in MFMA order;
+//   5. h prep: h per entry as scaled fp16 (hi + lo parts for the exact-
+//      fragment codecs) in MFMA order;
 //   6. down: grouped int4 GEMM per (tile, 256 output rows);
 //   7. combine: y = sum_j w_j d_j + d_shared in slot order (no atomics).
 //
@@ -346,12 +347,14 @@ __global__ void __launch_bounds__(1024) batch_dispatch_kernel(BatchArgs a) {
     int n2 = kWave;
     while (n2 < n) n2 <<= 1;
     // a dropped choice (id -1, top-p cut) sorts to the end with the padding
+    // an id outside [0, E) takes no entry, as a choice the top-p cut dropped
+    auto valid = [&](int i) { return i < n && a.ids[i] >= 0 && a.ids[i] < a.E; };
     for (int i = tid; i < n2; i += 1024)
-        keys[i] = i < n && a.ids[i] >= 0 ? (((unsigned)a.ids[i] << 16) | (unsigned)i) : 0xFFFFFFFFu;
+        keys[i] = valid(i) ? (((unsigned)a.ids[i] << 16) | (unsigned)i) : 0xFFFFFFFFu;
     if (tid < 256) cnt[tid] = 0;
     __syncthreads();
     for (int i = tid; i < n; i += 1024)
-        if (a.ids[i] >= 0) atomicAdd(&cnt[a.ids[i]], 1);
+        if (valid(i)) atomicAdd(&cnt[a.ids[i]], 1);
     for (int k = 2; k <= n2; k <<= 1) {
         for (int j = k >> 1; j > 0; j >>= 1) {
             __syncthreads();
@@ -417,7 +420,7 @@ __global__ void __launch_bounds__(1024) batch_dispatch_kernel(BatchArgs a) {
     // dropped choice's inv is -1
     const int n_kept = totals[0];
     for (int i = tid; i < n; i += 1024)
-        if (a.ids[i] < 0) a.inv[i] = -1;
+        if (!valid(i)) a.inv[i] = -1;
     for (int p = tid; p < n; p += 1024) {
         if (p < n_kept) {
             const int idx = (int)(keys[p] & 0xFFFFu);
@@ -711,7 +714,8 @@ __global__ void __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(4))
 
 // ---------------------------------------------------------------- h prep
 // One workgroup per entry: h as scaled fp16 hi + lo (hi = fp16(h 2^kh),
-// lo = fp16(h 2^kh - hi)), kh putting max |h| into [2^13, 2^14).
+// lo = fp16(h 2^kh - hi)), kh putting max |h| into [2^13, 2^14); int4
+// calls write the hi part only.
 template <int CPT>
 __global__ void __launch_bounds__(256) batch_hprep_kernel(BatchArgs a) {
     __shared__ unsigned wmax[4];
@@ -754,8 +758,9 @@ __global__ void __launch_bounds__(256) batch_hprep_kernel(BatchArgs a) {
         const size_t o = (size_t)p * a.I + (size_t)e * 8;
         *reinterpret_cast<u32x4*>(a.ha_hi + o) = u32x4{pack_h2(hi[0], hi[1]), pack_h2(hi[2], hi[3]),
                                                        pack_h2(hi[4], hi[5]), pack_h2(hi[6], hi[7])};
-        *reinterpret_cast<u32x4*>(a.ha_lo + o) = u32x4{pack_h2(lo[0], lo[1]), pack_h2(lo[2], lo[3]),
-                                                       pack_h2(lo[4], lo[5]), pack_h2(lo[6], lo[7])};
+        if (a.codec != kCodecInt4)  // the int4 down kernel reads the hi part only
+            *reinterpret_cast<u32x4*>(a.ha_lo + o) = u32x4{pack_h2(lo[0], lo[1]), pack_h2(lo[2], lo[3]),
+                                                           pack_h2(lo[4], lo[5]), pack_h2(lo[6], lo[7])};
     }
     if (tid == 0) a.kh[p] = k;
 }
@@ -765,8 +770,10 @@ constexpr int kDownThreads = 1024;                   // 16 waves
 constexpr int kDownBlockRows = kDownThreads / 4;     // 16 rows per wave
 // Workgroup = 16 waves over 256 output rows for the (up to) 16 entries of
 // one tile (one workgroup per CU: the staged h, as many bytes per item as
-// 128 rows of codes, serves twice the rows); each group is two MFMAs (hi and
-// lo parts of h) into one result.  Rows are stored rows (int2: 512 output
+// 128 rows of codes, serves twice the rows).  Int4: one MFMA per group on h
+// as fp16 (one rounding of at most 2^-11, the size of the weight fragments'
+// own); the exact-fragment codecs: two MFMAs (hi and lo parts of h, ~22
+// bits) into one result.  Rows are stored rows (int2: 512 output
 // rows, even and odd accumulated apart, the two rows' scales of a group in
 // one dword).
 template <int KGI, int F, int TT>
@@ -776,9 +783,13 @@ __global__ void __launch_bounds__(kDownThreads) __attribute__((amdgpu_waves_per_
     constexpr int CK = KGI < 16 ? KGI : (NB > 1 || code_planes(F) > 1 || row_pack(F) > 1 ? 8 : 16);
     constexpr int NST = KGI / CK;
     constexpr int PART = CK * 64 * NB;       // staging elements of one part
-    constexpr int PT = (2 * PART + kDownThreads - 1) / kDownThreads;  // per thread (hi and lo)
+    // parts of h staged: int4 takes h as one fp16 value (the weight
+    // fragments are fp16(code x scale) already); the exact-fragment codecs
+    // take hi and lo
+    constexpr int NPARTS = F == kCodecInt4 ? 1 : 2;
+    constexpr int PT = (NPARTS * PART + kDownThreads - 1) / kDownThreads;  // per thread
     static_assert(CK % 4 == 0 && KGI % CK == 0 && PT >= 1, "down stage shape");
-    __shared__ u32x4 hs[2][2 * PART];        // [part * PART + (g * 4 + q) * TT + token]
+    __shared__ u32x4 hs[2][NPARTS * PART];   // [part * PART + (g * 4 + q) * TT + token]
     const int tid = threadIdx.x, lane = tid & 63, wv = wave_in_block();
     const int i = lane & 15, q = lane >> 4;
     const int n_tiles = a.n_tiles[0];
@@ -832,7 +843,7 @@ __global__ void __launch_bounds__(kDownThreads) __attribute__((amdgpu_waves_per_
 #pragma unroll
             for (int r = 0; r < PT; ++r) {
                 const int e = tid + kDownThreads * r;
-                if (e >= 2 * PART) break;
+                if (e >= NPARTS * PART) break;
                 const int part = e / PART, rest = e - part * PART;
                 const uint16_t* base = part ? a.ha_lo : a.ha_hi;
                 v[r] = has ? *as_global<u32x4>(base + src + (size_t)((st * CK + rest / (4 * TT)) * 4 +
@@ -850,7 +861,7 @@ __global__ void __launch_bounds__(kDownThreads) __attribute__((amdgpu_waves_per_
             const int buf = gs & 1;
 #pragma unroll
             for (int r = 0; r < PT; ++r)
-                if (tid + kDownThreads * r < 2 * PART) hs[buf][tid + kDownThreads * r] = v[r];
+                if (tid + kDownThreads * r < NPARTS * PART) hs[buf][tid + kDownThreads * r] = v[r];
             __syncthreads();
             if (st + 1 < NST) stage_load(st + 1, v);
 #pragma unroll
@@ -863,7 +874,8 @@ __global__ void __launch_bounds__(kDownThreads) __attribute__((amdgpu_waves_per_
                     if (k + 2 < NSP) load_step(k + 2, cd2, sc2);
                     transpose_quarters(cd0);
                     if constexpr (F == kCodecInt4) {
-                        // int4: fp16(code x scale) fragments, as in gate/up
+                        // int4: fp16(code x scale) fragments, as in gate/up,
+                        // against h as one fp16 value
 #pragma unroll
                         for (int m = 0; m < 4; ++m) {
                             const f16x8 bw = codes_to_f16x8(cd0[m], mg) * splat_h8(sc0[m]);
@@ -871,8 +883,7 @@ __global__ void __launch_bounds__(kDownThreads) __attribute__((amdgpu_waves_per_
                             for (int z = 0; z < NB; ++z) {
                                 const int slot = ((4 * c + m) * 4 + q) * TT + 16 * z + i;
                                 const f16x8 ah = __builtin_bit_cast(f16x8, hs[buf][slot]);
-                                const f16x8 al = __builtin_bit_cast(f16x8, hs[buf][PART + slot]);
-                                acc[0][z] = mfma16(al, bw, mfma16(ah, bw, acc[0][z]));
+                                acc[0][z] = mfma16(ah, bw, acc[0][z]);
                             }
                         }
                     } else {

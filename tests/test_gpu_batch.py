@@ -77,7 +77,7 @@ def dispatch_layer(torch_cuda):
 
 @pytest.mark.parametrize("T,kind", [(1, "uniform"), (2, "uniform"), (32, "zipf"), (37, "uniform"), (512, "uniform"),
                                     (1024, "uniform"), (1024, "zipf"), (300, "same"), (200, "dropped"),
-                                    (3, "all_dropped_but_one")])
+                                    (3, "all_dropped_but_one"), (64, "out_of_range")])
 def test_dispatch_matches_oracle(torch_cuda, dispatch_layer, T, kind):
     say(f"[gpu] dispatch T={T} {kind}")
     E, k = MID_D.n_experts, MID_D.top_k
@@ -93,8 +93,14 @@ def test_dispatch_matches_oracle(torch_cuda, dispatch_layer, T, kind):
         ids[rng.random(ids.shape) < 0.3] = -1
     if kind == "all_dropped_but_one":
         ids[:, 1:] = -1
+    ref_ids = ids
+    if kind == "out_of_range":  # ids outside [-1, E) take no entry, as -1 does
+        ids = ids.copy()
+        ids[rng.random(ids.shape) < 0.2] = E
+        ids[rng.random(ids.shape) < 0.1] = -7
+        ref_ids = np.where((ids >= 0) & (ids < E), ids, -1).astype(np.int32)
     got = gpu_dispatch(torch_cuda, dispatch_layer, ids)
-    ref = oracle_dispatch(ids, E)
+    ref = oracle_dispatch(ref_ids, E)
     for key in ("counts", "offsets", "perm", "distinct"):
         np.testing.assert_array_equal(got[key], ref[key], err_msg=key)
 

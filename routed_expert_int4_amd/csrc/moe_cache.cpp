@@ -29,14 +29,21 @@
 
 namespace moe {
 
+// Which event covers a slot's last read: none yet, the slot's own (a batched
+// group), or the layer's end-of-call event (a one-token call).
+enum : char { kUseNone = 0, kUseSlotEvent = 1, kUseCallEvent = 2 };
+
 struct LayerSlots {
     explicit LayerSlots(int n_experts, int n_slots) : policy(n_experts, n_slots) {}
     SlotPolicy policy;
     std::vector<const void*> host_blob;    // [E] registered pinned blobs
     std::vector<hipEvent_t> copy_done;     // [slots]
-    std::vector<hipEvent_t> last_use;      // [slots]
-    std::vector<char> use_recorded;        // [slots]
-    std::vector<char> copy_recorded;       // [slots]
+    std::vector<hipEvent_t> last_use;      // [slots] last batched read of the slot
+    std::vector<char> use_kind;            // [slots] kUse*: the event that covers the slot's last read
+    std::vector<char> copy_recorded;       // [slots] a copy was queued and not yet seen complete
+    hipEvent_t last_call = nullptr;        // end of the layer's latest call (after all of its reads)
+    hipStream_t call_stream = nullptr;     // the stream last_call was recorded on
+    bool call_recorded = false;
     std::vector<uint64_t> usage;           // [E] routed uses (the learning cache's counts)
     std::vector<char> fresh;               // [E] brought in by a prefetch and not used since
     std::vector<int> prediction;           // experts predicted for this layer's next call
@@ -84,6 +91,7 @@ static void destroy_cache(moe_cache* c) {
             if (e) (void)hipEventDestroy(e);
         for (hipEvent_t e : L->last_use)
             if (e) (void)hipEventDestroy(e);
+        if (L->last_call) (void)hipEventDestroy(L->last_call);
         delete L;
     }
     for (hipEvent_t e : c->tl_events) (void)hipEventDestroy(e);
@@ -129,6 +137,39 @@ LaunchTiming cache_kernel_timing(moe_cache* c) {
 
 // Makes expert e of layer l resident; `protect` lists experts that must not
 // be evicted.  Sets *slot and *missed.
+// A layer's end-of-call event is re-recorded by every call, so it has to
+// cover the reads of all earlier calls.  Calls on one stream do by stream
+// order; a call on another stream first waits for the previous call's event.
+static hipError_t join_layer_stream(LayerSlots& L, hipStream_t st) {
+    if (!L.call_recorded || L.call_stream == st) return hipSuccess;
+    return hipStreamWaitEvent(st, L.last_call, 0);
+}
+
+static hipError_t record_layer_call(LayerSlots& L, hipStream_t st) {
+    const hipError_t err = hipEventRecord(L.last_call, st);
+    if (err == hipSuccess) {
+        L.call_recorded = true;
+        L.call_stream = st;
+    }
+    return err;
+}
+
+// Whether the copy into slot s may still be running.  A copy seen complete
+// is forgotten, so that later reads of the slot need neither a query nor a
+// wait.
+static hipError_t copy_pending(LayerSlots& L, int s, bool* pending) {
+    *pending = false;
+    if (!L.copy_recorded[s]) return hipSuccess;
+    const hipError_t q = hipEventQuery(L.copy_done[s]);
+    if (q == hipErrorNotReady) {
+        (void)hipGetLastError();
+        *pending = true;
+        return hipSuccess;
+    }
+    if (q == hipSuccess) L.copy_recorded[s] = 0;
+    return q;
+}
+
 static moe_status_t make_resident(moe_cache* c, int l, int e, const std::vector<int>& protect, int* slot,
                                   bool* missed) {
     LayerSlots& L = *c->layers[l];
@@ -150,7 +191,8 @@ static moe_status_t make_resident(moe_cache* c, int l, int e, const std::vector<
     hipEvent_t tb = nullptr, te = nullptr;
     const bool stamp = timeline_pair(c, 0, &tb, &te);
     hipError_t err = hipSuccess;
-    if (L.use_recorded[s]) err = hipStreamWaitEvent(c->copy_stream, L.last_use[s], 0);
+    if (L.use_kind[s] == kUseSlotEvent) err = hipStreamWaitEvent(c->copy_stream, L.last_use[s], 0);
+    if (L.use_kind[s] == kUseCallEvent) err = hipStreamWaitEvent(c->copy_stream, L.last_call, 0);
     if (err == hipSuccess && stamp) err = hipEventRecord(tb, c->copy_stream);
     if (err == hipSuccess)
         err = hipMemcpyAsync(c->slot_ptr(l, s), L.host_blob[e], c->expert_bytes, hipMemcpyHostToDevice,
@@ -195,7 +237,9 @@ moe_status_t cache_prepare_token(moe_layer* layer, DecodeArgs& a, hipStream_t st
     const int l = layer->cache_layer;
     LayerSlots& L = *c->layers[l];
     const int K = a.K;
-    hipError_t err = hipMemcpyAsync(c->pinned_ids, a.ids, sizeof(int32_t) * K, hipMemcpyDeviceToHost, st);
+    hipError_t err = join_layer_stream(L, st);
+    if (err == hipSuccess)
+        err = hipMemcpyAsync(c->pinned_ids, a.ids, sizeof(int32_t) * K, hipMemcpyDeviceToHost, st);
     if (err == hipSuccess && d_pred)
         err = hipMemcpyAsync(c->pinned_ids + 16, d_pred, sizeof(int32_t) * K, hipMemcpyDeviceToHost, st);
     if (err == hipSuccess) err = hipEventRecord(c->ids_ready, st);
@@ -251,15 +295,8 @@ moe_status_t cache_prepare_token(moe_layer* layer, DecodeArgs& a, hipStream_t st
         // a hit whose (prefetch) copy is still running goes with the misses,
         // so that it does not hold back the hits that are ready
         bool copying = false;
-        if (L.copy_recorded[s]) {
-            const hipError_t q = hipEventQuery(L.copy_done[s]);
-            if (q == hipErrorNotReady) {
-                copying = true;
-                (void)hipGetLastError();
-            } else if (q != hipSuccess) {
-                return hip_fail(q, "expert cache: copy event query");
-            }
-        }
+        err = copy_pending(L, s, &copying);
+        if (err != hipSuccess) return hip_fail(err, "expert cache: copy event query");
         (copying ? miss_slots : hit_slots).push_back(j);
     }
     a.direct = 1;
@@ -331,10 +368,10 @@ static moe_status_t run_group(moe_layer* layer, const BatchArgs& b, const int32_
         L.fresh[e] = 0;
         table.p[e] = c->slot_ptr(l, s);
         slots.push_back(s);
-        if (L.copy_recorded[s]) {
-            hipError_t err = hipStreamWaitEvent(st, L.copy_done[s], 0);
-            if (err != hipSuccess) return hip_fail(err, "expert cache: stream wait");
-        }
+        bool copying = false;
+        hipError_t err = copy_pending(L, s, &copying);
+        if (err == hipSuccess && copying) err = hipStreamWaitEvent(st, L.copy_done[s], 0);
+        if (err != hipSuccess) return hip_fail(err, "expert cache: stream wait");
     }
     BatchArgs g = b;
     const int n = g1 - g0;
@@ -359,7 +396,7 @@ static moe_status_t run_group(moe_layer* layer, const BatchArgs& b, const int32_
     for (int s : slots) {
         err = hipEventRecord(L.last_use[s], st);
         if (err != hipSuccess) return hip_fail(err, "expert cache: last-use event");
-        L.use_recorded[s] = 1;
+        L.use_kind[s] = kUseSlotEvent;
     }
     return MOE_OK;
 }
@@ -372,6 +409,8 @@ moe_status_t cache_batch_forward(moe_layer* layer, const uint16_t* d_x, int T, f
     const int K = cfg.top_k, E = cfg.n_experts, H = cfg.hidden;
     const int tb = layer->W.batch_tokens;
     L.has_prediction = false;  // a one-token prediction does not carry over to a batched call
+    hipError_t jerr = join_layer_stream(L, st);
+    if (jerr != hipSuccess) return hip_fail(jerr, "expert cache: stream wait");
     for (int t0 = 0; t0 < T; t0 += tb) {
         const int n = T - t0 < tb ? T - t0 : tb;
         BatchArgs b = batch_args(layer, d_x + (size_t)t0 * H, n, ids_base + (size_t)t0 * K, w_base + (size_t)t0 * K,
@@ -413,17 +452,20 @@ moe_status_t cache_batch_forward(moe_layer* layer, const uint16_t* d_x, int T, f
             g0 = t;
         }
     }
+    // the slots read here carry their own events; this one keeps the layer's
+    // end-of-call event on the stream of its latest call
+    jerr = record_layer_call(L, st);
+    if (jerr != hipSuccess) return hip_fail(jerr, "expert cache: end-of-call event");
     return MOE_OK;
 }
 
 moe_status_t cache_finish_token(moe_layer* layer, hipStream_t st) {
     moe_cache* c = layer->cache;
     LayerSlots& L = *c->layers[c->pending_layer];
-    for (int s : c->pending_slots) {
-        hipError_t err = hipEventRecord(L.last_use[s], st);
-        if (err != hipSuccess) return hip_fail(err, "expert cache: last-use event");
-        L.use_recorded[s] = 1;
-    }
+    // one event after the token's reads covers every slot it read
+    hipError_t err = record_layer_call(L, st);
+    if (err != hipSuccess) return hip_fail(err, "expert cache: end-of-call event");
+    for (int s : c->pending_slots) L.use_kind[s] = kUseCallEvent;
     c->pending_slots.clear();
     c->pending_layer = -1;
     return MOE_OK;
@@ -473,10 +515,11 @@ moe_status_t expert_cache_create(const moe_config_t* cfg, int n_layers, int slot
         L->host_blob.assign(cfg->n_experts, nullptr);
         L->copy_done.assign(slots_per_layer, nullptr);
         L->last_use.assign(slots_per_layer, nullptr);
-        L->use_recorded.assign(slots_per_layer, 0);
+        L->use_kind.assign(slots_per_layer, kUseNone);
         L->copy_recorded.assign(slots_per_layer, 0);
         L->usage.assign(cfg->n_experts, 0);
         L->fresh.assign(cfg->n_experts, 0);
+        err = hipEventCreateWithFlags(&L->last_call, hipEventDisableTiming);
         for (int s = 0; s < slots_per_layer && err == hipSuccess; ++s) {
             err = hipEventCreateWithFlags(&L->copy_done[s], hipEventDisableTiming);
             if (err == hipSuccess) err = hipEventCreateWithFlags(&L->last_use[s], hipEventDisableTiming);
@@ -520,7 +563,7 @@ moe_status_t expert_cache_evict(moe_cache_t* cache, int layer, int expert) {
     if (layer < 0 || layer >= cache->n_layers || expert < 0 || expert >= cache->cfg.n_experts)
         return fail(MOE_EINVAL, "expert_cache_evict: layer %d / expert %d out of range", layer, expert);
     LayerSlots& L = *cache->layers[layer];
-    // The slot's next copy waits on its last-use event, so freeing it now is safe.
+    // The slot's next copy waits on the event that covers its last read, so freeing it now is safe.
     if (L.policy.release(expert) >= 0) ++L.stats.evictions;
     L.fresh[expert] = 0;
     return MOE_OK;

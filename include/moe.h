@@ -306,7 +306,10 @@ moe_status_t moe_layer_profile_read(moe_layer_t* layer, double* total_ms, uint64
  * completed).  expert_cache_evict: frees the expert's slot once its last use
  * has completed (no-op MOE_OK if not resident).  expert_cache_stats: counters
  * of one layer.  moe_layer_attach_cache: routes the layer's routed experts
- * through the cache as layer layer_id. */
+ * through the cache as layer layer_id.  A copy into a slot waits for every
+ * earlier call's reads of it, whichever stream each call ran on; calls of
+ * layers that share a workspace (and calls of one layer) are still ordered
+ * by the caller. */
 typedef struct {
     uint64_t hits;
     uint64_t misses;

@@ -15,6 +15,7 @@ the C ABI:
   * copy/compute ordering with the minimum slot count (every token evicts
     experts the previous token read);
   * prefetch and evict semantics and their errors;
+  * calls alternating between two streams that the caller orders;
   * batched calls (T > 1) behind the cache: outputs bit-identical to the
     resident batched path run on the same token groups (one group: the whole
     call; groups of one token, which a resident call would run on the decode
@@ -142,6 +143,51 @@ def test_cache_prefetch_and_evict(torch_cuda):
     assert err.value.code == B.MOE_EINVAL
     with pytest.raises(B.MoeError):
         cache.evict(0, -1)
+    for lay in cached + resident:
+        lay.close()
+    cache.close()
+
+
+def test_cache_calls_on_two_streams(torch_cuda):
+    """One-token and batched calls of a cached layer alternating between two
+    streams that the caller orders (each call's stream waits for the other
+    one first), with as many slots as top_k, so every token evicts experts
+    that the previous call, on the other stream, read: outputs bit-identical
+    to the resident layer's, counts equal to the LRU replay."""
+    torch = torch_cuda
+    from routed_expert_int4_amd.layer import DeviceLayer
+    slots, T = CFG.top_k, 12
+    say(f"[gpu] cache calls on two streams: {slots} slots, {T} one-token calls, then a batched call")
+    cache, weights, cached, resident = make_stack(torch, slots, n_layers=1, max_T=4)
+    x_bits = synth.gen_tokens(CFG, T, seed=33)
+    x = DeviceLayer.to_device_bf16(x_bits)
+    y_res, ids_res, w_res = resident[0].forward_each(x)
+    yb_res, idsb_res, _ = resident[0].forward(x[:4])
+    y = torch.empty_like(y_res)
+    ids = torch.empty_like(ids_res)
+    w = torch.empty_like(w_res)
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for t in range(T):
+        s, other = streams[t % 2], streams[(t + 1) % 2]
+        s.wait_stream(other)
+        cached[0].forward(x[t:t + 1], y[t:t + 1], ids[t:t + 1], w[t:t + 1], stream=s)
+    s = streams[T % 2]
+    s.wait_stream(streams[(T + 1) % 2])
+    yb, idsb, wb = cached[0].forward(x[:4], stream=s)
+    torch.cuda.synchronize()
+    assert torch.equal(ids, ids_res) and torch.equal(w, w_res)
+    assert torch.equal(y, y_res), "cached outputs on two streams differ from the resident layer's"
+    assert torch.equal(idsb, idsb_res)
+    idh = ids.cpu().numpy()
+    groups, spans = token_groups(idsb.cpu().numpy(), slots, [], ranges=True)
+    y_g, multi = resident_by_groups(torch, resident[0], x[:4], spans)
+    assert torch.equal(yb[multi], y_g[multi])
+    check_layer(weights[0], x_bits[:4], yb.cpu().numpy(), idsb.cpu().numpy(), wb.cpu().numpy())
+    hits, misses, evictions = lru.replay(list(idh) + groups, slots)
+    st = cache.stats(0)
+    say(f"[gpu] two streams: stats {st}, replay {(hits, misses, evictions)}")
+    assert (st["hits"], st["misses"], st["evictions"]) == (hits, misses, evictions)
     for lay in cached + resident:
         lay.close()
     cache.close()

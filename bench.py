@@ -81,6 +81,9 @@ def algorithmic_bytes(cfg):
         "router_launch": router + cfg.hidden * 2 + cfg.n_shared * gu,
         "gateup_launch": cfg.top_k * gu,
         "down_launch": n * dn + n * cfg.inter * 4 + cfg.hidden * 4,
+        # gate/up + down launch: both of the above (h is written and read
+        # inside the launch)
+        "gateup_down_launch": cfg.top_k * gu + n * dn + n * cfg.inter * 4 + cfg.hidden * 4,
     }
 
 
@@ -111,16 +114,16 @@ def read_record(path, tag, sources, **match):
     return rec
 
 
-def measured_traffic():
-    """HBM bytes per launch of the dominant decode kernel from the committed
-    rocprofv3 counter record.
+def measured_traffic(kernel):
+    """HBM bytes per launch of a decode kernel (its name as rocprofv3 prints
+    it, up to the argument list) from the committed rocprofv3 counter record.
 
     The record holds FETCH_SIZE and WRITE_SIZE per dispatch of the kernel,
     each scaled by what the counter reads for a device copy of known size,
     and the digest of the kernel sources they were taken on.  Returns None
     when there is no record or the kernel source has changed since.
     """
-    rec = read_record(TRAFFIC_RECORD, "traffic-record", KERNEL_SOURCES)
+    rec = read_record(TRAFFIC_RECORD, "traffic-record", KERNEL_SOURCES, kernel_name=kernel)
     return int(rec["hbm_bytes_per_launch"]) if rec else None
 
 
@@ -192,6 +195,10 @@ def main() -> int:
     ap.add_argument("--top-p", type=float, default=1.0,
                     help="decode and cache-stack: adaptive expert top-p (1: plain top-k); decode prices its bytes "
                          "by the experts kept")
+    ap.add_argument("--decode-launches", type=int, default=3, choices=[1, 2, 3],
+                    help="decode: launches per token of the timed path (3: router, gate/up, down, the library's "
+                         "default; 2: router launch + one gate/up + down launch; 1: one fused launch); the other "
+                         "two are timed beside it for comparison")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported (this layer's path is "
@@ -739,74 +746,99 @@ def bench_decode(args) -> int:
             if rc != 0:
                 raise B.MoeError(rc, B.last_error())
 
-    log(f"warmup {args.warmup} step(s)")
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    log(f"timing {args.steps} step(s) of {args.tokens} tokens")
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    e0.record(stream)
-    for _ in range(args.steps):
-        step()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_total = e0.elapsed_time(e1)
-    ms_per_step = ms_total / args.steps
-    tokens_per_s = args.tokens * args.steps / (ms_total / 1e3)
-    # with the top-p cut only the kept routed experts are read: price the
-    # routed bytes by the mean kept count (every step routes the same tokens)
-    kept = float((ids >= 0).sum().item()) / args.tokens
-    if kept != cfg.top_k:
-        for key in ("routed_per_token", "gateup_launch"):
-            nbytes[key] = int(round(nbytes[key] * kept / cfg.top_k))
-        nbytes["layer_per_token"] -= int(round((cfg.top_k - kept) * nbytes["expert"]))
-        nbytes["down_launch"] = int(round(nbytes["down_launch"] * (kept + cfg.n_shared) / (cfg.top_k + cfg.n_shared)))
-    routed_gbs = tokens_per_s * nbytes["routed_per_token"] / 1e9
-    layer_gbs = tokens_per_s * nbytes["layer_per_token"] / 1e9
-    log(f"{ms_per_step:.3f} ms/step, {tokens_per_s:.0f} tokens/s, routed {routed_gbs:.0f} GB/s (wall {wall:.2f} s)")
-
     def kernel_avg_us():
         """Per-kind average launch duration (us) over one step, from HIP
         events stamped with each kernel's own begin and end on the launch
-        stream: router, gate/up, down + combine, fused one-token launch."""
+        stream (None for a kind that did not run)."""
         B.moe_layer_profile(layer.handle, True)
         step()
         torch.cuda.synchronize()
         kms, kn = B.moe_layer_profile_read(layer.handle)
         B.moe_layer_profile(layer.handle, False)
-        return [1e3 * kms[k] / kn[k] if kn[k] else None for k in range(4)]
+        return [1e3 * kms[k] / kn[k] if kn[k] else None for k in range(len(kn))]
 
-    avg3 = kernel_avg_us()
-    gateup_gbs = nbytes["gateup_launch"] / (avg3[1] * 1e-6) / 1e9
-    down_gbs = nbytes["down_launch"] / (avg3[2] * 1e-6) / 1e9
-    router_gbs = nbytes["router_launch"] / (avg3[0] * 1e-6) / 1e9
-    log(f"kernel avg us: router {avg3[0]:.2f} ({router_gbs:.0f} GB/s), gate/up {avg3[1]:.2f} ({gateup_gbs:.0f} GB/s), "
-        f"down+combine {avg3[2]:.2f} ({down_gbs:.0f} GB/s)")
-    # the fused one-token launch on the same tokens, for comparison (opt-in:
-    # moe_layer_set_decode(layer, 1); bit-identical results)
-    fused = None
-    B.moe_layer_set_decode(layer.handle, 1)
-    for _ in range(max(1, args.warmup)):
-        step()
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for _ in range(args.steps):
-        step()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms1 = e0.elapsed_time(e1) / args.steps
-    avg1 = kernel_avg_us()
-    B.moe_layer_set_decode(layer.handle, 3)
-    if avg1[3] is not None:
-        fused = {
-            "ms_per_step": round(ms1, 4),
-            "tokens_per_s": round(args.tokens / (ms1 / 1e3), 1),
-            "avg_launch_us": round(avg1[3], 3),
-            "layer_gbs": round(nbytes["layer_per_token"] / (avg1[3] * 1e-6) / 1e9, 1),
-        }
-        log(f"fused one-token launch: {ms1:.3f} ms/step, launch avg {avg1[3]:.2f} us")
+    def time_mode(launches, warmup):
+        """Steps of one decode mode: ms per step, tokens/s and the launches'
+        average durations."""
+        B.moe_layer_set_decode(layer.handle, launches)
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record(stream)
+        for _ in range(args.steps):
+            step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        ms_total = e0.elapsed_time(e1)
+        return {"ms_per_step": ms_total / args.steps, "tokens_per_s": args.tokens * args.steps / (ms_total / 1e3),
+                "wall": wall, "avg_us": kernel_avg_us()}
+
+    # what each mode's launches are and the bytes each must move
+    KINDS = {1: [(3, "fused_one_token", "layer_per_token")],
+             2: [(0, "router_shared_gateup", "router_launch"), (8, "gateup_down_combine", "gateup_down_launch")],
+             3: [(0, "router_shared_gateup", "router_launch"), (1, "gateup_swiglu", "gateup_launch"),
+                 (2, "down_combine", "down_launch")]}
+    ROOFLINE_KERNEL = {
+        1: (3, "the whole layer in one fused launch (fused_decode_kernel<192, 64, 24, 4, 0, 8>)",
+            "void moe::(anonymous namespace)::fused_decode_kernel<192, 64, 24, 4, 0, 8>", "layer_per_token"),
+        2: (8, "routed gate/up + SwiGLU, down projections of the 8 routed and the shared expert and the combine "
+               "(gateup_down_kernel<192, 64, 24, 0>)",
+            "void moe::(anonymous namespace)::gateup_down_kernel<192, 64, 24, 0>", "gateup_down_launch"),
+        3: (1, "gate/up + SwiGLU of the 8 routed experts (gateup_kernel<192>)",
+            "void moe::(anonymous namespace)::gateup_kernel<192, 0>", "gateup_launch")}
+
+    def ran_mode(avg):
+        """The mode the launches show (a mode without an instance for the
+        shape or codec falls back to three launches)."""
+        return 1 if avg[3] else (2 if avg[8] else 3)
+
+    def mode_summary(r):
+        m = ran_mode(r["avg_us"])
+        kern = {name: round(r["avg_us"][k], 3) for k, name, _ in KINDS[m]}
+        gbs = {name: round(nbytes[b] / (r["avg_us"][k] * 1e-6) / 1e9, 1) for k, name, b in KINDS[m]}
+        return {"launches_per_token": m, "ms_per_step": round(r["ms_per_step"], 4),
+                "tokens_per_s": round(r["tokens_per_s"], 1),
+                "layer_gbs": round(r["tokens_per_s"] * nbytes["layer_per_token"] / 1e9, 2),
+                "kernels_avg_us": kern, "kernels_gbs": gbs}
+
+    log(f"warmup {args.warmup} step(s), decode mode {args.decode_launches}")
+    log(f"timing {args.steps} step(s) of {args.tokens} tokens")
+    main_run = time_mode(args.decode_launches, args.warmup)
+    ids_main = ids.clone()
+    ms_per_step = main_run["ms_per_step"]
+    tokens_per_s = main_run["tokens_per_s"]
+    mode = ran_mode(main_run["avg_us"])
+    # with the top-p cut only the kept routed experts are read: price the
+    # routed bytes by the mean kept count (every step routes the same tokens)
+    kept = float((ids_main >= 0).sum().item()) / args.tokens
+    if kept != cfg.top_k:
+        scale_down = (kept + cfg.n_shared) / (cfg.top_k + cfg.n_shared)
+        gu_kept = int(round(nbytes["gateup_launch"] * kept / cfg.top_k))
+        dn_kept = int(round(nbytes["down_launch"] * scale_down))
+        nbytes["routed_per_token"] = int(round(nbytes["routed_per_token"] * kept / cfg.top_k))
+        nbytes["layer_per_token"] -= int(round((cfg.top_k - kept) * nbytes["expert"]))
+        nbytes["gateup_launch"], nbytes["down_launch"] = gu_kept, dn_kept
+        nbytes["gateup_down_launch"] = gu_kept + dn_kept
+    routed_gbs = tokens_per_s * nbytes["routed_per_token"] / 1e9
+    layer_gbs = tokens_per_s * nbytes["layer_per_token"] / 1e9
+    log(f"{ms_per_step:.3f} ms/step, {tokens_per_s:.0f} tokens/s, routed {routed_gbs:.0f} GB/s "
+        f"(wall {main_run['wall']:.2f} s), launches {mode}: {main_run['avg_us']}")
+    main_summary = mode_summary(main_run)
+    # the other decode modes on the same tokens, for comparison (bit-identical
+    # results)
+    others = {}
+    for m in (3, 2, 1):
+        if m != args.decode_launches:
+            r = time_mode(m, max(1, args.warmup))
+            others[str(m)] = mode_summary(r)
+            log(f"decode mode {m}: {r['ms_per_step']:.3f} ms/step, kernels {others[str(m)]['kernels_avg_us']}")
+    B.moe_layer_set_decode(layer.handle, args.decode_launches)
+    rk, rdesc, rname, rbytes = ROOFLINE_KERNEL[mode]
+    roof_us = main_run["avg_us"][rk]
+    roof_gbs = nbytes[rbytes] / (roof_us * 1e-6) / 1e9
 
     cpu = None
     if args.cpu_sample > 0:
@@ -839,23 +871,22 @@ def bench_decode(args) -> int:
         "tokens_per_s": round(tokens_per_s, 1),
         "pct_of_hbm_peak": round(100 * routed_gbs / HBM_PEAK_GBS, 2),
         "layer_gbs": round(layer_gbs, 2),
+        "layer_frac_of_hbm_peak": round(layer_gbs / HBM_PEAK_GBS, 4),
         "bytes_per_token": {"routed": nbytes["routed_per_token"], "layer": nbytes["layer_per_token"]},
-        "decode_launches_per_token": 3,
-        "kernels_avg_us": {"router_shared_gateup": round(avg3[0], 3), "gateup_swiglu": round(avg3[1], 3),
-                           "down_combine": round(avg3[2], 3)},
-        "kernels_gbs": {"router_shared_gateup": round(router_gbs, 1), "gateup_swiglu": round(gateup_gbs, 1),
-                        "down_combine": round(down_gbs, 1)},
-        "fused_single_launch": fused,
+        "decode_launches_per_token": mode,
+        "kernels_avg_us": main_summary["kernels_avg_us"],
+        "kernels_gbs": main_summary["kernels_gbs"],
+        "other_decode_modes": others,
         "roofline": {
-            "kernel": "gate/up + SwiGLU of the 8 routed experts (gateup_kernel<192>)",
+            "kernel": rdesc,
             "bound": "hbm",
-            "achieved": round(gateup_gbs, 1),
+            "achieved": round(roof_gbs, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
-            "frac": round(gateup_gbs / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic() if cfg.top_p >= 1.0 and cfg.codec == "int4" else None,
-            "bytes_per_launch": nbytes["gateup_launch"],
-            "avg_launch_us": round(avg3[1], 3),
+            "frac": round(roof_gbs / HBM_PEAK_GBS, 4),
+            "traffic": measured_traffic(rname) if cfg.top_p >= 1.0 and cfg.codec == "int4" else None,
+            "bytes_per_launch": nbytes[rbytes],
+            "avg_launch_us": round(roof_us, 3),
         },
         "cpu_baseline": cpu,
     }

@@ -174,8 +174,8 @@ moe_status_t moe_router_topk(moe_layer_t* layer, const uint16_t* d_x, int T, int
 /* moe_layer_forward: the whole layer for T tokens.  d_x bf16 bits
  * [T][hidden]; d_y fp32 [T][hidden] (the block output without residual);
  * d_ids / d_w may be NULL, else receive the routing as in moe_router_topk.
- * T = 1 runs the decode kernels (three launches per token, or one fused
- * launch: moe_layer_set_decode).  T > 1 runs the batch-union path for
+ * T = 1 runs the decode kernels (three launches per token, or two, or one
+ * fused launch: moe_layer_set_decode).  T > 1 runs the batch-union path for
  * every codec (colibrì summary, fr.news.hada.io topic 31297, "Principales
  * fonctionnalités implémentées": in prefill and batched verification each
  * distinct expert of the batch is read once and applied to every position
@@ -250,17 +250,21 @@ moe_status_t moe_dispatch(moe_layer_t* layer, const int32_t* d_ids, int T, int32
 
 /* moe_layer_set_decode: how one-token calls run.  launches = 3 (the
  * default): three launches per token (router + shared gate/up, routed
- * gate/up, down + combine).  launches = 1: one fused launch per token, in
- * which co-resident workgroups run the router, the top-k, the routed and
- * shared gate/up, the down projections and the combine with the hand-offs
- * between them done inside the kernel, used when the kernel has an instance
- * for the layer's shape and codec (int4 experts), the layer has no expert
- * cache and all of its workgroups fit on the device at once (checked once
- * per layer with the occupancy API); otherwise three launches.  On the
- * GLM-shaped layer the fused launch takes longer than the three (with one
- * workgroup per CU its gate/up streaming keeps fewer loads in flight than
- * the dedicated kernel's), hence the default.  Both give bit-identical
- * results.  spin_limit: polls of an in-kernel wait before
+ * gate/up, down + combine).  launches = 2: the router launch, then one
+ * launch of co-resident workgroups that runs the routed gate/up and the down
+ * projections and combine, each workgroup issuing its down weight loads
+ * before it waits (inside the kernel) for every routed h.  launches = 1: one
+ * fused launch per token, in which co-resident workgroups run the router,
+ * the top-k, the routed and shared gate/up, the down projections and the
+ * combine with the hand-offs between them done inside the kernel.  Modes 2
+ * and 1 are used when their kernel has an instance for the layer's shape and
+ * codec (int4 experts), the layer has no expert cache and all of the
+ * launch's workgroups fit on the device at once (checked once per layer with
+ * the occupancy API); otherwise three launches.  On the GLM-shaped layer
+ * both take longer than the three (in one launch the waves of a CU finish
+ * their gate/up work far apart and the down projections' arithmetic runs
+ * after the wait instead of beside their loads), hence the default.  All
+ * three give bit-identical results.  spin_limit: polls of an in-kernel wait before
  * it gives up (0: the default, about one second); a wait that gives up lets
  * the launch finish, and every later moe_layer_forward,
  * moe_layer_forward_noalloc or moe_layer_profile_read of the layer returns
@@ -282,8 +286,9 @@ moe_status_t moe_layer_set_decode(moe_layer_t* layer, int launches, unsigned spi
  * preparation; 2 down + combine, or the batched grouped down + combine; 3
  * fused one-token launch; 4 batched grouped gate/up kernel; 5 batched
  * grouped down kernel; 6 batched gate/up of single-entry experts; 7 batched
- * down of single-entry experts), the summed duration in milliseconds and
- * the number of launches since profiling was enabled; arrays of 8 entries.
+ * down of single-entry experts; 8 one-token gate/up + down launch), the
+ * summed duration in milliseconds and the number of launches since
+ * profiling was enabled; arrays of 9 entries.
  * Timings taken with profiling enabled are per-kernel durations, not
  * end-to-end throughput. */
 moe_status_t moe_layer_profile(moe_layer_t* layer, int enable);

@@ -215,11 +215,11 @@ def moe_layer_set_decode(layer: int, launches: int, spin_limit: int = 0) -> None
 
 
 def moe_layer_profile_read(layer: int):
-    """-> (total_ms[8], launches[8]) for router, gate/up + SwiGLU, down + combine, fused one-token launch,
+    """-> (total_ms[9], launches[9]) for router, gate/up + SwiGLU, down + combine, fused one-token launch,
     batched grouped gate/up kernel, batched grouped down kernel, batched gate/up and down of single-entry
-    experts."""
-    ms = (ctypes.c_double * 8)()
-    n = (ctypes.c_uint64 * 8)()
+    experts, one-token gate/up + down launch."""
+    ms = (ctypes.c_double * 9)()
+    n = (ctypes.c_uint64 * 9)()
     check(lib().moe_layer_profile_read(layer, ms, n))
     return [float(v) for v in ms], [int(v) for v in n]
 

@@ -296,7 +296,7 @@ moe_status_t moe_layer_set_workspace(moe_layer_t* layer, void* d_ws, size_t byte
     layer->ws_bytes = bytes;
     layer->max_T = max_T;
     layer->W = W;
-    layer->fused_seq = 0;  // the control words were just cleared
+    layer->seq = DecodeSeq();  // the control words were just cleared
     *layer->status = 0u;
     if (layer->experts_set) {
         e = hipMemcpy(layer->ws + W.table, layer->host_table.data(), sizeof(void*) * layer->host_table.size(),
@@ -358,7 +358,7 @@ moe_status_t moe_layer_profile_read(moe_layer_t* layer, double* total_ms, uint64
 
 moe_status_t moe_layer_set_decode(moe_layer_t* layer, int launches, unsigned spin_limit) {
     if (!layer) return fail(MOE_EINVAL, "moe_layer_set_decode: layer is NULL");
-    if (launches != 1 && launches != 3) return fail(MOE_EINVAL, "moe_layer_set_decode: launches must be 1 or 3");
+    if (launches < 1 || launches > 3) return fail(MOE_EINVAL, "moe_layer_set_decode: launches must be 1, 2 or 3");
     layer->decode_launches = launches;
     layer->spin_limit = spin_limit ? spin_limit : kDefaultSpinLimit;
     return MOE_OK;
@@ -600,7 +600,7 @@ moe_status_t moe_layer_forward(moe_layer_t* layer, const uint16_t* d_x, int T, f
         return MOE_OK;
     }
     return decode_tokens(layer, layer->ws, layer->W, d_x, T, d_y, ids_base, c.top_k, w_base, c.top_k,
-                         &layer->fused_seq, s);
+                         &layer->seq, s);
 }
 
 }  // extern "C"
@@ -634,9 +634,28 @@ static bool use_fused(moe_layer_t* L, const DecodeArgs& a) {
     return L->fused_fits == 1;
 }
 
+// Whether the gate/up + down launch serves this layer (after the router
+// launch): as for the fused launch, not behind an expert cache, an instance
+// for the shape and codec, and every workgroup resident at once.
+static bool use_gateup_down(moe_layer_t* L, const DecodeArgs& a) {
+    if (L->cache || L->decode_launches != 2) return false;
+    if (L->gateup_down_fits < 0) {
+        L->gateup_down_fits = 0;
+        int threads = 0, per_cu = 0, dev = 0, cus = 0;
+        const int grid = gateup_down_grid(a, &threads);
+        const void* fn = gateup_down_kernel_function(a);
+        if (grid > 0 && fn && hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, threads, 0) == hipSuccess)
+            L->gateup_down_fits = (long long)per_cu * cus >= grid ? 1 : 0;
+        (void)hipGetLastError();
+    }
+    return L->gateup_down_fits == 1;
+}
+
 moe_status_t decode_tokens(moe_layer_t* layer, uint8_t* ws, const WorkspaceLayout& W, const uint16_t* d_x, int T,
                            float* d_y, int32_t* ids_base, int ids_stride, float* w_base, int w_stride,
-                           unsigned* fused_seq, hipStream_t s) {
+                           DecodeSeq* seq, hipStream_t s) {
     const moe_config_t& c = layer->cfg;
     moe_status_t st = MOE_OK;
     if (layer->cache && layer->next) {
@@ -651,12 +670,12 @@ moe_status_t decode_tokens(moe_layer_t* layer, uint8_t* ws, const WorkspaceLayou
                                    w_base + (size_t)t * w_stride, d_y + (size_t)t * c.hidden);
         if (use_fused(layer, a)) {
             FusedArgs f;
-            f.h_done = reinterpret_cast<unsigned*>(ws + W.sync);
-            f.shared_done = reinterpret_cast<unsigned*>(ws + W.sync + kSyncCounterBytes);
-            f.s_rec = reinterpret_cast<unsigned long long*>(ws + W.sync + 2 * kSyncCounterBytes);
+            f.h_done = reinterpret_cast<unsigned*>(ws + W.sync + kSyncHDone);
+            f.shared_done = reinterpret_cast<unsigned*>(ws + W.sync + kSyncSharedDone);
+            f.s_rec = reinterpret_cast<unsigned long long*>(ws + W.sync + kSyncScoreRecords);
             f.sb_rec = f.s_rec + kSyncMaxExperts;
             f.status = layer->status;
-            f.seq = ++*fused_seq;
+            f.seq = ++seq->fused;
             f.spin_limit = layer->spin_limit;
             ProfileScope pf(layer, 3, s, ProfileScope::kKernel);
             hipError_t e = decode_fused(a, f, s, pf.timing());
@@ -685,6 +704,17 @@ moe_status_t decode_tokens(moe_layer_t* layer, uint8_t* ws, const WorkspaceLayou
             e = decode_router(pa, s, cache_kernel_timing(layer->cache));
             if (e != hipSuccess) return hip_fail(e, "next-layer router launch");
             d_pred = pa.ids;
+        }
+        if (!layer->cache && use_gateup_down(layer, a)) {
+            FusedArgs f{};
+            f.h_done = reinterpret_cast<unsigned*>(ws + W.sync + kSyncGateUpDownDone);
+            f.status = layer->status;
+            f.seq = ++seq->gateup_down;
+            f.spin_limit = layer->spin_limit;
+            ProfileScope p8(layer, 8, s, ProfileScope::kKernel);
+            e = decode_gateup_down(a, f, s, p8.timing());
+            if (e != hipSuccess) return hip_fail(e, "gate/up + down kernel launch");
+            continue;
         }
         ProfileScope p1(layer, 1, s, layer->cache ? ProfileScope::kSpan : ProfileScope::kKernel);
         if (layer->cache) {

@@ -776,35 +776,18 @@ __global__ void __launch_bounds__(256) router_kernel(DecodeArgs a) {
     }
 }
 
-// ---------------------------------------------------------------- kernel 2
-// Items: (routed slot, block of R rows); blobs from the router's top-k, or
-// given directly by the expert cache.  A wave takes items wave_id + j *
-// n_waves in rounds of NI, in straight-line code (items past the end are
-// clamped to the last item and their results not stored), so the
-// compiler's wait counts stay exact.
-template <int KG, int F>
-__global__ void __launch_bounds__(256) gateup_kernel(DecodeArgs a) {
+// The routed gate/up items of one wave: items wave_id, wave_id + n_waves,
+// ... of n_items (wave_id < n_items).  kept is the wave's LDS copy of the
+// kept-slot list (read when a.kept is set) and blobs a 16-entry LDS row
+// that receives the slots' blobs.  With SC the h values are stored with
+// device-scope atomic stores, for workgroups of the same launch to read.
+template <int KG, int F, bool SC>
+__device__ __forceinline__ void routed_gateup_wave(const DecodeArgs& a, int lane, int wave_id, int n_waves,
+                                                   int n_items, const int* kept, const uint8_t** blobs) {
     using S = GateUpShape<KG>;
     constexpr int NI = kGateUpItemsPerRound;
-    const int lane = threadIdx.x & 63;
-    const int wave = wave_in_block();
-    const int wave_id = blockIdx.x * 4 + wave;
-    const int n_waves = gridDim.x * 4;
     const BlobLayout L = blob_layout(a.H, a.I, F);
     const int per_slot = a.I / row_pack(F) / S::R;
-    // With the router's kept-slot list (top-p cut) the items cover only the
-    // kept slots; the list goes to this wave's LDS row.
-    // (the slot count from the arguments first, so that all argument loads
-    // go out together before the kept-list branch)
-    __shared__ int wave_kept[4][17];
-    int n_routed_slots = a.use_slot_list ? a.n_slot_list : a.K;
-    if (a.kept) {
-        if (lane < 17) wave_kept[wave][lane] = lane <= a.K ? a.kept[lane] : 0;
-        __builtin_amdgcn_wave_barrier();
-        n_routed_slots = wave_kept[wave][0];
-    }
-    const int n_items = n_routed_slots * per_slot;
-    if (wave_id >= n_items) return;
 
     // Small dependent inputs first (vector loads complete in order, so
     // waiting for them must not mean waiting for weight streams issued
@@ -816,9 +799,8 @@ __global__ void __launch_bounds__(256) gateup_kernel(DecodeArgs a) {
     // item then waits only on the LDS counter, whereas reading a register
     // that a global load filled earlier can make the compiler drain every
     // outstanding weight load first.
-    __shared__ const uint8_t* wave_blobs[4][16];
     if (lane < 16)
-        wave_blobs[wave][lane] = a.direct ? lane_pick(a.blobs, lane) : (lane < a.K ? a.slot_blobs[lane] : nullptr);
+        blobs[lane] = a.direct ? lane_pick(a.blobs, lane) : (lane < a.K ? a.slot_blobs[lane] : nullptr);
     __builtin_amdgcn_wave_barrier();
     // Settle the activation registers here, once: an empty asm that reads
     // and rewrites each of them makes the compiler wait for their loads at
@@ -836,7 +818,7 @@ __global__ void __launch_bounds__(256) gateup_kernel(DecodeArgs a) {
         const int k = item / per_slot;
         int s = k;
         if (a.kept) {
-            s = wave_kept[wave][1 + k];
+            s = kept[1 + k];
         } else if (a.use_slot_list) {
 #pragma unroll
             for (int j = 0; j < 16; ++j)
@@ -845,14 +827,14 @@ __global__ void __launch_bounds__(256) gateup_kernel(DecodeArgs a) {
         return s;
     };
     auto rb_of = [&](int item) { return item % per_slot; };
-    auto blob_of = [&](int slot) { return wave_blobs[wave][slot]; };
+    auto blob_of = [&](int slot) { return blobs[slot]; };
     auto issue = [&](int item, GateUpBuf<KG, F>& buf) {
         const int it = item < n_items ? item : n_items - 1;
         gateup_issue<KG, F>(blob_of(slot_of(it)), L, rb_of(it), lane, buf);
     };
     auto compute = [&](int item, const GateUpBuf<KG, F>& buf) {
         const int it = item < n_items ? item : n_items - 1;
-        gateup_compute<KG, F>(buf, rb_of(it), lane, xa, xs, a.h + (size_t)slot_of(it) * a.I, a.I / 32, item < n_items);
+        gateup_compute<KG, F, SC>(buf, rb_of(it), lane, xa, xs, a.h + (size_t)slot_of(it) * a.I, a.I / 32, item < n_items);
     };
 
     // One to four items for this wave (every wave gets four at 4 x 4096
@@ -902,6 +884,37 @@ __global__ void __launch_bounds__(256) gateup_kernel(DecodeArgs a) {
 #pragma unroll
         for (int k = 0; k < NI; ++k) compute(base + k * n_waves, b[k]);
     }
+}
+
+// ---------------------------------------------------------------- kernel 2
+// Items: (routed slot, block of R rows); blobs from the router's top-k, or
+// given directly by the expert cache.  A wave takes items wave_id + j *
+// n_waves in rounds of NI, in straight-line code (items past the end are
+// clamped to the last item and their results not stored), so the
+// compiler's wait counts stay exact.
+template <int KG, int F>
+__global__ void __launch_bounds__(256) gateup_kernel(DecodeArgs a) {
+    using S = GateUpShape<KG>;
+    const int lane = threadIdx.x & 63;
+    const int wave = wave_in_block();
+    const int wave_id = blockIdx.x * 4 + wave;
+    const int n_waves = gridDim.x * 4;
+    const int per_slot = a.I / row_pack(F) / S::R;
+    // With the router's kept-slot list (top-p cut) the items cover only the
+    // kept slots; the list goes to this wave's LDS row.
+    // (the slot count from the arguments first, so that all argument loads
+    // go out together before the kept-list branch)
+    __shared__ int wave_kept[4][17];
+    int n_routed_slots = a.use_slot_list ? a.n_slot_list : a.K;
+    if (a.kept) {
+        if (lane < 17) wave_kept[wave][lane] = lane <= a.K ? a.kept[lane] : 0;
+        __builtin_amdgcn_wave_barrier();
+        n_routed_slots = wave_kept[wave][0];
+    }
+    const int n_items = n_routed_slots * per_slot;
+    if (wave_id >= n_items) return;
+    __shared__ const uint8_t* wave_blobs[4][16];
+    routed_gateup_wave<KG, F, false>(a, lane, wave_id, n_waves, n_items, wave_kept[wave], wave_blobs[wave]);
 }
 
 // ---------------------------------------------------------------- kernel 3
@@ -1423,6 +1436,11 @@ struct DownSteps {
         HI8 ha[S::CPL];
         float hscale[S::CPL];
         to_operands<F, S::CPL>(hraw, ha, hscale);
+        finish_ops(ha, hscale, lane, m, part);
+    }
+    // The same from h already converted to operands.
+    __device__ __forceinline__ void finish_ops(const HI8 (&ha)[S::CPL], const float (&hscale)[S::CPL], int lane, int m,
+                                               float* part) {
         float acc[MAXOWN];
 #pragma unroll
         for (int i = 0; i < MAXOWN; ++i) {
@@ -1733,6 +1751,142 @@ __global__ void __launch_bounds__(64 * kFusedWavesPerSlot * NK) fused_decode_ker
     if (threadIdx.x == 0 && s_fail) __hip_atomic_store(f.status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
+// ---------------------------------------------------------------- kernels 2 and 3 in one launch
+// h of one slot as dot operands (to_operands), staged in LDS for the waves
+// that share the slot; structure of arrays over the lanes (one 32-input
+// group of h per lane).
+struct HOperandsLds {
+    u32x4 he[kWave], ho[kWave], le[kWave], lo[kWave];
+    int corr[kWave];
+    float scale[kWave];
+    __device__ __forceinline__ void put(int lane, const HI8& o, float f) {
+        he[lane] = o.he;
+        ho[lane] = o.ho;
+        le[lane] = o.le;
+        lo[lane] = o.lo;
+        corr[lane] = o.corr;
+        scale[lane] = f;
+    }
+    __device__ __forceinline__ void get(int lane, HI8 (&o)[1], float (&f)[1]) const {
+        o[0].he = he[lane];
+        o[0].ho = ho[lane];
+        o[0].le = le[lane];
+        o[0].lo = lo[lane];
+        o[0].corr = corr[lane];
+        f[0] = scale[lane];
+    }
+};
+
+// Routed gate/up + SwiGLU, down projections and combine of one token in one
+// launch after the router launch: workgroups of 16 waves, one per block of R
+// output rows, all resident at once (the host checks the occupancy).  Every
+// wave first runs the gate/up items that gateup_kernel gives wave
+// blockIdx * 16 + wave of a 16-wave grid, storing h with device-scope
+// stores; then it issues the code loads of its down steps: routed slot
+// wave / 2, the steps of the block congruent to wave mod 2, and the shared
+// expert's steps congruent to wave mod 16.  Once every workgroup has counted
+// its h as published (a spread counter; a bounded wait), the wave of each
+// routed slot converts that slot's h into dot operands in LDS (the shared
+// expert's h, complete since the router launch, was converted before the
+// wait), every wave finishes its steps from them and the block is combined in
+// slot order.  Dot products, reductions and combine are down_combine_kernel's,
+// so y is bit-identical to the three-launch path's.
+constexpr int kGdWaves = 16;        // waves per workgroup
+constexpr int kGdWavesPerSlot = 2;  // waves sharing a routed slot's down steps
+
+template <int KG, int KGI, int NLD, int F>
+__global__ void __launch_bounds__(64 * kGdWaves) gateup_down_kernel(DecodeArgs a, FusedArgs f) {
+    using SG = GateUpShape<KG>;
+    using SD = DownShape<KGI, NLD>;
+    static_assert(SD::CPL == 1 && row_pack(F) == 1, "one h group per lane, one matrix row per stored row");
+    const int lane = threadIdx.x & 63;
+    const int wave = wave_in_block();
+    const int rb = blockIdx.x;
+    const int wave_id = rb * kGdWaves + wave;
+    const int n_waves = gridDim.x * kGdWaves;
+    const int per_slot = a.I / SG::R;
+    const BlobLayout L = blob_layout(a.H, a.I, F);
+    const int g0 = KGI >= kWave ? lane : (lane & (KGI - 1));
+    __shared__ int wave_kept[kGdWaves][17];
+    __shared__ const uint8_t* wave_blobs[kGdWaves][16];
+    __shared__ HOperandsLds hops[kFusedMaxSlots + 1];  // routed slots, then the shared expert
+    __shared__ float part[kFusedMaxSlots + 1][SD::R];
+    __shared__ int s_fail;
+    if (threadIdx.x == 0) s_fail = 0;
+    // the blobs of this wave's down slot and of the slot whose h it converts
+    const int slot = wave / kGdWavesPerSlot;
+    const uint8_t* dblob = slot < a.K ? a.slot_blobs[slot] : nullptr;
+    const uint8_t* hblob = wave < a.K ? a.slot_blobs[wave] : nullptr;
+
+    // ---- gate/up + SwiGLU of the routed slots (the kept ones with top-p)
+    int n_routed_slots = a.K;
+    if (a.kept) {
+        if (lane < 17) wave_kept[wave][lane] = lane <= a.K ? a.kept[lane] : 0;
+        __builtin_amdgcn_wave_barrier();
+        n_routed_slots = wave_kept[wave][0];
+    }
+    const int n_items = n_routed_slots * per_slot;
+    if (wave_id < n_items)
+        routed_gateup_wave<KG, F, true>(a, lane, wave_id, n_waves, n_items, wave_kept[wave], wave_blobs[wave]);
+
+    // ---- down: this wave's code loads go out before any wait
+    DownSteps<KGI, NLD, F, kGdWavesPerSlot> d;
+    if (dblob) d.issue(dblob, L, rb, lane, wave % kGdWavesPerSlot);
+    DownSteps<KGI, NLD, F, kGdWaves> sh;
+    if (a.S > 0) {
+        sh.issue(a.shared_blob, L, rb, lane, wave);
+        if (wave == kGdWaves - 1) {
+            float hraw[1][32];
+            load_h<1, KGI>(a.h + (size_t)a.K * a.I, g0, hraw);
+            HI8 ha[1];
+            float hs[1];
+            to_operands<F, 1>(hraw, ha, hs);
+            hops[a.K].put(lane, ha[0], hs[0]);
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's h stores are acknowledged
+    __syncthreads();
+    if (wave == 0) {
+        if (lane == 0) count_up(f.h_done, rb);
+        if (!wait_count(f.h_done, f.seq * (unsigned)gridDim.x, f.spin_limit, lane) && lane == 0) s_fail = 1;
+    }
+    __syncthreads();
+    // every routed h is published
+    if (hblob) {
+        float hraw[1][32];
+        load_h_device_scope<1, KGI>(a.h + (size_t)wave * a.I, g0, hraw);
+        HI8 ha[1];
+        float hs[1];
+        to_operands<F, 1>(hraw, ha, hs);
+        hops[wave].put(lane, ha[0], hs[0]);
+    }
+    __syncthreads();
+    if (dblob) {
+        HI8 ha[1];
+        float hs[1];
+        hops[slot].get(lane, ha, hs);
+        d.finish_ops(ha, hs, lane, wave % kGdWavesPerSlot, part[slot]);
+    } else if (slot < a.K && wave % kGdWavesPerSlot == 0) {
+        // a routed slot that the top-p cut dropped: weight 0, nothing read
+        for (int t = lane; t < SD::R; t += kWave) part[slot][t] = 0.0f;
+    }
+    if (a.S > 0) {
+        HI8 ha[1];
+        float hs[1];
+        hops[a.K].get(lane, ha, hs);
+        sh.finish_ops(ha, hs, lane, wave, part[a.K]);
+    }
+    __syncthreads();
+    if ((int)threadIdx.x < SD::R) {
+        const int t = threadIdx.x;
+        float y = 0.0f;
+        for (int j = 0; j < a.K; ++j) y = fmaf(a.w[j], part[j][t], y);
+        if (a.S > 0) y += part[a.K][t];
+        a.y[(size_t)rb * SD::R + t] = y;
+    }
+    if (threadIdx.x == 0 && s_fail) __hip_atomic_store(f.status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
 // ---------------------------------------------------------------- launchers
 // With timing events the launch goes through hipExtLaunchKernelGGL, which
 // stamps the events with the kernel's own start and end (no gap from the
@@ -1841,6 +1995,26 @@ const void* fused_fn(const DecodeArgs& a) {
     if (kg == 32 && kgi == 8 && epl == 1 && a.K == 6) return fused_fn_shape<32, 8, 1, kCodecInt4, 6>();
     if (kg == 128 && kgi == 32 && epl == 2 && a.K == 8) return fused_fn_shape<128, 32, 2, kCodecInt4, 8>();
     if (kg == 16 && kgi == 4 && epl == 4 && a.K == 8) return fused_fn_shape<16, 4, 4, kCodecInt4, 8>();
+    return nullptr;
+}
+
+// Instances of the gate/up + down launch: the fused kernel's shapes, int4
+// experts; other shapes and codecs take the three launches.
+template <int KG, int KGI, int F>
+const void* gateup_down_fn_shape() {
+    constexpr int NLD = down_rows(32 * KG, KGI, F) / rows_per_load(KGI);
+    return reinterpret_cast<const void*>(gateup_down_kernel<KG, KGI, NLD, F>);
+}
+
+const void* gateup_down_fn(const DecodeArgs& a) {
+    const int kg = a.H / 32, kgi = a.I / 32;
+    if (a.S > 1 || a.K > kFusedMaxSlots || a.direct || a.use_slot_list || !a.table) return nullptr;
+    if (a.codec != kCodecInt4) return nullptr;
+    if (kg == 192 && kgi == 64) return gateup_down_fn_shape<192, 64, kCodecInt4>();
+    if (kg == 8 && kgi == 4) return gateup_down_fn_shape<8, 4, kCodecInt4>();
+    if (kg == 32 && kgi == 8) return gateup_down_fn_shape<32, 8, kCodecInt4>();
+    if (kg == 128 && kgi == 32) return gateup_down_fn_shape<128, 32, kCodecInt4>();
+    if (kg == 16 && kgi == 4) return gateup_down_fn_shape<16, 4, kCodecInt4>();
     return nullptr;
 }
 
@@ -1978,6 +2152,27 @@ hipError_t decode_fused(const DecodeArgs& a, const FusedArgs& f, hipStream_t st,
     const void* fn = fused_fn(a);
     int threads = 0;
     const int grid = fused_grid(a, &threads);
+    if (!fn || grid == 0) return hipErrorInvalidValue;
+    DecodeArgs args = a;
+    FusedArgs fargs = f;
+    void* params[] = {&args, &fargs};
+    if (tm.start)
+        return hipExtLaunchKernel(fn, dim3(grid), dim3(threads), params, 0, st, tm.start, tm.stop, 0);
+    return hipLaunchKernel(fn, dim3(grid), dim3(threads), params, 0, st);
+}
+
+int gateup_down_grid(const DecodeArgs& a, int* threads) {
+    if (!gateup_down_fn(a)) return 0;
+    *threads = 64 * kGdWaves;
+    return a.H / down_rows(a.H, a.I / 32, a.codec);
+}
+
+const void* gateup_down_kernel_function(const DecodeArgs& a) { return gateup_down_fn(a); }
+
+hipError_t decode_gateup_down(const DecodeArgs& a, const FusedArgs& f, hipStream_t st, const LaunchTiming& tm) {
+    const void* fn = gateup_down_fn(a);
+    int threads = 0;
+    const int grid = gateup_down_grid(a, &threads);
     if (!fn || grid == 0) return hipErrorInvalidValue;
     DecodeArgs args = a;
     FusedArgs fargs = f;

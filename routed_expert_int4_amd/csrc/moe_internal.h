@@ -48,11 +48,16 @@ moe_status_t validate_supported(const moe_config_t* c);
 // The one-token decode path over T tokens with the per-call state at ws
 // (laid out as W): token t reads x[t], writes y[t] and its routing to
 // ids_base + t * ids_stride and w_base + t * w_stride.
-// fused_seq counts the fused launches made on ws since its control words
-// were cleared (the fused kernel's counters count up across calls).
+// seq counts, per kernel, the launches made on ws since its control words
+// were cleared (the in-kernel counters of the fused launch and of the
+// gate/up + down launch count up across calls).
+struct DecodeSeq {
+    unsigned fused = 0;        // fused one-token launches
+    unsigned gateup_down = 0;  // gate/up + down launches
+};
 moe_status_t decode_tokens(moe_layer* L, uint8_t* ws, const WorkspaceLayout& W, const uint16_t* d_x, int T,
                            float* d_y, int32_t* ids_base, int ids_stride, float* w_base, int w_stride,
-                           unsigned* fused_seq, hipStream_t s);
+                           DecodeSeq* seq, hipStream_t s);
 // Kernel arguments of one token's decode launches, and of one batched launch
 // sequence over n tokens starting at x (outputs at ids / w / y).
 DecodeArgs decode_args(moe_layer* L, uint8_t* ws, const WorkspaceLayout& W, const uint16_t* x, int32_t* ids,
@@ -63,8 +68,9 @@ moe_status_t check_layer_status(const moe_layer* L, const char* who);
 
 constexpr unsigned kDefaultSpinLimit = 1u << 20;  // polls, about a second
 // moe_layer_profile kinds: router, gate/up, down + combine, fused one-token
-// launch, and the batched path's grouped gate/up and down kernels alone
-constexpr int kProfileKinds = 8;
+// launch, the batched path's grouped gate/up and down kernels alone, the
+// batched GEMVs of single-entry experts, and the gate/up + down launch
+constexpr int kProfileKinds = 9;
 
 }  // namespace moe
 
@@ -85,12 +91,15 @@ struct moe_layer {
     // whose experts one-token calls predict and prefetch, and the copy limit
     moe_layer* next = nullptr;
     int max_prefetch = 0;
-    // one-token calls: 3 = three launches (the default), 1 = one fused
-    // launch when its workgroups fit on the device at once (moe_layer_set_decode)
+    // one-token calls: 3 = three launches (the default), 2 = the router
+    // launch and one gate/up + down launch, 1 = one fused launch; 2 and 1
+    // when their workgroups fit on the device at once, else three
+    // (moe_layer_set_decode)
     int decode_launches = 3;
     unsigned spin_limit = moe::kDefaultSpinLimit;
     int fused_fits = -1;           // occupancy check of the fused launch (-1: not yet made)
-    unsigned fused_seq = 0;        // fused launches on the bound workspace
+    int gateup_down_fits = -1;     // occupancy check of the gate/up + down launch
+    moe::DecodeSeq seq;            // in-kernel counted launches on the bound workspace
     unsigned* status = nullptr;    // host-visible word the fused kernel sets when a wait gives up
     // per-kernel event timing (moe_layer_profile)
     bool profiling = false;

@@ -70,7 +70,13 @@ constexpr int kSyncCounters = 32;
 constexpr int kSyncStride = 64;  // words (256 bytes)
 constexpr int kSyncMaxExperts = 256;
 constexpr size_t kSyncCounterBytes = kSyncCounters * kSyncStride * sizeof(unsigned);
-constexpr size_t kSyncBytes = 2 * kSyncCounterBytes + 2 * kSyncMaxExperts * sizeof(unsigned long long);
+// Offsets in the sync region: the fused launch's h and shared-expert
+// counts, its score records, and the count of the gate/up + down launch.
+constexpr size_t kSyncHDone = 0;
+constexpr size_t kSyncSharedDone = kSyncCounterBytes;
+constexpr size_t kSyncScoreRecords = 2 * kSyncCounterBytes;
+constexpr size_t kSyncGateUpDownDone = kSyncScoreRecords + 2 * kSyncMaxExperts * sizeof(unsigned long long);
+constexpr size_t kSyncBytes = kSyncGateUpDownDone + kSyncCounterBytes;
 struct FusedArgs {
     unsigned* h_done;               // kSyncCounters words
     unsigned* shared_done;          // kSyncCounters words: workgroups whose shared expert h is published
@@ -100,6 +106,15 @@ bool decode_shape_supported(int hidden, int inter, int top_k, int n_shared);
 int fused_grid(const DecodeArgs& a, int* threads);
 const void* fused_kernel_function(const DecodeArgs& a);
 hipError_t decode_fused(const DecodeArgs& a, const FusedArgs& f, hipStream_t st, const LaunchTiming& tm = {});
+// Routed gate/up + SwiGLU, down projections and combine of one token in one
+// launch of co-resident workgroups after decode_router (the hand-off from h
+// to the down projections done in the kernel; f.h_done, f.seq, f.spin_limit
+// and f.status are used).  gateup_down_grid returns the launch's workgroups
+// and threads per workgroup, or 0 when the kernel has no instance for this
+// shape and codec; gateup_down_kernel_function returns the kernel.
+int gateup_down_grid(const DecodeArgs& a, int* threads);
+const void* gateup_down_kernel_function(const DecodeArgs& a);
+hipError_t decode_gateup_down(const DecodeArgs& a, const FusedArgs& f, hipStream_t st, const LaunchTiming& tm = {});
 
 // ------------------------------------------------------------ batched path
 // Tokens per MFMA row block (the smallest tile) and rows per gate/up

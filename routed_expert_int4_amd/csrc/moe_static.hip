@@ -108,9 +108,10 @@ moe_status_t moe_layer_forward_noalloc(moe_layer_t* layer, const uint16_t* d_x, 
     // slots, overwritten token after token
     int32_t* ids = d_ids ? d_ids : reinterpret_cast<int32_t*>(base + W.ids);
     float* w = d_w ? d_w : reinterpret_cast<float*>(base + W.w);
-    // the setup launch cleared the control words: fused launches count from 0
-    unsigned fused_seq = 0;
-    return decode_tokens(layer, base, W, d_x, T, d_y, ids, d_ids ? c.top_k : 0, w, d_w ? c.top_k : 0, &fused_seq, s);
+    // the setup launch cleared the control words: in-kernel counted launches
+    // count from 0
+    DecodeSeq seq;
+    return decode_tokens(layer, base, W, d_x, T, d_y, ids, d_ids ? c.top_k : 0, w, d_w ? c.top_k : 0, &seq, s);
 }
 
 }  // extern "C"

@@ -193,52 +193,67 @@ __device__ __forceinline__ int pair_token(const BatchArgs& a, int p) {
 __device__ __forceinline__ constexpr int frag_col(int j) { return (j >> 1) + 4 * (j & 1); }
 
 // ---------------------------------------------------------------- router
-// Partial logits of a 16-token x 16-expert tile over one of router_splits
-// column ranges, on the matrix cores (v_mfma_f32_16x16x4_f32: tokens as A
-// rows, W_r rows as B columns, bf16 activations widened exactly to fp32).
-// The 4 waves of a workgroup split the range again and are summed in wave
-// order through LDS; the splits are summed in order by the top-k kernel
-// (deterministic).  A lane loads 4 consecutive columns of its token and of
-// its expert and feeds them to 4 MFMAs, one column each, so every k-block of
-// an MFMA covers the same columns in A and B.
+// Partial logits of a 64-token x 16 NEB-expert tile over one of
+// router_splits column ranges, on the matrix cores (v_mfma_f32_16x16x4_f32:
+// tokens as A rows, W_r rows as B columns, bf16 activations widened exactly
+// to fp32).  Wave w of the workgroup takes tokens 16w..16w+15 of the tile
+// over the whole range, NEB expert blocks sharing each activation load; a
+// lane loads 4 consecutive columns of its token and of its experts and feeds
+// them to 4 MFMAs, one column each, so every k-block of an MFMA covers the
+// same columns in A and B.  The splits are summed in order by the top-k
+// kernel (deterministic).  Grid (expert tiles, splits, token tiles): with 4
+// expert tiles and 16 splits a workgroup's XCD (its linear index mod 8)
+// depends on the expert tile and the split only, so each block of W_r is read
+// into one XCD's L2 for all token tiles.
+template <int NEB, int NS>
 __global__ void __launch_bounds__(256) batch_router_kernel(BatchArgs a) {
-    __shared__ f32x4 part[4][kWave];
+    constexpr int D = NS < 4 ? NS : 4;  // steps of 16 columns in flight
     const int lane = threadIdx.x & 63, wv = wave_in_block();
     const int m = lane & 15, q = lane >> 4;
-    const int e0 = blockIdx.x * 16, t0 = blockIdx.y * 16, split = blockIdx.z;
+    const int e0 = blockIdx.x * 16 * NEB, split = blockIdx.y, t0 = blockIdx.z * 64 + 16 * wv;
+    if (t0 >= a.T) return;
     const int t = t0 + m;
     const bool tok = t < a.T;
-    const int kw = a.H / (4 * a.router_splits);  // columns per wave (a multiple of 16)
-    const int c0 = (split * 4 + wv) * kw + 4 * q;
+    const int c0 = split * (16 * NS) + 4 * q;  // a split is NS steps of 16 columns
     const uint16_t* xr = a.x + (size_t)(tok ? t : 0) * a.H + c0;
     const float* wr = a.router_w + (size_t)(e0 + m) * a.H + c0;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-    for (int k = 0; k < kw; k += 16) {
-        const u32x2 xv = tok ? *as_global<u32x2>(xr + k) : u32x2{0u, 0u};
-        const f32x4 wv4 = *as_global<f32x4>(wr + k);
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(bf16_lo(xv[0]), wv4[0], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(bf16_hi(xv[0]), wv4[1], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(bf16_lo(xv[1]), wv4[2], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(bf16_hi(xv[1]), wv4[3], acc, 0, 0, 0);
-    }
-    part[wv][lane] = acc;
-    __syncthreads();
-    if (wv != 0) return;
-    f32x4 r = part[0][lane];
+    f32x4 acc[NEB];
 #pragma unroll
-    for (int w = 1; w < 4; ++w) {
-        const f32x4 v = part[w][lane];
+    for (int b = 0; b < NEB; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    u32x2 xv[D];
+    f32x4 w[D][NEB];
+    auto load = [&](int k, int slot) {
+        xv[slot] = tok ? *as_global<u32x2>(xr + 16 * k) : u32x2{0u, 0u};
 #pragma unroll
-        for (int j = 0; j < 4; ++j) r[j] += v[j];
+        for (int b = 0; b < NEB; ++b) w[slot][b] = *as_global<f32x4>(wr + (size_t)16 * b * a.H + 16 * k);
+    };
+#pragma unroll
+    for (int k = 0; k < D; ++k) load(k, k);
+    // straight-line over the split: step k is computed from its slot, which
+    // then takes step k + D
+#pragma unroll
+    for (int k = 0; k < NS; ++k) {
+        const int slot = k % D;
+        const float x0 = bf16_lo(xv[slot][0]), x1 = bf16_hi(xv[slot][0]);
+        const float x2 = bf16_lo(xv[slot][1]), x3 = bf16_hi(xv[slot][1]);
+#pragma unroll
+        for (int b = 0; b < NEB; ++b) {
+            acc[b] = __builtin_amdgcn_mfma_f32_16x16x4f32(x0, w[slot][b][0], acc[b], 0, 0, 0);
+            acc[b] = __builtin_amdgcn_mfma_f32_16x16x4f32(x1, w[slot][b][1], acc[b], 0, 0, 0);
+            acc[b] = __builtin_amdgcn_mfma_f32_16x16x4f32(x2, w[slot][b][2], acc[b], 0, 0, 0);
+            acc[b] = __builtin_amdgcn_mfma_f32_16x16x4f32(x3, w[slot][b][3], acc[b], 0, 0, 0);
+        }
+        if (k + D < NS) load(k + D, slot);
     }
-    // lane holds tokens t0 + 4q + j of expert e0 + m
+    // lane holds tokens t0 + 4q + j of experts e0 + 16b + m
     float* out = a.logit_part + (size_t)split * a.T * a.E;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int tt = t0 + 4 * q + j;
-        if (tt < a.T) out[(size_t)tt * a.E + e0 + m] = r[j];
-    }
+    for (int b = 0; b < NEB; ++b)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int tt = t0 + 4 * q + j;
+            if (tt < a.T) out[(size_t)tt * a.E + e0 + 16 * b + m] = acc[b][j];
+        }
 }
 
 // ---------------------------------------------------------------- top-k
@@ -336,40 +351,51 @@ __device__ __forceinline__ int wave_exclusive_scan(int v, int lane, int* total) 
     return x - v;
 }
 
-// One workgroup.  Keys (expert << 16 | entry) are unique, so the bitonic
-// sort gives the stable order by expert, then token, then slot.
-__global__ void __launch_bounds__(1024) batch_dispatch_kernel(BatchArgs a) {
-    __shared__ unsigned keys[kMaxDispatchEntries];
+// One workgroup of 16 waves; a stable counting placement (entries by
+// expert, then token, then slot).  Wave w owns a consecutive range of
+// entries and walks it 64 at a time: a lane finds the lanes holding the same
+// expert with eight ballots over the id's bits, so its rank among the wave's
+// entries of that expert so far is the wave's running count (LDS) plus the
+// number of such lanes below it.  The counts per wave and expert are then
+// turned into each wave's first place per expert (expert offset plus the
+// counts of the waves before it), and every entry goes to that place plus
+// its rank.
+constexpr int kDispatchWaves = 16;
+__global__ void __launch_bounds__(64 * kDispatchWaves) batch_dispatch_kernel(BatchArgs a) {
+    __shared__ int whist[kDispatchWaves][256];  // per wave: entries per expert, then its first place per expert
+    __shared__ int rank[kMaxDispatchEntries];   // an entry's rank among its wave's entries of its expert
     __shared__ int cnt[256], off[256], toff[256], dpos[256], spos[256];
     __shared__ int totals[4];
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int n = a.T * a.K;
-    int n2 = kWave;
-    while (n2 < n) n2 <<= 1;
-    // a dropped choice (id -1, top-p cut) sorts to the end with the padding
     // an id outside [0, E) takes no entry, as a choice the top-p cut dropped
     auto valid = [&](int i) { return i < n && a.ids[i] >= 0 && a.ids[i] < a.E; };
-    for (int i = tid; i < n2; i += 1024)
-        keys[i] = valid(i) ? (((unsigned)a.ids[i] << 16) | (unsigned)i) : 0xFFFFFFFFu;
-    if (tid < 256) cnt[tid] = 0;
+    for (int i = tid; i < kDispatchWaves * 256; i += 64 * kDispatchWaves) (&whist[0][0])[i] = 0;
     __syncthreads();
-    for (int i = tid; i < n; i += 1024)
-        if (valid(i)) atomicAdd(&cnt[a.ids[i]], 1);
-    for (int k = 2; k <= n2; k <<= 1) {
-        for (int j = k >> 1; j > 0; j >>= 1) {
-            __syncthreads();
-            for (int i = tid; i < n2; i += 1024) {
-                const int p = i ^ j;
-                if (p > i) {
-                    const unsigned x = keys[i], y = keys[p];
-                    const bool up = (i & k) == 0;
-                    if ((x > y) == up) {
-                        keys[i] = y;
-                        keys[p] = x;
-                    }
-                }
-            }
+    const int per_wave = (n + 64 * kDispatchWaves - 1) / (64 * kDispatchWaves) * 64;
+    const int first = wv * per_wave;
+    for (int i = first + lane; i < first + per_wave; i += 64) {
+        const bool v = valid(i);
+        const int e = v ? a.ids[i] : 0;
+        unsigned long long same = __ballot(v);
+#pragma unroll
+        for (int bit = 0; bit < 8; ++bit) {
+            const unsigned long long ones = __ballot((e >> bit) & 1);
+            same &= ((e >> bit) & 1) ? ones : ~ones;
         }
+        const int below = __popcll(same & ((1ull << lane) - 1));
+        const int prev = v ? whist[wv][e] : 0;
+        if (v) rank[i] = prev + below;
+        __builtin_amdgcn_wave_barrier();
+        if (v && below == 0) whist[wv][e] = prev + __popcll(same);
+        __builtin_amdgcn_wave_barrier();
+    }
+    __syncthreads();
+    if (tid < 256) {
+        int c = 0;
+#pragma unroll
+        for (int w = 0; w < kDispatchWaves; ++w) c += whist[w][tid];
+        cnt[tid] = c;
     }
     __syncthreads();
     if (tid < kWave) {
@@ -416,21 +442,31 @@ __global__ void __launch_bounds__(1024) batch_dispatch_kernel(BatchArgs a) {
         }
     }
     __syncthreads();
+    // each wave's first place per expert
+    if (tid < a.E) {
+        int p = off[tid];
+#pragma unroll
+        for (int w = 0; w < kDispatchWaves; ++w) {
+            const int c = whist[w][tid];
+            whist[w][tid] = p;
+            p += c;
+        }
+    }
+    __syncthreads();
     // kept entries fill pairs [0, totals[0]); the rest of perm is -1 and a
     // dropped choice's inv is -1
     const int n_kept = totals[0];
-    for (int i = tid; i < n; i += 1024)
-        if (!valid(i)) a.inv[i] = -1;
-    for (int p = tid; p < n; p += 1024) {
-        if (p < n_kept) {
-            const int idx = (int)(keys[p] & 0xFFFFu);
-            a.perm[p] = idx;
-            a.inv[idx] = p;
+    for (int i = first + lane; i < first + per_wave && i < n; i += 64) {
+        if (valid(i)) {
+            const int p = whist[wv][a.ids[i]] + rank[i];
+            a.perm[p] = i;
+            a.inv[i] = p;
         } else {
-            a.perm[p] = -1;
+            a.inv[i] = -1;
         }
     }
-    for (int e = tid; e < a.E; e += 1024) {
+    for (int p = n_kept + tid; p < n; p += 64 * kDispatchWaves) a.perm[p] = -1;
+    for (int e = tid; e < a.E; e += 64 * kDispatchWaves) {
         const int c = cnt[e];
         a.counts[e] = c;
         a.offsets[e] = off[e];
@@ -1049,10 +1085,29 @@ hipError_t launch_down(const BatchArgs& a, hipStream_t st, const LaunchTiming& t
 
 }  // namespace
 
+namespace {
+template <int NS>
+hipError_t launch_router_ns(const BatchArgs& a, int neb, hipStream_t st) {
+    const dim3 grid(a.E / (16 * neb), a.router_splits, (a.T + 63) / 64);
+    if (neb == 4) hipLaunchKernelGGL((batch_router_kernel<4, NS>), grid, dim3(256), 0, st, a);
+    else if (neb == 2) hipLaunchKernelGGL((batch_router_kernel<2, NS>), grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((batch_router_kernel<1, NS>), grid, dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+}  // namespace
+
 hipError_t batch_router(const BatchArgs& a, hipStream_t st) {
     if (a.E % 16 || a.router_splits < 1 || a.H % (64 * a.router_splits)) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(batch_router_kernel, dim3(a.E / 16, (a.T + 15) / 16, a.router_splits), dim3(256), 0, st, a);
-    return hipGetLastError();
+    // expert blocks of 16 per wave: 4 (64-expert tiles) where they divide E
+    const int neb = a.E % 64 == 0 ? 4 : (a.E % 32 == 0 ? 2 : 1);
+    switch (a.H / a.router_splits / 16) {
+        case 4: return launch_router_ns<4>(a, neb, st);
+        case 8: return launch_router_ns<8>(a, neb, st);
+        case 16: return launch_router_ns<16>(a, neb, st);
+        case 24: return launch_router_ns<24>(a, neb, st);
+        case 32: return launch_router_ns<32>(a, neb, st);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 hipError_t batch_topk(const BatchArgs& a, bool convert, hipStream_t st) {
@@ -1063,7 +1118,7 @@ hipError_t batch_topk(const BatchArgs& a, bool convert, hipStream_t st) {
 
 hipError_t batch_dispatch(const BatchArgs& a, hipStream_t st) {
     if (a.T * a.K > kMaxDispatchEntries || a.E > 256) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(batch_dispatch_kernel, dim3(1), dim3(1024), 0, st, a);
+    hipLaunchKernelGGL(batch_dispatch_kernel, dim3(1), dim3(64 * kDispatchWaves), 0, st, a);
     return hipGetLastError();
 }
 

@@ -207,7 +207,9 @@ __device__ __forceinline__ constexpr int frag_col(int j) { return (j >> 1) + 4 *
 // into one XCD's L2 for all token tiles.
 template <int NEB, int NS>
 __global__ void __launch_bounds__(256) batch_router_kernel(BatchArgs a) {
-    constexpr int D = NS < 4 ? NS : 4;  // steps of 16 columns in flight
+    // steps of 16 columns in flight (8 x 18 registers with 4 expert blocks)
+    constexpr int DMAX = NEB == 4 ? 8 : 12;
+    constexpr int D = NS < DMAX ? NS : DMAX;
     const int lane = threadIdx.x & 63, wv = wave_in_block();
     const int m = lane & 15, q = lane >> 4;
     const int e0 = blockIdx.x * 16 * NEB, split = blockIdx.y, t0 = blockIdx.z * 64 + 16 * wv;
@@ -257,14 +259,9 @@ __global__ void __launch_bounds__(256) batch_router_kernel(BatchArgs a) {
 }
 
 // ---------------------------------------------------------------- top-k
-// One wave per token: group-limited top-k, then (convert) the token's
-// activations as fp16 scaled by 2^kx (max |x| into [2^13, 2^14)), stored per
-// (group, quarter) as 8 values in fragment order.
-template <int EPL, int CPL>
-__global__ void __launch_bounds__(256) batch_topk_kernel(BatchArgs a, int convert) {
-    const int lane = threadIdx.x & 63;
-    const int t = blockIdx.x * 4 + wave_in_block();
-    if (t >= a.T) return;
+// Group-limited top-k of token t on one wave.
+template <int EPL>
+__device__ __forceinline__ void topk_token(const BatchArgs& a, int t, int lane) {
     // logits = in-order sum of the router's partial sums (all partials
     // loaded first, so the loads overlap); s = sigmoid, sb = s + bias
     constexpr int MAXSP = kMaxRouterSplits;
@@ -298,7 +295,12 @@ __global__ void __launch_bounds__(256) batch_topk_kernel(BatchArgs a, int conver
         a.ids[(size_t)t * a.K + lane] = id;
         a.w[(size_t)t * a.K + lane] = wt;
     }
-    if (!convert) return;
+}
+
+// Token t's activations on one wave: fp16 scaled by 2^kx (max |x| into
+// [2^13, 2^14)), stored per (group, quarter) as 8 values in fragment order.
+template <int CPL>
+__device__ __forceinline__ void convert_token(const BatchArgs& a, int t, int lane) {
     const int KG = a.H / 32;
     const uint16_t* xr = a.x + (size_t)t * a.H;
     u32x4 raw[CPL][4];
@@ -337,6 +339,20 @@ __global__ void __launch_bounds__(256) batch_topk_kernel(BatchArgs a, int conver
         }
     }
     if (lane == 0) a.kx[t] = k;
+}
+
+// One wave per token: the top-k in workgroups with blockIdx.y = 0 and,
+// when the launch has a second row (convert), the activations in those with
+// blockIdx.y = 1 (the two do not depend on each other).
+template <int EPL, int CPL>
+__global__ void __launch_bounds__(256) batch_topk_kernel(BatchArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int t = blockIdx.x * 4 + wave_in_block();
+    if (t >= a.T) return;
+    if (blockIdx.y == 0)
+        topk_token<EPL>(a, t, lane);
+    else
+        convert_token<CPL>(a, t, lane);
 }
 
 // ---------------------------------------------------------------- dispatch
@@ -1004,12 +1020,12 @@ constexpr int kGroupedGrid = 512;  // 2 workgroups of 8 waves per CU
 
 template <int EPL>
 hipError_t launch_topk(const BatchArgs& a, bool convert, hipStream_t st) {
-    const dim3 grid((a.T + 3) / 4);
+    const dim3 grid((a.T + 3) / 4, convert ? 2 : 1);
     switch ((a.H / 32 + kWave - 1) / kWave) {
-        case 1: hipLaunchKernelGGL((batch_topk_kernel<EPL, 1>), grid, dim3(256), 0, st, a, (int)convert); break;
-        case 2: hipLaunchKernelGGL((batch_topk_kernel<EPL, 2>), grid, dim3(256), 0, st, a, (int)convert); break;
-        case 3: hipLaunchKernelGGL((batch_topk_kernel<EPL, 3>), grid, dim3(256), 0, st, a, (int)convert); break;
-        case 4: hipLaunchKernelGGL((batch_topk_kernel<EPL, 4>), grid, dim3(256), 0, st, a, (int)convert); break;
+        case 1: hipLaunchKernelGGL((batch_topk_kernel<EPL, 1>), grid, dim3(256), 0, st, a); break;
+        case 2: hipLaunchKernelGGL((batch_topk_kernel<EPL, 2>), grid, dim3(256), 0, st, a); break;
+        case 3: hipLaunchKernelGGL((batch_topk_kernel<EPL, 3>), grid, dim3(256), 0, st, a); break;
+        case 4: hipLaunchKernelGGL((batch_topk_kernel<EPL, 4>), grid, dim3(256), 0, st, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

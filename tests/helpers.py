@@ -63,6 +63,9 @@ MID_A = synth.LayerConfig(hidden=1024, inter=256, n_experts=64, n_groups=8, topk
 MID_B = synth.LayerConfig(hidden=4096, inter=1024, n_experts=128, n_groups=4, topk_group=2, top_k=8)
 MID_C = synth.LayerConfig(hidden=8192, inter=4096, n_experts=16, n_groups=4, topk_group=2, top_k=4)
 MID_D = synth.LayerConfig(hidden=512, inter=128, n_experts=256, n_groups=8, topk_group=4, top_k=8)
+# 96 experts (the batched router's two-block expert tiles) in 3 groups,
+# hidden 2048 (8 steps of 16 columns per router split)
+MID_E = synth.LayerConfig(hidden=2048, inter=512, n_experts=96, n_groups=3, topk_group=2, top_k=6)
 
 
 def zipf_glm_weights():

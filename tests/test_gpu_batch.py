@@ -24,7 +24,7 @@ from oracle import oracle
 from oracle.dispatch import dispatch as oracle_dispatch
 from routed_expert_int4_amd import binding as B
 from routed_expert_int4_amd import synth
-from tests.helpers import MID_A, MID_B, MID_C, MID_D, check_layer, check_routing, zipf_glm_weights
+from tests.helpers import MID_A, MID_B, MID_C, MID_D, MID_E, check_layer, check_routing, zipf_glm_weights
 
 pytestmark = pytest.mark.gpu
 
@@ -117,10 +117,11 @@ def test_dispatch_errors(torch_cuda, dispatch_layer):
 
 # ---------------------------------------------------------------- layer
 @pytest.mark.parametrize("cfg_name,T", [("TINY", 4), ("TINY", 2), ("MID_A", 37), ("MID_B", 16), ("MID_C", 5),
-                                        ("MID_D", 100)])
+                                        ("MID_D", 100), ("MID_E", 70), ("MID_E", 130)])
 def test_batch_layer_parity(torch_cuda, cfg_name, T):
     from routed_expert_int4_amd.layer import DeviceLayer
-    cfg = {"TINY": synth.TINY, "MID_A": MID_A, "MID_B": MID_B, "MID_C": MID_C, "MID_D": MID_D}[cfg_name]
+    cfg = {"TINY": synth.TINY, "MID_A": MID_A, "MID_B": MID_B, "MID_C": MID_C, "MID_D": MID_D,
+           "MID_E": MID_E}[cfg_name]
     say(f"[gpu] batched parity {cfg_name} T={T}")
     weights = synth.gen_layer(cfg, seed=0)
     x = synth.gen_tokens(cfg, T, seed=11)

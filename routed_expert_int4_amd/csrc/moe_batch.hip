@@ -876,9 +876,17 @@ __global__ void __launch_bounds__(kDownThreads) __attribute__((amdgpu_waves_per_
         constexpr int NSP = NS * P;  // (step, plane) loads, plane fastest
         // codes of plane pl and the scales of step s for load k = (s, pl)
         // (both planes of a step share its scales)
+        // (int4 keeps each lane's own group, 4s + q, and needs its scale only)
+        const uint16_t* dsc_q = reinterpret_cast<const uint16_t*>(dsc) + scale_index(row, q, KGI, a.down_p);
         auto load_step = [&](int k, u32x4& c, u32x4& sc) {
             const int s = k / P, pl = k - s * P;
             c = *as_global<u32x4>((pl ? dql : dq) + (4 * s + q) * 16);
+            if constexpr (F == kCodecInt4) {
+                // within a row the scale of group g + 1 lies down_p halves
+                // after that of group g
+                sc[0] = *as_global<uint16_t>(dsc_q + (size_t)4 * s * a.down_p);
+                return;
+            }
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
                 const size_t si = scale_index(row, 4 * s + m, KGI, a.down_p);
@@ -924,21 +932,23 @@ __global__ void __launch_bounds__(kDownThreads) __attribute__((amdgpu_waves_per_
                     const int k = sidx * P + pl;
                     u32x4 cd2 = cd1, sc2 = sc1;
                     if (k + 2 < NSP) load_step(k + 2, cd2, sc2);
-                    transpose_quarters(cd0);
                     if constexpr (F == kCodecInt4) {
-                        // int4: fp16(code x scale) fragments, as in gate/up,
-                        // against h as one fp16 value
+                        // int4: fp16(code x scale) fragments, as in gate/up
+                        // (lane (i, q) keeps group 4s + q, MFMA d takes its
+                        // dword d), against h as one fp16 value
+                        const unsigned sv = sc0[0];
 #pragma unroll
-                        for (int m = 0; m < 4; ++m) {
-                            const f16x8 bw = codes_to_f16x8(cd0[m], mg) * splat_h8(sc0[m]);
+                        for (int d = 0; d < 4; ++d) {
+                            const f16x8 bw = codes_to_f16x8(cd0[d], mg) * splat_h8(sv);
 #pragma unroll
                             for (int z = 0; z < NB; ++z) {
-                                const int slot = ((4 * c + m) * 4 + q) * TT + 16 * z + i;
+                                const int slot = ((4 * c + q) * 4 + d) * TT + 16 * z + i;
                                 const f16x8 ah = __builtin_bit_cast(f16x8, hs[buf][slot]);
                                 acc[0][z] = mfma16(ah, bw, acc[0][z]);
                             }
                         }
                     } else {
+                    transpose_quarters(cd0);
 #pragma unroll
                     for (int m = 0; m < 4; ++m) {
 #pragma unroll

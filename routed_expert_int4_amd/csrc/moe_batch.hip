@@ -581,6 +581,7 @@ __global__ void __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(4))
     constexpr int PT = (NX + NT - 1) / NT;  // per thread
     static_assert(CK % 4 == 0 && KG % CK == 0, "gate/up stage shape");
     __shared__ u32x4 xs[2][CK * 64 * NB];   // [(g * 4 + q) * TT + token]
+    __shared__ int s_kx[2][TT];             // the entries' activation exponents, by item parity
     const int tid = threadIdx.x, lane = tid & 63, wv = wave_in_block();
     const int i = lane & 15, q = lane >> 4;
     const int n_tiles = a.n_tiles[0];
@@ -610,6 +611,22 @@ __global__ void __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(4))
         for (int h = 0; h < RP; ++h)
 #pragma unroll
             for (int z = 0; z < NB; ++z) accg[h][z] = accu[h][z] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // the activation scaling exponents of the tile's entries for the
+        // stores after the last step: thread tt < TT fetches entry tt's token
+        // now and its exponent a quarter into the item and writes it to LDS
+        // half-way (before a stage barrier); every thread issues the loads
+        // (an entry past the count takes the last entry's), so the code
+        // loads' wait counts stay exact and the stores wait on no load
+        // (int4; the other codecs' kernels have no register to spare and
+        // load the exponents in the stores)
+        const int ib = ik & 1;
+        int kxr = 0;
+        if constexpr (F == kCodecInt4) {
+            const int n_pairs = a.T * a.K;
+            const int p = td.first_pair + (sm < td.count ? sm : td.count - 1);
+            const int v = a.perm[p < n_pairs ? p : n_pairs - 1];
+            kxr = p < n_pairs ? v / a.K : p - n_pairs;
+        }
         const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
         constexpr int NS = KG / 4;  // steps of 4 groups
         constexpr int P = code_planes(F);
@@ -655,6 +672,10 @@ __global__ void __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(4))
         // the compiler drain the prefetched loads (register rotation copies)
 #pragma unroll
         for (int st = 0; st < NST; ++st, ++gs) {
+            if constexpr (F == kCodecInt4) {
+                if (st == NST / 4) kxr = a.kx[kxr];
+                if (st == NST / 2 && tid < TT) s_kx[ib][tid] = kxr;
+            }
             const int buf = gs & 1;
 #pragma unroll
             for (int r = 0; r < PT; ++r)
@@ -753,7 +774,7 @@ __global__ void __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(4))
                 const int tt = 16 * z + 4 * q + j;
                 if (tt < td.count) {
                     const int p = td.first_pair + tt;
-                    const int kx = a.kx[pair_token(a, p)];
+                    const int kx = F == kCodecInt4 ? s_kx[ib][tt] : a.kx[pair_token(a, p)];
 #pragma unroll
                     for (int h = 0; h < RP; ++h) {
                         const float g = ldexpf(accg[h][z][j], -kx), u = ldexpf(accu[h][z][j], -kx);
@@ -842,6 +863,7 @@ __global__ void __launch_bounds__(kDownThreads) __attribute__((amdgpu_waves_per_
     constexpr int PT = (NPARTS * PART + kDownThreads - 1) / kDownThreads;  // per thread
     static_assert(CK % 4 == 0 && KGI % CK == 0 && PT >= 1, "down stage shape");
     __shared__ u32x4 hs[2][NPARTS * PART];   // [part * PART + (g * 4 + q) * TT + token]
+    __shared__ int s_kh[2][TT];              // the entries' h exponents, by item parity
     const int tid = threadIdx.x, lane = tid & 63, wv = wave_in_block();
     const int i = lane & 15, q = lane >> 4;
     const int n_tiles = a.n_tiles[0];
@@ -865,6 +887,13 @@ __global__ void __launch_bounds__(kDownThreads) __attribute__((amdgpu_waves_per_
         const int sm = tid & (TT - 1);
         const bool has = sm < td.count;
         const size_t src = (size_t)(td.first_pair + sm) * a.I;
+        // the entries' h scaling exponents for the stores after the last
+        // step: thread tt < TT loads entry tt's now (every thread loads; an
+        // entry past the count takes the last entry's) and writes it to LDS
+        // half-way through the item (before a stage barrier), so the stores
+        // wait on no load
+        const int ib = ik & 1;
+        int khr = a.kh[td.first_pair + (sm < td.count ? sm : td.count - 1)];
         f32x4 acc[RP][NB];
 #pragma unroll
         for (int h = 0; h < RP; ++h)
@@ -918,6 +947,7 @@ __global__ void __launch_bounds__(kDownThreads) __attribute__((amdgpu_waves_per_
         if (NSP > 1) load_step(1, cd1, sc1);
 #pragma unroll
         for (int st = 0; st < NST; ++st, ++gs) {
+            if (st == NST / 2 && tid < TT) s_kh[ib][tid] = khr;
             const int buf = gs & 1;
 #pragma unroll
             for (int r = 0; r < PT; ++r)
@@ -986,7 +1016,7 @@ __global__ void __launch_bounds__(kDownThreads) __attribute__((amdgpu_waves_per_
                     const int p = td.first_pair + tt;
 #pragma unroll
                     for (int h = 0; h < RP; ++h)
-                        a.d[(size_t)p * a.H + RP * row + h] = ldexpf(acc[h][z][j], -a.kh[p]);
+                        a.d[(size_t)p * a.H + RP * row + h] = ldexpf(acc[h][z][j], -s_kh[ib][tt]);
                 }
             }
     }

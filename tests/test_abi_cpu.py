@@ -335,3 +335,17 @@ def test_cache_replay_rejects_too_many_pins():
     tr = np.zeros((1, 4), np.int32) + np.arange(4, dtype=np.int32)
     with pytest.raises(B.MoeError):
         B.expert_cache_replay(16, 8, 4, tr, pinned=list(range(5)))
+
+
+@pytest.mark.parametrize("n", [2, 8])
+def test_bench_refuses_more_than_one_gpu(n):
+    # one GPU only: asking for more exits with status 2 and says why, before
+    # any device is touched
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", str(n), "--steps", "1"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert f"--gpus {n} is not supported" in r.stderr
+    assert r.stdout.strip() == ""
